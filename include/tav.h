@@ -1,0 +1,246 @@
+/*
+ * tav.h -- C ABI of the tree-masked scoring pass on AMD MI355X (gfx950).
+ *
+ * One batched pass over B token trees: every tree node is a query that attends
+ * to its sequence's cached prefix (paged KV) plus only its own root-to-node
+ * ancestors, followed by per-node verification of the tree against the target
+ * distribution, and (optionally) PreSTO's log-acceptance and MH walk over a
+ * prefetched subtree.
+ *
+ * Sources (the method is defined on these pages; the numbering is the pages'):
+ *  - Progressive Tree Drafting (arXiv 2607.10661), Section 3.1 "Tree
+ *    Construction": pi(v) = {v} U pi(P(v)); position from |pi(v)|.
+ *    Section 3.2 "Candidate Verification" and Appendix E / F: sequential
+ *    rejection with renormalisation; accepted sequence X' = (n0..nk, V_nk).
+ *  - RheoSampling (arXiv 2609.21827), Section 3.3 Algorithm 1
+ *    (RheoVerification), Section 5.4 (temperature decoupling).
+ *  - PreSTO (arXiv 2610.13171), Section 3.2 Example 3 / Equation 6
+ *    (log-acceptance), Appendix B.1 (Equations 7-9), Appendix B.3 Example 5
+ *    (walk over the prefetched subtree).
+ *
+ * Conventions shared by every entry point
+ *  - All array arguments are device pointers unless the field name ends in
+ *    _host.  Arrays are dense, row-major, and 16-byte aligned.
+ *  - The caller owns every buffer.  The library never allocates device memory
+ *    and keeps no pointer after a call returns; scratch lives in a caller-owned
+ *    workspace of at least tav_workspace_size() bytes (256-byte aligned).
+ *  - Calls are asynchronous on the given stream(s): host-checkable problems
+ *    return a tav_status synchronously and enqueue nothing; problems only the
+ *    device can see set bits in a status word inside the workspace
+ *    (tav_read_status).  The affected sequence's outputs are then unspecified.
+ *  - Streams are passed as void* and are hipStream_t values (NULL = the null
+ *    stream).  Calls on different workspaces are independent; two calls that
+ *    share a workspace must be ordered by the caller.
+ *
+ * Tree layout
+ *  - Sequence b owns nodes [node_offsets[b], node_offsets[b+1]) (at least one).
+ *  - parent[] is sequence-local: node 0 of a sequence is its root (parent -1,
+ *    the last committed token); every other node's parent is an earlier node
+ *    of the same sequence.  Hence every ancestor of node v has an id <= v.
+ *  - A sequence whose every node's parent is the node just before it is a
+ *    chain (causal attention, any length).  Any other tree may have at most
+ *    256 nodes (ancestor sets are 256-bit masks).
+ */
+#ifndef TAV_H
+#define TAV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tav_status {
+  TAV_OK = 0,
+  TAV_ERR_NULL_POINTER = 1,      /* a required pointer is NULL */
+  TAV_ERR_BAD_SHAPE = 2,         /* sizes inconsistent (offsets, heads, prefix vs block table, ...) */
+  TAV_ERR_UNSUPPORTED = 3,       /* valid but not implemented (head_dim, dtype, group size, vocab) */
+  TAV_ERR_WORKSPACE = 4,         /* workspace NULL, misaligned or smaller than tav_workspace_size() */
+  TAV_ERR_HIP = 5,               /* a HIP runtime call or kernel launch failed */
+  TAV_ERR_INVALID_ARGUMENT = 6   /* other invalid scalar argument (temperature field, counts, ...) */
+} tav_status;
+
+typedef enum tav_dtype {
+  TAV_F32 = 0,   /* float32 q/k/v/cache/out/logits */
+  TAV_BF16 = 1   /* bfloat16 q/k/v/cache/out/logits; fp32 accumulation */
+} tav_dtype;
+
+/* Device status bits (OR-ed into the workspace status word). */
+enum {
+  TAV_DEV_BAD_PARENT = 1u << 0,         /* parent not in [-1, v) or node 0 not a root */
+  TAV_DEV_TREE_TOO_LARGE = 1u << 1,     /* non-chain tree with more than 256 nodes */
+  TAV_DEV_BAD_BLOCK = 1u << 2,          /* block-table entry outside [0, num_blocks) */
+  TAV_DEV_BAD_TOKEN = 1u << 3,          /* a child token outside [0, vocab) */
+  TAV_DEV_DUP_SIBLING_TOKEN = 1u << 4,  /* two children of one node carry the same token */
+  TAV_DEV_MULTI_SAMPLED = 1u << 5,      /* more than one sampled child under one node */
+  TAV_DEV_NO_DRAFT = 1u << 6,           /* sampled child but draft_row of its parent < 0 or >= R */
+  TAV_DEV_ZERO_DRAFT_MASS = 1u << 7,    /* the sampled token has zero draft probability */
+  TAV_DEV_NONFINITE_LOGITS = 1u << 8,   /* NaN or +inf logit (-inf is allowed: zero mass) */
+  TAV_DEV_EMPTY_RESIDUAL = 1u << 9,     /* the final residual of the walk has no mass */
+  TAV_DEV_PATH_OVERFLOW = 1u << 10,     /* accepted path longer than max_path */
+  TAV_DEV_TOO_MANY_CHILDREN = 1u << 11, /* a node with more than 256 children */
+  TAV_DEV_PRESTO_BAD_TREE = 1u << 12,   /* malformed prefetching tree / request ids */
+  TAV_DEV_PLAN_MISMATCH = 1u << 13,     /* internal: device work plan differs from the host's */
+  TAV_DEV_BAD_TEMPERATURE = 1u << 14    /* a temperature that is not finite and > 0 */
+};
+
+/* Problem description (host struct). */
+typedef struct tav_problem {
+  int32_t num_seqs;                  /* B >= 1 */
+  const int32_t* node_offsets_host;  /* [B+1] host copy; node_offsets[0] = 0, strictly increasing */
+  const int32_t* node_offsets;       /* [B+1] device copy of the same */
+  const int32_t* prefix_len_host;    /* [B] host copy; cached prefix rows of each sequence (>= 0) */
+  const int32_t* prefix_len;         /* [B] device copy of the same */
+  int32_t num_q_heads;               /* Hq */
+  int32_t num_kv_heads;              /* Hkv; query head h reads KV head h / (Hq / Hkv) */
+  int32_t head_dim;                  /* 64 or 128 */
+  int32_t dtype;                     /* tav_dtype of q, k, v, caches, out and logits */
+  float sm_scale;                    /* softmax scale; 0 means 1/sqrt(head_dim) */
+  int32_t block_size;                /* prefix rows per KV block: 8, 16, 32 or 64 */
+  int32_t num_blocks;                /* physical blocks in k_cache / v_cache */
+  int32_t max_blocks_per_seq;        /* row stride of block_table; prefix_len <= this * block_size */
+  int32_t vocab;                     /* V for verification (0 when no verification is run) */
+} tav_problem;
+
+/* Tree arrays (device). token and sampled are only read by verification. */
+typedef struct tav_tree {
+  const int32_t* parent;    /* [N] sequence-local parent, -1 at each sequence's node 0 */
+  const int32_t* token;     /* [N] token of each node (the root's token is not read) */
+  const uint8_t* sampled;   /* [N] 1 if the node was drawn from its parent's draft distribution */
+} tav_tree;
+
+/* Optional outputs of tree preparation (each may be NULL). */
+typedef struct tav_tree_out {
+  int32_t* depth;       /* [N] |pi(v)| - 1 */
+  int32_t* position;    /* [N] prefix_len + depth (0-based position of the node's token) */
+  uint64_t* mask;       /* [N][4] bit j set iff node j (sequence-local) is in pi(v); zero for chains */
+  uint8_t* is_chain;    /* [B] 1 for a chain sequence */
+} tav_tree_out;
+
+/* Attention inputs and outputs.  Layouts:
+ *   q [N, Hq, D];  k_node, v_node [N, Hkv, D] (the tree nodes' own keys/values);
+ *   k_cache, v_cache [num_blocks, Hkv, block_size, D]: prefix row r of sequence b
+ *     is slot r % block_size of block block_table[b * max_blocks_per_seq + r / block_size];
+ *   out [N, Hq, D] in the problem dtype; lse [N, Hq] float (natural log), optional. */
+typedef struct tav_attn_io {
+  const void* q;
+  const void* k_node;
+  const void* v_node;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_table;
+  void* out;
+  float* lse;
+} tav_attn_io;
+
+/* Verification inputs and outputs.
+ *   logits [N, V] (problem dtype): target logits at each node (the distribution
+ *     over the token that follows the node);
+ *   temperature [B] > 0: p = softmax(logits / T);
+ *   draft [R, V] float and draft_row [N]: row draft_row[v] is the (already
+ *     tempered) distribution v's sampled child was drawn from; -1 if none;
+ *   uniforms [N, 2] in [0, 1): uniforms[c][0] tests node c as a candidate,
+ *     uniforms[v][1] drives the final draw at v.
+ * Outputs:
+ *   node_status [N]: 0 not reached, 1 accepted (the root always), 2 rejected;
+ *   path [B, max_path]: accepted sequence-local node ids from the root, -1 padded;
+ *   path_len [B]; bonus_token [B]: the final token drawn at the last path node.
+ *   node_stats [N, 3] float (optional): M = max l/T, S = sum exp(l/T - M), Z = sum (p - q~)+;
+ *   node_term_token [N] (optional): the token the final draw would give if the walk ended at v. */
+typedef struct tav_verify_io {
+  const void* logits;
+  const float* temperature;
+  const float* draft;
+  int32_t num_draft_rows;
+  const int32_t* draft_row;
+  const float* uniforms;
+  uint8_t* node_status;
+  int32_t* path;
+  int32_t max_path;
+  int32_t* path_len;
+  int32_t* bonus_token;
+  float* node_stats;
+  int32_t* node_term_token;
+} tav_verify_io;
+
+/* PreSTO prefetch round.  Per-token arrays hold tokens t = 1..T at index t-1.
+ *   root_lp0 / root_lq [T]: log p0 and log q_tau of the current state's tokens;
+ *   request i (0..R-1): cut[i] in [0, T); its suffix (tokens cut[i]+1..T) occupies
+ *     lp0/lq[suffix_off[i] .. suffix_off[i+1]) with suffix_off[i+1]-suffix_off[i] = T - cut[i];
+ *   prefetching tree over M nodes (node 0 = current state): pf_parent[v] < v;
+ *     pf_is_accept[v] = 1 for an acceptance child; pf_request[v] = its request id,
+ *     or -1 for a rejection child or a deferred request; u[v] = the MH uniform
+ *     used for the decision taken at node v.
+ * Outputs: log_accept [R] (Equation 6, computed in float64, stored as float);
+ *   pf_path [M] tree nodes visited from the root, -1 padded; pf_path_len [1]
+ *   = completed transitions + 1. */
+typedef struct tav_presto_io {
+  int32_t T;
+  float alpha;
+  const float* root_lp0;
+  const float* root_lq;
+  int32_t num_requests;
+  const int32_t* cut;
+  const int32_t* suffix_off;
+  const float* lp0;
+  const float* lq;
+  int32_t num_nodes;
+  const int32_t* pf_parent;
+  const uint8_t* pf_is_accept;
+  const int32_t* pf_request;
+  const float* u;
+  int32_t max_transitions;
+  float* log_accept;
+  int32_t* pf_path;
+  int32_t* pf_path_len;
+} tav_presto_io;
+
+/* Bytes of workspace the calls below need for this problem (host only; no HIP
+ * call).  presto may be NULL.  Errors: NULL pointer, bad shape. */
+tav_status tav_workspace_size(const tav_problem* prob, const tav_presto_io* presto, size_t* bytes);
+
+/* Tree preparation: validation, depth, position, ancestor masks, chain flags
+ * (Progressive Tree Drafting, Section 3.1).  Also clears the status word. */
+tav_status tav_tree_prep(const tav_problem* prob, const tav_tree* tree, const tav_tree_out* out,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Tree-masked attention (prep + split-KV prefix/tail attention + merge). */
+tav_status tav_tree_attention(const tav_problem* prob, const tav_tree* tree, const tav_attn_io* io,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Verification (vocabulary statistics + walk) of every sequence.  Clears the
+ * status word first. */
+tav_status tav_tree_verify(const tav_problem* prob, const tav_tree* tree, const tav_verify_io* io,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* PreSTO log-acceptance of every request and the MH walk. */
+tav_status tav_presto_accept(const tav_presto_io* io, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* The whole pass: tree prep and attention on attn_stream; verification (if
+ * verify != NULL) on verify_stream (may equal attn_stream; it runs concurrently
+ * otherwise); PreSTO (if presto != NULL) on verify_stream.  tree_out may be
+ * NULL.  Returns after enqueueing; verify_stream is made to wait for the status
+ * reset on attn_stream, and attn_stream is made to wait for verify_stream's
+ * work before the call returns, so synchronising attn_stream covers both. */
+tav_status tav_tree_attn_verify(const tav_problem* prob, const tav_tree* tree,
+                                const tav_attn_io* attn, const tav_verify_io* verify,
+                                const tav_presto_io* presto, const tav_tree_out* tree_out,
+                                void* workspace, size_t workspace_bytes,
+                                void* attn_stream, void* verify_stream);
+
+/* Waits for stream, then copies the device status word to *status_bits. */
+tav_status tav_read_status(const void* workspace, void* stream, uint32_t* status_bits);
+
+/* Static description of a status code. */
+const char* tav_status_string(tav_status s);
+
+/* Message of the last error returned on the calling thread ("" if none). */
+const char* tav_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TAV_H */

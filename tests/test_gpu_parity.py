@@ -1,0 +1,94 @@
+"""GPU parity of libtav against the oracle on seeded inputs (small and mid-size cases).
+
+Tolerances: attention out / lse within 2e-2 abs+rel in bf16 and 1e-5 in fp32;
+tree prep, accept flags, paths and tokens bit-exact except at decisions the
+oracle flags as near-ties (|u - threshold| < 1e-5, or u within 1e-5 of a CDF
+step); PreSTO log A within 1e-3.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+from workloads import gen
+import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+SEEDS = [10086, 1, 2]
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_c1_tiny_fp32(seed):
+    _say("c1", seed)
+    w = gen.make("c1", seed)
+    got = gu.run(w)
+    assert got["status"] == 0, got["status"]
+    gu.check_tree_prep(w, got)
+    gu.check_attention(w, got)
+    gu.check_verify(w, got)
+    gu.check_node_stats(w, got, range(w.N))
+
+
+CASES = {
+    # name: (tree, n_nodes, prefix_len, Hq, Hkv, D, V, T, extra)
+    "random_ragged": ("random", [1, 3, 64, 65, 200], [0, 1, 63, 700, 129], 32, 8, 128, 4096, 1.0, {}),
+    "binary_g8_d64": ("binary", [15, 31, 7], [16, 200, 3], 16, 2, 64, 2048, 0.7, {}),
+    "random_g1": ("random", [40, 10], [77, 1000], 4, 4, 128, 1024, 1.3, {}),
+    "eagle_hybrid": ("eagle", [30, 22], [2048, 300], 32, 8, 128, 8192, 0.7, {"max_depth": 5, "hybrid": "all"}),
+    "random_g16": ("random", [16, 17], [64, 65], 16, 1, 128, 512, 1.0, {}),
+}
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_small_bf16_trees(case, seed):
+    tree, n, L, Hq, Hkv, D, V, T, extra = CASES[case]
+    _say("tree case", case, seed)
+    w = gen.tree_batch(seed, B=len(n), prefix_len=L, tree=tree, n_nodes=n, Hq=Hq, Hkv=Hkv, D=D,
+                       dtype="bf16", V=V, temperature=T, **extra)
+    got = gu.run(w, two_streams=(seed == 1))
+    assert got["status"] == 0, got["status"]
+    gu.check_tree_prep(w, got)
+    gu.check_attention(w, got)
+    gu.check_verify(w, got)
+    gu.check_node_stats(w, got, range(w.N))
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_chains_bf16(seed):
+    _say("chains", seed)
+    w = gen.tree_batch(seed, B=3, prefix_len=[5, 0, 130], tree="chain", n_nodes=[1, 100, 300],
+                       Hq=32, Hkv=8, D=128, dtype="bf16", V=1024, temperature=1.0)
+    got = gu.run(w, max_path=512)
+    assert got["status"] == 0, got["status"]
+    gu.check_tree_prep(w, got)
+    gu.check_attention(w, got)
+    gu.check_verify(w, got)
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_split_kv_long_prefix(seed):
+    _say("split", seed)
+    w = gen.tree_batch(seed, B=2, prefix_len=[20000, 3000], tree="random", n_nodes=[48, 9],
+                       Hq=8, Hkv=2, D=128, dtype="bf16")
+    got = gu.run(w, with_verify=False)
+    assert got["status"] == 0, got["status"]
+    gu.check_attention(w, got)
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_presto_small(seed):
+    _say("presto", seed)
+    w = gen.presto_batch(seed, T=96, n_pf=12, Hq=8, Hkv=2, D=128, dtype="bf16", alpha=4.0,
+                         max_transitions=6)
+    got = gu.run(w)
+    assert got["status"] == 0, got["status"]
+    gu.check_attention(w, got)
+    gu.check_presto(w, got)

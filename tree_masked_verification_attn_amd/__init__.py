@@ -1,0 +1,249 @@
+"""Python binding of libtav, the tree-masked scoring pass for MI355X (gfx950).
+
+Argument marshalling only: every function here packs torch tensors (device
+memory) and host integers into the C structs of ``include/tav.h`` and calls the
+library entry point of the same name.  All computation happens in the HIP
+kernels; if ``libtav.so`` is missing the import of any entry point raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtav.so")
+
+TAV_F32, TAV_BF16 = 0, 1
+STATUS_NAMES = {0: "TAV_OK", 1: "TAV_ERR_NULL_POINTER", 2: "TAV_ERR_BAD_SHAPE", 3: "TAV_ERR_UNSUPPORTED",
+                4: "TAV_ERR_WORKSPACE", 5: "TAV_ERR_HIP", 6: "TAV_ERR_INVALID_ARGUMENT"}
+DEVICE_BITS = {
+    0: "BAD_PARENT", 1: "TREE_TOO_LARGE", 2: "BAD_BLOCK", 3: "BAD_TOKEN", 4: "DUP_SIBLING_TOKEN",
+    5: "MULTI_SAMPLED", 6: "NO_DRAFT", 7: "ZERO_DRAFT_MASS", 8: "NONFINITE_LOGITS",
+    9: "EMPTY_RESIDUAL", 10: "PATH_OVERFLOW", 11: "TOO_MANY_CHILDREN", 12: "PRESTO_BAD_TREE",
+    13: "PLAN_MISMATCH", 14: "BAD_TEMPERATURE",
+}
+ENTRY_POINTS = ("tav_workspace_size", "tav_tree_prep", "tav_tree_attention", "tav_tree_verify",
+                "tav_presto_accept", "tav_tree_attn_verify", "tav_read_status", "tav_status_string",
+                "tav_last_error")
+
+_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_f32 = ctypes.c_float
+
+
+class tav_problem(ctypes.Structure):
+    _fields_ = [("num_seqs", _i32), ("node_offsets_host", _p), ("node_offsets", _p),
+                ("prefix_len_host", _p), ("prefix_len", _p), ("num_q_heads", _i32),
+                ("num_kv_heads", _i32), ("head_dim", _i32), ("dtype", _i32), ("sm_scale", _f32),
+                ("block_size", _i32), ("num_blocks", _i32), ("max_blocks_per_seq", _i32),
+                ("vocab", _i32)]
+
+
+class tav_tree(ctypes.Structure):
+    _fields_ = [("parent", _p), ("token", _p), ("sampled", _p)]
+
+
+class tav_tree_out(ctypes.Structure):
+    _fields_ = [("depth", _p), ("position", _p), ("mask", _p), ("is_chain", _p)]
+
+
+class tav_attn_io(ctypes.Structure):
+    _fields_ = [("q", _p), ("k_node", _p), ("v_node", _p), ("k_cache", _p), ("v_cache", _p),
+                ("block_table", _p), ("out", _p), ("lse", _p)]
+
+
+class tav_verify_io(ctypes.Structure):
+    _fields_ = [("logits", _p), ("temperature", _p), ("draft", _p), ("num_draft_rows", _i32),
+                ("draft_row", _p), ("uniforms", _p), ("node_status", _p), ("path", _p),
+                ("max_path", _i32), ("path_len", _p), ("bonus_token", _p), ("node_stats", _p),
+                ("node_term_token", _p)]
+
+
+class tav_presto_io(ctypes.Structure):
+    _fields_ = [("T", _i32), ("alpha", _f32), ("root_lp0", _p), ("root_lq", _p),
+                ("num_requests", _i32), ("cut", _p), ("suffix_off", _p), ("lp0", _p), ("lq", _p),
+                ("num_nodes", _i32), ("pf_parent", _p), ("pf_is_accept", _p), ("pf_request", _p),
+                ("u", _p), ("max_transitions", _i32), ("log_accept", _p), ("pf_path", _p),
+                ("pf_path_len", _p)]
+
+
+class TavError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libtav.so (raises FileNotFoundError if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise FileNotFoundError(f"{LIB_PATH} is missing: build it with "
+                                    "tree_masked_verification_attn_amd/build.py")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name in ENTRY_POINTS:
+            getattr(lib, name)
+        lib.tav_workspace_size.argtypes = [ctypes.POINTER(tav_problem), ctypes.POINTER(tav_presto_io),
+                                           ctypes.POINTER(ctypes.c_size_t)]
+        lib.tav_tree_prep.argtypes = [ctypes.POINTER(tav_problem), ctypes.POINTER(tav_tree),
+                                      ctypes.POINTER(tav_tree_out), _p, ctypes.c_size_t, _p]
+        lib.tav_tree_attention.argtypes = [ctypes.POINTER(tav_problem), ctypes.POINTER(tav_tree),
+                                           ctypes.POINTER(tav_attn_io), _p, ctypes.c_size_t, _p]
+        lib.tav_tree_verify.argtypes = [ctypes.POINTER(tav_problem), ctypes.POINTER(tav_tree),
+                                        ctypes.POINTER(tav_verify_io), _p, ctypes.c_size_t, _p]
+        lib.tav_presto_accept.argtypes = [ctypes.POINTER(tav_presto_io), _p, ctypes.c_size_t, _p]
+        lib.tav_tree_attn_verify.argtypes = [
+            ctypes.POINTER(tav_problem), ctypes.POINTER(tav_tree), ctypes.POINTER(tav_attn_io),
+            ctypes.POINTER(tav_verify_io), ctypes.POINTER(tav_presto_io), ctypes.POINTER(tav_tree_out),
+            _p, ctypes.c_size_t, _p, _p]
+        lib.tav_read_status.argtypes = [_p, _p, ctypes.POINTER(ctypes.c_uint32)]
+        lib.tav_status_string.argtypes = [ctypes.c_int]
+        lib.tav_status_string.restype = ctypes.c_char_p
+        lib.tav_last_error.restype = ctypes.c_char_p
+        for name in ENTRY_POINTS[:7]:
+            getattr(lib, name).restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libtav must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _check(status: int):
+    if status != 0:
+        raise TavError(status, load().tav_last_error().decode())
+
+
+def _stream(s) -> Optional[ctypes.c_void_p]:
+    if s is None:
+        s = torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+@dataclass
+class Problem:
+    """Host description of a batch; node_offsets / prefix_len are int32 CPU tensors,
+    and their device copies are made once here."""
+    node_offsets: torch.Tensor
+    prefix_len: torch.Tensor
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    dtype: int
+    block_size: int
+    num_blocks: int
+    max_blocks_per_seq: int
+    vocab: int = 0
+    sm_scale: float = 0.0
+    device: str = "cuda"
+
+    def __post_init__(self):
+        self.node_offsets = self.node_offsets.to("cpu", torch.int32).contiguous()
+        self.prefix_len = self.prefix_len.to("cpu", torch.int32).contiguous()
+        self.node_offsets_dev = self.node_offsets.to(self.device)
+        self.prefix_len_dev = self.prefix_len.to(self.device)
+
+    def struct(self) -> tav_problem:
+        return tav_problem(
+            num_seqs=self.node_offsets.numel() - 1,
+            node_offsets_host=_ptr(self.node_offsets), node_offsets=_ptr(self.node_offsets_dev),
+            prefix_len_host=_ptr(self.prefix_len), prefix_len=_ptr(self.prefix_len_dev),
+            num_q_heads=self.num_q_heads, num_kv_heads=self.num_kv_heads, head_dim=self.head_dim,
+            dtype=self.dtype, sm_scale=self.sm_scale, block_size=self.block_size,
+            num_blocks=self.num_blocks, max_blocks_per_seq=self.max_blocks_per_seq, vocab=self.vocab)
+
+
+def _struct_of(cls, obj, **scalars):
+    """Build a ctypes struct from an object whose attributes are tensors / ints."""
+    if obj is None:
+        return None
+    vals = {}
+    for name, typ in cls._fields_:
+        if name in scalars:
+            vals[name] = scalars[name]
+            continue
+        v = getattr(obj, name, None)
+        vals[name] = _ptr(v) if (typ is _p and isinstance(v, torch.Tensor)) else (v if v is not None else (None if typ is _p else 0))
+    return cls(**vals)
+
+
+def _ref(s):
+    return ctypes.byref(s) if s is not None else None
+
+
+def tav_workspace_size(prob: Problem, presto=None) -> int:
+    n = ctypes.c_size_t(0)
+    ps = prob.struct()
+    pr = _struct_of(tav_presto_io, presto)
+    _check(load().tav_workspace_size(ctypes.byref(ps), _ref(pr), ctypes.byref(n)))
+    return n.value
+
+
+def tav_tree_prep(prob: Problem, tree, tree_out, workspace: torch.Tensor, stream=None):
+    ps, ts, to = prob.struct(), _struct_of(tav_tree, tree), _struct_of(tav_tree_out, tree_out)
+    _check(load().tav_tree_prep(ctypes.byref(ps), ctypes.byref(ts), _ref(to), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def tav_tree_attention(prob: Problem, tree, attn, workspace: torch.Tensor, stream=None):
+    ps, ts, ai = prob.struct(), _struct_of(tav_tree, tree), _struct_of(tav_attn_io, attn)
+    _check(load().tav_tree_attention(ctypes.byref(ps), ctypes.byref(ts), ctypes.byref(ai), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def tav_tree_verify(prob: Problem, tree, verify, workspace: torch.Tensor, stream=None):
+    ps, ts, vi = prob.struct(), _struct_of(tav_tree, tree), _struct_of(tav_verify_io, verify)
+    _check(load().tav_tree_verify(ctypes.byref(ps), ctypes.byref(ts), ctypes.byref(vi), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def tav_presto_accept(presto, workspace: torch.Tensor, stream=None):
+    pr = _struct_of(tav_presto_io, presto)
+    _check(load().tav_presto_accept(ctypes.byref(pr), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def tav_tree_attn_verify(prob: Problem, tree, attn, verify, presto, tree_out, workspace: torch.Tensor,
+                         attn_stream=None, verify_stream=None):
+    ps = prob.struct()
+    ts = _struct_of(tav_tree, tree)
+    ai = _struct_of(tav_attn_io, attn)
+    vi = _struct_of(tav_verify_io, verify)
+    pr = _struct_of(tav_presto_io, presto)
+    to = _struct_of(tav_tree_out, tree_out)
+    sa = _stream(attn_stream)
+    sv = _stream(verify_stream) if verify_stream is not None else sa
+    _check(load().tav_tree_attn_verify(ctypes.byref(ps), ctypes.byref(ts), ctypes.byref(ai), _ref(vi),
+                                       _ref(pr), _ref(to), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), sa, sv))
+
+
+def tav_read_status(workspace: torch.Tensor, stream=None) -> int:
+    bits = ctypes.c_uint32(0)
+    _check(load().tav_read_status(_ptr(workspace), _stream(stream), ctypes.byref(bits)))
+    return bits.value
+
+
+def device_status_names(bits: int):
+    return [name for i, name in DEVICE_BITS.items() if bits >> i & 1]
+
+
+def tav_status_string(status: int) -> str:
+    return load().tav_status_string(status).decode()
+
+
+def tav_last_error() -> str:
+    return load().tav_last_error().decode()

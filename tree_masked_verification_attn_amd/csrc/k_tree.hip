@@ -1,0 +1,187 @@
+// Tree preparation and the attention work plan.
+//
+// Visibility follows Progressive Tree Drafting, Section 3.1 ("Tree
+// Construction"): pi(v) = {v} U pi(P(v)), and a node's position is fixed by
+// |pi(v)|; behind a cached prefix of L rows, position = L + depth(v).
+#include "tav_internal.h"
+
+namespace tav {
+namespace {
+
+__global__ void clear_status_kernel(uint32_t* status) {
+  if (threadIdx.x == 0) status[0] = 0u;
+}
+
+// Exclusive scan of one int per thread over a 1024-thread block; also returns the total.
+__device__ int block_exclusive_scan(int v, int* lds, int* total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) lds[wid] = x;
+  __syncthreads();
+  if (wid == 0) {
+    int s = lane < nw ? lds[lane] : 0;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      int y = __shfl_up(s, d, 64);
+      if (lane >= d) s += y;
+    }
+    if (lane < nw) lds[lane] = s;
+  }
+  __syncthreads();
+  int excl = (wid > 0 ? lds[wid - 1] : 0) + x - v;
+  *total = lds[nw - 1];
+  __syncthreads();
+  return excl;
+}
+
+// One 1024-thread block: seq_rb_off[B+1] (row blocks per sequence), rb_seq
+// and item_off[total_rb+1] (work items per row block), identical to the host plan.
+__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* node_offsets,
+                                                     const int32_t* prefix_len, int B, int NB,
+                                                     int tiles_per_split, int total_rb_host,
+                                                     int total_items_host, int32_t* seq_rb_off,
+                                                     int32_t* rb_seq, int32_t* item_off,
+                                                     uint32_t* status) {
+  __shared__ int lds[16];
+  int carry = 0;
+  for (int base = 0; base < B; base += 1024) {
+    int b = base + threadIdx.x;
+    int cnt = 0;
+    if (b < B) cnt = (node_offsets[b + 1] - node_offsets[b] + NB - 1) / NB;
+    int tot;
+    int ex = block_exclusive_scan(cnt, lds, &tot);
+    if (b < B) seq_rb_off[b] = carry + ex;
+    carry += tot;
+  }
+  if (threadIdx.x == 0) seq_rb_off[B] = carry;
+  const int total_rb = carry;
+  if (total_rb != total_rb_host) {
+    if (threadIdx.x == 0) atomicOr(status, (uint32_t)TAV_DEV_PLAN_MISMATCH);
+    return;
+  }
+  __syncthreads();
+  int icarry = 0;
+  for (int base = 0; base < total_rb; base += 1024) {
+    int r = base + threadIdx.x;
+    int cnt = 0;
+    if (r < total_rb) {
+      int lo = 0, hi = B;  // largest b with seq_rb_off[b] <= r
+      while (hi - lo > 1) {
+        int mid = (lo + hi) >> 1;
+        if (seq_rb_off[mid] <= r) lo = mid; else hi = mid;
+      }
+      int b = lo;
+      int rb = r - seq_rb_off[b];
+      int n = node_offsets[b + 1] - node_offsets[b];
+      cnt = ceil_div(rb_tiles(prefix_len[b], n, rb, NB), tiles_per_split);
+      rb_seq[r] = b;
+    }
+    int tot;
+    int ex = block_exclusive_scan(cnt, lds, &tot);
+    if (r < total_rb) item_off[r] = icarry + ex;
+    icarry += tot;
+  }
+  if (threadIdx.x == 0) {
+    item_off[total_rb] = icarry;
+    if (icarry != total_items_host) atomicOr(status, (uint32_t)TAV_DEV_PLAN_MISMATCH);
+  }
+}
+
+// One block per sequence: validate parents, detect chains, and build depth,
+// position and the 256-bit ancestor masks of non-chain trees.
+__global__ __launch_bounds__(256) void prep_kernel(const int32_t* node_offsets,
+                                                    const int32_t* prefix_len,
+                                                    const int32_t* parent, uint8_t* chain_ws,
+                                                    uint64_t* mask_ws, int32_t* depth_out,
+                                                    int32_t* pos_out, uint64_t* mask_out,
+                                                    uint8_t* chain_out, uint32_t* status) {
+  __shared__ int par_s[kMaxTreeNodes];
+  const int b = blockIdx.x;
+  const int s0 = node_offsets[b];
+  const int n = node_offsets[b + 1] - s0;
+  const int L = prefix_len[b];
+  int bad = 0, not_chain = 0;
+  for (int v = threadIdx.x; v < n; v += blockDim.x) {
+    int p = parent[s0 + v];
+    if (v == 0 ? p != -1 : (p < 0 || p >= v)) bad = 1;
+    if (v > 0 && p != v - 1) not_chain = 1;
+  }
+  bad = __syncthreads_or(bad);
+  not_chain = __syncthreads_or(not_chain);
+  if (bad) {
+    if (threadIdx.x == 0) atomicOr(status, (uint32_t)TAV_DEV_BAD_PARENT);
+    if (threadIdx.x == 0) chain_ws[b] = 0;
+    return;
+  }
+  if (threadIdx.x == 0) {
+    chain_ws[b] = not_chain ? 0 : 1;
+    if (chain_out) chain_out[b] = not_chain ? 0 : 1;
+  }
+  if (!not_chain) {
+    for (int v = threadIdx.x; v < n; v += blockDim.x) {
+      if (depth_out) depth_out[s0 + v] = v;
+      if (pos_out) pos_out[s0 + v] = L + v;
+      if (mask_out) {
+#pragma unroll
+        for (int w = 0; w < kMaskWords; ++w) mask_out[(size_t)(s0 + v) * kMaskWords + w] = 0ull;
+      }
+    }
+    return;
+  }
+  if (n > kMaxTreeNodes) {
+    if (threadIdx.x == 0) atomicOr(status, (uint32_t)TAV_DEV_TREE_TOO_LARGE);
+    return;
+  }
+  for (int v = threadIdx.x; v < n; v += blockDim.x) par_s[v] = parent[s0 + v];
+  __syncthreads();
+  for (int v = threadIdx.x; v < n; v += blockDim.x) {
+    uint64_t w[kMaskWords] = {0ull, 0ull, 0ull, 0ull};
+    int x = v, d = 0;
+    // walk to the root; parents were validated to be earlier nodes, so this ends
+    for (int step = 0; step < kMaxTreeNodes; ++step) {
+      w[x >> 6] |= 1ull << (x & 63);
+      if (x == 0) break;
+      x = par_s[x];
+      ++d;
+    }
+#pragma unroll
+    for (int k = 0; k < kMaskWords; ++k) {
+      mask_ws[(size_t)(s0 + v) * kMaskWords + k] = w[k];
+      if (mask_out) mask_out[(size_t)(s0 + v) * kMaskWords + k] = w[k];
+    }
+    if (depth_out) depth_out[s0 + v] = d;
+    if (pos_out) pos_out[s0 + v] = L + d;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_clear_status(uint32_t* status, hipStream_t s) {
+  clear_status_kernel<<<1, 64, 0, s>>>(status);
+  return hipGetLastError();
+}
+
+hipError_t launch_plan(const Plan& p, const int32_t* node_offsets, const int32_t* prefix_len,
+                       int32_t* seq_rb_off, int32_t* rb_seq, int32_t* item_off, uint32_t* status,
+                       hipStream_t s) {
+  plan_kernel<<<1, 1024, 0, s>>>(node_offsets, prefix_len, p.B, p.NB, p.tiles_per_split,
+                                 p.total_rb, p.total_items, seq_rb_off, rb_seq, item_off, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep(const Plan& p, const int32_t* node_offsets, const int32_t* prefix_len,
+                       const int32_t* parent, uint8_t* chain_ws, uint64_t* mask_ws,
+                       const tav_tree_out* out, uint32_t* status, hipStream_t s) {
+  prep_kernel<<<p.B, 256, 0, s>>>(node_offsets, prefix_len, parent, chain_ws, mask_ws,
+                                  out ? out->depth : nullptr, out ? out->position : nullptr,
+                                  out ? out->mask : nullptr, out ? out->is_chain : nullptr, status);
+  return hipGetLastError();
+}
+
+}  // namespace tav

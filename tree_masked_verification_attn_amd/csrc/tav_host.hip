@@ -1,0 +1,455 @@
+// Host side of libtav: argument validation, the work plan, the workspace
+// layout, kernel launches and error reporting.  Nothing here allocates device
+// memory; every call only enqueues work on the caller's stream(s).
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "tav_internal.h"
+
+namespace tav {
+namespace {
+
+thread_local std::string g_last_error;
+
+tav_status fail(tav_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+tav_status fail(tav_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+tav_status ok() {
+  g_last_error.clear();
+  return TAV_OK;
+}
+
+#define TAV_HIP(call)                                                                   \
+  do {                                                                                  \
+    hipError_t e_ = (call);                                                             \
+    if (e_ != hipSuccess) return fail(TAV_ERR_HIP, "%s: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+constexpr int kTargetWorkgroups = 512;  // about two workgroups per MI355X compute unit
+constexpr int kMinTilesPerSplit = 8;    // at least 512 keys per split
+
+int log2_exact(int x) {
+  int l = 0;
+  while ((1 << l) < x) ++l;
+  return (1 << l) == x ? l : -1;
+}
+
+tav_status check_problem(const tav_problem* p) {
+  if (!p) return fail(TAV_ERR_NULL_POINTER, "problem is NULL");
+  if (p->num_seqs < 1) return fail(TAV_ERR_BAD_SHAPE, "num_seqs must be >= 1 (got %d)", p->num_seqs);
+  if (!p->node_offsets_host || !p->node_offsets || !p->prefix_len_host || !p->prefix_len)
+    return fail(TAV_ERR_NULL_POINTER, "node_offsets / prefix_len (host and device copies) are required");
+  const int32_t* off = p->node_offsets_host;
+  if (off[0] != 0) return fail(TAV_ERR_BAD_SHAPE, "node_offsets[0] must be 0");
+  for (int b = 0; b < p->num_seqs; ++b)
+    if (off[b + 1] <= off[b])
+      return fail(TAV_ERR_BAD_SHAPE, "sequence %d has no nodes (node_offsets must increase)", b);
+  if (p->num_q_heads < 1 || p->num_kv_heads < 1 || p->num_q_heads % p->num_kv_heads)
+    return fail(TAV_ERR_BAD_SHAPE, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                p->num_q_heads, p->num_kv_heads);
+  const int G = p->num_q_heads / p->num_kv_heads;
+  if (log2_exact(G) < 0 || G > 16)
+    return fail(TAV_ERR_UNSUPPORTED, "query heads per KV head must be 1, 2, 4, 8 or 16 (got %d)", G);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(TAV_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", p->head_dim);
+  if (p->dtype != TAV_F32 && p->dtype != TAV_BF16)
+    return fail(TAV_ERR_UNSUPPORTED, "dtype must be TAV_F32 or TAV_BF16 (got %d)", p->dtype);
+  if (!(p->sm_scale >= 0.f) || !isfinite(p->sm_scale))
+    return fail(TAV_ERR_INVALID_ARGUMENT, "sm_scale must be finite and >= 0");
+  if (p->block_size != 8 && p->block_size != 16 && p->block_size != 32 && p->block_size != 64)
+    return fail(TAV_ERR_UNSUPPORTED, "block_size must be 8, 16, 32 or 64 (got %d)", p->block_size);
+  if (p->max_blocks_per_seq < 1 || p->num_blocks < 0)
+    return fail(TAV_ERR_BAD_SHAPE, "max_blocks_per_seq must be >= 1 and num_blocks >= 0");
+  for (int b = 0; b < p->num_seqs; ++b) {
+    const int L = p->prefix_len_host[b];
+    if (L < 0 || (int64_t)L > (int64_t)p->max_blocks_per_seq * p->block_size)
+      return fail(TAV_ERR_BAD_SHAPE, "prefix_len[%d] = %d outside [0, max_blocks_per_seq * block_size]", b, L);
+  }
+  if (p->vocab < 0) return fail(TAV_ERR_BAD_SHAPE, "vocab must be >= 0");
+  return TAV_OK;
+}
+
+tav_status check_presto(const tav_presto_io* io) {
+  if (!io->root_lp0 || !io->root_lq || !io->cut || !io->suffix_off || !io->lp0 || !io->lq ||
+      !io->pf_parent || !io->pf_is_accept || !io->pf_request || !io->u || !io->log_accept ||
+      !io->pf_path || !io->pf_path_len)
+    return fail(TAV_ERR_NULL_POINTER, "a PreSTO array is NULL");
+  if (io->T < 1 || io->num_requests < 1 || io->num_nodes < 1 || io->max_transitions < 0)
+    return fail(TAV_ERR_BAD_SHAPE, "PreSTO sizes: T=%d requests=%d nodes=%d max_transitions=%d", io->T,
+                io->num_requests, io->num_nodes, io->max_transitions);
+  if (!isfinite(io->alpha)) return fail(TAV_ERR_INVALID_ARGUMENT, "alpha must be finite");
+  return TAV_OK;
+}
+
+// The plan and workspace layout; identical integer formulas run in plan_kernel.
+tav_status make_plan(const tav_problem* p, const tav_presto_io* pr, Plan* out) {
+  tav_status st = check_problem(p);
+  if (st != TAV_OK) return st;
+  if (pr) {
+    st = check_presto(pr);
+    if (st != TAV_OK) return st;
+  }
+  Plan P;
+  P.B = p->num_seqs;
+  P.N = p->node_offsets_host[P.B];
+  P.Hq = p->num_q_heads;
+  P.Hkv = p->num_kv_heads;
+  P.D = p->head_dim;
+  P.G = P.Hq / P.Hkv;
+  P.log2G = log2_exact(P.G);
+  P.NB = kRowsPerWG >> P.log2G;
+  int64_t tiles = 0;
+  for (int b = 0; b < P.B; ++b) {
+    const int n = p->node_offsets_host[b + 1] - p->node_offsets_host[b];
+    const int nrb = ceil_div(n, P.NB);
+    P.total_rb += nrb;
+    for (int rb = 0; rb < nrb; ++rb) tiles += rb_tiles(p->prefix_len_host[b], n, rb, P.NB);
+  }
+  tiles *= P.Hkv;
+  int64_t tps = (tiles + kTargetWorkgroups - 1) / kTargetWorkgroups;
+  P.tiles_per_split = (int)(tps < kMinTilesPerSplit ? kMinTilesPerSplit : tps);
+  if (p->dtype == TAV_BF16) {
+    for (int b = 0; b < P.B; ++b) {
+      const int n = p->node_offsets_host[b + 1] - p->node_offsets_host[b];
+      for (int rb = 0; rb < ceil_div(n, P.NB); ++rb) {
+        const int c = ceil_div(rb_tiles(p->prefix_len_host[b], n, rb, P.NB), P.tiles_per_split);
+        P.total_items += c;
+        if (c > 1) P.any_split = true;
+      }
+    }
+  }
+  size_t o = 0;
+  P.off_status = o; o = align_up(o + 256);
+  P.off_chain = o; o = align_up(o + (size_t)P.B);
+  P.off_mask = o; o = align_up(o + (size_t)P.N * kMaskWords * 8);
+  P.off_seq_rb = o; o = align_up(o + (size_t)(P.B + 1) * 4);
+  P.off_rb_seq = o; o = align_up(o + (size_t)P.total_rb * 4);
+  P.off_item_off = o; o = align_up(o + (size_t)(P.total_rb + 1) * 4);
+  P.off_part_o = o;
+  if (P.any_split) o = align_up(o + (size_t)P.total_items * P.Hkv * kRowsPerWG * P.D * 4);
+  P.off_part_lse = o;
+  if (P.any_split) o = align_up(o + (size_t)P.total_items * P.Hkv * kRowsPerWG * 4);
+  P.off_stats = o; o = align_up(o + (size_t)P.N * 3 * 4);
+  P.off_term = o; o = align_up(o + (size_t)P.N * 4);
+  P.off_presto = o; o = align_up(o + (size_t)(pr ? pr->num_requests : 0) * 8);
+  P.total = o;
+  *out = P;
+  return TAV_OK;
+}
+
+template <typename T>
+T* ws_at(void* ws, size_t off) {
+  return (T*)((char*)ws + off);
+}
+
+tav_status check_ws(const Plan& P, void* ws, size_t bytes) {
+  if (!ws) return fail(TAV_ERR_WORKSPACE, "workspace is NULL");
+  if ((uintptr_t)ws & 255u) return fail(TAV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (bytes < P.total)
+    return fail(TAV_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", bytes, P.total);
+  return TAV_OK;
+}
+
+tav_status check_tree(const tav_tree* t, bool verify) {
+  if (!t || !t->parent) return fail(TAV_ERR_NULL_POINTER, "tree / tree.parent is NULL");
+  if (verify && (!t->token || !t->sampled))
+    return fail(TAV_ERR_NULL_POINTER, "verification needs tree.token and tree.sampled");
+  return TAV_OK;
+}
+
+tav_status check_attn(const tav_problem* p, const tav_attn_io* io) {
+  if (!io || !io->q || !io->k_node || !io->v_node || !io->out)
+    return fail(TAV_ERR_NULL_POINTER, "attention q / k_node / v_node / out is NULL");
+  bool any_prefix = false;
+  for (int b = 0; b < p->num_seqs; ++b) any_prefix |= p->prefix_len_host[b] > 0;
+  if (any_prefix && (!io->k_cache || !io->v_cache || !io->block_table))
+    return fail(TAV_ERR_NULL_POINTER, "k_cache / v_cache / block_table are required when a prefix is present");
+  if (any_prefix && p->num_blocks < 1) return fail(TAV_ERR_BAD_SHAPE, "num_blocks must be >= 1");
+  if (!aligned16(io->q) || !aligned16(io->k_node) || !aligned16(io->v_node) || !aligned16(io->out) ||
+      !aligned16(io->k_cache) || !aligned16(io->v_cache))
+    return fail(TAV_ERR_INVALID_ARGUMENT, "attention arrays must be 16-byte aligned");
+  return TAV_OK;
+}
+
+tav_status check_verify(const tav_problem* p, const tav_verify_io* io) {
+  if (!io || !io->logits || !io->temperature || !io->draft_row || !io->uniforms || !io->node_status ||
+      !io->path || !io->path_len || !io->bonus_token)
+    return fail(TAV_ERR_NULL_POINTER, "a verification array is NULL");
+  if (io->num_draft_rows < 0) return fail(TAV_ERR_BAD_SHAPE, "num_draft_rows must be >= 0");
+  if (io->num_draft_rows > 0 && !io->draft) return fail(TAV_ERR_NULL_POINTER, "draft is NULL");
+  if (io->max_path < 1) return fail(TAV_ERR_BAD_SHAPE, "max_path must be >= 1");
+  if (p->vocab < 1) return fail(TAV_ERR_BAD_SHAPE, "vocab must be >= 1 for verification");
+  const int epu = p->dtype == TAV_BF16 ? 8 : 4;
+  const int64_t cap = (int64_t)kVocabThreads * kVocabSlots * epu;
+  if (p->vocab % epu)
+    return fail(TAV_ERR_UNSUPPORTED, "vocab must be a multiple of %d for this logits dtype (got %d)", epu, p->vocab);
+  if (p->vocab > cap)
+    return fail(TAV_ERR_UNSUPPORTED, "vocab %d exceeds the %lld tokens one workgroup holds for this dtype",
+                p->vocab, (long long)cap);
+  if (!aligned16(io->logits) || !aligned16(io->draft))
+    return fail(TAV_ERR_INVALID_ARGUMENT, "logits and draft must be 16-byte aligned");
+  return TAV_OK;
+}
+
+AttnArgs attn_args(const tav_problem* p, const Plan& P, const tav_attn_io* io, void* ws) {
+  AttnArgs a;
+  a.q = io->q; a.k_node = io->k_node; a.v_node = io->v_node;
+  a.k_cache = io->k_cache; a.v_cache = io->v_cache; a.block_table = io->block_table;
+  a.out = io->out; a.lse = io->lse;
+  a.node_offsets = p->node_offsets; a.prefix_len = p->prefix_len;
+  a.is_chain = ws_at<uint8_t>(ws, P.off_chain);
+  a.mask = ws_at<uint64_t>(ws, P.off_mask);
+  a.seq_rb_off = ws_at<int32_t>(ws, P.off_seq_rb);
+  a.rb_seq = ws_at<int32_t>(ws, P.off_rb_seq);
+  a.item_off = ws_at<int32_t>(ws, P.off_item_off);
+  a.part_o = ws_at<float>(ws, P.off_part_o);
+  a.part_lse = ws_at<float>(ws, P.off_part_lse);
+  a.status = ws_at<uint32_t>(ws, P.off_status);
+  a.B = P.B; a.Hq = P.Hq; a.Hkv = P.Hkv; a.total_rb = P.total_rb; a.total_items = P.total_items;
+  a.tiles_per_split = P.tiles_per_split; a.block_size = p->block_size; a.num_blocks = p->num_blocks;
+  a.max_blocks = p->max_blocks_per_seq;
+  a.scale = p->sm_scale > 0.f ? p->sm_scale : 1.f / sqrtf((float)p->head_dim);
+  return a;
+}
+
+tav_status enqueue_prep(const tav_problem* p, const Plan& P, const tav_tree* t,
+                        const tav_tree_out* out, void* ws, hipStream_t s) {
+  uint32_t* status = ws_at<uint32_t>(ws, P.off_status);
+  TAV_HIP(launch_prep(P, p->node_offsets, p->prefix_len, t->parent, ws_at<uint8_t>(ws, P.off_chain),
+                      ws_at<uint64_t>(ws, P.off_mask), out, status, s));
+  return TAV_OK;
+}
+
+tav_status enqueue_attention(const tav_problem* p, const Plan& P, const tav_attn_io* io, void* ws,
+                             hipStream_t s) {
+  const AttnArgs a = attn_args(p, P, io, ws);
+  if (p->dtype == TAV_BF16) {
+    TAV_HIP(launch_plan(P, p->node_offsets, p->prefix_len, const_cast<int32_t*>(a.seq_rb_off),
+                        const_cast<int32_t*>(a.rb_seq), const_cast<int32_t*>(a.item_off), a.status, s));
+    TAV_HIP(launch_attn_bf16(P, a, s));
+    TAV_HIP(launch_merge(P, a, true, s));
+  } else {
+    TAV_HIP(launch_attn_f32(P, a, s));
+  }
+  return TAV_OK;
+}
+
+tav_status enqueue_verify(const tav_problem* p, const Plan& P, const tav_tree* t,
+                          const tav_verify_io* io, void* ws, hipStream_t s) {
+  uint32_t* status = ws_at<uint32_t>(ws, P.off_status);
+  float* stats = io->node_stats ? io->node_stats : ws_at<float>(ws, P.off_stats);
+  int32_t* term = io->node_term_token ? io->node_term_token : ws_at<int32_t>(ws, P.off_term);
+  VocabArgs va;
+  va.logits = io->logits; va.temperature = io->temperature; va.draft = io->draft;
+  va.draft_row = io->draft_row; va.node_offsets = p->node_offsets; va.parent = t->parent;
+  va.token = t->token; va.sampled = t->sampled; va.uniforms = io->uniforms;
+  va.stats = stats; va.term_token = term; va.status = status;
+  va.B = P.B; va.N = P.N; va.V = p->vocab; va.R = io->num_draft_rows;
+  TAV_HIP(launch_vocab(va, p->dtype == TAV_BF16, s));
+  WalkArgs wa;
+  wa.logits = io->logits; wa.temperature = io->temperature; wa.draft = io->draft;
+  wa.draft_row = io->draft_row; wa.node_offsets = p->node_offsets; wa.parent = t->parent;
+  wa.token = t->token; wa.sampled = t->sampled; wa.uniforms = io->uniforms;
+  wa.stats = stats; wa.term_token = term; wa.node_status = io->node_status; wa.path = io->path;
+  wa.path_len = io->path_len; wa.bonus = io->bonus_token; wa.status = status;
+  wa.B = P.B; wa.V = p->vocab; wa.R = io->num_draft_rows; wa.max_path = io->max_path;
+  wa.logits_bf16 = p->dtype == TAV_BF16;
+  TAV_HIP(launch_walk(wa, s));
+  return TAV_OK;
+}
+
+tav_status enqueue_presto(const Plan& P, const tav_presto_io* io, void* ws, hipStream_t s) {
+  PrestoArgs pa;
+  pa.T = io->T; pa.R = io->num_requests; pa.M = io->num_nodes; pa.max_transitions = io->max_transitions;
+  pa.alpha = (double)io->alpha;
+  pa.root_lp0 = io->root_lp0; pa.root_lq = io->root_lq; pa.cut = io->cut; pa.suffix_off = io->suffix_off;
+  pa.lp0 = io->lp0; pa.lq = io->lq; pa.pf_parent = io->pf_parent; pa.pf_is_accept = io->pf_is_accept;
+  pa.pf_request = io->pf_request; pa.u = io->u; pa.log_accept = io->log_accept;
+  pa.log_accept64 = ws_at<double>(ws, P.off_presto);
+  pa.pf_path = io->pf_path; pa.pf_path_len = io->pf_path_len;
+  pa.status = ws_at<uint32_t>(ws, P.off_status);
+  TAV_HIP(launch_presto(pa, s));
+  return TAV_OK;
+}
+
+struct StreamEvents {
+  int device = -1;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+thread_local StreamEvents g_events;
+
+tav_status get_events(hipEvent_t* fork, hipEvent_t* join) {
+  int dev = 0;
+  TAV_HIP(hipGetDevice(&dev));
+  if (g_events.device != dev) {
+    if (g_events.fork) (void)hipEventDestroy(g_events.fork);
+    if (g_events.join) (void)hipEventDestroy(g_events.join);
+    g_events.fork = g_events.join = nullptr;
+    TAV_HIP(hipEventCreateWithFlags(&g_events.fork, hipEventDisableTiming));
+    TAV_HIP(hipEventCreateWithFlags(&g_events.join, hipEventDisableTiming));
+    g_events.device = dev;
+  }
+  *fork = g_events.fork;
+  *join = g_events.join;
+  return TAV_OK;
+}
+
+}  // namespace
+}  // namespace tav
+
+using namespace tav;
+
+extern "C" {
+
+tav_status tav_workspace_size(const tav_problem* prob, const tav_presto_io* presto, size_t* bytes) {
+  if (!bytes) return fail(TAV_ERR_NULL_POINTER, "bytes is NULL");
+  Plan P;
+  tav_status st = make_plan(prob, presto, &P);
+  if (st != TAV_OK) return st;
+  *bytes = P.total;
+  return ok();
+}
+
+tav_status tav_tree_prep(const tav_problem* prob, const tav_tree* tree, const tav_tree_out* out,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  Plan P;
+  tav_status st = make_plan(prob, nullptr, &P);
+  if (st == TAV_OK) st = check_ws(P, workspace, workspace_bytes);
+  if (st == TAV_OK) st = check_tree(tree, false);
+  if (st != TAV_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  TAV_HIP(launch_clear_status(ws_at<uint32_t>(workspace, P.off_status), s));
+  st = enqueue_prep(prob, P, tree, out, workspace, s);
+  return st == TAV_OK ? ok() : st;
+}
+
+tav_status tav_tree_attention(const tav_problem* prob, const tav_tree* tree, const tav_attn_io* io,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  Plan P;
+  tav_status st = make_plan(prob, nullptr, &P);
+  if (st == TAV_OK) st = check_ws(P, workspace, workspace_bytes);
+  if (st == TAV_OK) st = check_tree(tree, false);
+  if (st == TAV_OK) st = check_attn(prob, io);
+  if (st != TAV_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  TAV_HIP(launch_clear_status(ws_at<uint32_t>(workspace, P.off_status), s));
+  st = enqueue_prep(prob, P, tree, nullptr, workspace, s);
+  if (st == TAV_OK) st = enqueue_attention(prob, P, io, workspace, s);
+  return st == TAV_OK ? ok() : st;
+}
+
+tav_status tav_tree_verify(const tav_problem* prob, const tav_tree* tree, const tav_verify_io* io,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  Plan P;
+  tav_status st = make_plan(prob, nullptr, &P);
+  if (st == TAV_OK) st = check_ws(P, workspace, workspace_bytes);
+  if (st == TAV_OK) st = check_tree(tree, true);
+  if (st == TAV_OK) st = check_verify(prob, io);
+  if (st != TAV_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  TAV_HIP(launch_clear_status(ws_at<uint32_t>(workspace, P.off_status), s));
+  st = enqueue_prep(prob, P, tree, nullptr, workspace, s);
+  if (st == TAV_OK) st = enqueue_verify(prob, P, tree, io, workspace, s);
+  return st == TAV_OK ? ok() : st;
+}
+
+tav_status tav_presto_accept(const tav_presto_io* io, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (!io) return fail(TAV_ERR_NULL_POINTER, "presto io is NULL");
+  tav_status st = check_presto(io);
+  if (st != TAV_OK) return st;
+  Plan P;  // PreSTO alone needs only the status word and the fp64 log A buffer
+  P.off_status = 0;
+  P.off_presto = 256;
+  P.total = 256 + align_up((size_t)io->num_requests * 8);
+  st = check_ws(P, workspace, workspace_bytes);
+  if (st != TAV_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  TAV_HIP(launch_clear_status(ws_at<uint32_t>(workspace, P.off_status), s));
+  st = enqueue_presto(P, io, workspace, s);
+  return st == TAV_OK ? ok() : st;
+}
+
+tav_status tav_tree_attn_verify(const tav_problem* prob, const tav_tree* tree, const tav_attn_io* attn,
+                                const tav_verify_io* verify, const tav_presto_io* presto,
+                                const tav_tree_out* tree_out, void* workspace, size_t workspace_bytes,
+                                void* attn_stream, void* verify_stream) {
+  Plan P;
+  tav_status st = make_plan(prob, presto, &P);
+  if (st == TAV_OK) st = check_ws(P, workspace, workspace_bytes);
+  if (st == TAV_OK) st = check_tree(tree, verify != nullptr);
+  if (st == TAV_OK) st = check_attn(prob, attn);
+  if (st == TAV_OK && verify) st = check_verify(prob, verify);
+  if (st != TAV_OK) return st;
+  hipStream_t sa = (hipStream_t)attn_stream;
+  hipStream_t sv = (hipStream_t)verify_stream;
+  const bool two = sv != sa && (verify || presto);
+  hipEvent_t fork = nullptr, join = nullptr;
+  if (two) {
+    st = get_events(&fork, &join);
+    if (st != TAV_OK) return st;
+  }
+  TAV_HIP(launch_clear_status(ws_at<uint32_t>(workspace, P.off_status), sa));
+  st = enqueue_prep(prob, P, tree, tree_out, workspace, sa);
+  if (st != TAV_OK) return st;
+  if (two) {
+    TAV_HIP(hipEventRecord(fork, sa));
+    TAV_HIP(hipStreamWaitEvent(sv, fork, 0));
+  }
+  hipStream_t s2 = two ? sv : sa;
+  if (verify) {
+    st = enqueue_verify(prob, P, tree, verify, workspace, s2);
+    if (st != TAV_OK) return st;
+  }
+  if (presto) {
+    st = enqueue_presto(P, presto, workspace, s2);
+    if (st != TAV_OK) return st;
+  }
+  st = enqueue_attention(prob, P, attn, workspace, sa);
+  if (st != TAV_OK) return st;
+  if (two) {
+    TAV_HIP(hipEventRecord(join, sv));
+    TAV_HIP(hipStreamWaitEvent(sa, join, 0));
+  }
+  return ok();
+}
+
+tav_status tav_read_status(const void* workspace, void* stream, uint32_t* status_bits) {
+  if (!workspace || !status_bits) return fail(TAV_ERR_NULL_POINTER, "workspace / status_bits is NULL");
+  TAV_HIP(hipStreamSynchronize((hipStream_t)stream));
+  TAV_HIP(hipMemcpy(status_bits, workspace, sizeof(uint32_t), hipMemcpyDeviceToHost));
+  return ok();
+}
+
+const char* tav_status_string(tav_status s) {
+  switch (s) {
+    case TAV_OK: return "TAV_OK";
+    case TAV_ERR_NULL_POINTER: return "TAV_ERR_NULL_POINTER";
+    case TAV_ERR_BAD_SHAPE: return "TAV_ERR_BAD_SHAPE";
+    case TAV_ERR_UNSUPPORTED: return "TAV_ERR_UNSUPPORTED";
+    case TAV_ERR_WORKSPACE: return "TAV_ERR_WORKSPACE";
+    case TAV_ERR_HIP: return "TAV_ERR_HIP";
+    case TAV_ERR_INVALID_ARGUMENT: return "TAV_ERR_INVALID_ARGUMENT";
+  }
+  return "unknown tav_status";
+}
+
+const char* tav_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

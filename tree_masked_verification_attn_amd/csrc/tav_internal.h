@@ -1,0 +1,143 @@
+// Internal declarations shared by the host code and the gfx950 kernels of libtav.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "tav.h"
+
+namespace tav {
+
+constexpr int kTileKeys = 64;      // keys per attention tile (prefix or tree-tail)
+constexpr int kRowsPerWG = 256;    // query rows (node x head-in-group) per attention workgroup
+constexpr int kMaxTreeNodes = 256; // non-chain trees: ancestor sets are 256-bit masks
+constexpr int kMaskWords = 4;
+constexpr int kMaxChildren = 256;  // children of one node held by the verification kernels
+constexpr int kVocabThreads = 1024;
+constexpr int kVocabSlots = 19;    // 16-byte units held in registers per thread
+
+// Work decomposition of the attention pass.  A "row block" is up to
+// kRowsPerWG / G consecutive nodes of one sequence; a "work item" is one
+// contiguous range of key tiles (prefix tiles first, then tree-tail tiles) of
+// one row block.  The same integer formulas run on the host (grid sizes,
+// workspace) and on the device (plan_kernel), so both agree on the item list.
+struct Plan {
+  int B = 0, N = 0, Hq = 0, Hkv = 0, D = 0, G = 0, log2G = 0, NB = 0;
+  int total_rb = 0;       // row blocks over all sequences
+  int tiles_per_split = 1;
+  int total_items = 0;    // work items over all row blocks
+  bool any_split = false; // some row block has more than one item
+  int max_children = 0;
+  // workspace layout (byte offsets)
+  size_t off_status = 0, off_chain = 0, off_mask = 0, off_seq_rb = 0, off_rb_seq = 0,
+         off_item_off = 0, off_part_o = 0, off_part_lse = 0, off_stats = 0, off_term = 0,
+         off_presto = 0, total = 0;
+};
+
+__host__ __device__ static inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Tiles of the key sequence seen by row block rb of a sequence with n nodes
+// and L prefix rows: ceil(L / 64) prefix tiles, then the tree nodes 0 ..
+// min(n, (rb+1) * NB) - 1 (every ancestor of a node has an id <= the node).
+__host__ __device__ static inline int rb_tiles(int L, int n, int rb, int NB) {
+  int tail = n < (rb + 1) * NB ? n : (rb + 1) * NB;
+  return (L + kTileKeys - 1) / kTileKeys + (tail + kTileKeys - 1) / kTileKeys;
+}
+
+struct AttnArgs {
+  const void* q;
+  const void* k_node;
+  const void* v_node;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_table;
+  void* out;
+  float* lse;
+  const int32_t* node_offsets;
+  const int32_t* prefix_len;
+  const uint8_t* is_chain;
+  const uint64_t* mask;
+  const int32_t* seq_rb_off;
+  const int32_t* rb_seq;
+  const int32_t* item_off;
+  float* part_o;
+  float* part_lse;
+  uint32_t* status;
+  int B, Hq, Hkv, total_rb, total_items, tiles_per_split, block_size, num_blocks, max_blocks;
+  float scale;        // softmax scale (natural)
+};
+
+struct VocabArgs {
+  const void* logits;
+  const float* temperature;
+  const float* draft;
+  const int32_t* draft_row;
+  const int32_t* node_offsets;
+  const int32_t* parent;
+  const int32_t* token;
+  const uint8_t* sampled;
+  const float* uniforms;
+  float* stats;          // [N, 3]
+  int32_t* term_token;   // [N]
+  uint32_t* status;
+  int B, N, V, R;
+};
+
+struct WalkArgs {
+  const void* logits;
+  const float* temperature;
+  const float* draft;
+  const int32_t* draft_row;
+  const int32_t* node_offsets;
+  const int32_t* parent;
+  const int32_t* token;
+  const uint8_t* sampled;
+  const float* uniforms;
+  const float* stats;
+  const int32_t* term_token;
+  uint8_t* node_status;
+  int32_t* path;
+  int32_t* path_len;
+  int32_t* bonus;
+  uint32_t* status;
+  int B, V, R, max_path, logits_bf16;
+};
+
+struct PrestoArgs {
+  int T, R, M, max_transitions;
+  double alpha;
+  const float* root_lp0;
+  const float* root_lq;
+  const int32_t* cut;
+  const int32_t* suffix_off;
+  const float* lp0;
+  const float* lq;
+  const int32_t* pf_parent;
+  const uint8_t* pf_is_accept;
+  const int32_t* pf_request;
+  const float* u;
+  float* log_accept;
+  double* log_accept64;
+  int32_t* pf_path;
+  int32_t* pf_path_len;
+  uint32_t* status;
+};
+
+// Kernel launchers (defined next to their kernels).  They return the HIP error
+// of the launch.
+hipError_t launch_clear_status(uint32_t* status, hipStream_t s);
+hipError_t launch_plan(const Plan& p, const int32_t* node_offsets, const int32_t* prefix_len,
+                       int32_t* seq_rb_off, int32_t* rb_seq, int32_t* item_off, uint32_t* status,
+                       hipStream_t s);
+hipError_t launch_prep(const Plan& p, const int32_t* node_offsets, const int32_t* prefix_len,
+                       const int32_t* parent, uint8_t* chain_ws, uint64_t* mask_ws,
+                       const tav_tree_out* out, uint32_t* status, hipStream_t s);
+hipError_t launch_attn_bf16(const Plan& p, const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_f32(const Plan& p, const AttnArgs& a, hipStream_t s);
+hipError_t launch_merge(const Plan& p, const AttnArgs& a, bool bf16_out, hipStream_t s);
+hipError_t launch_vocab(const VocabArgs& a, bool bf16_logits, hipStream_t s);
+hipError_t launch_walk(const WalkArgs& a, hipStream_t s);
+hipError_t launch_presto(const PrestoArgs& a, hipStream_t s);
+
+}  // namespace tav
