@@ -1,0 +1,187 @@
+"""Throughput of the tree-masked scoring pass on one MI355X.
+
+Workload (default): 16 sequences, prefix lengths uniform in [1024, 8192] in a
+paged KV cache (block 16, shuffled block table), 64-node random trees of depth
+<= 8, 32 query / 8 KV heads, head_dim 128, bf16, vocabulary 151936, T = 1.0,
+seed 10086 -- the batched verification shape.  Inputs are synthetic (seeded).
+
+One step = one whole pass: tree preparation, split-KV tree attention + merge
+on one stream and vocabulary statistics + verification walk on a second
+stream (the two halves are independent), i.e. tav_tree_attention followed by
+tav_tree_verify on their own streams and workspaces.  Inputs are resident in
+HBM; two input copies alternate so consecutive steps do not re-read one
+step's data from the 256 MB last-level cache.
+
+Prints one JSON line:  value = tree nodes scored per second (attention +
+verification), plus the step's algorithmic HBM GB/s, the roofline of the
+dominant kernel (HIP-event durations over the timed region) and the oracle's
+throughput on a bounded sample of the same workload on the host CPU.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+
+
+def algorithmic_bytes(w):
+    """Bytes the pass must move: each prefix KV row once per (sequence, KV head),
+    each node's q / k / v / out once, each logits row once, each draft row that
+    verification uses once (nodes with a sampled child), small per-node arrays."""
+    import numpy as np
+
+    eb = 2 if w.dtype == "bf16" else 4
+    kv = int(sum(int(L) for L in w.prefix_len)) * w.Hkv * w.D * eb * 2
+    nodes = w.N * (w.Hq * w.D * eb * 2 + w.Hkv * w.D * eb * 2 + w.Hq * 4)
+    attn = kv + nodes + int(w.block_table.size) * 4
+    verify = 0
+    if w.logits is not None:
+        has_s = np.zeros(w.N, bool)
+        for b in range(w.B):
+            s = int(w.node_offsets[b])
+            for c in range(s + 1, int(w.node_offsets[b + 1])):
+                if w.sampled[c]:
+                    has_s[s + int(w.parent[c])] = True
+        used = int(np.sum(has_s & (w.draft_row >= 0)))
+        verify = w.N * w.V * eb + used * w.V * 4 + w.N * (4 + 1 + 4 + 1 + 8)
+    return attn, verify
+
+
+def attention_flops(w):
+    import oracle
+
+    prep = oracle.tree_prep(w.parent, w.node_offsets, w.prefix_len)
+    keys = 0
+    for b in range(w.B):
+        for v in w.seq_nodes(b):
+            keys += int(w.prefix_len[b]) + int(prep["depth"][v]) + 1
+    return 4 * w.D * w.Hq * keys
+
+
+def cpu_baseline(w, seqs):
+    """The oracle, as it is, on the given sequences of the workload (one thread)."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    nodes = [v for b in seqs for v in w.seq_nodes(b)]
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        oracle.tree_attention(w, nodes)
+        oracle.verify_workload(w, seqs)
+        dt = time.perf_counter() - t0
+    return {"value": len(nodes) / dt, "unit": "nodes/s", "cores": 1, "kind": "oracle",
+            "sample": f"sequences {list(seqs)} of the same workload ({len(nodes)} nodes: "
+                      f"attention of every node + verification walk), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--seed", type=int, default=10086)
+    ap.add_argument("--workload", default="c3", choices=["c2", "c3", "c5"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copies", type=int, default=2)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the scoring pass has no multi-GPU path in this build "
+              "(each configuration is one GPU's share); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import tree_masked_verification_attn_amd as tav
+    from workloads import device as wdev
+    from workloads import gen
+
+    torch.cuda.set_device(0)
+    w = gen.make(args.workload, args.seed)
+    copies = [wdev.upload(w, "cuda") for _ in range(max(1, args.copies))]
+    ws_v = [torch.zeros_like(c.workspace) for c in copies]     # verification's own workspace
+    sa = torch.cuda.Stream()
+    sv = torch.cuda.Stream()
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        c = copies[i % len(copies)]
+        if ev is not None:
+            ev[0].record(sa)
+        tav.tav_tree_attention(c.prob, c.tree, c.attn, c.workspace, sa)
+        if ev is not None:
+            ev[1].record(sa)
+            ev[2].record(sv)
+        tav.tav_tree_verify(c.prob, c.tree, c.verify, ws_v[i % len(copies)], sv)
+        if ev is not None:
+            ev[3].record(sv)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for c, wv in zip(copies, ws_v):
+        bits = tav.tav_read_status(c.workspace) | tav.tav_read_status(wv)
+        if bits:
+            raise RuntimeError(f"device status bits set: {tav.device_status_names(bits)}")
+    attn_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    ver_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
+
+    ms = wall * 1e3 / args.steps
+    attn_b, ver_b = algorithmic_bytes(w)
+    flops = attention_flops(w)
+    step_gbs = (attn_b + ver_b) / (ms * 1e-3) / 1e9
+    attn_gbs = attn_b / (attn_ms * 1e-3) / 1e9
+    ver_gbs = ver_b / (ver_ms * 1e-3) / 1e9
+    if attn_ms >= ver_ms:
+        roof = {"kernel": "tree attention (split-KV MFMA + merge)", "bound": "hbm",
+                "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "avg_launch_ms": round(attn_ms, 4), "algorithmic_bytes": attn_b,
+                "mfma_tflops": round(flops / (attn_ms * 1e-3) / 1e12, 1)}
+    else:
+        roof = {"kernel": "verification (vocabulary statistics + walk)", "bound": "hbm",
+                "achieved": round(ver_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ver_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "avg_launch_ms": round(ver_ms, 4), "algorithmic_bytes": ver_b}
+    other = {"attention_ms": round(attn_ms, 4), "attention_gbs": round(attn_gbs, 1),
+             "attention_tflops": round(flops / (attn_ms * 1e-3) / 1e12, 1),
+             "verify_ms": round(ver_ms, 4), "verify_gbs": round(ver_gbs, 1)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, list(range(min(6, w.B))))
+
+    desc = gen.CONFIG_DESCRIPTIONS[args.workload]
+    line = {
+        "metric": "tree nodes scored/sec (attn+verify) and achieved HBM GB/s vs MI355X peak",
+        "value": round(w.N / (ms * 1e-3), 1), "unit": "nodes/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded)",
+        "config": {"workload": f"{args.workload}: {desc}", "seed": args.seed, "nodes": w.N,
+                   "sequences": w.B, "prefix_rows": int(np.sum(w.prefix_len)),
+                   "draft_rows": int(w.draft.shape[0]) if w.draft is not None else 0},
+        "step_gbs": round(step_gbs, 1), "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+        "step_algorithmic_bytes": attn_b + ver_b,
+        "roofline": roof, "kernels": other, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -97,7 +97,7 @@ typedef struct tav_problem {
   int32_t head_dim;                  /* 64 or 128 */
   int32_t dtype;                     /* tav_dtype of q, k, v, caches, out and logits */
   float sm_scale;                    /* softmax scale; 0 means 1/sqrt(head_dim) */
-  int32_t block_size;                /* prefix rows per KV block: 8, 16, 32 or 64 */
+  int32_t block_size;                /* prefix rows per KV block: 16, 32 or 64 (bf16); 8 also for f32 */
   int32_t num_blocks;                /* physical blocks in k_cache / v_cache */
   int32_t max_blocks_per_seq;        /* row stride of block_table; prefix_len <= this * block_size */
   int32_t vocab;                     /* V for verification (0 when no verification is run) */
@@ -120,8 +120,9 @@ typedef struct tav_tree_out {
 
 /* Attention inputs and outputs.  Layouts:
  *   q [N, Hq, D];  k_node, v_node [N, Hkv, D] (the tree nodes' own keys/values);
- *   k_cache, v_cache [num_blocks, Hkv, block_size, D]: prefix row r of sequence b
- *     is slot r % block_size of block block_table[b * max_blocks_per_seq + r / block_size];
+ *   k_cache [num_blocks, Hkv, block_size, D] and v_cache [num_blocks, Hkv, D, block_size]
+ *     (values d-major inside a block): prefix row r of sequence b is slot
+ *     r % block_size of block block_table[b * max_blocks_per_seq + r / block_size];
  *   out [N, Hq, D] in the problem dtype; lse [N, Hq] float (natural log), optional. */
 typedef struct tav_attn_io {
   const void* q;

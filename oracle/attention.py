@@ -11,7 +11,8 @@ attention, evaluated exactly in float64:
 
   keys/values of node v, KV head g = floor(h / G):
      prefix rows r = 0 .. L_b - 1 (row r lives in physical block
-       block_table[b][r // block_size], slot r % block_size),
+       block_table[b][r // block_size], slot r % block_size; the key cache is
+       stored [block, head, slot, d] and the value cache [block, head, d, slot]),
      then the nodes of pi(v) from the root down to v;
   s_j = scale * <q_v,h , k_j>,  w_j = exp(s_j - max s),
   out = sum_j w_j v_j / sum_j w_j,  lse = max s + log sum_j w_j.
@@ -40,7 +41,7 @@ def prefix_rows(w, b: int, g: int):
     if nblk and (blocks.min() < 0 or blocks.max() >= w.k_cache.shape[0]):
         raise ValueError("block table entry out of range")
     K = _f64(w.k_cache[blocks, g], w.dtype).reshape(-1, w.D)[:L]
-    V = _f64(w.v_cache[blocks, g], w.dtype).reshape(-1, w.D)[:L]
+    V = _f64(w.v_cache[blocks, g], w.dtype).transpose(0, 2, 1).reshape(-1, w.D)[:L]
     return K, V
 
 

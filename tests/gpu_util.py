@@ -10,15 +10,31 @@ from workloads import device as wdev
 TIE = 1e-5
 
 
-def run(w, two_streams=False, max_path=64, with_verify=True, with_presto=True):
-    """Upload w, run tav_tree_attn_verify once, return numpy outputs and the status bits."""
+def run(w, two_streams=False, max_path=64, with_verify=True, with_presto=True, split_calls=False):
+    """Upload w, run the pass once, return numpy outputs and the status bits.
+
+    split_calls=True runs tav_tree_prep, tav_tree_attention and tav_tree_verify /
+    tav_presto_accept on two streams with their own workspaces (the benchmark's
+    launch configuration); otherwise one tav_tree_attn_verify call."""
     import tree_masked_verification_attn_amd as tav
 
     d = wdev.upload(w, "cuda", with_verify=with_verify, with_presto=with_presto, max_path=max_path)
-    sv = torch.cuda.Stream() if two_streams else None
-    tav.tav_tree_attn_verify(d.prob, d.tree, d.attn, d.verify, d.presto, d.tree_out, d.workspace,
-                             None, sv)
-    status = tav.tav_read_status(d.workspace)
+    if split_calls:
+        sa, sv = torch.cuda.Stream(), torch.cuda.Stream()
+        ws2 = torch.zeros_like(d.workspace)
+        tav.tav_tree_prep(d.prob, d.tree, d.tree_out, d.workspace, sa)
+        tav.tav_tree_attention(d.prob, d.tree, d.attn, d.workspace, sa)
+        if d.verify is not None:
+            tav.tav_tree_verify(d.prob, d.tree, d.verify, ws2, sv)
+        if d.presto is not None:
+            tav.tav_presto_accept(d.presto, ws2, sv)
+        torch.cuda.synchronize()
+        status = tav.tav_read_status(d.workspace) | tav.tav_read_status(ws2)
+    else:
+        sv = torch.cuda.Stream() if two_streams else None
+        tav.tav_tree_attn_verify(d.prob, d.tree, d.attn, d.verify, d.presto, d.tree_out, d.workspace,
+                                 None, sv)
+        status = tav.tav_read_status(d.workspace)
     torch.cuda.synchronize()
     out = {"status": status, "dev": d}
     out["out"] = d.attn.out.float().cpu().numpy().astype(np.float64)

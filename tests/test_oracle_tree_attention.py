@@ -123,7 +123,7 @@ def test_each_node_equals_attention_over_its_path(seed, tree):
                 for r in range(L):
                     blk = int(w.block_table[b, r // w.block_size])
                     rows_k.append(gen.as_f64(w.k_cache[blk, g, r % w.block_size], "bf16"))
-                    rows_v.append(gen.as_f64(w.v_cache[blk, g, r % w.block_size], "bf16"))
+                    rows_v.append(gen.as_f64(w.v_cache[blk, g, :, r % w.block_size], "bf16"))
                 K = np.array(rows_k + [gen.as_f64(w.k_node[p, g], "bf16") for p in path])
                 V = np.array(rows_v + [gen.as_f64(w.v_node[p, g], "bf16") for p in path])
                 for h in range(g * w.G, (g + 1) * w.G):

@@ -36,21 +36,52 @@ union Bf16Pack8 {
   __bf16 e[8];
 };
 
+// Direct global -> LDS copy of 16 bytes per lane; the LDS destination is
+// wave-uniform and lane i's bytes land at lds + 16 * i.
+__device__ inline void dma16(const void* gsrc, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
+// s_waitcnt on outstanding vector-memory operations only (lgkm / exp counters untouched).
+template <int N>
+__device__ inline void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Row of MFMA output m (within a 32-row block) -> key of the tile: bits 2 and 3 of
+// each 16-group swapped, so a lane's 8 probabilities of one 16-key group are 8
+// consecutive keys and the V^T operand is one 16-byte read.
+__device__ inline int sigma(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+constexpr int kStages = 4;          // key tiles in LDS (3 in flight while one is computed)
+constexpr float kRescaleSlack = 8.f;  // keep a stale max while the tile max exceeds it by <= 2^8
+
+// Stored 16-byte position of chunk c of key row k in a K tile (bank spreading
+// for the MFMA operand reads: rows are 256 B for D = 128 and 128 B for D = 64).
+template <int D>
+__device__ inline int kpos(int c, int key) {
+  return D == 128 ? (c ^ (key & 15)) : (c ^ ((key >> 1) & 7));
+}
+
 template <int D, int LOG2G>
 __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
   constexpr int G = 1 << LOG2G;
-  constexpr int NB = kRowsPerWG >> LOG2G;        // nodes per row block
-  constexpr int KS = D / 16;                     // k-steps of S^T = K Q^T
-  constexpr int DB = D / 32;                     // 32-wide output blocks of O^T
-  constexpr int CH = D / 8;                      // 16-byte chunks per key row
-  constexpr int LOADS = (kTileKeys * CH) / 512;  // chunks per thread per operand and tile
-  constexpr int KSTR = D + 8;                    // K tile row stride (elements), bank-spread
-  constexpr int VSTR = kTileKeys + 4;            // V^T tile row stride (elements)
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kTileKeys * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VSTR];
+  constexpr int KS = D / 16;               // k-steps of S^T = K Q^T
+  constexpr int DB = D / 32;               // 32-wide d blocks of O^T
+  constexpr int CH = D / 8;                // 16-byte chunks per key row
+  constexpr int NB = kRowsPerWG >> LOG2G;  // nodes per row block
+  constexpr int TILE_BYTES = kTileKeys * D * 2;
+  constexpr int KEYS_PER_DMA = 1024 / (D * 2);          // key rows per 1 KB wave load
+  constexpr int DMA_PER_OPERAND = TILE_BYTES / 1024 / 8;  // per wave and tile, for K and for V
+  constexpr int DMA_PER_TILE = 2 * DMA_PER_OPERAND;
+  // LDS: per stage a K tile [64 keys][D] (16-byte chunk c of key k stored at kpos(c, k))
+  // and a V^T tile [4 sub-blocks of 16 keys][D][16 keys].
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages][2 * TILE_BYTES];
 
   if (a.status[0] & TAV_DEV_PLAN_MISMATCH) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h32 = lane >> 5, l32 = lane & 31;
   const int item = blockIdx.x, g = blockIdx.y;
 
@@ -79,124 +110,97 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
   const bool chain = a.is_chain[b] != 0;
   if (!chain && n > kMaxTreeNodes) return;  // rejected by tree preparation
   const int Hq = a.Hq, Hkv = a.Hkv, bs = a.block_size;
+  const int32_t* btab = a.block_table + (size_t)b * a.max_blocks;
 
+  // this lane's query row
   const int row = wave * 32 + l32;
-  const int rnode = node0 + (row >> LOG2G);     // sequence-local node of this lane's row
+  const int rnode = node0 + (row >> LOG2G);
   const bool rvalid = (row >> LOG2G) < nodes_here;
   const int rhead = g * G + (row & (G - 1));
-
-  const uint16_t* qp = (const uint16_t*)a.q;
   bf16x8_t qreg[KS];
+  {
+    const uint16_t* qp = (const uint16_t*)a.q +
+                         ((size_t)(s0 + (rvalid ? rnode : 0)) * Hq + rhead) * D + h32 * 8;
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    Bf16Pack8 t;
-    t.u = make_uint4(0u, 0u, 0u, 0u);
-    if (rvalid)
-      t.u = *(const uint4*)(qp + ((size_t)(s0 + rnode) * Hq + rhead) * D + ks * 16 + h32 * 8);
-    qreg[ks] = t.v;
+    for (int ks = 0; ks < KS; ++ks) {
+      Bf16Pack8 t;
+      t.u = *(const uint4*)(qp + ks * 16);
+      if (!rvalid) t.u = make_uint4(0u, 0u, 0u, 0u);
+      qreg[ks] = t.v;
+    }
   }
 
   const uint16_t* kc = (const uint16_t*)a.k_cache;
   const uint16_t* vc = (const uint16_t*)a.v_cache;
-  const uint16_t* kn = (const uint16_t*)a.k_node;
-  const uint16_t* vn = (const uint16_t*)a.v_node;
-  uint4 kr[LOADS], vr[LOADS];
+  const int first_blk = L > 0 ? btab[0] : 0;
 
-  auto gload = [&](int t) {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int c = tid + i * 512;
-      const int key = c / CH, dc = c % CH;
-      bool valid;
-      size_t off = 0;
-      const uint16_t* ks_ = kc;
-      const uint16_t* vs_ = vc;
-      if (t < Tp) {
-        const int k = t * kTileKeys + key;
-        valid = k < L;
-        if (valid) {
-          const int blk = a.block_table[(size_t)b * a.max_blocks + k / bs];
-          if ((unsigned)blk >= (unsigned)a.num_blocks) {
-            atomicOr(a.status, (uint32_t)TAV_DEV_BAD_BLOCK);
-            valid = false;
-          } else {
-            off = (((size_t)blk * Hkv + g) * bs + (k % bs)) * D + dc * 8;
-          }
-        }
-      } else {
-        const int j = (t - Tp) * kTileKeys + key;
-        valid = j < tail_n;
-        off = ((size_t)(s0 + j) * Hkv + g) * D + dc * 8;
-        ks_ = kn;
-        vs_ = vn;
-      }
-      kr[i] = valid ? *(const uint4*)(ks_ + off) : make_uint4(0u, 0u, 0u, 0u);
-      vr[i] = valid ? *(const uint4*)(vs_ + off) : make_uint4(0u, 0u, 0u, 0u);
+  // DMA of prefix tile t into stage st.  Wave w copies key rows 8w..8w+7 of the K tile
+  // and d rows (w%2)*D/2 .. of sub-block w/2 of the V^T tile; every address stays inside
+  // a valid block (rows past the prefix read the first block and are masked).
+  auto issue_prefix = [&](int t, int st) {
+    uint8_t* kbase = lds[st];
+    uint8_t* vbase = lds[st] + TILE_BYTES;
+    const int sb = wave >> 1;
+    const int r0 = t * kTileKeys + sb * 16;              // first key row of the sub-block
+    int blk = r0 < L ? btab[r0 / bs] : first_blk;
+    if ((unsigned)blk >= (unsigned)a.num_blocks) {
+      if (lane == 0) atomicOr(a.status, (uint32_t)TAV_DEV_BAD_BLOCK);
+      blk = 0;
     }
-  };
-  auto lstore = [&](int buf) {
+    const int slot0 = r0 % bs;
+    const size_t kblk = (((size_t)blk * Hkv + g) * bs + slot0) * D;
+    const size_t vblk = ((size_t)blk * Hkv + g) * D * bs + slot0;
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int c = tid + i * 512;
-      const int key = c / CH, dc = c % CH;
-      *(uint4*)&Ks[buf][key * KSTR + dc * 8] = kr[i];
-      const uint16_t* ve = (const uint16_t*)&vr[i];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) Vt[buf][(dc * 8 + e) * VSTR + key] = ve[e];
+    for (int i = 0; i < DMA_PER_OPERAND; ++i) {
+      const int kt = wave * 8 + i * KEYS_PER_DMA + lane / CH;   // key of the tile
+      const int pos = lane % CH;
+      dma16(kc + kblk + (size_t)(kt - sb * 16) * D + kpos<D>(pos, kt) * 8,
+            kbase + (wave * 8 + i * KEYS_PER_DMA) * (D * 2));
+      const int d0 = (wave & 1) * (D / 2) + i * 32;
+      const int d = d0 + (lane >> 1);
+      dma16(vc + vblk + (size_t)d * bs + (lane & 1) * 8, vbase + sb * (D * 32) + d0 * 32);
     }
   };
 
-  const float sl2 = a.scale * kLog2e;
   float m_run = -INFINITY, l_run = 0.f;
   f32x16_t acc[DB];
 #pragma unroll
   for (int mb = 0; mb < DB; ++mb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
+  const float sl2 = a.scale * kLog2e;
 
-  if (t_begin < t_end) {
-    gload(t_begin);
-    lstore(0);
-  }
-  __syncthreads();
-  for (int t = t_begin; t < t_end; ++t) {
-    const int buf = (t - t_begin) & 1;
-    const bool more = t + 1 < t_end;
-    if (more) gload(t + 1);
-
+  // one tile of math from stage st; kind: 0 full prefix tile, 1 partial prefix tile, 2 tail tile
+  auto compute = [&](int t, int st, int kind) {
+    const uint8_t* kbase = lds[st];
+    const uint8_t* vbase = lds[st] + TILE_BYTES;
     f32x16_t sacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+      const int key = kb * 32 + sigma(l32);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8_t ka = *(const bf16x8_t*)&Ks[buf][(kb * 32 + l32) * KSTR + ks * 16 + h32 * 8];
+        const bf16x8_t ka = *(const bf16x8_t*)(kbase + key * (D * 2) + kpos<D>(ks * 2 + h32, key) * 16);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], sacc[kb], 0, 0, 0);
       }
     }
-
-    // scale, mask, running max (this lane's row; its partner lane l ^ 32 holds the other keys)
-    const bool is_prefix = t < Tp;
-    const int tt = t - Tp;
+    // scale + mask; key of (kb, r) for this lane = kb*32 + (r/8)*16 + h*8 + r%8
     uint64_t mw = 0;
-    if (!is_prefix && !chain && rvalid) mw = a.mask[(size_t)(s0 + rnode) * kMaskWords + tt];
-    const bool full_prefix = is_prefix && (t + 1) * kTileKeys <= L;
+    if (kind == 2 && !chain && rvalid) mw = a.mask[(size_t)(s0 + rnode) * kMaskWords + (t - Tp)];
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int kin = kb * 32 + (r >> 2) * 8 + h32 * 4 + (r & 3);
+        const int kin = kb * 32 + (r >> 3) * 16 + h32 * 8 + (r & 7);
         float s = sacc[kb][r] * sl2;
-        if (!full_prefix) {
-          bool vis;
-          if (is_prefix) {
-            vis = t * kTileKeys + kin < L;
-          } else {
-            const int j = tt * kTileKeys + kin;
-            vis = j < tail_n && (chain ? j <= rnode : ((mw >> (j & 63)) & 1ull) != 0ull);
-          }
+        if (kind == 1) {
+          s = (t * kTileKeys + kin < L) ? s : -INFINITY;
+        } else if (kind == 2) {
+          const int j = (t - Tp) * kTileKeys + kin;
+          const bool vis = j < tail_n && (chain ? j <= rnode : ((mw >> (j & 63)) & 1ull) != 0ull);
           s = vis ? s : -INFINITY;
         }
         sacc[kb][r] = s;
@@ -204,43 +208,97 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
       }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
-
-    Bf16Pack8 pb[4];
-    float psum = 0.f;
+    // lazy rescaling: keep the running max until some row's tile max exceeds it by 2^8
+    if (__ballot(mx > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < DB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mb][r] *= alpha;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    bf16x8_t pb[4];
+    float ps = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = fast_exp2(sacc[kb][r] - m_use);
-        psum += p;
-        pb[kb * 2 + (r >> 3)].e[r & 7] = (__bf16)p;
+        ps += p;
+        pb[kb * 2 + (r >> 3)][r & 7] = (__bf16)p;
       }
     }
-    l_run = l_run * alpha + psum;
+    l_run += ps;
+    // O^T += V^T P^T over the four 16-key groups (one sub-block each)
 #pragma unroll
-    for (int mb = 0; mb < DB; ++mb)
+    for (int k2 = 0; k2 < 4; ++k2) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mb][r] *= alpha;
-
-    // O^T += V^T P^T; the lane's k-slots are keys {h*4..h*4+3, 8+h*4..8+h*4+3} of each
-    // 16-key step, matching where the S^T layout left this lane's probabilities.
-#pragma unroll
-    for (int mb = 0; mb < DB; ++mb) {
-#pragma unroll
-      for (int k2 = 0; k2 < 4; ++k2) {
-        const uint16_t* vrow = &Vt[buf][(mb * 32 + l32) * VSTR + k2 * 16 + h32 * 4];
-        Bf16Pack8 va;
-        va.h[0] = *(const uint2*)vrow;
-        va.h[1] = *(const uint2*)(vrow + 8);
-        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va.v, pb[k2].v, acc[mb], 0, 0, 0);
+      for (int mb = 0; mb < DB; ++mb) {
+        const bf16x8_t va = *(const bf16x8_t*)(vbase + k2 * (D * 32) + (mb * 32 + l32) * 32 + h32 * 16);
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[k2], acc[mb], 0, 0, 0);
       }
     }
+  };
 
-    if (more) lstore(buf ^ 1);
+  // ---- prefix tiles: DMA pipeline with kStages - 1 tiles in flight, one barrier per tile ----
+  const int p_end = min(t_end, Tp);
+  if (t_begin < p_end) {
+    int issued = t_begin;
+    for (; issued < min(p_end, t_begin + kStages - 1); ++issued) issue_prefix(issued, (issued - t_begin) % kStages);
+    for (int t = t_begin; t < p_end; ++t) {
+      const int after = issued - 1 - t;       // tiles issued after t, still in flight
+      if (after >= 2) wait_vm<2 * DMA_PER_TILE>();
+      else if (after == 1) wait_vm<DMA_PER_TILE>();
+      else wait_vm<0>();
+      __builtin_amdgcn_s_barrier();           // tile t landed for every wave; tile t-1's stage is free
+      if (issued < p_end) {
+        issue_prefix(issued, (issued - t_begin) % kStages);
+        ++issued;
+      }
+      const int st = (t - t_begin) % kStages;
+      if ((t + 1) * kTileKeys > L) {
+        // last, partial prefix tile: zero V^T of keys >= L so 0 * stale data never reaches O
+        uint16_t* vbase = (uint16_t*)(lds[st] + TILE_BYTES);
+        for (int e = tid; e < 4 * D * 16; e += 512) {
+          const int sb = e / (D * 16), kk = e % 16;
+          if (t * kTileKeys + sb * 16 + kk >= L) vbase[e] = 0;
+        }
+        __syncthreads();
+        compute(t, st, 1);
+      } else {
+        compute(t, st, 0);
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- tree-tail tiles (the sequence's own nodes), staged through registers ----
+  const uint16_t* kn = (const uint16_t*)a.k_node;
+  const uint16_t* vn = (const uint16_t*)a.v_node;
+  for (int t = max(t_begin, Tp); t < t_end; ++t) {
+    uint8_t* kbase = lds[0];
+    uint16_t* vbase = (uint16_t*)(lds[0] + TILE_BYTES);
+#pragma unroll
+    for (int i = 0; i < (kTileKeys * CH) / 512; ++i) {
+      const int c = tid + i * 512;                // 64 keys x CH chunks of 8 d
+      const int key = c / CH, ch = c % CH;
+      const int j = (t - Tp) * kTileKeys + key;
+      const bool valid = j < tail_n;
+      const size_t off = ((size_t)(s0 + (valid ? j : 0)) * Hkv + g) * D + ch * 8;
+      uint4 kv = *(const uint4*)(kn + off);
+      uint4 vv = *(const uint4*)(vn + off);
+      if (!valid) kv = vv = make_uint4(0u, 0u, 0u, 0u);
+      *(uint4*)(kbase + key * (D * 2) + kpos<D>(ch, key) * 16) = kv;
+      const uint32_t w4[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        vbase[(key >> 4) * (D * 16) + (ch * 8 + e) * 16 + (key & 15)] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+    }
+    __syncthreads();
+    compute(t, 0, 2);
     __syncthreads();
   }
 
@@ -275,6 +333,7 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
 }
 
 // Online-softmax merge of the split partials: out = sum_s exp(lse_s - LSE) O_s.
+// One block per (row block, KV head, group of 16 rows); a thread owns 4 outputs.
 template <typename OutT>
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int D, int log2G) {
   const int rbi = blockIdx.x, g = blockIdx.y;
@@ -291,8 +350,8 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int D, int log2G
   const int node0 = rb * NB;
   const int nodes_here = min(NB, n - node0);
   const int DQ = D / 4;
-  for (int task = threadIdx.x; task < kRowsPerWG * DQ; task += blockDim.x) {
-    const int row = task / DQ, dq = task % DQ;
+  for (int task = threadIdx.x; task < 16 * DQ; task += blockDim.x) {
+    const int row = blockIdx.z * 16 + task / DQ, dq = task % DQ;
     if ((row >> log2G) >= nodes_here) continue;
     const int node = s0 + node0 + (row >> log2G);
     const int head = g * G + (row & (G - 1));
@@ -363,7 +422,9 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   const float* vn = (const float*)a.v_node;
   for (int d = lane; d < D; d += 64) qs[d] = q[((size_t)v * a.Hq + h) * D + d];
   __syncthreads();
-  auto row_ptr = [&](int k, bool key, bool* ok) -> const float* {
+  // pointer to element 0 of key k's key (or value) vector and the stride between its elements
+  auto row_ptr = [&](int k, bool key, bool* ok, int* stride) -> const float* {
+    *stride = 1;
     if (k < L) {
       const int blk = a.block_table[(size_t)b * a.max_blocks + k / a.block_size];
       if ((unsigned)blk >= (unsigned)a.num_blocks) {
@@ -371,8 +432,10 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
         *ok = false;
         return nullptr;
       }
-      const size_t off = (((size_t)blk * a.Hkv + g) * a.block_size + (k % a.block_size)) * D;
-      return (key ? kc : vc) + off;
+      const int slot = k % a.block_size;
+      if (key) return kc + (((size_t)blk * a.Hkv + g) * a.block_size + slot) * D;
+      *stride = a.block_size;                    // values: [block, head, d, slot]
+      return vc + ((size_t)blk * a.Hkv + g) * D * a.block_size + slot;
     }
     const int j = k - L;
     *ok = chain || ((mw[j >> 6] >> (j & 63)) & 1ull);
@@ -388,7 +451,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
     float s = -INFINITY;
     if (k < total) {
       bool ok = true;
-      const float* kp = row_ptr(k, true, &ok);
+      int st1;
+      const float* kp = row_ptr(k, true, &ok, &st1);
       if (ok) {
         float dot = 0.f;
         for (int d = 0; d < D; ++d) dot = fmaf(qs[d], kp[d], dot);
@@ -411,10 +475,11 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
       const float pj = ps[jj];
       if (pj == 0.f) continue;
       bool ok = true;
-      const float* vp = row_ptr(base + jj, false, &ok);
+      int vst;
+      const float* vp = row_ptr(base + jj, false, &ok, &vst);
       if (!ok) continue;
 #pragma unroll
-      for (int i = 0; i < DPL; ++i) o[i] = fmaf(pj, vp[lane + 64 * i], o[i]);
+      for (int i = 0; i < DPL; ++i) o[i] = fmaf(pj, vp[(size_t)(lane + 64 * i) * vst], o[i]);
     }
     __syncthreads();
   }
@@ -455,7 +520,7 @@ hipError_t launch_attn_f32(const Plan& p, const AttnArgs& a, hipStream_t s) {
 
 hipError_t launch_merge(const Plan& p, const AttnArgs& a, bool bf16_out, hipStream_t s) {
   if (!p.any_split) return hipSuccess;
-  dim3 grid(p.total_rb, p.Hkv);
+  dim3 grid(p.total_rb, p.Hkv, kRowsPerWG / 16);
   if (bf16_out) merge_kernel<__bf16><<<grid, 256, 0, s>>>(a, p.D, p.log2G);
   else merge_kernel<float><<<grid, 256, 0, s>>>(a, p.D, p.log2G);
   return hipGetLastError();

@@ -41,7 +41,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
-constexpr int kTargetWorkgroups = 512;  // about two workgroups per MI355X compute unit
+constexpr int kTargetWorkgroups = 512;  // two rounds of one workgroup per MI355X compute unit
 constexpr int kMinTilesPerSplit = 8;    // at least 512 keys per split
 
 int log2_exact(int x) {
@@ -74,6 +74,8 @@ tav_status check_problem(const tav_problem* p) {
     return fail(TAV_ERR_INVALID_ARGUMENT, "sm_scale must be finite and >= 0");
   if (p->block_size != 8 && p->block_size != 16 && p->block_size != 32 && p->block_size != 64)
     return fail(TAV_ERR_UNSUPPORTED, "block_size must be 8, 16, 32 or 64 (got %d)", p->block_size);
+  if (p->dtype == TAV_BF16 && p->block_size < 16)
+    return fail(TAV_ERR_UNSUPPORTED, "bf16 attention needs block_size 16, 32 or 64 (got %d)", p->block_size);
   if (p->max_blocks_per_seq < 1 || p->num_blocks < 0)
     return fail(TAV_ERR_BAD_SHAPE, "max_blocks_per_seq must be >= 1 and num_blocks >= 0");
   for (int b = 0; b < p->num_seqs; ++b) {
@@ -122,9 +124,26 @@ tav_status make_plan(const tav_problem* p, const tav_presto_io* pr, Plan* out) {
     for (int rb = 0; rb < nrb; ++rb) tiles += rb_tiles(p->prefix_len_host[b], n, rb, P.NB);
   }
   tiles *= P.Hkv;
+  // key tiles per work item: the smallest count (from an even share of kTargetWorkgroups)
+  // whose item total stays within kTargetWorkgroups, so no nearly empty extra round of
+  // workgroups is left for the (one workgroup per CU) attention kernel
   int64_t tps = (tiles + kTargetWorkgroups - 1) / kTargetWorkgroups;
   P.tiles_per_split = (int)(tps < kMinTilesPerSplit ? kMinTilesPerSplit : tps);
   if (p->dtype == TAV_BF16) {
+    for (;;) {
+      int64_t items = 0;
+      int max_t = 0;
+      for (int b = 0; b < P.B; ++b) {
+        const int n = p->node_offsets_host[b + 1] - p->node_offsets_host[b];
+        for (int rb = 0; rb < ceil_div(n, P.NB); ++rb) {
+          const int tr = rb_tiles(p->prefix_len_host[b], n, rb, P.NB);
+          items += ceil_div(tr, P.tiles_per_split);
+          max_t = tr > max_t ? tr : max_t;
+        }
+      }
+      if (items * P.Hkv <= kTargetWorkgroups || P.tiles_per_split >= max_t) break;
+      ++P.tiles_per_split;
+    }
     for (int b = 0; b < P.B; ++b) {
       const int n = p->node_offsets_host[b + 1] - p->node_offsets_host[b];
       for (int rb = 0; rb < ceil_div(n, P.NB); ++rb) {
@@ -147,6 +166,8 @@ tav_status make_plan(const tav_problem* p, const tav_presto_io* pr, Plan* out) {
   if (P.any_split) o = align_up(o + (size_t)P.total_items * P.Hkv * kRowsPerWG * 4);
   P.off_stats = o; o = align_up(o + (size_t)P.N * 3 * 4);
   P.off_term = o; o = align_up(o + (size_t)P.N * 4);
+  P.off_child_p = o; o = align_up(o + (size_t)P.N * 8);
+  P.off_child_q = o; o = align_up(o + (size_t)P.N * 4);
   P.off_presto = o; o = align_up(o + (size_t)(pr ? pr->num_requests : 0) * 8);
   P.total = o;
   *out = P;
@@ -260,6 +281,8 @@ tav_status enqueue_verify(const tav_problem* p, const Plan& P, const tav_tree* t
   va.draft_row = io->draft_row; va.node_offsets = p->node_offsets; va.parent = t->parent;
   va.token = t->token; va.sampled = t->sampled; va.uniforms = io->uniforms;
   va.stats = stats; va.term_token = term; va.status = status;
+  va.child_p = ws_at<double>(ws, P.off_child_p);
+  va.child_q = ws_at<float>(ws, P.off_child_q);
   va.B = P.B; va.N = P.N; va.V = p->vocab; va.R = io->num_draft_rows;
   TAV_HIP(launch_vocab(va, p->dtype == TAV_BF16, s));
   WalkArgs wa;
@@ -267,6 +290,7 @@ tav_status enqueue_verify(const tav_problem* p, const Plan& P, const tav_tree* t
   wa.draft_row = io->draft_row; wa.node_offsets = p->node_offsets; wa.parent = t->parent;
   wa.token = t->token; wa.sampled = t->sampled; wa.uniforms = io->uniforms;
   wa.stats = stats; wa.term_token = term; wa.node_status = io->node_status; wa.path = io->path;
+  wa.child_p = va.child_p; wa.child_q = va.child_q;
   wa.path_len = io->path_len; wa.bonus = io->bonus_token; wa.status = status;
   wa.B = P.B; wa.V = p->vocab; wa.R = io->num_draft_rows; wa.max_path = io->max_path;
   wa.logits_bf16 = p->dtype == TAV_BF16;
@@ -364,8 +388,7 @@ tav_status tav_tree_verify(const tav_problem* prob, const tav_tree* tree, const 
   if (st != TAV_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   TAV_HIP(launch_clear_status(ws_at<uint32_t>(workspace, P.off_status), s));
-  st = enqueue_prep(prob, P, tree, nullptr, workspace, s);
-  if (st == TAV_OK) st = enqueue_verify(prob, P, tree, io, workspace, s);
+  st = enqueue_verify(prob, P, tree, io, workspace, s);
   return st == TAV_OK ? ok() : st;
 }
 

@@ -32,7 +32,7 @@ struct Plan {
   // workspace layout (byte offsets)
   size_t off_status = 0, off_chain = 0, off_mask = 0, off_seq_rb = 0, off_rb_seq = 0,
          off_item_off = 0, off_part_o = 0, off_part_lse = 0, off_stats = 0, off_term = 0,
-         off_presto = 0, total = 0;
+         off_child_p = 0, off_child_q = 0, off_presto = 0, total = 0;
 };
 
 __host__ __device__ static inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -80,6 +80,8 @@ struct VocabArgs {
   const float* uniforms;
   float* stats;          // [N, 3]
   int32_t* term_token;   // [N]
+  double* child_p;       // [N] p of the node's token under its parent's target distribution
+  float* child_q;        // [N] q~ of the node's token under its parent's draft row (0 if none)
   uint32_t* status;
   int B, N, V, R;
 };
@@ -96,6 +98,8 @@ struct WalkArgs {
   const float* uniforms;
   const float* stats;
   const int32_t* term_token;
+  const double* child_p;
+  const float* child_q;
   uint8_t* node_status;
   int32_t* path;
   int32_t* path_len;

@@ -142,7 +142,7 @@ class Workload:
     k_node: np.ndarray            # [N, Hkv, D]
     v_node: np.ndarray            # [N, Hkv, D]
     k_cache: np.ndarray           # [num_blocks, Hkv, block_size, D]
-    v_cache: np.ndarray
+    v_cache: np.ndarray           # [num_blocks, Hkv, D, block_size] (d-major within a block)
     block_table: np.ndarray       # [B, max_blocks] i32 (-1 where unused)
     V: int = 0
     logits: Optional[np.ndarray] = None       # [N, V]
@@ -309,7 +309,7 @@ def _paged_prefix(seed, prefix_len, Hkv, D, bs, dtype, shuffle=True, shared=Fals
             off += nblk[b]
     nb = max(total, 1)
     k_cache = _store(_normal(_key(seed, "k_cache"), (nb, Hkv, bs, D)), dtype)
-    v_cache = _store(_normal(_key(seed, "v_cache"), (nb, Hkv, bs, D)), dtype)
+    v_cache = _store(_normal(_key(seed, "v_cache"), (nb, Hkv, D, bs)), dtype)
     return k_cache, v_cache, table
 
 
@@ -532,7 +532,7 @@ def presto_batch(seed: int, *, T: int, n_pf: int, Hq: int, Hkv: int, D: int, dty
                      parent=np.zeros(0, np.int32), prefix_len=np.zeros(0, np.int32),
                      q=np.zeros((0, Hq, D)), k_node=np.zeros((0, Hkv, D)),
                      v_node=np.zeros((0, Hkv, D)), k_cache=np.zeros((1, Hkv, block_size, D)),
-                     v_cache=np.zeros((1, Hkv, block_size, D)),
+                     v_cache=np.zeros((1, Hkv, D, block_size)),
                      block_table=np.full((0, 1), -1, np.int32), presto=pr)
         return w
     B = R
