@@ -122,7 +122,7 @@ def test_verify_validation_codes():
 
     assert status(_Host(vocab=0)) == 2                       # no vocabulary
     assert status(_Host(vocab=1001)) == 3                    # not a multiple of 8 for bf16 logits
-    assert status(_Host(vocab=155656)) == 3                  # beyond one workgroup's registers
+    assert status(_Host(vocab=1048584)) == 3                 # beyond 64 slices of 16384 tokens
     assert status(_Host(vocab=1000, dtype=tav.TAV_F32), max_path=0) == 2
     assert status(_Host(vocab=1000), logits=None) == 1
     assert status(_Host(vocab=1000), num_draft_rows=2, draft=None) == 1

@@ -43,6 +43,9 @@ CASES = {
     "random_g1": ("random", [40, 10], [77, 1000], 4, 4, 128, 1024, 1.3, {}),
     "eagle_hybrid": ("eagle", [30, 22], [2048, 300], 32, 8, 128, 8192, 0.7, {"max_depth": 5, "hybrid": "all"}),
     "random_g16": ("random", [16, 17], [64, 65], 16, 1, 128, 512, 1.0, {}),
+    # 39 / 13 / 12 children of one node (beyond and at the children kept per node record);
+    # V = 20008 spans two vocabulary slices, the second one ragged
+    "star_two_slices": ("star", [40, 14, 13], [33, 0, 16], 8, 2, 64, 20008, 0.9, {}),
 }
 
 
@@ -69,6 +72,31 @@ def test_chains_bf16(seed):
     got = gu.run(w, max_path=512)
     assert got["status"] == 0, got["status"]
     gu.check_tree_prep(w, got)
+    gu.check_attention(w, got)
+    gu.check_verify(w, got)
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_f32_multi_slice(seed):
+    """fp32 logits over three vocabulary slices (8192 tokens each), the last one ragged."""
+    _say("f32 multi-slice", seed)
+    w = gen.tree_batch(seed, B=2, prefix_len=[50, 3], tree="random", n_nodes=[20, 9], Hq=4, Hkv=1,
+                       D=64, dtype="f32", V=20004, temperature=1.1)
+    got = gu.run(w)
+    assert got["status"] == 0, got["status"]
+    gu.check_attention(w, got)
+    gu.check_verify(w, got)
+    gu.check_node_stats(w, got, range(w.N))
+
+
+@pytest.mark.parametrize("seed", SEEDS[:1])
+def test_long_chain_walk(seed):
+    """A 1100-node chain: the walk reads its per-node values from memory, not LDS."""
+    _say("long chain", seed)
+    w = gen.tree_batch(seed, B=2, prefix_len=[10, 40], tree="chain", n_nodes=[1100, 30], Hq=4, Hkv=1,
+                       D=64, dtype="bf16", V=256, temperature=1.0)
+    got = gu.run(w, max_path=1200)
+    assert got["status"] == 0, got["status"]
     gu.check_attention(w, got)
     gu.check_verify(w, got)
 

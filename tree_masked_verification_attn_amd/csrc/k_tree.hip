@@ -8,8 +8,9 @@
 namespace tav {
 namespace {
 
+// Clears the status word and the counter word that follows it in the status block.
 __global__ void clear_status_kernel(uint32_t* status) {
-  if (threadIdx.x == 0) status[0] = 0u;
+  if (threadIdx.x == 0) { status[0] = 0u; status[kCounterWord] = 0u; }
 }
 
 // Exclusive scan of one int per thread over a 1024-thread block; also returns the total.

@@ -9,20 +9,23 @@
 // the sequential rejection of Progressive Tree Drafting (Section 3.2, Appendix
 // E / F).  p = softmax(logits / T) (RheoSampling Section 5.4).
 //
-// vocab_kernel (one 1024-thread workgroup per node) reads the node's logits
-// row once into registers (bf16: 19 x 16 bytes per thread covers 155648
-// tokens) and its draft row once, and produces M = max l/T, S = sum exp(l/T-M),
-// Z = sum (p - q~)+ and the token the final draw would give if the walk ended
-// at this node.  Sums run per lane in fp32 and across lanes in fp64.
-// walk_kernel (one wave per sequence) then takes the accept/reject decisions
-// in fp64 from these statistics and point reads of the logits / draft rows.
+// The vocabulary work is three streaming kernels over fixed slices of each row
+// (256 threads x 8 sixteen-byte units): vocab_stats_kernel reads every logits
+// row once (slice maxima, exp sums and chunk sums); vocab_residual_kernel reads
+// the draft row (and the logits row again) only for nodes with a sampled child
+// and replaces the chunk sums with those of (p - q~)+; vocab_pick_kernel (one
+// workgroup per node) combines the slices into M = max l/T, S = sum exp(l/T-M)
+// and Z = sum (p - q~)+, records p and q~ of each child's token, and finds the
+// token the final draw would give if the walk ended at the node (fp64 scan over
+// chunks, then one chunk re-read).  Sums run per lane in fp32 and across lanes
+// in fp64.  walk_kernel (one wave per sequence) then takes the accept/reject
+// decisions in fp64 from these values.
 #include "tav_internal.h"
 
 namespace tav {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kWaves = kVocabThreads / 64;
 
 template <typename LT>
 __device__ inline float to_f(LT x);
@@ -65,327 +68,503 @@ __device__ inline float wave_max_f(float x) {
   return x;
 }
 
-__device__ inline void dma16(const void* gsrc, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
-}
-template <int N>
-__device__ inline void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+constexpr int kSW = kSliceThreads / 64;           // waves of a slice workgroup
+constexpr int kChunksPerSlice = kSliceUnits * kSW;  // chunks of 64 units per slice
+constexpr int kResUnits = kSliceUnits / 2;          // units per thread of a residual item
+constexpr int kChunksPerHalf = kResUnits * kSW;
+
+// Per-node record written by workgroup (node, slice 0) of the stats kernel.
+enum RecField {
+  kRecSeq = 0, kRecS0, kRecN, kRecKids, kRecSampled, kRecInvT, kRecErr, kRecSmpMask,
+  kRecKidId = 8,                      // kRecKidsMax child ids (local) ...
+  kRecKidTok = 8 + kRecKidsMax,       // ... and their tokens
+};
+static_assert(kRecKidTok + kRecKidsMax <= kRecWords, "record layout");
+
+__device__ inline void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
 }
 
-constexpr int kDraftStages = 4;
+// Sequence of node v: the number of sequence ends node_offsets[1..B] that are <= v, counted by
+// the whole workgroup with one read per thread.
+__device__ int block_seq_of(const int32_t* node_offsets, int B, int v, int* cnt_s) {
+  if (threadIdx.x == 0) *cnt_s = 0;
+  __syncthreads();
+  int c = 0;
+  for (int t = threadIdx.x + 1; t <= B; t += blockDim.x) c += node_offsets[t] <= v;
+  if (c) atomicAdd(cnt_s, c);
+  __syncthreads();
+  const int b = *cnt_s;
+  return b < B ? b : B - 1;   // v < N = node_offsets[B] already gives b < B
+}
 
+// log2-domain reference of a slice maximum (a slice of -inf logits uses 0; its sum is 0).
+__device__ inline float ref_l2(float m_raw, float invT) {
+  return (m_raw == -INFINITY ? 0.f : m_raw * invT) * kLog2e;
+}
+
+// Row statistics from the slice maxima and sums: M = max l / T and S = sum exp(l/T - M).
+struct RowStats {
+  float M, Ml2, invS;
+  double S;
+  bool no_mass;
+};
+__device__ inline RowStats finish_stats(float Mraw, double S_at_Mraw, float invT) {
+  RowStats r;
+  r.no_mass = Mraw == -INFINITY;
+  r.M = r.no_mass ? 0.f : Mraw * invT;
+  r.Ml2 = r.M * kLog2e;
+  r.S = S_at_Mraw;
+  r.invS = (float)(1.0 / S_at_Mraw);
+  return r;
+}
+// Workgroup version: slice values staged in LDS, every thread gets the same values.
+__device__ RowStats row_stats_block(const float* sl_m, const double* sl_s, int nsl, float invT,
+                                    float* m_s, double* s_s) {
+  for (int j = threadIdx.x; j < nsl; j += blockDim.x) { m_s[j] = sl_m[j]; s_s[j] = sl_s[j]; }
+  __syncthreads();
+  float Mraw = -INFINITY;
+  for (int j = 0; j < nsl; ++j) Mraw = fmaxf(Mraw, m_s[j]);
+  const float Ml2 = (Mraw == -INFINITY ? 0.f : Mraw * invT) * kLog2e;
+  double S = 0.0;
+  for (int j = 0; j < nsl; ++j) {
+    const double sj = s_s[j];
+    if (sj != 0.0) S += sj * exp2((double)ref_l2(m_s[j], invT) - (double)Ml2);
+  }
+  return finish_stats(Mraw, S, invT);
+}
+
+// Sums each unit's per-lane values over the 64 lanes of its wave (one chunk per unit and
+// wave), transposed through LDS: 64 / UN threads per chunk, UN values each.  Returns the
+// chunk total in the first thread of each group; chunk index (tid * UN) / 64.
+template <int UN>
+__device__ inline float chunk_totals(const float (&x)[UN], float* part) {
+  constexpr int TPC = 64 / UN;   // threads per chunk
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int k = 0; k < UN; ++k) part[(k * kSW + wave) * 64 + lane] = x[k];
+  __syncthreads();
+  const float* src = part + (tid / TPC) * 64 + (tid % TPC) * UN;
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < UN; i += 4) {
+    const float4 a4 = *(const float4*)(src + i);
+    t += (a4.x + a4.y) + (a4.z + a4.w);
+  }
+#pragma unroll
+  for (int d = 1; d < TPC; d <<= 1) t += __shfl_xor(t, d);
+  return t;
+}
+
+// Slice statistics of every (node, slice): one 256-thread workgroup reads kSliceUnits 16-byte
+// units per thread of the node's logits row and writes the slice's largest raw logit m, the
+// sum s = sum exp2(l * log2e / T - ref_l2(m)) (fp32 per lane and chunk, fp64 across chunks)
+// and the same sum over each chunk of 64 units (the weights of the final draw when the node
+// has no sampled child).  Workgroup (node, 0) also writes the node's record (sequence, 1/T,
+// children, checks of the parent array and temperature) and lists the node when it has a
+// sampled child and a draft row.
 template <typename LT>
-__global__ __launch_bounds__(kVocabThreads) void vocab_kernel(VocabArgs a) {
-  constexpr int EPU = 16 / sizeof(LT);  // logits per 16-byte unit (8 bf16 / 4 f32)
-  constexpr int DPS = EPU / 4;          // 16-byte draft loads per thread and slot
-  constexpr int SLOTS = kVocabSlots;
-  constexpr int NCH = SLOTS * kWaves;   // chunks of 64 * EPU consecutive tokens
-  constexpr int STAGE = kVocabThreads * EPU * 4;
-  __shared__ __attribute__((aligned(1024))) uint8_t dstage[kDraftStages][STAGE];
-  __shared__ float red_f[kWaves];
-  __shared__ double red_d[kWaves];
-  __shared__ float csum[NCH];
-  __shared__ int kid_id[kMaxChildren];
-  __shared__ int kid_tok[kMaxChildren];
-  __shared__ uint8_t kid_smp[kMaxChildren];
-  __shared__ int n_kids, n_samp, bad_s;
-  __shared__ int pick_chunk;
-  __shared__ float pick_rem;
-  __shared__ int pick_token;
-
-  const int v = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int V = a.V;
-  int lo = 0, hi = a.B;
-  while (hi - lo > 1) {
-    int mid = (lo + hi) >> 1;
-    if (a.node_offsets[mid] <= v) lo = mid; else hi = mid;
+__global__ __launch_bounds__(kSliceThreads) void vocab_stats_kernel(VocabArgs a) {
+  constexpr int EPU = 16 / sizeof(LT);
+  constexpr int U = kSliceUnits;
+  __shared__ __attribute__((aligned(16))) float part[U * kSliceThreads];
+  __shared__ float red_f[kSW];
+  __shared__ double red_d[kSW];
+  __shared__ int cnt_s, kc_s, ks_s, err_s, smask_s;
+  __shared__ int kid_i[kRecKidsMax], kid_t[kRecKidsMax];
+  const int v = blockIdx.x / a.nsl, j = blockIdx.x % a.nsl;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nunits = a.V / EPU;
+  const LT* row = (const LT*)a.logits + (size_t)v * a.V;
+  const int u0 = j * (U * kSliceThreads) + tid;
+  uint4 r[U];
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+    const int u = u0 + k * kSliceThreads;
+    r[k] = *(const uint4*)(row + (size_t)(u < nunits ? u : 0) * EPU);
   }
-  const int b = lo;
-  const int s0 = a.node_offsets[b];
-  const int n = a.node_offsets[b + 1] - s0;
-  const int local = v - s0;
-  if (tid == 0) { n_kids = 0; n_samp = 0; bad_s = 0; pick_chunk = -1; pick_token = -1; }
-  __syncthreads();
-  // children of this node (and a check of the parent array at the same time)
-  uint32_t err = 0;
-  for (int j = tid; j < n; j += kVocabThreads) {
-    const int pj = a.parent[s0 + j];
-    if (j == 0 ? pj != -1 : (pj < 0 || pj >= j)) err |= TAV_DEV_BAD_PARENT;
-    if (j > 0 && pj == local) {
-      const int k = atomicAdd(&n_kids, 1);
-      const uint8_t sj = a.sampled[s0 + j];
-      if (k < kMaxChildren) { kid_id[k] = j; kid_tok[k] = a.token[s0 + j]; kid_smp[k] = sj; }
-      if (sj) atomicAdd(&n_samp, 1);
-    }
-  }
-  __syncthreads();
-  const int nk = min(n_kids, kMaxChildren);
-  if (tid == 0) {
-    if (n_kids > kMaxChildren) err |= TAV_DEV_TOO_MANY_CHILDREN;
-    if (n_samp > 1) err |= TAV_DEV_MULTI_SAMPLED;
-  }
-  if (tid < nk) {
-    const int tk = kid_tok[tid];
-    if (tk < 0 || tk >= V) err |= TAV_DEV_BAD_TOKEN;
-    for (int k = 0; k < tid; ++k)
-      if (kid_tok[k] == tk) err |= TAV_DEV_DUP_SIBLING_TOKEN;
-  }
-  const int dr = a.draft_row[v];
-  const bool has_sampled = n_samp > 0;
-  if (tid == 0 && has_sampled && (dr < 0 || dr >= a.R)) err |= TAV_DEV_NO_DRAFT;
-  const bool use_draft = has_sampled && dr >= 0 && dr < a.R;
+  const int b = block_seq_of(a.node_offsets, a.B, v, &cnt_s);
   const float Tb = a.temperature[b];
-  if (tid == 0 && !(Tb > 0.f && Tb < INFINITY)) err |= TAV_DEV_BAD_TEMPERATURE;
   const float invT = 1.f / Tb;
-
-  // ---- the logits row into registers (19 x 16 bytes per thread), draft DMA started ----
-  const LT* row = (const LT*)a.logits + (size_t)v * V;
-  uint4 r[SLOTS];
-#pragma unroll
-  for (int i = 0; i < SLOTS; ++i) {
-    const int e0 = (i * kVocabThreads + tid) * EPU;
-    r[i] = *(const uint4*)(row + (e0 < V ? e0 : 0));
-  }
-  const float* drow = a.draft + (size_t)(use_draft ? dr : 0) * V;
-  // draft slot i of this thread: elements e0 .. e0+EPU-1, copied to stage i % kDraftStages
-  // at [j][wave][lane] (16 bytes each); every lane issues every copy (addresses clamped
-  // inside the row) so the per-wave count of outstanding copies is exact
-  auto issue_draft = [&](int i) {
-    const int e0 = (i * kVocabThreads + tid) * EPU;
-    const float* src = drow + (e0 < V ? e0 : 0);
-#pragma unroll
-    for (int j = 0; j < DPS; ++j)
-      dma16(src + 4 * j, dstage[i % kDraftStages] + (j * kWaves + wave) * 1024);
-  };
-  if (use_draft) {
-#pragma unroll
-    for (int i = 0; i < kDraftStages - 1; ++i) issue_draft(i);
-  }
-
-  // ---- pass 1: M = max l/T, S = sum exp(l/T - M) ----
-  float mx = -INFINITY;
-  int nonfinite = 0;
-#pragma unroll
-  for (int i = 0; i < SLOTS; ++i) {
-    const int e0 = (i * kVocabThreads + tid) * EPU;
-    if (e0 < V) {
-#pragma unroll
-      for (int e = 0; e < EPU; ++e) {
-        const float z = unit_elem<LT>(r[i], e) * invT;
-        nonfinite |= (z != z) | (z == INFINITY);
-        mx = fmaxf(mx, z);
+  if (j == 0) {   // the node's record
+    const int s0 = a.node_offsets[b];
+    const int n = a.node_offsets[b + 1] - s0;
+    if (tid == 0) { kc_s = 0; ks_s = 0; err_s = 0; smask_s = 0; }
+    __syncthreads();
+    uint32_t err = 0;
+    for (int c = tid; c < n; c += kSliceThreads) {
+      const int pc = a.parent[s0 + c];
+      if (c == 0 ? pc != -1 : (pc < 0 || pc >= c)) err |= TAV_DEV_BAD_PARENT;
+      if (c > 0 && pc == v - s0) {
+        const int k = atomicAdd(&kc_s, 1);
+        const bool smp = a.sampled[s0 + c] != 0;
+        if (smp) atomicAdd(&ks_s, 1);
+        if (k < kRecKidsMax) {
+          kid_i[k] = c;
+          kid_t[k] = a.token[s0 + c];
+          if (smp) atomicOr(&smask_s, 1 << k);
+        }
       }
     }
+    if (tid == 0 && !(Tb > 0.f && Tb < INFINITY)) err |= TAV_DEV_BAD_TEMPERATURE;
+    if (err) atomicOr(&err_s, (int)err);
+    __syncthreads();
+    int32_t* rec = a.rec + (size_t)v * kRecWords;
+    const int nk = kc_s < kRecKidsMax ? kc_s : kRecKidsMax;
+    if (tid < kRecKidsMax) {
+      rec[kRecKidId + tid] = tid < nk ? kid_i[tid] : -1;
+      rec[kRecKidTok + tid] = tid < nk ? kid_t[tid] : -1;
+    }
+    if (tid == 0) {
+      rec[kRecSeq] = b; rec[kRecS0] = s0; rec[kRecN] = n; rec[kRecKids] = kc_s;
+      rec[kRecSampled] = ks_s; rec[kRecInvT] = __float_as_int(invT); rec[kRecErr] = err_s;
+      rec[kRecSmpMask] = smask_s;
+      const int dr = a.draft_row[v];
+      if (ks_s > 0 && dr >= 0 && dr < a.R) a.dlist[atomicAdd(a.dcount, 1)] = v;
+    }
   }
-  if (nonfinite) err |= TAV_DEV_NONFINITE_LOGITS;
+  // largest raw logit (max l / T = (max l) / T for T > 0)
+  float mx = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+    if (u0 + k * kSliceThreads < nunits) {
+#pragma unroll
+      for (int e = 0; e < EPU; ++e) mx = fmaxf(mx, unit_elem<LT>(r[k], e));
+    }
+  }
   mx = wave_max_f(mx);
   if (lane == 0) red_f[wave] = mx;
   __syncthreads();
-  float M = red_f[0];
+  float m = red_f[0];
 #pragma unroll
-  for (int w = 1; w < kWaves; ++w) M = fmaxf(M, red_f[w]);
-  if (M == -INFINITY) {  // every logit is -inf: the row has no mass
-    err |= TAV_DEV_NONFINITE_LOGITS;
-    M = 0.f;
-  }
-  const float Ml2 = M * kLog2e;
+  for (int w = 1; w < kSW; ++w) m = fmaxf(m, red_f[w]);
   const float invTl2 = invT * kLog2e;
+  const float r2 = ref_l2(m, invT);
+  // a NaN or +inf logit makes the sum NaN; the pick kernel reports it
+  float su[U];
   double sl = 0.0;
 #pragma unroll
-  for (int i = 0; i < SLOTS; ++i) {
-    const int e0 = (i * kVocabThreads + tid) * EPU;
-    if (e0 < V) {
-      float su = 0.f;
+  for (int k = 0; k < U; ++k) {
+    su[k] = 0.f;
+    if (u0 + k * kSliceThreads < nunits) {
 #pragma unroll
-      for (int e = 0; e < EPU; ++e) su += __builtin_amdgcn_exp2f(unit_elem<LT>(r[i], e) * invTl2 - Ml2);
-      sl += (double)su;
+      for (int e = 0; e < EPU; ++e) su[k] += __builtin_amdgcn_exp2f(unit_elem<LT>(r[k], e) * invTl2 - r2);
     }
+    sl += (double)su[k];
   }
+  const float ct = chunk_totals<U>(su, part);
+  const int c = j * kChunksPerSlice + (tid * U) / 64;
+  if ((tid % (64 / U)) == 0 && c < a.nch) a.ch_w[(size_t)v * a.nch + c] = ct;
   sl = wave_sum_d(sl);
   if (lane == 0) red_d[wave] = sl;
   __syncthreads();
-  double S = 0.0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) S += red_d[w];
-  const float invS = (float)(1.0 / S);
-
-  // ---- pass 2: final-draw weights w = (p - q~)+ or p, per-chunk sums, Z ----
-  double zl = 0.0;
-#pragma unroll
-  for (int i = 0; i < SLOTS; ++i) {
-    float q[EPU];
-    if (use_draft) {
-      const int after = (SLOTS - 1 - i) < (kDraftStages - 2) ? (SLOTS - 1 - i) : (kDraftStages - 2);
-      if (after >= 2) wait_vm<2 * DPS>();
-      else if (after == 1) wait_vm<DPS>();
-      else wait_vm<0>();
-#pragma unroll
-      for (int j = 0; j < DPS; ++j) {
-        const float4 t = *(const float4*)(dstage[i % kDraftStages] + (j * kWaves + wave) * 1024 + lane * 16);
-        q[4 * j + 0] = t.x; q[4 * j + 1] = t.y; q[4 * j + 2] = t.z; q[4 * j + 3] = t.w;
-      }
-      if (i + kDraftStages - 1 < SLOTS) issue_draft(i + kDraftStages - 1);
-    }
-    const int e0 = (i * kVocabThreads + tid) * EPU;
-    float ws = 0.f;
-    if (e0 < V) {
-#pragma unroll
-      for (int e = 0; e < EPU; ++e) {
-        const float p = __builtin_amdgcn_exp2f(unit_elem<LT>(r[i], e) * invTl2 - Ml2) * invS;
-        ws += use_draft ? fmaxf(0.f, p - q[e]) : p;
-      }
-    }
-    zl += (double)ws;
-    ws = wave_sum_f(ws);
-    if (lane == 0) csum[i * kWaves + wave] = ws;
-  }
-  zl = wave_sum_d(zl);
-  __syncthreads();
-  if (lane == 0) red_d[wave] = zl;
-
-  // the children's own point values for the walk, and their removal from the final draw
-  auto weight_of = [&](float p, int tok) -> float { return use_draft ? fmaxf(0.f, p - drow[tok]) : p; };
-  if (tid < nk) {
-    const int tok = kid_tok[tid];
-    const int c = kid_id[tid];
-    if (tok >= 0 && tok < V) {
-      const float z = logit_at<LT>(a.logits, (size_t)v * V + tok);
-      a.child_p[s0 + c] = exp((double)(z * invT) - (double)M) / S;
-      a.child_q[s0 + c] = use_draft ? drow[tok] : 0.f;
-      if (!kid_smp[tid]) {
-        const float p = __builtin_amdgcn_exp2f(z * invTl2 - Ml2) * invS;
-        const int unit = tok / EPU;
-        atomicAdd(&csum[(unit / kVocabThreads) * kWaves + (unit % kVocabThreads) / 64], -weight_of(p, tok));
-      }
-    }
-  }
-  __syncthreads();
-  double Zt = 0.0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) Zt += red_d[w];
-  const float Z = use_draft ? (float)Zt : 0.f;
-
-  // locate the chunk of the final draw: wave 0 scans the NCH chunk sums
-  if (wave == 0) {
-    constexpr int PER = (NCH + 63) / 64;
-    double part = 0.0;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int c = lane * PER + k;
-      if (c < NCH) part += (double)fmaxf(csum[c], 0.f);
-    }
-    double incl = part;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const double y = __shfl_up(incl, d, 64);
-      if (lane >= d) incl += y;
-    }
-    const double W = __shfl(incl, 63);
-    if (W > 0.0) {
-      const double target = (double)a.uniforms[(size_t)v * 2 + 1] * W;
-      const unsigned long long hit = __ballot(incl > target && part > 0.0);
-      int L0;
-      if (hit) L0 = __ffsll((long long)hit) - 1;
-      else {
-        const unsigned long long has = __ballot(part > 0.0);
-        L0 = 63 - __clzll((long long)has);
-      }
-      if (lane == L0) {
-        double cum = incl - part;
-        int cfound = -1, clast = -1;
-        for (int k = 0; k < PER; ++k) {
-          const int c = lane * PER + k;
-          if (c >= NCH) break;
-          const double cs = (double)fmaxf(csum[c], 0.f);
-          if (cs > 0.0) {
-            clast = c;
-            if (cfound < 0 && cum + cs > target) { cfound = c; break; }
-          }
-          cum += cs;
-        }
-        if (cfound < 0) {  // rounding put the target past the total: last chunk with mass
-          cfound = clast;
-          cum -= (double)fmaxf(csum[clast], 0.f);
-        }
-        pick_chunk = cfound;
-        pick_rem = (float)(target - cum);
-      }
-    }
-  }
-  __syncthreads();
-  const int pc = pick_chunk;
-  if (pc >= 0 && wave == pc % kWaves) {
-    const int slot = pc / kWaves;
-    float wv[EPU];
-    float lsum = 0.f;
-#pragma unroll
-    for (int i = 0; i < SLOTS; ++i) {
-      if (i == slot) {
-        const int e0 = (i * kVocabThreads + tid) * EPU;
-#pragma unroll
-        for (int e = 0; e < EPU; ++e) {
-          float w = 0.f;
-          if (e0 + e < V) {
-            const float p = __builtin_amdgcn_exp2f(unit_elem<LT>(r[i], e) * invTl2 - Ml2) * invS;
-            w = weight_of(p, e0 + e);
-            for (int k = 0; k < nk; ++k)
-              if (kid_tok[k] == e0 + e && !kid_smp[k]) w = 0.f;
-          }
-          wv[e] = w;
-          lsum += w;
-        }
-      }
-    }
-    float incl = lsum;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const float y = __shfl_up(incl, d, 64);
-      if (lane >= d) incl += y;
-    }
-    const float rem = pick_rem;
-    const unsigned long long hit = __ballot(incl > rem && lsum > 0.f);
-    int chosen;
-    if (hit) chosen = __ffsll((long long)hit) - 1;
-    else {
-      const unsigned long long has = __ballot(lsum > 0.f);
-      chosen = has ? 63 - __clzll((long long)has) : -1;
-    }
-    if (lane == chosen) {
-      float cum = incl - lsum;
-      int tok = -1, lastpos = -1;
-      const int e0 = (slot * kVocabThreads + tid) * EPU;
-#pragma unroll
-      for (int e = 0; e < EPU; ++e) {
-        if (wv[e] > 0.f) lastpos = e0 + e;
-        cum += wv[e];
-        if (tok < 0 && wv[e] > 0.f && cum > rem) tok = e0 + e;
-      }
-      pick_token = tok >= 0 ? tok : lastpos;
-    }
-  }
-  if (err) atomicOr(&bad_s, (int)err);
-  __syncthreads();
   if (tid == 0) {
-    a.stats[(size_t)v * 3 + 0] = M;
-    a.stats[(size_t)v * 3 + 1] = (float)S;
-    a.stats[(size_t)v * 3 + 2] = Z;
-    a.term_token[v] = pick_token;
-    if (bad_s) atomicOr(a.status, (uint32_t)bad_s);
+    double s = 0.0;
+#pragma unroll
+    for (int w = 0; w < kSW; ++w) s += red_d[w];
+    a.sl_m[(size_t)v * a.nsl + j] = m;
+    a.sl_s[(size_t)v * a.nsl + j] = s;
   }
 }
 
-constexpr int kWalkLds = 2048;  // nodes whose walk data fit in LDS
+// Residual weights (p - q~)+ of the listed rows (nodes with a sampled child): p from the row
+// statistics, q~ from the node's draft row.  Overwrites the row's chunk sums with those of
+// (p - q~)+ and writes each half slice's sum of (p - q~)+ (fp32 per lane, fp64 across lanes).
+// A grid-stride loop over (listed row, half slice), rows taken from the end of the list
+// (the most recently read logits rows first); the list length is read on the device.
+template <typename LT>
+__global__ __launch_bounds__(kSliceThreads) void vocab_residual_kernel(VocabArgs a) {
+  constexpr int EPU = 16 / sizeof(LT);
+  constexpr int U = kResUnits;
+  __shared__ __attribute__((aligned(16))) float part[U * kSliceThreads];
+  __shared__ double red_d[kSW];
+  __shared__ float m_s[kMaxSlices];
+  __shared__ double s_s[kMaxSlices];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nunits = a.V / EPU;
+  const int nh = 2 * a.nsl;
+  const int cnt = *a.dcount;
+  for (int item = blockIdx.x; item < cnt * nh; item += gridDim.x) {
+    const int v = a.dlist[cnt - 1 - item / nh], h = item % nh;
+    const LT* row = (const LT*)a.logits + (size_t)v * a.V;
+    const float* drow = a.draft + (size_t)a.draft_row[v] * a.V;
+    const int u0 = h * (U * kSliceThreads) + tid;
+    uint4 r[U];
+    float4 q[U][EPU / 4];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const int u = u0 + k * kSliceThreads;
+      const size_t e0 = (size_t)(u < nunits ? u : 0) * EPU;
+      r[k] = *(const uint4*)(row + e0);
+#pragma unroll
+      for (int i = 0; i < EPU / 4; ++i) q[k][i] = *(const float4*)(drow + e0 + 4 * i);
+    }
+    const float invT = __int_as_float(a.rec[(size_t)v * kRecWords + kRecInvT]);
+    const RowStats st = row_stats_block(a.sl_m + (size_t)v * a.nsl, a.sl_s + (size_t)v * a.nsl, a.nsl,
+                                        invT, m_s, s_s);
+    const float invTl2 = invT * kLog2e;
+    float wu[U];
+    double zl = 0.0;
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      wu[k] = 0.f;
+      if (u0 + k * kSliceThreads < nunits) {
+#pragma unroll
+        for (int e = 0; e < EPU; ++e) {
+          const float4 q4 = q[k][e / 4];
+          const float qe = (e & 3) == 0 ? q4.x : (e & 3) == 1 ? q4.y : (e & 3) == 2 ? q4.z : q4.w;
+          const float p = __builtin_amdgcn_exp2f(unit_elem<LT>(r[k], e) * invTl2 - st.Ml2) * st.invS;
+          wu[k] += fmaxf(0.f, p - qe);
+        }
+      }
+      zl += (double)wu[k];
+    }
+    const float ct = chunk_totals<U>(wu, part);
+    const int c = h * kChunksPerHalf + (tid * U) / 64;
+    if ((tid % (64 / U)) == 0 && c < a.nch) a.ch_w[(size_t)v * a.nch + c] = ct;
+    zl = wave_sum_d(zl);
+    if (lane == 0) red_d[wave] = zl;
+    __syncthreads();
+    if (tid == 0) {
+      double z = 0.0;
+#pragma unroll
+      for (int w = 0; w < kSW; ++w) z += red_d[w];
+      a.sl_z[(size_t)v * nh + h] = z;
+    }
+    __syncthreads();   // LDS reused by the next item
+  }
+}
+
+// Per node, one wave: the children's point values p(token) / q~(token) for the walk, the row
+// statistics (M, S, Z), the checks, and the token the final draw would give if the walk ended
+// here: chunk weights (scaled to p, or the residual weights) less the deterministic children's
+// own weights, an fp64 scan over chunks for u * W, then one chunk re-read and scanned.
+template <typename LT>
+__global__ __launch_bounds__(kSliceThreads) void vocab_pick_kernel(VocabArgs a) {
+  constexpr int EPU = 16 / sizeof(LT);
+  constexpr int CT = 64 * EPU;   // tokens per chunk
+  __shared__ float cw_all[kSW][kMaxChunks];
+  __shared__ int kid_id_all[kSW][kMaxChildren];
+  __shared__ int kid_tok_all[kSW][kMaxChildren];
+  __shared__ uint8_t kid_smp_all[kSW][kMaxChildren];
+  __shared__ int cnt_all[kSW][2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int v = blockIdx.x * kSW + wave;
+  if (v >= a.N) return;   // the wave's node; no workgroup barrier is used below
+  float* cw = cw_all[wave];
+  int* kid_id = kid_id_all[wave];
+  int* kid_tok = kid_tok_all[wave];
+  uint8_t* kid_smp = kid_smp_all[wave];
+  const int V = a.V, nch = a.nch, nsl = a.nsl;
+  // ---- everything indexed by the node alone ----
+  const int32_t* rec = a.rec + (size_t)v * kRecWords;
+  const int rv = lane < kRecWords ? rec[lane] : 0;
+  const int dr = a.draft_row[v];
+  float ml = -INFINITY;
+  double sl = 0.0, zl = 0.0;
+  for (int j = lane; j < nsl; j += 64) {
+    ml = a.sl_m[(size_t)v * nsl + j];   // (lane's last slice; nsl <= 64 keeps one per lane)
+    sl = a.sl_s[(size_t)v * nsl + j];
+    zl += a.sl_z[(size_t)v * 2 * nsl + 2 * j] + a.sl_z[(size_t)v * 2 * nsl + 2 * j + 1];
+  }
+  for (int c0 = 0; c0 < nch; c0 += 8 * 64) {   // eight loads in flight per lane
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = c0 + i * 64 + lane;
+      x[i] = c < nch ? a.ch_w[(size_t)v * nch + c] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = c0 + i * 64 + lane;
+      if (c < nch) cw[c] = x[i];
+    }
+  }
+  const int s0 = __shfl(rv, kRecS0), nkids = __shfl(rv, kRecKids), nsamp = __shfl(rv, kRecSampled);
+  const float invT = __int_as_float(__shfl(rv, kRecInvT));
+  uint32_t err = (uint32_t)__shfl(rv, kRecErr);
+  const int smask = __shfl(rv, kRecSmpMask);
+  const float invTl2 = invT * kLog2e;
+  // row statistics (nsl <= 64: one slice per lane)
+  const float Mraw = wave_max_f(ml);
+  const float Ml2r = (Mraw == -INFINITY ? 0.f : Mraw * invT) * kLog2e;
+  const double sc = (sl != 0.0) ? sl * exp2((double)ref_l2(ml, invT) - (double)Ml2r) : 0.0;
+  const RowStats st = finish_stats(Mraw, wave_sum_d(sc), invT);
+  const double Zt = wave_sum_d(zl);
+  const bool dr_ok = dr >= 0 && dr < a.R;
+  const bool use_draft = nsamp > 0 && dr_ok;
+  if (nkids > kMaxChildren) err |= TAV_DEV_TOO_MANY_CHILDREN;
+  if (nsamp > 1) err |= TAV_DEV_MULTI_SAMPLED;
+  if (nsamp > 0 && !dr_ok) err |= TAV_DEV_NO_DRAFT;
+  if (st.no_mass || !(st.S > 0.0 && st.S < INFINITY)) err |= TAV_DEV_NONFINITE_LOGITS;
+  // children: from the record, or (more than it holds) a scan of the parent array
+  int nk;
+  if (nkids <= kRecKidsMax) {
+    nk = nkids;
+    const int kid_i = __shfl(rv, kRecKidId + (lane < kRecKidsMax ? lane : 0));
+    const int kid_t = __shfl(rv, kRecKidTok + (lane < kRecKidsMax ? lane : 0));
+    if (lane < nk) { kid_id[lane] = kid_i; kid_tok[lane] = kid_t; kid_smp[lane] = (smask >> lane) & 1; }
+  } else {
+    const int n = __shfl(rv, kRecN);
+    nk = 0;
+    for (int base = 1; base < n; base += 64) {
+      const int c = base + lane;
+      const bool is_kid = c < n && a.parent[s0 + c] == v - s0;
+      const unsigned long long m = __ballot(is_kid);
+      if (is_kid) {
+        const int at = nk + __popcll(m & ((1ull << lane) - 1ull));
+        if (at < kMaxChildren) { kid_id[at] = c; kid_tok[at] = a.token[s0 + c]; kid_smp[at] = a.sampled[s0 + c]; }
+      }
+      nk += __popcll(m);
+    }
+    nk = nk < kMaxChildren ? nk : kMaxChildren;
+  }
+  wave_sync();
+  // non-draft rows: chunk sums relative to their slice -> p
+  if (!use_draft) {
+    for (int c = lane; c < nch; c += 64) {
+      const int jj = c / kChunksPerSlice;
+      const float mj = __shfl(ml, jj);
+      cw[c] = cw[c] * __builtin_amdgcn_exp2f(ref_l2(mj, invT) - st.Ml2) * st.invS;
+    }
+  }
+  wave_sync();
+  // children: point values for the walk; deterministic children leave the final draw
+  for (int k = lane; k < nk; k += 64) {
+    const int tk = kid_tok[k];
+    if (tk < 0 || tk >= V) err |= TAV_DEV_BAD_TOKEN;
+    for (int k2 = 0; k2 < k; ++k2)
+      if (kid_tok[k2] == tk) err |= TAV_DEV_DUP_SIBLING_TOKEN;
+    if (tk >= 0 && tk < V) {
+      const float z = logit_at<LT>(a.logits, (size_t)v * V + tk);
+      const float qz = dr_ok ? a.draft[(size_t)dr * V + tk] : 0.f;
+      const int cid = s0 + kid_id[k];
+      a.child_p[cid] = exp((double)(z * invT) - (double)st.M) / st.S;
+      a.child_q[cid] = use_draft ? qz : 0.f;
+      if (!kid_smp[k]) {
+        const float p = __builtin_amdgcn_exp2f(z * invTl2 - st.Ml2) * st.invS;
+        atomicAdd(&cw[tk / CT], -(use_draft ? fmaxf(0.f, p - qz) : p));
+      }
+    }
+  }
+  wave_sync();
+  // fp64 scan over chunks: lane l owns chunks [l * per, (l + 1) * per)
+  const int per = (nch + 63) / 64;
+  double part = 0.0;
+  for (int k = 0; k < per; ++k) {
+    const int c = lane * per + k;
+    if (c < nch) part += (double)fmaxf(cw[c], 0.f);
+  }
+  double incl = part;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const double y = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += y;
+  }
+  const double W = __shfl(incl, 63);
+  const double target = (double)a.uniforms[(size_t)v * 2 + 1] * W;
+  int tok = -1;
+  if (W > 0.0) {
+    const unsigned long long hit = __ballot(part > 0.0 && incl > target);
+    const unsigned long long has = __ballot(part > 0.0);
+    const int owner = hit ? __ffsll((long long)hit) - 1 : 63 - __clzll((long long)has);
+    int pc = -1;
+    double rem = 0.0;
+    if (lane == owner) {
+      double cum = incl - part, cum_l = 0.0;
+      int cl = -1;
+      for (int k = 0; k < per; ++k) {
+        const int c = lane * per + k;
+        if (c >= nch) break;
+        const double cs = (double)fmaxf(cw[c], 0.f);
+        if (cs > 0.0) {
+          cl = c; cum_l = cum;
+          if (pc < 0 && cum + cs > target) { pc = c; break; }
+        }
+        cum += cs;
+      }
+      if (pc < 0) { pc = cl; cum = cum_l; }   // rounding past the total: last chunk with mass
+      rem = target - cum;
+    }
+    pc = __shfl(pc, owner);
+    rem = __shfl(rem, owner);
+    // the final draw inside the chosen chunk
+    const int e0 = pc * CT + lane * EPU;
+    const bool in = e0 < V;
+    const uint4 ru = *(const uint4*)((const LT*)a.logits + (size_t)v * V + (in ? e0 : 0));
+    float qv[EPU];
+    if (use_draft) {
+#pragma unroll
+      for (int i = 0; i < EPU / 4; ++i) {
+        const float4 t = *(const float4*)(a.draft + (size_t)dr * V + (in ? e0 : 0) + 4 * i);
+        qv[4 * i + 0] = t.x; qv[4 * i + 1] = t.y; qv[4 * i + 2] = t.z; qv[4 * i + 3] = t.w;
+      }
+    }
+    float w[EPU];
+    float lsum = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPU; ++e) {
+      float x = 0.f;
+      if (in) {
+        const float p = __builtin_amdgcn_exp2f(unit_elem<LT>(ru, e) * invTl2 - st.Ml2) * st.invS;
+        x = use_draft ? fmaxf(0.f, p - qv[e]) : p;
+        for (int k = 0; k < nk; ++k)
+          if (kid_tok[k] == e0 + e && !kid_smp[k]) x = 0.f;
+      }
+      w[e] = x;
+      lsum += x;
+    }
+    float inc = lsum;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const float y = __shfl_up(inc, d, 64);
+      if (lane >= d) inc += y;
+    }
+    const float remf = (float)rem;
+    const unsigned long long hit2 = __ballot(inc > remf && lsum > 0.f);
+    const unsigned long long has2 = __ballot(lsum > 0.f);
+    const int chosen = hit2 ? __ffsll((long long)hit2) - 1 : (has2 ? 63 - __clzll((long long)has2) : -1);
+    int mine = -1;
+    if (lane == chosen) {
+      float cum = inc - lsum;
+      int lastpos = -1;
+#pragma unroll
+      for (int e = 0; e < EPU; ++e) {
+        if (w[e] > 0.f) lastpos = e0 + e;
+        cum += w[e];
+        if (mine < 0 && w[e] > 0.f && cum > remf) mine = e0 + e;
+      }
+      if (mine < 0) mine = lastpos;
+    }
+    tok = chosen >= 0 ? __shfl(mine, chosen) : -1;
+  }
+  // status bits of any lane
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) err |= (uint32_t)__shfl_xor((int)err, d);
+  if (lane == 0) {
+    a.stats[(size_t)v * 3 + 0] = st.M;
+    a.stats[(size_t)v * 3 + 1] = (float)st.S;
+    a.stats[(size_t)v * 3 + 2] = use_draft ? (float)Zt : 0.f;
+    a.term_token[v] = tok;
+    if (err) atomicOr(a.status, err);
+  }
+}
+
+constexpr int kWalkLds = 1024;  // nodes whose walk data fit in LDS
 
 // One wave per sequence: the layer-by-layer walk, decisions in fp64 from the values the
-// vocabulary kernel left: p(token) and q~(token) of every child, Z and the final draw of
-// every node.  Sequences of up to 2048 nodes are staged in LDS first.
+// vocabulary kernels left: p(token) and q~(token) of every child, Z and the final draw of
+// every node.  For sequences of up to kWalkLds nodes these values, the parents and the
+// sampled flags are first staged in LDS (one round of loads).
 __global__ __launch_bounds__(64) void walk_kernel(WalkArgs a) {
   __shared__ int par_s[kWalkLds];
   __shared__ uint8_t smp_s[kWalkLds];
+  __shared__ double cp_s[kWalkLds];
+  __shared__ float cq_s[kWalkLds];
+  __shared__ float u_s[kWalkLds];
+  __shared__ float z_s[kWalkLds];
+  __shared__ int tt_s[kWalkLds];
   __shared__ int kids[kMaxChildren];
   const int b = blockIdx.x, lane = threadIdx.x;
   const int s0 = a.node_offsets[b];
@@ -393,9 +572,22 @@ __global__ __launch_bounds__(64) void walk_kernel(WalkArgs a) {
   const bool staged = n <= kWalkLds;
   for (int j = lane; j < n; j += 64) {
     a.node_status[s0 + j] = 0;
-    if (staged) { par_s[j] = a.parent[s0 + j]; smp_s[j] = a.sampled[s0 + j]; }
+    if (staged) {
+      par_s[j] = a.parent[s0 + j];
+      smp_s[j] = a.sampled[s0 + j];
+      cp_s[j] = a.child_p[s0 + j];
+      cq_s[j] = a.child_q[s0 + j];
+      u_s[j] = a.uniforms[(size_t)(s0 + j) * 2];
+      z_s[j] = a.stats[(size_t)(s0 + j) * 3 + 2];
+      tt_s[j] = a.term_token[s0 + j];
+    }
   }
   for (int j = lane; j < a.max_path; j += 64) a.path[(size_t)b * a.max_path + j] = -1;
+  auto parent_of = [&](int j) { return staged ? par_s[j] : a.parent[s0 + j]; };
+  auto sampled_of = [&](int j) { return staged ? (int)smp_s[j] : (int)a.sampled[s0 + j]; };
+  auto p_of = [&](int j) { return staged ? cp_s[j] : a.child_p[s0 + j]; };
+  auto q_of = [&](int j) { return (double)(staged ? cq_s[j] : a.child_q[s0 + j]); };
+  auto u_of = [&](int j) { return (double)(staged ? u_s[j] : a.uniforms[(size_t)(s0 + j) * 2]); };
   __syncthreads();
   uint32_t err = 0;
   int plen = 1, v = 0, bonus = -1;
@@ -408,13 +600,13 @@ __global__ __launch_bounds__(64) void walk_kernel(WalkArgs a) {
     int nk = 0, s = -1;
     for (int base = 1; base < n; base += 64) {
       const int j = base + lane;
-      const int pj = j < n ? (staged ? par_s[j] : a.parent[s0 + j]) : -2;
+      const int pj = j < n ? parent_of(j) : -2;
       const bool is_kid = pj == v;
       const unsigned long long m = __ballot(is_kid);
       if (is_kid) {
         const int at = nk + __popcll(m & ((1ull << lane) - 1ull));
         if (at < kMaxChildren) kids[at] = j;
-        if (staged ? smp_s[j] : a.sampled[s0 + j]) s = j;
+        if (sampled_of(j)) s = j;
       }
       nk += __popcll(m);
     }
@@ -425,14 +617,14 @@ __global__ __launch_bounds__(64) void walk_kernel(WalkArgs a) {
     int next = -1;
     if (lane == 0) {
       bool resid = false;
-      const double Zv = (double)a.stats[(size_t)(s0 + v) * 3 + 2];
+      const double Zv = (double)(staged ? z_s[v] : a.stats[(size_t)(s0 + v) * 3 + 2]);
       if (s >= 0) {
-        const double qs = (double)a.child_q[s0 + s];
+        const double qs = q_of(s);
         if (!(qs > 0.0)) {
           err |= TAV_DEV_ZERO_DRAFT_MASS;
         } else {
-          const double ratio = fmin(1.0, a.child_p[s0 + s] / qs);
-          if ((double)a.uniforms[(size_t)(s0 + s) * 2] <= ratio) {
+          const double ratio = fmin(1.0, p_of(s) / qs);
+          if (u_of(s) <= ratio) {
             next = s;
           } else {
             a.node_status[s0 + s] = 2;
@@ -445,11 +637,11 @@ __global__ __launch_bounds__(64) void walk_kernel(WalkArgs a) {
         for (int k = 0; k < nk && next < 0; ++k) {
           const int c = kids[k];
           if (c == s) continue;
-          const double p = a.child_p[s0 + c];
-          const double r0 = resid ? (Zv > 0.0 ? fmax(0.0, p - (double)a.child_q[s0 + c]) / Zv : 0.0) : p;
+          const double p = p_of(c);
+          const double r0 = resid ? (Zv > 0.0 ? fmax(0.0, p - q_of(c)) / Zv : 0.0) : p;
           const double rem = 1.0 - rej;
           const double rc = rem > 0.0 ? r0 / rem : 0.0;
-          if ((double)a.uniforms[(size_t)(s0 + c) * 2] <= rc) {
+          if (u_of(c) <= rc) {
             next = c;
           } else {
             a.node_status[s0 + c] = 2;
@@ -463,7 +655,7 @@ __global__ __launch_bounds__(64) void walk_kernel(WalkArgs a) {
         else a.path[(size_t)b * a.max_path + plen] = next;
         ++plen;
       } else if (!err) {
-        bonus = a.term_token[s0 + v];
+        bonus = staged ? tt_s[v] : a.term_token[s0 + v];
         if (bonus < 0) err |= TAV_DEV_EMPTY_RESIDUAL;
       }
     }
@@ -480,12 +672,26 @@ __global__ __launch_bounds__(64) void walk_kernel(WalkArgs a) {
   }
 }
 
+template <typename LT>
+void launch_vocab_t(const VocabArgs& a, int num_cus, hipStream_t s) {
+  static int per_cu = 0;   // resident residual workgroups per CU
+  if (per_cu == 0 &&
+      (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, vocab_residual_kernel<LT>, kSliceThreads, 0) !=
+           hipSuccess || per_cu < 1))
+    per_cu = 1;
+  const int g1 = a.N * a.nsl;
+  const int g2 = 2 * g1 < per_cu * num_cus ? 2 * g1 : per_cu * num_cus;
+  vocab_stats_kernel<LT><<<g1, kSliceThreads, 0, s>>>(a);
+  vocab_residual_kernel<LT><<<g2, kSliceThreads, 0, s>>>(a);
+  vocab_pick_kernel<LT><<<ceil_div(a.N, kSW), kSliceThreads, 0, s>>>(a);
+}
+
 }  // namespace
 
-hipError_t launch_vocab(const VocabArgs& a, bool bf16_logits, hipStream_t s) {
+hipError_t launch_vocab(const VocabArgs& a, bool bf16_logits, int num_cus, hipStream_t s) {
   if (a.N == 0) return hipSuccess;
-  if (bf16_logits) vocab_kernel<uint16_t><<<a.N, kVocabThreads, 0, s>>>(a);
-  else vocab_kernel<float><<<a.N, kVocabThreads, 0, s>>>(a);
+  if (bf16_logits) launch_vocab_t<uint16_t>(a, num_cus, s);
+  else launch_vocab_t<float>(a, num_cus, s);
   return hipGetLastError();
 }
 

@@ -169,6 +169,17 @@ tav_status make_plan(const tav_problem* p, const tav_presto_io* pr, Plan* out) {
   P.off_child_p = o; o = align_up(o + (size_t)P.N * 8);
   P.off_child_q = o; o = align_up(o + (size_t)P.N * 4);
   P.off_presto = o; o = align_up(o + (size_t)(pr ? pr->num_requests : 0) * 8);
+  if (p->vocab > 0) {
+    const int epu = p->dtype == TAV_BF16 ? 8 : 4;
+    P.nsl = ceil_div(p->vocab, kSliceThreads * kSliceUnits * epu);
+    P.nch = ceil_div(ceil_div(p->vocab, epu), 64);
+  }
+  P.off_sl_m = o; o = align_up(o + (size_t)P.N * P.nsl * 4);
+  P.off_sl_s = o; o = align_up(o + (size_t)P.N * P.nsl * 8);
+  P.off_sl_z = o; o = align_up(o + (size_t)P.N * P.nsl * 2 * 8);
+  P.off_ch_w = o; o = align_up(o + (size_t)P.N * P.nch * 4);
+  P.off_dlist = o; o = align_up(o + (size_t)P.N * 4);
+  P.off_rec = o; o = align_up(o + (size_t)(p->vocab > 0 ? P.N : 0) * kRecWords * 4);
   P.total = o;
   *out = P;
   return TAV_OK;
@@ -217,11 +228,11 @@ tav_status check_verify(const tav_problem* p, const tav_verify_io* io) {
   if (io->max_path < 1) return fail(TAV_ERR_BAD_SHAPE, "max_path must be >= 1");
   if (p->vocab < 1) return fail(TAV_ERR_BAD_SHAPE, "vocab must be >= 1 for verification");
   const int epu = p->dtype == TAV_BF16 ? 8 : 4;
-  const int64_t cap = (int64_t)kVocabThreads * kVocabSlots * epu;
+  const int64_t cap = (int64_t)kMaxSlices * kSliceThreads * kSliceUnits * epu;
   if (p->vocab % epu)
     return fail(TAV_ERR_UNSUPPORTED, "vocab must be a multiple of %d for this logits dtype (got %d)", epu, p->vocab);
   if (p->vocab > cap)
-    return fail(TAV_ERR_UNSUPPORTED, "vocab %d exceeds the %lld tokens one workgroup holds for this dtype",
+    return fail(TAV_ERR_UNSUPPORTED, "vocab %d exceeds the %lld tokens supported for this dtype",
                 p->vocab, (long long)cap);
   if (!aligned16(io->logits) || !aligned16(io->draft))
     return fail(TAV_ERR_INVALID_ARGUMENT, "logits and draft must be 16-byte aligned");
@@ -284,7 +295,18 @@ tav_status enqueue_verify(const tav_problem* p, const Plan& P, const tav_tree* t
   va.child_p = ws_at<double>(ws, P.off_child_p);
   va.child_q = ws_at<float>(ws, P.off_child_q);
   va.B = P.B; va.N = P.N; va.V = p->vocab; va.R = io->num_draft_rows;
-  TAV_HIP(launch_vocab(va, p->dtype == TAV_BF16, s));
+  va.sl_m = ws_at<float>(ws, P.off_sl_m);
+  va.sl_s = ws_at<double>(ws, P.off_sl_s);
+  va.sl_z = ws_at<double>(ws, P.off_sl_z);
+  va.ch_w = ws_at<float>(ws, P.off_ch_w);
+  va.dlist = ws_at<int32_t>(ws, P.off_dlist);
+  va.rec = ws_at<int32_t>(ws, P.off_rec);
+  va.dcount = (int32_t*)(status + kCounterWord);
+  va.nsl = P.nsl; va.nch = P.nch;
+  int dev = 0, cus = 0;
+  TAV_HIP(hipGetDevice(&dev));
+  TAV_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+  TAV_HIP(launch_vocab(va, p->dtype == TAV_BF16, cus > 0 ? cus : 256, s));
   WalkArgs wa;
   wa.logits = io->logits; wa.temperature = io->temperature; wa.draft = io->draft;
   wa.draft_row = io->draft_row; wa.node_offsets = p->node_offsets; wa.parent = t->parent;

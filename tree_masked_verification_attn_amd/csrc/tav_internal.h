@@ -14,8 +14,13 @@ constexpr int kRowsPerWG = 256;    // query rows (node x head-in-group) per atte
 constexpr int kMaxTreeNodes = 256; // non-chain trees: ancestor sets are 256-bit masks
 constexpr int kMaskWords = 4;
 constexpr int kMaxChildren = 256;  // children of one node held by the verification kernels
-constexpr int kVocabThreads = 1024;
-constexpr int kVocabSlots = 19;    // 16-byte units held in registers per thread
+constexpr int kSliceThreads = 256; // threads of a vocabulary-slice workgroup
+constexpr int kSliceUnits = 8;     // 16-byte units of a row per thread and slice
+constexpr int kMaxSlices = 64;     // slices per vocabulary row (V <= 1 Mi bf16 / 512 Ki f32)
+constexpr int kMaxChunks = kMaxSlices * kSliceUnits * (kSliceThreads / 64);
+constexpr int kRecWords = 32;      // per-node record of the vocabulary kernels (int32 words)
+constexpr int kRecKidsMax = 12;    // children held in the record
+constexpr int kCounterWord = 16;   // status block: word 0 = status bits, word 16 = a counter
 
 // Work decomposition of the attention pass.  A "row block" is up to
 // kRowsPerWG / G consecutive nodes of one sequence; a "work item" is one
@@ -32,7 +37,9 @@ struct Plan {
   // workspace layout (byte offsets)
   size_t off_status = 0, off_chain = 0, off_mask = 0, off_seq_rb = 0, off_rb_seq = 0,
          off_item_off = 0, off_part_o = 0, off_part_lse = 0, off_stats = 0, off_term = 0,
-         off_child_p = 0, off_child_q = 0, off_presto = 0, total = 0;
+         off_child_p = 0, off_child_q = 0, off_presto = 0, off_sl_m = 0, off_sl_s = 0,
+         off_sl_z = 0, off_ch_w = 0, off_dlist = 0, off_rec = 0, total = 0;
+  int nsl = 0, nch = 0;   // vocabulary slices and chunks (64 units) per row
 };
 
 __host__ __device__ static inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -83,7 +90,14 @@ struct VocabArgs {
   double* child_p;       // [N] p of the node's token under its parent's target distribution
   float* child_q;        // [N] q~ of the node's token under its parent's draft row (0 if none)
   uint32_t* status;
-  int B, N, V, R;
+  float* sl_m;           // [N, nsl] largest raw logit of each slice
+  double* sl_s;          // [N, nsl] sum exp2(l * log2e / T - ref) of each slice
+  double* sl_z;          // [N, 2 nsl] sum (p - q~)+ of each half slice (listed rows)
+  float* ch_w;           // [N, nch] chunk sums: of exp2(..) (relative to the slice) or of (p - q~)+
+  int32_t* dlist;        // [N] nodes with a sampled child and a draft row
+  int32_t* rec;          // [N, kRecWords] per-node record (sequence, 1/T, children)
+  int32_t* dcount;       // length of dlist (cleared with the status word)
+  int B, N, V, R, nsl, nch;
 };
 
 struct WalkArgs {
@@ -140,7 +154,7 @@ hipError_t launch_prep(const Plan& p, const int32_t* node_offsets, const int32_t
 hipError_t launch_attn_bf16(const Plan& p, const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_f32(const Plan& p, const AttnArgs& a, hipStream_t s);
 hipError_t launch_merge(const Plan& p, const AttnArgs& a, bool bf16_out, hipStream_t s);
-hipError_t launch_vocab(const VocabArgs& a, bool bf16_logits, hipStream_t s);
+hipError_t launch_vocab(const VocabArgs& a, bool bf16_logits, int num_cus, hipStream_t s);
 hipError_t launch_walk(const WalkArgs& a, hipStream_t s);
 hipError_t launch_presto(const PrestoArgs& a, hipStream_t s);
 

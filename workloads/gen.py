@@ -179,6 +179,11 @@ def chain_parents(n: int) -> np.ndarray:
     return np.arange(-1, n - 1, dtype=np.int32)
 
 
+def star_parents(n: int) -> np.ndarray:
+    """The root and n - 1 children of the root."""
+    return np.array([-1] + [0] * (n - 1), dtype=np.int32)
+
+
 def random_depth_parents(n: int, max_depth: int, rng) -> np.ndarray:
     """Node i picks a depth d uniform in 1..min(max_depth, deepest so far + 1) and a
     parent uniform among the nodes already at depth d-1."""
@@ -328,6 +333,7 @@ def tree_batch(seed: int, *, B: int, prefix_len, tree: str, n_nodes, Hq: int, Hk
     tree: "binary" (complete binary, children 2i+1 sampled / 2i+2 deterministic),
           "random" (random-depth tree, first child of each node sampled),
           "chain"  (a path; no verification decoration beyond the same rule),
+          "star"   (n - 1 children of the root),
           "eagle"  (top-k expand-then-rerank with the Rheo hybrid pool).
     """
     prefix_len = np.asarray(prefix_len, dtype=np.int32).reshape(-1)
@@ -349,6 +355,8 @@ def tree_batch(seed: int, *, B: int, prefix_len, tree: str, n_nodes, Hq: int, Hk
                 par = complete_binary_parents(n)
             elif tree == "chain":
                 par = chain_parents(n)
+            elif tree == "star":
+                par = star_parents(n)
             elif tree == "random":
                 par = random_depth_parents(n, max_depth, _rng(seed, "tree", b))
             else:
