@@ -14,8 +14,12 @@
 //   S^T = K Q^T   (v_mfma_f32_32x32x16_bf16, keys x rows), online softmax per
 //   row in registers (each lane holds one row's scores, so P^T feeds the next
 //   MFMA directly), and O^T += V^T P^T.
-// K tiles are staged in LDS row-major, V tiles transposed, double-buffered with
-// the next tile's global loads issued before the current tile's math.
+// Prefix tiles reach LDS by global->LDS copies through a ring of four stages
+// (three tiles in flight), one barrier per tile; block-table entries are read
+// through the scalar cache so they do not drain the copy counter.  K tiles are
+// row-major with an XOR swizzle, V tiles d-major in a layout whose operand
+// reads are free of bank conflicts.  The softmax scale is folded into one FMA
+// per score in the exponent.
 #include "tav_internal.h"
 
 namespace tav {
@@ -64,6 +68,15 @@ __device__ inline int kpos(int c, int key) {
   return D == 128 ? (c ^ (key & 15)) : (c ^ ((key >> 1) & 7));
 }
 
+// Byte offset of (key kk of a 16-key sub-block, d) inside the sub-block's V^T region: groups of
+// 32 d rows, each [key half (2)][32 d][8 keys], so the MFMA operand reads (16 lanes = 16
+// consecutive d rows of one key half) cover 256 contiguous bytes.
+__device__ inline int vt_off(int d, int kk) {
+  return (d >> 5) * 1024 + (kk >> 3) * 512 + (d & 31) * 16 + (kk & 7) * 2;
+}
+
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+
 template <int D, int LOG2G>
 __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
   constexpr int G = 1 << LOG2G;
@@ -72,11 +85,12 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
   constexpr int CH = D / 8;                // 16-byte chunks per key row
   constexpr int NB = kRowsPerWG >> LOG2G;  // nodes per row block
   constexpr int TILE_BYTES = kTileKeys * D * 2;
+  constexpr int SUB_BYTES = D * 32;                     // one 16-key sub-block of V^T
   constexpr int KEYS_PER_DMA = 1024 / (D * 2);          // key rows per 1 KB wave load
   constexpr int DMA_PER_OPERAND = TILE_BYTES / 1024 / 8;  // per wave and tile, for K and for V
   constexpr int DMA_PER_TILE = 2 * DMA_PER_OPERAND;
-  // LDS: per stage a K tile [64 keys][D] (16-byte chunk c of key k stored at kpos(c, k))
-  // and a V^T tile [4 sub-blocks of 16 keys][D][16 keys].
+  // LDS: per stage a K tile [64 keys][D] (16-byte chunk c of key k stored at kpos(c, k)) and
+  // a V^T tile [4 sub-blocks of 16 keys] laid out by vt_off.
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages][2 * TILE_BYTES];
 
   if (a.status[0] & TAV_DEV_PLAN_MISMATCH) return;
@@ -110,7 +124,9 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
   const bool chain = a.is_chain[b] != 0;
   if (!chain && n > kMaxTreeNodes) return;  // rejected by tree preparation
   const int Hq = a.Hq, Hkv = a.Hkv, bs = a.block_size;
-  const int32_t* btab = a.block_table + (size_t)b * a.max_blocks;
+  // block-table entries are read through the scalar cache: they do not count against the
+  // vector-memory counter that paces the tile copies
+  const const_i32_ptr btab = (const_i32_ptr)(a.block_table + (size_t)b * a.max_blocks);
 
   // this lane's query row
   const int row = wave * 32 + l32;
@@ -134,116 +150,138 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
   const uint16_t* vc = (const uint16_t*)a.v_cache;
   const int first_blk = L > 0 ? btab[0] : 0;
 
-  // DMA of prefix tile t into stage st.  Wave w copies key rows 8w..8w+7 of the K tile
-  // and d rows (w%2)*D/2 .. of sub-block w/2 of the V^T tile; every address stays inside
-  // a valid block (rows past the prefix read the first block and are masked).
+  // DMA of prefix tile t into stage st.  Wave w copies key rows 8w..8w+7 of the K tile and
+  // d rows (w%2)*D/2 .. of sub-block w/2 of the V^T tile (lanes 0-31 keys 0-7, lanes 32-63
+  // keys 8-15 of 32 d rows per copy); every address stays inside a valid block (rows past
+  // the prefix read the first block and are masked).
+  const int lbs = __builtin_ctz(bs);   // block sizes are powers of two
+  // per-lane element offsets of the copies inside a 16-key sub-block (the same for every tile)
+  int k_lane[DMA_PER_OPERAND], v_lane[DMA_PER_OPERAND];
+#pragma unroll
+  for (int i = 0; i < DMA_PER_OPERAND; ++i) {
+    const int kt = wave * 8 + i * KEYS_PER_DMA + lane / CH;   // key of the tile
+    k_lane[i] = (kt - (wave >> 1) * 16) * D + kpos<D>(lane % CH, kt) * 8;
+    const int d = (wave & 1) * (D / 2) + i * 32 + l32;
+    v_lane[i] = d * bs + h32 * 8;
+  }
   auto issue_prefix = [&](int t, int st) {
     uint8_t* kbase = lds[st];
     uint8_t* vbase = lds[st] + TILE_BYTES;
     const int sb = wave >> 1;
     const int r0 = t * kTileKeys + sb * 16;              // first key row of the sub-block
-    int blk = r0 < L ? btab[r0 / bs] : first_blk;
+    int blk = r0 < L ? btab[r0 >> lbs] : first_blk;
     if ((unsigned)blk >= (unsigned)a.num_blocks) {
       if (lane == 0) atomicOr(a.status, (uint32_t)TAV_DEV_BAD_BLOCK);
       blk = 0;
     }
-    const int slot0 = r0 % bs;
-    const size_t kblk = (((size_t)blk * Hkv + g) * bs + slot0) * D;
-    const size_t vblk = ((size_t)blk * Hkv + g) * D * bs + slot0;
+    const int slot0 = r0 & (bs - 1);
+    const uint16_t* ksrc = kc + (((size_t)blk * Hkv + g) * bs + slot0) * D;
+    const uint16_t* vsrc = vc + ((size_t)blk * Hkv + g) * D * bs + slot0;
 #pragma unroll
     for (int i = 0; i < DMA_PER_OPERAND; ++i) {
-      const int kt = wave * 8 + i * KEYS_PER_DMA + lane / CH;   // key of the tile
-      const int pos = lane % CH;
-      dma16(kc + kblk + (size_t)(kt - sb * 16) * D + kpos<D>(pos, kt) * 8,
-            kbase + (wave * 8 + i * KEYS_PER_DMA) * (D * 2));
-      const int d0 = (wave & 1) * (D / 2) + i * 32;
-      const int d = d0 + (lane >> 1);
-      dma16(vc + vblk + (size_t)d * bs + (lane & 1) * 8, vbase + sb * (D * 32) + d0 * 32);
+      dma16(ksrc + k_lane[i], kbase + (wave * 8 + i * KEYS_PER_DMA) * (D * 2));
+      dma16(vsrc + v_lane[i], vbase + sb * SUB_BYTES + (((wave & 1) * (D / 2) + i * 32) >> 5) * 1024);
     }
   };
 
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;  // running max (log2 units) and sum of this lane's row
   f32x16_t acc[DB];
 #pragma unroll
   for (int mb = 0; mb < DB; ++mb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
-  const float sl2 = a.scale * kLog2e;
+  const float c2 = a.scale * kLog2e;      // score -> log2 units
 
-  // one tile of math from stage st; kind: 0 full prefix tile, 1 partial prefix tile, 2 tail tile
-  auto compute = [&](int t, int st, int kind) {
+  // raw scores S^T = K Q^T of the tile in stage st; element r of block kb of this lane is
+  // key kb*32 + (r/8)*16 + h32*8 + r%8 of the tile, query row `row`
+  auto s_tile = [&](int st, f32x16_t (&sacc)[2]) {
     const uint8_t* kbase = lds[st];
-    const uint8_t* vbase = lds[st] + TILE_BYTES;
-    f32x16_t sacc[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-      const int key = kb * 32 + sigma(l32);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int key = kb * 32 + sigma(l32);
         const bf16x8_t ka = *(const bf16x8_t*)(kbase + key * (D * 2) + kpos<D>(ks * 2 + h32, key) * 16);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], sacc[kb], 0, 0, 0);
       }
     }
-    // scale + mask; key of (kb, r) for this lane = kb*32 + (r/8)*16 + h*8 + r%8
+  };
+
+  // masking of a tile's scores: kind 1 = the last, partial prefix tile, kind 2 = a tree-tail tile
+  auto mask_tile = [&](int t, int kind, f32x16_t (&sacc)[2]) {
     uint64_t mw = 0;
     if (kind == 2 && !chain && rvalid) mw = a.mask[(size_t)(s0 + rnode) * kMaskWords + (t - Tp)];
-    float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kin = kb * 32 + (r >> 3) * 16 + h32 * 8 + (r & 7);
-        float s = sacc[kb][r] * sl2;
+        bool vis;
         if (kind == 1) {
-          s = (t * kTileKeys + kin < L) ? s : -INFINITY;
-        } else if (kind == 2) {
+          vis = t * kTileKeys + kin < L;
+        } else {
           const int j = (t - Tp) * kTileKeys + kin;
-          const bool vis = j < tail_n && (chain ? j <= rnode : ((mw >> (j & 63)) & 1ull) != 0ull);
-          s = vis ? s : -INFINITY;
+          vis = j < tail_n && (chain ? j <= rnode : ((mw >> (j & 63)) & 1ull) != 0ull);
         }
-        sacc[kb][r] = s;
-        mx = fmaxf(mx, s);
+        sacc[kb][r] = vis ? sacc[kb][r] : -INFINITY;
       }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    // lazy rescaling: keep the running max until some row's tile max exceeds it by 2^8
-    if (__ballot(mx > m_run + kRescaleSlack)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
-      m_run = m_new;
-      l_run *= alpha;
+  };
+
+  // online softmax of one tile: P (bf16, this lane's 32 keys as 4 MFMA operands), the new
+  // running max / sum, and whether the accumulator needs rescaling by *alpha.  The running
+  // max is kept until some row's tile max exceeds it by 2^8 (a wave-uniform decision).
+  auto softmax_tile = [&](f32x16_t (&sacc)[2], bf16x8_t (&pb)[4], float& alpha) -> bool {
+    float mx = -INFINITY;
 #pragma unroll
-      for (int mb = 0; mb < DB; ++mb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[mb][r] *= alpha;
-    }
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    bf16x8_t pb[4];
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
+    const bool need = __ballot(mx > m_run + kRescaleSlack) != 0ull;
+    const float m_new = need ? fmaxf(m_run, mx) : m_run;
+    alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
+    m_run = m_new;
+    const float mu = m_new == -INFINITY ? 0.f : m_new;
     float ps = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(sacc[kb][r] - m_use);
+        const float p = fast_exp2(fmaf(sacc[kb][r], c2, -mu));
         ps += p;
         pb[kb * 2 + (r >> 3)][r & 7] = (__bf16)p;
       }
     }
-    l_run += ps;
-    // O^T += V^T P^T over the four 16-key groups (one sub-block each)
+    l_run = l_run * alpha + ps;
+    return need;
+  };
+
+  // O^T += V^T P^T over the four 16-key sub-blocks of the tile in stage st
+  auto pv_tile = [&](int st, const bf16x8_t (&pb)[4]) {
+    const uint8_t* vbase = lds[st] + TILE_BYTES;
 #pragma unroll
     for (int k2 = 0; k2 < 4; ++k2) {
 #pragma unroll
       for (int mb = 0; mb < DB; ++mb) {
-        const bf16x8_t va = *(const bf16x8_t*)(vbase + k2 * (D * 32) + (mb * 32 + l32) * 32 + h32 * 16);
+        const bf16x8_t va = *(const bf16x8_t*)(vbase + k2 * SUB_BYTES + mb * 1024 + h32 * 512 + l32 * 16);
         acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[k2], acc[mb], 0, 0, 0);
       }
     }
   };
+  auto rescale = [&](float alpha) {
+#pragma unroll
+    for (int mb = 0; mb < DB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mb][r] *= alpha;
+  };
 
-  // ---- prefix tiles: DMA pipeline with kStages - 1 tiles in flight, one barrier per tile ----
+  // ---- prefix tiles: DMA ring of kStages tiles (kStages - 1 in flight), one barrier per
+  // tile; per tile: scores, softmax, P V ----
   const int p_end = min(t_end, Tp);
   if (t_begin < p_end) {
     int issued = t_begin;
@@ -259,18 +297,24 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
         ++issued;
       }
       const int st = (t - t_begin) % kStages;
+      f32x16_t sacc[2];
       if ((t + 1) * kTileKeys > L) {
         // last, partial prefix tile: zero V^T of keys >= L so 0 * stale data never reaches O
-        uint16_t* vbase = (uint16_t*)(lds[st] + TILE_BYTES);
+        uint8_t* vbase = lds[st] + TILE_BYTES;
         for (int e = tid; e < 4 * D * 16; e += 512) {
-          const int sb = e / (D * 16), kk = e % 16;
-          if (t * kTileKeys + sb * 16 + kk >= L) vbase[e] = 0;
+          const int sbk = e / (D * 16), d = (e / 16) % D, kk = e % 16;
+          if (t * kTileKeys + sbk * 16 + kk >= L) *(uint16_t*)(vbase + sbk * SUB_BYTES + vt_off(d, kk)) = 0;
         }
         __syncthreads();
-        compute(t, st, 1);
+        s_tile(st, sacc);
+        mask_tile(t, 1, sacc);
       } else {
-        compute(t, st, 0);
+        s_tile(st, sacc);
       }
+      bf16x8_t pb[4];
+      float alpha;
+      if (softmax_tile(sacc, pb, alpha)) rescale(alpha);
+      pv_tile(st, pb);
     }
     __syncthreads();
   }
@@ -280,7 +324,7 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
   const uint16_t* vn = (const uint16_t*)a.v_node;
   for (int t = max(t_begin, Tp); t < t_end; ++t) {
     uint8_t* kbase = lds[0];
-    uint16_t* vbase = (uint16_t*)(lds[0] + TILE_BYTES);
+    uint8_t* vbase = lds[0] + TILE_BYTES;
 #pragma unroll
     for (int i = 0; i < (kTileKeys * CH) / 512; ++i) {
       const int c = tid + i * 512;                // 64 keys x CH chunks of 8 d
@@ -295,10 +339,17 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
       const uint32_t w4[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        vbase[(key >> 4) * (D * 16) + (ch * 8 + e) * 16 + (key & 15)] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+        *(uint16_t*)(vbase + (key >> 4) * SUB_BYTES + vt_off(ch * 8 + e, key & 15)) =
+            (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
     }
     __syncthreads();
-    compute(t, 0, 2);
+    f32x16_t sacc[2];
+    s_tile(0, sacc);
+    mask_tile(t, 2, sacc);
+    bf16x8_t pb[4];
+    float alpha;
+    if (softmax_tile(sacc, pb, alpha)) rescale(alpha);
+    pv_tile(0, pb);
     __syncthreads();
   }
 

@@ -41,7 +41,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
-constexpr int kTargetWorkgroups = 512;  // two rounds of one workgroup per MI355X compute unit
+constexpr int kTargetWorkgroups = 256;  // one round of one workgroup per MI355X compute unit
 constexpr int kMinTilesPerSplit = 8;    // at least 512 keys per split
 
 int log2_exact(int x) {
