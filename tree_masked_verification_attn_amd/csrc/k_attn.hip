@@ -40,10 +40,20 @@ union Bf16Pack8 {
   __bf16 e[8];
 };
 
-// Direct global -> LDS copy of 16 bytes per lane; the LDS destination is
-// wave-uniform and lane i's bytes land at lds + 16 * i.
+// Direct global -> LDS copy of 16 bytes per lane; the LDS destination is wave-uniform and
+// lane i's bytes land at lds + 16 * i.  Issued through inline assembly: the compiler then
+// does not treat every later LDS read as possibly aliasing the copy (which makes it wait for
+// all copies in flight before each read, so the copies of later tiles never overlap the
+// math).  The copies are ordered explicitly instead: wait_vm on the copy count of each tile,
+// a barrier, and compiler-only memory barriers around both.  M0 holds the LDS address; the
+// compiler keeps no value of its own in M0 in this kernel.
 __device__ inline void dma16(const void* gsrc, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+  const uint32_t lds_off = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)lds_wave_base;
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :: "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds_off)) : "memory");
 }
 
 // s_waitcnt on outstanding vector-memory operations only (lgkm / exp counters untouched).
@@ -288,10 +298,12 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
     for (; issued < min(p_end, t_begin + kStages - 1); ++issued) issue_prefix(issued, (issued - t_begin) % kStages);
     for (int t = t_begin; t < p_end; ++t) {
       const int after = issued - 1 - t;       // tiles issued after t, still in flight
+      asm volatile("" ::: "memory");          // no LDS access moves across the wait and barrier
       if (after >= 2) wait_vm<2 * DMA_PER_TILE>();
       else if (after == 1) wait_vm<DMA_PER_TILE>();
       else wait_vm<0>();
       __builtin_amdgcn_s_barrier();           // tile t landed for every wave; tile t-1's stage is free
+      asm volatile("" ::: "memory");
       if (issued < p_end) {
         issue_prefix(issued, (issued - t_begin) % kStages);
         ++issued;
