@@ -234,6 +234,18 @@ tav_status tav_tree_attn_verify(const tav_problem* prob, const tav_tree* tree,
 /* Waits for stream, then copies the device status word to *status_bits. */
 tav_status tav_read_status(const void* workspace, void* stream, uint32_t* status_bits);
 
+/* Optional timing of the attention kernel, the largest kernel of the pass, for benchmarks.
+ * After tav_kernel_timing(1), every bf16 tree-attention call records a pair of HIP events on
+ * its attention stream immediately before and after the attention kernel launch (not around
+ * the preparation, plan or merge launches).  tav_kernel_timing_read waits for the recorded
+ * events, returns the summed elapsed milliseconds and the number of launches recorded since
+ * the previous read or enable, and starts a new record.  tav_kernel_timing(0) stops recording
+ * and releases the events.  The events belong to the device current at the first recording;
+ * recording on another device returns TAV_ERR_INVALID_ARGUMENT.  Process-wide host state:
+ * calls from several threads at once are not supported. */
+tav_status tav_kernel_timing(int enable);
+tav_status tav_kernel_timing_read(double* total_ms, int32_t* launches);
+
 /* Static description of a status code. */
 const char* tav_status_string(tav_status s);
 

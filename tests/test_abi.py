@@ -160,3 +160,11 @@ def test_presto_validation_codes():
 def test_status_strings():
     assert tav.tav_status_string(0) == "TAV_OK"
     assert tav.tav_status_string(4) == "TAV_ERR_WORKSPACE"
+
+
+def test_kernel_timing_state_without_gpu_work():
+    """Enabling, reading an empty record and disabling touch no device."""
+    tav.tav_kernel_timing(True)
+    assert tav.tav_kernel_timing_read() == (0.0, 0)
+    tav.tav_kernel_timing(False)
+    assert tav.tav_kernel_timing_read() == (0.0, 0)

@@ -120,3 +120,20 @@ def test_presto_small(seed):
     assert got["status"] == 0, got["status"]
     gu.check_attention(w, got)
     gu.check_presto(w, got)
+
+
+@pytest.mark.gpu
+def test_attention_kernel_timing_events():
+    """The timing hook records one event pair per bf16 attention call, around the kernel."""
+    import tree_masked_verification_attn_amd as tav
+    from workloads import device as wdev
+
+    w = gen.tree_batch(5, B=2, prefix_len=[300, 70], tree="random", n_nodes=[20, 9], Hq=8, Hkv=2,
+                       D=128, dtype="bf16")
+    d = wdev.upload(w, "cuda", with_verify=False)
+    tav.tav_kernel_timing(True)
+    for _ in range(3):
+        tav.tav_tree_attention(d.prob, d.tree, d.attn, d.workspace)
+    ms, n = tav.tav_kernel_timing_read()
+    tav.tav_kernel_timing(False)
+    assert n == 3 and ms > 0.0

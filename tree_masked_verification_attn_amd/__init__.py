@@ -28,8 +28,8 @@ DEVICE_BITS = {
     13: "PLAN_MISMATCH", 14: "BAD_TEMPERATURE",
 }
 ENTRY_POINTS = ("tav_workspace_size", "tav_tree_prep", "tav_tree_attention", "tav_tree_verify",
-                "tav_presto_accept", "tav_tree_attn_verify", "tav_read_status", "tav_status_string",
-                "tav_last_error")
+                "tav_presto_accept", "tav_tree_attn_verify", "tav_read_status", "tav_kernel_timing",
+                "tav_kernel_timing_read", "tav_status_string", "tav_last_error")
 
 _p = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -105,10 +105,12 @@ def load() -> ctypes.CDLL:
             ctypes.POINTER(tav_verify_io), ctypes.POINTER(tav_presto_io), ctypes.POINTER(tav_tree_out),
             _p, ctypes.c_size_t, _p, _p]
         lib.tav_read_status.argtypes = [_p, _p, ctypes.POINTER(ctypes.c_uint32)]
+        lib.tav_kernel_timing.argtypes = [ctypes.c_int]
+        lib.tav_kernel_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i32)]
         lib.tav_status_string.argtypes = [ctypes.c_int]
         lib.tav_status_string.restype = ctypes.c_char_p
         lib.tav_last_error.restype = ctypes.c_char_p
-        for name in ENTRY_POINTS[:7]:
+        for name in ENTRY_POINTS[:9]:
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -235,6 +237,17 @@ def tav_read_status(workspace: torch.Tensor, stream=None) -> int:
     bits = ctypes.c_uint32(0)
     _check(load().tav_read_status(_ptr(workspace), _stream(stream), ctypes.byref(bits)))
     return bits.value
+
+
+def tav_kernel_timing(enable: bool):
+    _check(load().tav_kernel_timing(1 if enable else 0))
+
+
+def tav_kernel_timing_read():
+    """(summed milliseconds, launches) of the attention kernel since the previous read."""
+    ms, n = ctypes.c_double(0.0), _i32(0)
+    _check(load().tav_kernel_timing_read(ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
 
 
 def device_status_names(bits: int):

@@ -8,6 +8,9 @@
 
 #include <string>
 
+#include <utility>
+#include <vector>
+
 #include "tav_internal.h"
 
 namespace tav {
@@ -268,13 +271,60 @@ tav_status enqueue_prep(const tav_problem* p, const Plan& P, const tav_tree* t,
   return TAV_OK;
 }
 
+// Event pairs around the attention kernel (tav_kernel_timing).
+struct KernelTiming {
+  bool on = false;
+  int device = -1;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pool;
+  size_t used = 0;
+};
+KernelTiming g_timing;
+
+void release_timing_events() {
+  for (auto& e : g_timing.pool) {
+    (void)hipEventDestroy(e.first);
+    (void)hipEventDestroy(e.second);
+  }
+  g_timing.pool.clear();
+  g_timing.used = 0;
+  g_timing.device = -1;
+}
+
+tav_status timing_pair(hipEvent_t* start, hipEvent_t* stop) {
+  int dev = 0;
+  TAV_HIP(hipGetDevice(&dev));
+  if (g_timing.device < 0) g_timing.device = dev;
+  if (g_timing.device != dev)
+    return fail(TAV_ERR_INVALID_ARGUMENT, "kernel timing events belong to device %d, not %d", g_timing.device, dev);
+  if (g_timing.used == g_timing.pool.size()) {
+    hipEvent_t a = nullptr, b = nullptr;
+    TAV_HIP(hipEventCreate(&a));
+    if (hipEventCreate(&b) != hipSuccess) {
+      (void)hipEventDestroy(a);
+      return fail(TAV_ERR_HIP, "hipEventCreate failed");
+    }
+    g_timing.pool.emplace_back(a, b);
+  }
+  *start = g_timing.pool[g_timing.used].first;
+  *stop = g_timing.pool[g_timing.used].second;
+  ++g_timing.used;
+  return TAV_OK;
+}
+
 tav_status enqueue_attention(const tav_problem* p, const Plan& P, const tav_attn_io* io, void* ws,
                              hipStream_t s) {
   const AttnArgs a = attn_args(p, P, io, ws);
   if (p->dtype == TAV_BF16) {
     TAV_HIP(launch_plan(P, p->node_offsets, p->prefix_len, const_cast<int32_t*>(a.seq_rb_off),
                         const_cast<int32_t*>(a.rb_seq), const_cast<int32_t*>(a.item_off), a.status, s));
+    hipEvent_t ev0 = nullptr, ev1 = nullptr;
+    if (g_timing.on) {
+      const tav_status st = timing_pair(&ev0, &ev1);
+      if (st != TAV_OK) return st;
+      TAV_HIP(hipEventRecord(ev0, s));
+    }
     TAV_HIP(launch_attn_bf16(P, a, s));
+    if (g_timing.on) TAV_HIP(hipEventRecord(ev1, s));
     TAV_HIP(launch_merge(P, a, true, s));
   } else {
     TAV_HIP(launch_attn_f32(P, a, s));
@@ -479,6 +529,27 @@ tav_status tav_read_status(const void* workspace, void* stream, uint32_t* status
   if (!workspace || !status_bits) return fail(TAV_ERR_NULL_POINTER, "workspace / status_bits is NULL");
   TAV_HIP(hipStreamSynchronize((hipStream_t)stream));
   TAV_HIP(hipMemcpy(status_bits, workspace, sizeof(uint32_t), hipMemcpyDeviceToHost));
+  return ok();
+}
+
+tav_status tav_kernel_timing(int enable) {
+  release_timing_events();
+  g_timing.on = enable != 0;
+  return ok();
+}
+
+tav_status tav_kernel_timing_read(double* total_ms, int32_t* launches) {
+  if (!total_ms || !launches) return fail(TAV_ERR_NULL_POINTER, "total_ms / launches is NULL");
+  double total = 0.0;
+  for (size_t i = 0; i < g_timing.used; ++i) {
+    TAV_HIP(hipEventSynchronize(g_timing.pool[i].second));
+    float ms = 0.f;
+    TAV_HIP(hipEventElapsedTime(&ms, g_timing.pool[i].first, g_timing.pool[i].second));
+    total += ms;
+  }
+  *total_ms = total;
+  *launches = (int32_t)g_timing.used;
+  g_timing.used = 0;
   return ok();
 }
 
