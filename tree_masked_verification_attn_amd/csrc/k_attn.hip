@@ -7,19 +7,28 @@
 // requests share the cached prefix x_{0:c}, Section 3.2 and Appendix B.3
 // Example 4).  Scores are scale * <q, k>, softmax over the visible keys.
 //
-// bf16 path (gfx950 MFMA): one workgroup = one work item = (row block, KV
-// head, range of 64-key tiles).  A row block holds up to 256 query rows (nodes
-// x the G query heads sharing the KV head), so every KV tile is read from HBM
-// once and used by all rows.  Each of the 8 waves owns 32 rows and computes
+// bf16 path (gfx950 MFMA).  A row block holds up to 256 query rows (nodes x
+// the G query heads sharing a KV head), so every KV tile is read from HBM once
+// and used by all rows.  Per KV head the 64-key tiles of all row blocks are
+// concatenated and cut into equal ranges, one workgroup each (so every compute
+// unit gets the same number of tiles); a workgroup walks its range across
+// row-block boundaries, finishing a row block's output itself when it holds the
+// whole block and leaving a partial (O, lse) for merge_kernel otherwise.
+// Each of the 8 waves owns 32 rows and computes
 //   S^T = K Q^T   (v_mfma_f32_32x32x16_bf16, keys x rows), online softmax per
 //   row in registers (each lane holds one row's scores, so P^T feeds the next
 //   MFMA directly), and O^T += V^T P^T.
-// Prefix tiles reach LDS by global->LDS copies through a ring of four stages
-// (three tiles in flight), one barrier per tile; block-table entries are read
-// through the scalar cache so they do not drain the copy counter.  K tiles are
-// row-major with an XOR swizzle, V tiles d-major in a layout whose operand
-// reads are free of bank conflicts.  The softmax scale is folded into one FMA
-// per score in the exponent.
+// A tile is taken in two halves of 32 keys with one online-softmax update each,
+// pipelined inside the wave: the scores of the second half run on the matrix
+// cores while the first half's softmax runs on the vector ALU, and the first
+// half's P V products run next to the second half's softmax.  Tiles reach LDS
+// by global->LDS copies through a ring of four stages (three in flight while
+// one is used, one barrier per tile).  The tree nodes' own keys and
+// values are first packed into blocks of the cache layout (pack_tail_kernel), so
+// tree-tail tiles take the same copy path as prefix tiles.  Block-table and
+// plan entries are read through the scalar cache.  K tiles are row-major with
+// an XOR swizzle, V tiles d-major in a layout whose operand reads are free of
+// bank conflicts.  The softmax scale is folded into one FMA per score.
 #include "tav_internal.h"
 
 namespace tav {
@@ -45,15 +54,14 @@ union Bf16Pack8 {
 // does not treat every later LDS read as possibly aliasing the copy (which makes it wait for
 // all copies in flight before each read, so the copies of later tiles never overlap the
 // math).  The copies are ordered explicitly instead: wait_vm on the copy count of each tile,
-// a barrier, and compiler-only memory barriers around both.  M0 holds the LDS address; the
-// compiler keeps no value of its own in M0 in this kernel.
+// a barrier, and compiler-only memory barriers around both.
 __device__ inline void dma16(const void* gsrc, void* lds_wave_base) {
   const uint32_t lds_off = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)lds_wave_base;
   asm volatile(
       "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
       "global_load_lds_dwordx4 %0, off"
-      :: "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds_off)) : "memory");
+      :: "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds_off)) : "memory", "m0");
 }
 
 // s_waitcnt on outstanding vector-memory operations only (lgkm / exp counters untouched).
@@ -68,7 +76,7 @@ __device__ inline void wait_vm() {
 // consecutive keys and the V^T operand is one 16-byte read.
 __device__ inline int sigma(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
-constexpr int kStages = 4;          // key tiles in LDS (3 in flight while one is computed)
+constexpr int kStages = 4;            // ring stages in LDS (3 in flight while one is used)
 constexpr float kRescaleSlack = 8.f;  // keep a stale max while the tile max exceeds it by <= 2^8
 
 // Stored 16-byte position of chunk c of key row k in a K tile (bank spreading
@@ -78,14 +86,82 @@ __device__ inline int kpos(int c, int key) {
   return D == 128 ? (c ^ (key & 15)) : (c ^ ((key >> 1) & 7));
 }
 
-// Byte offset of (key kk of a 16-key sub-block, d) inside the sub-block's V^T region: groups of
-// 32 d rows, each [key half (2)][32 d][8 keys], so the MFMA operand reads (16 lanes = 16
-// consecutive d rows of one key half) cover 256 contiguous bytes.
-__device__ inline int vt_off(int d, int kk) {
-  return (d >> 5) * 1024 + (kk >> 3) * 512 + (d & 31) * 16 + (kk & 7) * 2;
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+typedef const __attribute__((address_space(4))) uint8_t* const_u8_ptr;
+
+// Scalar-cache views of the work plan (wave-uniform reads).
+struct PlanView {
+  const_i32_ptr rb_tile, rb_seq, pref_len, tail_blk;
+  const int32_t* block_table;
+  int max_blocks, total_rb;
+};
+
+// Where the tiles of one row block come from (wave-uniform).
+struct TileCursor {
+  int r;          // row block
+  int t;          // tile within the row block
+  int T;          // tiles of the row block
+  int Tp;         // prefix tiles
+  int L;          // prefix rows
+  int tail_off;   // first packed node block of the sequence
+  int tail_nblk;  // packed node blocks of the sequence
+  int first_blk;  // block of prefix row 0 (a valid block for rows past the prefix)
+  const_i32_ptr btab;
+};
+
+__device__ __forceinline__ void cursor_load(TileCursor& c, const PlanView& pv, int r) {
+  const int b = pv.rb_seq[r];
+  c.r = r;
+  c.T = pv.rb_tile[r + 1] - pv.rb_tile[r];
+  c.L = pv.pref_len[b];
+  c.Tp = (c.L + kTileKeys - 1) / kTileKeys;
+  c.tail_off = pv.tail_blk[b];
+  c.tail_nblk = pv.tail_blk[b + 1] - c.tail_off;
+  c.btab = (const_i32_ptr)(pv.block_table + (size_t)b * pv.max_blocks);
+  c.first_blk = c.L > 0 ? c.btab[0] : 0;
 }
 
-typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+__device__ __forceinline__ void cursor_advance(TileCursor& c, const PlanView& pv) {
+  if (++c.t == c.T) {
+    c.t = 0;
+    if (c.r + 1 < pv.total_rb) cursor_load(c, pv, c.r + 1);
+  }
+}
+
+// Where the 16-key sub-block sb of the tile under cursor c lies: for a prefix tile the
+// block-table entry (loaded now, checked when used, so the scalar load's latency overlaps the
+// math) or a stand-in block for rows past the prefix; for a tree-node tile the packed block.
+struct BlockRef {
+  int blk, slot0;
+  bool tail;
+};
+__device__ __forceinline__ BlockRef cursor_block(const TileCursor& c, int sb, int lbs) {
+  const int bs = 1 << lbs;
+  BlockRef ref;
+  if (c.t < c.Tp) {
+    const int r0 = c.t * kTileKeys + sb * 16;
+    ref.blk = r0 < c.L ? c.btab[r0 >> lbs] : c.first_blk;
+    ref.slot0 = r0 & (bs - 1);
+    ref.tail = false;
+  } else {
+    const int j0 = (c.t - c.Tp) * kTileKeys + sb * 16;
+    const int lb = j0 >> lbs;
+    ref.blk = c.tail_off + (lb < c.tail_nblk ? lb : 0);
+    ref.slot0 = j0 & (bs - 1);
+    ref.tail = true;
+  }
+  return ref;
+}
+
+// x combined with its value in the other half of the wave (lane i ^ 32), by max
+__device__ inline float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 template <int D, int LOG2G>
 __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
@@ -96,57 +172,107 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
   constexpr int NB = kRowsPerWG >> LOG2G;  // nodes per row block
   constexpr int TILE_BYTES = kTileKeys * D * 2;
   constexpr int SUB_BYTES = D * 32;                     // one 16-key sub-block of V^T
-  constexpr int KEYS_PER_DMA = 1024 / (D * 2);          // key rows per 1 KB wave load
+  constexpr int KEYS_PER_DMA = 1024 / (D * 2);          // key rows per 1 KB wave copy
   constexpr int DMA_PER_OPERAND = TILE_BYTES / 1024 / 8;  // per wave and tile, for K and for V
   constexpr int DMA_PER_TILE = 2 * DMA_PER_OPERAND;
   // LDS: per stage a K tile [64 keys][D] (16-byte chunk c of key k stored at kpos(c, k)) and
-  // a V^T tile [4 sub-blocks of 16 keys] laid out by vt_off.
+  // a V^T tile of 4 sub-blocks of 16 keys, each [32-d group][key half][32 d][8 keys].
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages][2 * TILE_BYTES];
 
   if (a.status[0] & TAV_DEV_PLAN_MISMATCH) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h32 = lane >> 5, l32 = lane & 31;
-  const int item = blockIdx.x, g = blockIdx.y;
-
-  int lo = 0, hi = a.total_rb;  // row block of this item: largest r with item_off[r] <= item
-  while (hi - lo > 1) {
-    int mid = (lo + hi) >> 1;
-    if (a.item_off[mid] <= item) lo = mid; else hi = mid;
-  }
-  const int rbi = lo;
-  const int i0 = a.item_off[rbi];
-  const int nsplit = a.item_off[rbi + 1] - i0;
-  const int split = item - i0;
-  const int b = a.rb_seq[rbi];
-  if (b < 0 || b >= a.B || split < 0 || split >= nsplit) return;
-  const int rb = rbi - a.seq_rb_off[b];
-  const int s0 = a.node_offsets[b];
-  const int n = a.node_offsets[b + 1] - s0;
-  const int L = a.prefix_len[b];
-  const int node0 = rb * NB;
-  const int nodes_here = min(NB, n - node0);
-  const int tail_n = min(n, node0 + NB);
-  const int Tp = (L + kTileKeys - 1) / kTileKeys;
-  const int Ttot = Tp + (tail_n + kTileKeys - 1) / kTileKeys;
-  const int t_begin = split * a.tiles_per_split;
-  const int t_end = min(Ttot, t_begin + a.tiles_per_split);
-  const bool chain = a.is_chain[b] != 0;
-  if (!chain && n > kMaxTreeNodes) return;  // rejected by tree preparation
+  const int wg = blockIdx.x, g = blockIdx.y;
+  const int j_begin = wg * a.C;
+  const int j_end = min(a.tiles_per_head, j_begin + a.C);
+  if (j_begin >= j_end) return;
   const int Hq = a.Hq, Hkv = a.Hkv, bs = a.block_size;
-  // block-table entries are read through the scalar cache: they do not count against the
-  // vector-memory counter that paces the tile copies
-  const const_i32_ptr btab = (const_i32_ptr)(a.block_table + (size_t)b * a.max_blocks);
+  const int lbs = __builtin_ctz(bs);   // block sizes are powers of two
+  const const_i32_ptr rb_tile = (const_i32_ptr)a.rb_tile;
+  const const_i32_ptr rb_seq = (const_i32_ptr)a.rb_seq;
+  const const_i32_ptr seq_rb_off = (const_i32_ptr)a.seq_rb_off;
+  const const_i32_ptr node_off = (const_i32_ptr)a.node_offsets;
+  const const_i32_ptr pref_len = (const_i32_ptr)a.prefix_len;
+  const const_i32_ptr tail_blk = (const_i32_ptr)a.tail_blk;
+  const const_u8_ptr is_chain = (const const_u8_ptr)a.is_chain;
+  const uint16_t* kc = (const uint16_t*)a.k_cache;
+  const uint16_t* vc = (const uint16_t*)a.v_cache;
+  const uint16_t* ktl = (const uint16_t*)a.k_tail;
+  const uint16_t* vtl = (const uint16_t*)a.v_tail;
+  const PlanView pview{rb_tile, rb_seq, pref_len, tail_blk, a.block_table, a.max_blocks, a.total_rb};
+  const int sb = wave >> 1;   // 16-key sub-block of each tile this wave copies
 
-  // this lane's query row
-  const int row = wave * 32 + l32;
-  const int rnode = node0 + (row >> LOG2G);
-  const bool rvalid = (row >> LOG2G) < nodes_here;
-  const int rhead = g * G + (row & (G - 1));
+  // ---- global -> LDS copies of tile j into ring slot (j - j_begin) % kStages.  Wave w copies
+  // key rows 8w..8w+7 and d rows (w%2)*D/2 .. of V^T sub-block w/2.  Sources are resolved one
+  // tile ahead of the issue, so the scalar loads overlap the math.
+  const int r_first = a.wg_rb[wg];
+  TileCursor cur;
+  cursor_load(cur, pview, r_first);
+  cur.t = j_begin - rb_tile[r_first];
+  BlockRef nref;   // the next tile's sub-block (its block-table entry may still be loading)
+  auto resolve = [&]() __attribute__((always_inline)) {   // the tile under cur, then advance
+    nref = cursor_block(cur, sb, lbs);
+    cursor_advance(cur, pview);
+  };
+  auto issue = [&](int j) __attribute__((always_inline)) {
+    int blk = nref.blk;
+    if (!nref.tail && (unsigned)blk >= (unsigned)a.num_blocks) {
+      if (lane == 0) atomicOr(a.status, (uint32_t)TAV_DEV_BAD_BLOCK);
+      blk = 0;
+    }
+    const uint16_t* rk = (nref.tail ? ktl : kc) + (((size_t)blk * Hkv + g) * bs + nref.slot0) * D;
+    const uint16_t* rv = (nref.tail ? vtl : vc) + ((size_t)blk * Hkv + g) * D * bs + nref.slot0;
+    uint8_t* kbase = lds[(j - j_begin) & (kStages - 1)];
+    uint8_t* vbase = kbase + TILE_BYTES + sb * SUB_BYTES;
+#pragma unroll
+    for (int i = 0; i < DMA_PER_OPERAND; ++i) {
+      const int kt = wave * 8 + i * KEYS_PER_DMA + lane / CH;   // key of the tile
+      const int k_off = (kt - sb * 16) * D + kpos<D>(lane % CH, kt) * 8;
+      const int v_off = ((wave & 1) * (D / 2) + i * 32 + l32) * bs + h32 * 8;
+      dma16(rk + k_off, kbase + (wave * 8 + i * KEYS_PER_DMA) * (D * 2));
+      dma16(rv + v_off, vbase + (((wave & 1) * (D / 2) + i * 32) >> 5) * 1024);
+    }
+  };
+
+  // ---- the row block being computed (a segment of this workgroup's range)
+  const int row = wave * 32 + l32;   // this lane's query row in the row block
+  int seg_r = 0, seg_A = 0, seg_E = 0, seg_s0 = 0, seg_n = 0, seg_L = 0, seg_Tp = 0;
+  int seg_node0 = 0, seg_tail_n = 0;
+  bool seg_chain = false, seg_ok = true;
+  int rnode = 0;
+  bool rvalid = false;
+  int rhead = 0;
   bf16x8_t qreg[KS];
-  {
+  uint64_t mw0 = 0, mw1 = 0, mw2 = 0, mw3 = 0;   // this row's ancestor mask (trees)
+  auto load_segment = [&](int r) __attribute__((always_inline)) {
+    const int b = rb_seq[r];
+    seg_r = r;
+    seg_A = rb_tile[r];
+    seg_E = rb_tile[r + 1];
+    seg_s0 = node_off[b];
+    seg_n = node_off[b + 1] - seg_s0;
+    seg_L = pref_len[b];
+    seg_Tp = (seg_L + kTileKeys - 1) / kTileKeys;
+    seg_node0 = (r - seq_rb_off[b]) * NB;
+    seg_tail_n = min(seg_n, seg_node0 + NB);
+    seg_chain = is_chain[b] != 0;
+    seg_ok = seg_chain || seg_n <= kMaxTreeNodes;   // larger trees were rejected by preparation
+    rnode = seg_node0 + (row >> LOG2G);
+    rvalid = (row >> LOG2G) < min(NB, seg_n - seg_node0);
+    rhead = g * G + (row & (G - 1));
+    // the mask words are loaded before q: the wait for the last q load then covers them too
+    mw0 = mw1 = mw2 = mw3 = 0ull;
+    if (!seg_chain && seg_ok && rvalid) {
+      const uint4* mp = (const uint4*)(a.mask + (size_t)(seg_s0 + rnode) * kMaskWords);
+      const uint4 m01 = mp[0], m23 = mp[1];
+      mw0 = (uint64_t)m01.x | ((uint64_t)m01.y << 32);
+      mw1 = (uint64_t)m01.z | ((uint64_t)m01.w << 32);
+      mw2 = (uint64_t)m23.x | ((uint64_t)m23.y << 32);
+      mw3 = (uint64_t)m23.z | ((uint64_t)m23.w << 32);
+    }
     const uint16_t* qp = (const uint16_t*)a.q +
-                         ((size_t)(s0 + (rvalid ? rnode : 0)) * Hq + rhead) * D + h32 * 8;
+                         ((size_t)(seg_s0 + (rvalid ? rnode : 0)) * Hq + rhead) * D + h32 * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       Bf16Pack8 t;
@@ -154,263 +280,350 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
       if (!rvalid) t.u = make_uint4(0u, 0u, 0u, 0u);
       qreg[ks] = t.v;
     }
-  }
-
-  const uint16_t* kc = (const uint16_t*)a.k_cache;
-  const uint16_t* vc = (const uint16_t*)a.v_cache;
-  const int first_blk = L > 0 ? btab[0] : 0;
-
-  // DMA of prefix tile t into stage st.  Wave w copies key rows 8w..8w+7 of the K tile and
-  // d rows (w%2)*D/2 .. of sub-block w/2 of the V^T tile (lanes 0-31 keys 0-7, lanes 32-63
-  // keys 8-15 of 32 d rows per copy); every address stays inside a valid block (rows past
-  // the prefix read the first block and are masked).
-  const int lbs = __builtin_ctz(bs);   // block sizes are powers of two
-  // per-lane element offsets of the copies inside a 16-key sub-block (the same for every tile)
-  int k_lane[DMA_PER_OPERAND], v_lane[DMA_PER_OPERAND];
-#pragma unroll
-  for (int i = 0; i < DMA_PER_OPERAND; ++i) {
-    const int kt = wave * 8 + i * KEYS_PER_DMA + lane / CH;   // key of the tile
-    k_lane[i] = (kt - (wave >> 1) * 16) * D + kpos<D>(lane % CH, kt) * 8;
-    const int d = (wave & 1) * (D / 2) + i * 32 + l32;
-    v_lane[i] = d * bs + h32 * 8;
-  }
-  auto issue_prefix = [&](int t, int st) {
-    uint8_t* kbase = lds[st];
-    uint8_t* vbase = lds[st] + TILE_BYTES;
-    const int sb = wave >> 1;
-    const int r0 = t * kTileKeys + sb * 16;              // first key row of the sub-block
-    int blk = r0 < L ? btab[r0 >> lbs] : first_blk;
-    if ((unsigned)blk >= (unsigned)a.num_blocks) {
-      if (lane == 0) atomicOr(a.status, (uint32_t)TAV_DEV_BAD_BLOCK);
-      blk = 0;
-    }
-    const int slot0 = r0 & (bs - 1);
-    const uint16_t* ksrc = kc + (((size_t)blk * Hkv + g) * bs + slot0) * D;
-    const uint16_t* vsrc = vc + ((size_t)blk * Hkv + g) * D * bs + slot0;
-#pragma unroll
-    for (int i = 0; i < DMA_PER_OPERAND; ++i) {
-      dma16(ksrc + k_lane[i], kbase + (wave * 8 + i * KEYS_PER_DMA) * (D * 2));
-      dma16(vsrc + v_lane[i], vbase + sb * SUB_BYTES + (((wave & 1) * (D / 2) + i * 32) >> 5) * 1024);
-    }
   };
 
-  float m_run = -INFINITY, l_run = 0.f;  // running max (log2 units) and sum of this lane's row
+  const float c2 = a.scale * kLog2e;      // score -> log2 units
+  float m_run = -INFINITY, l_run = 0.f;   // running max (log2 units) and sum of this lane's row
   f32x16_t acc[DB];
 #pragma unroll
   for (int mb = 0; mb < DB; ++mb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
-  const float c2 = a.scale * kLog2e;      // score -> log2 units
 
-  // raw scores S^T = K Q^T of the tile in stage st; element r of block kb of this lane is
-  // key kb*32 + (r/8)*16 + h32*8 + r%8 of the tile, query row `row`
-  auto s_tile = [&](int st, f32x16_t (&sacc)[2]) {
+  // raw scores S^T = K Q^T of key half kb (keys kb*32 .. kb*32+31 of the tile in ring slot
+  // st); element r of this lane is key kb*32 + (r/8)*16 + h32*8 + r%8, query row `row`
+  auto scores = [&](int st, int kb, f32x16_t& s) __attribute__((always_inline)) {
     const uint8_t* kbase = lds[st];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+    const int key = kb * 32 + sigma(l32);
+    const f32x16_t zero = {};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int key = kb * 32 + sigma(l32);
-        const bf16x8_t ka = *(const bf16x8_t*)(kbase + key * (D * 2) + kpos<D>(ks * 2 + h32, key) * 16);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], sacc[kb], 0, 0, 0);
-      }
+      const bf16x8_t ka = *(const bf16x8_t*)(kbase + key * (D * 2) + kpos<D>(ks * 2 + h32, key) * 16);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], ks == 0 ? zero : s, 0, 0, 0);
     }
   };
 
-  // masking of a tile's scores: kind 1 = the last, partial prefix tile, kind 2 = a tree-tail tile
-  auto mask_tile = [&](int t, int kind, f32x16_t (&sacc)[2]) {
-    uint64_t mw = 0;
-    if (kind == 2 && !chain && rvalid) mw = a.mask[(size_t)(s0 + rnode) * kMaskWords + (t - Tp)];
+  // Online-softmax update with one half's scores, cut into pieces for interleaving with
+  // MFMAs: piece 0 the row maximum, piece 1 the running-max bookkeeping, pieces 2.. the
+  // exponentials (ceil(16 / nexp) per piece) into P (bf16, two MFMA operands).  The running max is
+  // kept until some row's max exceeds it by 2^8 (a wave-uniform decision), so the accumulator
+  // rescale (by alpha) is rare.  State between pieces lives in SoftmaxState.
+  struct SoftmaxState { float mx, mu, alpha, ps; bool need; };
+  auto softmax_piece = [&](int piece, int nexp, const f32x16_t& s, bf16x8_t (&pb)[2],
+                           SoftmaxState& z) __attribute__((always_inline)) {
+    if (piece == 0) {
+      float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      z.mx = mx;
+    } else if (piece == 1) {
+      const float mx = max_halves(z.mx) * c2;
+      z.need = __ballot(mx > m_run + kRescaleSlack) != 0ull;
+      const float m_new = z.need ? fmaxf(m_run, mx) : m_run;
+      z.alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
+      m_run = m_new;
+      z.mu = m_new == -INFINITY ? 0.f : m_new;
+      z.ps = 0.f;
+    } else {
+      const int per = (16 + nexp - 1) / nexp;   // the last piece may hold fewer
+      const int r0 = (piece - 2) * per;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int kin = kb * 32 + (r >> 3) * 16 + h32 * 8 + (r & 7);
-        bool vis;
-        if (kind == 1) {
-          vis = t * kTileKeys + kin < L;
-        } else {
-          const int j = (t - Tp) * kTileKeys + kin;
-          vis = j < tail_n && (chain ? j <= rnode : ((mw >> (j & 63)) & 1ull) != 0ull);
-        }
-        sacc[kb][r] = vis ? sacc[kb][r] : -INFINITY;
+        if (r < r0 || r >= r0 + per) continue;
+        const float p = fast_exp2(fmaf(s[r], c2, -z.mu));
+        z.ps += p;
+        pb[r >> 3][r & 7] = (__bf16)p;
       }
     }
   };
 
-  // online softmax of one tile: P (bf16, this lane's 32 keys as 4 MFMA operands), the new
-  // running max / sum, and whether the accumulator needs rescaling by *alpha.  The running
-  // max is kept until some row's tile max exceeds it by 2^8 (a wave-uniform decision).
-  auto softmax_tile = [&](f32x16_t (&sacc)[2], bf16x8_t (&pb)[4], float& alpha) -> bool {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
-    const bool need = __ballot(mx > m_run + kRescaleSlack) != 0ull;
-    const float m_new = need ? fmaxf(m_run, mx) : m_run;
-    alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
-    m_run = m_new;
-    const float mu = m_new == -INFINITY ? 0.f : m_new;
-    float ps = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(fmaf(sacc[kb][r], c2, -mu));
-        ps += p;
-        pb[kb * 2 + (r >> 3)][r & 7] = (__bf16)p;
-      }
-    }
-    l_run = l_run * alpha + ps;
-    return need;
+  auto kread = [&](int st, int kb, int ks) __attribute__((always_inline)) -> bf16x8_t {
+    const int key = kb * 32 + sigma(l32);
+    return *(const bf16x8_t*)(lds[st] + key * (D * 2) + kpos<D>(ks * 2 + h32, key) * 16);
+  };
+  auto vread = [&](int st, int k2, int mb) __attribute__((always_inline)) -> bf16x8_t {
+    return *(const bf16x8_t*)(lds[st] + TILE_BYTES + k2 * SUB_BYTES + mb * 1024 + h32 * 512 + l32 * 16);
   };
 
-  // O^T += V^T P^T over the four 16-key sub-blocks of the tile in stage st
-  auto pv_tile = [&](int st, const bf16x8_t (&pb)[4]) {
-    const uint8_t* vbase = lds[st] + TILE_BYTES;
-#pragma unroll
-    for (int k2 = 0; k2 < 4; ++k2) {
-#pragma unroll
-      for (int mb = 0; mb < DB; ++mb) {
-        const bf16x8_t va = *(const bf16x8_t*)(vbase + k2 * SUB_BYTES + mb * 1024 + h32 * 512 + l32 * 16);
-        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[k2], acc[mb], 0, 0, 0);
-      }
-    }
-  };
-  auto rescale = [&](float alpha) {
+  auto rescale = [&](float alpha) __attribute__((always_inline)) {
 #pragma unroll
     for (int mb = 0; mb < DB; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mb][r] *= alpha;
   };
 
-  // ---- prefix tiles: DMA ring of kStages tiles (kStages - 1 in flight), one barrier per
-  // tile; per tile: scores, softmax, P V ----
-  const int p_end = min(t_end, Tp);
-  if (t_begin < p_end) {
-    int issued = t_begin;
-    for (; issued < min(p_end, t_begin + kStages - 1); ++issued) issue_prefix(issued, (issued - t_begin) % kStages);
-    for (int t = t_begin; t < p_end; ++t) {
-      const int after = issued - 1 - t;       // tiles issued after t, still in flight
-      asm volatile("" ::: "memory");          // no LDS access moves across the wait and barrier
-      if (after >= 2) wait_vm<2 * DMA_PER_TILE>();
-      else if (after == 1) wait_vm<DMA_PER_TILE>();
-      else wait_vm<0>();
-      __builtin_amdgcn_s_barrier();           // tile t landed for every wave; tile t-1's stage is free
-      asm volatile("" ::: "memory");
-      if (issued < p_end) {
-        issue_prefix(issued, (issued - t_begin) % kStages);
-        ++issued;
+  // whether tile t of the current row block has keys some row must not see: the partial last
+  // prefix tile, or a tree-node tile (except a chain's tiles wholly below every row)
+  auto needs_mask = [&](int t) __attribute__((always_inline)) -> bool {
+    if (t < seg_Tp - 1) return false;
+    if (t == seg_Tp - 1) return (seg_L & (kTileKeys - 1)) != 0;
+    const int j0 = (t - seg_Tp) * kTileKeys;
+    return !(seg_chain && j0 + kTileKeys - 1 <= seg_node0 && j0 + kTileKeys - 1 < seg_tail_n);
+  };
+
+  // masking of the scores of half kb of tile t.  Element r is key kb*32 + (r/8)*16 + h32*8 +
+  // r%8 of the tile: every test compares the compile-time part of that index with one
+  // lane-adjusted bound.
+  auto mask = [&](int t, int kb, f32x16_t& s) __attribute__((always_inline)) {
+    if (t < seg_Tp) {
+      const int x = seg_L - t * kTileKeys - h32 * 8;   // element visible iff its constant < x
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kc_ = kb * 32 + (r >> 3) * 16 + (r & 7);
+        s[r] = kc_ < x ? s[r] : -INFINITY;
       }
-      const int st = (t - t_begin) % kStages;
-      f32x16_t sacc[2];
-      if ((t + 1) * kTileKeys > L) {
-        // last, partial prefix tile: zero V^T of keys >= L so 0 * stale data never reaches O
-        uint8_t* vbase = lds[st] + TILE_BYTES;
-        for (int e = tid; e < 4 * D * 16; e += 512) {
-          const int sbk = e / (D * 16), d = (e / 16) % D, kk = e % 16;
-          if (t * kTileKeys + sbk * 16 + kk >= L) *(uint16_t*)(vbase + sbk * SUB_BYTES + vt_off(d, kk)) = 0;
+    } else {
+      const int j0 = (t - seg_Tp) * kTileKeys;  // first tree node of the tile
+      const int wi = t - seg_Tp;
+      // pick the word arithmetically (a select between the words could become a dynamically
+      // indexed access)
+      const uint64_t word = (mw0 & (0ull - (uint64_t)(wi == 0))) | (mw1 & (0ull - (uint64_t)(wi == 1))) |
+                            (mw2 & (0ull - (uint64_t)(wi == 2))) | (mw3 & (0ull - (uint64_t)(wi >= 3)));
+      const int xn = seg_tail_n - j0 - h32 * 8;          // node exists iff constant < xn
+      const int xc = rnode - j0 - h32 * 8;               // chain: visible iff constant <= xc
+      const uint64_t ml = word >> (h32 * 8);             // tree: bit `constant` of ml
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kc_ = kb * 32 + (r >> 3) * 16 + (r & 7);
+        const bool vis = kc_ < xn && (seg_chain ? kc_ <= xc : ((ml >> kc_) & 1ull) != 0ull);
+        s[r] = vis ? s[r] : -INFINITY;
+      }
+    }
+  };
+
+  // output of the finished segment: the whole row block -> out / lse; a cut one -> its slot
+  auto finish_segment = [&]() __attribute__((always_inline)) {
+    const float l_tot = sum_halves(l_run);
+    const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float lse_nat = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    if (seg_A >= j_begin && seg_E <= j_end) {
+      if (rvalid && seg_ok) {
+        uint16_t* op = (uint16_t*)a.out + ((size_t)(seg_s0 + rnode) * Hq + rhead) * D;
+#pragma unroll
+        for (int mb = 0; mb < DB; ++mb) {
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq) {
+            union { __bf16 e[4]; uint2 u; } o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o.e[e] = (__bf16)(acc[mb][rq * 4 + e] * inv_l);
+            *(uint2*)(op + mb * 32 + rq * 8 + h32 * 4) = o.u;
+          }
         }
-        __syncthreads();
-        s_tile(st, sacc);
-        mask_tile(t, 1, sacc);
-      } else {
-        s_tile(st, sacc);
+        if (h32 == 0 && a.lse) a.lse[(size_t)(seg_s0 + rnode) * Hq + rhead] = lse_nat;
       }
-      bf16x8_t pb[4];
-      float alpha;
-      if (softmax_tile(sacc, pb, alpha)) rescale(alpha);
-      pv_tile(st, pb);
+    } else {
+      const int slot = seg_A < j_begin ? 2 * wg : 2 * wg + 1;
+      const size_t prow = ((size_t)slot * Hkv + g) * kRowsPerWG + row;
+      float* po = a.part_o + prow * D;
+#pragma unroll
+      for (int mb = 0; mb < DB; ++mb)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq)
+          *(float4*)(po + mb * 32 + rq * 8 + h32 * 4) =
+              make_float4(acc[mb][rq * 4 + 0] * inv_l, acc[mb][rq * 4 + 1] * inv_l,
+                          acc[mb][rq * 4 + 2] * inv_l, acc[mb][rq * 4 + 3] * inv_l);
+      if (h32 == 0) a.part_lse[prow] = lse_nat;
     }
-    __syncthreads();
-  }
-
-  // ---- tree-tail tiles (the sequence's own nodes), staged through registers ----
-  const uint16_t* kn = (const uint16_t*)a.k_node;
-  const uint16_t* vn = (const uint16_t*)a.v_node;
-  for (int t = max(t_begin, Tp); t < t_end; ++t) {
-    uint8_t* kbase = lds[0];
-    uint8_t* vbase = lds[0] + TILE_BYTES;
-#pragma unroll
-    for (int i = 0; i < (kTileKeys * CH) / 512; ++i) {
-      const int c = tid + i * 512;                // 64 keys x CH chunks of 8 d
-      const int key = c / CH, ch = c % CH;
-      const int j = (t - Tp) * kTileKeys + key;
-      const bool valid = j < tail_n;
-      const size_t off = ((size_t)(s0 + (valid ? j : 0)) * Hkv + g) * D + ch * 8;
-      uint4 kv = *(const uint4*)(kn + off);
-      uint4 vv = *(const uint4*)(vn + off);
-      if (!valid) kv = vv = make_uint4(0u, 0u, 0u, 0u);
-      *(uint4*)(kbase + key * (D * 2) + kpos<D>(ch, key) * 16) = kv;
-      const uint32_t w4[4] = {vv.x, vv.y, vv.z, vv.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        *(uint16_t*)(vbase + (key >> 4) * SUB_BYTES + vt_off(ch * 8 + e, key & 15)) =
-            (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
-    }
-    __syncthreads();
-    f32x16_t sacc[2];
-    s_tile(0, sacc);
-    mask_tile(t, 2, sacc);
-    bf16x8_t pb[4];
-    float alpha;
-    if (softmax_tile(sacc, pb, alpha)) rescale(alpha);
-    pv_tile(0, pb);
-    __syncthreads();
-  }
-
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  const float lse_nat = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
-  if (nsplit == 1) {
-    if (!rvalid) return;
-    uint16_t* op = (uint16_t*)a.out + ((size_t)(s0 + rnode) * Hq + rhead) * D;
-#pragma unroll
-    for (int mb = 0; mb < DB; ++mb) {
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        union { __bf16 e[4]; uint2 u; } o;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o.e[e] = (__bf16)(acc[mb][rq * 4 + e] * inv_l);
-        *(uint2*)(op + mb * 32 + rq * 8 + h32 * 4) = o.u;
-      }
-    }
-    if (h32 == 0 && a.lse) a.lse[(size_t)(s0 + rnode) * Hq + rhead] = lse_nat;
-  } else {
-    float* po = a.part_o + (((size_t)item * Hkv + g) * kRowsPerWG + row) * D;
+    m_run = -INFINITY;
+    l_run = 0.f;
 #pragma unroll
     for (int mb = 0; mb < DB; ++mb)
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq)
-        *(float4*)(po + mb * 32 + rq * 8 + h32 * 4) =
-            make_float4(acc[mb][rq * 4 + 0] * inv_l, acc[mb][rq * 4 + 1] * inv_l,
-                        acc[mb][rq * 4 + 2] * inv_l, acc[mb][rq * 4 + 3] * inv_l);
-    if (h32 == 0) a.part_lse[((size_t)item * Hkv + g) * kRowsPerWG + row] = lse_nat;
+      for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
+  };
+
+  // ---- prologue: the first kStages - 1 tiles in flight, the first segment
+  int next_issue = j_begin;
+  resolve();
+  for (int k = 0; k < kStages - 1 && next_issue < j_end; ++k) {
+    issue(next_issue);
+    ++next_issue;
+    if (next_issue < j_end) resolve();
+  }
+  load_segment(r_first);
+
+  for (int j = j_begin; j < j_end; ++j) {
+    // tile j landed for every wave, and the ring slot of tile j-1 is free
+    const int after = next_issue - 1 - j;   // tiles issued after tile j
+    asm volatile("" ::: "memory");
+    if (after >= 2) wait_vm<2 * DMA_PER_TILE>();
+    else if (after == 1) wait_vm<DMA_PER_TILE>();
+    else wait_vm<0>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (next_issue < j_end) {
+      issue(next_issue);
+      ++next_issue;
+      if (next_issue < j_end) resolve();
+    }
+    const int st = (j - j_begin) & (kStages - 1);
+    const int t = j - seg_A;
+    const bool masked = needs_mask(t);
+    if (masked && t < seg_Tp) {
+      // the partial last prefix tile: zero the values of keys past the prefix (cache slots
+      // past it may hold anything, and 0 * NaN would reach the output); 16-byte units of V^T
+      // are [sub-block][32-d group][key half][32 d] of 8 keys each
+      const int lim = seg_L - t * kTileKeys;
+      uint8_t* vbase = lds[st] + TILE_BYTES;
+      for (int u = tid; u < 4 * (D / 32) * 2 * 32; u += 512) {
+        const int k0 = (u / ((D / 32) * 64)) * 16 + ((u >> 5) & 1) * 8;   // first key of the unit
+        if (k0 + 8 <= lim) continue;
+        uint4* p = (uint4*)(vbase + u * 16);
+        uint4 v = *p;
+        const int x = lim - k0;   // keys k0 + e, e >= x, are zeroed
+        v.x &= (0 < x ? 0xFFFFu : 0u) | (1 < x ? 0xFFFF0000u : 0u);
+        v.y &= (2 < x ? 0xFFFFu : 0u) | (3 < x ? 0xFFFF0000u : 0u);
+        v.z &= (4 < x ? 0xFFFFu : 0u) | (5 < x ? 0xFFFF0000u : 0u);
+        v.w &= (6 < x ? 0xFFFFu : 0u) | (7 < x ? 0xFFFF0000u : 0u);
+        *p = v;
+      }
+      __syncthreads();
+    }
+    // Four windows, each a chain of MFMAs with vector work between them (the order is fixed
+    // by scheduling barriers; operand reads run two MFMAs ahead):
+    //   A: scores of keys 0..31;  B: scores of keys 32..63 + softmax of keys 0..31;
+    //   C: P V of keys 0..31 + softmax of keys 32..63;  D: P V of keys 32..63.
+    constexpr int NPV = 2 * DB;          // P V MFMAs per half
+    constexpr int NEXP_B = KS - 2;       // exponential pieces in window B
+    constexpr int NEXP_C = NPV - 2;      // and in window C
+    f32x16_t s0, s1;
+    bf16x8_t p0[2], p1[2];
+    SoftmaxState z0, z1;
+    bf16x8_t opa = kread(st, 0, 0), opb = kread(st, 0, 1);
+    // A
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa, qreg[ks], ks == 0 ? f32x16_t{} : s0, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      const bf16x8_t nxt = ks + 2 < KS ? kread(st, 0, ks + 2) : kread(st, 1, ks + 2 - KS);
+      __builtin_amdgcn_sched_barrier(0);
+      opa = opb;
+      opb = nxt;
+    }
+    if (masked) mask(t, 0, s0);
+    // B
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa, qreg[ks], ks == 0 ? f32x16_t{} : s1, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      const bf16x8_t nxt = ks + 2 < KS ? kread(st, 1, ks + 2) : vread(st, (ks + 2 - KS) / DB, (ks + 2 - KS) % DB);
+      __builtin_amdgcn_sched_barrier(0);
+      if (ks >= 1) softmax_piece(ks - 1, NEXP_B, s0, p0, z0);
+      __builtin_amdgcn_sched_barrier(0);
+      opa = opb;
+      opb = nxt;
+    }
+#pragma unroll
+    for (int piece = KS - 1; piece < NEXP_B + 2; ++piece) softmax_piece(piece, NEXP_B, s0, p0, z0);
+    l_run = l_run * z0.alpha + z0.ps;
+    // The branch also tests ps (always >= 0, so the test adds nothing; a NaN would only rescale
+    // by alpha = 1): that keeps the exponentials in window B instead of being moved past it.
+    if (z0.need || !(z0.ps >= 0.f)) rescale(z0.alpha);
+    if (masked) mask(t, 1, s1);
+    // C
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      const int ni = i + 2;
+      acc[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa, p0[i / DB], acc[i % DB], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      const bf16x8_t nxt = ni < NPV ? vread(st, ni / DB, ni % DB) : vread(st, 2 + (ni - NPV) / DB, (ni - NPV) % DB);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i >= 1) softmax_piece(i - 1, NEXP_C, s1, p1, z1);
+      __builtin_amdgcn_sched_barrier(0);
+      opa = opb;
+      opb = nxt;
+    }
+#pragma unroll
+    for (int piece = NPV - 1; piece < NEXP_C + 2; ++piece) softmax_piece(piece, NEXP_C, s1, p1, z1);
+    l_run = l_run * z1.alpha + z1.ps;
+    if (z1.need || !(z1.ps >= 0.f)) rescale(z1.alpha);
+    // D
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      const int ni = i + 2;
+      acc[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa, p1[i / DB], acc[i % DB], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      const bf16x8_t nxt = ni < NPV ? vread(st, 2 + ni / DB, ni % DB) : opb;
+      __builtin_amdgcn_sched_barrier(0);
+      opa = opb;
+      opb = nxt;
+    }
+    if (j + 1 == min(seg_E, j_end)) {
+      finish_segment();
+      if (j + 1 < j_end) load_segment(seg_r + 1);
+    }
   }
 }
 
-// Online-softmax merge of the split partials: out = sum_s exp(lse_s - LSE) O_s.
-// One block per (row block, KV head, group of 16 rows); a thread owns 4 outputs.
-template <typename OutT>
-__global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int D, int log2G) {
-  const int rbi = blockIdx.x, g = blockIdx.y;
-  const int i0 = a.item_off[rbi];
-  const int ns = a.item_off[rbi + 1] - i0;
-  if (ns <= 1) return;
-  const int b = a.rb_seq[rbi];
-  if (b < 0 || b >= a.B) return;
-  const int NB = kRowsPerWG >> log2G;
-  const int G = 1 << log2G;
-  const int rb = rbi - a.seq_rb_off[b];
+// Copies the tree nodes' keys and values into blocks laid out like the paged cache (block_size
+// rows: keys [block, head, slot, d], values [block, head, d, slot]), zero-padded past each
+// sequence's last node, so tree-tail tiles take the same global->LDS copy path as prefix tiles.
+// One workgroup per (packed block, KV head).
+template <int D>
+__global__ __launch_bounds__(256) void pack_tail_kernel(AttnArgs a) {
+  constexpr int CH = D / 8;
+  __shared__ uint16_t vs[64][D + 8];   // values of the block, [slot][d]
+  if (a.status[0] & TAV_DEV_PLAN_MISMATCH) return;
+  const int tb = blockIdx.x, g = blockIdx.y, bs = a.block_size, Hkv = a.Hkv;
+  int lo = 0, hi = a.B;  // sequence of this block: largest b with tail_blk[b] <= tb
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.tail_blk[mid] <= tb) lo = mid; else hi = mid;
+  }
+  const int b = lo;
   const int s0 = a.node_offsets[b];
   const int n = a.node_offsets[b + 1] - s0;
-  const int node0 = rb * NB;
+  const int node_base = (tb - a.tail_blk[b]) * bs;
+  const uint16_t* kn = (const uint16_t*)a.k_node;
+  const uint16_t* vn = (const uint16_t*)a.v_node;
+  uint16_t* kt = (uint16_t*)a.k_tail;
+  uint16_t* vt = (uint16_t*)a.v_tail;
+  for (int c = threadIdx.x; c < bs * CH; c += blockDim.x) {
+    const int slot = c / CH, ch = c % CH;
+    const int node = node_base + slot;
+    uint4 kv = make_uint4(0u, 0u, 0u, 0u), vv = kv;
+    if (node < n) {
+      const size_t off = ((size_t)(s0 + node) * Hkv + g) * D + ch * 8;
+      kv = *(const uint4*)(kn + off);
+      vv = *(const uint4*)(vn + off);
+    }
+    *(uint4*)(kt + (((size_t)tb * Hkv + g) * bs + slot) * D + ch * 8) = kv;
+    const uint32_t w4[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vs[slot][ch * 8 + e] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+  }
+  __syncthreads();
+  const int groups = bs / 8;
+  for (int c = threadIdx.x; c < D * groups; c += blockDim.x) {
+    const int d = c / groups, sg = c % groups;
+    uint32_t w4[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w4[e] = (uint32_t)vs[sg * 8 + 2 * e][d] | ((uint32_t)vs[sg * 8 + 2 * e + 1][d] << 16);
+    *(uint4*)(vt + (((size_t)tb * Hkv + g) * D + d) * bs + sg * 8) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+  }
+}
+
+// Online-softmax merge of the pieces of a row block cut between workgroups:
+// out = sum_s exp(lse_s - LSE) O_s.  Row block r's key tiles [A, E) were cut into the pieces of
+// workgroups A/C .. (E-1)/C; the first piece sits in slot 2w+1 of its workgroup (its last
+// segment), the others in slot 2w (their workgroup's first segment).  One block per (row block,
+// KV head, group of 16 rows); a thread owns 4 outputs.
+template <typename OutT>
+__global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int D, int log2G) {
+  if (a.status[0] & TAV_DEV_PLAN_MISMATCH) return;
+  const int r = blockIdx.x, g = blockIdx.y;
+  const int rA = a.rb_tile[r], rE = a.rb_tile[r + 1];
+  const int wf = rA / a.C, wl = (rE - 1) / a.C;
+  if (wf == wl) return;  // one workgroup held the whole row block
+  const int b = a.rb_seq[r];
+  if (b < 0 || b >= a.B) return;
+  const int s0 = a.node_offsets[b];
+  const int n = a.node_offsets[b + 1] - s0;
+  if (a.is_chain[b] == 0 && n > kMaxTreeNodes) return;  // rejected by tree preparation
+  const int NB = kRowsPerWG >> log2G;
+  const int G = 1 << log2G;
+  const int node0 = (r - a.seq_rb_off[b]) * NB;
   const int nodes_here = min(NB, n - node0);
   const int DQ = D / 4;
   for (int task = threadIdx.x; task < 16 * DQ; task += blockDim.x) {
@@ -419,18 +632,21 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int D, int log2G
     const int node = s0 + node0 + (row >> log2G);
     const int head = g * G + (row & (G - 1));
     float M = -INFINITY;
-    for (int s = 0; s < ns; ++s)
-      M = fmaxf(M, a.part_lse[((size_t)(i0 + s) * a.Hkv + g) * kRowsPerWG + row]);
+    for (int w = wf; w <= wl; ++w) {
+      const int slot = w == wf ? 2 * w + 1 : 2 * w;
+      M = fmaxf(M, a.part_lse[((size_t)slot * a.Hkv + g) * kRowsPerWG + row]);
+    }
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float den = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const size_t base = ((size_t)(i0 + s) * a.Hkv + g) * kRowsPerWG + row;
+    for (int w = wf; w <= wl; ++w) {
+      const int slot = w == wf ? 2 * w + 1 : 2 * w;
+      const size_t base = ((size_t)slot * a.Hkv + g) * kRowsPerWG + row;
       const float ls = a.part_lse[base];
       if (ls == -INFINITY) continue;
-      const float w = __expf(ls - M);
+      const float wgt = __expf(ls - M);
       const float4 o = *(const float4*)(a.part_o + base * D + dq * 4);
-      den += w;
-      acc.x += w * o.x; acc.y += w * o.y; acc.z += w * o.z; acc.w += w * o.w;
+      den += wgt;
+      acc.x += wgt * o.x; acc.y += wgt * o.y; acc.z += wgt * o.z; acc.w += wgt * o.w;
     }
     const float inv = den > 0.f ? 1.f / den : 0.f;
     OutT* op = (OutT*)a.out + ((size_t)node * a.Hq + head) * D + dq * 4;
@@ -555,7 +771,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
 
 template <int D>
 hipError_t launch_bf16_d(const Plan& p, const AttnArgs& a, hipStream_t s) {
-  dim3 grid(p.total_items, p.Hkv);
+  dim3 grid(p.W, p.Hkv);
   switch (p.log2G) {
     case 0: attn_bf16_kernel<D, 0><<<grid, 512, 0, s>>>(a); break;
     case 1: attn_bf16_kernel<D, 1><<<grid, 512, 0, s>>>(a); break;
@@ -569,8 +785,16 @@ hipError_t launch_bf16_d(const Plan& p, const AttnArgs& a, hipStream_t s) {
 
 }  // namespace
 
+hipError_t launch_pack_tail(const Plan& p, const AttnArgs& a, hipStream_t s) {
+  if (p.tail_blocks == 0) return hipSuccess;
+  dim3 grid(p.tail_blocks, p.Hkv);
+  if (p.D == 128) pack_tail_kernel<128><<<grid, 256, 0, s>>>(a);
+  else pack_tail_kernel<64><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_bf16(const Plan& p, const AttnArgs& a, hipStream_t s) {
-  if (p.total_items == 0) return hipSuccess;
+  if (p.W == 0) return hipSuccess;
   return p.D == 128 ? launch_bf16_d<128>(p, a, s) : launch_bf16_d<64>(p, a, s);
 }
 
@@ -582,7 +806,7 @@ hipError_t launch_attn_f32(const Plan& p, const AttnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_merge(const Plan& p, const AttnArgs& a, bool bf16_out, hipStream_t s) {
-  if (!p.any_split) return hipSuccess;
+  if (p.W <= 1) return hipSuccess;
   dim3 grid(p.total_rb, p.Hkv, kRowsPerWG / 16);
   if (bf16_out) merge_kernel<__bf16><<<grid, 256, 0, s>>>(a, p.D, p.log2G);
   else merge_kernel<float><<<grid, 256, 0, s>>>(a, p.D, p.log2G);

@@ -41,56 +41,82 @@ __device__ int block_exclusive_scan(int v, int* lds, int* total) {
   return excl;
 }
 
-// One 1024-thread block: seq_rb_off[B+1] (row blocks per sequence), rb_seq
-// and item_off[total_rb+1] (work items per row block), identical to the host plan.
+// One 1024-thread block: seq_rb_off[B+1] (row blocks per sequence), rb_seq,
+// rb_tile[total_rb+1] (first key tile of each row block, per KV head) and
+// tail_blk[B+1] (first packed node block of each sequence), identical to the
+// host plan; a disagreement with the host's totals sets TAV_DEV_PLAN_MISMATCH.
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* node_offsets,
                                                      const int32_t* prefix_len, int B, int NB,
-                                                     int tiles_per_split, int total_rb_host,
-                                                     int total_items_host, int32_t* seq_rb_off,
-                                                     int32_t* rb_seq, int32_t* item_off,
-                                                     uint32_t* status) {
+                                                     int bs, int total_rb_host, int tiles_host,
+                                                     int tail_blocks_host, int C, int W,
+                                                     int32_t* seq_rb_off, int32_t* rb_seq,
+                                                     int32_t* rb_tile, int32_t* tail_blk,
+                                                     int32_t* wg_rb, uint32_t* status) {
   __shared__ int lds[16];
-  int carry = 0;
+  int carry = 0, bcarry = 0;
   for (int base = 0; base < B; base += 1024) {
-    int b = base + threadIdx.x;
-    int cnt = 0;
-    if (b < B) cnt = (node_offsets[b + 1] - node_offsets[b] + NB - 1) / NB;
-    int tot;
-    int ex = block_exclusive_scan(cnt, lds, &tot);
-    if (b < B) seq_rb_off[b] = carry + ex;
+    const int b = base + threadIdx.x;
+    int cnt = 0, nblk = 0;
+    if (b < B) {
+      const int n = node_offsets[b + 1] - node_offsets[b];
+      cnt = (n + NB - 1) / NB;
+      nblk = (n + bs - 1) / bs;
+    }
+    int tot, btot;
+    const int ex = block_exclusive_scan(cnt, lds, &tot);
+    const int bex = block_exclusive_scan(nblk, lds, &btot);
+    if (b < B) {
+      seq_rb_off[b] = carry + ex;
+      tail_blk[b] = bcarry + bex;
+    }
     carry += tot;
+    bcarry += btot;
   }
-  if (threadIdx.x == 0) seq_rb_off[B] = carry;
+  if (threadIdx.x == 0) {
+    seq_rb_off[B] = carry;
+    tail_blk[B] = bcarry;
+  }
   const int total_rb = carry;
-  if (total_rb != total_rb_host) {
+  if (total_rb != total_rb_host || bcarry != tail_blocks_host) {
     if (threadIdx.x == 0) atomicOr(status, (uint32_t)TAV_DEV_PLAN_MISMATCH);
     return;
   }
   __syncthreads();
-  int icarry = 0;
+  int tcarry = 0;
   for (int base = 0; base < total_rb; base += 1024) {
-    int r = base + threadIdx.x;
+    const int r = base + threadIdx.x;
     int cnt = 0;
     if (r < total_rb) {
       int lo = 0, hi = B;  // largest b with seq_rb_off[b] <= r
       while (hi - lo > 1) {
-        int mid = (lo + hi) >> 1;
+        const int mid = (lo + hi) >> 1;
         if (seq_rb_off[mid] <= r) lo = mid; else hi = mid;
       }
-      int b = lo;
-      int rb = r - seq_rb_off[b];
-      int n = node_offsets[b + 1] - node_offsets[b];
-      cnt = ceil_div(rb_tiles(prefix_len[b], n, rb, NB), tiles_per_split);
+      const int b = lo;
+      const int n = node_offsets[b + 1] - node_offsets[b];
+      cnt = rb_tiles(prefix_len[b], n, r - seq_rb_off[b], NB);
       rb_seq[r] = b;
     }
     int tot;
-    int ex = block_exclusive_scan(cnt, lds, &tot);
-    if (r < total_rb) item_off[r] = icarry + ex;
-    icarry += tot;
+    const int ex = block_exclusive_scan(cnt, lds, &tot);
+    if (r < total_rb) rb_tile[r] = tcarry + ex;
+    tcarry += tot;
   }
   if (threadIdx.x == 0) {
-    item_off[total_rb] = icarry;
-    if (icarry != total_items_host) atomicOr(status, (uint32_t)TAV_DEV_PLAN_MISMATCH);
+    rb_tile[total_rb] = tcarry;
+    if (tcarry != tiles_host) atomicOr(status, (uint32_t)TAV_DEV_PLAN_MISMATCH);
+  }
+  if (tcarry != tiles_host) return;
+  __syncthreads();
+  // the row block holding key tile w * C, for each attention workgroup w
+  for (int w = threadIdx.x; w < W; w += blockDim.x) {
+    const int j = w * C;
+    int lo = 0, hi = total_rb;  // largest r with rb_tile[r] <= j
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (rb_tile[mid] <= j) lo = mid; else hi = mid;
+    }
+    wg_rb[w] = lo;
   }
 }
 
@@ -169,10 +195,11 @@ hipError_t launch_clear_status(uint32_t* status, hipStream_t s) {
 }
 
 hipError_t launch_plan(const Plan& p, const int32_t* node_offsets, const int32_t* prefix_len,
-                       int32_t* seq_rb_off, int32_t* rb_seq, int32_t* item_off, uint32_t* status,
-                       hipStream_t s) {
-  plan_kernel<<<1, 1024, 0, s>>>(node_offsets, prefix_len, p.B, p.NB, p.tiles_per_split,
-                                 p.total_rb, p.total_items, seq_rb_off, rb_seq, item_off, status);
+                       int32_t* seq_rb_off, int32_t* rb_seq, int32_t* rb_tile, int32_t* tail_blk,
+                       int32_t* wg_rb, uint32_t* status, hipStream_t s) {
+  plan_kernel<<<1, 1024, 0, s>>>(node_offsets, prefix_len, p.B, p.NB, p.bs, p.total_rb,
+                                 p.tiles_per_head, p.tail_blocks, p.C, p.W, seq_rb_off, rb_seq,
+                                 rb_tile, tail_blk, wg_rb, status);
   return hipGetLastError();
 }
 

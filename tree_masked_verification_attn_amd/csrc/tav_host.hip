@@ -45,7 +45,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 constexpr int kTargetWorkgroups = 256;  // one round of one workgroup per MI355X compute unit
-constexpr int kMinTilesPerSplit = 8;    // at least 512 keys per split
+constexpr int kMinTilesPerWG = 4;       // at least 256 keys per attention workgroup
 
 int log2_exact(int x) {
   int l = 0;
@@ -119,42 +119,26 @@ tav_status make_plan(const tav_problem* p, const tav_presto_io* pr, Plan* out) {
   P.G = P.Hq / P.Hkv;
   P.log2G = log2_exact(P.G);
   P.NB = kRowsPerWG >> P.log2G;
-  int64_t tiles = 0;
+  P.bs = p->block_size;
+  P.lbs = log2_exact(p->block_size);
+  int64_t tiles = 0, tail_blocks = 0;
   for (int b = 0; b < P.B; ++b) {
     const int n = p->node_offsets_host[b + 1] - p->node_offsets_host[b];
     const int nrb = ceil_div(n, P.NB);
     P.total_rb += nrb;
     for (int rb = 0; rb < nrb; ++rb) tiles += rb_tiles(p->prefix_len_host[b], n, rb, P.NB);
+    tail_blocks += ceil_div(n, P.bs);
   }
-  tiles *= P.Hkv;
-  // key tiles per work item: the smallest count (from an even share of kTargetWorkgroups)
-  // whose item total stays within kTargetWorkgroups, so no nearly empty extra round of
-  // workgroups is left for the (one workgroup per CU) attention kernel
-  int64_t tps = (tiles + kTargetWorkgroups - 1) / kTargetWorkgroups;
-  P.tiles_per_split = (int)(tps < kMinTilesPerSplit ? kMinTilesPerSplit : tps);
+  if (tiles > (int64_t)1 << 30 || tail_blocks > (int64_t)1 << 30)
+    return fail(TAV_ERR_UNSUPPORTED, "problem too large: %lld key tiles per KV head", (long long)tiles);
+  P.tiles_per_head = (int)tiles;
+  P.tail_blocks = (int)tail_blocks;
   if (p->dtype == TAV_BF16) {
-    for (;;) {
-      int64_t items = 0;
-      int max_t = 0;
-      for (int b = 0; b < P.B; ++b) {
-        const int n = p->node_offsets_host[b + 1] - p->node_offsets_host[b];
-        for (int rb = 0; rb < ceil_div(n, P.NB); ++rb) {
-          const int tr = rb_tiles(p->prefix_len_host[b], n, rb, P.NB);
-          items += ceil_div(tr, P.tiles_per_split);
-          max_t = tr > max_t ? tr : max_t;
-        }
-      }
-      if (items * P.Hkv <= kTargetWorkgroups || P.tiles_per_split >= max_t) break;
-      ++P.tiles_per_split;
-    }
-    for (int b = 0; b < P.B; ++b) {
-      const int n = p->node_offsets_host[b + 1] - p->node_offsets_host[b];
-      for (int rb = 0; rb < ceil_div(n, P.NB); ++rb) {
-        const int c = ceil_div(rb_tiles(p->prefix_len_host[b], n, rb, P.NB), P.tiles_per_split);
-        P.total_items += c;
-        if (c > 1) P.any_split = true;
-      }
-    }
+    // equal ranges of C key tiles, about one workgroup per compute unit over all KV heads
+    const int target = kTargetWorkgroups / P.Hkv > 1 ? kTargetWorkgroups / P.Hkv : 1;
+    P.C = ceil_div(P.tiles_per_head, target);
+    if (P.C < kMinTilesPerWG) P.C = kMinTilesPerWG;
+    P.W = ceil_div(P.tiles_per_head, P.C);
   }
   size_t o = 0;
   P.off_status = o; o = align_up(o + 256);
@@ -162,11 +146,18 @@ tav_status make_plan(const tav_problem* p, const tav_presto_io* pr, Plan* out) {
   P.off_mask = o; o = align_up(o + (size_t)P.N * kMaskWords * 8);
   P.off_seq_rb = o; o = align_up(o + (size_t)(P.B + 1) * 4);
   P.off_rb_seq = o; o = align_up(o + (size_t)P.total_rb * 4);
-  P.off_item_off = o; o = align_up(o + (size_t)(P.total_rb + 1) * 4);
+  P.off_rb_tile = o; o = align_up(o + (size_t)(P.total_rb + 1) * 4);
+  P.off_tail_blk = o; o = align_up(o + (size_t)(P.B + 1) * 4);
+  P.off_wg_rb = o; o = align_up(o + (size_t)P.W * 4);
+  const size_t tail_bytes = (size_t)P.tail_blocks * P.Hkv * P.bs * P.D * 2;
+  P.off_ktail = o;
+  if (p->dtype == TAV_BF16) o = align_up(o + tail_bytes);
+  P.off_vtail = o;
+  if (p->dtype == TAV_BF16) o = align_up(o + tail_bytes);
   P.off_part_o = o;
-  if (P.any_split) o = align_up(o + (size_t)P.total_items * P.Hkv * kRowsPerWG * P.D * 4);
+  o = align_up(o + (size_t)2 * P.W * P.Hkv * kRowsPerWG * P.D * 4);
   P.off_part_lse = o;
-  if (P.any_split) o = align_up(o + (size_t)P.total_items * P.Hkv * kRowsPerWG * 4);
+  o = align_up(o + (size_t)2 * P.W * P.Hkv * kRowsPerWG * 4);
   P.off_stats = o; o = align_up(o + (size_t)P.N * 3 * 4);
   P.off_term = o; o = align_up(o + (size_t)P.N * 4);
   P.off_child_p = o; o = align_up(o + (size_t)P.N * 8);
@@ -252,12 +243,17 @@ AttnArgs attn_args(const tav_problem* p, const Plan& P, const tav_attn_io* io, v
   a.mask = ws_at<uint64_t>(ws, P.off_mask);
   a.seq_rb_off = ws_at<int32_t>(ws, P.off_seq_rb);
   a.rb_seq = ws_at<int32_t>(ws, P.off_rb_seq);
-  a.item_off = ws_at<int32_t>(ws, P.off_item_off);
+  a.rb_tile = ws_at<int32_t>(ws, P.off_rb_tile);
+  a.tail_blk = ws_at<int32_t>(ws, P.off_tail_blk);
+  a.wg_rb = ws_at<int32_t>(ws, P.off_wg_rb);
+  a.k_tail = ws_at<void>(ws, P.off_ktail);
+  a.v_tail = ws_at<void>(ws, P.off_vtail);
   a.part_o = ws_at<float>(ws, P.off_part_o);
   a.part_lse = ws_at<float>(ws, P.off_part_lse);
   a.status = ws_at<uint32_t>(ws, P.off_status);
-  a.B = P.B; a.Hq = P.Hq; a.Hkv = P.Hkv; a.total_rb = P.total_rb; a.total_items = P.total_items;
-  a.tiles_per_split = P.tiles_per_split; a.block_size = p->block_size; a.num_blocks = p->num_blocks;
+  a.B = P.B; a.Hq = P.Hq; a.Hkv = P.Hkv; a.total_rb = P.total_rb;
+  a.tiles_per_head = P.tiles_per_head; a.C = P.C; a.W = P.W; a.tail_blocks = P.tail_blocks;
+  a.block_size = p->block_size; a.num_blocks = p->num_blocks;
   a.max_blocks = p->max_blocks_per_seq;
   a.scale = p->sm_scale > 0.f ? p->sm_scale : 1.f / sqrtf((float)p->head_dim);
   return a;
@@ -316,7 +312,9 @@ tav_status enqueue_attention(const tav_problem* p, const Plan& P, const tav_attn
   const AttnArgs a = attn_args(p, P, io, ws);
   if (p->dtype == TAV_BF16) {
     TAV_HIP(launch_plan(P, p->node_offsets, p->prefix_len, const_cast<int32_t*>(a.seq_rb_off),
-                        const_cast<int32_t*>(a.rb_seq), const_cast<int32_t*>(a.item_off), a.status, s));
+                        const_cast<int32_t*>(a.rb_seq), const_cast<int32_t*>(a.rb_tile),
+                        const_cast<int32_t*>(a.tail_blk), const_cast<int32_t*>(a.wg_rb), a.status, s));
+    TAV_HIP(launch_pack_tail(P, a, s));
     hipEvent_t ev0 = nullptr, ev1 = nullptr;
     if (g_timing.on) {
       const tav_status st = timing_pair(&ev0, &ev1);

@@ -23,22 +23,28 @@ constexpr int kRecKidsMax = 12;    // children held in the record
 constexpr int kCounterWord = 16;   // status block: word 0 = status bits, word 16 = a counter
 
 // Work decomposition of the attention pass.  A "row block" is up to
-// kRowsPerWG / G consecutive nodes of one sequence; a "work item" is one
-// contiguous range of key tiles (prefix tiles first, then tree-tail tiles) of
-// one row block.  The same integer formulas run on the host (grid sizes,
-// workspace) and on the device (plan_kernel), so both agree on the item list.
+// kRowsPerWG / G consecutive nodes of one sequence; it sees ceil(L / 64) prefix
+// key tiles followed by the tiles of its sequence's tree nodes.  Per KV head,
+// the key tiles of all row blocks are concatenated in row-block order
+// (rb_tile[r] = first tile of row block r) and cut into W equal ranges of C
+// tiles, one workgroup each; a workgroup crosses row-block boundaries, and a
+// row block cut between workgroups is finished by the merge kernel.  The same
+// integer formulas run on the host (grid sizes, workspace) and on the device
+// (plan_kernel), so both agree.
 struct Plan {
   int B = 0, N = 0, Hq = 0, Hkv = 0, D = 0, G = 0, log2G = 0, NB = 0;
+  int bs = 16, lbs = 4;   // KV block size and its log2
   int total_rb = 0;       // row blocks over all sequences
-  int tiles_per_split = 1;
-  int total_items = 0;    // work items over all row blocks
-  bool any_split = false; // some row block has more than one item
-  int max_children = 0;
+  int tiles_per_head = 0; // key tiles per KV head over all row blocks
+  int C = 0;              // key tiles per attention workgroup
+  int W = 0;              // attention workgroups per KV head
+  int tail_blocks = 0;    // packed blocks (block_size rows) of tree-node keys / values
   // workspace layout (byte offsets)
   size_t off_status = 0, off_chain = 0, off_mask = 0, off_seq_rb = 0, off_rb_seq = 0,
-         off_item_off = 0, off_part_o = 0, off_part_lse = 0, off_stats = 0, off_term = 0,
-         off_child_p = 0, off_child_q = 0, off_presto = 0, off_sl_m = 0, off_sl_s = 0,
-         off_sl_z = 0, off_ch_w = 0, off_dlist = 0, off_rec = 0, total = 0;
+         off_rb_tile = 0, off_tail_blk = 0, off_wg_rb = 0, off_ktail = 0, off_vtail = 0, off_part_o = 0,
+         off_part_lse = 0, off_stats = 0, off_term = 0, off_child_p = 0, off_child_q = 0,
+         off_presto = 0, off_sl_m = 0, off_sl_s = 0, off_sl_z = 0, off_ch_w = 0, off_dlist = 0,
+         off_rec = 0, total = 0;
   int nsl = 0, nch = 0;   // vocabulary slices and chunks (64 units) per row
 };
 
@@ -65,13 +71,17 @@ struct AttnArgs {
   const int32_t* prefix_len;
   const uint8_t* is_chain;
   const uint64_t* mask;
-  const int32_t* seq_rb_off;
-  const int32_t* rb_seq;
-  const int32_t* item_off;
-  float* part_o;
-  float* part_lse;
+  const int32_t* seq_rb_off;  // [B+1] first row block of each sequence
+  const int32_t* rb_seq;      // [total_rb] sequence of each row block
+  const int32_t* rb_tile;     // [total_rb+1] first key tile (per KV head) of each row block
+  const int32_t* tail_blk;    // [B+1] first packed node block of each sequence
+  const int32_t* wg_rb;       // [W] row block holding the first key tile of each workgroup
+  void* k_tail;               // [tail_blocks, Hkv, bs, D] node keys in the cache layout
+  void* v_tail;               // [tail_blocks, Hkv, D, bs] node values in the cache layout
+  float* part_o;              // [2W, Hkv, 256, D] partial outputs of cut row blocks
+  float* part_lse;            // [2W, Hkv, 256]
   uint32_t* status;
-  int B, Hq, Hkv, total_rb, total_items, tiles_per_split, block_size, num_blocks, max_blocks;
+  int B, Hq, Hkv, total_rb, tiles_per_head, C, W, tail_blocks, block_size, num_blocks, max_blocks;
   float scale;        // softmax scale (natural)
 };
 
@@ -146,8 +156,9 @@ struct PrestoArgs {
 // of the launch.
 hipError_t launch_clear_status(uint32_t* status, hipStream_t s);
 hipError_t launch_plan(const Plan& p, const int32_t* node_offsets, const int32_t* prefix_len,
-                       int32_t* seq_rb_off, int32_t* rb_seq, int32_t* item_off, uint32_t* status,
-                       hipStream_t s);
+                       int32_t* seq_rb_off, int32_t* rb_seq, int32_t* rb_tile, int32_t* tail_blk,
+                       int32_t* wg_rb, uint32_t* status, hipStream_t s);
+hipError_t launch_pack_tail(const Plan& p, const AttnArgs& a, hipStream_t s);
 hipError_t launch_prep(const Plan& p, const int32_t* node_offsets, const int32_t* prefix_len,
                        const int32_t* parent, uint8_t* chain_ws, uint64_t* mask_ws,
                        const tav_tree_out* out, uint32_t* status, hipStream_t s);
