@@ -116,6 +116,8 @@ def main():
     ap.add_argument("--workload", default="c3", choices=["c2", "c3", "c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copies", type=int, default=2)
+    ap.add_argument("--one-stream", action="store_true",
+                    help="run verification after attention on the same stream (no overlap)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -143,7 +145,7 @@ def main():
     copies = [wdev.upload(w, "cuda") for _ in range(max(1, args.copies))]
     ws_v = [torch.zeros_like(c.workspace) for c in copies]     # verification's own workspace
     sa = torch.cuda.Stream()
-    sv = torch.cuda.Stream()
+    sv = sa if args.one_stream else torch.cuda.Stream()
     torch.cuda.synchronize()
 
     def step(i, ev=None):
