@@ -184,18 +184,16 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h32 = lane >> 5, l32 = lane & 31;
   const int wg = blockIdx.x, g = blockIdx.y;
-  const int j_begin = wg * a.C;
-  const int j_end = min(a.tiles_per_head, j_begin + a.C);
+  const int j_begin = a.wg_tile[wg];
+  const int j_end = a.wg_tile[wg + 1];
   if (j_begin >= j_end) return;
   const int Hq = a.Hq, Hkv = a.Hkv, bs = a.block_size;
   const int lbs = __builtin_ctz(bs);   // block sizes are powers of two
   const const_i32_ptr rb_tile = (const_i32_ptr)a.rb_tile;
   const const_i32_ptr rb_seq = (const_i32_ptr)a.rb_seq;
-  const const_i32_ptr seq_rb_off = (const_i32_ptr)a.seq_rb_off;
-  const const_i32_ptr node_off = (const_i32_ptr)a.node_offsets;
   const const_i32_ptr pref_len = (const_i32_ptr)a.prefix_len;
   const const_i32_ptr tail_blk = (const_i32_ptr)a.tail_blk;
-  const const_u8_ptr is_chain = (const const_u8_ptr)a.is_chain;
+  const const_i32_ptr rb_meta = (const_i32_ptr)a.rb_meta;
   const uint16_t* kc = (const uint16_t*)a.k_cache;
   const uint16_t* vc = (const uint16_t*)a.v_cache;
   const uint16_t* ktl = (const uint16_t*)a.k_tail;
@@ -244,42 +242,66 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
   bool rvalid = false;
   int rhead = 0;
   bf16x8_t qreg[KS];
-  uint64_t mw0 = 0, mw1 = 0, mw2 = 0, mw3 = 0;   // this row's ancestor mask (trees)
-  auto load_segment = [&](int r) __attribute__((always_inline)) {
-    const int b = rb_seq[r];
+  uint4 mwa = make_uint4(0u, 0u, 0u, 0u), mwb = mwa;   // this row's ancestor mask words (trees)
+  // start_segment(r): row block r's record (one scalar load), this lane's row, and its query and
+  // ancestor mask words in qreg / mwa, mwb.  The loads and the wait for them are one assembly
+  // statement: a compiler-placed wait would sit at the registers' first use, after later copies
+  // to LDS have been issued, and (the counts being in order) wait for those too.  The wait covers
+  // every copy issued before it.  Rows past the block's nodes read node 0's query (finite values
+  // whose outputs are dropped); rows without mask words read node 0's and clear them.
+  auto start_segment = [&](int r) __attribute__((always_inline)) {
+    const const_i32_ptr m = rb_meta + (size_t)r * kMetaWords;
     seg_r = r;
-    seg_A = rb_tile[r];
-    seg_E = rb_tile[r + 1];
-    seg_s0 = node_off[b];
-    seg_n = node_off[b + 1] - seg_s0;
-    seg_L = pref_len[b];
+    seg_A = m[kMetaTile0];
+    seg_E = m[kMetaTileEnd];
+    seg_s0 = m[kMetaS0];
+    seg_n = m[kMetaN];
+    seg_L = m[kMetaL];
+    seg_node0 = m[kMetaNode0];
+    seg_tail_n = m[kMetaTailN];
+    const int flags = m[kMetaFlags];
+    seg_chain = (flags & 1) != 0;
+    seg_ok = (flags & 2) != 0;   // larger trees were rejected by preparation
     seg_Tp = (seg_L + kTileKeys - 1) / kTileKeys;
-    seg_node0 = (r - seq_rb_off[b]) * NB;
-    seg_tail_n = min(seg_n, seg_node0 + NB);
-    seg_chain = is_chain[b] != 0;
-    seg_ok = seg_chain || seg_n <= kMaxTreeNodes;   // larger trees were rejected by preparation
     rnode = seg_node0 + (row >> LOG2G);
     rvalid = (row >> LOG2G) < min(NB, seg_n - seg_node0);
     rhead = g * G + (row & (G - 1));
-    // the mask words are loaded before q: the wait for the last q load then covers them too
-    mw0 = mw1 = mw2 = mw3 = 0ull;
-    if (!seg_chain && seg_ok && rvalid) {
-      const uint4* mp = (const uint4*)(a.mask + (size_t)(seg_s0 + rnode) * kMaskWords);
-      const uint4 m01 = mp[0], m23 = mp[1];
-      mw0 = (uint64_t)m01.x | ((uint64_t)m01.y << 32);
-      mw1 = (uint64_t)m01.z | ((uint64_t)m01.w << 32);
-      mw2 = (uint64_t)m23.x | ((uint64_t)m23.y << 32);
-      mw3 = (uint64_t)m23.z | ((uint64_t)m23.w << 32);
+    const bool mask_rows = !seg_chain && seg_ok && rvalid;
+    const int qnode = seg_s0 + (rvalid ? rnode : 0);
+    const uint4* mp = (const uint4*)(a.mask + (size_t)(mask_rows ? qnode : seg_s0) * kMaskWords);
+    const uint16_t* qp = (const uint16_t*)a.q + ((size_t)qnode * Hq + rhead) * D + h32 * 8;
+    static_assert(KS == 4 || KS == 8, "query registers");
+    if constexpr (KS == 8) {
+      asm volatile(
+          "global_load_dwordx4 %0, %10, off\n\t"
+          "global_load_dwordx4 %1, %10, off offset:32\n\t"
+          "global_load_dwordx4 %2, %10, off offset:64\n\t"
+          "global_load_dwordx4 %3, %10, off offset:96\n\t"
+          "global_load_dwordx4 %4, %10, off offset:128\n\t"
+          "global_load_dwordx4 %5, %10, off offset:160\n\t"
+          "global_load_dwordx4 %6, %10, off offset:192\n\t"
+          "global_load_dwordx4 %7, %10, off offset:224\n\t"
+          "global_load_dwordx4 %8, %11, off\n\t"
+          "global_load_dwordx4 %9, %11, off offset:16\n\t"
+          "s_waitcnt vmcnt(0)"
+          : "=&v"(qreg[0]), "=&v"(qreg[1]), "=&v"(qreg[2]), "=&v"(qreg[3]), "=&v"(qreg[4]),
+            "=&v"(qreg[5]), "=&v"(qreg[6]), "=&v"(qreg[7]), "=&v"(mwa), "=&v"(mwb)
+          : "v"(qp), "v"(mp)
+          : "memory");
+    } else {
+      asm volatile(
+          "global_load_dwordx4 %0, %6, off\n\t"
+          "global_load_dwordx4 %1, %6, off offset:32\n\t"
+          "global_load_dwordx4 %2, %6, off offset:64\n\t"
+          "global_load_dwordx4 %3, %6, off offset:96\n\t"
+          "global_load_dwordx4 %4, %7, off\n\t"
+          "global_load_dwordx4 %5, %7, off offset:16\n\t"
+          "s_waitcnt vmcnt(0)"
+          : "=&v"(qreg[0]), "=&v"(qreg[1]), "=&v"(qreg[2]), "=&v"(qreg[3]), "=&v"(mwa), "=&v"(mwb)
+          : "v"(qp), "v"(mp)
+          : "memory");
     }
-    const uint16_t* qp = (const uint16_t*)a.q +
-                         ((size_t)(seg_s0 + (rvalid ? rnode : 0)) * Hq + rhead) * D + h32 * 8;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      Bf16Pack8 t;
-      t.u = *(const uint4*)(qp + ks * 16);
-      if (!rvalid) t.u = make_uint4(0u, 0u, 0u, 0u);
-      qreg[ks] = t.v;
-    }
+    if (!mask_rows) mwa = mwb = make_uint4(0u, 0u, 0u, 0u);
   };
 
   const float c2 = a.scale * kLog2e;      // score -> log2 units
@@ -377,6 +399,10 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
       const int wi = t - seg_Tp;
       // pick the word arithmetically (a select between the words could become a dynamically
       // indexed access)
+      const uint64_t mw0 = (uint64_t)mwa.x | ((uint64_t)mwa.y << 32);
+      const uint64_t mw1 = (uint64_t)mwa.z | ((uint64_t)mwa.w << 32);
+      const uint64_t mw2 = (uint64_t)mwb.x | ((uint64_t)mwb.y << 32);
+      const uint64_t mw3 = (uint64_t)mwb.z | ((uint64_t)mwb.w << 32);
       const uint64_t word = (mw0 & (0ull - (uint64_t)(wi == 0))) | (mw1 & (0ull - (uint64_t)(wi == 1))) |
                             (mw2 & (0ull - (uint64_t)(wi == 2))) | (mw3 & (0ull - (uint64_t)(wi >= 3)));
       const int xn = seg_tail_n - j0 - h32 * 8;          // node exists iff constant < xn
@@ -392,13 +418,14 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
   };
 
   // output of the finished segment: the whole row block -> out / lse; a cut one -> its slot
-  auto finish_segment = [&]() __attribute__((always_inline)) {
+  struct OutRow { int A, E, s0, node; bool valid; };   // a finished segment's output row
+  auto finish_segment = [&](const OutRow& o_) __attribute__((always_inline)) {
     const float l_tot = sum_halves(l_run);
     const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const float lse_nat = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
-    if (seg_A >= j_begin && seg_E <= j_end) {
-      if (rvalid && seg_ok) {
-        uint16_t* op = (uint16_t*)a.out + ((size_t)(seg_s0 + rnode) * Hq + rhead) * D;
+    if (o_.A >= j_begin && o_.E <= j_end) {
+      if (o_.valid) {
+        uint16_t* op = (uint16_t*)a.out + ((size_t)(o_.s0 + o_.node) * Hq + rhead) * D;
 #pragma unroll
         for (int mb = 0; mb < DB; ++mb) {
 #pragma unroll
@@ -409,10 +436,10 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
             *(uint2*)(op + mb * 32 + rq * 8 + h32 * 4) = o.u;
           }
         }
-        if (h32 == 0 && a.lse) a.lse[(size_t)(seg_s0 + rnode) * Hq + rhead] = lse_nat;
+        if (h32 == 0 && a.lse) a.lse[(size_t)(o_.s0 + o_.node) * Hq + rhead] = lse_nat;
       }
     } else {
-      const int slot = seg_A < j_begin ? 2 * wg : 2 * wg + 1;
+      const int slot = o_.A < j_begin ? 2 * wg : 2 * wg + 1;
       const size_t prow = ((size_t)slot * Hkv + g) * kRowsPerWG + row;
       float* po = a.part_o + prow * D;
 #pragma unroll
@@ -440,15 +467,20 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
     ++next_issue;
     if (next_issue < j_end) resolve();
   }
-  load_segment(r_first);
+  start_segment(r_first);
+  int landed = next_issue - 1;   // tiles whose copies are known to have landed (this wave's)
 
   for (int j = j_begin; j < j_end; ++j) {
-    // tile j landed for every wave, and the ring slot of tile j-1 is free
+    // tile j landed for every wave, and the ring slot of tile j-1 is free.  Past a segment
+    // start every copy issued before it has landed; later tiles wait by count (the output
+    // stores of the finished segment, issued in between, are older than their copies).
     const int after = next_issue - 1 - j;   // tiles issued after tile j
     asm volatile("" ::: "memory");
-    if (after >= 2) wait_vm<2 * DMA_PER_TILE>();
-    else if (after == 1) wait_vm<DMA_PER_TILE>();
-    else wait_vm<0>();
+    if (j > landed) {
+      if (after >= 2) wait_vm<2 * DMA_PER_TILE>();
+      else if (after == 1) wait_vm<DMA_PER_TILE>();
+      else wait_vm<0>();
+    }
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (next_issue < j_end) {
@@ -549,8 +581,13 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
       opb = nxt;
     }
     if (j + 1 == min(seg_E, j_end)) {
-      finish_segment();
-      if (j + 1 < j_end) load_segment(seg_r + 1);
+      // the next segment's query first: its wait then does not cover the output stores
+      const OutRow orow{seg_A, seg_E, seg_s0, rnode, rvalid && seg_ok};
+      if (j + 1 < j_end) {
+        start_segment(seg_r + 1);
+        landed = next_issue - 1;
+      }
+      finish_segment(orow);
     }
   }
 }
@@ -614,7 +651,17 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int D, int log2G
   if (a.status[0] & TAV_DEV_PLAN_MISMATCH) return;
   const int r = blockIdx.x, g = blockIdx.y;
   const int rA = a.rb_tile[r], rE = a.rb_tile[r + 1];
-  const int wf = rA / a.C, wl = (rE - 1) / a.C;
+  // the workgroups holding the row block's first and last tiles: the largest w with
+  // wg_tile[w] <= tile (never an empty share: the next share starts at the same tile)
+  auto owner = [&](int t) {
+    int lo = 0, hi = a.W;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.wg_tile[mid] <= t) lo = mid; else hi = mid;
+    }
+    return lo;
+  };
+  const int wf = owner(rA), wl = owner(rE - 1);
   if (wf == wl) return;  // one workgroup held the whole row block
   const int b = a.rb_seq[r];
   if (b < 0 || b >= a.B) return;

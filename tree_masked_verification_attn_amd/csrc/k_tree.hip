@@ -51,7 +51,9 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* node_offsets,
                                                      int tail_blocks_host, int C, int W,
                                                      int32_t* seq_rb_off, int32_t* rb_seq,
                                                      int32_t* rb_tile, int32_t* tail_blk,
-                                                     int32_t* wg_rb, uint32_t* status) {
+                                                     int32_t* wg_rb, int32_t* wg_tile,
+                                                     const uint8_t* is_chain, int32_t* rb_meta,
+                                                     uint32_t* status) {
   __shared__ int lds[16];
   int carry = 0, bcarry = 0;
   for (int base = 0; base < B; base += 1024) {
@@ -108,15 +110,40 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* node_offsets,
   }
   if (tcarry != tiles_host) return;
   __syncthreads();
-  // the row block holding key tile w * C, for each attention workgroup w
-  for (int w = threadIdx.x; w < W; w += blockDim.x) {
-    const int j = w * C;
-    int lo = 0, hi = total_rb;  // largest r with rb_tile[r] <= j
+  // each attention workgroup's first key tile (its share of the weighted tile axis: tile t of
+  // row block r at t + kRbCost * r) and the row block holding it
+  for (int w = threadIdx.x; w <= W; w += blockDim.x) {
+    const int x = w * C;   // weighted position of the share's start
+    int lo = 0, hi = total_rb;  // largest r with rb_tile[r] + kRbCost * r <= x
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (rb_tile[mid] <= j) lo = mid; else hi = mid;
+      if (rb_tile[mid] + kRbCost * mid <= x) lo = mid; else hi = mid;
     }
-    wg_rb[w] = lo;
+    // a share starting inside a row block's fixed-cost gap starts at the next row block
+    const int j = w == W ? tcarry : min(rb_tile[lo] + (x - rb_tile[lo] - kRbCost * lo), rb_tile[lo + 1]);
+    wg_tile[w] = j;
+    if (w < W) {
+      int r = lo;   // the row block holding tile j (an empty share keeps any valid index)
+      if (j >= rb_tile[lo + 1] && lo + 1 < total_rb) r = lo + 1;
+      wg_rb[w] = r;
+    }
+  }
+  // the attention kernel's record of each row block
+  for (int r = threadIdx.x; r < total_rb; r += blockDim.x) {
+    const int b = rb_seq[r];
+    const int s0 = node_offsets[b];
+    const int n = node_offsets[b + 1] - s0;
+    const int node0 = (r - seq_rb_off[b]) * NB;
+    const bool chain = is_chain[b] != 0;
+    int32_t* m = rb_meta + (size_t)r * kMetaWords;
+    m[kMetaTile0] = rb_tile[r];
+    m[kMetaTileEnd] = rb_tile[r + 1];
+    m[kMetaS0] = s0;
+    m[kMetaN] = n;
+    m[kMetaL] = prefix_len[b];
+    m[kMetaNode0] = node0;
+    m[kMetaTailN] = min(n, node0 + NB);
+    m[kMetaFlags] = (chain ? 1 : 0) | ((chain || n <= kMaxTreeNodes) ? 2 : 0);
   }
 }
 
@@ -195,11 +222,12 @@ hipError_t launch_clear_status(uint32_t* status, hipStream_t s) {
 }
 
 hipError_t launch_plan(const Plan& p, const int32_t* node_offsets, const int32_t* prefix_len,
-                       int32_t* seq_rb_off, int32_t* rb_seq, int32_t* rb_tile, int32_t* tail_blk,
-                       int32_t* wg_rb, uint32_t* status, hipStream_t s) {
+                       const uint8_t* is_chain, int32_t* seq_rb_off, int32_t* rb_seq, int32_t* rb_tile,
+                       int32_t* tail_blk, int32_t* wg_rb, int32_t* wg_tile, int32_t* rb_meta,
+                       uint32_t* status, hipStream_t s) {
   plan_kernel<<<1, 1024, 0, s>>>(node_offsets, prefix_len, p.B, p.NB, p.bs, p.total_rb,
                                  p.tiles_per_head, p.tail_blocks, p.C, p.W, seq_rb_off, rb_seq,
-                                 rb_tile, tail_blk, wg_rb, status);
+                                 rb_tile, tail_blk, wg_rb, wg_tile, is_chain, rb_meta, status);
   return hipGetLastError();
 }
 

@@ -45,7 +45,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 constexpr int kTargetWorkgroups = 256;  // one round of one workgroup per MI355X compute unit
-constexpr int kMinTilesPerWG = 4;       // at least 256 keys per attention workgroup
+constexpr int kMinTilesPerWG = 8;       // at least 512 keys per attention workgroup (more than kRbCost)
 
 int log2_exact(int x) {
   int l = 0;
@@ -129,16 +129,19 @@ tav_status make_plan(const tav_problem* p, const tav_presto_io* pr, Plan* out) {
     for (int rb = 0; rb < nrb; ++rb) tiles += rb_tiles(p->prefix_len_host[b], n, rb, P.NB);
     tail_blocks += ceil_div(n, P.bs);
   }
-  if (tiles > (int64_t)1 << 30 || tail_blocks > (int64_t)1 << 30)
+  if (tiles + (int64_t)kRbCost * P.total_rb > (int64_t)1 << 30 || tail_blocks > (int64_t)1 << 30)
     return fail(TAV_ERR_UNSUPPORTED, "problem too large: %lld key tiles per KV head", (long long)tiles);
   P.tiles_per_head = (int)tiles;
   P.tail_blocks = (int)tail_blocks;
   if (p->dtype == TAV_BF16) {
-    // equal ranges of C key tiles, about one workgroup per compute unit over all KV heads
+    // equal shares C of the weighted tile axis, about one workgroup per compute unit over all
+    // KV heads
+    const int64_t weighted = (int64_t)P.tiles_per_head + (int64_t)kRbCost * P.total_rb;
     const int target = kTargetWorkgroups / P.Hkv > 1 ? kTargetWorkgroups / P.Hkv : 1;
-    P.C = ceil_div(P.tiles_per_head, target);
+    P.C = (int)ceil_div64(weighted, target);
     if (P.C < kMinTilesPerWG) P.C = kMinTilesPerWG;
-    P.W = ceil_div(P.tiles_per_head, P.C);
+    static_assert(kMinTilesPerWG > kRbCost, "a share must not fit inside one row block's fixed cost");
+    P.W = (int)ceil_div64(weighted, P.C);
   }
   size_t o = 0;
   P.off_status = o; o = align_up(o + 256);
@@ -149,6 +152,8 @@ tav_status make_plan(const tav_problem* p, const tav_presto_io* pr, Plan* out) {
   P.off_rb_tile = o; o = align_up(o + (size_t)(P.total_rb + 1) * 4);
   P.off_tail_blk = o; o = align_up(o + (size_t)(P.B + 1) * 4);
   P.off_wg_rb = o; o = align_up(o + (size_t)P.W * 4);
+  P.off_wg_tile = o; o = align_up(o + (size_t)(P.W + 1) * 4);
+  P.off_rb_meta = o; o = align_up(o + (size_t)P.total_rb * kMetaWords * 4);
   const size_t tail_bytes = (size_t)P.tail_blocks * P.Hkv * P.bs * P.D * 2;
   P.off_ktail = o;
   if (p->dtype == TAV_BF16) o = align_up(o + tail_bytes);
@@ -246,6 +251,8 @@ AttnArgs attn_args(const tav_problem* p, const Plan& P, const tav_attn_io* io, v
   a.rb_tile = ws_at<int32_t>(ws, P.off_rb_tile);
   a.tail_blk = ws_at<int32_t>(ws, P.off_tail_blk);
   a.wg_rb = ws_at<int32_t>(ws, P.off_wg_rb);
+  a.wg_tile = ws_at<int32_t>(ws, P.off_wg_tile);
+  a.rb_meta = ws_at<int32_t>(ws, P.off_rb_meta);
   a.k_tail = ws_at<void>(ws, P.off_ktail);
   a.v_tail = ws_at<void>(ws, P.off_vtail);
   a.part_o = ws_at<float>(ws, P.off_part_o);
@@ -311,9 +318,10 @@ tav_status enqueue_attention(const tav_problem* p, const Plan& P, const tav_attn
                              hipStream_t s) {
   const AttnArgs a = attn_args(p, P, io, ws);
   if (p->dtype == TAV_BF16) {
-    TAV_HIP(launch_plan(P, p->node_offsets, p->prefix_len, const_cast<int32_t*>(a.seq_rb_off),
+    TAV_HIP(launch_plan(P, p->node_offsets, p->prefix_len, a.is_chain, const_cast<int32_t*>(a.seq_rb_off),
                         const_cast<int32_t*>(a.rb_seq), const_cast<int32_t*>(a.rb_tile),
-                        const_cast<int32_t*>(a.tail_blk), const_cast<int32_t*>(a.wg_rb), a.status, s));
+                        const_cast<int32_t*>(a.tail_blk), const_cast<int32_t*>(a.wg_rb),
+                        const_cast<int32_t*>(a.wg_tile), const_cast<int32_t*>(a.rb_meta), a.status, s));
     TAV_HIP(launch_pack_tail(P, a, s));
     hipEvent_t ev0 = nullptr, ev1 = nullptr;
     if (g_timing.on) {

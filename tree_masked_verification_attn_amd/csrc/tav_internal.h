@@ -41,7 +41,7 @@ struct Plan {
   int tail_blocks = 0;    // packed blocks (block_size rows) of tree-node keys / values
   // workspace layout (byte offsets)
   size_t off_status = 0, off_chain = 0, off_mask = 0, off_seq_rb = 0, off_rb_seq = 0,
-         off_rb_tile = 0, off_tail_blk = 0, off_wg_rb = 0, off_ktail = 0, off_vtail = 0, off_part_o = 0,
+         off_rb_tile = 0, off_tail_blk = 0, off_wg_rb = 0, off_wg_tile = 0, off_rb_meta = 0, off_ktail = 0, off_vtail = 0, off_part_o = 0,
          off_part_lse = 0, off_stats = 0, off_term = 0, off_child_p = 0, off_child_q = 0,
          off_presto = 0, off_sl_m = 0, off_sl_s = 0, off_sl_z = 0, off_ch_w = 0, off_dlist = 0,
          off_rec = 0, total = 0;
@@ -49,6 +49,7 @@ struct Plan {
 };
 
 __host__ __device__ static inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+__host__ __device__ static inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Tiles of the key sequence seen by row block rb of a sequence with n nodes
 // and L prefix rows: ceil(L / 64) prefix tiles, then the tree nodes 0 ..
@@ -57,6 +58,21 @@ __host__ __device__ static inline int rb_tiles(int L, int n, int rb, int NB) {
   int tail = n < (rb + 1) * NB ? n : (rb + 1) * NB;
   return (L + kTileKeys - 1) / kTileKeys + (tail + kTileKeys - 1) / kTileKeys;
 }
+
+// What the attention kernel needs of a row block when it starts computing it, gathered by the
+// plan kernel into one record (one scalar load): its key tiles [tile0, tile_end) per KV head,
+// the sequence's first node and node count, its prefix length, the block's first node, the
+// bound on its nodes (min(n, node0 + nodes per block)) and flags (1: the tree is a chain,
+// 2: the row block is computed -- a chain, or a tree within the mask width).
+// Work split of the attention kernel: every row block costs its key tiles plus kRbCost tiles'
+// worth of fixed work (its partial prefix tile and masked tree tile, the output of the finished
+// segment and the start of the next), and each workgroup takes an equal share Cv of that
+// weighted length: tile t of row block r sits at t + kRbCost * r, and workgroup w holds the tiles
+// whose position lies in [w Cv, (w+1) Cv).  The cost was measured per tile on MI355X.
+constexpr int kRbCost = 4;
+
+enum RbMeta { kMetaTile0 = 0, kMetaTileEnd, kMetaS0, kMetaN, kMetaL, kMetaNode0, kMetaTailN, kMetaFlags,
+              kMetaWords };
 
 struct AttnArgs {
   const void* q;
@@ -76,6 +92,8 @@ struct AttnArgs {
   const int32_t* rb_tile;     // [total_rb+1] first key tile (per KV head) of each row block
   const int32_t* tail_blk;    // [B+1] first packed node block of each sequence
   const int32_t* wg_rb;       // [W] row block holding the first key tile of each workgroup
+  const int32_t* wg_tile;     // [W+1] first key tile of each workgroup (per KV head)
+  const int32_t* rb_meta;     // [total_rb, kMetaWords] per row block, fields RbMeta
   void* k_tail;               // [tail_blocks, Hkv, bs, D] node keys in the cache layout
   void* v_tail;               // [tail_blocks, Hkv, D, bs] node values in the cache layout
   float* part_o;              // [2W, Hkv, 256, D] partial outputs of cut row blocks
@@ -156,8 +174,9 @@ struct PrestoArgs {
 // of the launch.
 hipError_t launch_clear_status(uint32_t* status, hipStream_t s);
 hipError_t launch_plan(const Plan& p, const int32_t* node_offsets, const int32_t* prefix_len,
-                       int32_t* seq_rb_off, int32_t* rb_seq, int32_t* rb_tile, int32_t* tail_blk,
-                       int32_t* wg_rb, uint32_t* status, hipStream_t s);
+                       const uint8_t* is_chain, int32_t* seq_rb_off, int32_t* rb_seq, int32_t* rb_tile,
+                       int32_t* tail_blk, int32_t* wg_rb, int32_t* wg_tile, int32_t* rb_meta,
+                       uint32_t* status, hipStream_t s);
 hipError_t launch_pack_tail(const Plan& p, const AttnArgs& a, hipStream_t s);
 hipError_t launch_prep(const Plan& p, const int32_t* node_offsets, const int32_t* prefix_len,
                        const int32_t* parent, uint8_t* chain_ws, uint64_t* mask_ws,
