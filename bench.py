@@ -5,12 +5,14 @@ paged KV cache (block 16, shuffled block table), 64-node random trees of depth
 <= 8, 32 query / 8 KV heads, head_dim 128, bf16, vocabulary 151936, T = 1.0,
 seed 10086 -- the batched verification shape.  Inputs are synthetic (seeded).
 
-One step = one whole pass: tree preparation, split-KV tree attention + merge
-on one stream and vocabulary statistics + verification walk on a second
-stream (the two halves are independent), i.e. tav_tree_attention followed by
-tav_tree_verify on their own streams and workspaces.  Inputs are resident in
-HBM; two input copies alternate so consecutive steps do not re-read one
-step's data from the 256 MB last-level cache.
+One step = one whole pass, one tav_tree_attn_verify call: tree preparation,
+split-KV tree attention + merge on one stream and vocabulary statistics +
+verification walk on a second stream (the two halves are independent).  With
+--separate the step is tav_tree_attention and tav_tree_verify on their own
+streams and workspaces instead (which also times each half); with --one-stream
+everything runs on one stream.  Inputs are resident in HBM; two input copies
+alternate so consecutive steps do not re-read one step's data from the 256 MB
+last-level cache.
 
 Prints one JSON line:  value = tree nodes scored per second (attention +
 verification), plus the step's algorithmic HBM GB/s, the roofline of the
@@ -118,6 +120,8 @@ def main():
     ap.add_argument("--copies", type=int, default=2)
     ap.add_argument("--one-stream", action="store_true",
                     help="run verification after attention on the same stream (no overlap)")
+    ap.add_argument("--separate", action="store_true",
+                    help="attention and verification as two calls with their own workspaces")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -143,13 +147,21 @@ def main():
         del src, dst
     w = gen.make(args.workload, args.seed)
     copies = [wdev.upload(w, "cuda") for _ in range(max(1, args.copies))]
-    ws_v = [torch.zeros_like(c.workspace) for c in copies]     # verification's own workspace
+    # verification's own workspaces (separate calls only)
+    ws_v = [torch.zeros_like(c.workspace) for c in copies] if args.separate else [None] * len(copies)
     sa = torch.cuda.Stream()
     sv = sa if args.one_stream else torch.cuda.Stream()
     torch.cuda.synchronize()
 
     def step(i, ev=None):
         c = copies[i % len(copies)]
+        if not args.separate:
+            if ev is not None:
+                ev[0].record(sa)
+            tav.tav_tree_attn_verify(c.prob, c.tree, c.attn, c.verify, None, None, c.workspace, sa, sv)
+            if ev is not None:
+                ev[1].record(sa)
+            return
         if ev is not None:
             ev[0].record(sa)
         tav.tav_tree_attention(c.prob, c.tree, c.attn, c.workspace, sa)
@@ -175,18 +187,17 @@ def main():
     tav.tav_kernel_timing(False)
     kern_ms = kern_ms_total / max(1, kern_launches)
     for c, wv in zip(copies, ws_v):
-        bits = tav.tav_read_status(c.workspace) | tav.tav_read_status(wv)
+        bits = tav.tav_read_status(c.workspace) | (tav.tav_read_status(wv) if wv is not None else 0)
         if bits:
             raise RuntimeError(f"device status bits set: {tav.device_status_names(bits)}")
     attn_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-    ver_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
+    ver_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events])) if args.separate else None
 
     ms = wall * 1e3 / args.steps
     attn_b, ver_b = algorithmic_bytes(w)
     flops = attention_flops(w)
     step_gbs = (attn_b + ver_b) / (ms * 1e-3) / 1e9
-    attn_gbs = attn_b / (attn_ms * 1e-3) / 1e9
-    ver_gbs = ver_b / (ver_ms * 1e-3) / 1e9
+
     # roofline of the dominant kernel: the attention kernel (per launch = one step's attention)
     kern_gbs = attn_b / (kern_ms * 1e-3) / 1e9
     traffic = measured_traffic()
@@ -197,8 +208,14 @@ def main():
             "algorithmic_bytes": attn_b,
             "mfma_tflops": round(flops / (kern_ms * 1e-3) / 1e12, 1),
             "mfma_frac": round(flops / (kern_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
-    other = {"attention_half_ms": round(attn_ms, 4), "attention_half_gbs": round(attn_gbs, 1),
-             "verify_half_ms": round(ver_ms, 4), "verify_half_gbs": round(ver_gbs, 1)}
+    if args.separate:
+        other = {"mode": "separate calls", "attention_half_ms": round(attn_ms, 4),
+                 "attention_half_gbs": round(attn_b / (attn_ms * 1e-3) / 1e9, 1),
+                 "verify_half_ms": round(ver_ms, 4),
+                 "verify_half_gbs": round(ver_b / (ver_ms * 1e-3) / 1e9, 1)}
+    else:
+        other = {"mode": "one tav_tree_attn_verify call" + (" on one stream" if args.one_stream else ""),
+                 "pass_event_ms": round(attn_ms, 4)}
 
     cpu = None
     if not args.no_cpu_baseline:
