@@ -45,10 +45,11 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 constexpr int kTargetWorkgroups = 256;  // one round of one workgroup per MI355X compute unit
-// With verification running beside it on another stream, attention leaves a quarter of the
+// With verification running beside it on another stream, attention leaves an eighth of the
 // compute units to the streaming verification kernels (measured on the batched-verify workload:
-// the whole pass 3-4% shorter than with all 256 taken, 2% shorter than with 224).
-constexpr int kConcurrentAttnWorkgroups = 192;
+// the whole pass ~2% shorter than with all 256 taken; at 192 it is ~2% shorter again, but the
+// attention kernel itself ~10% longer).
+constexpr int kConcurrentAttnWorkgroups = 224;
 constexpr int kMinTilesPerWG = 8;       // at least 512 keys per attention workgroup (more than kRbCost)
 
 int log2_exact(int x) {
