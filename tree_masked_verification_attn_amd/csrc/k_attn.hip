@@ -194,6 +194,7 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
   const const_i32_ptr pref_len = (const_i32_ptr)a.prefix_len;
   const const_i32_ptr tail_blk = (const_i32_ptr)a.tail_blk;
   const const_i32_ptr rb_meta = (const_i32_ptr)a.rb_meta;
+  const const_i32_ptr chain_w = (const_i32_ptr)a.is_chain;   // chain flags, 4 per word
   const uint16_t* kc = (const uint16_t*)a.k_cache;
   const uint16_t* vc = (const uint16_t*)a.v_cache;
   const uint16_t* ktl = (const uint16_t*)a.k_tail;
@@ -260,8 +261,9 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
     seg_node0 = m[kMetaNode0];
     seg_tail_n = m[kMetaTailN];
     const int flags = m[kMetaFlags];
-    seg_chain = (flags & 1) != 0;
-    seg_ok = (flags & 2) != 0;   // larger trees were rejected by preparation
+    const int sb_ = m[kMetaSeq];
+    seg_chain = ((chain_w[sb_ >> 2] >> ((sb_ & 3) * 8)) & 0xff) != 0;
+    seg_ok = seg_chain || (flags & 2) != 0;   // larger trees were rejected by preparation
     seg_Tp = (seg_L + kTileKeys - 1) / kTileKeys;
     rnode = seg_node0 + (row >> LOG2G);
     rvalid = (row >> LOG2G) < min(NB, seg_n - seg_node0);
@@ -592,55 +594,6 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
   }
 }
 
-// Copies the tree nodes' keys and values into blocks laid out like the paged cache (block_size
-// rows: keys [block, head, slot, d], values [block, head, d, slot]), zero-padded past each
-// sequence's last node, so tree-tail tiles take the same global->LDS copy path as prefix tiles.
-// One workgroup per (packed block, KV head).
-template <int D>
-__global__ __launch_bounds__(256) void pack_tail_kernel(AttnArgs a) {
-  constexpr int CH = D / 8;
-  __shared__ uint16_t vs[64][D + 8];   // values of the block, [slot][d]
-  if (a.status[0] & TAV_DEV_PLAN_MISMATCH) return;
-  const int tb = blockIdx.x, g = blockIdx.y, bs = a.block_size, Hkv = a.Hkv;
-  int lo = 0, hi = a.B;  // sequence of this block: largest b with tail_blk[b] <= tb
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (a.tail_blk[mid] <= tb) lo = mid; else hi = mid;
-  }
-  const int b = lo;
-  const int s0 = a.node_offsets[b];
-  const int n = a.node_offsets[b + 1] - s0;
-  const int node_base = (tb - a.tail_blk[b]) * bs;
-  const uint16_t* kn = (const uint16_t*)a.k_node;
-  const uint16_t* vn = (const uint16_t*)a.v_node;
-  uint16_t* kt = (uint16_t*)a.k_tail;
-  uint16_t* vt = (uint16_t*)a.v_tail;
-  for (int c = threadIdx.x; c < bs * CH; c += blockDim.x) {
-    const int slot = c / CH, ch = c % CH;
-    const int node = node_base + slot;
-    uint4 kv = make_uint4(0u, 0u, 0u, 0u), vv = kv;
-    if (node < n) {
-      const size_t off = ((size_t)(s0 + node) * Hkv + g) * D + ch * 8;
-      kv = *(const uint4*)(kn + off);
-      vv = *(const uint4*)(vn + off);
-    }
-    *(uint4*)(kt + (((size_t)tb * Hkv + g) * bs + slot) * D + ch * 8) = kv;
-    const uint32_t w4[4] = {vv.x, vv.y, vv.z, vv.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) vs[slot][ch * 8 + e] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
-  }
-  __syncthreads();
-  const int groups = bs / 8;
-  for (int c = threadIdx.x; c < D * groups; c += blockDim.x) {
-    const int d = c / groups, sg = c % groups;
-    uint32_t w4[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      w4[e] = (uint32_t)vs[sg * 8 + 2 * e][d] | ((uint32_t)vs[sg * 8 + 2 * e + 1][d] << 16);
-    *(uint4*)(vt + (((size_t)tb * Hkv + g) * D + d) * bs + sg * 8) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
-  }
-}
-
 // Online-softmax merge of the pieces of a row block cut between workgroups:
 // out = sum_s exp(lse_s - LSE) O_s.  Row block r's key tiles [A, E) were cut into the pieces of
 // workgroups A/C .. (E-1)/C; the first piece sits in slot 2w+1 of its workgroup (its last
@@ -831,14 +784,6 @@ hipError_t launch_bf16_d(const Plan& p, const AttnArgs& a, hipStream_t s) {
 }
 
 }  // namespace
-
-hipError_t launch_pack_tail(const Plan& p, const AttnArgs& a, hipStream_t s) {
-  if (p.tail_blocks == 0) return hipSuccess;
-  dim3 grid(p.tail_blocks, p.Hkv);
-  if (p.D == 128) pack_tail_kernel<128><<<grid, 256, 0, s>>>(a);
-  else pack_tail_kernel<64><<<grid, 256, 0, s>>>(a);
-  return hipGetLastError();
-}
 
 hipError_t launch_attn_bf16(const Plan& p, const AttnArgs& a, hipStream_t s) {
   if (p.W == 0) return hipSuccess;

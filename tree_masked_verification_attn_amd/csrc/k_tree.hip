@@ -1,19 +1,27 @@
-// Tree preparation and the attention work plan.
+// Tree preparation, the attention work plan and the packing of the tree nodes' keys / values.
 //
 // Visibility follows Progressive Tree Drafting, Section 3.1 ("Tree
 // Construction"): pi(v) = {v} U pi(P(v)), and a node's position is fixed by
 // |pi(v)|; behind a cached prefix of L rows, position = L + depth(v).
+//
+// For bf16 attention the three jobs run as one launch (prelude_kernel): blocks
+// [0, B) prepare one sequence each, block B computes the work plan, and the
+// remaining blocks pack one (node block, KV head) each.  None of them reads
+// another's output; the attention kernel that follows reads all three.
 #include "tav_internal.h"
 
 namespace tav {
 namespace {
 
-// Clears the status word and the counter word that follows it in the status block.
+constexpr int kPrepThreads = 256;
+constexpr int kPlanLds = 2048;   // sequences / row blocks whose plan arrays are staged in LDS
+
+// Clears the status word and the work-queue counter of the status block.
 __global__ void clear_status_kernel(uint32_t* status) {
   if (threadIdx.x == 0) { status[0] = 0u; status[kCounterWord] = 0u; }
 }
 
-// Exclusive scan of one int per thread over a 1024-thread block; also returns the total.
+// Exclusive scan of one int per thread over the block; also returns the total.
 __device__ int block_exclusive_scan(int v, int* lds, int* total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
@@ -41,158 +49,59 @@ __device__ int block_exclusive_scan(int v, int* lds, int* total) {
   return excl;
 }
 
-// One 1024-thread block: seq_rb_off[B+1] (row blocks per sequence), rb_seq,
-// rb_tile[total_rb+1] (first key tile of each row block, per KV head) and
-// tail_blk[B+1] (first packed node block of each sequence), identical to the
-// host plan; a disagreement with the host's totals sets TAV_DEV_PLAN_MISMATCH.
-__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* node_offsets,
-                                                     const int32_t* prefix_len, int B, int NB,
-                                                     int bs, int total_rb_host, int tiles_host,
-                                                     int tail_blocks_host, int C, int W,
-                                                     int32_t* seq_rb_off, int32_t* rb_seq,
-                                                     int32_t* rb_tile, int32_t* tail_blk,
-                                                     int32_t* wg_rb, int32_t* wg_tile,
-                                                     const uint8_t* is_chain, int32_t* rb_meta,
-                                                     uint32_t* status) {
-  __shared__ int lds[16];
-  int carry = 0, bcarry = 0;
-  for (int base = 0; base < B; base += 1024) {
-    const int b = base + threadIdx.x;
-    int cnt = 0, nblk = 0;
-    if (b < B) {
-      const int n = node_offsets[b + 1] - node_offsets[b];
-      cnt = (n + NB - 1) / NB;
-      nblk = (n + bs - 1) / bs;
-    }
-    int tot, btot;
-    const int ex = block_exclusive_scan(cnt, lds, &tot);
-    const int bex = block_exclusive_scan(nblk, lds, &btot);
-    if (b < B) {
-      seq_rb_off[b] = carry + ex;
-      tail_blk[b] = bcarry + bex;
-    }
-    carry += tot;
-    bcarry += btot;
-  }
-  if (threadIdx.x == 0) {
-    seq_rb_off[B] = carry;
-    tail_blk[B] = bcarry;
-  }
-  const int total_rb = carry;
-  if (total_rb != total_rb_host || bcarry != tail_blocks_host) {
-    if (threadIdx.x == 0) atomicOr(status, (uint32_t)TAV_DEV_PLAN_MISMATCH);
-    return;
-  }
-  __syncthreads();
-  int tcarry = 0;
-  for (int base = 0; base < total_rb; base += 1024) {
-    const int r = base + threadIdx.x;
-    int cnt = 0;
-    if (r < total_rb) {
-      int lo = 0, hi = B;  // largest b with seq_rb_off[b] <= r
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (seq_rb_off[mid] <= r) lo = mid; else hi = mid;
-      }
-      const int b = lo;
-      const int n = node_offsets[b + 1] - node_offsets[b];
-      cnt = rb_tiles(prefix_len[b], n, r - seq_rb_off[b], NB);
-      rb_seq[r] = b;
-    }
-    int tot;
-    const int ex = block_exclusive_scan(cnt, lds, &tot);
-    if (r < total_rb) rb_tile[r] = tcarry + ex;
-    tcarry += tot;
-  }
-  if (threadIdx.x == 0) {
-    rb_tile[total_rb] = tcarry;
-    if (tcarry != tiles_host) atomicOr(status, (uint32_t)TAV_DEV_PLAN_MISMATCH);
-  }
-  if (tcarry != tiles_host) return;
-  __syncthreads();
-  // each attention workgroup's first key tile (its share of the weighted tile axis: tile t of
-  // row block r at t + kRbCost * r) and the row block holding it
-  for (int w = threadIdx.x; w <= W; w += blockDim.x) {
-    const int x = w * C;   // weighted position of the share's start
-    int lo = 0, hi = total_rb;  // largest r with rb_tile[r] + kRbCost * r <= x
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (rb_tile[mid] + kRbCost * mid <= x) lo = mid; else hi = mid;
-    }
-    // a share starting inside a row block's fixed-cost gap starts at the next row block
-    const int j = w == W ? tcarry : min(rb_tile[lo] + (x - rb_tile[lo] - kRbCost * lo), rb_tile[lo + 1]);
-    wg_tile[w] = j;
-    if (w < W) {
-      int r = lo;   // the row block holding tile j (an empty share keeps any valid index)
-      if (j >= rb_tile[lo + 1] && lo + 1 < total_rb) r = lo + 1;
-      wg_rb[w] = r;
-    }
-  }
-  // the attention kernel's record of each row block
-  for (int r = threadIdx.x; r < total_rb; r += blockDim.x) {
-    const int b = rb_seq[r];
-    const int s0 = node_offsets[b];
-    const int n = node_offsets[b + 1] - s0;
-    const int node0 = (r - seq_rb_off[b]) * NB;
-    const bool chain = is_chain[b] != 0;
-    int32_t* m = rb_meta + (size_t)r * kMetaWords;
-    m[kMetaTile0] = rb_tile[r];
-    m[kMetaTileEnd] = rb_tile[r + 1];
-    m[kMetaS0] = s0;
-    m[kMetaN] = n;
-    m[kMetaL] = prefix_len[b];
-    m[kMetaNode0] = node0;
-    m[kMetaTailN] = min(n, node0 + NB);
-    m[kMetaFlags] = (chain ? 1 : 0) | ((chain || n <= kMaxTreeNodes) ? 2 : 0);
-  }
-}
+struct PrepArgs {
+  const int32_t* node_offsets;
+  const int32_t* prefix_len;
+  const int32_t* parent;
+  uint8_t* chain_ws;
+  uint64_t* mask_ws;
+  int32_t* depth_out;
+  int32_t* pos_out;
+  uint64_t* mask_out;
+  uint8_t* chain_out;
+  uint32_t* status;
+};
 
-// One block per sequence: validate parents, detect chains, and build depth,
-// position and the 256-bit ancestor masks of non-chain trees.
-__global__ __launch_bounds__(256) void prep_kernel(const int32_t* node_offsets,
-                                                    const int32_t* prefix_len,
-                                                    const int32_t* parent, uint8_t* chain_ws,
-                                                    uint64_t* mask_ws, int32_t* depth_out,
-                                                    int32_t* pos_out, uint64_t* mask_out,
-                                                    uint8_t* chain_out, uint32_t* status) {
+// Sequence b: validate parents, detect a chain, and build depth, position and the 256-bit
+// ancestor masks of a non-chain tree.
+__device__ void prep_sequence(const PrepArgs& a, int b) {
   __shared__ int par_s[kMaxTreeNodes];
-  const int b = blockIdx.x;
-  const int s0 = node_offsets[b];
-  const int n = node_offsets[b + 1] - s0;
-  const int L = prefix_len[b];
+  const int s0 = a.node_offsets[b];
+  const int n = a.node_offsets[b + 1] - s0;
+  const int L = a.prefix_len[b];
   int bad = 0, not_chain = 0;
   for (int v = threadIdx.x; v < n; v += blockDim.x) {
-    int p = parent[s0 + v];
+    int p = a.parent[s0 + v];
     if (v == 0 ? p != -1 : (p < 0 || p >= v)) bad = 1;
     if (v > 0 && p != v - 1) not_chain = 1;
   }
   bad = __syncthreads_or(bad);
   not_chain = __syncthreads_or(not_chain);
   if (bad) {
-    if (threadIdx.x == 0) atomicOr(status, (uint32_t)TAV_DEV_BAD_PARENT);
-    if (threadIdx.x == 0) chain_ws[b] = 0;
+    if (threadIdx.x == 0) atomicOr(a.status, (uint32_t)TAV_DEV_BAD_PARENT);
+    if (threadIdx.x == 0) a.chain_ws[b] = 0;
     return;
   }
   if (threadIdx.x == 0) {
-    chain_ws[b] = not_chain ? 0 : 1;
-    if (chain_out) chain_out[b] = not_chain ? 0 : 1;
+    a.chain_ws[b] = not_chain ? 0 : 1;
+    if (a.chain_out) a.chain_out[b] = not_chain ? 0 : 1;
   }
   if (!not_chain) {
     for (int v = threadIdx.x; v < n; v += blockDim.x) {
-      if (depth_out) depth_out[s0 + v] = v;
-      if (pos_out) pos_out[s0 + v] = L + v;
-      if (mask_out) {
+      if (a.depth_out) a.depth_out[s0 + v] = v;
+      if (a.pos_out) a.pos_out[s0 + v] = L + v;
+      if (a.mask_out) {
 #pragma unroll
-        for (int w = 0; w < kMaskWords; ++w) mask_out[(size_t)(s0 + v) * kMaskWords + w] = 0ull;
+        for (int w = 0; w < kMaskWords; ++w) a.mask_out[(size_t)(s0 + v) * kMaskWords + w] = 0ull;
       }
     }
     return;
   }
   if (n > kMaxTreeNodes) {
-    if (threadIdx.x == 0) atomicOr(status, (uint32_t)TAV_DEV_TREE_TOO_LARGE);
+    if (threadIdx.x == 0) atomicOr(a.status, (uint32_t)TAV_DEV_TREE_TOO_LARGE);
     return;
   }
-  for (int v = threadIdx.x; v < n; v += blockDim.x) par_s[v] = parent[s0 + v];
+  for (int v = threadIdx.x; v < n; v += blockDim.x) par_s[v] = a.parent[s0 + v];
   __syncthreads();
   for (int v = threadIdx.x; v < n; v += blockDim.x) {
     uint64_t w[kMaskWords] = {0ull, 0ull, 0ull, 0ull};
@@ -206,12 +115,232 @@ __global__ __launch_bounds__(256) void prep_kernel(const int32_t* node_offsets,
     }
 #pragma unroll
     for (int k = 0; k < kMaskWords; ++k) {
-      mask_ws[(size_t)(s0 + v) * kMaskWords + k] = w[k];
-      if (mask_out) mask_out[(size_t)(s0 + v) * kMaskWords + k] = w[k];
+      a.mask_ws[(size_t)(s0 + v) * kMaskWords + k] = w[k];
+      if (a.mask_out) a.mask_out[(size_t)(s0 + v) * kMaskWords + k] = w[k];
     }
-    if (depth_out) depth_out[s0 + v] = d;
-    if (pos_out) pos_out[s0 + v] = L + d;
+    if (a.depth_out) a.depth_out[s0 + v] = d;
+    if (a.pos_out) a.pos_out[s0 + v] = L + d;
   }
+}
+
+struct PlanArgs {
+  int B, NB, bs, total_rb_host, tiles_host, tail_blocks_host, C, W;
+};
+
+// The attention work plan (one block): seq_rb_off[B+1] (row blocks per sequence), rb_seq,
+// rb_tile[total_rb+1] (first key tile of each row block, per KV head), tail_blk[B+1] (first
+// packed node block of each sequence), each workgroup's share wg_tile / wg_rb, and the record
+// of each row block, identical to the host plan; a disagreement with the host's totals sets
+// TAV_DEV_PLAN_MISMATCH.  The row-block offsets and tiles are staged in LDS when they fit.
+__device__ void plan_block(const PlanArgs& p, const AttnArgs& a) {
+  __shared__ int scan_s[16];
+  __shared__ int off_s[kPlanLds], tile_s[kPlanLds];
+  const int B = p.B, NB = p.NB, bs = p.bs, C = p.C, W = p.W;
+  const int32_t* node_offsets = a.node_offsets;
+  const int32_t* prefix_len = a.prefix_len;
+  int32_t* seq_rb_off = const_cast<int32_t*>(a.seq_rb_off);
+  int32_t* rb_seq = const_cast<int32_t*>(a.rb_seq);
+  int32_t* rb_tile = const_cast<int32_t*>(a.rb_tile);
+  int32_t* tail_blk = const_cast<int32_t*>(a.tail_blk);
+  int32_t* wg_rb = const_cast<int32_t*>(a.wg_rb);
+  int32_t* wg_tile = const_cast<int32_t*>(a.wg_tile);
+  int32_t* rb_meta = const_cast<int32_t*>(a.rb_meta);
+  const bool small = B + 1 <= kPlanLds && p.total_rb_host + 1 <= kPlanLds;
+  int* off = small ? off_s : seq_rb_off;   // working copies (LDS or the outputs themselves)
+  int* tile = small ? tile_s : rb_tile;
+  int carry = 0, bcarry = 0;
+  for (int base = 0; base < B; base += blockDim.x) {
+    const int b = base + threadIdx.x;
+    int cnt = 0, nblk = 0;
+    if (b < B) {
+      const int n = node_offsets[b + 1] - node_offsets[b];
+      cnt = (n + NB - 1) / NB;
+      nblk = (n + bs - 1) / bs;
+    }
+    int tot, btot;
+    const int ex = block_exclusive_scan(cnt, scan_s, &tot);
+    const int bex = block_exclusive_scan(nblk, scan_s, &btot);
+    if (b < B) {
+      off[b] = carry + ex;
+      tail_blk[b] = bcarry + bex;
+    }
+    carry += tot;
+    bcarry += btot;
+  }
+  if (threadIdx.x == 0) {
+    off[B] = carry;
+    tail_blk[B] = bcarry;
+  }
+  const int total_rb = carry;
+  if (total_rb != p.total_rb_host || bcarry != p.tail_blocks_host) {
+    if (threadIdx.x == 0) atomicOr(a.status, (uint32_t)TAV_DEV_PLAN_MISMATCH);
+    return;
+  }
+  __syncthreads();
+  int tcarry = 0;
+  for (int base = 0; base < total_rb; base += blockDim.x) {
+    const int r = base + threadIdx.x;
+    int cnt = 0;
+    if (r < total_rb) {
+      int lo = 0, hi = B;  // largest b with off[b] <= r
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (off[mid] <= r) lo = mid; else hi = mid;
+      }
+      const int b = lo;
+      const int n = node_offsets[b + 1] - node_offsets[b];
+      cnt = rb_tiles(prefix_len[b], n, r - off[b], NB);
+      rb_seq[r] = b;
+    }
+    int tot;
+    const int ex = block_exclusive_scan(cnt, scan_s, &tot);
+    if (r < total_rb) tile[r] = tcarry + ex;
+    tcarry += tot;
+  }
+  if (threadIdx.x == 0) {
+    tile[total_rb] = tcarry;
+    if (tcarry != p.tiles_host) atomicOr(a.status, (uint32_t)TAV_DEV_PLAN_MISMATCH);
+  }
+  if (tcarry != p.tiles_host) return;
+  __syncthreads();
+  if (small) {
+    for (int b = threadIdx.x; b <= B; b += blockDim.x) seq_rb_off[b] = off[b];
+    for (int r = threadIdx.x; r <= total_rb; r += blockDim.x) rb_tile[r] = tile[r];
+  }
+  // each attention workgroup's first key tile (its share of the weighted tile axis: tile t of
+  // row block r at t + kRbCost * r) and the row block holding it
+  for (int w = threadIdx.x; w <= W; w += blockDim.x) {
+    const int x = w * C;   // weighted position of the share's start
+    int lo = 0, hi = total_rb;  // largest r with tile[r] + kRbCost * r <= x
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (tile[mid] + kRbCost * mid <= x) lo = mid; else hi = mid;
+    }
+    // a share starting inside a row block's fixed-cost gap starts at the next row block
+    const int j = w == W ? tcarry : min(tile[lo] + (x - tile[lo] - kRbCost * lo), tile[lo + 1]);
+    wg_tile[w] = j;
+    if (w < W) {
+      int r = lo;   // the row block holding tile j (an empty share keeps any valid index)
+      if (j >= tile[lo + 1] && lo + 1 < total_rb) r = lo + 1;
+      wg_rb[w] = r;
+    }
+  }
+  // the attention kernel's record of each row block (the chain flag is read by the attention
+  // kernel itself from the preparation's output)
+  for (int r = threadIdx.x; r < total_rb; r += blockDim.x) {
+    int lo = 0, hi = B;  // the row block's sequence: largest b with off[b] <= r
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (off[mid] <= r) lo = mid; else hi = mid;
+    }
+    const int b = lo;
+    const int s0 = node_offsets[b];
+    const int n = node_offsets[b + 1] - s0;
+    const int node0 = (r - off[b]) * NB;
+    int32_t* m = rb_meta + (size_t)r * kMetaWords;
+    m[kMetaTile0] = tile[r];
+    m[kMetaTileEnd] = tile[r + 1];
+    m[kMetaS0] = s0;
+    m[kMetaN] = n;
+    m[kMetaL] = prefix_len[b];
+    m[kMetaNode0] = node0;
+    m[kMetaTailN] = min(n, node0 + NB);
+    m[kMetaFlags] = n <= kMaxTreeNodes ? 2 : 0;
+    m[kMetaSeq] = b;
+  }
+}
+
+// Copies the keys and values of block_size consecutive tree nodes of one sequence (packed node
+// block tb, KV head g) into the paged cache's layout (keys [block, head, slot, d], values
+// [block, head, d, slot]), zero-padded past the sequence's last node, so tree-tail tiles take the
+// same copy path as prefix tiles.  The sequence of block tb is found from the node counts.
+template <int D>
+__device__ void pack_block(const AttnArgs& a, int tb, int g) {
+  constexpr int CH = D / 8;
+  __shared__ uint16_t vs[64][D + 8];   // values of the block, [slot][d]
+  __shared__ int scan_s[16];
+  __shared__ int seq_s, base_s;
+  const int bs = a.block_size, Hkv = a.Hkv, B = a.B;
+  // sequence b with tail offset off(b) <= tb < off(b) + ceil(n_b / bs)
+  if (threadIdx.x == 0) seq_s = -1;
+  int carry = 0;
+  for (int base = 0; base < B; base += blockDim.x) {
+    const int b = base + threadIdx.x;
+    const int nblk = b < B ? (a.node_offsets[b + 1] - a.node_offsets[b] + bs - 1) / bs : 0;
+    int tot;
+    const int ex = block_exclusive_scan(nblk, scan_s, &tot);   // (its barriers order seq_s)
+    if (b < B && tb >= carry + ex && tb < carry + ex + nblk) {
+      seq_s = b;
+      base_s = carry + ex;
+    }
+    carry += tot;
+    __syncthreads();
+    if (seq_s >= 0) break;
+  }
+  const int b = seq_s;
+  if (b < 0) return;   // tb past the last block (not launched)
+  const int s0 = a.node_offsets[b];
+  const int n = a.node_offsets[b + 1] - s0;
+  const int node_base = (tb - base_s) * bs;
+  const uint16_t* kn = (const uint16_t*)a.k_node;
+  const uint16_t* vn = (const uint16_t*)a.v_node;
+  uint16_t* kt = (uint16_t*)a.k_tail;
+  uint16_t* vt = (uint16_t*)a.v_tail;
+  for (int c = threadIdx.x; c < bs * CH; c += blockDim.x) {
+    const int slot = c / CH, ch = c % CH;
+    const int node = node_base + slot;
+    uint4 kv = make_uint4(0u, 0u, 0u, 0u), vv = kv;
+    if (node < n) {
+      const size_t off = ((size_t)(s0 + node) * Hkv + g) * D + ch * 8;
+      kv = *(const uint4*)(kn + off);
+      vv = *(const uint4*)(vn + off);
+    }
+    *(uint4*)(kt + (((size_t)tb * Hkv + g) * bs + slot) * D + ch * 8) = kv;
+    const uint32_t w4[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vs[slot][ch * 8 + e] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+  }
+  __syncthreads();
+  const int groups = bs / 8;
+  for (int c = threadIdx.x; c < D * groups; c += blockDim.x) {
+    const int d = c / groups, sg = c % groups;
+    uint32_t w4[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w4[e] = (uint32_t)vs[sg * 8 + 2 * e][d] | ((uint32_t)vs[sg * 8 + 2 * e + 1][d] << 16);
+    *(uint4*)(vt + (((size_t)tb * Hkv + g) * D + d) * bs + sg * 8) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+  }
+}
+
+__global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) { prep_sequence(a, blockIdx.x); }
+
+// Blocks [0, B): preparation of sequence blockIdx.x; block B: the work plan; blocks past it: one
+// packed node block (index % tail_blocks) of one KV head (index / tail_blocks).
+template <int D>
+__global__ __launch_bounds__(kPrepThreads) void prelude_kernel(PrepArgs pa, PlanArgs pl, AttnArgs a,
+                                                               int tail_blocks) {
+  const int bid = blockIdx.x;
+  if (bid < pl.B) {
+    prep_sequence(pa, bid);
+  } else if (bid == pl.B) {
+    plan_block(pl, a);
+  } else {
+    const int i = bid - pl.B - 1;
+    pack_block<D>(a, i % tail_blocks, i / tail_blocks);
+  }
+}
+
+PrepArgs prep_args(const int32_t* node_offsets, const int32_t* prefix_len, const int32_t* parent,
+                   uint8_t* chain_ws, uint64_t* mask_ws, const tav_tree_out* out, uint32_t* status) {
+  PrepArgs a;
+  a.node_offsets = node_offsets; a.prefix_len = prefix_len; a.parent = parent;
+  a.chain_ws = chain_ws; a.mask_ws = mask_ws;
+  a.depth_out = out ? out->depth : nullptr;
+  a.pos_out = out ? out->position : nullptr;
+  a.mask_out = out ? out->mask : nullptr;
+  a.chain_out = out ? out->is_chain : nullptr;
+  a.status = status;
+  return a;
 }
 
 }  // namespace
@@ -221,22 +350,24 @@ hipError_t launch_clear_status(uint32_t* status, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_plan(const Plan& p, const int32_t* node_offsets, const int32_t* prefix_len,
-                       const uint8_t* is_chain, int32_t* seq_rb_off, int32_t* rb_seq, int32_t* rb_tile,
-                       int32_t* tail_blk, int32_t* wg_rb, int32_t* wg_tile, int32_t* rb_meta,
-                       uint32_t* status, hipStream_t s) {
-  plan_kernel<<<1, 1024, 0, s>>>(node_offsets, prefix_len, p.B, p.NB, p.bs, p.total_rb,
-                                 p.tiles_per_head, p.tail_blocks, p.C, p.W, seq_rb_off, rb_seq,
-                                 rb_tile, tail_blk, wg_rb, wg_tile, is_chain, rb_meta, status);
-  return hipGetLastError();
-}
-
 hipError_t launch_prep(const Plan& p, const int32_t* node_offsets, const int32_t* prefix_len,
                        const int32_t* parent, uint8_t* chain_ws, uint64_t* mask_ws,
                        const tav_tree_out* out, uint32_t* status, hipStream_t s) {
-  prep_kernel<<<p.B, 256, 0, s>>>(node_offsets, prefix_len, parent, chain_ws, mask_ws,
-                                  out ? out->depth : nullptr, out ? out->position : nullptr,
-                                  out ? out->mask : nullptr, out ? out->is_chain : nullptr, status);
+  prep_kernel<<<p.B, kPrepThreads, 0, s>>>(
+      prep_args(node_offsets, prefix_len, parent, chain_ws, mask_ws, out, status));
+  return hipGetLastError();
+}
+
+hipError_t launch_prelude(const Plan& p, const int32_t* parent, const tav_tree_out* out, const AttnArgs& a,
+                          hipStream_t s) {
+  const PrepArgs pa = prep_args(a.node_offsets, a.prefix_len, parent, const_cast<uint8_t*>(a.is_chain),
+                                const_cast<uint64_t*>(a.mask), out, a.status);
+  PlanArgs pl;
+  pl.B = p.B; pl.NB = p.NB; pl.bs = p.bs; pl.total_rb_host = p.total_rb; pl.tiles_host = p.tiles_per_head;
+  pl.tail_blocks_host = p.tail_blocks; pl.C = p.C; pl.W = p.W;
+  const int grid = p.B + 1 + p.tail_blocks * p.Hkv;
+  if (p.D == 128) prelude_kernel<128><<<grid, kPrepThreads, 0, s>>>(pa, pl, a, p.tail_blocks > 0 ? p.tail_blocks : 1);
+  else prelude_kernel<64><<<grid, kPrepThreads, 0, s>>>(pa, pl, a, p.tail_blocks > 0 ? p.tail_blocks : 1);
   return hipGetLastError();
 }
 

@@ -45,11 +45,6 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 constexpr int kTargetWorkgroups = 256;  // one round of one workgroup per MI355X compute unit
-// With verification running beside it on another stream, attention leaves an eighth of the
-// compute units to the streaming verification kernels (measured on the batched-verify workload:
-// the whole pass ~2% shorter than with all 256 taken; at 192 it is ~2% shorter again, but the
-// attention kernel itself ~10% longer).
-constexpr int kConcurrentAttnWorkgroups = 224;
 constexpr int kMinTilesPerWG = 8;       // at least 512 keys per attention workgroup (more than kRbCost)
 
 int log2_exact(int x) {
@@ -175,17 +170,7 @@ tav_status make_plan(const tav_problem* p, const tav_presto_io* pr, Plan* out,
   P.off_child_p = o; o = align_up(o + (size_t)P.N * 8);
   P.off_child_q = o; o = align_up(o + (size_t)P.N * 4);
   P.off_presto = o; o = align_up(o + (size_t)(pr ? pr->num_requests : 0) * 8);
-  if (p->vocab > 0) {
-    const int epu = p->dtype == TAV_BF16 ? 8 : 4;
-    P.nsl = ceil_div(p->vocab, kSliceThreads * kSliceUnits * epu);
-    P.nch = ceil_div(ceil_div(p->vocab, epu), 64);
-  }
-  P.off_sl_m = o; o = align_up(o + (size_t)P.N * P.nsl * 4);
-  P.off_sl_s = o; o = align_up(o + (size_t)P.N * P.nsl * 8);
-  P.off_sl_z = o; o = align_up(o + (size_t)P.N * P.nsl * 2 * 8);
-  P.off_ch_w = o; o = align_up(o + (size_t)P.N * P.nch * 4);
-  P.off_dlist = o; o = align_up(o + (size_t)P.N * 4);
-  P.off_rec = o; o = align_up(o + (size_t)(p->vocab > 0 ? P.N : 0) * kRecWords * 4);
+  if (p->vocab > 0) P.nch = ceil_div(ceil_div(p->vocab, p->dtype == TAV_BF16 ? 8 : 4), 64);
   P.total = o;
   *out = P;
   return TAV_OK;
@@ -234,7 +219,7 @@ tav_status check_verify(const tav_problem* p, const tav_verify_io* io) {
   if (io->max_path < 1) return fail(TAV_ERR_BAD_SHAPE, "max_path must be >= 1");
   if (p->vocab < 1) return fail(TAV_ERR_BAD_SHAPE, "vocab must be >= 1 for verification");
   const int epu = p->dtype == TAV_BF16 ? 8 : 4;
-  const int64_t cap = (int64_t)kMaxSlices * kSliceThreads * kSliceUnits * epu;
+  const int64_t cap = (int64_t)kMaxChunks * 64 * epu;
   if (p->vocab % epu)
     return fail(TAV_ERR_UNSUPPORTED, "vocab must be a multiple of %d for this logits dtype (got %d)", epu, p->vocab);
   if (p->vocab > cap)
@@ -321,15 +306,12 @@ tav_status timing_pair(hipEvent_t* start, hipEvent_t* stop) {
   return TAV_OK;
 }
 
-tav_status enqueue_attention(const tav_problem* p, const Plan& P, const tav_attn_io* io, void* ws,
-                             hipStream_t s) {
+// Tree preparation and attention (bf16: preparation, plan and node packing in one launch).
+tav_status enqueue_prep_attention(const tav_problem* p, const Plan& P, const tav_tree* t,
+                                  const tav_tree_out* out, const tav_attn_io* io, void* ws, hipStream_t s) {
   const AttnArgs a = attn_args(p, P, io, ws);
   if (p->dtype == TAV_BF16) {
-    TAV_HIP(launch_plan(P, p->node_offsets, p->prefix_len, a.is_chain, const_cast<int32_t*>(a.seq_rb_off),
-                        const_cast<int32_t*>(a.rb_seq), const_cast<int32_t*>(a.rb_tile),
-                        const_cast<int32_t*>(a.tail_blk), const_cast<int32_t*>(a.wg_rb),
-                        const_cast<int32_t*>(a.wg_tile), const_cast<int32_t*>(a.rb_meta), a.status, s));
-    TAV_HIP(launch_pack_tail(P, a, s));
+    TAV_HIP(launch_prelude(P, t->parent, out, a, s));
     hipEvent_t ev0 = nullptr, ev1 = nullptr;
     if (g_timing.on) {
       const tav_status st = timing_pair(&ev0, &ev1);
@@ -340,47 +322,62 @@ tav_status enqueue_attention(const tav_problem* p, const Plan& P, const tav_attn
     if (g_timing.on) TAV_HIP(hipEventRecord(ev1, s));
     TAV_HIP(launch_merge(P, a, true, s));
   } else {
+    const tav_status st = enqueue_prep(p, P, t, out, ws, s);
+    if (st != TAV_OK) return st;
     TAV_HIP(launch_attn_f32(P, a, s));
   }
   return TAV_OK;
 }
 
-tav_status enqueue_verify(const tav_problem* p, const Plan& P, const tav_tree* t,
-                          const tav_verify_io* io, void* ws, hipStream_t s) {
+VocabArgs vocab_args(const tav_problem* p, const Plan& P, const tav_tree* t, const tav_verify_io* io, void* ws) {
   uint32_t* status = ws_at<uint32_t>(ws, P.off_status);
-  float* stats = io->node_stats ? io->node_stats : ws_at<float>(ws, P.off_stats);
-  int32_t* term = io->node_term_token ? io->node_term_token : ws_at<int32_t>(ws, P.off_term);
   VocabArgs va;
   va.logits = io->logits; va.temperature = io->temperature; va.draft = io->draft;
   va.draft_row = io->draft_row; va.node_offsets = p->node_offsets; va.parent = t->parent;
   va.token = t->token; va.sampled = t->sampled; va.uniforms = io->uniforms;
-  va.stats = stats; va.term_token = term; va.status = status;
+  va.stats = io->node_stats ? io->node_stats : ws_at<float>(ws, P.off_stats);
+  va.term_token = io->node_term_token ? io->node_term_token : ws_at<int32_t>(ws, P.off_term);
+  va.status = status;
   va.child_p = ws_at<double>(ws, P.off_child_p);
   va.child_q = ws_at<float>(ws, P.off_child_q);
   va.B = P.B; va.N = P.N; va.V = p->vocab; va.R = io->num_draft_rows;
-  va.sl_m = ws_at<float>(ws, P.off_sl_m);
-  va.sl_s = ws_at<double>(ws, P.off_sl_s);
-  va.sl_z = ws_at<double>(ws, P.off_sl_z);
-  va.ch_w = ws_at<float>(ws, P.off_ch_w);
-  va.dlist = ws_at<int32_t>(ws, P.off_dlist);
-  va.rec = ws_at<int32_t>(ws, P.off_rec);
-  va.dcount = (int32_t*)(status + kCounterWord);
-  va.nsl = P.nsl; va.nch = P.nch;
-  int dev = 0, cus = 0;
-  TAV_HIP(hipGetDevice(&dev));
-  TAV_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
-  TAV_HIP(launch_vocab(va, p->dtype == TAV_BF16, cus > 0 ? cus : 256, s));
+  va.queue = (int32_t*)(status + kCounterWord);
+  va.nch = P.nch;
+  return va;
+}
+
+tav_status enqueue_walk(const tav_problem* p, const Plan& P, const tav_tree* t, const tav_verify_io* io,
+                        const VocabArgs& va, hipStream_t s) {
   WalkArgs wa;
   wa.logits = io->logits; wa.temperature = io->temperature; wa.draft = io->draft;
   wa.draft_row = io->draft_row; wa.node_offsets = p->node_offsets; wa.parent = t->parent;
   wa.token = t->token; wa.sampled = t->sampled; wa.uniforms = io->uniforms;
-  wa.stats = stats; wa.term_token = term; wa.node_status = io->node_status; wa.path = io->path;
+  wa.stats = va.stats; wa.term_token = va.term_token; wa.node_status = io->node_status; wa.path = io->path;
   wa.child_p = va.child_p; wa.child_q = va.child_q;
-  wa.path_len = io->path_len; wa.bonus = io->bonus_token; wa.status = status;
+  wa.path_len = io->path_len; wa.bonus = io->bonus_token; wa.status = va.status;
   wa.B = P.B; wa.V = p->vocab; wa.R = io->num_draft_rows; wa.max_path = io->max_path;
   wa.logits_bf16 = p->dtype == TAV_BF16;
   TAV_HIP(launch_walk(wa, s));
   return TAV_OK;
+}
+
+tav_status num_compute_units(int* cus) {
+  int dev = 0;
+  TAV_HIP(hipGetDevice(&dev));
+  TAV_HIP(hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev));
+  if (*cus < 1) *cus = 1;
+  return TAV_OK;
+}
+
+// Verification: the vocabulary workers' kernel, then the walk.
+tav_status enqueue_verify(const tav_problem* p, const Plan& P, const tav_tree* t,
+                          const tav_verify_io* io, void* ws, hipStream_t s) {
+  const VocabArgs va = vocab_args(p, P, t, io, ws);
+  int cus = 0;
+  tav_status st = num_compute_units(&cus);
+  if (st != TAV_OK) return st;
+  TAV_HIP(launch_vocab(va, p->dtype == TAV_BF16, cus, s));
+  return enqueue_walk(p, P, t, io, va, s);
 }
 
 tav_status enqueue_presto(const Plan& P, const tav_presto_io* io, void* ws, hipStream_t s) {
@@ -397,6 +394,7 @@ tav_status enqueue_presto(const Plan& P, const tav_presto_io* io, void* ws, hipS
   return TAV_OK;
 }
 
+// Events ordering the two streams of the whole-pass call (per host thread and device).
 struct StreamEvents {
   int device = -1;
   hipEvent_t fork = nullptr, join = nullptr;
@@ -407,11 +405,13 @@ tav_status get_events(hipEvent_t* fork, hipEvent_t* join) {
   int dev = 0;
   TAV_HIP(hipGetDevice(&dev));
   if (g_events.device != dev) {
-    if (g_events.fork) (void)hipEventDestroy(g_events.fork);
-    if (g_events.join) (void)hipEventDestroy(g_events.join);
-    g_events.fork = g_events.join = nullptr;
-    TAV_HIP(hipEventCreateWithFlags(&g_events.fork, hipEventDisableTiming));
-    TAV_HIP(hipEventCreateWithFlags(&g_events.join, hipEventDisableTiming));
+    for (hipEvent_t* e : {&g_events.fork, &g_events.join}) {
+      if (*e) (void)hipEventDestroy(*e);
+      *e = nullptr;
+    }
+    g_events.device = -1;
+    for (hipEvent_t* e : {&g_events.fork, &g_events.join})
+      TAV_HIP(hipEventCreateWithFlags(e, hipEventDisableTiming));
     g_events.device = dev;
   }
   *fork = g_events.fork;
@@ -458,8 +458,7 @@ tav_status tav_tree_attention(const tav_problem* prob, const tav_tree* tree, con
   if (st != TAV_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   TAV_HIP(launch_clear_status(ws_at<uint32_t>(workspace, P.off_status), s));
-  st = enqueue_prep(prob, P, tree, nullptr, workspace, s);
-  if (st == TAV_OK) st = enqueue_attention(prob, P, io, workspace, s);
+  st = enqueue_prep_attention(prob, P, tree, nullptr, io, workspace, s);
   return st == TAV_OK ? ok() : st;
 }
 
@@ -500,7 +499,7 @@ tav_status tav_tree_attn_verify(const tav_problem* prob, const tav_tree* tree, c
                                 void* attn_stream, void* verify_stream) {
   const bool two = verify_stream != attn_stream && (verify || presto);
   Plan P;
-  tav_status st = make_plan(prob, presto, &P, two && verify ? kConcurrentAttnWorkgroups : kTargetWorkgroups);
+  tav_status st = make_plan(prob, presto, &P);
   if (st == TAV_OK) st = check_ws(P, workspace, workspace_bytes);
   if (st == TAV_OK) st = check_tree(tree, verify != nullptr);
   if (st == TAV_OK) st = check_attn(prob, attn);
@@ -513,25 +512,25 @@ tav_status tav_tree_attn_verify(const tav_problem* prob, const tav_tree* tree, c
     st = get_events(&fork, &join);
     if (st != TAV_OK) return st;
   }
-  // Verification needs only the status reset.  The attention chain is enqueued first so that the
-  // attention workgroups, which each take a whole compute unit, are dispatched before the
-  // streaming verification kernels fill the chip.
-  TAV_HIP(launch_clear_status(ws_at<uint32_t>(workspace, P.off_status), sa));
-  if (two) TAV_HIP(hipEventRecord(fork, sa));
-  st = enqueue_prep(prob, P, tree, tree_out, workspace, sa);
-  if (st != TAV_OK) return st;
-  st = enqueue_attention(prob, P, attn, workspace, sa);
-  if (st != TAV_OK) return st;
-  if (two) TAV_HIP(hipStreamWaitEvent(sv, fork, 0));
   hipStream_t s2 = two ? sv : sa;
+  // Verification needs only the status reset.  Its workers (one per compute unit) are enqueued
+  // before the attention chain: they stream the vocabulary while the preparation kernels run, and
+  // each attention workgroup starts on a compute unit whose worker has found the queue empty.
+  TAV_HIP(launch_clear_status(ws_at<uint32_t>(workspace, P.off_status), sa));
+  if (two) {
+    TAV_HIP(hipEventRecord(fork, sa));
+    TAV_HIP(hipStreamWaitEvent(sv, fork, 0));
+  }
+  if (presto) {   // independent of everything else; tiny
+    st = enqueue_presto(P, presto, workspace, s2);
+    if (st != TAV_OK) return st;
+  }
   if (verify) {
     st = enqueue_verify(prob, P, tree, verify, workspace, s2);
     if (st != TAV_OK) return st;
   }
-  if (presto) {
-    st = enqueue_presto(P, presto, workspace, s2);
-    if (st != TAV_OK) return st;
-  }
+  st = enqueue_prep_attention(prob, P, tree, tree_out, attn, workspace, sa);
+  if (st != TAV_OK) return st;
   if (two) {
     TAV_HIP(hipEventRecord(join, sv));
     TAV_HIP(hipStreamWaitEvent(sa, join, 0));

@@ -14,13 +14,9 @@ constexpr int kRowsPerWG = 256;    // query rows (node x head-in-group) per atte
 constexpr int kMaxTreeNodes = 256; // non-chain trees: ancestor sets are 256-bit masks
 constexpr int kMaskWords = 4;
 constexpr int kMaxChildren = 256;  // children of one node held by the verification kernels
-constexpr int kSliceThreads = 256; // threads of a vocabulary-slice workgroup
-constexpr int kSliceUnits = 8;     // 16-byte units of a row per thread and slice
-constexpr int kMaxSlices = 64;     // slices per vocabulary row (V <= 1 Mi bf16 / 512 Ki f32)
-constexpr int kMaxChunks = kMaxSlices * kSliceUnits * (kSliceThreads / 64);
-constexpr int kRecWords = 32;      // per-node record of the vocabulary kernels (int32 words)
-constexpr int kRecKidsMax = 12;    // children held in the record
-constexpr int kCounterWord = 16;   // status block: word 0 = status bits, word 16 = a counter
+constexpr int kMaxChunks = 2048;   // chunks of 64 sixteen-byte units per vocabulary row
+                                   // (V <= 1 Mi bf16 / 512 Ki f32 tokens)
+constexpr int kCounterWord = 16;   // status block: word 0 = status bits, word 16 = a work-queue counter
 
 // Work decomposition of the attention pass.  A "row block" is up to
 // kRowsPerWG / G consecutive nodes of one sequence; it sees ceil(L / 64) prefix
@@ -43,9 +39,8 @@ struct Plan {
   size_t off_status = 0, off_chain = 0, off_mask = 0, off_seq_rb = 0, off_rb_seq = 0,
          off_rb_tile = 0, off_tail_blk = 0, off_wg_rb = 0, off_wg_tile = 0, off_rb_meta = 0, off_ktail = 0, off_vtail = 0, off_part_o = 0,
          off_part_lse = 0, off_stats = 0, off_term = 0, off_child_p = 0, off_child_q = 0,
-         off_presto = 0, off_sl_m = 0, off_sl_s = 0, off_sl_z = 0, off_ch_w = 0, off_dlist = 0,
-         off_rec = 0, total = 0;
-  int nsl = 0, nch = 0;   // vocabulary slices and chunks (64 units) per row
+         off_presto = 0, total = 0;
+  int nch = 0;            // vocabulary chunks (64 sixteen-byte units) per row
 };
 
 __host__ __device__ static inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -60,10 +55,10 @@ __host__ __device__ static inline int rb_tiles(int L, int n, int rb, int NB) {
 }
 
 // What the attention kernel needs of a row block when it starts computing it, gathered by the
-// plan kernel into one record (one scalar load): its key tiles [tile0, tile_end) per KV head,
-// the sequence's first node and node count, its prefix length, the block's first node, the
-// bound on its nodes (min(n, node0 + nodes per block)) and flags (1: the tree is a chain,
-// 2: the row block is computed -- a chain, or a tree within the mask width).
+// plan into one record (scalar loads): its key tiles [tile0, tile_end) per KV head, the
+// sequence's first node and node count, its prefix length, the block's first node, the bound on
+// its nodes (min(n, node0 + nodes per block)), flags (2: the tree fits the ancestor masks) and
+// the sequence index (whose chain flag the preparation writes).
 // Work split of the attention kernel: every row block costs its key tiles plus kRbCost tiles'
 // worth of fixed work (its partial prefix tile and masked tree tile, the output of the finished
 // segment and the start of the next), and each workgroup takes an equal share Cv of that
@@ -72,7 +67,7 @@ __host__ __device__ static inline int rb_tiles(int L, int n, int rb, int NB) {
 constexpr int kRbCost = 4;
 
 enum RbMeta { kMetaTile0 = 0, kMetaTileEnd, kMetaS0, kMetaN, kMetaL, kMetaNode0, kMetaTailN, kMetaFlags,
-              kMetaWords };
+              kMetaSeq, kMetaWords };
 
 struct AttnArgs {
   const void* q;
@@ -118,14 +113,8 @@ struct VocabArgs {
   double* child_p;       // [N] p of the node's token under its parent's target distribution
   float* child_q;        // [N] q~ of the node's token under its parent's draft row (0 if none)
   uint32_t* status;
-  float* sl_m;           // [N, nsl] largest raw logit of each slice
-  double* sl_s;          // [N, nsl] sum exp2(l * log2e / T - ref) of each slice
-  double* sl_z;          // [N, 2 nsl] sum (p - q~)+ of each half slice (listed rows)
-  float* ch_w;           // [N, nch] chunk sums: of exp2(..) (relative to the slice) or of (p - q~)+
-  int32_t* dlist;        // [N] nodes with a sampled child and a draft row
-  int32_t* rec;          // [N, kRecWords] per-node record (sequence, 1/T, children)
-  int32_t* dcount;       // length of dlist (cleared with the status word)
-  int B, N, V, R, nsl, nch;
+  int32_t* queue;        // node counter of the vocabulary workers (cleared with the status word)
+  int B, N, V, R, nch;
 };
 
 struct WalkArgs {
@@ -173,17 +162,16 @@ struct PrestoArgs {
 // Kernel launchers (defined next to their kernels).  They return the HIP error
 // of the launch.
 hipError_t launch_clear_status(uint32_t* status, hipStream_t s);
-hipError_t launch_plan(const Plan& p, const int32_t* node_offsets, const int32_t* prefix_len,
-                       const uint8_t* is_chain, int32_t* seq_rb_off, int32_t* rb_seq, int32_t* rb_tile,
-                       int32_t* tail_blk, int32_t* wg_rb, int32_t* wg_tile, int32_t* rb_meta,
-                       uint32_t* status, hipStream_t s);
-hipError_t launch_pack_tail(const Plan& p, const AttnArgs& a, hipStream_t s);
 hipError_t launch_prep(const Plan& p, const int32_t* node_offsets, const int32_t* prefix_len,
                        const int32_t* parent, uint8_t* chain_ws, uint64_t* mask_ws,
                        const tav_tree_out* out, uint32_t* status, hipStream_t s);
+// bf16 attention: preparation, work plan and node packing in one launch.
+hipError_t launch_prelude(const Plan& p, const int32_t* parent, const tav_tree_out* out, const AttnArgs& a,
+                          hipStream_t s);
 hipError_t launch_attn_bf16(const Plan& p, const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_f32(const Plan& p, const AttnArgs& a, hipStream_t s);
 hipError_t launch_merge(const Plan& p, const AttnArgs& a, bool bf16_out, hipStream_t s);
+// Vocabulary workers: one 512-thread workgroup per compute unit, persistent over the node queue.
 hipError_t launch_vocab(const VocabArgs& a, bool bf16_logits, int num_cus, hipStream_t s);
 hipError_t launch_walk(const WalkArgs& a, hipStream_t s);
 hipError_t launch_presto(const PrestoArgs& a, hipStream_t s);

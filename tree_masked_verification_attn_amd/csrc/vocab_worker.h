@@ -1,0 +1,455 @@
+// Per-node vocabulary work of the verification, done by one 512-thread workgroup per node.
+//
+// RheoSampling, Section 3.3 Algorithm 1 (RheoVerification): the target distribution at
+// node v is p = softmax(l / T) (temperature only in sampling and verification, Section
+// 5.4); when v has a sampled child Y drawn from q~ (the draft row of v), Y is tested with
+// min(1, p(Y) / q~(Y)) and a rejection replaces p by the residual r = norm(max(0, p - q~));
+// the other children are tested against r (or p) one by one, each rejection zeroing its
+// token; if the walk ends at v the output token is drawn from what is left.  Without a
+// sampled child this is the sequential rejection of Progressive Tree Drafting (Section
+// 3.2, Appendix E / F).
+//
+// For node v the worker computes, with the logits row streamed from HBM once:
+//   M = max l / T, S = sum exp(l / T - M)                (the normaliser of p),
+//   Z = sum (p - q~)+ when v has a sampled child          (the normaliser of r),
+//   p and q~ at each child's token                       (the walk's tests),
+//   the token the final draw at v would give               (inverse CDF in token order with
+//                                                           u[v][1], deterministic children's
+//                                                           tokens removed).
+// Pass 1 streams the row in steps of 64 KB (512 threads x 8 sixteen-byte units, the next step's
+// loads in flight while the current one is summed): each wave keeps the largest raw logit m of
+// its part of the step as a reference and writes sum exp2(l log2e / T - ref(m)) of every chunk of
+// 64 units (one unit per lane) to LDS.  M and S follow from these pieces in fp64.  Pass 2 (nodes
+// with a sampled child) streams the draft row with the logits row again (the second read of a
+// row just read mostly hits the cache) and replaces the chunk weights with those of (p - q~)+.
+// The pick then runs on one wave: point values of the children, the deterministic children's
+// weights taken out of their chunks, an fp64 scan over the chunks for u * W, and one chunk re-read.
+// Nodes are taken from a device queue; a worker never waits for another workgroup.
+#pragma once
+
+#include "tav_internal.h"
+
+namespace tav {
+namespace vw {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// A worker of NT threads reading NU sixteen-byte units per thread and step.  A chunk is 64 units,
+// one per lane of a wave, so chunk k * waves + w of a step is unit k of every lane of wave w.
+template <int NT, int NU>
+struct Cfg {
+  static constexpr int kThreads = NT;
+  static constexpr int kWaves = NT / 64;
+  static constexpr int kUnits = NU;
+  static constexpr int kStepUnits = NT * NU;
+  static constexpr int kChunksPerStep = kStepUnits / 64;
+  static constexpr int kMaxSteps = kMaxChunks / kChunksPerStep;   // rows of up to kMaxChunks chunks
+  static constexpr int kMaxPieces = kMaxSteps * kWaves;           // (step, wave) references
+  static_assert(NU % 2 == 0 && NT % 64 == 0, "worker shape");
+};
+
+template <class C>
+struct Lds {
+  float cw[kMaxChunks];                      // chunk weights
+  float part[C::kWaves][C::kUnits * 64];     // per-wave transpose of unit sums into chunk sums
+  float ref_m[C::kMaxPieces];                // largest raw logit of each (step, wave) piece
+  double ref_s[C::kMaxPieces];               // sum exp2(l log2e / T - ref) of each piece
+  double red_d[C::kWaves];
+  int kid_id[kMaxChildren];                  // children of the node (sequence-local ids) ...
+  int kid_tok[kMaxChildren];                 // ... their tokens
+  uint8_t kid_smp[kMaxChildren];             // ... and sampled flags
+  int item, cnt, nk, ns, err;
+};
+
+template <typename LT>
+__device__ inline float unit_elem(const uint4& u, int e);
+template <>
+__device__ inline float unit_elem<uint16_t>(const uint4& u, int e) {
+  const uint32_t w = (e >> 1) == 0 ? u.x : (e >> 1) == 1 ? u.y : (e >> 1) == 2 ? u.z : u.w;
+  return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+}
+template <>
+__device__ inline float unit_elem<float>(const uint4& u, int e) {
+  return __uint_as_float(e == 0 ? u.x : e == 1 ? u.y : e == 2 ? u.z : u.w);
+}
+
+template <typename LT>
+__device__ inline float logit_at(const void* logits, size_t idx);
+template <>
+__device__ inline float logit_at<uint16_t>(const void* logits, size_t idx) {
+  return __uint_as_float(((uint32_t)((const uint16_t*)logits)[idx]) << 16);
+}
+template <>
+__device__ inline float logit_at<float>(const void* logits, size_t idx) {
+  return ((const float*)logits)[idx];
+}
+
+__device__ inline double wave_sum_d(double x) {
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) x += __shfl_xor(x, d);
+  return x;
+}
+__device__ inline float wave_max_f(float x) {
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) x = fmaxf(x, __shfl_xor(x, d));
+  return x;
+}
+__device__ inline void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// log2-domain reference of a piece maximum (a piece of -inf logits uses 0; its sum is 0).
+__device__ inline float ref_l2(float m_raw, float invT) {
+  return (m_raw == -INFINITY ? 0.f : m_raw * invT) * kLog2e;
+}
+
+// Sums x[k] over the 64 lanes of the wave for each k (chunk k * waves + wave of the step),
+// through the wave's LDS transpose buffer; returns chunk (lane / (64 / NU))'s total in the first
+// lane of each group of 64 / NU lanes.
+template <int NU>
+__device__ inline float wave_chunk_totals(const float (&x)[NU], float* part, int lane) {
+  constexpr int TPC = 64 / NU;   // lanes per chunk, each summing NU values
+#pragma unroll
+  for (int k = 0; k < NU; ++k) part[k * 64 + lane] = x[k];
+  wave_sync();
+  const float* src = part + (lane / TPC) * 64 + (lane % TPC) * NU;
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < NU; i += 4) {
+    const float4 a4 = *(const float4*)(src + i);
+    t += (a4.x + a4.y) + (a4.z + a4.w);
+  }
+#pragma unroll
+  for (int d = 1; d < TPC; d <<= 1) t += __shfl_xor(t, d);
+  wave_sync();   // the buffer is reused by the next step
+  return t;
+}
+
+template <typename LT, class C>
+__device__ inline void load_step(uint4 (&r)[C::kUnits], const LT* row, int step, int tid, int nunits) {
+  constexpr int EPU = 16 / sizeof(LT);
+#pragma unroll
+  for (int k = 0; k < C::kUnits; ++k) {
+    const int u = step * C::kStepUnits + k * C::kThreads + tid;
+    r[k] = *(const uint4*)(row + (size_t)(u < nunits ? u : 0) * EPU);
+  }
+}
+
+// Everything the walk needs of node v.
+template <typename LT, class C>
+__device__ void process_node(const VocabArgs& a, Lds<C>& L, int v) {
+  constexpr int kThreads = C::kThreads, kWaves = C::kWaves, kUnits = C::kUnits;
+  constexpr int kStepUnits = C::kStepUnits, kChunksPerStep = C::kChunksPerStep;
+  constexpr int TPC = 64 / kUnits;   // lanes per chunk total
+  constexpr int EPU = 16 / sizeof(LT);
+  constexpr int QPU = EPU / 4;
+  constexpr int CT = 64 * EPU;   // tokens per chunk
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int V = a.V, nunits = V / EPU, nch = a.nch;
+  const int nsteps = (nunits + kStepUnits - 1) / kStepUnits;
+  const LT* row = (const LT*)a.logits + (size_t)v * V;
+  // the first step's loads go out before anything else
+  uint4 cur[kUnits];
+  load_step<LT, C>(cur, row, 0, tid, nunits);
+  // sequence of v: the number of sequence ends node_offsets[1..B] that are <= v
+  if (tid == 0) { L.cnt = 0; L.nk = 0; L.ns = 0; L.err = 0; }
+  __syncthreads();
+  {
+    int c = 0;
+    for (int t = tid + 1; t <= a.B; t += kThreads) c += a.node_offsets[t] <= v;
+    if (c) atomicAdd(&L.cnt, c);
+  }
+  __syncthreads();
+  const int b = L.cnt < a.B ? L.cnt : a.B - 1;
+  const int s0 = a.node_offsets[b];
+  const int n = a.node_offsets[b + 1] - s0;
+  const float Tb = a.temperature[b];
+  const float invT = 1.f / Tb;
+  const float invTl2 = invT * kLog2e;
+  const int dr = a.draft_row[v];
+  const bool dr_ok = dr >= 0 && dr < a.R;
+  // children of v, the parent-array and temperature checks
+  {
+    uint32_t err = 0;
+    for (int c = tid; c < n; c += kThreads) {
+      const int pc = a.parent[s0 + c];
+      if (c == 0 ? pc != -1 : (pc < 0 || pc >= c)) err |= TAV_DEV_BAD_PARENT;
+      if (c > 0 && pc == v - s0) {
+        const int k = atomicAdd(&L.nk, 1);
+        const uint8_t smp = a.sampled[s0 + c];
+        if (smp) atomicAdd(&L.ns, 1);
+        if (k < kMaxChildren) {
+          L.kid_id[k] = c;
+          L.kid_tok[k] = a.token[s0 + c];
+          L.kid_smp[k] = smp;
+        }
+      }
+    }
+    if (tid == 0 && !(Tb > 0.f && Tb < INFINITY)) err |= TAV_DEV_BAD_TEMPERATURE;
+    if (err) atomicOr(&L.err, (int)err);
+  }
+  // ---- pass 1: per-piece references and sums, chunk weights relative to their piece
+  float* part = L.part[wave];
+  for (int s = 0; s < nsteps; ++s) {
+    uint4 nxt[kUnits];
+    if (s + 1 < nsteps) load_step<LT, C>(nxt, row, s + 1, tid, nunits);
+    const int ub = s * kStepUnits + tid;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kUnits; ++k)
+      if (ub + k * kThreads < nunits) {
+#pragma unroll
+        for (int e = 0; e < EPU; ++e) mx = fmaxf(mx, unit_elem<LT>(cur[k], e));
+      }
+    mx = wave_max_f(mx);
+    const float r2 = ref_l2(mx, invT);
+    // a NaN or +inf logit makes the sum NaN, which is reported below
+    float su[kUnits];
+    double sd = 0.0;
+#pragma unroll
+    for (int k = 0; k < kUnits; ++k) {
+      su[k] = 0.f;
+      if (ub + k * kThreads < nunits) {
+#pragma unroll
+        for (int e = 0; e < EPU; ++e) su[k] += __builtin_amdgcn_exp2f(unit_elem<LT>(cur[k], e) * invTl2 - r2);
+      }
+      sd += (double)su[k];
+    }
+    const float ct = wave_chunk_totals(su, part, lane);
+    const int c = s * kChunksPerStep + (lane / TPC) * kWaves + wave;
+    if ((lane % TPC) == 0 && c < nch) L.cw[c] = ct;
+    sd = wave_sum_d(sd);
+    if (lane == 0) {
+      L.ref_m[s * kWaves + wave] = mx;
+      L.ref_s[s * kWaves + wave] = sd;
+    }
+    if (s + 1 < nsteps) {
+#pragma unroll
+      for (int k = 0; k < kUnits; ++k) cur[k] = nxt[k];
+    }
+  }
+  __syncthreads();
+  // ---- M and S from the pieces (every wave computes the same values)
+  const int npieces = nsteps * kWaves;
+  float ml = -INFINITY;
+  for (int i = lane; i < npieces; i += 64) ml = fmaxf(ml, L.ref_m[i]);
+  const float Mraw = wave_max_f(ml);
+  const bool no_mass = Mraw == -INFINITY;
+  const float M = no_mass ? 0.f : Mraw * invT;
+  const float Ml2 = M * kLog2e;
+  double sc = 0.0;
+  for (int i = lane; i < npieces; i += 64) {
+    const double si = L.ref_s[i];
+    if (si != 0.0) sc += si * exp2((double)ref_l2(L.ref_m[i], invT) - (double)Ml2);
+  }
+  const double S = wave_sum_d(sc);
+  const float invS = (float)(1.0 / S);
+  const int nk = L.nk < kMaxChildren ? L.nk : kMaxChildren;
+  const bool use_draft = L.ns > 0 && dr_ok;
+  double Zt = 0.0;
+  if (use_draft) {
+    // ---- pass 2: chunk weights of (p - q~)+ and their total Z.  Each step is taken in two
+    // halves of kUnits / 2 units per thread, one half computed while the other's loads fly.
+    constexpr int HU = kUnits / 2;
+    const float* drow = a.draft + (size_t)dr * V;
+    auto load_half = [&](uint4 (&r)[HU], float4 (&q)[HU][QPU], int s, int h) __attribute__((always_inline)) {
+#pragma unroll
+      for (int k = 0; k < HU; ++k) {
+        const int u = s * kStepUnits + (h * HU + k) * kThreads + tid;
+        const size_t e0 = (size_t)(u < nunits ? u : 0) * EPU;
+        r[k] = *(const uint4*)(row + e0);
+#pragma unroll
+        for (int i = 0; i < QPU; ++i) q[k][i] = *(const float4*)(drow + e0 + 4 * i);
+      }
+    };
+    float wu[kUnits];
+    auto compute_half = [&](const uint4 (&r)[HU], const float4 (&q)[HU][QPU], int s, int h)
+        __attribute__((always_inline)) {
+#pragma unroll
+      for (int k = 0; k < HU; ++k) {
+        float w = 0.f;
+        if (s * kStepUnits + (h * HU + k) * kThreads + tid < nunits) {
+#pragma unroll
+          for (int e = 0; e < EPU; ++e) {
+            const float4 q4 = q[k][e / 4];
+            const float qe = (e & 3) == 0 ? q4.x : (e & 3) == 1 ? q4.y : (e & 3) == 2 ? q4.z : q4.w;
+            const float p = __builtin_amdgcn_exp2f(unit_elem<LT>(r[k], e) * invTl2 - Ml2) * invS;
+            w += fmaxf(0.f, p - qe);
+          }
+        }
+        wu[h * HU + k] = w;
+      }
+    };
+    uint4 ra[HU], rb[HU];
+    float4 qa[HU][QPU], qb[HU][QPU];
+    load_half(ra, qa, 0, 0);
+    double zl = 0.0;
+    for (int s = 0; s < nsteps; ++s) {
+      load_half(rb, qb, s, 1);
+      compute_half(ra, qa, s, 0);
+      if (s + 1 < nsteps) load_half(ra, qa, s + 1, 0);
+      compute_half(rb, qb, s, 1);
+#pragma unroll
+      for (int k = 0; k < kUnits; ++k) zl += (double)wu[k];
+      const float ct = wave_chunk_totals(wu, part, lane);
+      const int c = s * kChunksPerStep + (lane / TPC) * kWaves + wave;
+      if ((lane % TPC) == 0 && c < nch) L.cw[c] = ct;
+    }
+    zl = wave_sum_d(zl);
+    if (lane == 0) L.red_d[wave] = zl;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) Zt += L.red_d[w];
+  } else {
+    // chunk weights relative to their piece -> p
+    for (int c = tid; c < nch; c += kThreads) {
+      const int piece = (c / kChunksPerStep) * kWaves + (c % kWaves);
+      L.cw[c] *= __builtin_amdgcn_exp2f(ref_l2(L.ref_m[piece], invT) - Ml2) * invS;
+    }
+    __syncthreads();
+  }
+  if (wave != 0) return;
+  // ---- the pick, on wave 0
+  uint32_t err = (uint32_t)L.err;
+  if (L.nk > kMaxChildren) err |= TAV_DEV_TOO_MANY_CHILDREN;
+  if (L.ns > 1) err |= TAV_DEV_MULTI_SAMPLED;
+  if (L.ns > 0 && !dr_ok) err |= TAV_DEV_NO_DRAFT;
+  if (no_mass || !(S > 0.0 && S < INFINITY)) err |= TAV_DEV_NONFINITE_LOGITS;
+  // children: point values for the walk; deterministic children leave the final draw
+  for (int k = lane; k < nk; k += 64) {
+    const int tk = L.kid_tok[k];
+    if (tk < 0 || tk >= V) err |= TAV_DEV_BAD_TOKEN;
+    for (int k2 = 0; k2 < k; ++k2)
+      if (L.kid_tok[k2] == tk) err |= TAV_DEV_DUP_SIBLING_TOKEN;
+    if (tk >= 0 && tk < V) {
+      const float z = logit_at<LT>(a.logits, (size_t)v * V + tk);
+      const float qz = dr_ok ? a.draft[(size_t)dr * V + tk] : 0.f;
+      const int cid = s0 + L.kid_id[k];
+      a.child_p[cid] = exp((double)(z * invT) - (double)M) / S;
+      a.child_q[cid] = use_draft ? qz : 0.f;
+      if (!L.kid_smp[k]) {
+        const float p = __builtin_amdgcn_exp2f(z * invTl2 - Ml2) * invS;
+        atomicAdd(&L.cw[tk / CT], -(use_draft ? fmaxf(0.f, p - qz) : p));
+      }
+    }
+  }
+  wave_sync();
+  // fp64 scan over chunks: lane l owns chunks [l * per, (l + 1) * per)
+  const int per = (nch + 63) / 64;
+  double pm = 0.0;
+  for (int k = 0; k < per; ++k) {
+    const int c = lane * per + k;
+    if (c < nch) pm += (double)fmaxf(L.cw[c], 0.f);
+  }
+  double incl = pm;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const double y = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += y;
+  }
+  const double W = __shfl(incl, 63);
+  const double target = (double)a.uniforms[(size_t)v * 2 + 1] * W;
+  int tok = -1;
+  if (W > 0.0) {
+    const unsigned long long hit = __ballot(pm > 0.0 && incl > target);
+    const unsigned long long has = __ballot(pm > 0.0);
+    const int owner = hit ? __ffsll((long long)hit) - 1 : 63 - __clzll((long long)has);
+    int pc = -1;
+    double rem = 0.0;
+    if (lane == owner) {
+      double cum = incl - pm, cum_l = 0.0;
+      int cl = -1;
+      for (int k = 0; k < per; ++k) {
+        const int c = lane * per + k;
+        if (c >= nch) break;
+        const double cs = (double)fmaxf(L.cw[c], 0.f);
+        if (cs > 0.0) {
+          cl = c; cum_l = cum;
+          if (pc < 0 && cum + cs > target) { pc = c; break; }
+        }
+        cum += cs;
+      }
+      if (pc < 0) { pc = cl; cum = cum_l; }   // rounding past the total: last chunk with mass
+      rem = target - cum;
+    }
+    pc = __shfl(pc, owner);
+    rem = __shfl(rem, owner);
+    // the final draw inside the chosen chunk
+    const int e0 = pc * CT + lane * EPU;
+    const bool in = e0 < V;
+    const uint4 ru = *(const uint4*)((const LT*)a.logits + (size_t)v * V + (in ? e0 : 0));
+    float qv[EPU];
+    if (use_draft) {
+#pragma unroll
+      for (int i = 0; i < EPU / 4; ++i) {
+        const float4 t = *(const float4*)(a.draft + (size_t)dr * V + (in ? e0 : 0) + 4 * i);
+        qv[4 * i + 0] = t.x; qv[4 * i + 1] = t.y; qv[4 * i + 2] = t.z; qv[4 * i + 3] = t.w;
+      }
+    }
+    float w[EPU];
+    float lsum = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPU; ++e) {
+      float x = 0.f;
+      if (in) {
+        const float p = __builtin_amdgcn_exp2f(unit_elem<LT>(ru, e) * invTl2 - Ml2) * invS;
+        x = use_draft ? fmaxf(0.f, p - qv[e]) : p;
+        for (int k = 0; k < nk; ++k)
+          if (L.kid_tok[k] == e0 + e && !L.kid_smp[k]) x = 0.f;
+      }
+      w[e] = x;
+      lsum += x;
+    }
+    float inc = lsum;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const float y = __shfl_up(inc, d, 64);
+      if (lane >= d) inc += y;
+    }
+    const float remf = (float)rem;
+    const unsigned long long hit2 = __ballot(inc > remf && lsum > 0.f);
+    const unsigned long long has2 = __ballot(lsum > 0.f);
+    const int chosen = hit2 ? __ffsll((long long)hit2) - 1 : (has2 ? 63 - __clzll((long long)has2) : -1);
+    int mine = -1;
+    if (lane == chosen) {
+      float cum = inc - lsum;
+      int lastpos = -1;
+#pragma unroll
+      for (int e = 0; e < EPU; ++e) {
+        if (w[e] > 0.f) lastpos = e0 + e;
+        cum += w[e];
+        if (mine < 0 && w[e] > 0.f && cum > remf) mine = e0 + e;
+      }
+      if (mine < 0) mine = lastpos;
+    }
+    tok = chosen >= 0 ? __shfl(mine, chosen) : -1;
+  }
+  // status bits of any lane
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) err |= (uint32_t)__shfl_xor((int)err, d);
+  if (lane == 0) {
+    a.stats[(size_t)v * 3 + 0] = M;
+    a.stats[(size_t)v * 3 + 1] = (float)S;
+    a.stats[(size_t)v * 3 + 2] = use_draft ? (float)Zt : 0.f;
+    a.term_token[v] = tok;
+    if (err) atomicOr(a.status, err);
+  }
+}
+
+// Takes nodes from the device queue until none is left.  Called by every thread of a workgroup
+// of C::kThreads threads; L is the workgroup's LDS.
+template <typename LT, class C>
+__device__ void vocab_worker(const VocabArgs& a, Lds<C>& L) {
+  for (;;) {
+    if (threadIdx.x == 0) L.item = atomicAdd(a.queue, 1);
+    __syncthreads();
+    const int v = L.item;
+    if (v >= a.N) return;
+    process_node<LT, C>(a, L, v);
+    __syncthreads();   // LDS reused by the next node
+  }
+}
+
+}  // namespace vw
+}  // namespace tav
