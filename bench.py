@@ -5,21 +5,23 @@ paged KV cache (block 16, shuffled block table), 64-node random trees of depth
 <= 8, 32 query / 8 KV heads, head_dim 128, bf16, vocabulary 151936, T = 1.0,
 seed 10086 -- the batched verification shape.  Inputs are synthetic (seeded).
 
-One step = one whole pass, one tav_tree_attn_verify call: tree preparation,
-split-KV tree attention + merge on one stream and vocabulary statistics +
-verification walk on a second stream (the two halves are independent).  With
---separate the step is tav_tree_attention and tav_tree_verify on their own
-streams and workspaces instead (which also times each half); with --one-stream
-everything runs on one stream.  Inputs are resident in HBM; two input copies
-alternate so consecutive steps do not re-read one step's data from the 256 MB
-last-level cache.
+One step = one whole pass, one tav_tree_attn_verify call: the call's start
+kernel (status reset, the verification workers' node order), tree preparation
+(with the attention work plan and node packing), split-KV tree attention and its
+merge, then the verification's vocabulary workers and the walk, all on one
+stream.  With --separate the step is tav_tree_attention and tav_tree_verify on
+their own streams and workspaces instead (which also times each half).  Inputs
+are resident in HBM; two input copies alternate so consecutive steps do not
+re-read one step's data from the 256 MB last-level cache.
 
 Prints one JSON line:  value = tree nodes scored per second (attention +
 verification), plus the step's algorithmic HBM GB/s, the roofline of the
-dominant kernel -- the attention kernel, timed per launch by HIP events the
+dominant kernel -- the vocabulary workers of the verification, the longest
+kernel of the pass and an HBM stream, timed per launch by HIP events the
 library records around it on its own stream over the timed region -- with the
-HBM traffic measured by counters for the same kernel source (or null), and the
-oracle's throughput on the same workload on one host core.
+HBM traffic measured by counters for the same kernel source (or null), the
+attention kernel's roofline from a second timed loop of attention-only calls,
+and the oracle's throughput on the same workload on one host core.
 """
 
 import argparse
@@ -33,10 +35,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
-# Counter data of the attention kernel (FETCH_SIZE / WRITE_SIZE per dispatch, scaled by a plain
-# copy of known size), valid while the kernel source is the one it was taken from.
-PMC_FILE = os.path.join(ROOT, "profiles", "pmc_attention_batched_verify.json")
-KERNEL_SOURCE = os.path.join(ROOT, "tree_masked_verification_attn_amd", "csrc", "k_attn.hip")
+# Counter data of the vocabulary workers' kernel (FETCH_SIZE / WRITE_SIZE per dispatch, scaled by a
+# plain copy of known size), valid while the kernel sources are the ones it was taken from.
+PMC_FILE = os.path.join(ROOT, "profiles", "pmc_vocab_worker_batched_verify.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "tree_masked_verification_attn_amd", "csrc", f)
+                  for f in ("vocab_worker.h", "k_verify.hip")]
 
 
 def algorithmic_bytes(w):
@@ -95,16 +98,22 @@ def cpu_baseline(w, min_seconds=10.0, max_passes=4):
                       f"node + verification walk) x {passes} passes, {dt:.1f} s"}
 
 
-def measured_traffic():
-    """HBM bytes per attention-kernel launch from the committed counter data, or None when the
-    kernel source has changed since the counters were taken."""
+def kernel_source_sha256():
     import hashlib
 
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the vocabulary workers' kernel from the committed counter data, or
+    None when the kernel sources have changed since the counters were taken."""
     if not os.path.exists(PMC_FILE):
         return None
     rec = json.load(open(PMC_FILE))
-    src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
-    if rec.get("kernel_source_sha256") != src:
+    if rec.get("kernel_source_sha256") != kernel_source_sha256():
         return None
     return int(rec["hbm_bytes_per_launch"])
 
@@ -118,13 +127,18 @@ def main():
     ap.add_argument("--workload", default="c3", choices=["c2", "c3", "c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copies", type=int, default=2)
-    ap.add_argument("--one-stream", action="store_true",
-                    help="run verification after attention on the same stream (no overlap)")
     ap.add_argument("--separate", action="store_true",
                     help="attention and verification as two calls with their own workspaces")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (counter calibration)")
+    ap.add_argument("--attn-steps", type=int, default=20,
+                    help="attention-only calls timed after the main loop (the attention kernel's roofline)")
+    ap.add_argument("--print-sha", action="store_true",
+                    help="print the SHA-256 of the vocabulary workers' sources and exit")
     args = ap.parse_args()
+    if args.print_sha:
+        print(kernel_source_sha256())
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the scoring pass has no multi-GPU path in this build "
               "(each configuration is one GPU's share); run with --gpus 1", file=sys.stderr)
@@ -150,7 +164,7 @@ def main():
     # verification's own workspaces (separate calls only)
     ws_v = [torch.zeros_like(c.workspace) for c in copies] if args.separate else [None] * len(copies)
     sa = torch.cuda.Stream()
-    sv = sa if args.one_stream else torch.cuda.Stream()
+    sv = torch.cuda.Stream()
     torch.cuda.synchronize()
 
     def step(i, ev=None):
@@ -176,7 +190,7 @@ def main():
         step(i)
     torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    tav.tav_kernel_timing(True)     # HIP events around the attention kernel, on its stream
+    tav.tav_kernel_timing(2)     # HIP events around the vocabulary workers' kernel, on its stream
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -184,7 +198,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kern_ms_total, kern_launches = tav.tav_kernel_timing_read()
-    tav.tav_kernel_timing(False)
+    tav.tav_kernel_timing(0)
     kern_ms = kern_ms_total / max(1, kern_launches)
     for c, wv in zip(copies, ws_v):
         bits = tav.tav_read_status(c.workspace) | (tav.tav_read_status(wv) if wv is not None else 0)
@@ -193,29 +207,50 @@ def main():
     attn_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
     ver_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events])) if args.separate else None
 
+    # the attention kernel alone: attention-only calls on one stream, events around the kernel
+    a_ms = None
+    if args.attn_steps > 0:
+        for i in range(2):
+            c = copies[i % len(copies)]
+            tav.tav_tree_attention(c.prob, c.tree, c.attn, c.workspace, sa)
+        torch.cuda.synchronize()
+        tav.tav_kernel_timing(1)
+        for i in range(args.attn_steps):
+            c = copies[i % len(copies)]
+            tav.tav_tree_attention(c.prob, c.tree, c.attn, c.workspace, sa)
+        torch.cuda.synchronize()
+        a_total, a_n = tav.tav_kernel_timing_read()
+        tav.tav_kernel_timing(0)
+        a_ms = a_total / max(1, a_n)
+
     ms = wall * 1e3 / args.steps
     attn_b, ver_b = algorithmic_bytes(w)
     flops = attention_flops(w)
     step_gbs = (attn_b + ver_b) / (ms * 1e-3) / 1e9
 
-    # roofline of the dominant kernel: the attention kernel (per launch = one step's attention)
-    kern_gbs = attn_b / (kern_ms * 1e-3) / 1e9
-    traffic = measured_traffic()
-    roof = {"kernel": "attn_bf16_kernel (tree-masked attention, bf16 MFMA)", "bound": "hbm",
-            "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(kern_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+    # roofline of the dominant kernel: the vocabulary workers (per launch = one step's verification)
+    kern_gbs = ver_b / (kern_ms * 1e-3) / 1e9
+    roof = {"kernel": "vocab_worker_kernel (verification: logits and draft rows streamed per node)",
+            "bound": "hbm", "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(kern_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
             "avg_launch_ms": round(kern_ms, 4), "launches_timed": kern_launches,
-            "algorithmic_bytes": attn_b,
-            "mfma_tflops": round(flops / (kern_ms * 1e-3) / 1e12, 1),
-            "mfma_frac": round(flops / (kern_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+            "algorithmic_bytes": ver_b}
+    attn_roof = None
+    if a_ms is not None:
+        a_gbs = attn_b / (a_ms * 1e-3) / 1e9
+        attn_roof = {"kernel": "attn_bf16_kernel (tree-masked attention, bf16 MFMA), attention-only calls",
+                     "bound": "hbm", "achieved": round(a_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(a_gbs / HBM_PEAK_GBS, 4), "avg_launch_ms": round(a_ms, 4),
+                     "launches_timed": args.attn_steps, "algorithmic_bytes": attn_b,
+                     "mfma_tflops": round(flops / (a_ms * 1e-3) / 1e12, 1),
+                     "mfma_frac": round(flops / (a_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
     if args.separate:
         other = {"mode": "separate calls", "attention_half_ms": round(attn_ms, 4),
                  "attention_half_gbs": round(attn_b / (attn_ms * 1e-3) / 1e9, 1),
                  "verify_half_ms": round(ver_ms, 4),
                  "verify_half_gbs": round(ver_b / (ver_ms * 1e-3) / 1e9, 1)}
     else:
-        other = {"mode": "one tav_tree_attn_verify call" + (" on one stream" if args.one_stream else ""),
-                 "pass_event_ms": round(attn_ms, 4)}
+        other = {"mode": "one tav_tree_attn_verify call", "pass_event_ms": round(attn_ms, 4)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -233,7 +268,7 @@ def main():
                    "draft_rows": int(w.draft.shape[0]) if w.draft is not None else 0},
         "step_gbs": round(step_gbs, 1), "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
         "step_algorithmic_bytes": attn_b + ver_b,
-        "roofline": roof, "kernels": other, "cpu_baseline": cpu,
+        "roofline": roof, "attention_kernel": attn_roof, "kernels": other, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 

@@ -219,12 +219,11 @@ tav_status tav_tree_verify(const tav_problem* prob, const tav_tree* tree, const 
 tav_status tav_presto_accept(const tav_presto_io* io, void* workspace, size_t workspace_bytes,
                              void* stream);
 
-/* The whole pass: tree prep and attention on attn_stream; verification (if
- * verify != NULL) on verify_stream (may equal attn_stream; it runs concurrently
- * otherwise); PreSTO (if presto != NULL) on verify_stream.  tree_out may be
- * NULL.  Returns after enqueueing; verify_stream is made to wait for the status
- * reset on attn_stream, and attn_stream is made to wait for verify_stream's
- * work before the call returns, so synchronising attn_stream covers both. */
+/* The whole pass, on attn_stream: tree prep, attention, then (if verify != NULL) the
+ * verification's vocabulary work and walk.  PreSTO (if presto != NULL) runs on verify_stream from the
+ * start when that differs from attn_stream (attn_stream then waits for it before the call returns),
+ * else on attn_stream.  tree_out may be NULL.  Returns after enqueueing; synchronising attn_stream
+ * covers the whole pass. */
 tav_status tav_tree_attn_verify(const tav_problem* prob, const tav_tree* tree,
                                 const tav_attn_io* attn, const tav_verify_io* verify,
                                 const tav_presto_io* presto, const tav_tree_out* tree_out,
@@ -234,16 +233,18 @@ tav_status tav_tree_attn_verify(const tav_problem* prob, const tav_tree* tree,
 /* Waits for stream, then copies the device status word to *status_bits. */
 tav_status tav_read_status(const void* workspace, void* stream, uint32_t* status_bits);
 
-/* Optional timing of the attention kernel, the largest kernel of the pass, for benchmarks.
- * After tav_kernel_timing(1), every bf16 tree-attention call records a pair of HIP events on
- * its attention stream immediately before and after the attention kernel launch (not around
- * the preparation, plan or merge launches).  tav_kernel_timing_read waits for the recorded
- * events, returns the summed elapsed milliseconds and the number of launches recorded since
- * the previous read or enable, and starts a new record.  tav_kernel_timing(0) stops recording
- * and releases the events.  The events belong to the device current at the first recording;
- * recording on another device returns TAV_ERR_INVALID_ARGUMENT.  Process-wide host state:
- * calls from several threads at once are not supported. */
-tav_status tav_kernel_timing(int enable);
+/* Optional timing of one kernel of the pass, for benchmarks.  tav_kernel_timing(which) with
+ * which = 1 records a pair of HIP events on the attention stream immediately before and after
+ * every bf16 tree-attention kernel launch (not around the preparation or merge launches); with
+ * which = 2 around every launch of the vocabulary workers' kernel of the verification, on the
+ * stream the verification runs on; which = 0 stops recording and releases the events.
+ * tav_kernel_timing_read waits for the recorded events, returns the summed elapsed milliseconds
+ * and the number of launches recorded since the previous read or enable, and starts a new
+ * record.  The events are timing-only (no system-scope fence when recorded).  They belong to the
+ * device current at the first recording; recording on another device returns
+ * TAV_ERR_INVALID_ARGUMENT, and so does a which outside 0..2.  Process-wide host state: calls
+ * from several threads at once are not supported. */
+tav_status tav_kernel_timing(int which);
 tav_status tav_kernel_timing_read(double* total_ms, int32_t* launches);
 
 /* Static description of a status code. */

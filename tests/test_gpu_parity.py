@@ -137,3 +137,22 @@ def test_attention_kernel_timing_events():
     ms, n = tav.tav_kernel_timing_read()
     tav.tav_kernel_timing(False)
     assert n == 3 and ms > 0.0
+
+
+@pytest.mark.parametrize("B", [300, 2100])
+def test_many_sequences(B):
+    """More sequences than one block-wide scan of the preparation covers (300), and more than the
+    work plan stages in LDS (2100): row-block offsets, node packing, chain flags and the walk of
+    every sequence."""
+    _say("many sequences", B)
+    rng = np.random.default_rng(B)
+    n = rng.integers(1, 20, size=B)
+    L = rng.integers(0, 40, size=B)
+    w = gen.tree_batch(3, B=B, prefix_len=L, tree="random", n_nodes=n, Hq=8, Hkv=2, D=64,
+                       dtype="bf16", V=512, temperature=1.0)
+    got = gu.run(w)
+    assert got["status"] == 0, got["status"]
+    gu.check_tree_prep(w, got)
+    gu.check_attention(w, got, list(range(0, w.N, 7)) + [w.N - 1])
+    gu.check_verify(w, got)
+    gu.check_node_stats(w, got, range(0, w.N, 97))

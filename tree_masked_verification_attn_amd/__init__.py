@@ -239,8 +239,9 @@ def tav_read_status(workspace: torch.Tensor, stream=None) -> int:
     return bits.value
 
 
-def tav_kernel_timing(enable: bool):
-    _check(load().tav_kernel_timing(1 if enable else 0))
+def tav_kernel_timing(which):
+    """0 / False: off; 1 / True: the attention kernel; 2: the vocabulary workers' kernel."""
+    _check(load().tav_kernel_timing(int(which)))
 
 
 def tav_kernel_timing_read():

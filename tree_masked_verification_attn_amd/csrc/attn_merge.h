@@ -1,0 +1,71 @@
+// Online-softmax merge of the pieces of attention row blocks cut between workgroups, shared by the
+// merge kernel and the verification's workers (which take merge items before their first node).
+#pragma once
+
+#include "tav_internal.h"
+
+namespace tav {
+
+// out = sum_s exp(lse_s - LSE) O_s over the pieces of row block r, KV head g, rows [row0, row0 +
+// nrows).  Row block r's key tiles [A, E) were cut into the pieces of workgroups A/C .. (E-1)/C;
+// the first piece sits in slot 2w+1 of its workgroup (its last segment), the others in slot 2w
+// (their workgroup's first segment).  A thread owns 4 outputs at a time.
+template <typename OutT>
+__device__ inline void merge_rows(const AttnArgs& a, int D, int log2G, int r, int g, int row0, int nrows) {
+  if (a.status[0] & TAV_DEV_PLAN_MISMATCH) return;
+  const int rA = a.rb_tile[r], rE = a.rb_tile[r + 1];
+  // the workgroups holding the row block's first and last tiles: the largest w with
+  // wg_tile[w] <= tile (never an empty share: the next share starts at the same tile)
+  auto owner = [&](int t) {
+    int lo = 0, hi = a.W;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.wg_tile[mid] <= t) lo = mid; else hi = mid;
+    }
+    return lo;
+  };
+  const int wf = owner(rA), wl = owner(rE - 1);
+  if (wf == wl) return;  // one workgroup held the whole row block
+  const int b = a.rb_seq[r];
+  if (b < 0 || b >= a.B) return;
+  const int s0 = a.node_offsets[b];
+  const int n = a.node_offsets[b + 1] - s0;
+  if (a.is_chain[b] == 0 && n > kMaxTreeNodes) return;  // rejected by tree preparation
+  const int NB = kRowsPerWG >> log2G;
+  const int G = 1 << log2G;
+  const int node0 = (r - a.seq_rb_off[b]) * NB;
+  const int nodes_here = min(NB, n - node0);
+  const int DQ = D / 4;
+  for (int task = threadIdx.x; task < nrows * DQ; task += blockDim.x) {
+    const int row = row0 + task / DQ, dq = task % DQ;
+    if ((row >> log2G) >= nodes_here) continue;
+    const int node = s0 + node0 + (row >> log2G);
+    const int head = g * G + (row & (G - 1));
+    float M = -INFINITY;
+    for (int w = wf; w <= wl; ++w) {
+      const int slot = w == wf ? 2 * w + 1 : 2 * w;
+      M = fmaxf(M, a.part_lse[((size_t)slot * a.Hkv + g) * kRowsPerWG + row]);
+    }
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float den = 0.f;
+    for (int w = wf; w <= wl; ++w) {
+      const int slot = w == wf ? 2 * w + 1 : 2 * w;
+      const size_t base = ((size_t)slot * a.Hkv + g) * kRowsPerWG + row;
+      const float ls = a.part_lse[base];
+      if (ls == -INFINITY) continue;
+      const float wgt = __expf(ls - M);
+      const float4 o = *(const float4*)(a.part_o + base * D + dq * 4);
+      den += wgt;
+      acc.x += wgt * o.x; acc.y += wgt * o.y; acc.z += wgt * o.z; acc.w += wgt * o.w;
+    }
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    OutT* op = (OutT*)a.out + ((size_t)node * a.Hq + head) * D + dq * 4;
+    op[0] = (OutT)(acc.x * inv);
+    op[1] = (OutT)(acc.y * inv);
+    op[2] = (OutT)(acc.z * inv);
+    op[3] = (OutT)(acc.w * inv);
+    if (dq == 0 && a.lse) a.lse[(size_t)node * a.Hq + head] = den > 0.f ? M + __logf(den) : -INFINITY;
+  }
+}
+
+}  // namespace tav

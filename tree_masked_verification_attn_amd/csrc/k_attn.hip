@@ -30,6 +30,7 @@
 // an XOR swizzle, V tiles d-major in a layout whose operand reads are free of
 // bank conflicts.  The softmax scale is folded into one FMA per score.
 #include "tav_internal.h"
+#include "attn_merge.h"
 
 namespace tav {
 namespace {
@@ -594,68 +595,11 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
   }
 }
 
-// Online-softmax merge of the pieces of a row block cut between workgroups:
-// out = sum_s exp(lse_s - LSE) O_s.  Row block r's key tiles [A, E) were cut into the pieces of
-// workgroups A/C .. (E-1)/C; the first piece sits in slot 2w+1 of its workgroup (its last
-// segment), the others in slot 2w (their workgroup's first segment).  One block per (row block,
-// KV head, group of 16 rows); a thread owns 4 outputs.
+// Online-softmax merge of the split row blocks (attn_merge.h): one block per (row block, KV head,
+// group of 16 rows).
 template <typename OutT>
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int D, int log2G) {
-  if (a.status[0] & TAV_DEV_PLAN_MISMATCH) return;
-  const int r = blockIdx.x, g = blockIdx.y;
-  const int rA = a.rb_tile[r], rE = a.rb_tile[r + 1];
-  // the workgroups holding the row block's first and last tiles: the largest w with
-  // wg_tile[w] <= tile (never an empty share: the next share starts at the same tile)
-  auto owner = [&](int t) {
-    int lo = 0, hi = a.W;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (a.wg_tile[mid] <= t) lo = mid; else hi = mid;
-    }
-    return lo;
-  };
-  const int wf = owner(rA), wl = owner(rE - 1);
-  if (wf == wl) return;  // one workgroup held the whole row block
-  const int b = a.rb_seq[r];
-  if (b < 0 || b >= a.B) return;
-  const int s0 = a.node_offsets[b];
-  const int n = a.node_offsets[b + 1] - s0;
-  if (a.is_chain[b] == 0 && n > kMaxTreeNodes) return;  // rejected by tree preparation
-  const int NB = kRowsPerWG >> log2G;
-  const int G = 1 << log2G;
-  const int node0 = (r - a.seq_rb_off[b]) * NB;
-  const int nodes_here = min(NB, n - node0);
-  const int DQ = D / 4;
-  for (int task = threadIdx.x; task < 16 * DQ; task += blockDim.x) {
-    const int row = blockIdx.z * 16 + task / DQ, dq = task % DQ;
-    if ((row >> log2G) >= nodes_here) continue;
-    const int node = s0 + node0 + (row >> log2G);
-    const int head = g * G + (row & (G - 1));
-    float M = -INFINITY;
-    for (int w = wf; w <= wl; ++w) {
-      const int slot = w == wf ? 2 * w + 1 : 2 * w;
-      M = fmaxf(M, a.part_lse[((size_t)slot * a.Hkv + g) * kRowsPerWG + row]);
-    }
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    float den = 0.f;
-    for (int w = wf; w <= wl; ++w) {
-      const int slot = w == wf ? 2 * w + 1 : 2 * w;
-      const size_t base = ((size_t)slot * a.Hkv + g) * kRowsPerWG + row;
-      const float ls = a.part_lse[base];
-      if (ls == -INFINITY) continue;
-      const float wgt = __expf(ls - M);
-      const float4 o = *(const float4*)(a.part_o + base * D + dq * 4);
-      den += wgt;
-      acc.x += wgt * o.x; acc.y += wgt * o.y; acc.z += wgt * o.z; acc.w += wgt * o.w;
-    }
-    const float inv = den > 0.f ? 1.f / den : 0.f;
-    OutT* op = (OutT*)a.out + ((size_t)node * a.Hq + head) * D + dq * 4;
-    op[0] = (OutT)(acc.x * inv);
-    op[1] = (OutT)(acc.y * inv);
-    op[2] = (OutT)(acc.z * inv);
-    op[3] = (OutT)(acc.w * inv);
-    if (dq == 0 && a.lse) a.lse[(size_t)node * a.Hq + head] = den > 0.f ? M + __logf(den) : -INFINITY;
-  }
+  merge_rows<OutT>(a, D, log2G, blockIdx.x, blockIdx.y, blockIdx.z * 16, 16);
 }
 
 __device__ inline float wave_max(float x) {
@@ -798,7 +742,7 @@ hipError_t launch_attn_f32(const Plan& p, const AttnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_merge(const Plan& p, const AttnArgs& a, bool bf16_out, hipStream_t s) {
-  if (p.W <= 1) return hipSuccess;
+  if (p.W <= 1) return hipSuccess;   // one workgroup per KV head: nothing was cut
   dim3 grid(p.total_rb, p.Hkv, kRowsPerWG / 16);
   if (bf16_out) merge_kernel<__bf16><<<grid, 256, 0, s>>>(a, p.D, p.log2G);
   else merge_kernel<float><<<grid, 256, 0, s>>>(a, p.D, p.log2G);

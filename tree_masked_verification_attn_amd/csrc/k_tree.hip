@@ -16,10 +16,6 @@ namespace {
 constexpr int kPrepThreads = 256;
 constexpr int kPlanLds = 2048;   // sequences / row blocks whose plan arrays are staged in LDS
 
-// Clears the status word and the work-queue counter of the status block.
-__global__ void clear_status_kernel(uint32_t* status) {
-  if (threadIdx.x == 0) { status[0] = 0u; status[kCounterWord] = 0u; }
-}
 
 // Exclusive scan of one int per thread over the block; also returns the total.
 __device__ int block_exclusive_scan(int v, int* lds, int* total) {
@@ -312,9 +308,37 @@ __device__ void pack_block(const AttnArgs& a, int tb, int g) {
   }
 }
 
+// The order in which the verification's workers take the nodes: nodes with a draft row (which
+// stream their draft row too, three times the bytes of the others) first, in node order, then the
+// others, so that the long items do not come last.
+__device__ void order_block(const int32_t* draft_row, int R, int N, int32_t* order) {
+  __shared__ int scan_s[16];
+  int hcarry = 0;
+  for (int base = 0; base < N; base += blockDim.x) {
+    const int v = base + threadIdx.x;
+    const int dr = v < N ? draft_row[v] : -1;
+    const int h = v < N && dr >= 0 && dr < R;
+    int tot;
+    const int ex = block_exclusive_scan(h, scan_s, &tot);
+    if (v < N) order[h ? hcarry + ex : N - 1 - (v - hcarry - ex)] = v;
+    hcarry += tot;
+  }
+}
+
+// Start of a call: clears the status word and the workers' node counter; with draft_row, builds the
+// workers' node order.
+__global__ __launch_bounds__(kPrepThreads) void start_kernel(uint32_t* status, const int32_t* draft_row, int R,
+                                                             int N, int32_t* order) {
+  if (threadIdx.x == 0) {
+    status[0] = 0u;
+    status[kCounterWord] = 0u;
+  }
+  if (draft_row) order_block(draft_row, R, N, order);
+}
+
 __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) { prep_sequence(a, blockIdx.x); }
 
-// Blocks [0, B): preparation of sequence blockIdx.x; block B: the work plan; blocks past it: one
+// Blocks [0, B): preparation of sequence blockIdx.x; block B: the work plan; the blocks after: one
 // packed node block (index % tail_blocks) of one KV head (index / tail_blocks).
 template <int D>
 __global__ __launch_bounds__(kPrepThreads) void prelude_kernel(PrepArgs pa, PlanArgs pl, AttnArgs a,
@@ -345,8 +369,8 @@ PrepArgs prep_args(const int32_t* node_offsets, const int32_t* prefix_len, const
 
 }  // namespace
 
-hipError_t launch_clear_status(uint32_t* status, hipStream_t s) {
-  clear_status_kernel<<<1, 64, 0, s>>>(status);
+hipError_t launch_start(uint32_t* status, const int32_t* draft_row, int R, int N, int32_t* order, hipStream_t s) {
+  start_kernel<<<1, kPrepThreads, 0, s>>>(status, draft_row, R, N, order);
   return hipGetLastError();
 }
 
@@ -366,8 +390,9 @@ hipError_t launch_prelude(const Plan& p, const int32_t* parent, const tav_tree_o
   pl.B = p.B; pl.NB = p.NB; pl.bs = p.bs; pl.total_rb_host = p.total_rb; pl.tiles_host = p.tiles_per_head;
   pl.tail_blocks_host = p.tail_blocks; pl.C = p.C; pl.W = p.W;
   const int grid = p.B + 1 + p.tail_blocks * p.Hkv;
-  if (p.D == 128) prelude_kernel<128><<<grid, kPrepThreads, 0, s>>>(pa, pl, a, p.tail_blocks > 0 ? p.tail_blocks : 1);
-  else prelude_kernel<64><<<grid, kPrepThreads, 0, s>>>(pa, pl, a, p.tail_blocks > 0 ? p.tail_blocks : 1);
+  const int tb = p.tail_blocks > 0 ? p.tail_blocks : 1;
+  if (p.D == 128) prelude_kernel<128><<<grid, kPrepThreads, 0, s>>>(pa, pl, a, tb);
+  else prelude_kernel<64><<<grid, kPrepThreads, 0, s>>>(pa, pl, a, tb);
   return hipGetLastError();
 }
 

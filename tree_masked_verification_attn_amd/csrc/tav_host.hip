@@ -170,6 +170,7 @@ tav_status make_plan(const tav_problem* p, const tav_presto_io* pr, Plan* out,
   P.off_child_p = o; o = align_up(o + (size_t)P.N * 8);
   P.off_child_q = o; o = align_up(o + (size_t)P.N * 4);
   P.off_presto = o; o = align_up(o + (size_t)(pr ? pr->num_requests : 0) * 8);
+  P.off_order = o; o = align_up(o + (size_t)(p->vocab > 0 ? P.N : 0) * 4);
   if (p->vocab > 0) P.nch = ceil_div(ceil_div(p->vocab, p->dtype == TAV_BF16 ? 8 : 4), 64);
   P.total = o;
   *out = P;
@@ -266,9 +267,10 @@ tav_status enqueue_prep(const tav_problem* p, const Plan& P, const tav_tree* t,
   return TAV_OK;
 }
 
-// Event pairs around the attention kernel (tav_kernel_timing).
+// Event pairs around one kernel of the pass (tav_kernel_timing): 1 = the bf16 attention kernel,
+// 2 = the vocabulary workers' kernel.  Timing-only events: no system-scope fence on record.
 struct KernelTiming {
-  bool on = false;
+  int which = 0;
   int device = -1;
   std::vector<std::pair<hipEvent_t, hipEvent_t>> pool;
   size_t used = 0;
@@ -293,8 +295,8 @@ tav_status timing_pair(hipEvent_t* start, hipEvent_t* stop) {
     return fail(TAV_ERR_INVALID_ARGUMENT, "kernel timing events belong to device %d, not %d", g_timing.device, dev);
   if (g_timing.used == g_timing.pool.size()) {
     hipEvent_t a = nullptr, b = nullptr;
-    TAV_HIP(hipEventCreate(&a));
-    if (hipEventCreate(&b) != hipSuccess) {
+    TAV_HIP(hipEventCreateWithFlags(&a, hipEventDisableSystemFence));
+    if (hipEventCreateWithFlags(&b, hipEventDisableSystemFence) != hipSuccess) {
       (void)hipEventDestroy(a);
       return fail(TAV_ERR_HIP, "hipEventCreate failed");
     }
@@ -306,20 +308,21 @@ tav_status timing_pair(hipEvent_t* start, hipEvent_t* stop) {
   return TAV_OK;
 }
 
-// Tree preparation and attention (bf16: preparation, plan and node packing in one launch).
+// Tree preparation and attention (bf16: preparation, plan and node packing in one launch, then the
+// attention kernel and the merge of split row blocks).
 tav_status enqueue_prep_attention(const tav_problem* p, const Plan& P, const tav_tree* t,
                                   const tav_tree_out* out, const tav_attn_io* io, void* ws, hipStream_t s) {
   const AttnArgs a = attn_args(p, P, io, ws);
   if (p->dtype == TAV_BF16) {
     TAV_HIP(launch_prelude(P, t->parent, out, a, s));
     hipEvent_t ev0 = nullptr, ev1 = nullptr;
-    if (g_timing.on) {
+    if (g_timing.which == 1) {
       const tav_status st = timing_pair(&ev0, &ev1);
       if (st != TAV_OK) return st;
       TAV_HIP(hipEventRecord(ev0, s));
     }
     TAV_HIP(launch_attn_bf16(P, a, s));
-    if (g_timing.on) TAV_HIP(hipEventRecord(ev1, s));
+    if (ev1) TAV_HIP(hipEventRecord(ev1, s));
     TAV_HIP(launch_merge(P, a, true, s));
   } else {
     const tav_status st = enqueue_prep(p, P, t, out, ws, s);
@@ -342,6 +345,7 @@ VocabArgs vocab_args(const tav_problem* p, const Plan& P, const tav_tree* t, con
   va.child_q = ws_at<float>(ws, P.off_child_q);
   va.B = P.B; va.N = P.N; va.V = p->vocab; va.R = io->num_draft_rows;
   va.queue = (int32_t*)(status + kCounterWord);
+  va.order = ws_at<int32_t>(ws, P.off_order);
   va.nch = P.nch;
   return va;
 }
@@ -369,14 +373,23 @@ tav_status num_compute_units(int* cus) {
   return TAV_OK;
 }
 
-// Verification: the vocabulary workers' kernel, then the walk.
+// Verification: the vocabulary workers' kernel (the node order was built by the start kernel), then
+// the walk (after wait_before, when given, on s).
 tav_status enqueue_verify(const tav_problem* p, const Plan& P, const tav_tree* t,
-                          const tav_verify_io* io, void* ws, hipStream_t s) {
+                          const tav_verify_io* io, void* ws, hipStream_t s, hipEvent_t wait_before = nullptr) {
   const VocabArgs va = vocab_args(p, P, t, io, ws);
   int cus = 0;
   tav_status st = num_compute_units(&cus);
   if (st != TAV_OK) return st;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  if (g_timing.which == 2) {
+    st = timing_pair(&ev0, &ev1);
+    if (st != TAV_OK) return st;
+    TAV_HIP(hipEventRecord(ev0, s));
+  }
   TAV_HIP(launch_vocab(va, p->dtype == TAV_BF16, cus, s));
+  if (ev1) TAV_HIP(hipEventRecord(ev1, s));
+  if (wait_before) TAV_HIP(hipStreamWaitEvent(s, wait_before, 0));
   return enqueue_walk(p, P, t, io, va, s);
 }
 
@@ -394,7 +407,8 @@ tav_status enqueue_presto(const Plan& P, const tav_presto_io* io, void* ws, hipS
   return TAV_OK;
 }
 
-// Events ordering the two streams of the whole-pass call (per host thread and device).
+// Events ordering the two streams of the whole-pass call (per host thread and device): device-scope
+// release, no timing.
 struct StreamEvents {
   int device = -1;
   hipEvent_t fork = nullptr, join = nullptr;
@@ -411,7 +425,7 @@ tav_status get_events(hipEvent_t* fork, hipEvent_t* join) {
     }
     g_events.device = -1;
     for (hipEvent_t* e : {&g_events.fork, &g_events.join})
-      TAV_HIP(hipEventCreateWithFlags(e, hipEventDisableTiming));
+      TAV_HIP(hipEventCreateWithFlags(e, hipEventDisableTiming | hipEventReleaseToDevice));
     g_events.device = dev;
   }
   *fork = g_events.fork;
@@ -443,7 +457,7 @@ tav_status tav_tree_prep(const tav_problem* prob, const tav_tree* tree, const ta
   if (st == TAV_OK) st = check_tree(tree, false);
   if (st != TAV_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  TAV_HIP(launch_clear_status(ws_at<uint32_t>(workspace, P.off_status), s));
+  TAV_HIP(launch_start(ws_at<uint32_t>(workspace, P.off_status), nullptr, 0, 0, nullptr, s));
   st = enqueue_prep(prob, P, tree, out, workspace, s);
   return st == TAV_OK ? ok() : st;
 }
@@ -457,7 +471,7 @@ tav_status tav_tree_attention(const tav_problem* prob, const tav_tree* tree, con
   if (st == TAV_OK) st = check_attn(prob, io);
   if (st != TAV_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  TAV_HIP(launch_clear_status(ws_at<uint32_t>(workspace, P.off_status), s));
+  TAV_HIP(launch_start(ws_at<uint32_t>(workspace, P.off_status), nullptr, 0, 0, nullptr, s));
   st = enqueue_prep_attention(prob, P, tree, nullptr, io, workspace, s);
   return st == TAV_OK ? ok() : st;
 }
@@ -471,7 +485,8 @@ tav_status tav_tree_verify(const tav_problem* prob, const tav_tree* tree, const 
   if (st == TAV_OK) st = check_verify(prob, io);
   if (st != TAV_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  TAV_HIP(launch_clear_status(ws_at<uint32_t>(workspace, P.off_status), s));
+  TAV_HIP(launch_start(ws_at<uint32_t>(workspace, P.off_status), io->draft_row, io->num_draft_rows, P.N,
+                       ws_at<int32_t>(workspace, P.off_order), s));
   st = enqueue_verify(prob, P, tree, io, workspace, s);
   return st == TAV_OK ? ok() : st;
 }
@@ -488,7 +503,7 @@ tav_status tav_presto_accept(const tav_presto_io* io, void* workspace, size_t wo
   st = check_ws(P, workspace, workspace_bytes);
   if (st != TAV_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  TAV_HIP(launch_clear_status(ws_at<uint32_t>(workspace, P.off_status), s));
+  TAV_HIP(launch_start(ws_at<uint32_t>(workspace, P.off_status), nullptr, 0, 0, nullptr, s));
   st = enqueue_presto(P, io, workspace, s);
   return st == TAV_OK ? ok() : st;
 }
@@ -497,7 +512,7 @@ tav_status tav_tree_attn_verify(const tav_problem* prob, const tav_tree* tree, c
                                 const tav_verify_io* verify, const tav_presto_io* presto,
                                 const tav_tree_out* tree_out, void* workspace, size_t workspace_bytes,
                                 void* attn_stream, void* verify_stream) {
-  const bool two = verify_stream != attn_stream && (verify || presto);
+  const bool two = verify_stream != attn_stream && presto;
   Plan P;
   tav_status st = make_plan(prob, presto, &P);
   if (st == TAV_OK) st = check_ws(P, workspace, workspace_bytes);
@@ -512,27 +527,26 @@ tav_status tav_tree_attn_verify(const tav_problem* prob, const tav_tree* tree, c
     st = get_events(&fork, &join);
     if (st != TAV_OK) return st;
   }
-  hipStream_t s2 = two ? sv : sa;
-  // Verification needs only the status reset.  Its workers (one per compute unit) are enqueued
-  // before the attention chain: they stream the vocabulary while the preparation kernels run, and
-  // each attention workgroup starts on a compute unit whose worker has found the queue empty.
-  TAV_HIP(launch_clear_status(ws_at<uint32_t>(workspace, P.off_status), sa));
+  // attn_stream: start, preparation, attention, merge, the verification's workers, the walk.  The
+  // attention kernel and the workers each take whole compute units, so they run one after the
+  // other.  PreSTO is independent: on verify_stream (if different) from the start.
+  TAV_HIP(launch_start(ws_at<uint32_t>(workspace, P.off_status), verify ? verify->draft_row : nullptr,
+                       verify ? verify->num_draft_rows : 0, P.N, ws_at<int32_t>(workspace, P.off_order), sa));
   if (two) {
     TAV_HIP(hipEventRecord(fork, sa));
     TAV_HIP(hipStreamWaitEvent(sv, fork, 0));
   }
-  if (presto) {   // independent of everything else; tiny
-    st = enqueue_presto(P, presto, workspace, s2);
+  if (presto) {
+    st = enqueue_presto(P, presto, workspace, two ? sv : sa);
     if (st != TAV_OK) return st;
   }
-  if (verify) {
-    st = enqueue_verify(prob, P, tree, verify, workspace, s2);
-    if (st != TAV_OK) return st;
-  }
+  if (two) TAV_HIP(hipEventRecord(join, sv));
   st = enqueue_prep_attention(prob, P, tree, tree_out, attn, workspace, sa);
   if (st != TAV_OK) return st;
-  if (two) {
-    TAV_HIP(hipEventRecord(join, sv));
+  if (verify) {
+    st = enqueue_verify(prob, P, tree, verify, workspace, sa, two ? join : nullptr);
+    if (st != TAV_OK) return st;
+  } else if (two) {
     TAV_HIP(hipStreamWaitEvent(sa, join, 0));
   }
   return ok();
@@ -545,9 +559,10 @@ tav_status tav_read_status(const void* workspace, void* stream, uint32_t* status
   return ok();
 }
 
-tav_status tav_kernel_timing(int enable) {
+tav_status tav_kernel_timing(int which) {
+  if (which < 0 || which > 2) return fail(TAV_ERR_INVALID_ARGUMENT, "tav_kernel_timing: which must be 0, 1 or 2");
   release_timing_events();
-  g_timing.on = enable != 0;
+  g_timing.which = which;
   return ok();
 }
 

@@ -16,7 +16,7 @@ constexpr int kMaskWords = 4;
 constexpr int kMaxChildren = 256;  // children of one node held by the verification kernels
 constexpr int kMaxChunks = 2048;   // chunks of 64 sixteen-byte units per vocabulary row
                                    // (V <= 1 Mi bf16 / 512 Ki f32 tokens)
-constexpr int kCounterWord = 16;   // status block: word 0 = status bits, word 16 = a work-queue counter
+constexpr int kCounterWord = 16;   // status block: word 0 = status bits, word 16 = the workers' node counter
 
 // Work decomposition of the attention pass.  A "row block" is up to
 // kRowsPerWG / G consecutive nodes of one sequence; it sees ceil(L / 64) prefix
@@ -39,7 +39,7 @@ struct Plan {
   size_t off_status = 0, off_chain = 0, off_mask = 0, off_seq_rb = 0, off_rb_seq = 0,
          off_rb_tile = 0, off_tail_blk = 0, off_wg_rb = 0, off_wg_tile = 0, off_rb_meta = 0, off_ktail = 0, off_vtail = 0, off_part_o = 0,
          off_part_lse = 0, off_stats = 0, off_term = 0, off_child_p = 0, off_child_q = 0,
-         off_presto = 0, total = 0;
+         off_presto = 0, off_order = 0, total = 0;
   int nch = 0;            // vocabulary chunks (64 sixteen-byte units) per row
 };
 
@@ -113,7 +113,8 @@ struct VocabArgs {
   double* child_p;       // [N] p of the node's token under its parent's target distribution
   float* child_q;        // [N] q~ of the node's token under its parent's draft row (0 if none)
   uint32_t* status;
-  int32_t* queue;        // node counter of the vocabulary workers (cleared with the status word)
+  int32_t* queue;        // node counter of the workers' queue (cleared with the status word)
+  const int32_t* order;  // [N] the nodes in the order the workers take them (nodes with a draft row first)
   int B, N, V, R, nch;
 };
 
@@ -161,7 +162,9 @@ struct PrestoArgs {
 
 // Kernel launchers (defined next to their kernels).  They return the HIP error
 // of the launch.
-hipError_t launch_clear_status(uint32_t* status, hipStream_t s);
+// Start of every call: status word and counters cleared; with draft_row (verification), the order
+// in which the vocabulary workers take the nodes is built into order[N].
+hipError_t launch_start(uint32_t* status, const int32_t* draft_row, int R, int N, int32_t* order, hipStream_t s);
 hipError_t launch_prep(const Plan& p, const int32_t* node_offsets, const int32_t* prefix_len,
                        const int32_t* parent, uint8_t* chain_ws, uint64_t* mask_ws,
                        const tav_tree_out* out, uint32_t* status, hipStream_t s);

@@ -24,7 +24,8 @@
 // row just read mostly hits the cache) and replaces the chunk weights with those of (p - q~)+.
 // The pick then runs on one wave: point values of the children, the deterministic children's
 // weights taken out of their chunks, an fp64 scan over the chunks for u * W, and one chunk re-read.
-// Nodes are taken from a device queue; a worker never waits for another workgroup.
+// Nodes are taken from a device queue, in the order of an index list (nodes with a draft row first,
+// so that the long items do not come last); a worker never waits for another workgroup.
 #pragma once
 
 #include "tav_internal.h"
@@ -45,7 +46,7 @@ struct Cfg {
   static constexpr int kChunksPerStep = kStepUnits / 64;
   static constexpr int kMaxSteps = kMaxChunks / kChunksPerStep;   // rows of up to kMaxChunks chunks
   static constexpr int kMaxPieces = kMaxSteps * kWaves;           // (step, wave) references
-  static_assert(NU % 2 == 0 && NT % 64 == 0, "worker shape");
+  static_assert((NU == 2 || NU % 4 == 0) && NU <= 64 && NT % 64 == 0, "worker shape");
 };
 
 template <class C>
@@ -115,10 +116,18 @@ __device__ inline float wave_chunk_totals(const float (&x)[NU], float* part, int
   wave_sync();
   const float* src = part + (lane / TPC) * 64 + (lane % TPC) * NU;
   float t = 0.f;
+  if constexpr (NU % 4 == 0) {
 #pragma unroll
-  for (int i = 0; i < NU; i += 4) {
-    const float4 a4 = *(const float4*)(src + i);
-    t += (a4.x + a4.y) + (a4.z + a4.w);
+    for (int i = 0; i < NU; i += 4) {
+      const float4 a4 = *(const float4*)(src + i);
+      t += (a4.x + a4.y) + (a4.z + a4.w);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NU; i += 2) {
+      const float2 a2 = *(const float2*)(src + i);
+      t += a2.x + a2.y;
+    }
   }
 #pragma unroll
   for (int d = 1; d < TPC; d <<= 1) t += __shfl_xor(t, d);
@@ -437,15 +446,19 @@ __device__ void process_node(const VocabArgs& a, Lds<C>& L, int v) {
   }
 }
 
-// Takes nodes from the device queue until none is left.  Called by every thread of a workgroup
-// of C::kThreads threads; L is the workgroup's LDS.
+// Takes nodes from the device queue (in the order of order[]: nodes with a draft row first) until
+// none is left.  Called by every thread of a workgroup of C::kThreads threads; L is the workgroup's
+// LDS.
 template <typename LT, class C>
 __device__ void vocab_worker(const VocabArgs& a, Lds<C>& L) {
   for (;;) {
-    if (threadIdx.x == 0) L.item = atomicAdd(a.queue, 1);
+    if (threadIdx.x == 0) {
+      const int i = atomicAdd(a.queue, 1);
+      L.item = i < a.N ? a.order[i] : -1;
+    }
     __syncthreads();
     const int v = L.item;
-    if (v >= a.N) return;
+    if (v < 0) return;
     process_node<LT, C>(a, L, v);
     __syncthreads();   // LDS reused by the next node
   }
