@@ -85,14 +85,53 @@ __device__ inline float logit_at<float>(const void* logits, size_t idx) {
   return ((const float*)logits)[idx];
 }
 
+// Cross-lane moves for wave reductions, register to register: DPP row operations within rows of 16
+// lanes (quad permutations, the 8- and 16-lane mirrors) and the lane swaps between rows.  Applied in
+// the order 1, 2, 3, 4, 5, 6 each combines groups of 2, 4, 8, 16, 32, 64 lanes; every lane of a
+// group ends with the same value.
+constexpr int kDppXor1 = 0xB1;       // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;       // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+template <int STAGE>
+__device__ inline uint32_t lane_move(uint32_t x) {
+  if constexpr (STAGE == 1) return __builtin_amdgcn_update_dpp(0, x, kDppXor1, 0xF, 0xF, false);
+  else if constexpr (STAGE == 2) return __builtin_amdgcn_update_dpp(0, x, kDppXor2, 0xF, 0xF, false);
+  else if constexpr (STAGE == 3) return __builtin_amdgcn_update_dpp(0, x, kDppHalfMirror, 0xF, 0xF, false);
+  else if constexpr (STAGE == 4) return __builtin_amdgcn_update_dpp(0, x, kDppMirror, 0xF, 0xF, false);
+  else if constexpr (STAGE == 5) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);   // the other row of 32
+    return (threadIdx.x & 16) ? r[0] : r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);   // the other half
+    return (threadIdx.x & 32) ? r[0] : r[1];
+  }
+}
+template <int STAGE>
+__device__ inline float lane_move_f(float x) { return __uint_as_float(lane_move<STAGE>(__float_as_uint(x))); }
+template <int STAGE>
+__device__ inline double lane_move_d(double x) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(x);
+  const uint32_t lo = lane_move<STAGE>((uint32_t)b), hi = lane_move<STAGE>((uint32_t)(b >> 32));
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
 __device__ inline double wave_sum_d(double x) {
-#pragma unroll
-  for (int d = 32; d > 0; d >>= 1) x += __shfl_xor(x, d);
+  x += lane_move_d<1>(x);
+  x += lane_move_d<2>(x);
+  x += lane_move_d<3>(x);
+  x += lane_move_d<4>(x);
+  x += lane_move_d<5>(x);
+  x += lane_move_d<6>(x);
   return x;
 }
 __device__ inline float wave_max_f(float x) {
-#pragma unroll
-  for (int d = 32; d > 0; d >>= 1) x = fmaxf(x, __shfl_xor(x, d));
+  x = fmaxf(x, lane_move_f<1>(x));
+  x = fmaxf(x, lane_move_f<2>(x));
+  x = fmaxf(x, lane_move_f<3>(x));
+  x = fmaxf(x, lane_move_f<4>(x));
+  x = fmaxf(x, lane_move_f<5>(x));
+  x = fmaxf(x, lane_move_f<6>(x));
   return x;
 }
 __device__ inline void wave_sync() {
@@ -129,8 +168,12 @@ __device__ inline float wave_chunk_totals(const float (&x)[NU], float* part, int
       t += a2.x + a2.y;
     }
   }
-#pragma unroll
-  for (int d = 1; d < TPC; d <<= 1) t += __shfl_xor(t, d);
+  // the TPC lanes of each chunk (aligned groups of 8, 16 or 32)
+  if constexpr (TPC >= 2) t += lane_move_f<1>(t);
+  if constexpr (TPC >= 4) t += lane_move_f<2>(t);
+  if constexpr (TPC >= 8) t += lane_move_f<3>(t);
+  if constexpr (TPC >= 16) t += lane_move_f<4>(t);
+  if constexpr (TPC >= 32) t += lane_move_f<5>(t);
   wave_sync();   // the buffer is reused by the next step
   return t;
 }
