@@ -7,7 +7,7 @@
 namespace tav {
 
 // out = sum_s exp(lse_s - LSE) O_s over the pieces of row block r, KV head g, rows [row0, row0 +
-// nrows).  Row block r's key tiles [A, E) were cut into the pieces of workgroups A/C .. (E-1)/C;
+// nrows); the pieces O_s are normalised by their own sums and stored in bf16, lse_s in float.  Row block r's key tiles [A, E) were cut into the pieces of workgroups A/C .. (E-1)/C;
 // the first piece sits in slot 2w+1 of its workgroup (its last segment), the others in slot 2w
 // (their workgroup's first segment).  A thread owns 4 outputs at a time.
 template <typename OutT>
@@ -54,9 +54,12 @@ __device__ inline void merge_rows(const AttnArgs& a, int D, int log2G, int r, in
       const float ls = a.part_lse[base];
       if (ls == -INFINITY) continue;
       const float wgt = __expf(ls - M);
-      const float4 o = *(const float4*)(a.part_o + base * D + dq * 4);
+      const uint2 ob = *(const uint2*)(a.part_o + base * D + dq * 4);   // 4 bf16
       den += wgt;
-      acc.x += wgt * o.x; acc.y += wgt * o.y; acc.z += wgt * o.z; acc.w += wgt * o.w;
+      acc.x += wgt * __uint_as_float(ob.x << 16);
+      acc.y += wgt * __uint_as_float(ob.x & 0xFFFF0000u);
+      acc.z += wgt * __uint_as_float(ob.y << 16);
+      acc.w += wgt * __uint_as_float(ob.y & 0xFFFF0000u);
     }
     const float inv = den > 0.f ? 1.f / den : 0.f;
     OutT* op = (OutT*)a.out + ((size_t)node * a.Hq + head) * D + dq * 4;

@@ -444,14 +444,17 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
     } else {
       const int slot = o_.A < j_begin ? 2 * wg : 2 * wg + 1;
       const size_t prow = ((size_t)slot * Hkv + g) * kRowsPerWG + row;
-      float* po = a.part_o + prow * D;
+      uint16_t* po = a.part_o + prow * D;
 #pragma unroll
-      for (int mb = 0; mb < DB; ++mb)
+      for (int mb = 0; mb < DB; ++mb) {
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq)
-          *(float4*)(po + mb * 32 + rq * 8 + h32 * 4) =
-              make_float4(acc[mb][rq * 4 + 0] * inv_l, acc[mb][rq * 4 + 1] * inv_l,
-                          acc[mb][rq * 4 + 2] * inv_l, acc[mb][rq * 4 + 3] * inv_l);
+        for (int rq = 0; rq < 4; ++rq) {
+          union { __bf16 e[4]; uint2 u; } o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o.e[e] = (__bf16)(acc[mb][rq * 4 + e] * inv_l);
+          *(uint2*)(po + mb * 32 + rq * 8 + h32 * 4) = o.u;
+        }
+      }
       if (h32 == 0) a.part_lse[prow] = lse_nat;
     }
     m_run = -INFINITY;

@@ -162,7 +162,7 @@ tav_status make_plan(const tav_problem* p, const tav_presto_io* pr, Plan* out,
   P.off_vtail = o;
   if (p->dtype == TAV_BF16) o = align_up(o + tail_bytes);
   P.off_part_o = o;
-  o = align_up(o + (size_t)2 * P.W * P.Hkv * kRowsPerWG * P.D * 4);
+  o = align_up(o + (size_t)2 * P.W * P.Hkv * kRowsPerWG * P.D * 2);
   P.off_part_lse = o;
   o = align_up(o + (size_t)2 * P.W * P.Hkv * kRowsPerWG * 4);
   P.off_stats = o; o = align_up(o + (size_t)P.N * 3 * 4);
@@ -248,7 +248,7 @@ AttnArgs attn_args(const tav_problem* p, const Plan& P, const tav_attn_io* io, v
   a.rb_meta = ws_at<int32_t>(ws, P.off_rb_meta);
   a.k_tail = ws_at<void>(ws, P.off_ktail);
   a.v_tail = ws_at<void>(ws, P.off_vtail);
-  a.part_o = ws_at<float>(ws, P.off_part_o);
+  a.part_o = ws_at<uint16_t>(ws, P.off_part_o);
   a.part_lse = ws_at<float>(ws, P.off_part_lse);
   a.status = ws_at<uint32_t>(ws, P.off_status);
   a.B = P.B; a.Hq = P.Hq; a.Hkv = P.Hkv; a.total_rb = P.total_rb;

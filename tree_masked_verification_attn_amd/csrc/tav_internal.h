@@ -91,7 +91,7 @@ struct AttnArgs {
   const int32_t* rb_meta;     // [total_rb, kMetaWords] per row block, fields RbMeta
   void* k_tail;               // [tail_blocks, Hkv, bs, D] node keys in the cache layout
   void* v_tail;               // [tail_blocks, Hkv, D, bs] node values in the cache layout
-  float* part_o;              // [2W, Hkv, 256, D] partial outputs of cut row blocks
+  uint16_t* part_o;           // [2W, Hkv, 256, D] partial outputs of cut row blocks (bf16)
   float* part_lse;            // [2W, Hkv, 256]
   uint32_t* status;
   int B, Hq, Hkv, total_rb, tiles_per_head, C, W, tail_blocks, block_size, num_blocks, max_blocks;
