@@ -36,30 +36,52 @@ __device__ inline void merge_rows(const AttnArgs& a, int D, int log2G, int r, in
   const int node0 = (r - a.seq_rb_off[b]) * NB;
   const int nodes_here = min(NB, n - node0);
   const int DQ = D / 4;
+  constexpr int kPre = 4;   // pieces whose loads are all issued before any is used
+  const int np = wl - wf + 1;
   for (int task = threadIdx.x; task < nrows * DQ; task += blockDim.x) {
     const int row = row0 + task / DQ, dq = task % DQ;
     if ((row >> log2G) >= nodes_here) continue;
     const int node = s0 + node0 + (row >> log2G);
     const int head = g * G + (row & (G - 1));
     float M = -INFINITY;
-    for (int w = wf; w <= wl; ++w) {
-      const int slot = w == wf ? 2 * w + 1 : 2 * w;
-      M = fmaxf(M, a.part_lse[((size_t)slot * a.Hkv + g) * kRowsPerWG + row]);
-    }
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float den = 0.f;
-    for (int w = wf; w <= wl; ++w) {
-      const int slot = w == wf ? 2 * w + 1 : 2 * w;
-      const size_t base = ((size_t)slot * a.Hkv + g) * kRowsPerWG + row;
-      const float ls = a.part_lse[base];
-      if (ls == -INFINITY) continue;
+    auto add_piece = [&](float ls, uint2 ob) {
+      if (ls == -INFINITY) return;
       const float wgt = __expf(ls - M);
-      const uint2 ob = *(const uint2*)(a.part_o + base * D + dq * 4);   // 4 bf16
       den += wgt;
       acc.x += wgt * __uint_as_float(ob.x << 16);
       acc.y += wgt * __uint_as_float(ob.x & 0xFFFF0000u);
       acc.z += wgt * __uint_as_float(ob.y << 16);
       acc.w += wgt * __uint_as_float(ob.y & 0xFFFF0000u);
+    };
+    auto base_of = [&](int w) {
+      const int slot = w == wf ? 2 * w + 1 : 2 * w;
+      return ((size_t)slot * a.Hkv + g) * kRowsPerWG + row;
+    };
+    if (np <= kPre) {
+      float ls[kPre];
+      uint2 ob[kPre];
+#pragma unroll
+      for (int i = 0; i < kPre; ++i) {
+        ls[i] = -INFINITY;
+        ob[i] = make_uint2(0u, 0u);
+        if (i < np) {
+          const size_t base = base_of(wf + i);
+          ls[i] = a.part_lse[base];
+          ob[i] = *(const uint2*)(a.part_o + base * D + dq * 4);   // 4 bf16
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kPre; ++i) M = fmaxf(M, ls[i]);
+#pragma unroll
+      for (int i = 0; i < kPre; ++i) add_piece(ls[i], ob[i]);
+    } else {
+      for (int w = wf; w <= wl; ++w) M = fmaxf(M, a.part_lse[base_of(w)]);
+      for (int w = wf; w <= wl; ++w) {
+        const size_t base = base_of(w);
+        add_piece(a.part_lse[base], *(const uint2*)(a.part_o + base * D + dq * 4));
+      }
     }
     const float inv = den > 0.f ? 1.f / den : 0.f;
     OutT* op = (OutT*)a.out + ((size_t)node * a.Hq + head) * D + dq * 4;
