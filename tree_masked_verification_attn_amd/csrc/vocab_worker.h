@@ -333,14 +333,15 @@ __device__ void process_node(const VocabArgs& a, Lds<C>& L, int v) {
         wu[h * HU + k] = w;
       }
     };
+    // the steps in reverse: the last steps of pass 1 are the likeliest still to be in the cache
     uint4 ra[HU], rb[HU];
     float4 qa[HU][QPU], qb[HU][QPU];
-    load_half(ra, qa, 0, 0);
+    load_half(ra, qa, nsteps - 1, 0);
     double zl = 0.0;
-    for (int s = 0; s < nsteps; ++s) {
+    for (int s = nsteps - 1; s >= 0; --s) {
       load_half(rb, qb, s, 1);
       compute_half(ra, qa, s, 0);
-      if (s + 1 < nsteps) load_half(ra, qa, s + 1, 0);
+      if (s > 0) load_half(ra, qa, s - 1, 0);
       compute_half(rb, qb, s, 1);
 #pragma unroll
       for (int k = 0; k < kUnits; ++k) zl += (double)wu[k];
