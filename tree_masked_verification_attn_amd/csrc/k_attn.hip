@@ -36,6 +36,7 @@ namespace tav {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -77,8 +78,8 @@ __device__ inline void wait_vm() {
 // consecutive keys and the V^T operand is one 16-byte read.
 __device__ inline int sigma(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
-constexpr int kStages = 4;            // ring stages in LDS (3 in flight while one is used)
-constexpr float kRescaleSlack = 8.f;  // keep a stale max while the tile max exceeds it by <= 2^8
+constexpr int kStages = 5;            // ring stages in LDS (2 in use, 3 in flight)
+constexpr float kSumLimit = 65536.f;  // keep a stale max while every probability stays <= 2^16
 
 // Stored 16-byte position of chunk c of key row k in a K tile (bank spreading
 // for the MFMA operand reads: rows are 256 B for D = 128 and 128 B for D = 64).
@@ -223,7 +224,7 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
     }
     const uint16_t* rk = (nref.tail ? ktl : kc) + (((size_t)blk * Hkv + g) * bs + nref.slot0) * D;
     const uint16_t* rv = (nref.tail ? vtl : vc) + ((size_t)blk * Hkv + g) * D * bs + nref.slot0;
-    uint8_t* kbase = lds[(j - j_begin) & (kStages - 1)];
+    uint8_t* kbase = lds[(unsigned)(j - j_begin) % kStages];
     uint8_t* vbase = kbase + TILE_BYTES + sb * SUB_BYTES;
 #pragma unroll
     for (int i = 0; i < DMA_PER_OPERAND; ++i) {
@@ -325,40 +326,6 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
     for (int ks = 0; ks < KS; ++ks) {
       const bf16x8_t ka = *(const bf16x8_t*)(kbase + key * (D * 2) + kpos<D>(ks * 2 + h32, key) * 16);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], ks == 0 ? zero : s, 0, 0, 0);
-    }
-  };
-
-  // Online-softmax update with one half's scores, cut into pieces for interleaving with
-  // MFMAs: piece 0 the row maximum, piece 1 the running-max bookkeeping, pieces 2.. the
-  // exponentials (ceil(16 / nexp) per piece) into P (bf16, two MFMA operands).  The running max is
-  // kept until some row's max exceeds it by 2^8 (a wave-uniform decision), so the accumulator
-  // rescale (by alpha) is rare.  State between pieces lives in SoftmaxState.
-  struct SoftmaxState { float mx, mu, alpha, ps; bool need; };
-  auto softmax_piece = [&](int piece, int nexp, const f32x16_t& s, bf16x8_t (&pb)[2],
-                           SoftmaxState& z) __attribute__((always_inline)) {
-    if (piece == 0) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
-      z.mx = mx;
-    } else if (piece == 1) {
-      const float mx = max_halves(z.mx) * c2;
-      z.need = __ballot(mx > m_run + kRescaleSlack) != 0ull;
-      const float m_new = z.need ? fmaxf(m_run, mx) : m_run;
-      z.alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
-      m_run = m_new;
-      z.mu = m_new == -INFINITY ? 0.f : m_new;
-      z.ps = 0.f;
-    } else {
-      const int per = (16 + nexp - 1) / nexp;   // the last piece may hold fewer
-      const int r0 = (piece - 2) * per;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (r < r0 || r >= r0 + per) continue;
-        const float p = fast_exp2(fmaf(s[r], c2, -z.mu));
-        z.ps += p;
-        pb[r >> 3][r & 7] = (__bf16)p;
-      }
     }
   };
 
@@ -465,10 +432,11 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
       for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
   };
 
-  // ---- prologue: the first kStages - 1 tiles in flight, the first segment
+  // ---- prologue: the first kStages - 2 tiles in flight, the first segment
+  const int n = j_end - j_begin;   // tiles of this workgroup
   int next_issue = j_begin;
   resolve();
-  for (int k = 0; k < kStages - 1 && next_issue < j_end; ++k) {
+  for (int k = 0; k < kStages - 2 && next_issue < j_end; ++k) {
     issue(next_issue);
     ++next_issue;
     if (next_issue < j_end) resolve();
@@ -476,34 +444,72 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
   start_segment(r_first);
   int landed = next_issue - 1;   // tiles whose copies are known to have landed (this wave's)
 
-  for (int j = j_begin; j < j_end; ++j) {
-    // tile j landed for every wave, and the ring slot of tile j-1 is free.  Past a segment
-    // start every copy issued before it has landed; later tiles wait by count (the output
-    // stores of the finished segment, issued in between, are older than their copies).
-    const int after = next_issue - 1 - j;   // tiles issued after tile j
-    asm volatile("" ::: "memory");
-    if (j > landed) {
-      if (after >= 2) wait_vm<2 * DMA_PER_TILE>();
-      else if (after == 1) wait_vm<DMA_PER_TILE>();
-      else wait_vm<0>();
+  f32x16_t s0, s1;   // scores of the tile between its M and V phases (keys 0..31, 32..63)
+  bf16x8_t pp[4];    // probabilities of the tile between its V phase and the next M phase,
+                     // one MFMA operand per 16-key sub-block
+
+  // M phase of tile k: P V of tile k-1 (then the segment's output if tile k-1 ended it), then
+  // the scores S^T = K Q^T of tile k.  Only MFMAs and their operand reads from LDS: one stream
+  // of operands (values of tile k-1, then keys of tile k) read PF ahead of the MFMAs (the order
+  // is fixed by scheduling barriers).
+  constexpr int PF = 3;
+  constexpr int NPV = 4 * DB;   // P V MFMAs of a tile
+  constexpr int NS = 2 * KS;    // score MFMAs of a tile (the two key halves interleaved)
+  auto m_phase = [&](int k) __attribute__((always_inline)) {
+    if (k >= 1) {
+      const int st = (unsigned)(k - 1) % kStages;
+      bf16x8_t op[PF];
+#pragma unroll
+      for (int f = 0; f < PF; ++f) op[f] = vread(st, f / DB, f % DB);
+#pragma unroll
+      for (int i = 0; i < NPV; ++i) {
+        acc[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % PF], pp[i / DB], acc[i % DB], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + PF < NPV) op[i % PF] = vread(st, (i + PF) / DB, (i + PF) % DB);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const int j = j_begin + k - 1;
+      if (j + 1 == min(seg_E, j_end)) {
+        const OutRow orow{seg_A, seg_E, seg_s0, rnode, rvalid && seg_ok};
+        if (j + 1 < j_end) {
+          start_segment(seg_r + 1);
+          landed = next_issue - 1;
+        }
+        finish_segment(orow);
+      }
     }
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (next_issue < j_end) {
-      issue(next_issue);
-      ++next_issue;
-      if (next_issue < j_end) resolve();
+    if (k < n) {
+      const int st = (unsigned)k % kStages;
+      bf16x8_t op[PF];
+#pragma unroll
+      for (int f = 0; f < PF; ++f) op[f] = kread(st, f & 1, f >> 1);
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        const int ks = i >> 1;
+        if (i & 1) s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % PF], qreg[ks], ks == 0 ? f32x16_t{} : s1, 0, 0, 0);
+        else s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % PF], qreg[ks], ks == 0 ? f32x16_t{} : s0, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + PF < NS) op[i % PF] = kread(st, (i + PF) & 1, (i + PF) >> 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      s0 = f32x16_t{};
+      s1 = f32x16_t{};
     }
-    const int st = (j - j_begin) & (kStages - 1);
-    const int t = j - seg_A;
+  };
+
+  // V phase of tile k: masking, one online-softmax update with all 64 keys, probabilities into
+  // pp.  In the partial last prefix tile the first group also zeroes the values of keys past the
+  // prefix (cache slots past it may hold anything, and 0 * NaN would reach the output); nobody
+  // reads them before the next barrier.
+  auto v_phase = [&](int k) __attribute__((always_inline)) {
+    const int t = j_begin + k - seg_A;
     const bool masked = needs_mask(t);
-    if (masked && t < seg_Tp) {
-      // the partial last prefix tile: zero the values of keys past the prefix (cache slots
-      // past it may hold anything, and 0 * NaN would reach the output); 16-byte units of V^T
-      // are [sub-block][32-d group][key half][32 d] of 8 keys each
+    if (masked && t < seg_Tp && tid < 256) {
+      // 16-byte units of V^T are [sub-block][32-d group][key half][32 d] of 8 keys each
       const int lim = seg_L - t * kTileKeys;
-      uint8_t* vbase = lds[st] + TILE_BYTES;
-      for (int u = tid; u < 4 * (D / 32) * 2 * 32; u += 512) {
+      uint8_t* vbase = lds[(unsigned)k % kStages] + TILE_BYTES;
+      for (int u = tid; u < 4 * (D / 32) * 2 * 32; u += 256) {
         const int k0 = (u / ((D / 32) * 64)) * 16 + ((u >> 5) & 1) * 8;   // first key of the unit
         if (k0 + 8 <= lim) continue;
         uint4* p = (uint4*)(vbase + u * 16);
@@ -515,85 +521,99 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
         v.w &= (6 < x ? 0xFFFFu : 0u) | (7 < x ? 0xFFFF0000u : 0u);
         *p = v;
       }
-      __syncthreads();
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
-    // Four windows, each a chain of MFMAs with vector work between them (the order is fixed
-    // by scheduling barriers; operand reads run two MFMAs ahead):
-    //   A: scores of keys 0..31;  B: scores of keys 32..63 + softmax of keys 0..31;
-    //   C: P V of keys 0..31 + softmax of keys 32..63;  D: P V of keys 32..63.
-    constexpr int NPV = 2 * DB;          // P V MFMAs per half
-    constexpr int NEXP_B = KS - 2;       // exponential pieces in window B
-    constexpr int NEXP_C = NPV - 2;      // and in window C
-    f32x16_t s0, s1;
-    bf16x8_t p0[2], p1[2];
-    SoftmaxState z0, z1;
-    bf16x8_t opa = kread(st, 0, 0), opb = kread(st, 0, 1);
-    // A
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa, qreg[ks], ks == 0 ? f32x16_t{} : s0, 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      const bf16x8_t nxt = ks + 2 < KS ? kread(st, 0, ks + 2) : kread(st, 1, ks + 2 - KS);
-      __builtin_amdgcn_sched_barrier(0);
-      opa = opb;
-      opb = nxt;
+    if (masked) {
+      mask(t, 0, s0);
+      mask(t, 1, s1);
     }
-    if (masked) mask(t, 0, s0);
-    // B
+    // Exponentials against the running max (in log2 units), packed to bf16; the row sum is
+    // taken over the packed values (the weights the P V products use).  While every lane's sum
+    // stays within 2^16 no probability exceeds 2^16 and the running max stands; otherwise (and
+    // at a segment's first tile, whose running max is -inf) the row max is taken and the
+    // exponentials are redone against it, with the accumulator rescaled.
+    const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
+    auto exps = [&](float mu) __attribute__((always_inline)) -> float {
+      Bf16Pack8 q[4];   // built whole here, so the registers of the previous tile's pp are free
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa, qreg[ks], ks == 0 ? f32x16_t{} : s1, 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      const bf16x8_t nxt = ks + 2 < KS ? kread(st, 1, ks + 2) : vread(st, (ks + 2 - KS) / DB, (ks + 2 - KS) % DB);
-      __builtin_amdgcn_sched_barrier(0);
-      if (ks >= 1) softmax_piece(ks - 1, NEXP_B, s0, p0, z0);
-      __builtin_amdgcn_sched_barrier(0);
-      opa = opb;
-      opb = nxt;
-    }
-#pragma unroll
-    for (int piece = KS - 1; piece < NEXP_B + 2; ++piece) softmax_piece(piece, NEXP_B, s0, p0, z0);
-    l_run = l_run * z0.alpha + z0.ps;
-    // The branch also tests ps (always >= 0, so the test adds nothing; a NaN would only rescale
-    // by alpha = 1): that keeps the exponentials in window B instead of being moved past it.
-    if (z0.need || !(z0.ps >= 0.f)) rescale(z0.alpha);
-    if (masked) mask(t, 1, s1);
-    // C
-#pragma unroll
-    for (int i = 0; i < NPV; ++i) {
-      const int ni = i + 2;
-      acc[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa, p0[i / DB], acc[i % DB], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      const bf16x8_t nxt = ni < NPV ? vread(st, ni / DB, ni % DB) : vread(st, 2 + (ni - NPV) / DB, (ni - NPV) % DB);
-      __builtin_amdgcn_sched_barrier(0);
-      if (i >= 1) softmax_piece(i - 1, NEXP_C, s1, p1, z1);
-      __builtin_amdgcn_sched_barrier(0);
-      opa = opb;
-      opb = nxt;
-    }
-#pragma unroll
-    for (int piece = NPV - 1; piece < NEXP_C + 2; ++piece) softmax_piece(piece, NEXP_C, s1, p1, z1);
-    l_run = l_run * z1.alpha + z1.ps;
-    if (z1.need || !(z1.ps >= 0.f)) rescale(z1.alpha);
-    // D
-#pragma unroll
-    for (int i = 0; i < NPV; ++i) {
-      const int ni = i + 2;
-      acc[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa, p1[i / DB], acc[i % DB], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      const bf16x8_t nxt = ni < NPV ? vread(st, 2 + ni / DB, ni % DB) : opb;
-      __builtin_amdgcn_sched_barrier(0);
-      opa = opb;
-      opb = nxt;
-    }
-    if (j + 1 == min(seg_E, j_end)) {
-      // the next segment's query first: its wait then does not cover the output stores
-      const OutRow orow{seg_A, seg_E, seg_s0, rnode, rvalid && seg_ok};
-      if (j + 1 < j_end) {
-        start_segment(seg_r + 1);
-        landed = next_issue - 1;
+      for (int r = 0; r < 16; ++r) {
+        q[r >> 3].e[r & 7] = (__bf16)fast_exp2(fmaf(s0[r], c2, -mu));
+        q[2 + (r >> 3)].e[r & 7] = (__bf16)fast_exp2(fmaf(s1[r], c2, -mu));
       }
-      finish_segment(orow);
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pp[i] = q[i].v;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) ps = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{pp[i][2 * h], pp[i][2 * h + 1]}, ones, ps, false);
+      }
+      return ps;
+    };
+    float ps = exps(m_run == -INFINITY ? 0.f : m_run);
+    if (__ballot(!(ps <= kSumLimit) || m_run == -INFINITY) != 0ull) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+      const float m_new = fmaxf(m_run, max_halves(mx) * c2);
+      const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
+      m_run = m_new;
+      ps = exps(m_new == -INFINITY ? 0.f : m_new);
+      l_run *= alpha;
+      rescale(alpha);
+    }
+    l_run += ps;
+  };
+
+  // Ping-pong: a wave takes the phases M(0) V(0) M(1) V(1) ... V(n-1) M(n), one per interval
+  // between workgroup barriers, and the second group of waves (4..7; wave w runs on SIMD w % 4)
+  // runs one interval behind the first, so on every SIMD one wave feeds the matrix cores while
+  // the other does the softmax.  Tile m is read in intervals 2m .. 2m+3 (its keys by the two
+  // groups in 2m and 2m+1, its values in 2m+2 and 2m+3): before the barrier that opens interval
+  // 2m every wave waits for its copies of tile m, and after it issues tile m+3 into the slot of
+  // tile m-2, which nobody reads any more.
+  auto open_pair = [&](int m) __attribute__((always_inline)) {   // the barrier opening interval 2m
+    const int need = j_begin + m;
+    asm volatile("" ::: "memory");
+    if (need < j_end && need > landed) {
+      // Past a segment start every copy issued before it has landed; later tiles wait by count
+      // (the output stores of the finished segment, issued in between, are older than their
+      // copies).
+      const int after = next_issue - 1 - need;   // tiles issued after the one needed
+      if (after >= 2) wait_vm<2 * DMA_PER_TILE>();
+      else if (after == 1) wait_vm<DMA_PER_TILE>();
+      else wait_vm<0>();
+    }
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (next_issue < j_end) {
+      issue(next_issue);
+      ++next_issue;
+      if (next_issue < j_end) resolve();
+    }
+  };
+  auto mid_pair = [&]() __attribute__((always_inline)) {   // the barrier opening interval 2m+1
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  // (each group as its own straight loop: the phases follow each other in a fixed order)
+  if (wave < 4) {
+    for (int m = 0; m <= n; ++m) {
+      open_pair(m);
+      __builtin_amdgcn_s_setprio(1);
+      m_phase(m);
+      __builtin_amdgcn_s_setprio(0);
+      mid_pair();
+      if (m < n) v_phase(m);
+    }
+  } else {
+    for (int m = 0; m <= n; ++m) {
+      open_pair(m);
+      if (m >= 1) v_phase(m - 1);
+      mid_pair();
+      __builtin_amdgcn_s_setprio(1);
+      m_phase(m);
+      __builtin_amdgcn_s_setprio(0);
     }
   }
 }
