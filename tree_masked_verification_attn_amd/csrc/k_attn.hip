@@ -36,7 +36,6 @@ namespace tav {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -527,26 +526,23 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
       mask(t, 0, s0);
       mask(t, 1, s1);
     }
-    // Exponentials against the running max (in log2 units), packed to bf16; the row sum is
-    // taken over the packed values (the weights the P V products use).  While every lane's sum
+    // Exponentials against the running max (in log2 units), summed in float and packed to bf16
+    // (a bf16 dot product would share the matrix cores with the other wave).  While every lane's sum
     // stays within 2^16 no probability exceeds 2^16 and the running max stands; otherwise (and
     // at a segment's first tile, whose running max is -inf) the row max is taken and the
     // exponentials are redone against it, with the accumulator rescaled.
-    const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
     auto exps = [&](float mu) __attribute__((always_inline)) -> float {
       Bf16Pack8 q[4];   // built whole here, so the registers of the previous tile's pp are free
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        q[r >> 3].e[r & 7] = (__bf16)fast_exp2(fmaf(s0[r], c2, -mu));
-        q[2 + (r >> 3)].e[r & 7] = (__bf16)fast_exp2(fmaf(s1[r], c2, -mu));
-      }
       float ps = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pp[i] = q[i].v;
-#pragma unroll
-        for (int h = 0; h < 4; ++h) ps = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{pp[i][2 * h], pp[i][2 * h + 1]}, ones, ps, false);
+      for (int r = 0; r < 16; ++r) {
+        const float e0 = fast_exp2(fmaf(s0[r], c2, -mu)), e1 = fast_exp2(fmaf(s1[r], c2, -mu));
+        ps += e0 + e1;
+        q[r >> 3].e[r & 7] = (__bf16)e0;
+        q[2 + (r >> 3)].e[r & 7] = (__bf16)e1;
       }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pp[i] = q[i].v;
       return ps;
     };
     float ps = exps(m_run == -INFINITY ? 0.f : m_run);
