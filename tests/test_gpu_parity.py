@@ -112,6 +112,20 @@ def test_split_kv_long_prefix(seed):
 
 
 @pytest.mark.parametrize("seed", SEEDS)
+def test_sharp_softmax(seed):
+    """Queries scaled by 24 (score std about 35 in log2 units): a row's running maximum keeps
+    rising by more than the kernel's slack from tile to tile inside one segment, so the rescale
+    path runs mid-segment, not only at a segment's first tile."""
+    _say("sharp softmax", seed)
+    w = gen.tree_batch(seed, B=2, prefix_len=[5000, 700], tree="random", n_nodes=[40, 12],
+                       Hq=8, Hkv=2, D=128, dtype="bf16")
+    w.q = gen.f32_to_bf16_bits(gen.bf16_bits_to_f32(w.q) * 24.0)
+    got = gu.run(w, with_verify=False)
+    assert got["status"] == 0, got["status"]
+    gu.check_attention(w, got)
+
+
+@pytest.mark.parametrize("seed", SEEDS)
 def test_presto_small(seed):
     _say("presto", seed)
     w = gen.presto_batch(seed, T=96, n_pf=12, Hq=8, Hkv=2, D=128, dtype="bf16", alpha=4.0,
