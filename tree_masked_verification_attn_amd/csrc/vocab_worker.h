@@ -46,6 +46,9 @@ struct Cfg {
   static constexpr int kChunksPerStep = kStepUnits / 64;
   static constexpr int kMaxSteps = kMaxChunks / kChunksPerStep;   // rows of up to kMaxChunks chunks
   static constexpr int kMaxPieces = kMaxSteps * kWaves;           // (step, wave) references
+  // the first steps of a logits row kept in LDS for the second pass (nodes with a draft row)
+  static constexpr int kCacheSteps = (128 * 1024) / (kStepUnits * 16);
+  static constexpr int kCacheUnits = kCacheSteps * kStepUnits;
   static_assert((NU == 2 || NU % 4 == 0) && NU <= 64 && NT % 64 == 0, "worker shape");
 };
 
@@ -60,6 +63,7 @@ struct Lds {
   int kid_tok[kMaxChildren];                 // ... their tokens
   uint8_t kid_smp[kMaxChildren];             // ... and sampled flags
   int item, cnt, nk, ns, err;
+  uint4 lc[C::kCacheUnits];                  // the row's first kCacheSteps steps (each thread its own units)
 };
 
 template <typename LT>
@@ -268,6 +272,11 @@ __device__ void process_node(const VocabArgs& a, Lds<C>& L, int v) {
       }
       sd += (double)su[k];
     }
+    if (dr_ok && s < C::kCacheSteps) {
+      // kept for the second pass, which reads them back in the same thread
+#pragma unroll
+      for (int k = 0; k < kUnits; ++k) L.lc[s * kStepUnits + k * kThreads + tid] = cur[k];
+    }
     const float ct = wave_chunk_totals(su, part, lane);
     const int c = s * kChunksPerStep + (lane / TPC) * kWaves + wave;
     if ((lane % TPC) == 0 && c < nch) L.cw[c] = ct;
@@ -310,7 +319,7 @@ __device__ void process_node(const VocabArgs& a, Lds<C>& L, int v) {
       for (int k = 0; k < HU; ++k) {
         const int u = s * kStepUnits + (h * HU + k) * kThreads + tid;
         const size_t e0 = (size_t)(u < nunits ? u : 0) * EPU;
-        r[k] = *(const uint4*)(row + e0);
+        r[k] = s < C::kCacheSteps ? L.lc[u] : *(const uint4*)(row + e0);
 #pragma unroll
         for (int i = 0; i < QPU; ++i) q[k][i] = *(const float4*)(drow + e0 + 4 * i);
       }
