@@ -338,16 +338,19 @@ __global__ __launch_bounds__(kPrepThreads) void start_kernel(uint32_t* status, c
 
 __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) { prep_sequence(a, blockIdx.x); }
 
-// Blocks [0, B): preparation of sequence blockIdx.x; block B: the work plan; the blocks after: one
-// packed node block (index % tail_blocks) of one KV head (index / tail_blocks).
+// Blocks [0, B): preparation of sequence blockIdx.x; block B: the work plan; with an order to
+// build, the last block: the verification workers' node order; the blocks between: one packed node
+// block (index % tail_blocks) of one KV head (index / tail_blocks).
 template <int D>
 __global__ __launch_bounds__(kPrepThreads) void prelude_kernel(PrepArgs pa, PlanArgs pl, AttnArgs a,
-                                                               int tail_blocks) {
+                                                               int tail_blocks, OrderArgs o) {
   const int bid = blockIdx.x;
   if (bid < pl.B) {
     prep_sequence(pa, bid);
   } else if (bid == pl.B) {
     plan_block(pl, a);
+  } else if (o.order && bid == (int)gridDim.x - 1) {
+    order_block(o.draft_row, o.R, o.N, o.order);
   } else {
     const int i = bid - pl.B - 1;
     pack_block<D>(a, i % tail_blocks, i / tail_blocks);
@@ -383,16 +386,16 @@ hipError_t launch_prep(const Plan& p, const int32_t* node_offsets, const int32_t
 }
 
 hipError_t launch_prelude(const Plan& p, const int32_t* parent, const tav_tree_out* out, const AttnArgs& a,
-                          hipStream_t s) {
+                          const OrderArgs& o, hipStream_t s) {
   const PrepArgs pa = prep_args(a.node_offsets, a.prefix_len, parent, const_cast<uint8_t*>(a.is_chain),
                                 const_cast<uint64_t*>(a.mask), out, a.status);
   PlanArgs pl;
   pl.B = p.B; pl.NB = p.NB; pl.bs = p.bs; pl.total_rb_host = p.total_rb; pl.tiles_host = p.tiles_per_head;
   pl.tail_blocks_host = p.tail_blocks; pl.C = p.C; pl.W = p.W;
-  const int grid = p.B + 1 + p.tail_blocks * p.Hkv;
+  const int grid = p.B + 1 + p.tail_blocks * p.Hkv + (o.order ? 1 : 0);
   const int tb = p.tail_blocks > 0 ? p.tail_blocks : 1;
-  if (p.D == 128) prelude_kernel<128><<<grid, kPrepThreads, 0, s>>>(pa, pl, a, tb);
-  else prelude_kernel<64><<<grid, kPrepThreads, 0, s>>>(pa, pl, a, tb);
+  if (p.D == 128) prelude_kernel<128><<<grid, kPrepThreads, 0, s>>>(pa, pl, a, tb, o);
+  else prelude_kernel<64><<<grid, kPrepThreads, 0, s>>>(pa, pl, a, tb, o);
   return hipGetLastError();
 }
 

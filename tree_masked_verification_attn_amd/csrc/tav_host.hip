@@ -311,10 +311,11 @@ tav_status timing_pair(hipEvent_t* start, hipEvent_t* stop) {
 // Tree preparation and attention (bf16: preparation, plan and node packing in one launch, then the
 // attention kernel and the merge of split row blocks).
 tav_status enqueue_prep_attention(const tav_problem* p, const Plan& P, const tav_tree* t,
-                                  const tav_tree_out* out, const tav_attn_io* io, void* ws, hipStream_t s) {
+                                  const tav_tree_out* out, const tav_attn_io* io, void* ws, hipStream_t s,
+                                  const OrderArgs& order = OrderArgs{nullptr, 0, 0, nullptr}) {
   const AttnArgs a = attn_args(p, P, io, ws);
   if (p->dtype == TAV_BF16) {
-    TAV_HIP(launch_prelude(P, t->parent, out, a, s));
+    TAV_HIP(launch_prelude(P, t->parent, out, a, order, s));
     hipEvent_t ev0 = nullptr, ev1 = nullptr;
     if (g_timing.which == 1) {
       const tav_status st = timing_pair(&ev0, &ev1);
@@ -530,8 +531,12 @@ tav_status tav_tree_attn_verify(const tav_problem* prob, const tav_tree* tree, c
   // attn_stream: start, preparation, attention, merge, the verification's workers, the walk.  The
   // attention kernel and the workers each take whole compute units, so they run one after the
   // other.  PreSTO is independent: on verify_stream (if different) from the start.
-  TAV_HIP(launch_start(ws_at<uint32_t>(workspace, P.off_status), verify ? verify->draft_row : nullptr,
-                       verify ? verify->num_draft_rows : 0, P.N, ws_at<int32_t>(workspace, P.off_order), sa));
+  // the workers' node order: built by an extra block of the bf16 prelude, else by the start kernel
+  const bool order_in_prelude = verify && prob->dtype == TAV_BF16;
+  const OrderArgs order{verify ? verify->draft_row : nullptr, verify ? verify->num_draft_rows : 0, P.N,
+                        verify ? ws_at<int32_t>(workspace, P.off_order) : nullptr};
+  TAV_HIP(launch_start(ws_at<uint32_t>(workspace, P.off_status), order_in_prelude ? nullptr : order.draft_row,
+                       order.R, P.N, order.order, sa));
   if (two) {
     TAV_HIP(hipEventRecord(fork, sa));
     TAV_HIP(hipStreamWaitEvent(sv, fork, 0));
@@ -541,7 +546,8 @@ tav_status tav_tree_attn_verify(const tav_problem* prob, const tav_tree* tree, c
     if (st != TAV_OK) return st;
   }
   if (two) TAV_HIP(hipEventRecord(join, sv));
-  st = enqueue_prep_attention(prob, P, tree, tree_out, attn, workspace, sa);
+  st = enqueue_prep_attention(prob, P, tree, tree_out, attn, workspace, sa,
+                              order_in_prelude ? order : OrderArgs{nullptr, 0, 0, nullptr});
   if (st != TAV_OK) return st;
   if (verify) {
     st = enqueue_verify(prob, P, tree, verify, workspace, sa, two ? join : nullptr);

@@ -169,8 +169,15 @@ hipError_t launch_prep(const Plan& p, const int32_t* node_offsets, const int32_t
                        const int32_t* parent, uint8_t* chain_ws, uint64_t* mask_ws,
                        const tav_tree_out* out, uint32_t* status, hipStream_t s);
 // bf16 attention: preparation, work plan and node packing in one launch.
+// The verification workers' node order (built by the start kernel, or by one extra block of the
+// prelude when the same call runs both): order null = none.
+struct OrderArgs {
+  const int32_t* draft_row;
+  int R, N;
+  int32_t* order;
+};
 hipError_t launch_prelude(const Plan& p, const int32_t* parent, const tav_tree_out* out, const AttnArgs& a,
-                          hipStream_t s);
+                          const OrderArgs& o, hipStream_t s);
 hipError_t launch_attn_bf16(const Plan& p, const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_f32(const Plan& p, const AttnArgs& a, hipStream_t s);
 hipError_t launch_merge(const Plan& p, const AttnArgs& a, bool bf16_out, hipStream_t s);
