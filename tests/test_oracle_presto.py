@@ -142,12 +142,13 @@ def test_example5_walk_golden():
     assert traj == e5["trajectory_states"]
 
 
-@pytest.mark.parametrize("seed", [10086, 1, 2, 3, 4])
-@pytest.mark.parametrize("n_pf,T", [(6, 12), (20, 30), (32, 64)])
-def test_proposition1_coupling_with_sequential_mh(seed, n_pf, T):
+def _coupling(seed, n_pf, T, u_pattern=None):
     rng = np.random.default_rng(seed)
     pf_parent, pf_acc, pf_req, pf_cut, cuts = gen.bfs_prefetch_tree(T, n_pf, rng)
     pr = _inputs(T, (pf_parent, pf_acc, pf_req, pf_cut), cuts, rng, max_transitions=int(rng.integers(2, 9)))
+    if u_pattern is not None:                       # forced decisions: 0 accepts, ~1 rejects
+        pr.u = np.array([u_pattern[v % len(u_pattern)] for v in range(len(pf_parent))], np.float64)
+        pr.max_transitions = 100
     res = oracle.presto_workload(pr)
     # sequential PowerMH: one proposal per step, drawn at the decision's own cut
     M = len(pf_parent)
@@ -173,3 +174,17 @@ def test_proposition1_coupling_with_sequential_mh(seed, n_pf, T):
     st = oracle.presto_states(pr)
     np.testing.assert_allclose(st[res["path"][-1]][0], lp0, rtol=0, atol=0)
     np.testing.assert_allclose(st[res["path"][-1]][1], lq, rtol=0, atol=0)
+
+
+@pytest.mark.parametrize("seed", [10086, 1, 2, 3, 4])
+@pytest.mark.parametrize("n_pf,T", [(6, 12), (20, 30), (32, 64)])
+def test_proposition1_coupling_with_sequential_mh(seed, n_pf, T):
+    _coupling(seed, n_pf, T)
+
+
+def test_proposition1_coupling_forced_decisions():
+    """Decision patterns that mix acceptances and rejections at every depth, so the walk
+    evaluates proposals from states reached through rejection children of accepted nodes."""
+    for seed in range(6):
+        for pattern in ([0.0, 1 - 1e-7], [0.0, 0.0, 1 - 1e-7], [1 - 1e-7, 0.0], [0.0, 1 - 1e-7, 1 - 1e-7]):
+            _coupling(seed, 32, 64, pattern)
