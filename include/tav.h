@@ -27,7 +27,21 @@
  *  - Calls are asynchronous on the given stream(s): host-checkable problems
  *    return a tav_status synchronously and enqueue nothing; problems only the
  *    device can see set bits in a status word inside the workspace
- *    (tav_read_status).  The affected sequence's outputs are then unspecified.
+ *    (tav_read_status) and the affected sequence's outputs become sentinels:
+ *      - an error of its tree or its prefix (TAV_DEV_BAD_PARENT,
+ *        TAV_DEV_TREE_TOO_LARGE, TAV_DEV_BAD_BLOCK) zeroes its attention rows
+ *        (out = 0, lse = -inf);
+ *      - any device-detected error of the sequence (those and the verification
+ *        ones: tokens, siblings, sampled children, draft rows, logits,
+ *        temperature, residual mass, path length) makes its verification
+ *        outputs path_len = 0, path = -1, bonus_token = -1, node_status = 0;
+ *      - TAV_DEV_PLAN_MISMATCH (device copies of node_offsets / prefix_len
+ *        differ from the host copies) leaves attention outputs unwritten and
+ *        makes every sequence's verification outputs sentinels;
+ *      - PreSTO errors (TAV_DEV_PRESTO_BAD_TREE) give NaN log_accept for the
+ *        affected request.
+ *    Every kernel checks an index before it uses it, so a bad input never
+ *    causes an out-of-bounds access.
  *  - Streams are passed as void* and are hipStream_t values (NULL = the null
  *    stream).  Calls on different workspaces are independent; two calls that
  *    share a workspace must be ordered by the caller.
@@ -40,6 +54,12 @@
  *  - A sequence whose every node's parent is the node just before it is a
  *    chain (causal attention, any length).  Any other tree may have at most
  *    256 nodes (ancestor sets are 256-bit masks).
+ *  - A forest whose roots share one cached prefix up to different lengths
+ *    (PreSTO's suffix requests, each keeping the state's prefix up to its own
+ *    cut: Section 3.2 step (2), Appendix B.3 Example 4) is passed as one
+ *    sequence per root: prefix_len of each is its root's prefix length, and
+ *    their block-table rows name the same physical blocks, so the shared
+ *    prefix is stored once.
  */
 #ifndef TAV_H
 #define TAV_H
@@ -233,7 +253,9 @@ tav_status tav_tree_attn_verify(const tav_problem* prob, const tav_tree* tree,
 /* Waits for stream, then copies the device status word to *status_bits. */
 tav_status tav_read_status(const void* workspace, void* stream, uint32_t* status_bits);
 
-/* Optional timing of one kernel of the pass, for benchmarks.  tav_kernel_timing(which) with
+/* Optional timing of one kernel of the pass, for benchmarks (the only host state the library keeps
+ * besides the per-thread error message and per-thread fork/join events of the two-stream call;
+ * it is per calling host thread).  tav_kernel_timing(which) with
  * which = 1 records a pair of HIP events on the attention stream immediately before and after
  * every bf16 tree-attention kernel launch (not around the preparation or merge launches); with
  * which = 2 around every launch of the vocabulary workers' kernel of the verification, on the
@@ -242,8 +264,8 @@ tav_status tav_read_status(const void* workspace, void* stream, uint32_t* status
  * and the number of launches recorded since the previous read or enable, and starts a new
  * record.  The events are timing-only (no system-scope fence when recorded).  They belong to the
  * device current at the first recording; recording on another device returns
- * TAV_ERR_INVALID_ARGUMENT, and so does a which outside 0..2.  Process-wide host state: calls
- * from several threads at once are not supported. */
+ * TAV_ERR_INVALID_ARGUMENT, and so does a which outside 0..2.  The record belongs to the calling
+ * host thread: only calls made on that thread are timed, and threads do not share it. */
 tav_status tav_kernel_timing(int which);
 tav_status tav_kernel_timing_read(double* total_ms, int32_t* launches);
 

@@ -58,12 +58,12 @@ def node_attention(q_rows, K, V, scale):
 
 def tree_attention(w, nodes=None, prep=None):
     """Attention output [len(nodes), Hq, D] and log-sum-exp [len(nodes), Hq] (float64)."""
-    if prep is None:
-        prep = tree_prep(w.parent, w.node_offsets, w.prefix_len)
     if nodes is None:
         nodes = range(w.N)
     nodes = [int(v) for v in nodes]
     seq_of = np.searchsorted(np.asarray(w.node_offsets), np.arange(w.N), side="right") - 1
+    if prep is None:
+        prep = tree_prep(w.parent, w.node_offsets, w.prefix_len, sorted({int(seq_of[v]) for v in nodes}))
     G = w.G
     out = np.zeros((len(nodes), w.Hq, w.D), dtype=np.float64)
     lse = np.zeros((len(nodes), w.Hq), dtype=np.float64)

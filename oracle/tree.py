@@ -43,13 +43,14 @@ def _seq_prep(parent_local: np.ndarray, prefix_len: int):
     return depth, pos, anc, is_chain
 
 
-def tree_prep(parent: np.ndarray, node_offsets: np.ndarray, prefix_len: np.ndarray):
+def tree_prep(parent: np.ndarray, node_offsets: np.ndarray, prefix_len: np.ndarray, seqs=None):
     """Per-node depth and position and the visibility set of every node.
 
     Returns a dict with ``depth`` [N], ``pos`` [N], ``anc`` (list, per node, of
     the sequence-local ids of pi(v) from the root down to v) and ``is_chain``
     [B] (True when every node's parent is the node just before it, i.e. the
-    tree is a path and the mask is ordinary causal attention).
+    tree is a path and the mask is ordinary causal attention).  With ``seqs``
+    only those sequences are prepared (the others' entries stay empty).
     """
     B = len(node_offsets) - 1
     N = int(node_offsets[-1])
@@ -57,7 +58,7 @@ def tree_prep(parent: np.ndarray, node_offsets: np.ndarray, prefix_len: np.ndarr
     pos = np.zeros(N, dtype=np.int64)
     anc = [None] * N
     is_chain = np.zeros(B, dtype=bool)
-    for b in range(B):
+    for b in (range(B) if seqs is None else seqs):
         s, e = int(node_offsets[b]), int(node_offsets[b + 1])
         d, p, a, ch = _seq_prep(np.asarray(parent[s:e]), int(prefix_len[b]))
         depth[s:e] = d

@@ -14,8 +14,8 @@ def run(w, two_streams=False, max_path=64, with_verify=True, with_presto=True, s
     """Upload w, run the pass once, return numpy outputs and the status bits.
 
     split_calls=True runs tav_tree_prep, tav_tree_attention and tav_tree_verify /
-    tav_presto_accept on two streams with their own workspaces (the benchmark's
-    launch configuration); otherwise one tav_tree_attn_verify call."""
+    tav_presto_accept on two streams with their own workspaces; otherwise one
+    tav_tree_attn_verify call (the benchmark's launch configuration)."""
     import tree_masked_verification_attn_amd as tav
 
     d = wdev.upload(w, "cuda", with_verify=with_verify, with_presto=with_presto, max_path=max_path)

@@ -1,5 +1,5 @@
-// Online-softmax merge of the pieces of attention row blocks cut between workgroups, shared by the
-// merge kernel and the verification's workers (which take merge items before their first node).
+// Online-softmax merge of the pieces of attention row blocks cut between workgroups (merge_kernel),
+// and the sentinel rows of sequences whose tree or prefix has a device-detected error.
 #pragma once
 
 #include "tav_internal.h"
@@ -13,6 +13,25 @@ namespace tav {
 template <typename OutT>
 __device__ inline void merge_rows(const AttnArgs& a, int D, int log2G, int r, int g, int row0, int nrows) {
   if (a.status[0] & TAV_DEV_PLAN_MISMATCH) return;
+  const int b = a.rb_seq[r];
+  if (b < 0 || b >= a.B) return;
+  const int s0 = a.node_offsets[b];
+  const int n = a.node_offsets[b + 1] - s0;
+  const int NB = kRowsPerWG >> log2G;
+  const int G = 1 << log2G;
+  const int node0 = (r - a.seq_rb_off[b]) * NB;
+  const int nodes_here = min(NB, n - node0);
+  if (a.seq_err[b] & kAttnErrBits) {
+    // the sequence's tree or prefix is unusable: its rows become sentinels (out = 0, lse = -inf)
+    for (int task = threadIdx.x; task < nrows * D; task += blockDim.x) {
+      const int row = row0 + task / D, d = task % D;
+      if ((row >> log2G) >= nodes_here) continue;
+      const size_t orow = (size_t)(s0 + node0 + (row >> log2G)) * a.Hq + g * G + (row & (G - 1));
+      ((OutT*)a.out)[orow * D + d] = (OutT)0.f;
+      if (d == 0 && a.lse) a.lse[orow] = -INFINITY;
+    }
+    return;
+  }
   const int rA = a.rb_tile[r], rE = a.rb_tile[r + 1];
   // the workgroups holding the row block's first and last tiles: the largest w with
   // wg_tile[w] <= tile (never an empty share: the next share starts at the same tile)
@@ -26,15 +45,6 @@ __device__ inline void merge_rows(const AttnArgs& a, int D, int log2G, int r, in
   };
   const int wf = owner(rA), wl = owner(rE - 1);
   if (wf == wl) return;  // one workgroup held the whole row block
-  const int b = a.rb_seq[r];
-  if (b < 0 || b >= a.B) return;
-  const int s0 = a.node_offsets[b];
-  const int n = a.node_offsets[b + 1] - s0;
-  if (a.is_chain[b] == 0 && n > kMaxTreeNodes) return;  // rejected by tree preparation
-  const int NB = kRowsPerWG >> log2G;
-  const int G = 1 << log2G;
-  const int node0 = (r - a.seq_rb_off[b]) * NB;
-  const int nodes_here = min(NB, n - node0);
   const int DQ = D / 4;
   constexpr int kPre = 4;   // pieces whose loads are all issued before any is used
   const int np = wl - wf + 1;

@@ -100,6 +100,7 @@ struct PlanView {
 // Where the tiles of one row block come from (wave-uniform).
 struct TileCursor {
   int r;          // row block
+  int seq;        // its sequence
   int t;          // tile within the row block
   int T;          // tiles of the row block
   int Tp;         // prefix tiles
@@ -113,6 +114,7 @@ struct TileCursor {
 __device__ __forceinline__ void cursor_load(TileCursor& c, const PlanView& pv, int r) {
   const int b = pv.rb_seq[r];
   c.r = r;
+  c.seq = b;
   c.T = pv.rb_tile[r + 1] - pv.rb_tile[r];
   c.L = pv.pref_len[b];
   c.Tp = (c.L + kTileKeys - 1) / kTileKeys;
@@ -133,12 +135,13 @@ __device__ __forceinline__ void cursor_advance(TileCursor& c, const PlanView& pv
 // block-table entry (loaded now, checked when used, so the scalar load's latency overlaps the
 // math) or a stand-in block for rows past the prefix; for a tree-node tile the packed block.
 struct BlockRef {
-  int blk, slot0;
+  int blk, slot0, seq;
   bool tail;
 };
 __device__ __forceinline__ BlockRef cursor_block(const TileCursor& c, int sb, int lbs) {
   const int bs = 1 << lbs;
   BlockRef ref;
+  ref.seq = c.seq;
   if (c.t < c.Tp) {
     const int r0 = c.t * kTileKeys + sb * 16;
     ref.blk = r0 < c.L ? c.btab[r0 >> lbs] : c.first_blk;
@@ -218,8 +221,11 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
   auto issue = [&](int j) __attribute__((always_inline)) {
     int blk = nref.blk;
     if (!nref.tail && (unsigned)blk >= (unsigned)a.num_blocks) {
-      if (lane == 0) atomicOr(a.status, (uint32_t)TAV_DEV_BAD_BLOCK);
-      blk = 0;
+      if (lane == 0) {
+        atomicOr(a.status, (uint32_t)TAV_DEV_BAD_BLOCK);
+        atomicOr(a.seq_err + nref.seq, (uint32_t)TAV_DEV_BAD_BLOCK);
+      }
+      blk = 0;   // (the sequence's rows become sentinels after the kernel)
     }
     const uint16_t* rk = (nref.tail ? ktl : kc) + (((size_t)blk * Hkv + g) * bs + nref.slot0) * D;
     const uint16_t* rv = (nref.tail ? vtl : vc) + ((size_t)blk * Hkv + g) * D * bs + nref.slot0;
@@ -671,6 +677,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
       const int blk = a.block_table[(size_t)b * a.max_blocks + k / a.block_size];
       if ((unsigned)blk >= (unsigned)a.num_blocks) {
         atomicOr(a.status, (uint32_t)TAV_DEV_BAD_BLOCK);
+        atomicOr(a.seq_err + b, (uint32_t)TAV_DEV_BAD_BLOCK);
         *ok = false;
         return nullptr;
       }
@@ -732,6 +739,21 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   if (lane == 0 && a.lse) a.lse[(size_t)v * a.Hq + h] = l > 0.f ? m + logf(l) : -INFINITY;
 }
 
+// float32 path: the rows of a sequence whose tree or prefix has a device-detected error become
+// sentinels (out = 0, lse = -inf); one block per sequence.
+__global__ __launch_bounds__(256) void attn_sentinel_f32_kernel(AttnArgs a, int D) {
+  const int b = blockIdx.x;
+  const bool all = (a.status[0] & TAV_DEV_PLAN_MISMATCH) != 0;
+  if (!all && !(a.seq_err[b] & kAttnErrBits)) return;
+  const int s0 = a.node_offsets[b], e0 = a.node_offsets[b + 1];
+  const size_t row_elems = (size_t)a.Hq * D;
+  float* out = (float*)a.out;
+  for (size_t i = threadIdx.x; i < (size_t)(e0 - s0) * row_elems; i += blockDim.x)
+    out[(size_t)s0 * row_elems + i] = 0.f;
+  if (a.lse)
+    for (int i = threadIdx.x; i < (e0 - s0) * a.Hq; i += blockDim.x) a.lse[(size_t)s0 * a.Hq + i] = -INFINITY;
+}
+
 template <int D>
 hipError_t launch_bf16_d(const Plan& p, const AttnArgs& a, hipStream_t s) {
   dim3 grid(p.W, p.Hkv);
@@ -753,6 +775,11 @@ hipError_t launch_attn_bf16(const Plan& p, const AttnArgs& a, hipStream_t s) {
   return p.D == 128 ? launch_bf16_d<128>(p, a, s) : launch_bf16_d<64>(p, a, s);
 }
 
+hipError_t launch_attn_sentinel_f32(const Plan& p, const AttnArgs& a, hipStream_t s) {
+  attn_sentinel_f32_kernel<<<p.B, 256, 0, s>>>(a, p.D);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_f32(const Plan& p, const AttnArgs& a, hipStream_t s) {
   dim3 grid(p.N, p.Hq);
   if (p.D == 128) attn_f32_kernel<128><<<grid, 64, 0, s>>>(a);
@@ -761,7 +788,7 @@ hipError_t launch_attn_f32(const Plan& p, const AttnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_merge(const Plan& p, const AttnArgs& a, bool bf16_out, hipStream_t s) {
-  if (p.W <= 1) return hipSuccess;   // one workgroup per KV head: nothing was cut
+  // (launched also when nothing was cut: it writes the sentinel rows of sequences with errors)
   dim3 grid(p.total_rb, p.Hkv, kRowsPerWG / 16);
   if (bf16_out) merge_kernel<__bf16><<<grid, 256, 0, s>>>(a, p.D, p.log2G);
   else merge_kernel<float><<<grid, 256, 0, s>>>(a, p.D, p.log2G);

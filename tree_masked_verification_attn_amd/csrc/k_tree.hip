@@ -56,6 +56,7 @@ struct PrepArgs {
   uint64_t* mask_out;
   uint8_t* chain_out;
   uint32_t* status;
+  uint32_t* seq_err;
 };
 
 // Sequence b: validate parents, detect a chain, and build depth, position and the 256-bit
@@ -74,8 +75,11 @@ __device__ void prep_sequence(const PrepArgs& a, int b) {
   bad = __syncthreads_or(bad);
   not_chain = __syncthreads_or(not_chain);
   if (bad) {
-    if (threadIdx.x == 0) atomicOr(a.status, (uint32_t)TAV_DEV_BAD_PARENT);
-    if (threadIdx.x == 0) a.chain_ws[b] = 0;
+    if (threadIdx.x == 0) {
+      atomicOr(a.status, (uint32_t)TAV_DEV_BAD_PARENT);
+      atomicOr(a.seq_err + b, (uint32_t)TAV_DEV_BAD_PARENT);
+      a.chain_ws[b] = 0;
+    }
     return;
   }
   if (threadIdx.x == 0) {
@@ -94,7 +98,10 @@ __device__ void prep_sequence(const PrepArgs& a, int b) {
     return;
   }
   if (n > kMaxTreeNodes) {
-    if (threadIdx.x == 0) atomicOr(a.status, (uint32_t)TAV_DEV_TREE_TOO_LARGE);
+    if (threadIdx.x == 0) {
+      atomicOr(a.status, (uint32_t)TAV_DEV_TREE_TOO_LARGE);
+      atomicOr(a.seq_err + b, (uint32_t)TAV_DEV_TREE_TOO_LARGE);
+    }
     return;
   }
   for (int v = threadIdx.x; v < n; v += blockDim.x) par_s[v] = a.parent[s0 + v];
@@ -325,14 +332,17 @@ __device__ void order_block(const int32_t* draft_row, int R, int N, int32_t* ord
   }
 }
 
-// Start of a call: clears the status word and the workers' node counter; with draft_row, builds the
-// workers' node order.
-__global__ __launch_bounds__(kPrepThreads) void start_kernel(uint32_t* status, const int32_t* draft_row, int R,
-                                                             int N, int32_t* order) {
+// Start of a call: clears the status word, the workers' node counter and the per-sequence error
+// words; with draft_row, builds the workers' node order.
+__global__ __launch_bounds__(kPrepThreads) void start_kernel(uint32_t* status, uint32_t* seq_err, int B,
+                                                             const int32_t* draft_row, int R, int N,
+                                                             int32_t* order) {
   if (threadIdx.x == 0) {
     status[0] = 0u;
     status[kCounterWord] = 0u;
   }
+  if (seq_err)
+    for (int b = threadIdx.x; b < B; b += blockDim.x) seq_err[b] = 0u;
   if (draft_row) order_block(draft_row, R, N, order);
 }
 
@@ -358,7 +368,8 @@ __global__ __launch_bounds__(kPrepThreads) void prelude_kernel(PrepArgs pa, Plan
 }
 
 PrepArgs prep_args(const int32_t* node_offsets, const int32_t* prefix_len, const int32_t* parent,
-                   uint8_t* chain_ws, uint64_t* mask_ws, const tav_tree_out* out, uint32_t* status) {
+                   uint8_t* chain_ws, uint64_t* mask_ws, const tav_tree_out* out, uint32_t* status,
+                   uint32_t* seq_err) {
   PrepArgs a;
   a.node_offsets = node_offsets; a.prefix_len = prefix_len; a.parent = parent;
   a.chain_ws = chain_ws; a.mask_ws = mask_ws;
@@ -367,28 +378,30 @@ PrepArgs prep_args(const int32_t* node_offsets, const int32_t* prefix_len, const
   a.mask_out = out ? out->mask : nullptr;
   a.chain_out = out ? out->is_chain : nullptr;
   a.status = status;
+  a.seq_err = seq_err;
   return a;
 }
 
 }  // namespace
 
-hipError_t launch_start(uint32_t* status, const int32_t* draft_row, int R, int N, int32_t* order, hipStream_t s) {
-  start_kernel<<<1, kPrepThreads, 0, s>>>(status, draft_row, R, N, order);
+hipError_t launch_start(uint32_t* status, uint32_t* seq_err, int B, const int32_t* draft_row, int R, int N,
+                        int32_t* order, hipStream_t s) {
+  start_kernel<<<1, kPrepThreads, 0, s>>>(status, seq_err, B, draft_row, R, N, order);
   return hipGetLastError();
 }
 
 hipError_t launch_prep(const Plan& p, const int32_t* node_offsets, const int32_t* prefix_len,
                        const int32_t* parent, uint8_t* chain_ws, uint64_t* mask_ws,
-                       const tav_tree_out* out, uint32_t* status, hipStream_t s) {
+                       const tav_tree_out* out, uint32_t* status, uint32_t* seq_err, hipStream_t s) {
   prep_kernel<<<p.B, kPrepThreads, 0, s>>>(
-      prep_args(node_offsets, prefix_len, parent, chain_ws, mask_ws, out, status));
+      prep_args(node_offsets, prefix_len, parent, chain_ws, mask_ws, out, status, seq_err));
   return hipGetLastError();
 }
 
 hipError_t launch_prelude(const Plan& p, const int32_t* parent, const tav_tree_out* out, const AttnArgs& a,
                           const OrderArgs& o, hipStream_t s) {
   const PrepArgs pa = prep_args(a.node_offsets, a.prefix_len, parent, const_cast<uint8_t*>(a.is_chain),
-                                const_cast<uint64_t*>(a.mask), out, a.status);
+                                const_cast<uint64_t*>(a.mask), out, a.status, a.seq_err);
   PlanArgs pl;
   pl.B = p.B; pl.NB = p.NB; pl.bs = p.bs; pl.total_rb_host = p.total_rb; pl.tiles_host = p.tiles_per_head;
   pl.tail_blocks_host = p.tail_blocks; pl.C = p.C; pl.W = p.W;

@@ -47,6 +47,16 @@ __global__ __launch_bounds__(64) void walk_kernel(WalkArgs a) {
   const int b = blockIdx.x, lane = threadIdx.x;
   const int s0 = a.node_offsets[b];
   const int n = a.node_offsets[b + 1] - s0;
+  // a sequence with an error found by an earlier kernel of the call: sentinel outputs
+  if (a.seq_err[b] != 0u || (a.status[0] & TAV_DEV_PLAN_MISMATCH) != 0u) {
+    for (int j = lane; j < n; j += 64) a.node_status[s0 + j] = 0;
+    for (int j = lane; j < a.max_path; j += 64) a.path[(size_t)b * a.max_path + j] = -1;
+    if (lane == 0) {
+      a.path_len[b] = 0;
+      a.bonus[b] = -1;
+    }
+    return;
+  }
   const bool staged = n <= kWalkLds;
   for (int j = lane; j < n; j += 64) {
     a.node_status[s0 + j] = 0;
@@ -142,6 +152,11 @@ __global__ __launch_bounds__(64) void walk_kernel(WalkArgs a) {
     __syncthreads();
     if (next < 0 || err) break;
     v = next;
+  }
+  __syncthreads();
+  if (err) {   // an error found by the walk itself: the same sentinel outputs
+    for (int j = lane; j < n; j += 64) a.node_status[s0 + j] = 0;
+    for (int j = lane; j < a.max_path; j += 64) a.path[(size_t)b * a.max_path + j] = -1;
   }
   if (lane == 0) {
     if (err) atomicOr(a.status, err);

@@ -171,6 +171,7 @@ tav_status make_plan(const tav_problem* p, const tav_presto_io* pr, Plan* out,
   P.off_child_q = o; o = align_up(o + (size_t)P.N * 4);
   P.off_presto = o; o = align_up(o + (size_t)(pr ? pr->num_requests : 0) * 8);
   P.off_order = o; o = align_up(o + (size_t)(p->vocab > 0 ? P.N : 0) * 4);
+  P.off_seq_err = o; o = align_up(o + (size_t)P.B * 4);
   if (p->vocab > 0) P.nch = ceil_div(ceil_div(p->vocab, p->dtype == TAV_BF16 ? 8 : 4), 64);
   P.total = o;
   *out = P;
@@ -251,6 +252,7 @@ AttnArgs attn_args(const tav_problem* p, const Plan& P, const tav_attn_io* io, v
   a.part_o = ws_at<uint16_t>(ws, P.off_part_o);
   a.part_lse = ws_at<float>(ws, P.off_part_lse);
   a.status = ws_at<uint32_t>(ws, P.off_status);
+  a.seq_err = ws_at<uint32_t>(ws, P.off_seq_err);
   a.B = P.B; a.Hq = P.Hq; a.Hkv = P.Hkv; a.total_rb = P.total_rb;
   a.tiles_per_head = P.tiles_per_head; a.C = P.C; a.W = P.W; a.tail_blocks = P.tail_blocks;
   a.block_size = p->block_size; a.num_blocks = p->num_blocks;
@@ -263,7 +265,7 @@ tav_status enqueue_prep(const tav_problem* p, const Plan& P, const tav_tree* t,
                         const tav_tree_out* out, void* ws, hipStream_t s) {
   uint32_t* status = ws_at<uint32_t>(ws, P.off_status);
   TAV_HIP(launch_prep(P, p->node_offsets, p->prefix_len, t->parent, ws_at<uint8_t>(ws, P.off_chain),
-                      ws_at<uint64_t>(ws, P.off_mask), out, status, s));
+                      ws_at<uint64_t>(ws, P.off_mask), out, status, ws_at<uint32_t>(ws, P.off_seq_err), s));
   return TAV_OK;
 }
 
@@ -275,7 +277,7 @@ struct KernelTiming {
   std::vector<std::pair<hipEvent_t, hipEvent_t>> pool;
   size_t used = 0;
 };
-KernelTiming g_timing;
+thread_local KernelTiming g_timing;   // per calling host thread
 
 void release_timing_events() {
   for (auto& e : g_timing.pool) {
@@ -329,6 +331,7 @@ tav_status enqueue_prep_attention(const tav_problem* p, const Plan& P, const tav
     const tav_status st = enqueue_prep(p, P, t, out, ws, s);
     if (st != TAV_OK) return st;
     TAV_HIP(launch_attn_f32(P, a, s));
+    TAV_HIP(launch_attn_sentinel_f32(P, a, s));
   }
   return TAV_OK;
 }
@@ -342,6 +345,7 @@ VocabArgs vocab_args(const tav_problem* p, const Plan& P, const tav_tree* t, con
   va.stats = io->node_stats ? io->node_stats : ws_at<float>(ws, P.off_stats);
   va.term_token = io->node_term_token ? io->node_term_token : ws_at<int32_t>(ws, P.off_term);
   va.status = status;
+  va.seq_err = ws_at<uint32_t>(ws, P.off_seq_err);
   va.child_p = ws_at<double>(ws, P.off_child_p);
   va.child_q = ws_at<float>(ws, P.off_child_q);
   va.B = P.B; va.N = P.N; va.V = p->vocab; va.R = io->num_draft_rows;
@@ -359,7 +363,7 @@ tav_status enqueue_walk(const tav_problem* p, const Plan& P, const tav_tree* t, 
   wa.token = t->token; wa.sampled = t->sampled; wa.uniforms = io->uniforms;
   wa.stats = va.stats; wa.term_token = va.term_token; wa.node_status = io->node_status; wa.path = io->path;
   wa.child_p = va.child_p; wa.child_q = va.child_q;
-  wa.path_len = io->path_len; wa.bonus = io->bonus_token; wa.status = va.status;
+  wa.path_len = io->path_len; wa.bonus = io->bonus_token; wa.status = va.status; wa.seq_err = va.seq_err;
   wa.B = P.B; wa.V = p->vocab; wa.R = io->num_draft_rows; wa.max_path = io->max_path;
   wa.logits_bf16 = p->dtype == TAV_BF16;
   TAV_HIP(launch_walk(wa, s));
@@ -434,6 +438,58 @@ tav_status get_events(hipEvent_t* fork, hipEvent_t* join) {
   return TAV_OK;
 }
 
+// The whole pass on a given workspace.
+tav_status attn_verify_impl(const tav_problem* prob, const tav_tree* tree, const tav_attn_io* attn,
+                            const tav_verify_io* verify, const tav_presto_io* presto,
+                            const tav_tree_out* tree_out, void* workspace, size_t workspace_bytes,
+                            void* attn_stream, void* verify_stream, const Plan* plan = nullptr) {
+  const bool two = verify_stream != attn_stream && presto;
+  Plan P;
+  tav_status st = TAV_OK;
+  if (plan) P = *plan;
+  else st = make_plan(prob, presto, &P);
+  if (st == TAV_OK) st = check_ws(P, workspace, workspace_bytes);
+  if (st == TAV_OK) st = check_tree(tree, verify != nullptr);
+  if (st == TAV_OK) st = check_attn(prob, attn);
+  if (st == TAV_OK && verify) st = check_verify(prob, verify);
+  if (st != TAV_OK) return st;
+  hipStream_t sa = (hipStream_t)attn_stream;
+  hipStream_t sv = (hipStream_t)verify_stream;
+  hipEvent_t fork = nullptr, join = nullptr;
+  if (two) {
+    st = get_events(&fork, &join);
+    if (st != TAV_OK) return st;
+  }
+  // attn_stream: start, preparation, attention, merge, the verification's workers, the walk.  The
+  // attention kernel and the workers each take whole compute units, so they run one after the
+  // other.  PreSTO is independent: on verify_stream (if different) from the start.
+  // the workers' node order: built by an extra block of the bf16 prelude, else by the start kernel
+  const bool order_in_prelude = verify && prob->dtype == TAV_BF16;
+  const OrderArgs order{verify ? verify->draft_row : nullptr, verify ? verify->num_draft_rows : 0, P.N,
+                        verify ? ws_at<int32_t>(workspace, P.off_order) : nullptr};
+  TAV_HIP(launch_start(ws_at<uint32_t>(workspace, P.off_status), ws_at<uint32_t>(workspace, P.off_seq_err), P.B,
+                       order_in_prelude ? nullptr : order.draft_row, order.R, P.N, order.order, sa));
+  if (two) {
+    TAV_HIP(hipEventRecord(fork, sa));
+    TAV_HIP(hipStreamWaitEvent(sv, fork, 0));
+  }
+  if (presto) {
+    st = enqueue_presto(P, presto, workspace, two ? sv : sa);
+    if (st != TAV_OK) return st;
+  }
+  if (two) TAV_HIP(hipEventRecord(join, sv));
+  st = enqueue_prep_attention(prob, P, tree, tree_out, attn, workspace, sa,
+                              order_in_prelude ? order : OrderArgs{nullptr, 0, 0, nullptr});
+  if (st != TAV_OK) return st;
+  if (verify) {
+    st = enqueue_verify(prob, P, tree, verify, workspace, sa, two ? join : nullptr);
+    if (st != TAV_OK) return st;
+  } else if (two) {
+    TAV_HIP(hipStreamWaitEvent(sa, join, 0));
+  }
+  return ok();
+}
+
 }  // namespace
 }  // namespace tav
 
@@ -458,7 +514,8 @@ tav_status tav_tree_prep(const tav_problem* prob, const tav_tree* tree, const ta
   if (st == TAV_OK) st = check_tree(tree, false);
   if (st != TAV_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  TAV_HIP(launch_start(ws_at<uint32_t>(workspace, P.off_status), nullptr, 0, 0, nullptr, s));
+  TAV_HIP(launch_start(ws_at<uint32_t>(workspace, P.off_status), ws_at<uint32_t>(workspace, P.off_seq_err), P.B,
+                       nullptr, 0, 0, nullptr, s));
   st = enqueue_prep(prob, P, tree, out, workspace, s);
   return st == TAV_OK ? ok() : st;
 }
@@ -472,7 +529,8 @@ tav_status tav_tree_attention(const tav_problem* prob, const tav_tree* tree, con
   if (st == TAV_OK) st = check_attn(prob, io);
   if (st != TAV_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  TAV_HIP(launch_start(ws_at<uint32_t>(workspace, P.off_status), nullptr, 0, 0, nullptr, s));
+  TAV_HIP(launch_start(ws_at<uint32_t>(workspace, P.off_status), ws_at<uint32_t>(workspace, P.off_seq_err), P.B,
+                       nullptr, 0, 0, nullptr, s));
   st = enqueue_prep_attention(prob, P, tree, nullptr, io, workspace, s);
   return st == TAV_OK ? ok() : st;
 }
@@ -486,8 +544,8 @@ tav_status tav_tree_verify(const tav_problem* prob, const tav_tree* tree, const 
   if (st == TAV_OK) st = check_verify(prob, io);
   if (st != TAV_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  TAV_HIP(launch_start(ws_at<uint32_t>(workspace, P.off_status), io->draft_row, io->num_draft_rows, P.N,
-                       ws_at<int32_t>(workspace, P.off_order), s));
+  TAV_HIP(launch_start(ws_at<uint32_t>(workspace, P.off_status), ws_at<uint32_t>(workspace, P.off_seq_err), P.B,
+                       io->draft_row, io->num_draft_rows, P.N, ws_at<int32_t>(workspace, P.off_order), s));
   st = enqueue_verify(prob, P, tree, io, workspace, s);
   return st == TAV_OK ? ok() : st;
 }
@@ -504,7 +562,7 @@ tav_status tav_presto_accept(const tav_presto_io* io, void* workspace, size_t wo
   st = check_ws(P, workspace, workspace_bytes);
   if (st != TAV_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  TAV_HIP(launch_start(ws_at<uint32_t>(workspace, P.off_status), nullptr, 0, 0, nullptr, s));
+  TAV_HIP(launch_start(ws_at<uint32_t>(workspace, P.off_status), nullptr, 0, nullptr, 0, 0, nullptr, s));
   st = enqueue_presto(P, io, workspace, s);
   return st == TAV_OK ? ok() : st;
 }
@@ -513,49 +571,8 @@ tav_status tav_tree_attn_verify(const tav_problem* prob, const tav_tree* tree, c
                                 const tav_verify_io* verify, const tav_presto_io* presto,
                                 const tav_tree_out* tree_out, void* workspace, size_t workspace_bytes,
                                 void* attn_stream, void* verify_stream) {
-  const bool two = verify_stream != attn_stream && presto;
-  Plan P;
-  tav_status st = make_plan(prob, presto, &P);
-  if (st == TAV_OK) st = check_ws(P, workspace, workspace_bytes);
-  if (st == TAV_OK) st = check_tree(tree, verify != nullptr);
-  if (st == TAV_OK) st = check_attn(prob, attn);
-  if (st == TAV_OK && verify) st = check_verify(prob, verify);
-  if (st != TAV_OK) return st;
-  hipStream_t sa = (hipStream_t)attn_stream;
-  hipStream_t sv = (hipStream_t)verify_stream;
-  hipEvent_t fork = nullptr, join = nullptr;
-  if (two) {
-    st = get_events(&fork, &join);
-    if (st != TAV_OK) return st;
-  }
-  // attn_stream: start, preparation, attention, merge, the verification's workers, the walk.  The
-  // attention kernel and the workers each take whole compute units, so they run one after the
-  // other.  PreSTO is independent: on verify_stream (if different) from the start.
-  // the workers' node order: built by an extra block of the bf16 prelude, else by the start kernel
-  const bool order_in_prelude = verify && prob->dtype == TAV_BF16;
-  const OrderArgs order{verify ? verify->draft_row : nullptr, verify ? verify->num_draft_rows : 0, P.N,
-                        verify ? ws_at<int32_t>(workspace, P.off_order) : nullptr};
-  TAV_HIP(launch_start(ws_at<uint32_t>(workspace, P.off_status), order_in_prelude ? nullptr : order.draft_row,
-                       order.R, P.N, order.order, sa));
-  if (two) {
-    TAV_HIP(hipEventRecord(fork, sa));
-    TAV_HIP(hipStreamWaitEvent(sv, fork, 0));
-  }
-  if (presto) {
-    st = enqueue_presto(P, presto, workspace, two ? sv : sa);
-    if (st != TAV_OK) return st;
-  }
-  if (two) TAV_HIP(hipEventRecord(join, sv));
-  st = enqueue_prep_attention(prob, P, tree, tree_out, attn, workspace, sa,
-                              order_in_prelude ? order : OrderArgs{nullptr, 0, 0, nullptr});
-  if (st != TAV_OK) return st;
-  if (verify) {
-    st = enqueue_verify(prob, P, tree, verify, workspace, sa, two ? join : nullptr);
-    if (st != TAV_OK) return st;
-  } else if (two) {
-    TAV_HIP(hipStreamWaitEvent(sa, join, 0));
-  }
-  return ok();
+  return attn_verify_impl(prob, tree, attn, verify, presto, tree_out, workspace, workspace_bytes, attn_stream,
+                          verify_stream);
 }
 
 tav_status tav_read_status(const void* workspace, void* stream, uint32_t* status_bits) {

@@ -17,6 +17,9 @@ constexpr int kMaxChildren = 256;  // children of one node held by the verificat
 constexpr int kMaxChunks = 2048;   // chunks of 64 sixteen-byte units per vocabulary row
                                    // (V <= 1 Mi bf16 / 512 Ki f32 tokens)
 constexpr int kCounterWord = 16;   // status block: word 0 = status bits, word 16 = the workers' node counter
+// Device-detected errors that make a sequence's attention rows sentinels (its tree or its prefix is
+// unusable); any device-detected error of a sequence makes its verification outputs sentinels.
+constexpr uint32_t kAttnErrBits = TAV_DEV_BAD_PARENT | TAV_DEV_TREE_TOO_LARGE | TAV_DEV_BAD_BLOCK;
 
 // Work decomposition of the attention pass.  A "row block" is up to
 // kRowsPerWG / G consecutive nodes of one sequence; it sees ceil(L / 64) prefix
@@ -39,7 +42,7 @@ struct Plan {
   size_t off_status = 0, off_chain = 0, off_mask = 0, off_seq_rb = 0, off_rb_seq = 0,
          off_rb_tile = 0, off_tail_blk = 0, off_wg_rb = 0, off_wg_tile = 0, off_rb_meta = 0, off_ktail = 0, off_vtail = 0, off_part_o = 0,
          off_part_lse = 0, off_stats = 0, off_term = 0, off_child_p = 0, off_child_q = 0,
-         off_presto = 0, off_order = 0, total = 0;
+         off_presto = 0, off_order = 0, off_seq_err = 0, total = 0;
   int nch = 0;            // vocabulary chunks (64 sixteen-byte units) per row
 };
 
@@ -94,6 +97,7 @@ struct AttnArgs {
   uint16_t* part_o;           // [2W, Hkv, 256, D] partial outputs of cut row blocks (bf16)
   float* part_lse;            // [2W, Hkv, 256]
   uint32_t* status;
+  uint32_t* seq_err;          // [B] device-detected errors of each sequence (TAV_DEV_* bits)
   int B, Hq, Hkv, total_rb, tiles_per_head, C, W, tail_blocks, block_size, num_blocks, max_blocks;
   float scale;        // softmax scale (natural)
 };
@@ -113,6 +117,7 @@ struct VocabArgs {
   double* child_p;       // [N] p of the node's token under its parent's target distribution
   float* child_q;        // [N] q~ of the node's token under its parent's draft row (0 if none)
   uint32_t* status;
+  uint32_t* seq_err;     // [B] device-detected errors of each sequence
   int32_t* queue;        // node counter of the workers' queue (cleared with the status word)
   const int32_t* order;  // [N] the nodes in the order the workers take them (nodes with a draft row first)
   int B, N, V, R, nch;
@@ -137,6 +142,7 @@ struct WalkArgs {
   int32_t* path_len;
   int32_t* bonus;
   uint32_t* status;
+  const uint32_t* seq_err;   // [B] errors found by the earlier kernels of the call
   int B, V, R, max_path, logits_bf16;
 };
 
@@ -162,12 +168,14 @@ struct PrestoArgs {
 
 // Kernel launchers (defined next to their kernels).  They return the HIP error
 // of the launch.
-// Start of every call: status word and counters cleared; with draft_row (verification), the order
-// in which the vocabulary workers take the nodes is built into order[N].
-hipError_t launch_start(uint32_t* status, const int32_t* draft_row, int R, int N, int32_t* order, hipStream_t s);
+// Start of every call: status word, counters and the per-sequence error words seq_err[B] cleared;
+// with draft_row (verification), the order in which the vocabulary workers take the nodes is built
+// into order[N].
+hipError_t launch_start(uint32_t* status, uint32_t* seq_err, int B, const int32_t* draft_row, int R, int N,
+                        int32_t* order, hipStream_t s);
 hipError_t launch_prep(const Plan& p, const int32_t* node_offsets, const int32_t* prefix_len,
                        const int32_t* parent, uint8_t* chain_ws, uint64_t* mask_ws,
-                       const tav_tree_out* out, uint32_t* status, hipStream_t s);
+                       const tav_tree_out* out, uint32_t* status, uint32_t* seq_err, hipStream_t s);
 // bf16 attention: preparation, work plan and node packing in one launch.
 // The verification workers' node order (built by the start kernel, or by one extra block of the
 // prelude when the same call runs both): order null = none.
@@ -180,7 +188,11 @@ hipError_t launch_prelude(const Plan& p, const int32_t* parent, const tav_tree_o
                           const OrderArgs& o, hipStream_t s);
 hipError_t launch_attn_bf16(const Plan& p, const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_f32(const Plan& p, const AttnArgs& a, hipStream_t s);
+// Merge of the cut row blocks; also writes the sentinel rows (out = 0, lse = -inf) of every
+// sequence whose tree or prefix has a device-detected error.
 hipError_t launch_merge(const Plan& p, const AttnArgs& a, bool bf16_out, hipStream_t s);
+// The same sentinel rows for the float32 path (one block per sequence).
+hipError_t launch_attn_sentinel_f32(const Plan& p, const AttnArgs& a, hipStream_t s);
 // Vocabulary workers: one 512-thread workgroup per compute unit, persistent over the node queue.
 hipError_t launch_vocab(const VocabArgs& a, bool bf16_logits, int num_cus, hipStream_t s);
 hipError_t launch_walk(const WalkArgs& a, hipStream_t s);

@@ -59,9 +59,11 @@ struct Lds {
   float ref_m[C::kMaxPieces];                // largest raw logit of each (step, wave) piece
   double ref_s[C::kMaxPieces];               // sum exp2(l log2e / T - ref) of each piece
   double red_d[C::kWaves];
-  int kid_id[kMaxChildren];                  // children of the node (sequence-local ids) ...
+  int kid_id[kMaxChildren];                  // children of the node (sequence-local ids, ascending) ...
   int kid_tok[kMaxChildren];                 // ... their tokens
   uint8_t kid_smp[kMaxChildren];             // ... and sampled flags
+  float kid_w[kMaxChildren];                 // ... and their weights in the final draw's chunks
+  int kid_cnt[C::kWaves];                    // children found by each wave in one round of the scan
   int item, cnt, nk, ns, err;
   uint4 lc[C::kCacheUnits];                  // the row's first kCacheSteps steps (each thread its own units)
 };
@@ -209,7 +211,7 @@ __device__ void process_node(const VocabArgs& a, Lds<C>& L, int v) {
   uint4 cur[kUnits];
   load_step<LT, C>(cur, row, 0, tid, nunits);
   // sequence of v: the number of sequence ends node_offsets[1..B] that are <= v
-  if (tid == 0) { L.cnt = 0; L.nk = 0; L.ns = 0; L.err = 0; }
+  if (tid == 0) { L.cnt = 0; L.ns = 0; L.err = 0; }
   __syncthreads();
   {
     int c = 0;
@@ -225,23 +227,44 @@ __device__ void process_node(const VocabArgs& a, Lds<C>& L, int v) {
   const float invTl2 = invT * kLog2e;
   const int dr = a.draft_row[v];
   const bool dr_ok = dr >= 0 && dr < a.R;
-  // children of v, the parent-array and temperature checks
+  // children of v in ascending id (a compaction with fixed order, so that everything computed from
+  // the list is the same on every run), the parent-array and temperature checks
   {
     uint32_t err = 0;
-    for (int c = tid; c < n; c += kThreads) {
-      const int pc = a.parent[s0 + c];
-      if (c == 0 ? pc != -1 : (pc < 0 || pc >= c)) err |= TAV_DEV_BAD_PARENT;
-      if (c > 0 && pc == v - s0) {
-        const int k = atomicAdd(&L.nk, 1);
-        const uint8_t smp = a.sampled[s0 + c];
-        if (smp) atomicAdd(&L.ns, 1);
+    int nk = 0, ns = 0;
+    for (int base = 0; base < n; base += kThreads) {
+      const int c = base + tid;
+      bool kid = false, smp = false;
+      if (c < n) {
+        const int pc = a.parent[s0 + c];
+        if (c == 0 ? pc != -1 : (pc < 0 || pc >= c)) err |= TAV_DEV_BAD_PARENT;
+        kid = c > 0 && pc == v - s0;
+        smp = kid && a.sampled[s0 + c] != 0;
+      }
+      const unsigned long long m = __ballot(kid);
+      const unsigned long long ms = __ballot(smp);
+      if (lane == 0) L.kid_cnt[wave] = __popcll(m);
+      __syncthreads();
+      int before = nk, total = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const int cw = L.kid_cnt[w];
+        before += w < wave ? cw : 0;
+        total += cw;
+      }
+      if (kid) {
+        const int k = before + __popcll(m & ((1ull << lane) - 1ull));
         if (k < kMaxChildren) {
           L.kid_id[k] = c;
           L.kid_tok[k] = a.token[s0 + c];
           L.kid_smp[k] = smp;
         }
       }
+      if (lane == 0 && ms) atomicAdd(&L.ns, __popcll(ms));
+      nk += total;
+      __syncthreads();   // kid_cnt is reused by the next round
     }
+    if (tid == 0) L.nk = nk;
     if (tid == 0 && !(Tb > 0.f && Tb < INFINITY)) err |= TAV_DEV_BAD_TEMPERATURE;
     if (err) atomicOr(&L.err, (int)err);
   }
@@ -390,12 +413,18 @@ __device__ void process_node(const VocabArgs& a, Lds<C>& L, int v) {
       const int cid = s0 + L.kid_id[k];
       a.child_p[cid] = exp((double)(z * invT) - (double)M) / S;
       a.child_q[cid] = use_draft ? qz : 0.f;
-      if (!L.kid_smp[k]) {
-        const float p = __builtin_amdgcn_exp2f(z * invTl2 - Ml2) * invS;
-        atomicAdd(&L.cw[tk / CT], -(use_draft ? fmaxf(0.f, p - qz) : p));
-      }
+      const float p = __builtin_amdgcn_exp2f(z * invTl2 - Ml2) * invS;
+      L.kid_w[k] = use_draft ? fmaxf(0.f, p - qz) : p;
     }
   }
+  wave_sync();
+  // the deterministic children's weights taken out of their chunks, one lane, in child order (a
+  // fixed order of the float subtractions: two runs give the same chunk weights bit for bit)
+  if (lane == 0)
+    for (int k = 0; k < nk; ++k) {
+      const int tk = L.kid_tok[k];
+      if (!L.kid_smp[k] && tk >= 0 && tk < V) L.cw[tk / CT] -= L.kid_w[k];
+    }
   wave_sync();
   // fp64 scan over chunks: lane l owns chunks [l * per, (l + 1) * per)
   const int per = (nch + 63) / 64;
@@ -495,7 +524,10 @@ __device__ void process_node(const VocabArgs& a, Lds<C>& L, int v) {
     a.stats[(size_t)v * 3 + 1] = (float)S;
     a.stats[(size_t)v * 3 + 2] = use_draft ? (float)Zt : 0.f;
     a.term_token[v] = tok;
-    if (err) atomicOr(a.status, err);
+    if (err) {
+      atomicOr(a.status, err);
+      atomicOr(a.seq_err + b, err);
+    }
   }
 }
 

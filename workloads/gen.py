@@ -326,7 +326,7 @@ def tree_batch(seed: int, *, B: int, prefix_len, tree: str, n_nodes, Hq: int, Hk
                dtype: str, V: int = 0, temperature: float = 1.0, logit_std: float = 3.0,
                draft_noise: float = 0.5, max_depth: int = 8, expand_k: int = 8,
                hybrid: str = "level", shuffle_blocks: bool = True, block_size: int = 16,
-               name: str = "custom") -> Workload:
+               draft_peak=None, name: str = "custom") -> Workload:
     """A batch of B independent sequences, each a prefix in paged KV plus one
     token tree whose node 0 is the root (the last committed token).
 
@@ -349,7 +349,7 @@ def tree_batch(seed: int, *, B: int, prefix_len, tree: str, n_nodes, Hq: int, Hk
         n = int(n_nodes[b])
         if tree == "eagle":
             par, tok, smp, dr, lg = _eagle_seq(seed, b, n, V, temperature, logit_std, draft_noise,
-                                               max_depth, expand_k, hybrid, dtype)
+                                               max_depth, expand_k, hybrid, dtype, draft_peak)
         else:
             if tree == "binary":
                 par = complete_binary_parents(n)
@@ -444,7 +444,7 @@ def _decorate_first_child_sampled(seed, b, parent, V, T, std, noise, dtype):
     return token, sampled, drafts, np.stack(stored)
 
 
-def _eagle_seq(seed, b, n_nodes, V, T, std, noise, depth, expand_k, hybrid, dtype):
+def _eagle_seq(seed, b, n_nodes, V, T, std, noise, depth, expand_k, hybrid, dtype, peak=None):
     cache = {}
 
     def logits_of(cid):
@@ -454,7 +454,12 @@ def _eagle_seq(seed, b, n_nodes, V, T, std, noise, depth, expand_k, hybrid, dtyp
 
     def draft_probs(path, cid):
         _, f = logits_of(cid)
-        z = f.astype(np.float64) + noise * _rng(seed, "draft_noise", b, cid).standard_normal(V)
+        r = _rng(seed, "draft_noise", b, cid)
+        z = f.astype(np.float64) + noise * r.standard_normal(V)
+        if peak is not None:
+            # a drafter's confident next token: its largest logit raised by U(peak) (the tree's
+            # depth then comes from the budget, as with a trained drafter, not from flat rows)
+            z[int(np.argmax(z))] += r.uniform(peak[0], peak[1])
         return _draft_softmax(z), _draft_softmax(z / T)
 
     tail_rng = _rng(seed, "tail", b)
@@ -565,6 +570,12 @@ def presto_batch(seed: int, *, T: int, n_pf: int, Hq: int, Hkv: int, D: int, dty
 # the five workload shapes
 # ----------------------------------------------------------------------------
 
+# Raise of each draft row's largest logit in the top-8 expansion trees of the one-tree and
+# long-context workloads (see _eagle_seq): flat N(0, 3^2) rows over 151936 tokens give a top-1
+# draft probability of a few percent, and the global prune then keeps only 3-4 levels.
+DRAFT_PEAK = (4.0, 7.0)
+
+
 def make(name: str, seed: int = 10086) -> Workload:
     if name == "c1":
         w = tree_batch(seed, B=1, prefix_len=128, tree="binary", n_nodes=15, Hq=4, Hkv=1, D=64,
@@ -573,7 +584,7 @@ def make(name: str, seed: int = 10086) -> Workload:
     elif name == "c2":
         w = tree_batch(seed, B=1, prefix_len=2048, tree="eagle", n_nodes=60, Hq=32, Hkv=8, D=128,
                        dtype="bf16", V=151936, temperature=0.7, logit_std=3.0, max_depth=6,
-                       expand_k=8, hybrid="level", name="c2")
+                       expand_k=8, hybrid="level", draft_peak=DRAFT_PEAK, name="c2")
     elif name == "c3":
         L = _rng(seed, "prefix_lens").integers(1024, 8193, size=16).astype(np.int32)
         w = tree_batch(seed, B=16, prefix_len=L, tree="random", n_nodes=64, Hq=32, Hkv=8, D=128,
@@ -585,7 +596,7 @@ def make(name: str, seed: int = 10086) -> Workload:
     elif name == "c5":
         w = tree_batch(seed, B=4, prefix_len=32768, tree="eagle", n_nodes=128, Hq=32, Hkv=8,
                        D=128, dtype="bf16", V=151936, temperature=1.0, logit_std=3.0,
-                       max_depth=10, expand_k=8, hybrid="all", name="c5")
+                       max_depth=10, expand_k=8, hybrid="all", draft_peak=DRAFT_PEAK, name="c5")
     else:
         raise ValueError(name)
     w.info["description"] = CONFIG_DESCRIPTIONS[name]
