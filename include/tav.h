@@ -250,6 +250,28 @@ tav_status tav_tree_attn_verify(const tav_problem* prob, const tav_tree* tree,
                                 void* workspace, size_t workspace_bytes,
                                 void* attn_stream, void* verify_stream);
 
+/* Bytes of the device array that serves as workspace of tav_tree_attn_verify_noalloc (64 MiB, one
+ * array per GPU the library runs on, held until the process ends). */
+#define TAV_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* The whole pass exactly as tav_tree_attn_verify, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation): the
+ * workspace is the library's own device array of TAV_NOALLOC_SCRATCH_BYTES on the current GPU
+ * instead of a caller buffer, and the call allocates nothing (no hipMalloc / hipFree, no
+ * allocating library routine).  The caller still passes every input and output.
+ *   status_out: optional device pointer; the call's device status word is copied there (on
+ *     attn_stream, after the pass) -- the array itself is not exposed.
+ * Errors: as tav_tree_attn_verify; TAV_ERR_WORKSPACE when tav_workspace_size() of the problem
+ * exceeds TAV_NOALLOC_SCRATCH_BYTES (nothing enqueued).  The array's address is looked up on the
+ * first call on each device.  Every call on one GPU uses that GPU's one array and the array keeps
+ * the last call's contents (each call clears what must start at zero): calls that may overlap on
+ * one GPU -- different streams without ordering, or several host threads -- race and must be
+ * ordered by the caller. */
+tav_status tav_tree_attn_verify_noalloc(const tav_problem* prob, const tav_tree* tree,
+                                        const tav_attn_io* attn, const tav_verify_io* verify,
+                                        const tav_presto_io* presto, const tav_tree_out* tree_out,
+                                        uint32_t* status_out, void* attn_stream, void* verify_stream);
+
 /* Waits for stream, then copies the device status word to *status_bits. */
 tav_status tav_read_status(const void* workspace, void* stream, uint32_t* status_bits);
 

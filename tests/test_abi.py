@@ -168,3 +168,21 @@ def test_kernel_timing_state_without_gpu_work():
     assert tav.tav_kernel_timing_read() == (0.0, 0)
     tav.tav_kernel_timing(False)
     assert tav.tav_kernel_timing_read() == (0.0, 0)
+
+
+def test_noalloc_rejects_problems_beyond_its_array():
+    """The allocation-free call checks the problem's workspace against its fixed device array
+    before any HIP call: a problem needing more returns TAV_ERR_WORKSPACE and enqueues nothing."""
+    lib = tav.load()
+    big = _Host(offsets=(0, 200000), prefix=(16,), max_blocks=4)          # a 200000-token chain
+    st, need = _ws_size(big)
+    assert st == 0 and need > tav.NOALLOC_SCRATCH_BYTES
+    parent = np.arange(-1, 199999, dtype=np.int32)
+    tree = tav.tav_tree(parent=parent.ctypes.data, token=None, sampled=None)
+    dummy = np.zeros(64, np.float32)
+    d = dummy.ctypes.data + (-dummy.ctypes.data) % 16
+    attn = tav.tav_attn_io(q=d, k_node=d, v_node=d, k_cache=d, v_cache=d, block_table=d, out=d, lse=None)
+    st = lib.tav_tree_attn_verify_noalloc(ctypes.byref(big.p), ctypes.byref(tree), ctypes.byref(attn), None,
+                                          None, None, None, None, None)
+    assert st == 4, tav.tav_last_error()
+    assert "allocation-free" in tav.tav_last_error()

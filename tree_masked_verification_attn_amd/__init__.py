@@ -29,7 +29,9 @@ DEVICE_BITS = {
 }
 ENTRY_POINTS = ("tav_workspace_size", "tav_tree_prep", "tav_tree_attention", "tav_tree_verify",
                 "tav_presto_accept", "tav_tree_attn_verify", "tav_read_status", "tav_kernel_timing",
-                "tav_kernel_timing_read", "tav_status_string", "tav_last_error")
+                "tav_kernel_timing_read", "tav_tree_attn_verify_noalloc", "tav_status_string",
+                "tav_last_error")
+NOALLOC_SCRATCH_BYTES = 64 << 20   # TAV_NOALLOC_SCRATCH_BYTES
 
 _p = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -104,13 +106,17 @@ def load() -> ctypes.CDLL:
             ctypes.POINTER(tav_problem), ctypes.POINTER(tav_tree), ctypes.POINTER(tav_attn_io),
             ctypes.POINTER(tav_verify_io), ctypes.POINTER(tav_presto_io), ctypes.POINTER(tav_tree_out),
             _p, ctypes.c_size_t, _p, _p]
+        lib.tav_tree_attn_verify_noalloc.argtypes = [
+            ctypes.POINTER(tav_problem), ctypes.POINTER(tav_tree), ctypes.POINTER(tav_attn_io),
+            ctypes.POINTER(tav_verify_io), ctypes.POINTER(tav_presto_io), ctypes.POINTER(tav_tree_out),
+            _p, _p, _p]
         lib.tav_read_status.argtypes = [_p, _p, ctypes.POINTER(ctypes.c_uint32)]
         lib.tav_kernel_timing.argtypes = [ctypes.c_int]
         lib.tav_kernel_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i32)]
         lib.tav_status_string.argtypes = [ctypes.c_int]
         lib.tav_status_string.restype = ctypes.c_char_p
         lib.tav_last_error.restype = ctypes.c_char_p
-        for name in ENTRY_POINTS[:9]:
+        for name in ENTRY_POINTS[:10]:
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -231,6 +237,23 @@ def tav_tree_attn_verify(prob: Problem, tree, attn, verify, presto, tree_out, wo
     _check(load().tav_tree_attn_verify(ctypes.byref(ps), ctypes.byref(ts), ctypes.byref(ai), _ref(vi),
                                        _ref(pr), _ref(to), _ptr(workspace),
                                        workspace.numel() * workspace.element_size(), sa, sv))
+
+
+def tav_tree_attn_verify_noalloc(prob: Problem, tree, attn, verify, presto, tree_out,
+                                 status_out: Optional[torch.Tensor] = None, attn_stream=None,
+                                 verify_stream=None):
+    """The whole pass on the library's own device array (no workspace argument, no allocation);
+    status_out: optional int32/uint32 device tensor of one element that receives the status word."""
+    ps = prob.struct()
+    ts = _struct_of(tav_tree, tree)
+    ai = _struct_of(tav_attn_io, attn)
+    vi = _struct_of(tav_verify_io, verify)
+    pr = _struct_of(tav_presto_io, presto)
+    to = _struct_of(tav_tree_out, tree_out)
+    sa = _stream(attn_stream)
+    sv = _stream(verify_stream) if verify_stream is not None else sa
+    _check(load().tav_tree_attn_verify_noalloc(ctypes.byref(ps), ctypes.byref(ts), ctypes.byref(ai), _ref(vi),
+                                               _ref(pr), _ref(to), _ptr(status_out), sa, sv))
 
 
 def tav_read_status(workspace: torch.Tensor, stream=None) -> int:

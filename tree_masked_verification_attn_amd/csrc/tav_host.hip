@@ -11,7 +11,15 @@
 #include <utility>
 #include <vector>
 
+#include <mutex>
+
 #include "tav_internal.h"
+
+// Workspace of tav_tree_attn_verify_noalloc: one device array per GPU the library runs on, held
+// until the process ends.  Host code never passes this name to a kernel or a copy (on the host it
+// is a stand-in, not a device address); it uses the address hipGetSymbolAddress returns for the
+// current device (scratch_address below).
+static __device__ __align__(256) uint8_t scratch[TAV_NOALLOC_SCRATCH_BYTES];
 
 namespace tav {
 namespace {
@@ -44,6 +52,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
+constexpr int kMaxDevices = 64;
 constexpr int kTargetWorkgroups = 256;  // one round of one workgroup per MI355X compute unit
 constexpr int kMinTilesPerWG = 8;       // at least 512 keys per attention workgroup (more than kRbCost)
 
@@ -438,7 +447,28 @@ tav_status get_events(hipEvent_t* fork, hipEvent_t* join) {
   return TAV_OK;
 }
 
-// The whole pass on a given workspace.
+// Device address of the allocation-free call's array on the current device, looked up once per
+// device (with that device current) and kept.
+tav_status scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  TAV_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(TAV_ERR_INVALID_ARGUMENT, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(TAV_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return TAV_OK;
+}
+
+// The whole pass on a given workspace (shared by tav_tree_attn_verify and the allocation-free
+// variant, which passes the library's own device array).
 tav_status attn_verify_impl(const tav_problem* prob, const tav_tree* tree, const tav_attn_io* attn,
                             const tav_verify_io* verify, const tav_presto_io* presto,
                             const tav_tree_out* tree_out, void* workspace, size_t workspace_bytes,
@@ -573,6 +603,30 @@ tav_status tav_tree_attn_verify(const tav_problem* prob, const tav_tree* tree, c
                                 void* attn_stream, void* verify_stream) {
   return attn_verify_impl(prob, tree, attn, verify, presto, tree_out, workspace, workspace_bytes, attn_stream,
                           verify_stream);
+}
+
+tav_status tav_tree_attn_verify_noalloc(const tav_problem* prob, const tav_tree* tree, const tav_attn_io* attn,
+                                        const tav_verify_io* verify, const tav_presto_io* presto,
+                                        const tav_tree_out* tree_out, uint32_t* status_out,
+                                        void* attn_stream, void* verify_stream) {
+  Plan P;
+  tav_status st = make_plan(prob, presto, &P);
+  if (st != TAV_OK) return st;
+  if (P.total > (size_t)TAV_NOALLOC_SCRATCH_BYTES)
+    return fail(TAV_ERR_WORKSPACE,
+                "this problem needs %zu bytes of workspace; the allocation-free call has %zu (use "
+                "tav_tree_attn_verify with a caller workspace)",
+                P.total, (size_t)TAV_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != TAV_OK) return st;
+  st = attn_verify_impl(prob, tree, attn, verify, presto, tree_out, ws, (size_t)TAV_NOALLOC_SCRATCH_BYTES,
+                        attn_stream, verify_stream, &P);
+  if (st != TAV_OK) return st;
+  if (status_out)   // the status word (written by this call's kernels) into the caller's buffer
+    TAV_HIP(hipMemcpyAsync(status_out, ws_at<uint32_t>(ws, P.off_status), sizeof(uint32_t),
+                           hipMemcpyDeviceToDevice, (hipStream_t)attn_stream));
+  return ok();
 }
 
 tav_status tav_read_status(const void* workspace, void* stream, uint32_t* status_bits) {
