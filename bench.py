@@ -1,32 +1,36 @@
 """Throughput of the tree-masked scoring pass on one MI355X.
 
-Workload (default): 16 sequences, prefix lengths uniform in [1024, 8192] in a
-paged KV cache (block 16, shuffled block table), 64-node random trees of depth
-<= 8, 32 query / 8 KV heads, head_dim 128, bf16, vocabulary 151936, T = 1.0,
-seed 10086 -- the batched verification shape.  Inputs are synthetic (seeded).
+Headline workload (default): 16 sequences, prefix lengths uniform in [1024, 8192] in
+a paged KV cache (block 16, shuffled block table), 64-node random trees of depth <= 8,
+32 query / 8 KV heads, head_dim 128, bf16, vocabulary 151936, T = 1.0, seed 10086 --
+the batched verification shape.  Inputs are synthetic (seeded).
 
-One step = one whole pass, one tav_tree_attn_verify call: the call's start
-kernel (status reset, the verification workers' node order), tree preparation
-(with the attention work plan and node packing), split-KV tree attention and its
-merge, then the verification's vocabulary workers and the walk, all on one
-stream.  With --separate the step is tav_tree_attention and tav_tree_verify on
-their own streams and workspaces instead (which also times each half).  Inputs
-are resident in HBM; two input copies alternate so consecutive steps do not
-re-read one step's data from the 256 MB last-level cache.
+One step = one whole pass, one tav_tree_attn_verify call: the call's start kernel,
+tree preparation (with the attention work plan, node packing and the verification
+workers' node order), split-KV tree attention and its merge, then the verification's
+vocabulary workers and the walk, all on one stream.  Inputs are resident in HBM; two
+input copies alternate so consecutive steps do not re-read one step's data from the
+256 MB last-level cache.  The K timed steps carry no events.
 
 Prints one JSON line:  value = tree nodes scored per second (attention +
-verification), plus the step's algorithmic HBM GB/s, the roofline of the
-dominant kernel -- the vocabulary workers of the verification, the longest
-kernel of the pass and an HBM stream, timed per launch by HIP events the
-library records around it on its own stream over the timed region -- with the
-HBM traffic measured by counters for the same kernel source (or null), the
-attention kernel's roofline from a second timed loop of attention-only calls,
-and the oracle's throughput on the same workload on one host core.
+verification) on the headline workload, plus
+  * the step's algorithmic HBM GB/s;
+  * roofline: the dominant kernel (the verification's vocabulary workers), timed per
+    launch by HIP events the library records around it on its own stream, with the HBM
+    traffic measured by counters for the same kernel source (or null);
+  * attention_kernel: the attention kernel's roofline from attention-only calls;
+  * achievable: a streaming-read kernel's HBM bandwidth and a matrix-core kernel's bf16
+    rate on this GPU (the fractions of those beside the fractions of the published peaks);
+  * sub_records: the same measurements for the long-context workload (4 x 32768 prefix,
+    128-node depth-10 trees), the PreSTO prefetch batch (attention MFMA utilisation,
+    log A + walk time) and the headline workload with sparse top-128 draft rows;
+  * cpu_baseline: the oracle on a bounded sample of the headline workload, on the host.
 """
 
 import argparse
 import json
 import os
+import platform
 import sys
 import time
 
@@ -42,43 +46,68 @@ KERNEL_SOURCES = [os.path.join(ROOT, "tree_masked_verification_attn_amd", "csrc"
                   for f in ("vocab_worker.h", "k_verify.hip")]
 
 
-def algorithmic_bytes(w):
-    """Bytes the pass must move: each prefix KV row once per (sequence, KV head),
-    each node's q / k / v / out once, each logits row once, each draft row that
-    verification uses once (nodes with a sampled child), small per-node arrays."""
+def _used_draft_rows(w):
+    """Nodes whose draft row verification reads: a sampled child and a draft row."""
     import numpy as np
 
+    has_s = np.zeros(w.N, bool)
+    for b in range(w.B):
+        s = int(w.node_offsets[b])
+        for c in range(s + 1, int(w.node_offsets[b + 1])):
+            if w.sampled[c]:
+                has_s[s + int(w.parent[c])] = True
+    return int(np.sum(has_s & (w.draft_row >= 0)))
+
+
+def algorithmic_bytes(w):
+    """Bytes the pass must move: each prefix KV row once per (sequence, KV head), each node's
+    q / k / v / out once, each logits row once, each draft row that verification uses once
+    (V floats dense, K ids + K floats sparse), small per-node arrays."""
     eb = 2 if w.dtype == "bf16" else 4
     kv = int(sum(int(L) for L in w.prefix_len)) * w.Hkv * w.D * eb * 2
     nodes = w.N * (w.Hq * w.D * eb * 2 + w.Hkv * w.D * eb * 2 + w.Hq * 4)
     attn = kv + nodes + int(w.block_table.size) * 4
     verify = 0
     if w.logits is not None:
-        has_s = np.zeros(w.N, bool)
-        for b in range(w.B):
-            s = int(w.node_offsets[b])
-            for c in range(s + 1, int(w.node_offsets[b + 1])):
-                if w.sampled[c]:
-                    has_s[s + int(w.parent[c])] = True
-        used = int(np.sum(has_s & (w.draft_row >= 0)))
-        verify = w.N * w.V * eb + used * w.V * 4 + w.N * (4 + 1 + 4 + 1 + 8)
+        row = w.draft_k * 8 if w.draft_k else w.V * 4
+        verify = w.N * w.V * eb + _used_draft_rows(w) * row + w.N * (4 + 1 + 4 + 1 + 8)
     return attn, verify
 
 
-def attention_flops(w):
-    import oracle
+def depths(w):
+    """Depth of every node (parents are earlier nodes of the same sequence)."""
+    import numpy as np
 
-    prep = oracle.tree_prep(w.parent, w.node_offsets, w.prefix_len)
-    keys = 0
+    d = np.zeros(w.N, np.int64)
     for b in range(w.B):
-        for v in w.seq_nodes(b):
-            keys += int(w.prefix_len[b]) + int(prep["depth"][v]) + 1
+        s = int(w.node_offsets[b])
+        for v in range(s + 1, int(w.node_offsets[b + 1])):
+            d[v] = d[s + int(w.parent[v])] + 1
+    return d
+
+
+def attention_flops(w):
+    """4 d flops per (query row, visible key): QK^T and PV over prefix + ancestors + self."""
+    import numpy as np
+
+    seq = np.repeat(np.arange(w.B), np.diff(w.node_offsets))
+    keys = int(np.sum(np.asarray(w.prefix_len, np.int64)[seq] + depths(w) + 1))
     return 4 * w.D * w.Hq * keys
 
 
-def cpu_baseline(w, min_seconds=10.0, max_passes=4):
-    """The oracle, as it is, on the whole workload (attention of every node + verification
-    walk of every sequence), one thread, repeated until about min_seconds of CPU work."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(w, threads, min_seconds=8.0, max_passes=4):
+    """The oracle, as it is, on the headline workload (attention of every node + verification
+    walk of every sequence), with `threads` BLAS threads, repeated to about min_seconds."""
     from threadpoolctl import threadpool_limits
 
     import oracle
@@ -86,14 +115,15 @@ def cpu_baseline(w, min_seconds=10.0, max_passes=4):
     seqs = list(range(w.B))
     nodes = [v for b in seqs for v in w.seq_nodes(b)]
     passes, dt = 0, 0.0
-    with threadpool_limits(1):
+    with threadpool_limits(threads):
         while passes < max_passes and (passes == 0 or dt < min_seconds):
             t0 = time.perf_counter()
             oracle.tree_attention(w, nodes)
             oracle.verify_workload(w, seqs)
             dt += time.perf_counter() - t0
             passes += 1
-    return {"value": passes * len(nodes) / dt, "unit": "nodes/s", "cores": 1, "kind": "oracle",
+    return {"value": round(passes * len(nodes) / dt, 1), "unit": "nodes/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"the whole workload ({w.B} sequences, {len(nodes)} nodes: attention of every "
                       f"node + verification walk) x {passes} passes, {dt:.1f} s"}
 
@@ -118,6 +148,195 @@ def measured_traffic():
     return int(rec["hbm_bytes_per_launch"])
 
 
+# ----------------------------------------------------------------------------------------------
+# GPU measurements
+# ----------------------------------------------------------------------------------------------
+
+def achievable(tav_dir):
+    """Streaming-read bandwidth (4 GiB read once, median of 5) and bf16 MFMA rate (256 x 4 waves,
+    median of 5) measured by the probe library on this GPU."""
+    import ctypes
+
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(tav_dir, "libtavprobe.so"))
+    lib.tavprobe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                         ctypes.c_void_p]
+    lib.tavprobe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    s = torch.cuda.Stream()
+    nbytes = 4 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    grid = 256 * 16
+    sink = torch.zeros(grid, dtype=torch.int32, device="cuda")
+    times = []
+    for i in range(7):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        assert lib.tavprobe_stream_read(src.data_ptr(), nbytes, sink.data_ptr(), grid, s.cuda_stream) == 0
+        e1.record(s)
+        torch.cuda.synchronize()
+        if i >= 2:
+            times.append(e0.elapsed_time(e1))
+    del src
+    read_gbs = nbytes / (sorted(times)[len(times) // 2] * 1e-3) / 1e9
+    mgrid, iters = 1024, 20000
+    msink = torch.zeros(mgrid * 256, dtype=torch.float32, device="cuda")
+    times = []
+    for i in range(7):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        assert lib.tavprobe_mfma(msink.data_ptr(), iters, mgrid, s.cuda_stream) == 0
+        e1.record(s)
+        torch.cuda.synchronize()
+        if i >= 2:
+            times.append(e0.elapsed_time(e1))
+    flops = mgrid * 4 * 4 * iters * 32768.0        # waves x chains x rounds x flops per MFMA
+    mfma_tflops = flops / (sorted(times)[len(times) // 2] * 1e-3) / 1e12
+    return {"hbm_read_gbs": round(read_gbs, 1), "hbm_read_frac_of_peak": round(read_gbs / HBM_PEAK_GBS, 4),
+            "mfma_bf16_tflops": round(mfma_tflops, 1),
+            "mfma_frac_of_peak": round(mfma_tflops / BF16_PEAK_TFLOPS, 4),
+            "how": "stream_read_kernel: 4 GiB read once with 16-byte loads, 8 in flight per thread; "
+                   "mfma_kernel: 4 independent v_mfma_f32_32x32x16_bf16 chains per wave, 1024 x 4 waves; "
+                   "medians of 5 timed launches"}
+
+
+class Pass:
+    """A workload uploaded twice, timed as whole passes and per kernel."""
+
+    def __init__(self, w, copies=2):
+        import torch
+
+        from workloads import device as wdev
+
+        self.w = w
+        self.copies = [wdev.upload(w, "cuda") for _ in range(max(1, copies))]
+        self.sa = torch.cuda.Stream()
+        torch.cuda.synchronize()
+
+    def step(self, i, presto=False):
+        import tree_masked_verification_attn_amd as tav
+
+        c = self.copies[i % len(self.copies)]
+        tav.tav_tree_attn_verify(c.prob, c.tree, c.attn, c.verify, c.presto if presto else None, None,
+                                 c.workspace, self.sa, self.sa)
+
+    def time_steps(self, steps, warmup, presto=False):
+        import torch
+
+        import tree_masked_verification_attn_amd as tav
+
+        for i in range(warmup):
+            self.step(i, presto)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(i, presto)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        for c in self.copies:
+            bits = tav.tav_read_status(c.workspace)
+            if bits:
+                raise RuntimeError(f"device status bits set: {tav.device_status_names(bits)}")
+        return ms
+
+    def kernel_ms(self, which, steps, call="pass"):
+        """Average launch time of one kernel (1 attention, 2 vocabulary workers) from the library's
+        own events over `steps` calls (whole passes, or attention-only calls)."""
+        import torch
+
+        import tree_masked_verification_attn_amd as tav
+
+        def run(i):
+            if call == "pass":
+                self.step(i)
+            else:
+                c = self.copies[i % len(self.copies)]
+                tav.tav_tree_attention(c.prob, c.tree, c.attn, c.workspace, self.sa)
+
+        for i in range(2):
+            run(i)
+        torch.cuda.synchronize()
+        tav.tav_kernel_timing(which)
+        for i in range(steps):
+            run(i)
+        torch.cuda.synchronize()
+        total, n = tav.tav_kernel_timing_read()
+        tav.tav_kernel_timing(0)
+        return total / max(1, n), n
+
+    def presto_ms(self, steps):
+        import torch
+
+        import tree_masked_verification_attn_amd as tav
+
+        c = self.copies[0]
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        tav.tav_presto_accept(c.presto, c.workspace, self.sa)
+        for e0, e1 in ev:
+            e0.record(self.sa)
+            tav.tav_presto_accept(c.presto, c.workspace, self.sa)
+            e1.record(self.sa)
+        torch.cuda.synchronize()
+        return sum(e0.elapsed_time(e1) for e0, e1 in ev) / steps
+
+
+def roofline_hbm(kernel, bytes_, ms, ach=None, traffic=None, launches=None):
+    gbs = bytes_ / (ms * 1e-3) / 1e9
+    r = {"kernel": kernel, "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "avg_launch_ms": round(ms, 4),
+         "launches_timed": launches, "algorithmic_bytes": bytes_}
+    if ach:
+        r["frac_of_achievable"] = round(gbs / ach["hbm_read_gbs"], 4)
+    return r
+
+
+def attention_record(p, flops, attn_b, steps, ach):
+    a_ms, n = p.kernel_ms(1, steps, call="attention")
+    rec = roofline_hbm("attn_bf16_kernel (tree-masked attention, bf16 MFMA), attention-only calls",
+                       attn_b, a_ms, ach, launches=n)
+    tf = flops / (a_ms * 1e-3) / 1e12
+    rec.update({"algorithmic_flops": flops, "mfma_tflops": round(tf, 1),
+                "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                "roofline_frac": round(max(attn_b / (HBM_PEAK_GBS * 1e9), flops / (BF16_PEAK_TFLOPS * 1e12))
+                                       / (a_ms * 1e-3), 4)})
+    if ach:
+        rec["mfma_frac_of_achievable"] = round(tf / ach["mfma_bf16_tflops"], 4)
+    return rec
+
+
+def tree_sub_record(w, steps, warmup, ach, label):
+    p = Pass(w)
+    ms = p.time_steps(steps, warmup)
+    attn_b, ver_b = algorithmic_bytes(w)
+    flops = attention_flops(w)
+    k_ms, kn = p.kernel_ms(2, min(steps, 10))
+    rec = {"workload": label, "nodes": w.N, "sequences": w.B, "ms_per_pass": round(ms, 4),
+           "nodes_per_s": round(w.N / (ms * 1e-3), 1), "algorithmic_bytes": attn_b + ver_b,
+           "algorithmic_flops": flops, "pass_gbs": round((attn_b + ver_b) / (ms * 1e-3) / 1e9, 1),
+           "pass_roofline_frac": round(max((attn_b + ver_b) / (HBM_PEAK_GBS * 1e9),
+                                           flops / (BF16_PEAK_TFLOPS * 1e12)) / (ms * 1e-3), 4),
+           "draft_rows_used": _used_draft_rows(w), "draft_k": int(w.draft_k),
+           "vocab_workers": roofline_hbm("vocab_worker_kernel", ver_b, k_ms, ach, launches=kn),
+           "attention_kernel": attention_record(p, flops, attn_b, min(steps, 10), ach)}
+    del p
+    return rec
+
+
+def presto_sub_record(w, steps, warmup, ach):
+    p = Pass(w)
+    ms = p.time_steps(steps, warmup, presto=True)
+    attn_b, _ = algorithmic_bytes(w)
+    flops = attention_flops(w)
+    rec = {"workload": "c4: " + w.info.get("description", ""), "requests": int(len(w.presto.cut)),
+           "query_tokens": w.N, "ms_per_pass": round(ms, 4), "algorithmic_bytes": attn_b,
+           "algorithmic_flops": flops,
+           "attention_kernel": attention_record(p, flops, attn_b, min(steps, 10), ach),
+           "presto_accept_ms": round(p.presto_ms(20), 4),
+           "note": "the 32 requests are 32 sequences whose block-table rows name the same prefix blocks"}
+    del p
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -125,14 +344,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--seed", type=int, default=10086)
     ap.add_argument("--workload", default="c3", choices=["c2", "c3", "c5"])
+    ap.add_argument("--draft-support", type=int, default=0,
+                    help="headline workload with sparse draft rows of this support (0: dense)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copies", type=int, default=2)
-    ap.add_argument("--separate", action="store_true",
-                    help="attention and verification as two calls with their own workspaces")
+    ap.add_argument("--no-sub", action="store_true", help="headline workload only (profiling runs)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (counter calibration)")
-    ap.add_argument("--attn-steps", type=int, default=20,
-                    help="attention-only calls timed after the main loop (the attention kernel's roofline)")
+    ap.add_argument("--kernel-steps", type=int, default=20,
+                    help="passes / attention-only calls timed by the library's kernel events")
     ap.add_argument("--print-sha", action="store_true",
                     help="print the SHA-256 of the vocabulary workers' sources and exit")
     args = ap.parse_args()
@@ -148,9 +367,9 @@ def main():
     import torch
 
     import tree_masked_verification_attn_amd as tav
-    from workloads import device as wdev
     from workloads import gen
 
+    tav.load()
     torch.cuda.set_device(0)
     if args.calib_copy_mib > 0:
         src = torch.ones(args.calib_copy_mib * 262144, dtype=torch.float32, device="cuda")
@@ -159,125 +378,52 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    w = gen.make(args.workload, args.seed)
-    copies = [wdev.upload(w, "cuda") for _ in range(max(1, args.copies))]
-    # verification's own workspaces (separate calls only)
-    ws_v = [torch.zeros_like(c.workspace) for c in copies] if args.separate else [None] * len(copies)
-    sa = torch.cuda.Stream()
-    sv = torch.cuda.Stream()
-    torch.cuda.synchronize()
 
-    def step(i, ev=None):
-        c = copies[i % len(copies)]
-        if not args.separate:
-            if ev is not None:
-                ev[0].record(sa)
-            tav.tav_tree_attn_verify(c.prob, c.tree, c.attn, c.verify, None, None, c.workspace, sa, sv)
-            if ev is not None:
-                ev[1].record(sa)
-            return
-        if ev is not None:
-            ev[0].record(sa)
-        tav.tav_tree_attention(c.prob, c.tree, c.attn, c.workspace, sa)
-        if ev is not None:
-            ev[1].record(sa)
-            ev[2].record(sv)
-        tav.tav_tree_verify(c.prob, c.tree, c.verify, ws_v[i % len(copies)], sv)
-        if ev is not None:
-            ev[3].record(sv)
+    ach = None if args.no_sub else achievable(os.path.dirname(tav.LIB_PATH))
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    # the timed steps: nothing but the calls (events between kernels cost a few microseconds each)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    for c, wv in zip(copies, ws_v):
-        bits = tav.tav_read_status(c.workspace) | (tav.tav_read_status(wv) if wv is not None else 0)
-        if bits:
-            raise RuntimeError(f"device status bits set: {tav.device_status_names(bits)}")
-
-    # then the same steps again with events: around each call, and (in the library) around the
-    # vocabulary workers' kernel on its stream, for that kernel's launch time
-    n_ev = min(args.steps, 20)
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_ev)]
-    tav.tav_kernel_timing(2)
-    torch.cuda.synchronize()
-    for i in range(n_ev):
-        step(i, events[i])
-    torch.cuda.synchronize()
-    kern_ms_total, kern_launches = tav.tav_kernel_timing_read()
-    tav.tav_kernel_timing(0)
-    kern_ms = kern_ms_total / max(1, kern_launches)
-    attn_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-    ver_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events])) if args.separate else None
-
-    # the attention kernel alone: attention-only calls on one stream, events around the kernel
-    a_ms = None
-    if args.attn_steps > 0:
-        for i in range(2):
-            c = copies[i % len(copies)]
-            tav.tav_tree_attention(c.prob, c.tree, c.attn, c.workspace, sa)
-        torch.cuda.synchronize()
-        tav.tav_kernel_timing(1)
-        for i in range(args.attn_steps):
-            c = copies[i % len(copies)]
-            tav.tav_tree_attention(c.prob, c.tree, c.attn, c.workspace, sa)
-        torch.cuda.synchronize()
-        a_total, a_n = tav.tav_kernel_timing_read()
-        tav.tav_kernel_timing(0)
-        a_ms = a_total / max(1, a_n)
-
-    ms = wall * 1e3 / args.steps
+    w = gen.make(args.workload, args.seed, draft_support=args.draft_support or None)
+    p = Pass(w)
+    ms = p.time_steps(args.steps, args.warmup)
+    kern_ms, kern_n = p.kernel_ms(2, min(args.steps, args.kernel_steps))
     attn_b, ver_b = algorithmic_bytes(w)
     flops = attention_flops(w)
+    attn_rec = attention_record(p, flops, attn_b, args.kernel_steps, ach) if args.kernel_steps > 0 else None
+    del p
     step_gbs = (attn_b + ver_b) / (ms * 1e-3) / 1e9
+    roof = roofline_hbm("vocab_worker_kernel (verification: logits and draft rows streamed per node)",
+                        ver_b, kern_ms, ach, traffic=measured_traffic(), launches=kern_n)
 
-    # roofline of the dominant kernel: the vocabulary workers (per launch = one step's verification)
-    kern_gbs = ver_b / (kern_ms * 1e-3) / 1e9
-    roof = {"kernel": "vocab_worker_kernel (verification: logits and draft rows streamed per node)",
-            "bound": "hbm", "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(kern_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-            "avg_launch_ms": round(kern_ms, 4), "launches_timed": kern_launches,
-            "algorithmic_bytes": ver_b}
-    attn_roof = None
-    if a_ms is not None:
-        a_gbs = attn_b / (a_ms * 1e-3) / 1e9
-        attn_roof = {"kernel": "attn_bf16_kernel (tree-masked attention, bf16 MFMA), attention-only calls",
-                     "bound": "hbm", "achieved": round(a_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(a_gbs / HBM_PEAK_GBS, 4), "avg_launch_ms": round(a_ms, 4),
-                     "launches_timed": args.attn_steps, "algorithmic_bytes": attn_b,
-                     "mfma_tflops": round(flops / (a_ms * 1e-3) / 1e12, 1),
-                     "mfma_frac": round(flops / (a_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
-    if args.separate:
-        other = {"mode": "separate calls", "attention_half_ms": round(attn_ms, 4),
-                 "attention_half_gbs": round(attn_b / (attn_ms * 1e-3) / 1e9, 1),
-                 "verify_half_ms": round(ver_ms, 4),
-                 "verify_half_gbs": round(ver_b / (ver_ms * 1e-3) / 1e9, 1)}
-    else:
-        other = {"mode": "one tav_tree_attn_verify call", "pass_event_ms": round(attn_ms, 4)}
+    subs = {}
+    if not args.no_sub:
+        sub_steps = max(5, min(args.steps, 20))
+        subs["c5_long_context"] = tree_sub_record(gen.make("c5", args.seed), sub_steps, 3, ach,
+                                                  "c5: " + gen.CONFIG_DESCRIPTIONS["c5"])
+        subs["c4_presto"] = presto_sub_record(gen.make("c4", args.seed), sub_steps, 3, ach)
+        if args.workload == "c3" and not args.draft_support:
+            subs["c3_sparse_draft_k128"] = tree_sub_record(
+                gen.make("c3", args.seed, draft_support=128), sub_steps, 3, ach,
+                "c3 with sparse draft rows: top-128 support per row (RheoSampling's sparse draft)")
+        torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w)
+        cpu = cpu_baseline(w, 1)
+        ncores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+        cpu["all_cores_run"] = cpu_baseline(w, ncores, min_seconds=5.0, max_passes=2)
 
-    desc = gen.CONFIG_DESCRIPTIONS[args.workload]
     line = {
         "metric": "tree nodes scored/sec (attn+verify) and achieved HBM GB/s vs MI355X peak",
         "value": round(w.N / (ms * 1e-3), 1), "unit": "nodes/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded)",
-        "config": {"workload": f"{args.workload}: {desc}", "seed": args.seed, "nodes": w.N,
+        "config": {"workload": f"{args.workload}: {w.info['description']}", "seed": args.seed, "nodes": w.N,
                    "sequences": w.B, "prefix_rows": int(np.sum(w.prefix_len)),
-                   "draft_rows": int(w.draft.shape[0]) if w.draft is not None else 0},
+                   "draft_rows_used": _used_draft_rows(w)},
         "step_gbs": round(step_gbs, 1), "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
         "step_algorithmic_bytes": attn_b + ver_b,
-        "roofline": roof, "attention_kernel": attn_roof, "kernels": other, "cpu_baseline": cpu,
+        "roofline": roof, "attention_kernel": attn_rec, "achievable": ach, "sub_records": subs,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 

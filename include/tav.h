@@ -102,7 +102,9 @@ enum {
   TAV_DEV_TOO_MANY_CHILDREN = 1u << 11, /* a node with more than 256 children */
   TAV_DEV_PRESTO_BAD_TREE = 1u << 12,   /* malformed prefetching tree / request ids */
   TAV_DEV_PLAN_MISMATCH = 1u << 13,     /* internal: device work plan differs from the host's */
-  TAV_DEV_BAD_TEMPERATURE = 1u << 14    /* a temperature that is not finite and > 0 */
+  TAV_DEV_BAD_TEMPERATURE = 1u << 14,   /* a temperature that is not finite and > 0 */
+  TAV_DEV_BAD_DRAFT = 1u << 15          /* sparse draft row: id outside [0, V), ids not strictly
+                                           ascending, or a value not finite and >= 0 */
 };
 
 /* Problem description (host struct). */
@@ -161,6 +163,11 @@ typedef struct tav_attn_io {
  *   temperature [B] > 0: p = softmax(logits / T);
  *   draft [R, V] float and draft_row [N]: row draft_row[v] is the (already
  *     tempered) distribution v's sampled child was drawn from; -1 if none;
+ *   or, with draft_k > 0, sparse rows (RheoSampling Section 3.2: the draft truncated to
+ *     its top entries before the softmax, so q~ is zero off a support of at most 128
+ *     tokens): draft_idx [R, draft_k] int32 support token ids in strictly ascending
+ *     order and draft_val [R, draft_k] float q~ at those ids (zeros allowed); draft is
+ *     then not read.  Verification reads K entries per row instead of V;
  *   uniforms [N, 2] in [0, 1): uniforms[c][0] tests node c as a candidate,
  *     uniforms[v][1] drives the final draw at v.
  * Outputs:
@@ -175,6 +182,9 @@ typedef struct tav_verify_io {
   const float* draft;
   int32_t num_draft_rows;
   const int32_t* draft_row;
+  const int32_t* draft_idx;
+  const float* draft_val;
+  int32_t draft_k;
   const float* uniforms;
   uint8_t* node_status;
   int32_t* path;

@@ -25,6 +25,6 @@ from .tree import tree_prep, ancestor_words  # noqa: F401
 from .attention import tree_attention, node_attention  # noqa: F401
 from .verify import (  # noqa: F401
     ACCEPTED, REJECTED, UNVISITED, UniformChooser, target_probs, rheo_verify_sequence,
-    verify_workload, inverse_cdf, node_terminal_stats,
+    verify_workload, inverse_cdf, node_terminal_stats, dense_draft_row,
 )
 from .presto import presto_states, presto_log_accept, presto_walk, presto_workload  # noqa: F401

@@ -207,7 +207,7 @@ def verify_workload(w, seqs=None):
 
         def qtilde_of(v, s=s):
             r = int(w.draft_row[s + v])
-            return None if r < 0 else np.asarray(w.draft[r], dtype=np.float64)
+            return None if r < 0 else dense_draft_row(w, r)
 
         ch = UniformChooser(w.uniforms[s:e])
         status, path, bonus = rheo_verify_sequence(w.parent[s:e], w.token[s:e], w.sampled[s:e],
@@ -215,6 +215,21 @@ def verify_workload(w, seqs=None):
         results.append({"status": status, "path": path, "bonus": bonus,
                         "decisions": ch.decisions})
     return results
+
+
+def dense_draft_row(w, r):
+    """Draft row r over the whole vocabulary in float64.  A sparse row (RheoSampling Section
+    3.2: the draft's logits truncated to their top entries before the softmax) is its support
+    values placed at their token ids, zero everywhere else -- the distribution the sampled
+    token was drawn from, so the verification rule applies to it unchanged."""
+    if getattr(w, "draft_k", 0):
+        q = np.zeros(w.V, dtype=np.float64)
+        idx = np.asarray(w.draft_idx[r], dtype=np.int64)
+        if len(set(idx.tolist())) != idx.size or idx.min() < 0 or idx.max() >= w.V:
+            raise ValueError("sparse draft row: support ids must be distinct tokens of the vocabulary")
+        q[idx] = np.asarray(w.draft_val[r], dtype=np.float64)
+        return q
+    return np.asarray(w.draft[r], dtype=np.float64)
 
 
 def _logits_f64(w, v):

@@ -154,7 +154,7 @@ def check_node_stats(w, got, nodes):
         det = [int(w.token[c]) for c in kids if not w.sampled[c]]
         has_s = any(w.sampled[c] for c in kids)
         dr = int(w.draft_row[v])
-        qt = w.draft[dr] if (has_s and dr >= 0) else None
+        qt = oracle.dense_draft_row(w, dr) if (has_s and dr >= 0) else None
         row = oracle.verify._logits_f64(w, v)
         M, S, Z, tok, (lo, hi) = node_terminal_stats(row, float(w.temperature[b]), qt, det,
                                                      float(w.uniforms[v][1]))

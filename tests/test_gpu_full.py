@@ -85,3 +85,17 @@ def test_full_size_presto(seed, split):
         picks += sorted({s, (s + e) // 2, e - 1})
     err = gu.check_attention(w, got, picks)
     _say("c4 attention max abs err", err, "over", len(picks), "query tokens")
+
+
+@pytest.mark.parametrize("name", ["c3", "c5"])
+def test_full_size_sparse_draft(name):
+    """The batched-verify and long-context workloads with sparse top-128 draft rows."""
+    _say("full sparse", name)
+    _cache.clear()
+    w = gen.make(name, 10086, draft_support=128)
+    got = gu.run(w, max_path=64)
+    assert got["status"] == 0, got["status"]
+    flagged = gu.check_verify(w, got)
+    _say(name, "sparse walks ok; near-tie flags", flagged)
+    gu.check_node_stats(w, got, _sample_nodes(w, 3, 7))
+    gu.check_attention(w, got, _sample_nodes(w, 1, 8))

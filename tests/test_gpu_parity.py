@@ -170,3 +170,46 @@ def test_many_sequences(B):
     gu.check_attention(w, got, list(range(0, w.N, 7)) + [w.N - 1])
     gu.check_verify(w, got)
     gu.check_node_stats(w, got, range(0, w.N, 97))
+
+
+SPARSE_CASES = {
+    # name: (tree, n_nodes, prefix_len, V, T, K, extra)
+    "random_k128": ("random", [64, 30, 9], [700, 129, 0], 20008, 1.0, 128, {}),
+    "eagle_k128": ("eagle", [40, 22], [2048, 300], 8192, 0.7, 128,
+                   {"max_depth": 6, "hybrid": "all", "draft_peak": (4.0, 7.0)}),
+    "star_k24": ("star", [40, 14], [33, 16], 4096, 0.9, 24, {}),
+    "random_k7_f32": ("random", [20, 9], [50, 3], 20004, 1.1, 7, {}),
+}
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+@pytest.mark.parametrize("case", sorted(SPARSE_CASES))
+def test_sparse_draft_rows(case, seed):
+    """Sparse top-K draft rows (RheoSampling Section 3.2): no second pass over the row; the walk
+    and every node's M, S, Z and would-be final draw match the oracle on the scattered rows."""
+    tree, n, L, V, T, K, extra = SPARSE_CASES[case]
+    _say("sparse draft", case, seed)
+    dtype = "f32" if case.endswith("f32") else "bf16"
+    Hq, Hkv, D = (4, 1, 64) if dtype == "f32" else (32, 8, 128)
+    w = gen.tree_batch(seed, B=len(n), prefix_len=L, tree=tree, n_nodes=n, Hq=Hq, Hkv=Hkv, D=D,
+                       dtype=dtype, V=V, temperature=T, draft_support=K, **extra)
+    assert w.draft_k == K and w.draft is None
+    got = gu.run(w)
+    assert got["status"] == 0, got["status"]
+    gu.check_attention(w, got, [v for b in range(w.B) for v in list(w.seq_nodes(b))[:3]])
+    gu.check_verify(w, got)
+    gu.check_node_stats(w, got, range(w.N))
+
+
+def test_sparse_draft_row_not_ascending():
+    import tree_masked_verification_attn_amd as tav
+
+    w = gen.tree_batch(4, B=3, prefix_len=[30, 40, 50], tree="random", n_nodes=[12, 15, 9], Hq=8, Hkv=2,
+                       D=128, dtype="bf16", V=4096, temperature=1.0, draft_support=32)
+    s = int(w.node_offsets[1])
+    r = int(w.draft_row[s])
+    w.draft_idx[r, 5], w.draft_idx[r, 6] = w.draft_idx[r, 6], w.draft_idx[r, 5]
+    got = gu.run(w)
+    assert got["status"] & (1 << 15), tav.device_status_names(got["status"])
+    assert int(got["path_len"][1]) == 0 and int(got["bonus"][1]) == -1
+    gu.check_verify(w, got, [0, 2])

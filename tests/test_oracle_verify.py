@@ -248,3 +248,48 @@ def test_terminal_stats_agree_with_walk_end():
         M, S, Z, tok, _ = node_terminal_stats(w.logits[s + v], w.temperature[b], qt, det,
                                               w.uniforms[s + v, 1])
         assert tok == r["bonus"]
+
+
+def _truncated(q, k):
+    """RheoSampling Section 3.2's sparse draft: the draft's logits kept at their k largest
+    entries before the softmax, i.e. q restricted to its top-k tokens and renormalised."""
+    keep = np.lexsort((np.arange(q.size), -q))[:k]
+    out = np.zeros_like(q)
+    out[keep] = q[keep]
+    return out / out.sum()
+
+
+@pytest.mark.parametrize("seed", range(5))
+@pytest.mark.parametrize("K,m,R,k", [(3, 1, 3, 3), (4, 0, 4, 2), (4, 2, 3, 4), (3, 1, 2, 4), (4, 1, 4, 5)])
+def test_one_layer_lossless_with_truncated_draft(seed, K, m, R, k):
+    """Verification with the truncated draft (tokens outside the support have q~ = 0, so the
+    residual (p - q~)+ keeps all their target mass) is still lossless: the emitted token follows
+    p exactly (RheoSampling Section 3.2: losslessness holds when verification uses the same
+    truncated distribution the draft was sampled from)."""
+    rng = np.random.default_rng(200 + seed)
+    V = 7
+    p = _dirichlet(rng, V)
+    q = _truncated(_dirichlet(rng, V), k)
+    dist, _ = _one_layer(p, q, K, m, R)
+    np.testing.assert_allclose(dist, p, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("tree", ["random", "eagle"])
+def test_sparse_rows_equal_their_dense_scatter(tree):
+    """The oracle's sparse draft rows are exactly the dense rows with zeros off the support: the
+    walk on a workload with sparse rows and on the same workload with each row scattered into a
+    dense one takes the same decisions and draws the same tokens."""
+    extra = {"max_depth": 4, "hybrid": "all", "draft_peak": (4.0, 7.0)} if tree == "eagle" else {}
+    w = gen.tree_batch(17, B=3, prefix_len=[5, 6, 7], tree=tree, n_nodes=[12, 20, 9], Hq=2, Hkv=1, D=8,
+                       dtype="f32", V=700, temperature=0.8, draft_support=24, **extra)
+    assert w.draft_k == 24 and w.draft is None
+    assert (np.diff(w.draft_idx, axis=1) > 0).all()
+    sparse = oracle.verify_workload(w)
+    dense = np.zeros((w.draft_idx.shape[0], w.V), np.float32)
+    for r in range(dense.shape[0]):
+        dense[r, w.draft_idx[r]] = w.draft_val[r]
+        assert np.count_nonzero(dense[r]) <= 24
+    w.draft, w.draft_k, w.draft_idx, w.draft_val = dense, 0, None, None
+    for a, b in zip(sparse, oracle.verify_workload(w)):
+        assert a["path"] == b["path"] and a["bonus"] == b["bonus"]
+        np.testing.assert_array_equal(a["status"], b["status"])

@@ -25,7 +25,7 @@ DEVICE_BITS = {
     0: "BAD_PARENT", 1: "TREE_TOO_LARGE", 2: "BAD_BLOCK", 3: "BAD_TOKEN", 4: "DUP_SIBLING_TOKEN",
     5: "MULTI_SAMPLED", 6: "NO_DRAFT", 7: "ZERO_DRAFT_MASS", 8: "NONFINITE_LOGITS",
     9: "EMPTY_RESIDUAL", 10: "PATH_OVERFLOW", 11: "TOO_MANY_CHILDREN", 12: "PRESTO_BAD_TREE",
-    13: "PLAN_MISMATCH", 14: "BAD_TEMPERATURE",
+    13: "PLAN_MISMATCH", 14: "BAD_TEMPERATURE", 15: "BAD_DRAFT",
 }
 ENTRY_POINTS = ("tav_workspace_size", "tav_tree_prep", "tav_tree_attention", "tav_tree_verify",
                 "tav_presto_accept", "tav_tree_attn_verify", "tav_read_status", "tav_kernel_timing",
@@ -61,7 +61,7 @@ class tav_attn_io(ctypes.Structure):
 
 class tav_verify_io(ctypes.Structure):
     _fields_ = [("logits", _p), ("temperature", _p), ("draft", _p), ("num_draft_rows", _i32),
-                ("draft_row", _p), ("uniforms", _p), ("node_status", _p), ("path", _p),
+                ("draft_row", _p), ("draft_idx", _p), ("draft_val", _p), ("draft_k", _i32), ("uniforms", _p), ("node_status", _p), ("path", _p),
                 ("max_path", _i32), ("path_len", _p), ("bonus_token", _p), ("node_stats", _p),
                 ("node_term_token", _p)]
 

@@ -57,7 +57,22 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}{r.stderr}")
     os.replace(tmp, LIB)
+    _build_probe()
     return LIB
+
+
+PROBE_SRC = os.path.join(CSRC, "probe", "roofline_probe.hip")
+PROBE_LIB = os.path.join(PKG, "libtavprobe.so")
+
+
+def _build_probe():
+    """The measurement library of the benchmark (a streaming-read and a matrix-core kernel)."""
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-shared", PROBE_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed:\n{' '.join(cmd)}\n{r.stdout}{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
 
 
 if __name__ == "__main__":

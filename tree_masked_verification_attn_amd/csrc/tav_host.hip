@@ -226,7 +226,11 @@ tav_status check_verify(const tav_problem* p, const tav_verify_io* io) {
       !io->path || !io->path_len || !io->bonus_token)
     return fail(TAV_ERR_NULL_POINTER, "a verification array is NULL");
   if (io->num_draft_rows < 0) return fail(TAV_ERR_BAD_SHAPE, "num_draft_rows must be >= 0");
-  if (io->num_draft_rows > 0 && !io->draft) return fail(TAV_ERR_NULL_POINTER, "draft is NULL");
+  if (io->draft_k < 0 || io->draft_k > kMaxDraftSupport)
+    return fail(TAV_ERR_UNSUPPORTED, "draft_k must be in [0, %d] (got %d)", kMaxDraftSupport, io->draft_k);
+  if (io->num_draft_rows > 0 && io->draft_k == 0 && !io->draft) return fail(TAV_ERR_NULL_POINTER, "draft is NULL");
+  if (io->num_draft_rows > 0 && io->draft_k > 0 && (!io->draft_idx || !io->draft_val))
+    return fail(TAV_ERR_NULL_POINTER, "draft_idx / draft_val are NULL (sparse draft rows)");
   if (io->max_path < 1) return fail(TAV_ERR_BAD_SHAPE, "max_path must be >= 1");
   if (p->vocab < 1) return fail(TAV_ERR_BAD_SHAPE, "vocab must be >= 1 for verification");
   const int epu = p->dtype == TAV_BF16 ? 8 : 4;
@@ -236,7 +240,7 @@ tav_status check_verify(const tav_problem* p, const tav_verify_io* io) {
   if (p->vocab > cap)
     return fail(TAV_ERR_UNSUPPORTED, "vocab %d exceeds the %lld tokens supported for this dtype",
                 p->vocab, (long long)cap);
-  if (!aligned16(io->logits) || !aligned16(io->draft))
+  if (!aligned16(io->logits) || (io->draft_k == 0 && !aligned16(io->draft)))
     return fail(TAV_ERR_INVALID_ARGUMENT, "logits and draft must be 16-byte aligned");
   return TAV_OK;
 }
@@ -349,6 +353,7 @@ VocabArgs vocab_args(const tav_problem* p, const Plan& P, const tav_tree* t, con
   uint32_t* status = ws_at<uint32_t>(ws, P.off_status);
   VocabArgs va;
   va.logits = io->logits; va.temperature = io->temperature; va.draft = io->draft;
+  va.draft_idx = io->draft_idx; va.draft_val = io->draft_val; va.K = io->draft_k;
   va.draft_row = io->draft_row; va.node_offsets = p->node_offsets; va.parent = t->parent;
   va.token = t->token; va.sampled = t->sampled; va.uniforms = io->uniforms;
   va.stats = io->node_stats ? io->node_stats : ws_at<float>(ws, P.off_stats);

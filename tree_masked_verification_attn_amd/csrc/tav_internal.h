@@ -16,6 +16,7 @@ constexpr int kMaskWords = 4;
 constexpr int kMaxChildren = 256;  // children of one node held by the verification kernels
 constexpr int kMaxChunks = 2048;   // chunks of 64 sixteen-byte units per vocabulary row
                                    // (V <= 1 Mi bf16 / 512 Ki f32 tokens)
+constexpr int kMaxDraftSupport = 128;  // tokens per sparse draft row
 constexpr int kCounterWord = 16;   // status block: word 0 = status bits, word 16 = the workers' node counter
 // Device-detected errors that make a sequence's attention rows sentinels (its tree or its prefix is
 // unusable); any device-detected error of a sequence makes its verification outputs sentinels.
@@ -105,7 +106,10 @@ struct AttnArgs {
 struct VocabArgs {
   const void* logits;
   const float* temperature;
-  const float* draft;
+  const float* draft;          // [R, V] dense draft rows (K == 0)
+  const int32_t* draft_idx;    // [R, K] sparse draft rows: support ids (ascending) ...
+  const float* draft_val;      // [R, K] ... and q~ there
+  int K;                       // sparse support size (0: dense rows)
   const int32_t* draft_row;
   const int32_t* node_offsets;
   const int32_t* parent;

@@ -24,8 +24,11 @@
 // row just read mostly hits the cache) and replaces the chunk weights with those of (p - q~)+.
 // The pick then runs on one wave: point values of the children, the deterministic children's
 // weights taken out of their chunks, an fp64 scan over the chunks for u * W, and one chunk re-read.
-// Nodes are taken from a device queue, in the order of an index list (nodes with a draft row first,
-// so that the long items do not come last); a worker never waits for another workgroup.
+// With sparse draft rows (at most 128 support tokens per row, RheoSampling Section 3.2) there is no
+// pass 2: the support's min(p, q~) is taken out of the chunk weights of p and Z is summed over the
+// support.  Nodes are taken from a device queue, in the order of an index list (nodes with a dense
+// draft row first, so that the long items do not come last); a worker never waits for another
+// workgroup.
 #pragma once
 
 #include "tav_internal.h"
@@ -65,7 +68,15 @@ struct Lds {
   float kid_w[kMaxChildren];                 // ... and their weights in the final draw's chunks
   int kid_cnt[C::kWaves];                    // children found by each wave in one round of the scan
   int item, cnt, nk, ns, err;
-  uint4 lc[C::kCacheUnits];                  // the row's first kCacheSteps steps (each thread its own units)
+  union {
+    uint4 lc[C::kCacheUnits];                // dense draft rows: the logits row's first kCacheSteps
+                                             // steps (each thread its own units)
+    struct {                                 // sparse draft rows: the node's support (ascending ids),
+      int idx[kMaxDraftSupport];             // q~ there and the part of each token's p taken out of
+      float val[kMaxDraftSupport];           // its chunk (min(p, q~))
+      float take[kMaxDraftSupport];
+    } sp;
+  };
 };
 
 template <typename LT>
@@ -295,7 +306,7 @@ __device__ void process_node(const VocabArgs& a, Lds<C>& L, int v) {
       }
       sd += (double)su[k];
     }
-    if (dr_ok && s < C::kCacheSteps) {
+    if (dr_ok && a.K == 0 && s < C::kCacheSteps) {
       // kept for the second pass, which reads them back in the same thread
 #pragma unroll
       for (int k = 0; k < kUnits; ++k) L.lc[s * kStepUnits + k * kThreads + tid] = cur[k];
@@ -331,8 +342,9 @@ __device__ void process_node(const VocabArgs& a, Lds<C>& L, int v) {
   const float invS = (float)(1.0 / S);
   const int nk = L.nk < kMaxChildren ? L.nk : kMaxChildren;
   const bool use_draft = L.ns > 0 && dr_ok;
+  const bool sparse = a.K > 0;
   double Zt = 0.0;
-  if (use_draft) {
+  if (use_draft && !sparse) {
     // ---- pass 2: chunk weights of (p - q~)+ and their total Z.  Each step is taken in two
     // halves of kUnits / 2 units per thread, one half computed while the other's loads fly.
     constexpr int HU = kUnits / 2;
@@ -401,6 +413,59 @@ __device__ void process_node(const VocabArgs& a, Lds<C>& L, int v) {
   if (L.ns > 1) err |= TAV_DEV_MULTI_SAMPLED;
   if (L.ns > 0 && !dr_ok) err |= TAV_DEV_NO_DRAFT;
   if (no_mass || !(S > 0.0 && S < INFINITY)) err |= TAV_DEV_NONFINITE_LOGITS;
+  // sparse draft row (RheoSampling Section 3.2: support of at most 128 tokens, q~ = 0 elsewhere):
+  // outside the support (p - q~)+ = p, so the chunk weights of p only lose min(p, q~) at the
+  // support tokens, and Z = sum (p - q~)+ = sum over the support of (q~ - p)+ (the two sides of
+  // the residual-mass identity, RheoSampling Appendix C Eq. 10) -- no second pass over the row.
+  const int K = a.K;
+  auto sp_q = [&](int tok) -> float {   // q~ at tok (binary search of the ascending support)
+    int lo = 0, hi = K;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (L.sp.idx[mid] < tok) lo = mid + 1; else hi = mid;
+    }
+    return lo < K && L.sp.idx[lo] == tok ? L.sp.val[lo] : 0.f;
+  };
+  if (use_draft && sparse) {
+    const int32_t* didx = a.draft_idx + (size_t)dr * K;
+    const float* dval = a.draft_val + (size_t)dr * K;
+    const LT* lrow = (const LT*)a.logits + (size_t)v * V;
+    double zl = 0.0;
+    for (int j = lane; j < K; j += 64) {
+      const int tk = didx[j];
+      const float qj = dval[j];
+      const int prev = j > 0 ? didx[j - 1] : -1;
+      const bool ok = tk >= 0 && tk < V && tk > prev && qj >= 0.f && qj < INFINITY;
+      float take = 0.f;
+      if (ok) {
+        const float p = __builtin_amdgcn_exp2f(logit_at<LT>(lrow, tk) * invTl2 - Ml2) * invS;
+        take = fminf(p, qj);
+        zl += (double)fmaxf(qj - p, 0.f);
+      } else {
+        err |= TAV_DEV_BAD_DRAFT;
+      }
+      L.sp.idx[j] = ok ? tk : -1;
+      L.sp.val[j] = ok ? qj : 0.f;
+      L.sp.take[j] = take;
+    }
+    Zt = wave_sum_d(zl);
+    wave_sync();
+    // each chunk's support tokens are consecutive entries; the last entry of a chunk's run sums the
+    // run in order and takes it out of the chunk (one lane per chunk, a fixed order of additions)
+    for (int j = lane; j < K; j += 64) {
+      const int tk = L.sp.idx[j];
+      if (tk < 0) continue;
+      const int c = tk / CT;
+      const int nx = j + 1 < K ? L.sp.idx[j + 1] : -1;
+      if (nx >= 0 && nx / CT == c) continue;
+      int j0 = j;
+      while (j0 > 0 && L.sp.idx[j0 - 1] >= 0 && L.sp.idx[j0 - 1] / CT == c) --j0;
+      float t = 0.f;
+      for (int i = j0; i <= j; ++i) t += L.sp.take[i];
+      L.cw[c] -= t;
+    }
+    wave_sync();
+  }
   // children: point values for the walk; deterministic children leave the final draw
   for (int k = lane; k < nk; k += 64) {
     const int tk = L.kid_tok[k];
@@ -409,7 +474,7 @@ __device__ void process_node(const VocabArgs& a, Lds<C>& L, int v) {
       if (L.kid_tok[k2] == tk) err |= TAV_DEV_DUP_SIBLING_TOKEN;
     if (tk >= 0 && tk < V) {
       const float z = logit_at<LT>(a.logits, (size_t)v * V + tk);
-      const float qz = dr_ok ? a.draft[(size_t)dr * V + tk] : 0.f;
+      const float qz = !use_draft ? 0.f : sparse ? sp_q(tk) : a.draft[(size_t)dr * V + tk];
       const int cid = s0 + L.kid_id[k];
       a.child_p[cid] = exp((double)(z * invT) - (double)M) / S;
       a.child_q[cid] = use_draft ? qz : 0.f;
@@ -471,7 +536,20 @@ __device__ void process_node(const VocabArgs& a, Lds<C>& L, int v) {
     const bool in = e0 < V;
     const uint4 ru = *(const uint4*)((const LT*)a.logits + (size_t)v * V + (in ? e0 : 0));
     float qv[EPU];
-    if (use_draft) {
+    if (use_draft && sparse) {
+      // the support entries inside the chosen chunk (a run of the ascending support)
+      int lo = 0, hi = K;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (L.sp.idx[mid] < pc * CT) lo = mid + 1; else hi = mid;
+      }
+#pragma unroll
+      for (int e = 0; e < EPU; ++e) {
+        qv[e] = 0.f;
+        for (int j = lo; j < K && L.sp.idx[j] >= 0 && L.sp.idx[j] < (pc + 1) * CT; ++j)
+          if (L.sp.idx[j] == e0 + e) qv[e] = L.sp.val[j];
+      }
+    } else if (use_draft) {
 #pragma unroll
       for (int i = 0; i < EPU / 4; ++i) {
         const float4 t = *(const float4*)(a.draft + (size_t)dr * V + (in ? e0 : 0) + 4 * i);

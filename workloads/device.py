@@ -54,11 +54,17 @@ def upload(w, device="cuda", with_verify=True, with_presto=True, max_path=None):
     ns.verify = None
     if with_verify and w.logits is not None:
         mp = max_path or 64
-        R = int(w.draft.shape[0])
+        R = int(w.draft.shape[0]) if w.draft is not None else 0
+        K = int(getattr(w, "draft_k", 0) or 0)
+        sparse = K > 0
+        R = int(w.draft_idx.shape[0]) if sparse else R
         ns.verify = SimpleNamespace(
             logits=_store_tensor(w.logits, w.dtype, device),
             temperature=_t(w.temperature, torch.float32, device),
-            draft=_t(w.draft if R else np.zeros((1, w.V), np.float32), torch.float32, device),
+            draft=None if sparse else _t(w.draft if R else np.zeros((1, w.V), np.float32), torch.float32, device),
+            draft_idx=_t(w.draft_idx if R else np.zeros((1, K), np.int32), torch.int32, device) if sparse else None,
+            draft_val=_t(w.draft_val if R else np.zeros((1, K), np.float32), torch.float32, device) if sparse else None,
+            draft_k=K,
             num_draft_rows=R, draft_row=_t(w.draft_row, torch.int32, device),
             uniforms=_t(w.uniforms, torch.float32, device),
             node_status=torch.full((N,), 9, dtype=torch.uint8, device=device),

@@ -99,6 +99,18 @@ def _draft_softmax(z: np.ndarray) -> np.ndarray:
     return e / e.sum()
 
 
+def _truncate(z: np.ndarray, k: Optional[int]):
+    """A draft row's logits kept at its k largest entries (ties: lower token id first), the
+    others set to -inf before the softmax (RheoSampling's sparse draft, Section 3.2); returns the
+    truncated logits and the kept token ids in ascending order (all ids when k is None)."""
+    if k is None or k >= z.size:
+        return z, np.arange(z.size)
+    keep = np.sort(_top_tokens(z, k))
+    out = np.full(z.size, -np.inf)
+    out[keep] = z[keep]
+    return out, keep
+
+
 # ----------------------------------------------------------------------------
 # containers
 # ----------------------------------------------------------------------------
@@ -147,8 +159,11 @@ class Workload:
     V: int = 0
     logits: Optional[np.ndarray] = None       # [N, V]
     temperature: Optional[np.ndarray] = None  # [B] f32
-    draft: Optional[np.ndarray] = None        # [R, V] f32
+    draft: Optional[np.ndarray] = None        # [R, V] f32 (dense draft rows), or None when sparse
     draft_row: Optional[np.ndarray] = None    # [N] i32, -1 if the node has no sampled child
+    draft_k: int = 0                          # sparse draft rows: support size K (0 = dense)
+    draft_idx: Optional[np.ndarray] = None    # [R, K] i32, support token ids, ascending
+    draft_val: Optional[np.ndarray] = None    # [R, K] f32, q~ at those tokens
     token: Optional[np.ndarray] = None        # [N] i32
     sampled: Optional[np.ndarray] = None      # [N] u8
     uniforms: Optional[np.ndarray] = None     # [N, 2] f32
@@ -326,7 +341,8 @@ def tree_batch(seed: int, *, B: int, prefix_len, tree: str, n_nodes, Hq: int, Hk
                dtype: str, V: int = 0, temperature: float = 1.0, logit_std: float = 3.0,
                draft_noise: float = 0.5, max_depth: int = 8, expand_k: int = 8,
                hybrid: str = "level", shuffle_blocks: bool = True, block_size: int = 16,
-               draft_peak=None, name: str = "custom") -> Workload:
+               draft_peak=None, draft_support: Optional[int] = None,
+               name: str = "custom") -> Workload:
     """A batch of B independent sequences, each a prefix in paged KV plus one
     token tree whose node 0 is the root (the last committed token).
 
@@ -343,13 +359,14 @@ def tree_batch(seed: int, *, B: int, prefix_len, tree: str, n_nodes, Hq: int, Hk
     if n_nodes.size == 1 and B > 1:
         n_nodes = np.full(B, int(n_nodes[0]))
 
-    parents, tokens, sampled_l, draft_rows_l, logits_l = [], [], [], [], []
+    parents, tokens, sampled_l, draft_rows_l, logits_l, supports_l = [], [], [], [], [], []
     have_verify = V > 0
     for b in range(B):
         n = int(n_nodes[b])
         if tree == "eagle":
-            par, tok, smp, dr, lg = _eagle_seq(seed, b, n, V, temperature, logit_std, draft_noise,
-                                               max_depth, expand_k, hybrid, dtype, draft_peak)
+            par, tok, smp, dr, lg, sup = _eagle_seq(seed, b, n, V, temperature, logit_std, draft_noise,
+                                                    max_depth, expand_k, hybrid, dtype, draft_peak,
+                                                    draft_support)
         else:
             if tree == "binary":
                 par = complete_binary_parents(n)
@@ -362,12 +379,13 @@ def tree_batch(seed: int, *, B: int, prefix_len, tree: str, n_nodes, Hq: int, Hk
             else:
                 raise ValueError(tree)
             if have_verify:
-                tok, smp, dr, lg = _decorate_first_child_sampled(seed, b, par, V, temperature,
-                                                                 logit_std, draft_noise, dtype)
+                tok, smp, dr, lg, sup = _decorate_first_child_sampled(seed, b, par, V, temperature,
+                                                                      logit_std, draft_noise, dtype,
+                                                                      draft_support)
             else:
-                tok = np.zeros(n, np.int64); smp = np.zeros(n, np.uint8); dr = {}; lg = None
+                tok = np.zeros(n, np.int64); smp = np.zeros(n, np.uint8); dr = {}; lg = None; sup = {}
         parents.append(par); tokens.append(tok); sampled_l.append(smp)
-        draft_rows_l.append(dr); logits_l.append(lg)
+        draft_rows_l.append(dr); logits_l.append(lg); supports_l.append(sup)
 
     node_offsets = np.zeros(B + 1, dtype=np.int32)
     node_offsets[1:] = np.cumsum([len(p) for p in parents])
@@ -390,13 +408,21 @@ def tree_batch(seed: int, *, B: int, prefix_len, tree: str, n_nodes, Hq: int, Hk
         w.token = np.concatenate(tokens).astype(np.int32)
         w.sampled = np.concatenate(sampled_l).astype(np.uint8)
         draft_row = np.full(N, -1, dtype=np.int32)
-        rows = []
+        rows, idx = [], []
         for b in range(B):
             for v_local in sorted(draft_rows_l[b]):
                 draft_row[node_offsets[b] + v_local] = len(rows)
                 rows.append(draft_rows_l[b][v_local])
+                idx.append(supports_l[b][v_local])
         w.draft_row = draft_row
-        w.draft = (np.stack(rows).astype(np.float32) if rows else np.zeros((0, V), np.float32))
+        if draft_support is None:
+            w.draft = (np.stack(rows).astype(np.float32) if rows else np.zeros((0, V), np.float32))
+        else:                      # sparse rows: the support ids (ascending) and q~ there
+            K = int(draft_support)
+            w.draft_k = K
+            w.draft_idx = (np.stack(idx).astype(np.int32) if idx else np.zeros((0, K), np.int32))
+            w.draft_val = (np.stack([r[i] for r, i in zip(rows, idx)]).astype(np.float32) if rows
+                           else np.zeros((0, K), np.float32))
         w.uniforms = _rng(seed, "uniforms").random((N, 2), dtype=np.float32)
     return w
 
@@ -407,11 +433,12 @@ def _node_logits(seed, b, key, V, std, dtype):
     return stored, (bf16_bits_to_f32(stored) if dtype == "bf16" else stored)
 
 
-def _decorate_first_child_sampled(seed, b, parent, V, T, std, noise, dtype):
-    """Per internal node v: draft q_v = softmax((l_v + N(0, noise)) / T).  The
-    lowest-id child is the sampled one (token ~ q_v, draft row = q_v); the other
-    children take the highest remaining draft tokens in child-id order (the
-    m = 0 hybrid pool).  The root's own token is arbitrary."""
+def _decorate_first_child_sampled(seed, b, parent, V, T, std, noise, dtype, support=None):
+    """Per internal node v: draft q_v = softmax((l_v + N(0, noise)) / T) (with ``support``,
+    the logits truncated to their ``support`` largest entries first).  The lowest-id child is
+    the sampled one (token ~ q_v, draft row = q_v); the other children take the highest
+    remaining draft tokens in child-id order (the m = 0 hybrid pool).  The root's own token
+    is arbitrary."""
     n = len(parent)
     stored, vals = [], []
     for v in range(n):
@@ -420,7 +447,7 @@ def _decorate_first_child_sampled(seed, b, parent, V, T, std, noise, dtype):
     token = np.zeros(n, dtype=np.int64)
     token[0] = int(_rng(seed, "root_token", b).integers(0, V))
     sampled = np.zeros(n, dtype=np.uint8)
-    drafts = {}
+    drafts, supports = {}, {}
     children = [[] for _ in range(n)]
     for c in range(1, n):
         children[parent[c]].append(c)
@@ -428,7 +455,8 @@ def _decorate_first_child_sampled(seed, b, parent, V, T, std, noise, dtype):
         if not children[v]:
             continue
         r = _rng(seed, "draft", b, v)
-        qv = _draft_softmax((vals[v].astype(np.float64) + noise * r.standard_normal(V)) / T)
+        zt, supports[v] = _truncate((vals[v].astype(np.float64) + noise * r.standard_normal(V)) / T, support)
+        qv = _draft_softmax(zt)
         q32 = qv.astype(np.float32)
         y = int(r.choice(V, p=qv))
         while q32[y] <= 0.0:              # the stored draft must give the sampled token mass
@@ -441,11 +469,13 @@ def _decorate_first_child_sampled(seed, b, parent, V, T, std, noise, dtype):
         rest = [int(t) for t in by_q[: len(kids) + 1] if int(t) != y][: len(kids) - 1]
         for c, t in zip(kids[1:], rest):
             token[c] = t
-    return token, sampled, drafts, np.stack(stored)
+    return token, sampled, drafts, np.stack(stored), supports
 
 
-def _eagle_seq(seed, b, n_nodes, V, T, std, noise, depth, expand_k, hybrid, dtype, peak=None):
+def _eagle_seq(seed, b, n_nodes, V, T, std, noise, depth, expand_k, hybrid, dtype, peak=None,
+               support=None):
     cache = {}
+    support_of = {}
 
     def logits_of(cid):
         if cid not in cache:
@@ -460,6 +490,7 @@ def _eagle_seq(seed, b, n_nodes, V, T, std, noise, depth, expand_k, hybrid, dtyp
             # a drafter's confident next token: its largest logit raised by U(peak) (the tree's
             # depth then comes from the budget, as with a trained drafter, not from flat rows)
             z[int(np.argmax(z))] += r.uniform(peak[0], peak[1])
+        z, support_of[cid] = _truncate(z, support)
         return _draft_softmax(z), _draft_softmax(z / T)
 
     tail_rng = _rng(seed, "tail", b)
@@ -483,7 +514,7 @@ def _eagle_seq(seed, b, n_nodes, V, T, std, noise, depth, expand_k, hybrid, dtyp
     token[0] = int(_rng(seed, "root_token", b).integers(0, V))
     logits = np.stack([logits_of(c)[0] for c in cids])
     drafts = {v: q.astype(np.float32) for v, q in draft_of.items()}
-    return parent, token, sampled, drafts, logits
+    return parent, token, sampled, drafts, logits, {v: support_of[cids[v]] for v in draft_of}
 
 
 # ----------------------------------------------------------------------------
@@ -576,7 +607,13 @@ def presto_batch(seed: int, *, T: int, n_pf: int, Hq: int, Hkv: int, D: int, dty
 DRAFT_PEAK = (4.0, 7.0)
 
 
-def make(name: str, seed: int = 10086) -> Workload:
+def make(name: str, seed: int = 10086, draft_support: Optional[int] = None) -> Workload:
+    """One of the five workloads; with draft_support (the tree workloads with verification),
+    its draft rows are sparse: the draft logits truncated to their top draft_support entries
+    before the softmax (RheoSampling Section 3.2), stored as (ids, values)."""
+    sp = {} if draft_support is None else {"draft_support": int(draft_support)}
+    if draft_support is not None and name not in ("c2", "c3", "c5"):
+        raise ValueError("sparse draft rows apply to the tree workloads c2, c3 and c5")
     if name == "c1":
         w = tree_batch(seed, B=1, prefix_len=128, tree="binary", n_nodes=15, Hq=4, Hkv=1, D=64,
                        dtype="f32", V=1000, temperature=1.0, logit_std=2.0, draft_noise=0.5,
@@ -584,21 +621,22 @@ def make(name: str, seed: int = 10086) -> Workload:
     elif name == "c2":
         w = tree_batch(seed, B=1, prefix_len=2048, tree="eagle", n_nodes=60, Hq=32, Hkv=8, D=128,
                        dtype="bf16", V=151936, temperature=0.7, logit_std=3.0, max_depth=6,
-                       expand_k=8, hybrid="level", draft_peak=DRAFT_PEAK, name="c2")
+                       expand_k=8, hybrid="level", draft_peak=DRAFT_PEAK, name="c2", **sp)
     elif name == "c3":
         L = _rng(seed, "prefix_lens").integers(1024, 8193, size=16).astype(np.int32)
         w = tree_batch(seed, B=16, prefix_len=L, tree="random", n_nodes=64, Hq=32, Hkv=8, D=128,
                        dtype="bf16", V=151936, temperature=1.0, logit_std=3.0, max_depth=8,
-                       name="c3")
+                       name="c3", **sp)
     elif name == "c4":
         w = presto_batch(seed, T=4096, n_pf=32, Hq=32, Hkv=8, D=128, dtype="bf16", alpha=4.0,
                          name="c4")
     elif name == "c5":
         w = tree_batch(seed, B=4, prefix_len=32768, tree="eagle", n_nodes=128, Hq=32, Hkv=8,
                        D=128, dtype="bf16", V=151936, temperature=1.0, logit_std=3.0,
-                       max_depth=10, expand_k=8, hybrid="all", draft_peak=DRAFT_PEAK, name="c5")
+                       max_depth=10, expand_k=8, hybrid="all", draft_peak=DRAFT_PEAK, name="c5", **sp)
     else:
         raise ValueError(name)
-    w.info["description"] = CONFIG_DESCRIPTIONS[name]
+    w.info["description"] = CONFIG_DESCRIPTIONS[name] + (
+        f", sparse draft rows (top-{draft_support} support)" if draft_support is not None else "")
     w.info["seed"] = seed
     return w
