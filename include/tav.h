@@ -160,7 +160,9 @@ typedef struct tav_attn_io {
 /* Verification inputs and outputs.
  *   logits [N, V] (problem dtype): target logits at each node (the distribution
  *     over the token that follows the node);
- *   temperature [B] > 0: p = softmax(logits / T);
+ *   temperature [B] >= 0: p = softmax(logits / T); T = 0 is greedy decoding (Progressive
+ *     Tree Drafting, Section 3.2: the child whose token is the argmax of its parent's logits
+ *     is accepted, the last node's argmax is the bonus token; draft rows are not read);
  *   draft [R, V] float and draft_row [N]: row draft_row[v] is the (already
  *     tempered) distribution v's sampled child was drawn from; -1 if none;
  *   or, with draft_k > 0, sparse rows (RheoSampling Section 3.2: the draft truncated to
@@ -226,6 +228,35 @@ typedef struct tav_presto_io {
   int32_t* pf_path;
   int32_t* pf_path_len;
 } tav_presto_io;
+
+/* Per-token scores of sampled tokens (PreSTO, Appendix D.3: the patched sampler returns, for
+ * each sampled token, its proposal log-probability under q_tau = softmax(l / tau), its base-model
+ * log-probability under p0 = softmax(l) from the unprocessed logits, and the full-vocabulary
+ * entropy of p0 in natural log -- the per-token inputs of log A, PreSTO Section 3.2 Example 3;
+ * Progressive Tree Drafting, Section 3.2: a node's greedy verification token is the argmax).
+ *   logits [num_rows, vocab] (dtype TAV_BF16 or TAV_F32, 16-byte aligned, vocab a multiple of 8
+ *     for bf16 and 4 for f32): the unprocessed logits of each row;
+ *   token [num_rows] (may be NULL: then log_p0 / log_q are not written): the sampled token;
+ *   tau > 0 finite: the proposal temperature;
+ * outputs (each may be NULL): log_p0 [num_rows], log_q [num_rows], entropy [num_rows] (float),
+ *   argmax [num_rows] (int32, smallest id among equal maxima; -1 for a row with no finite logit).
+ * Device-detected errors: a token outside [0, vocab) (TAV_DEV_BAD_TOKEN) or a NaN / +inf logit or
+ * a row with no finite logit (TAV_DEV_NONFINITE_LOGITS) make that row's scores NaN.  workspace:
+ * at least 256 bytes, 256-byte aligned (the status word; tav_read_status reads it). */
+typedef struct tav_score_io {
+  int32_t num_rows;
+  int32_t vocab;
+  int32_t dtype;
+  const void* logits;
+  const int32_t* token;
+  float tau;
+  float* log_p0;
+  float* log_q;
+  float* entropy;
+  int32_t* argmax;
+} tav_score_io;
+
+tav_status tav_token_scores(const tav_score_io* io, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace the calls below need for this problem (host only; no HIP
  * call).  presto may be NULL.  Errors: NULL pointer, bad shape. */

@@ -14,7 +14,9 @@ from the pages:
   Drafting, Section 3.2 and Appendix E);
 * PreSTO's log-acceptance and the MH walk over the prefetched subtree (PreSTO,
   Section 3.2 Example 3 / Equation 6, Appendix B.1 Equations 7-9, Appendix B.3
-  Example 5).
+  Example 5);
+* per-token scores of sampled tokens (log p0, log q_tau, entropy of p0; PreSTO
+  Appendix D.3) and greedy verification (Progressive Tree Drafting, Section 3.2).
 
 Only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import anything here.  The HIP library never does, and this
@@ -25,6 +27,7 @@ from .tree import tree_prep, ancestor_words  # noqa: F401
 from .attention import tree_attention, node_attention  # noqa: F401
 from .verify import (  # noqa: F401
     ACCEPTED, REJECTED, UNVISITED, UniformChooser, target_probs, rheo_verify_sequence,
-    verify_workload, inverse_cdf, node_terminal_stats, dense_draft_row,
+    verify_workload, inverse_cdf, node_terminal_stats, dense_draft_row, greedy_verify_sequence,
 )
 from .presto import presto_states, presto_log_accept, presto_walk, presto_workload  # noqa: F401
+from .scorer import token_scores, score_rows, argmax_token  # noqa: F401

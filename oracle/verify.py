@@ -158,6 +158,48 @@ def rheo_verify_sequence(parent, token, sampled, p_of, qtilde_of, chooser):
         return status, path, chooser.sample(v, r)
 
 
+def greedy_verify_sequence(parent, token, sampled, logits_of, decisions=None):
+    """Greedy verification (T = 0) of one tree, Progressive Tree Drafting Section 3.2: the
+    verification token of node n is its highest-probability prediction (the argmax of its
+    logits, smallest id among equal maxima); the edge to a child is eligible when the child's
+    token is that verification token; X' follows eligible edges from the root and ends with the
+    verification token of the last node.  The children are looked at in the stochastic walk's
+    order (sampled child first, then ascending id): each one passed over before the eligible
+    one is marked rejected.  Returns (status, path, token) like rheo_verify_sequence."""
+    from .scorer import argmax_token
+
+    n = len(parent)
+    children = [[] for _ in range(n)]
+    for c in range(1, n):
+        children[int(parent[c])].append(c)
+    status = np.zeros(n, dtype=np.uint8)
+    status[0] = ACCEPTED
+    path = [0]
+    v = 0
+    while True:
+        toks = [int(token[c]) for c in children[v]]
+        if len(set(toks)) != len(toks):
+            raise ValueError(f"children of node {v} repeat a token")
+        a = argmax_token(logits_of(v))
+        order = [c for c in children[v] if sampled[c]] + [c for c in children[v] if not sampled[c]]
+        nxt = None
+        for c in order:
+            hit = int(token[c]) == a
+            if decisions is not None:
+                decisions.append(("test", c, hit, False, None))
+            if hit:
+                nxt = c
+                break
+            status[c] = REJECTED
+        if nxt is None:
+            if decisions is not None:
+                decisions.append(("sample", v, a, False, None))
+            return status, path, a
+        status[nxt] = ACCEPTED
+        path.append(nxt)
+        v = nxt
+
+
 def node_terminal_stats(logits_row, temperature, qtilde, det_tokens, u1):
     """Vocabulary statistics of one node, as the walk would use them if it ended there.
 
@@ -190,7 +232,8 @@ def verify_workload(w, seqs=None):
     """Run the verification walk of every (or the given) sequence of a workload.
 
     Returns a list, per sequence, of dicts with node_status (sequence-local),
-    path (sequence-local ids), bonus token and the chooser's decision records.
+    path (sequence-local ids), bonus token and the chooser's decision records.  A sequence
+    with temperature 0 is verified greedily (greedy_verify_sequence).
     """
     if seqs is None:
         seqs = range(w.B)
@@ -209,6 +252,12 @@ def verify_workload(w, seqs=None):
             r = int(w.draft_row[s + v])
             return None if r < 0 else dense_draft_row(w, r)
 
+        if T == 0.0:                          # greedy decoding
+            dec = []
+            status, path, bonus = greedy_verify_sequence(w.parent[s:e], w.token[s:e], w.sampled[s:e],
+                                                         lambda v, s=s: _logits_f64(w, s + v), dec)
+            results.append({"status": status, "path": path, "bonus": bonus, "decisions": dec})
+            continue
         ch = UniformChooser(w.uniforms[s:e])
         status, path, bonus = rheo_verify_sequence(w.parent[s:e], w.token[s:e], w.sampled[s:e],
                                                    p_of, qtilde_of, ch)

@@ -126,6 +126,9 @@ def check_verify(w, got, seqs=None):
                 raise AssertionError(f"seq {b}: library stopped after {len(dec_g)} decisions, oracle has {len(dec_o)}")
             kg, ng, og = dec_g[k]
             assert (kg, ng) == (kind, node), f"seq {b} decision {k}: {dec_g[k]} vs oracle {d[:3]}"
+            if kind == "sample" and extra is None:      # greedy: the argmax, exactly
+                assert og == outcome, f"seq {b}: bonus {og} vs oracle {outcome}"
+                break
             if kind == "sample":
                 lo, hi, _F = extra
                 u = float(w.uniforms[int(w.node_offsets[b]) + node][1])
@@ -156,6 +159,11 @@ def check_node_stats(w, got, nodes):
         dr = int(w.draft_row[v])
         qt = oracle.dense_draft_row(w, dr) if (has_s and dr >= 0) else None
         row = oracle.verify._logits_f64(w, v)
+        if float(w.temperature[b]) == 0.0:              # greedy: M = max l, S = 1, Z = 0, argmax
+            gm, gs, gz = got["stats"][v]
+            assert gm == row.max() and gs == 1.0 and gz == 0.0, (v, gm, gs, gz)
+            assert int(got["term"][v]) == oracle.argmax_token(row), (v, int(got["term"][v]))
+            continue
         M, S, Z, tok, (lo, hi) = node_terminal_stats(row, float(w.temperature[b]), qt, det,
                                                      float(w.uniforms[v][1]))
         gm, gs, gz = got["stats"][v]

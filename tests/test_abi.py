@@ -186,3 +186,22 @@ def test_noalloc_rejects_problems_beyond_its_array():
                                           None, None, None, None, None)
     assert st == 4, tav.tav_last_error()
     assert "allocation-free" in tav.tav_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=5), 3), (dict(vocab=1001), 3), (dict(vocab=0), 2), (dict(num_rows=-1), 2),
+    (dict(tau=0.0), 6), (dict(tau=float("nan")), 6), (dict(logits=None), 1),
+])
+def test_token_scores_validation_codes(kw, code):
+    lib = tav.load()
+    buf = np.zeros(4096, np.uint8)
+    d = buf.ctypes.data + (-buf.ctypes.data) % 256
+    args = dict(num_rows=4, vocab=1024, dtype=tav.TAV_BF16, logits=d, token=None, tau=0.25, log_p0=None,
+                log_q=None, entropy=None, argmax=None)
+    args.update(kw)
+    io = tav.tav_score_io(**args)
+    st = lib.tav_token_scores(ctypes.byref(io), d, 256, None)
+    assert st == code, (st, tav.tav_last_error())
+    io = tav.tav_score_io(**dict(args, **{"logits": d}))
+    if code != 1:
+        assert lib.tav_token_scores(ctypes.byref(io), d, 100, None) in (code, 4)

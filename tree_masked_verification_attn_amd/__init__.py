@@ -29,8 +29,8 @@ DEVICE_BITS = {
 }
 ENTRY_POINTS = ("tav_workspace_size", "tav_tree_prep", "tav_tree_attention", "tav_tree_verify",
                 "tav_presto_accept", "tav_tree_attn_verify", "tav_read_status", "tav_kernel_timing",
-                "tav_kernel_timing_read", "tav_tree_attn_verify_noalloc", "tav_status_string",
-                "tav_last_error")
+                "tav_kernel_timing_read", "tav_tree_attn_verify_noalloc", "tav_token_scores",
+                "tav_status_string", "tav_last_error")
 NOALLOC_SCRATCH_BYTES = 64 << 20   # TAV_NOALLOC_SCRATCH_BYTES
 
 _p = ctypes.c_void_p
@@ -74,6 +74,11 @@ class tav_presto_io(ctypes.Structure):
                 ("pf_path_len", _p)]
 
 
+class tav_score_io(ctypes.Structure):
+    _fields_ = [("num_rows", _i32), ("vocab", _i32), ("dtype", _i32), ("logits", _p), ("token", _p),
+                ("tau", _f32), ("log_p0", _p), ("log_q", _p), ("entropy", _p), ("argmax", _p)]
+
+
 class TavError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
@@ -110,13 +115,14 @@ def load() -> ctypes.CDLL:
             ctypes.POINTER(tav_problem), ctypes.POINTER(tav_tree), ctypes.POINTER(tav_attn_io),
             ctypes.POINTER(tav_verify_io), ctypes.POINTER(tav_presto_io), ctypes.POINTER(tav_tree_out),
             _p, _p, _p]
+        lib.tav_token_scores.argtypes = [ctypes.POINTER(tav_score_io), _p, ctypes.c_size_t, _p]
         lib.tav_read_status.argtypes = [_p, _p, ctypes.POINTER(ctypes.c_uint32)]
         lib.tav_kernel_timing.argtypes = [ctypes.c_int]
         lib.tav_kernel_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i32)]
         lib.tav_status_string.argtypes = [ctypes.c_int]
         lib.tav_status_string.restype = ctypes.c_char_p
         lib.tav_last_error.restype = ctypes.c_char_p
-        for name in ENTRY_POINTS[:10]:
+        for name in ENTRY_POINTS[:11]:
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -254,6 +260,20 @@ def tav_tree_attn_verify_noalloc(prob: Problem, tree, attn, verify, presto, tree
     sv = _stream(verify_stream) if verify_stream is not None else sa
     _check(load().tav_tree_attn_verify_noalloc(ctypes.byref(ps), ctypes.byref(ts), ctypes.byref(ai), _ref(vi),
                                                _ref(pr), _ref(to), _ptr(status_out), sa, sv))
+
+
+def tav_token_scores(logits: torch.Tensor, token: Optional[torch.Tensor], tau: float, workspace: torch.Tensor,
+                     log_p0=None, log_q=None, entropy=None, argmax=None, stream=None):
+    """Per-token log p0, log q_tau, entropy of p0 and argmax of each row of logits [N, V]
+    (bfloat16 or float32); outputs are caller tensors of N elements (None: not written)."""
+    if logits.dim() != 2:
+        raise ValueError("logits must be [rows, vocab]")
+    dt = TAV_BF16 if logits.dtype == torch.bfloat16 else TAV_F32
+    io = tav_score_io(num_rows=logits.shape[0], vocab=logits.shape[1], dtype=dt, logits=_ptr(logits),
+                      token=_ptr(token), tau=float(tau), log_p0=_ptr(log_p0), log_q=_ptr(log_q),
+                      entropy=_ptr(entropy), argmax=_ptr(argmax))
+    _check(load().tav_token_scores(ctypes.byref(io), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream(stream)))
 
 
 def tav_read_status(workspace: torch.Tensor, stream=None) -> int:

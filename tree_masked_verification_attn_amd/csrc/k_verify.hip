@@ -79,6 +79,10 @@ __global__ __launch_bounds__(64) void walk_kernel(WalkArgs a) {
   __syncthreads();
   uint32_t err = 0;
   int plen = 1, v = 0, bonus = -1;
+  // temperature 0: greedy decoding (Progressive Tree Drafting, Section 3.2) -- the child whose
+  // token is the node's verification token (p = 1 there, 0 elsewhere) is accepted, the children
+  // passed over before it (sampled child first, then ascending id) are rejected
+  const bool greedy = a.temperature[b] == 0.f;
   if (lane == 0) {
     a.node_status[s0] = 1;
     a.path[(size_t)b * a.max_path] = 0;
@@ -103,7 +107,27 @@ __global__ __launch_bounds__(64) void walk_kernel(WalkArgs a) {
     for (int d = 32; d > 0; d >>= 1) s = max(s, __shfl_xor(s, d));
     if (nk > kMaxChildren) { err |= TAV_DEV_TOO_MANY_CHILDREN; break; }
     int next = -1;
-    if (lane == 0) {
+    if (lane == 0 && greedy) {
+      if (s >= 0) {
+        if (p_of(s) == 1.0) next = s;
+        else a.node_status[s0 + s] = 2;
+      }
+      for (int k = 0; k < nk && next < 0; ++k) {
+        const int c = kids[k];
+        if (c == s) continue;
+        if (p_of(c) == 1.0) next = c;
+        else a.node_status[s0 + c] = 2;
+      }
+      if (next >= 0) {
+        a.node_status[s0 + next] = 1;
+        if (plen >= a.max_path) err |= TAV_DEV_PATH_OVERFLOW;
+        else a.path[(size_t)b * a.max_path + plen] = next;
+        ++plen;
+      } else {
+        bonus = staged ? tt_s[v] : a.term_token[s0 + v];
+        if (bonus < 0) err |= TAV_DEV_EMPTY_RESIDUAL;
+      }
+    } else if (lane == 0) {
       bool resid = false;
       const double Zv = (double)(staged ? z_s[v] : a.stats[(size_t)(s0 + v) * 3 + 2]);
       if (s >= 0) {

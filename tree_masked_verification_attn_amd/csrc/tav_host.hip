@@ -634,6 +634,41 @@ tav_status tav_tree_attn_verify_noalloc(const tav_problem* prob, const tav_tree*
   return ok();
 }
 
+tav_status tav_token_scores(const tav_score_io* io, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!io) return fail(TAV_ERR_NULL_POINTER, "score io is NULL");
+  if (io->num_rows < 0 || io->vocab < 1) return fail(TAV_ERR_BAD_SHAPE, "num_rows must be >= 0 and vocab >= 1");
+  if (io->dtype != TAV_F32 && io->dtype != TAV_BF16)
+    return fail(TAV_ERR_UNSUPPORTED, "dtype must be TAV_F32 or TAV_BF16 (got %d)", io->dtype);
+  const int epu = io->dtype == TAV_BF16 ? 8 : 4;
+  if (io->vocab % epu)
+    return fail(TAV_ERR_UNSUPPORTED, "vocab must be a multiple of %d for this dtype (got %d)", epu, io->vocab);
+  if (io->num_rows > 0 && !io->logits) return fail(TAV_ERR_NULL_POINTER, "logits is NULL");
+  if (!aligned16(io->logits)) return fail(TAV_ERR_INVALID_ARGUMENT, "logits must be 16-byte aligned");
+  if (!(io->tau > 0.f) || !isfinite(io->tau)) return fail(TAV_ERR_INVALID_ARGUMENT, "tau must be finite and > 0");
+  Plan P;
+  P.off_status = 0;
+  P.total = 256;
+  tav_status st = check_ws(P, workspace, workspace_bytes);
+  if (st != TAV_OK) return st;
+  int cus = 0;
+  st = num_compute_units(&cus);
+  if (st != TAV_OK) return st;
+  ScoreArgs a;
+  a.logits = io->logits; a.token = io->token; a.tau = io->tau;
+  const float inv = 1.f / io->tau;
+  const int k = (int)lrintf(inv);
+  a.kpow = (k >= 1 && k <= 8 && fabsf(inv - (float)k) <= 1e-6f * inv) ? k : 0;
+  a.lp0 = io->token ? io->log_p0 : nullptr;
+  a.lq = io->token ? io->log_q : nullptr;
+  a.ent = io->entropy; a.argmax = io->argmax;
+  a.status = ws_at<uint32_t>(workspace, 0);
+  a.N = io->num_rows; a.V = io->vocab;
+  hipStream_t s = (hipStream_t)stream;
+  TAV_HIP(launch_start(a.status, nullptr, 0, nullptr, 0, 0, nullptr, s));
+  TAV_HIP(launch_score(a, io->dtype == TAV_BF16, cus, s));
+  return ok();
+}
+
 tav_status tav_read_status(const void* workspace, void* stream, uint32_t* status_bits) {
   if (!workspace || !status_bits) return fail(TAV_ERR_NULL_POINTER, "workspace / status_bits is NULL");
   TAV_HIP(hipStreamSynchronize((hipStream_t)stream));

@@ -170,6 +170,19 @@ struct PrestoArgs {
   uint32_t* status;
 };
 
+struct ScoreArgs {
+  const void* logits;      // [N, V]
+  const int32_t* token;    // [N] or null
+  float tau;               // proposal temperature
+  int kpow;                // 1 / tau when it is a whole number in 1..8, else 0
+  float* lp0;              // [N] outputs (each may be null)
+  float* lq;
+  float* ent;
+  int32_t* argmax;
+  uint32_t* status;
+  int N, V;
+};
+
 // Kernel launchers (defined next to their kernels).  They return the HIP error
 // of the launch.
 // Start of every call: status word, counters and the per-sequence error words seq_err[B] cleared;
@@ -200,6 +213,8 @@ hipError_t launch_attn_sentinel_f32(const Plan& p, const AttnArgs& a, hipStream_
 // Vocabulary workers: one 512-thread workgroup per compute unit, persistent over the node queue.
 hipError_t launch_vocab(const VocabArgs& a, bool bf16_logits, int num_cus, hipStream_t s);
 hipError_t launch_walk(const WalkArgs& a, hipStream_t s);
+// Per-token scores: one 512-thread workgroup per row, persistent over the rows.
+hipError_t launch_score(const ScoreArgs& a, bool bf16, int num_cus, hipStream_t s);
 hipError_t launch_presto(const PrestoArgs& a, hipStream_t s);
 
 }  // namespace tav

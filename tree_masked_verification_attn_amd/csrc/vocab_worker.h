@@ -67,6 +67,8 @@ struct Lds {
   uint8_t kid_smp[kMaxChildren];             // ... and sampled flags
   float kid_w[kMaxChildren];                 // ... and their weights in the final draw's chunks
   int kid_cnt[C::kWaves];                    // children found by each wave in one round of the scan
+  float g_best[C::kWaves];                   // greedy rows: each wave's largest logit ...
+  int g_idx[C::kWaves];                      // ... and its smallest token id
   int item, cnt, nk, ns, err;
   union {
     uint4 lc[C::kCacheUnits];                // dense draft rows: the logits row's first kCacheSteps
@@ -205,6 +207,97 @@ __device__ inline void load_step(uint4 (&r)[C::kUnits], const LT* row, int step,
   }
 }
 
+// (value, token id) pairs: the larger value wins, equal values go to the smaller id.
+__device__ inline void better_of(float& best, int& bi, float ob, int oi) {
+  if (ob > best || (ob == best && (unsigned)oi < (unsigned)bi)) {
+    best = ob;
+    bi = oi;
+  }
+}
+
+// Greedy decoding (temperature 0; Progressive Tree Drafting, Section 3.2): the node's verification
+// token is its highest-probability prediction, the argmax of the logits (smallest id among equal
+// maxima).  One pass over the row (the first step's loads already in flight in cur) with no
+// exponentials; the walk accepts the child carrying that token.  Stats: M = max l, S = 1, Z = 0;
+// p at a child's token is 1 for the argmax and 0 otherwise; the would-be final token is the argmax.
+template <typename LT, class C>
+__device__ void greedy_node(const VocabArgs& a, Lds<C>& L, int v, int b, int s0, uint4 (&cur)[C::kUnits],
+                            const LT* row, int nunits, int nsteps) {
+  constexpr int kThreads = C::kThreads, kUnits = C::kUnits, kStepUnits = C::kStepUnits;
+  constexpr int EPU = 16 / sizeof(LT);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int V = a.V;
+  float best = -INFINITY;
+  int bi = -1;
+  bool bad = false;
+  for (int s = 0; s < nsteps; ++s) {
+    uint4 nxt[kUnits];
+    if (s + 1 < nsteps) load_step<LT, C>(nxt, row, s + 1, tid, nunits);
+    // a thread's positions rise with (step, unit, element), so a strict > keeps the smallest id
+#pragma unroll
+    for (int k = 0; k < kUnits; ++k) {
+      const int u = s * kStepUnits + k * kThreads + tid;
+      if (u < nunits) {
+#pragma unroll
+        for (int e = 0; e < EPU; ++e) {
+          const float x = unit_elem<LT>(cur[k], e);
+          bad |= !(x < INFINITY);   // +inf or NaN
+          if (x > best) {
+            best = x;
+            bi = u * EPU + e;
+          }
+        }
+      }
+    }
+    if (s + 1 < nsteps) {
+#pragma unroll
+      for (int k = 0; k < kUnits; ++k) cur[k] = nxt[k];
+    }
+  }
+#define TAV_GREEDY_STAGE(S)                                                                  \
+  better_of(best, bi, lane_move_f<S>(best), (int)lane_move<S>((uint32_t)bi));
+  TAV_GREEDY_STAGE(1) TAV_GREEDY_STAGE(2) TAV_GREEDY_STAGE(3) TAV_GREEDY_STAGE(4) TAV_GREEDY_STAGE(5)
+  TAV_GREEDY_STAGE(6)
+#undef TAV_GREEDY_STAGE
+  const bool any_bad = __ballot(bad) != 0ull;
+  if (lane == 0) {
+    L.g_best[wave] = best;
+    L.g_idx[wave] = bi;
+    if (any_bad) atomicOr(&L.err, (int)TAV_DEV_NONFINITE_LOGITS);
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  float M = -INFINITY;
+  int A = -1;
+#pragma unroll
+  for (int w = 0; w < C::kWaves; ++w) better_of(M, A, L.g_best[w], L.g_idx[w]);
+  uint32_t err = (uint32_t)L.err;
+  if (L.nk > kMaxChildren) err |= TAV_DEV_TOO_MANY_CHILDREN;
+  if (M == -INFINITY) err |= TAV_DEV_NONFINITE_LOGITS;   // no finite logit: no prediction
+  const int nk = L.nk < kMaxChildren ? L.nk : kMaxChildren;
+  for (int k = lane; k < nk; k += 64) {
+    const int tk = L.kid_tok[k];
+    if (tk < 0 || tk >= V) err |= TAV_DEV_BAD_TOKEN;
+    for (int k2 = 0; k2 < k; ++k2)
+      if (L.kid_tok[k2] == tk) err |= TAV_DEV_DUP_SIBLING_TOKEN;
+    const int cid = s0 + L.kid_id[k];
+    a.child_p[cid] = tk == A ? 1.0 : 0.0;
+    a.child_q[cid] = 0.f;
+  }
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) err |= (uint32_t)__shfl_xor((int)err, d);
+  if (lane == 0) {
+    a.stats[(size_t)v * 3 + 0] = M;
+    a.stats[(size_t)v * 3 + 1] = 1.f;
+    a.stats[(size_t)v * 3 + 2] = 0.f;
+    a.term_token[v] = M == -INFINITY ? -1 : A;
+    if (err) {
+      atomicOr(a.status, err);
+      atomicOr(a.seq_err + b, err);
+    }
+  }
+}
+
 // Everything the walk needs of node v.
 template <typename LT, class C>
 __device__ void process_node(const VocabArgs& a, Lds<C>& L, int v) {
@@ -276,8 +369,12 @@ __device__ void process_node(const VocabArgs& a, Lds<C>& L, int v) {
       __syncthreads();   // kid_cnt is reused by the next round
     }
     if (tid == 0) L.nk = nk;
-    if (tid == 0 && !(Tb > 0.f && Tb < INFINITY)) err |= TAV_DEV_BAD_TEMPERATURE;
+    if (tid == 0 && !(Tb >= 0.f && Tb < INFINITY)) err |= TAV_DEV_BAD_TEMPERATURE;
     if (err) atomicOr(&L.err, (int)err);
+  }
+  if (Tb == 0.f) {   // greedy decoding: the verification token is the argmax
+    greedy_node<LT, C>(a, L, v, b, s0, cur, row, nunits, nsteps);
+    return;
   }
   // ---- pass 1: per-piece references and sums, chunk weights relative to their piece
   float* part = L.part[wave];
