@@ -23,11 +23,14 @@ verification) on the headline workload, plus
     rate on this GPU (the fractions of those beside the fractions of the published peaks);
   * sub_records: the same measurements for the long-context workload (4 x 32768 prefix,
     128-node depth-10 trees), the PreSTO prefetch batch (attention MFMA utilisation,
-    log A + walk time) and the headline workload with sparse top-128 draft rows;
+    log A + walk time), the per-token scorer over that batch's scored tokens, the headline
+    workload with sparse top-128 draft rows and at temperature 0 (greedy verification), and
+    the host prefetch-tree builder;
   * cpu_baseline: the oracle on a bounded sample of the headline workload, on the host.
 """
 
 import argparse
+import copy
 import json
 import os
 import platform
@@ -47,11 +50,14 @@ KERNEL_SOURCES = [os.path.join(ROOT, "tree_masked_verification_attn_amd", "csrc"
 
 
 def _used_draft_rows(w):
-    """Nodes whose draft row verification reads: a sampled child and a draft row."""
+    """Nodes whose draft row verification reads: a sampled child and a draft row, in a sequence
+    verified at a temperature above 0 (greedy verification reads no draft row)."""
     import numpy as np
 
     has_s = np.zeros(w.N, bool)
     for b in range(w.B):
+        if w.temperature is not None and float(w.temperature[b]) == 0.0:
+            continue
         s = int(w.node_offsets[b])
         for c in range(s + 1, int(w.node_offsets[b + 1])):
             if w.sampled[c]:
@@ -323,6 +329,8 @@ def tree_sub_record(w, steps, warmup, ach, label):
 
 
 def presto_sub_record(w, steps, warmup, ach):
+    """The PreSTO batch: the whole pass (tree attention of every suffix token + log A + walk), the
+    attention kernel alone, tav_presto_accept alone."""
     p = Pass(w)
     ms = p.time_steps(steps, warmup, presto=True)
     attn_b, _ = algorithmic_bytes(w)
@@ -334,6 +342,59 @@ def presto_sub_record(w, steps, warmup, ach):
            "presto_accept_ms": round(p.presto_ms(20), 4),
            "note": "the 32 requests are 32 sequences whose block-table rows name the same prefix blocks"}
     del p
+    return rec
+
+
+def scorer_record(seed, rows, V=151936, tau=0.25, reps=5):
+    """tav_token_scores over `rows` bf16 logits rows of V tokens drawn on the device (the PreSTO
+    batch's scored tokens: every suffix token and every token of the state), one launch per rep."""
+    import numpy as np
+    import torch
+
+    import tree_masked_verification_attn_amd as tav
+    from workloads import gen
+
+    logits = gen.device_logits(seed, rows, V)
+    tok = torch.from_numpy(np.random.default_rng(seed).integers(0, V, rows).astype(np.int32)).cuda()
+    outs = [torch.empty(rows, device="cuda") for _ in range(3)]
+    am = torch.empty(rows, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(64, dtype=torch.float64, device="cuda")
+    s = torch.cuda.Stream()
+    tav.tav_token_scores(logits, tok, tau, ws, *outs, am, stream=s)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record(s)
+        tav.tav_token_scores(logits, tok, tau, ws, *outs, am, stream=s)
+        e1.record(s)
+    torch.cuda.synchronize()
+    if tav.tav_read_status(ws, s):
+        raise RuntimeError("token scorer status bits set")
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)[reps // 2]
+    nbytes = rows * V * 2 + rows * (4 + 3 * 4 + 4)
+    del logits
+    torch.cuda.empty_cache()
+    rec = roofline_hbm("score_kernel (log p0, log q_tau, entropy, argmax per row)", nbytes, ms, None,
+                       launches=reps)
+    rec.update({"rows": rows, "vocab": V, "tau": tau, "tokens_per_s": round(rows / (ms * 1e-3), 1)})
+    return rec
+
+
+def prefetch_builder_record(seed, reps=200):
+    """Host time of tav_prefetch_build at the PreSTO batch's shape (T = 4096, N_pf = 32, K' = 100),
+    both rules, and each tree's predicted transition count."""
+    import tree_masked_verification_attn_amd as tav
+
+    w = [1.0, -3.0, -1.0, 2.5, 0.0, 0.0]
+    rec = {"shape": "T = 4096, N_pf = 32, depth cap 100; class weights (bias, slope) = "
+                    "(1, -3) reject, (-1, 2.5) accept, (0, 0) uncertain"}
+    for name, rule in (("bfs", tav.TAV_PREFETCH_BFS), ("predictive", tav.TAV_PREFETCH_PREDICTIVE)):
+        t0 = time.perf_counter()
+        for i in range(reps):
+            t = tav.tav_prefetch_build(4096, 32, 100, rule, seed + i, w)
+        us = (time.perf_counter() - t0) * 1e6 / reps
+        rec[name] = {"us_per_build": round(us, 1), "nodes": int(len(t["parent"])),
+                     "requests": int(len(t["request_cut"])),
+                     "predicted_transitions": round(float(t["predicted_transitions"]), 4)}
     return rec
 
 
@@ -398,11 +459,19 @@ def main():
         sub_steps = max(5, min(args.steps, 20))
         subs["c5_long_context"] = tree_sub_record(gen.make("c5", args.seed), sub_steps, 3, ach,
                                                   "c5: " + gen.CONFIG_DESCRIPTIONS["c5"])
-        subs["c4_presto"] = presto_sub_record(gen.make("c4", args.seed), sub_steps, 3, ach)
+        w4 = gen.make("c4", args.seed)
+        subs["c4_presto"] = presto_sub_record(w4, sub_steps, 3, ach)
+        subs["c4_token_scores"] = scorer_record(args.seed, w4.N + w4.presto.T)
+        del w4
+        wg = copy.copy(w)
+        wg.temperature = np.zeros_like(w.temperature)
+        subs["c3_greedy"] = tree_sub_record(wg, sub_steps, 3, ach,
+                                            "c3 at temperature 0: greedy verification (argmax verification tokens)")
         if args.workload == "c3" and not args.draft_support:
             subs["c3_sparse_draft_k128"] = tree_sub_record(
                 gen.make("c3", args.seed, draft_support=128), sub_steps, 3, ach,
                 "c3 with sparse draft rows: top-128 support per row (RheoSampling's sparse draft)")
+        subs["prefetch_builder_host"] = prefetch_builder_record(args.seed)
         torch.cuda.empty_cache()
 
     cpu = None

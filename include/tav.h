@@ -258,6 +258,64 @@ typedef struct tav_score_io {
 
 tav_status tav_token_scores(const tav_score_io* io, void* workspace, size_t workspace_bytes, void* stream);
 
+/* PreSTO's prefetching tree for one batch (host only, no HIP call; PreSTO Section 3.2 step (1)
+ * and Appendix C).  Node v holds an MH state with cut c_v (node 0, the root: the current state,
+ * cut T); expanding v creates an acceptance child carrying a suffix-resampling request whose cut
+ * is drawn uniformly from {0..T-1}, and a rejection child that keeps v's state and cut; the request
+ * joins this batch iff its cut <= c_v (Condition 1), else it is deferred.
+ *   TAV_PREFETCH_BFS: breadth-first expansion until `budget` requests or an empty queue (a deferred
+ *     acceptance child is created but not expanded; the rejection child is always queued).
+ *   TAV_PREFETCH_PREDICTIVE: the selection of at most `budget` candidate nodes (depth < depth_cap,
+ *     Condition 1 at the node and at every ancestor) maximising the predicted number of completed
+ *     transitions (Equation 17: the sum of predicted reaching weights, Equation 11, with branch
+ *     probability (1 + P(accept) - P(reject)) / 2, Equation 14, from a three-class logistic
+ *     regression on the cut fraction c/T); the tree is the root and both children of each
+ *     selected node.  The optimum of Equation 19.
+ * Nodes are named by heap index (root 1, acceptance child 2h, rejection child 2h + 1) and listed in
+ * ascending heap index (so parent < child); the cut of the acceptance child with heap index h is
+ * floor(U * T) with U the top 53 bits, over 2^53, of SplitMix64 (Steele, Lea and Flood) at state
+ * seed + h * 0x9E3779B97F4A7C15.  Requests are numbered in node order.  The output arrays feed
+ * tav_presto_io (pf_parent, pf_is_accept, pf_request; request_cut = cut of each request).
+ * Errors: NULL arrays, budget outside [1, 62], T or depth_cap < 1, capacity < 2 * budget + 1 or
+ * outgrown, non-finite class weights (all host-checked). */
+enum { TAV_PREFETCH_BFS = 0, TAV_PREFETCH_PREDICTIVE = 1 };
+
+typedef struct tav_prefetch_params {
+  int32_t T;           /* state length */
+  int32_t budget;      /* N_pf: at most this many requests */
+  int32_t depth_cap;   /* K' = K - k: only nodes of depth < K' are expanded */
+  int32_t rule;        /* TAV_PREFETCH_BFS or TAV_PREFETCH_PREDICTIVE */
+  uint64_t seed;       /* cut draws */
+  float class_w[6];    /* (bias, slope) on c/T for the classes certain reject, certain accept, uncertain */
+} tav_prefetch_params;
+
+typedef struct tav_prefetch_out {
+  int32_t capacity;               /* entries of the node arrays: 2 * budget + 1 suffices for the
+                                     predictive rule; a BFS expansion whose request is deferred adds
+                                     two nodes but no request, so BFS trees can be larger
+                                     (TAV_ERR_BAD_SHAPE when the tree outgrows capacity) */
+  int32_t num_nodes;              /* out */
+  int32_t num_requests;           /* out */
+  int32_t* parent;                /* [capacity] host arrays */
+  uint8_t* is_accept;
+  int32_t* request;               /* request id of an acceptance child in this batch, else -1 */
+  int32_t* cut;                   /* cut of every node (the root: T) */
+  int64_t* heap;                  /* [capacity] optional: heap index of every node */
+  int32_t* request_cut;           /* [budget] optional: cut of every request */
+  double predicted_transitions;   /* out: sum of predicted reaching weights of the expanded nodes */
+} tav_prefetch_out;
+
+tav_status tav_prefetch_build(const tav_prefetch_params* params, tav_prefetch_out* out);
+
+/* After scoring (host only): epsilon-rounded branch probabilities h(v+) = 0 if A <= eps, 1 if
+ * A >= 1 - eps, else A with A = exp(log_accept) (PreSTO Appendix C Equation 10), reaching weights
+ * R(root) = 1, R(v+-) = R(v) h(v+-) (Equation 11) and the expected number of completed transitions
+ * F = sum of R over the nodes whose acceptance child carries a request of this batch (Lemma 1,
+ * Equation 12).  parent < child, node 0 the root; reach [num_nodes] optional.  eps in [0, 1/2). */
+tav_status tav_prefetch_reach(int32_t num_nodes, const int32_t* parent, const uint8_t* is_accept,
+                              const int32_t* request, int32_t num_requests, const float* log_accept,
+                              float eps, double* reach, double* expected_transitions);
+
 /* Bytes of workspace the calls below need for this problem (host only; no HIP
  * call).  presto may be NULL.  Errors: NULL pointer, bad shape. */
 tav_status tav_workspace_size(const tav_problem* prob, const tav_presto_io* presto, size_t* bytes);

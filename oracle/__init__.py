@@ -16,7 +16,9 @@ from the pages:
   Section 3.2 Example 3 / Equation 6, Appendix B.1 Equations 7-9, Appendix B.3
   Example 5);
 * per-token scores of sampled tokens (log p0, log q_tau, entropy of p0; PreSTO
-  Appendix D.3) and greedy verification (Progressive Tree Drafting, Section 3.2).
+  Appendix D.3) and greedy verification (Progressive Tree Drafting, Section 3.2);
+* the prefetching tree of a PreSTO batch (BFS and predictive rules, rounded and
+  predicted reaching weights; PreSTO Section 3.2 step (1), Appendix C).
 
 Only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import anything here.  The HIP library never does, and this
@@ -31,3 +33,4 @@ from .verify import (  # noqa: F401
 )
 from .presto import presto_states, presto_log_accept, presto_walk, presto_workload  # noqa: F401
 from .scorer import token_scores, score_rows, argmax_token  # noqa: F401
+from . import prefetch  # noqa: F401

@@ -213,3 +213,37 @@ def test_sparse_draft_row_not_ascending():
     assert got["status"] & (1 << 15), tav.device_status_names(got["status"])
     assert int(got["path_len"][1]) == 0 and int(got["bonus"][1]) == -1
     gu.check_verify(w, got, [0, 2])
+
+
+@pytest.mark.parametrize("rule", [0, 1])
+@pytest.mark.parametrize("seed", SEEDS)
+def test_presto_batch_from_prefetch_builder(rule, seed):
+    """A prefetch batch whose tree comes from tav_prefetch_build (BFS or predictive rule): its
+    arrays feed tav_presto_io directly; log A and the walk match the oracle."""
+    import tree_masked_verification_attn_amd as tav
+
+    T = 512
+    t = tav.tav_prefetch_build(T, 24, 40, rule, seed, [1.0, -3.0, -1.0, 2.5, 0.0, 0.0])
+    rng = np.random.default_rng(seed)
+    cuts = t["request_cut"].astype(np.int32)
+    off = np.zeros(len(cuts) + 1, np.int32)
+    off[1:] = np.cumsum(T - cuts)
+    pr = gen.PrestoInputs(
+        T=T, alpha=4.0, root_lp0=(-rng.exponential(size=T)).astype(np.float32),
+        root_lq=(-rng.exponential(size=T)).astype(np.float32), cut=cuts, suffix_off=off,
+        lp0=(-rng.exponential(size=int(off[-1]))).astype(np.float32),
+        lq=(-rng.exponential(size=int(off[-1]))).astype(np.float32),
+        pf_parent=t["parent"], pf_is_accept=t["is_accept"], pf_request=t["request"], pf_cut=t["cut"],
+        u=rng.random(len(t["parent"]), dtype=np.float32), max_transitions=30)
+    w = gen.presto_batch(seed, T=8, n_pf=1, Hq=8, Hkv=2, D=128, with_attention=False)
+    w.presto = pr
+    from workloads import device as wdev
+
+    d = wdev.upload(w, "cuda")
+    tav.tav_presto_accept(d.presto, d.workspace)
+    status = tav.tav_read_status(d.workspace)
+    assert status == 0, status
+    got = {"logA": d.presto.log_accept.cpu().numpy().astype(np.float64),
+           "pf_path": d.presto.pf_path.cpu().numpy(),
+           "pf_path_len": int(d.presto.pf_path_len.cpu().numpy()[0])}
+    gu.check_presto(w, got)

@@ -30,7 +30,8 @@ DEVICE_BITS = {
 ENTRY_POINTS = ("tav_workspace_size", "tav_tree_prep", "tav_tree_attention", "tav_tree_verify",
                 "tav_presto_accept", "tav_tree_attn_verify", "tav_read_status", "tav_kernel_timing",
                 "tav_kernel_timing_read", "tav_tree_attn_verify_noalloc", "tav_token_scores",
-                "tav_status_string", "tav_last_error")
+                "tav_prefetch_build", "tav_prefetch_reach", "tav_status_string", "tav_last_error")
+TAV_PREFETCH_BFS, TAV_PREFETCH_PREDICTIVE = 0, 1
 NOALLOC_SCRATCH_BYTES = 64 << 20   # TAV_NOALLOC_SCRATCH_BYTES
 
 _p = ctypes.c_void_p
@@ -79,6 +80,17 @@ class tav_score_io(ctypes.Structure):
                 ("tau", _f32), ("log_p0", _p), ("log_q", _p), ("entropy", _p), ("argmax", _p)]
 
 
+class tav_prefetch_params(ctypes.Structure):
+    _fields_ = [("T", _i32), ("budget", _i32), ("depth_cap", _i32), ("rule", _i32), ("seed", ctypes.c_uint64),
+                ("class_w", _f32 * 6)]
+
+
+class tav_prefetch_out(ctypes.Structure):
+    _fields_ = [("capacity", _i32), ("num_nodes", _i32), ("num_requests", _i32), ("parent", _p),
+                ("is_accept", _p), ("request", _p), ("cut", _p), ("heap", _p), ("request_cut", _p),
+                ("predicted_transitions", ctypes.c_double)]
+
+
 class TavError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
@@ -116,13 +128,15 @@ def load() -> ctypes.CDLL:
             ctypes.POINTER(tav_verify_io), ctypes.POINTER(tav_presto_io), ctypes.POINTER(tav_tree_out),
             _p, _p, _p]
         lib.tav_token_scores.argtypes = [ctypes.POINTER(tav_score_io), _p, ctypes.c_size_t, _p]
+        lib.tav_prefetch_build.argtypes = [ctypes.POINTER(tav_prefetch_params), ctypes.POINTER(tav_prefetch_out)]
+        lib.tav_prefetch_reach.argtypes = [_i32, _p, _p, _p, _i32, _p, _f32, _p, ctypes.POINTER(ctypes.c_double)]
         lib.tav_read_status.argtypes = [_p, _p, ctypes.POINTER(ctypes.c_uint32)]
         lib.tav_kernel_timing.argtypes = [ctypes.c_int]
         lib.tav_kernel_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i32)]
         lib.tav_status_string.argtypes = [ctypes.c_int]
         lib.tav_status_string.restype = ctypes.c_char_p
         lib.tav_last_error.restype = ctypes.c_char_p
-        for name in ENTRY_POINTS[:11]:
+        for name in ENTRY_POINTS[:13]:
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -274,6 +288,44 @@ def tav_token_scores(logits: torch.Tensor, token: Optional[torch.Tensor], tau: f
                       entropy=_ptr(entropy), argmax=_ptr(argmax))
     _check(load().tav_token_scores(ctypes.byref(io), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                    _stream(stream)))
+
+
+def tav_prefetch_build(T: int, budget: int, depth_cap: int, rule: int, seed: int, class_w, capacity=None):
+    """PreSTO's prefetching tree for one batch (host only).  Returns a dict of numpy arrays:
+    parent, is_accept, request, cut, heap (one entry per node, ascending heap index),
+    request_cut, and predicted_transitions."""
+    import numpy as np
+
+    if capacity is None:   # BFS expansions whose request is deferred add nodes but no request
+        capacity = 2 * int(budget) + 1 if rule == TAV_PREFETCH_PREDICTIVE else 64 * int(budget) + 1024
+    cap = int(capacity)
+    arr = {"parent": np.zeros(cap, np.int32), "is_accept": np.zeros(cap, np.uint8),
+           "request": np.zeros(cap, np.int32), "cut": np.zeros(cap, np.int32),
+           "heap": np.zeros(cap, np.int64), "request_cut": np.zeros(max(1, int(budget)), np.int32)}
+    prm = tav_prefetch_params(T=int(T), budget=int(budget), depth_cap=int(depth_cap), rule=int(rule),
+                              seed=int(seed) & ((1 << 64) - 1), class_w=(_f32 * 6)(*[float(x) for x in class_w]))
+    out = tav_prefetch_out(capacity=cap, **{k: v.ctypes.data for k, v in arr.items()})
+    _check(load().tav_prefetch_build(ctypes.byref(prm), ctypes.byref(out)))
+    res = {k: v[: out.num_nodes].copy() for k, v in arr.items() if k != "request_cut"}
+    res["request_cut"] = arr["request_cut"][: out.num_requests].copy()
+    res["predicted_transitions"] = out.predicted_transitions
+    return res
+
+
+def tav_prefetch_reach(parent, is_accept, request, log_accept, eps: float):
+    """Epsilon-rounded reaching weights of a scored prefetching tree (host only): (reach, F)."""
+    import numpy as np
+
+    parent = np.ascontiguousarray(parent, np.int32)
+    is_accept = np.ascontiguousarray(is_accept, np.uint8)
+    request = np.ascontiguousarray(request, np.int32)
+    log_accept = np.ascontiguousarray(log_accept, np.float32)
+    reach = np.zeros(len(parent), np.float64)
+    F = ctypes.c_double(0.0)
+    _check(load().tav_prefetch_reach(len(parent), parent.ctypes.data, is_accept.ctypes.data, request.ctypes.data,
+                                     len(log_accept), log_accept.ctypes.data if len(log_accept) else None,
+                                     float(eps), reach.ctypes.data, ctypes.byref(F)))
+    return reach, F.value
 
 
 def tav_read_status(workspace: torch.Tensor, stream=None) -> int:

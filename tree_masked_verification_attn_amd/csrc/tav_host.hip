@@ -26,14 +26,19 @@ namespace {
 
 thread_local std::string g_last_error;
 
+tav_status vfail(tav_status s, const char* fmt, va_list ap) {
+  char buf[512];
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  g_last_error = buf;
+  return s;
+}
+
 tav_status fail(tav_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 tav_status fail(tav_status s, const char* fmt, ...) {
-  char buf[512];
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(buf, sizeof buf, fmt, ap);
+  vfail(s, fmt, ap);
   va_end(ap);
-  g_last_error = buf;
   return s;
 }
 
@@ -526,6 +531,17 @@ tav_status attn_verify_impl(const tav_problem* prob, const tav_tree* tree, const
 }
 
 }  // namespace
+
+tav_status tav_host_fail(tav_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vfail(s, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+tav_status tav_host_ok() { return ok(); }
+
 }  // namespace tav
 
 using namespace tav;

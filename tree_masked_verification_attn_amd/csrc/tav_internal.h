@@ -183,6 +183,11 @@ struct ScoreArgs {
   int N, V;
 };
 
+// The error message of the calling thread (tav_last_error) and the status to return, for host
+// code outside tav_host.hip.
+tav_status tav_host_fail(tav_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+tav_status tav_host_ok();
+
 // Kernel launchers (defined next to their kernels).  They return the HIP error
 // of the launch.
 // Start of every call: status word, counters and the per-sequence error words seq_err[B] cleared;

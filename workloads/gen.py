@@ -597,6 +597,15 @@ def presto_batch(seed: int, *, T: int, n_pf: int, Hq: int, Hkv: int, D: int, dty
                     v_cache=v_cache, block_table=table, presto=pr)
 
 
+def device_logits(seed: int, rows: int, V: int, std: float = 3.0, device="cuda"):
+    """[rows, V] bfloat16 logits ~ N(0, std^2) drawn on the device by torch's seeded generator
+    (for batches too large to draw on the host; sampled rows copied back serve the checks)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(np.random.SeedSequence(_key(seed, "device_logits")).generate_state(1, np.uint64)[0] >> 1))
+    out = torch.randn((int(rows), int(V)), generator=g, device=device, dtype=torch.float32)
+    return out.mul_(std).to(torch.bfloat16)
+
+
 # ----------------------------------------------------------------------------
 # the five workload shapes
 # ----------------------------------------------------------------------------
