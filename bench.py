@@ -24,8 +24,8 @@ verification) on the headline workload, plus
   * sub_records: the same measurements for the long-context workload (4 x 32768 prefix,
     128-node depth-10 trees), the PreSTO prefetch batch (attention MFMA utilisation,
     log A + walk time), the per-token scorer over that batch's scored tokens, the headline
-    workload with sparse top-128 draft rows and at temperature 0 (greedy verification), and
-    the host prefetch-tree builder;
+    workload with sparse top-128 draft rows and at temperature 0 (greedy verification), the
+    host prefetch-tree builder and the GPU draft-tree construction;
   * cpu_baseline: the oracle on a bounded sample of the headline workload, on the host.
 """
 
@@ -379,6 +379,58 @@ def scorer_record(seed, rows, V=151936, tau=0.25, reps=5):
     return rec
 
 
+def draft_tree_record(seed, reps=10):
+    """tav_draft_expand x D + tav_draft_prune at the long-context workload's tree shape (4 trees,
+    depth 10, 8 parents x 8 slots, hybrid pools with one lead token, top-128 sparse draft, 127 nodes
+    kept, V = 151936): the drafter's logits of each depth resident in HBM (drawn on the device)."""
+    import torch
+
+    import tree_masked_verification_attn_amd as tav
+    from workloads import gen
+
+    B, V, D, K, slots, S, R = 4, 151936, 10, 8, 8, 128, 127
+    prm = tav.draft_params(num_seqs=B, vocab=V, depth=D, expand_k=K, slots=slots, lead_m=1,
+                           hybrid=tav.TAV_DRAFT_HYBRID_ALL, support=S, budget=R, temperature=1.0, eps=1e-6)
+    ws = torch.zeros((tav.tav_draft_workspace_size(prm) + 7) // 8, dtype=torch.float64, device="cuda")
+    lg = gen.device_logits(seed, B * K, V).view(B, K, V)
+    lg1 = lg[:, :1].contiguous()
+    uni = torch.rand((B, K), generator=torch.Generator(device="cuda").manual_seed(seed), device="cuda")
+    uni1 = uni[:, :1].contiguous()
+    n = R + 1
+    outs = [torch.empty(B * n, dtype=torch.int32, device="cuda") for _ in range(2)]
+    smp = torch.empty(B * n, dtype=torch.uint8, device="cuda")
+    drow = torch.empty(B * n, dtype=torch.int32, device="cuda")
+    didx = torch.empty((B * n, S), dtype=torch.int32, device="cuda")
+    dval = torch.empty((B * n, S), dtype=torch.float32, device="cuda")
+    front = torch.empty((B, K), dtype=torch.int32, device="cuda")
+    s = torch.cuda.Stream()
+
+    def build():
+        for d in range(1, D + 1):
+            tav.tav_draft_expand(prm, d, lg1 if d == 1 else lg, uni1 if d == 1 else uni, front, ws, s)
+        tav.tav_draft_prune(prm, outs[0], outs[1], smp, None, drow, didx, dval, ws, s)
+
+    build()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(reps):
+        build()
+    e1.record(s)
+    torch.cuda.synchronize()
+    if tav.tav_read_status(ws, s):
+        raise RuntimeError("draft-tree status bits set")
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = B * V * 2 * (1 + (D - 1) * K)
+    rec = roofline_hbm("draft_expand_kernel x depth + frontier + prune (GPU draft-tree construction)", nbytes, ms,
+                       None, launches=reps)
+    rec.update({"trees": B, "depth": D, "parents_per_depth": K, "slots": slots, "support": S, "kept": R,
+                "ms_per_build": round(ms, 4), "us_per_depth": round(ms * 1e3 / D, 1),
+                "note": "latency-bound: each depth reads 8 logits rows per tree (9.7 MB) three times "
+                        "(two radix-select passes and the collection pass, the last two from the cache)"})
+    return rec
+
+
 def prefetch_builder_record(seed, reps=200):
     """Host time of tav_prefetch_build at the PreSTO batch's shape (T = 4096, N_pf = 32, K' = 100),
     both rules, and each tree's predicted transition count."""
@@ -472,6 +524,7 @@ def main():
                 gen.make("c3", args.seed, draft_support=128), sub_steps, 3, ach,
                 "c3 with sparse draft rows: top-128 support per row (RheoSampling's sparse draft)")
         subs["prefetch_builder_host"] = prefetch_builder_record(args.seed)
+        subs["draft_tree_gpu"] = draft_tree_record(args.seed)
         torch.cuda.empty_cache()
 
     cpu = None

@@ -103,8 +103,10 @@ enum {
   TAV_DEV_PRESTO_BAD_TREE = 1u << 12,   /* malformed prefetching tree / request ids */
   TAV_DEV_PLAN_MISMATCH = 1u << 13,     /* internal: device work plan differs from the host's */
   TAV_DEV_BAD_TEMPERATURE = 1u << 14,   /* a temperature that is not finite and > 0 */
-  TAV_DEV_BAD_DRAFT = 1u << 15          /* sparse draft row: id outside [0, V), ids not strictly
+  TAV_DEV_BAD_DRAFT = 1u << 15,         /* sparse draft row: id outside [0, V), ids not strictly
                                            ascending, or a value not finite and >= 0 */
+  TAV_DEV_DRAFT_TIES = 1u << 16         /* draft-tree construction: more than 2048 tokens share the
+                                           logit at the support's edge (support then unspecified) */
 };
 
 /* Problem description (host struct). */
@@ -315,6 +317,59 @@ tav_status tav_prefetch_build(const tav_prefetch_params* params, tav_prefetch_ou
 tav_status tav_prefetch_reach(int32_t num_nodes, const int32_t* parent, const uint8_t* is_accept,
                               const int32_t* request, int32_t num_requests, const float* log_accept,
                               float eps, double* reach, double* expected_transitions);
+
+/* Draft-tree construction on the GPU (RheoSampling Section 2.1: EAGLE's expand-then-rerank;
+ * Section 3.2 and Appendix C.1: the hybrid pool with the sampled token's proxy, the sparse draft,
+ * global pruning with its tie-break).  B trees are built at once, one depth per tav_draft_expand
+ * call (the drafter's forward pass on the selected parents happens between calls), then
+ * tav_draft_prune writes the pruned trees in the layout tav_tree / tav_verify_io take.
+ * Per parent: the drafter's bf16 logits z are truncated to their `support` largest entries (ties at
+ * the edge to the smaller token ids); q = softmax(z) over the support ranks tokens (path score =
+ * product of proxies); a hybrid pool takes the top lead_m tokens (proxy q), one token Y drawn from
+ * the tail of softmax(z / temperature) off the leads with the parent's uniform (inverse CDF in
+ * token-id order; proxy min{q(x_m), 1 - sum of the leads' q}, or q(x_1) + eps when lead_m = 0),
+ * then the highest remaining tokens (proxy q); a plain pool takes the top `slots` tokens.  Depth d
+ * expands the top min(expand_k, candidates of depth d - 1) candidates of depth d - 1 by score (ties:
+ * smaller candidate id); depth 1 expands the root.  The prune keeps the `budget` candidates with the
+ * highest scores (ties: shallower, then smaller id), numbered by (depth, id) after the root. */
+enum { TAV_DRAFT_HYBRID_NONE = 0, TAV_DRAFT_HYBRID_FIRST = 1, TAV_DRAFT_HYBRID_ALL = 2 };
+
+typedef struct tav_draft_params {
+  int32_t num_seqs;     /* B */
+  int32_t vocab;        /* V, a multiple of 8 (bf16 logits) */
+  int32_t depth;        /* D in [1, 32] */
+  int32_t expand_k;     /* parents expanded per depth, in [1, 64] */
+  int32_t slots;        /* pool slots per parent, in [1, support] */
+  int32_t lead_m;       /* hybrid pool: lead tokens, in [0, slots) */
+  int32_t hybrid;       /* TAV_DRAFT_HYBRID_ALL, _FIRST (the rank-0 parent of each depth) or _NONE */
+  int32_t support;      /* S in [slots, 128], <= V */
+  int32_t budget;       /* R: nodes kept besides the root, <= the number of candidates */
+  float temperature;    /* > 0: the sampled token's distribution is softmax(z / temperature) */
+  float eps;            /* lead_m = 0: the sampled token's proxy is q(x_1) + eps */
+} tav_draft_params;
+
+/* Workspace bytes of a construction (host only).  Errors: parameters outside the ranges above,
+ * more than 2048 candidates per tree. */
+tav_status tav_draft_workspace_size(const tav_draft_params* p, size_t* bytes);
+
+/* Depth d in [1, depth]: draft_logits [B, K_d, V] bf16 are the drafter's logits at the parents of
+ * depth d (K_1 = 1: the root; then the parents this call's predecessor listed), uniforms [B, K_d]
+ * the parents' uniforms in [0, 1).  frontier_out [B, expand_k] (optional): the candidate ids of
+ * the parents of depth d + 1 in rank order, -1 padded -- the nodes the drafter runs on next.
+ * Calls for one construction are issued in depth order on one stream with one workspace.  Device
+ * errors: non-finite draft logits (TAV_DEV_NONFINITE_LOGITS), TAV_DEV_DRAFT_TIES. */
+tav_status tav_draft_expand(const tav_draft_params* p, int32_t d, const void* draft_logits, const float* uniforms,
+                            int32_t* frontier_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* After depth D: the pruned trees, budget + 1 nodes per tree (node 0 the root), rows b * (budget
+ * + 1) ...: parent (-1 at roots, sequence-local), token (-1 at roots), sampled, cand_id (optional:
+ * the candidate id of each node), draft_row (the node's own index if its sampled child was kept,
+ * else -1) and the draft rows draft_idx / draft_val [B * (budget + 1), support] (support ids
+ * ascending and q~, written for the rows draft_row names) -- tav_verify_io's sparse draft rows with
+ * num_draft_rows = B * (budget + 1). */
+tav_status tav_draft_prune(const tav_draft_params* p, int32_t* parent, int32_t* token, uint8_t* sampled,
+                           int32_t* cand_id, int32_t* draft_row, int32_t* draft_idx, float* draft_val,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace the calls below need for this problem (host only; no HIP
  * call).  presto may be NULL.  Errors: NULL pointer, bad shape. */

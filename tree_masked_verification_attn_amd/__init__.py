@@ -30,7 +30,9 @@ DEVICE_BITS = {
 ENTRY_POINTS = ("tav_workspace_size", "tav_tree_prep", "tav_tree_attention", "tav_tree_verify",
                 "tav_presto_accept", "tav_tree_attn_verify", "tav_read_status", "tav_kernel_timing",
                 "tav_kernel_timing_read", "tav_tree_attn_verify_noalloc", "tav_token_scores",
-                "tav_prefetch_build", "tav_prefetch_reach", "tav_status_string", "tav_last_error")
+                "tav_prefetch_build", "tav_prefetch_reach", "tav_draft_workspace_size", "tav_draft_expand",
+                "tav_draft_prune", "tav_status_string", "tav_last_error")
+TAV_DRAFT_HYBRID_NONE, TAV_DRAFT_HYBRID_FIRST, TAV_DRAFT_HYBRID_ALL = 0, 1, 2
 TAV_PREFETCH_BFS, TAV_PREFETCH_PREDICTIVE = 0, 1
 NOALLOC_SCRATCH_BYTES = 64 << 20   # TAV_NOALLOC_SCRATCH_BYTES
 
@@ -91,6 +93,12 @@ class tav_prefetch_out(ctypes.Structure):
                 ("predicted_transitions", ctypes.c_double)]
 
 
+class tav_draft_params(ctypes.Structure):
+    _fields_ = [("num_seqs", _i32), ("vocab", _i32), ("depth", _i32), ("expand_k", _i32), ("slots", _i32),
+                ("lead_m", _i32), ("hybrid", _i32), ("support", _i32), ("budget", _i32),
+                ("temperature", _f32), ("eps", _f32)]
+
+
 class TavError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
@@ -130,13 +138,17 @@ def load() -> ctypes.CDLL:
         lib.tav_token_scores.argtypes = [ctypes.POINTER(tav_score_io), _p, ctypes.c_size_t, _p]
         lib.tav_prefetch_build.argtypes = [ctypes.POINTER(tav_prefetch_params), ctypes.POINTER(tav_prefetch_out)]
         lib.tav_prefetch_reach.argtypes = [_i32, _p, _p, _p, _i32, _p, _f32, _p, ctypes.POINTER(ctypes.c_double)]
+        lib.tav_draft_workspace_size.argtypes = [ctypes.POINTER(tav_draft_params), ctypes.POINTER(ctypes.c_size_t)]
+        lib.tav_draft_expand.argtypes = [ctypes.POINTER(tav_draft_params), _i32, _p, _p, _p, _p, ctypes.c_size_t, _p]
+        lib.tav_draft_prune.argtypes = [ctypes.POINTER(tav_draft_params), _p, _p, _p, _p, _p, _p, _p, _p,
+                                        ctypes.c_size_t, _p]
         lib.tav_read_status.argtypes = [_p, _p, ctypes.POINTER(ctypes.c_uint32)]
         lib.tav_kernel_timing.argtypes = [ctypes.c_int]
         lib.tav_kernel_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i32)]
         lib.tav_status_string.argtypes = [ctypes.c_int]
         lib.tav_status_string.restype = ctypes.c_char_p
         lib.tav_last_error.restype = ctypes.c_char_p
-        for name in ENTRY_POINTS[:13]:
+        for name in ENTRY_POINTS[:16]:
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -326,6 +338,33 @@ def tav_prefetch_reach(parent, is_accept, request, log_accept, eps: float):
                                      len(log_accept), log_accept.ctypes.data if len(log_accept) else None,
                                      float(eps), reach.ctypes.data, ctypes.byref(F)))
     return reach, F.value
+
+
+def draft_params(**kw) -> tav_draft_params:
+    """tav_draft_params from keyword arguments (the C field names)."""
+    return tav_draft_params(**kw)
+
+
+def tav_draft_workspace_size(params: tav_draft_params) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().tav_draft_workspace_size(ctypes.byref(params), ctypes.byref(n)))
+    return n.value
+
+
+def tav_draft_expand(params: tav_draft_params, d: int, draft_logits: torch.Tensor, uniforms: torch.Tensor,
+                     frontier_out: Optional[torch.Tensor], workspace: torch.Tensor, stream=None):
+    """Depth d of the draft-tree construction: draft_logits [B, K_d, V] bf16, uniforms [B, K_d] f32;
+    frontier_out [B, expand_k] int32 receives the next parents' candidate ids."""
+    _check(load().tav_draft_expand(ctypes.byref(params), int(d), _ptr(draft_logits), _ptr(uniforms),
+                                   _ptr(frontier_out), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def tav_draft_prune(params: tav_draft_params, parent, token, sampled, cand_id, draft_row, draft_idx, draft_val,
+                    workspace: torch.Tensor, stream=None):
+    _check(load().tav_draft_prune(ctypes.byref(params), _ptr(parent), _ptr(token), _ptr(sampled), _ptr(cand_id),
+                                  _ptr(draft_row), _ptr(draft_idx), _ptr(draft_val), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def tav_read_status(workspace: torch.Tensor, stream=None) -> int:

@@ -685,6 +685,126 @@ tav_status tav_token_scores(const tav_score_io* io, void* workspace, size_t work
   return ok();
 }
 
+namespace {
+
+// Sizes, candidate-id ranges and workspace layout of a draft-tree construction.
+tav_status draft_plan(const tav_draft_params* p, DraftArgs* a, size_t* total) {
+  if (!p) return fail(TAV_ERR_NULL_POINTER, "draft params are NULL");
+  if (p->num_seqs < 1 || p->vocab < 8 || p->vocab % 8)
+    return fail(TAV_ERR_BAD_SHAPE, "draft: num_seqs >= 1 and vocab a positive multiple of 8 (got %d, %d)",
+                p->num_seqs, p->vocab);
+  if (p->depth < 1 || p->depth > kMaxDraftDepth || p->expand_k < 1 || p->expand_k > 64)
+    return fail(TAV_ERR_UNSUPPORTED, "draft: depth in [1, %d], expand_k in [1, 64] (got %d, %d)", kMaxDraftDepth,
+                p->depth, p->expand_k);
+  if (p->support < 1 || p->support > kMaxDraftSupport || p->support > p->vocab || p->slots < 1 ||
+      p->slots > p->support || p->lead_m < 0 || p->lead_m >= p->slots)
+    return fail(TAV_ERR_UNSUPPORTED, "draft: need 0 <= lead_m < slots <= support <= min(128, vocab) (got %d, %d, %d)",
+                p->lead_m, p->slots, p->support);
+  if (p->hybrid < TAV_DRAFT_HYBRID_NONE || p->hybrid > TAV_DRAFT_HYBRID_ALL)
+    return fail(TAV_ERR_INVALID_ARGUMENT, "draft: hybrid must be TAV_DRAFT_HYBRID_NONE, _FIRST or _ALL");
+  if (!(p->temperature > 0.f) || !isfinite(p->temperature) || !(p->eps >= 0.f) || !isfinite(p->eps))
+    return fail(TAV_ERR_INVALID_ARGUMENT, "draft: temperature must be finite and > 0, eps finite and >= 0");
+  DraftArgs A{};
+  A.B = p->num_seqs; A.V = p->vocab; A.S = p->support; A.K = p->expand_k; A.slots = p->slots; A.m = p->lead_m;
+  A.hybrid = p->hybrid; A.R = p->budget; A.D = p->depth; A.temperature = p->temperature; A.eps = p->eps;
+  A.kcount[0] = 0;
+  A.base[0] = 0;
+  A.kcount[1] = 1;
+  A.base[1] = 1;
+  for (int d = 1; d <= A.D; ++d) {
+    const int nd = A.kcount[d] * A.slots;
+    A.base[d + 1] = A.base[d] + nd;
+    A.kcount[d + 1] = d < A.D ? (nd < A.K ? nd : A.K) : 0;
+    if (A.base[d + 1] > kMaxDraftCandidates)
+      return fail(TAV_ERR_UNSUPPORTED, "draft: more than %d candidates per tree", kMaxDraftCandidates);
+  }
+  A.C = A.base[A.D + 1];
+  if (p->budget < 1 || p->budget > A.C - 1)
+    return fail(TAV_ERR_BAD_SHAPE, "draft: budget must be in [1, %d] (got %d)", A.C - 1, p->budget);
+  const size_t B = (size_t)A.B, C = (size_t)A.C, S = (size_t)A.S;
+  size_t o = 0;
+  A.status = (uint32_t*)o; o = align_up(o + 256);
+  A.seq_err = (uint32_t*)o; o = align_up(o + B * 4);
+  A.cand_parent = (int32_t*)o; o = align_up(o + B * C * 4);
+  A.cand_token = (int32_t*)o; o = align_up(o + B * C * 4);
+  A.cand_score = (double*)o; o = align_up(o + B * C * 8);
+  A.cand_sampled = (uint8_t*)o; o = align_up(o + B * C);
+  A.cand_depth = (uint8_t*)o; o = align_up(o + B * C);
+  A.row_idx = (int32_t*)o; o = align_up(o + B * C * S * 4);
+  A.row_val = (float*)o; o = align_up(o + B * C * S * 4);
+  A.frontier = (int32_t*)o; o = align_up(o + B * (size_t)A.K * 4);
+  *a = A;
+  *total = o;
+  return TAV_OK;
+}
+
+// The layout's offsets turned into addresses inside the workspace.
+void draft_bind(DraftArgs* a, void* ws) {
+  char* w = (char*)ws;
+  a->status = (uint32_t*)(w + (size_t)a->status);
+  a->seq_err = (uint32_t*)(w + (size_t)a->seq_err);
+  a->cand_parent = (int32_t*)(w + (size_t)a->cand_parent);
+  a->cand_token = (int32_t*)(w + (size_t)a->cand_token);
+  a->cand_score = (double*)(w + (size_t)a->cand_score);
+  a->cand_sampled = (uint8_t*)(w + (size_t)a->cand_sampled);
+  a->cand_depth = (uint8_t*)(w + (size_t)a->cand_depth);
+  a->row_idx = (int32_t*)(w + (size_t)a->row_idx);
+  a->row_val = (float*)(w + (size_t)a->row_val);
+  a->frontier = (int32_t*)(w + (size_t)a->frontier);
+}
+
+}  // namespace
+
+tav_status tav_draft_workspace_size(const tav_draft_params* p, size_t* bytes) {
+  if (!bytes) return fail(TAV_ERR_NULL_POINTER, "bytes is NULL");
+  DraftArgs a;
+  size_t total = 0;
+  const tav_status st = draft_plan(p, &a, &total);
+  if (st != TAV_OK) return st;
+  *bytes = total;
+  return ok();
+}
+
+tav_status tav_draft_expand(const tav_draft_params* p, int32_t d, const void* draft_logits, const float* uniforms,
+                            int32_t* frontier_out, void* workspace, size_t workspace_bytes, void* stream) {
+  DraftArgs a;
+  size_t total = 0;
+  tav_status st = draft_plan(p, &a, &total);
+  if (st != TAV_OK) return st;
+  if (d < 1 || d > a.D) return fail(TAV_ERR_INVALID_ARGUMENT, "draft: depth %d outside [1, %d]", d, a.D);
+  if (!draft_logits || !uniforms) return fail(TAV_ERR_NULL_POINTER, "draft logits / uniforms are NULL");
+  if (!aligned16(draft_logits)) return fail(TAV_ERR_INVALID_ARGUMENT, "draft logits must be 16-byte aligned");
+  Plan P;
+  P.total = total;
+  st = check_ws(P, workspace, workspace_bytes);
+  if (st != TAV_OK) return st;
+  draft_bind(&a, workspace);
+  a.Kd = a.kcount[d];
+  hipStream_t s = (hipStream_t)stream;
+  if (d == 1) TAV_HIP(launch_start(a.status, a.seq_err, a.B, nullptr, 0, 0, nullptr, s));
+  TAV_HIP(launch_draft_expand(a, d, (const uint16_t*)draft_logits, uniforms, frontier_out, s));
+  return ok();
+}
+
+tav_status tav_draft_prune(const tav_draft_params* p, int32_t* parent, int32_t* token, uint8_t* sampled,
+                           int32_t* cand_id, int32_t* draft_row, int32_t* draft_idx, float* draft_val,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  DraftArgs a;
+  size_t total = 0;
+  tav_status st = draft_plan(p, &a, &total);
+  if (st != TAV_OK) return st;
+  if (!parent || !token || !sampled || !draft_row || !draft_idx || !draft_val)
+    return fail(TAV_ERR_NULL_POINTER, "draft prune: an output array is NULL");
+  Plan P;
+  P.total = total;
+  st = check_ws(P, workspace, workspace_bytes);
+  if (st != TAV_OK) return st;
+  draft_bind(&a, workspace);
+  DraftOut o{parent, token, sampled, cand_id, draft_row, draft_idx, draft_val};
+  TAV_HIP(launch_draft_prune(a, o, (hipStream_t)stream));
+  return ok();
+}
+
 tav_status tav_read_status(const void* workspace, void* stream, uint32_t* status_bits) {
   if (!workspace || !status_bits) return fail(TAV_ERR_NULL_POINTER, "workspace / status_bits is NULL");
   TAV_HIP(hipStreamSynchronize((hipStream_t)stream));

@@ -183,6 +183,39 @@ struct ScoreArgs {
   int N, V;
 };
 
+constexpr int kMaxDraftDepth = 32;           // draft-tree depths
+constexpr int kMaxDraftCandidates = 2048;    // candidates of one draft tree (the root included)
+
+// Draft-tree construction state (workspace) and sizes.  Candidate ids: the root 0, then per depth
+// d the parents in rank order, each parent's slots in pool order: depth d holds ids
+// [base[d], base[d + 1]), kcount[d] parents x slots of them.
+struct DraftArgs {
+  int B, V, S, K, Kd, C, slots, m, hybrid, R, D;
+  float temperature, eps;
+  int base[kMaxDraftDepth + 2];
+  int kcount[kMaxDraftDepth + 2];
+  int32_t* cand_parent;     // [B, C]
+  int32_t* cand_token;      // [B, C]
+  double* cand_score;       // [B, C]
+  uint8_t* cand_sampled;    // [B, C]
+  uint8_t* cand_depth;      // [B, C]
+  int32_t* row_idx;         // [B, C, S] a hybrid parent's draft row: support ids ascending ...
+  float* row_val;           // [B, C, S] ... and q~ there
+  int32_t* frontier;        // [B, K] the parents of the next depth
+  uint32_t* status;
+  uint32_t* seq_err;        // [B]
+};
+
+struct DraftOut {
+  int32_t* parent;          // [B, R + 1]
+  int32_t* token;
+  uint8_t* sampled;
+  int32_t* cand_id;         // optional
+  int32_t* draft_row;       // [B, R + 1]
+  int32_t* draft_idx;       // [B * (R + 1), S]
+  float* draft_val;
+};
+
 // The error message of the calling thread (tav_last_error) and the status to return, for host
 // code outside tav_host.hip.
 tav_status tav_host_fail(tav_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
@@ -218,6 +251,11 @@ hipError_t launch_attn_sentinel_f32(const Plan& p, const AttnArgs& a, hipStream_
 // Vocabulary workers: one 512-thread workgroup per compute unit, persistent over the node queue.
 hipError_t launch_vocab(const VocabArgs& a, bool bf16_logits, int num_cus, hipStream_t s);
 hipError_t launch_walk(const WalkArgs& a, hipStream_t s);
+// Draft-tree construction: depth d's pools (one workgroup per (sequence, parent)) and the next
+// parents (one workgroup per sequence); the global prune.
+hipError_t launch_draft_expand(const DraftArgs& a, int d, const uint16_t* logits, const float* uniforms,
+                               int32_t* frontier_out, hipStream_t s);
+hipError_t launch_draft_prune(const DraftArgs& a, const DraftOut& o, hipStream_t s);
 // Per-token scores: one 512-thread workgroup per row, persistent over the rows.
 hipError_t launch_score(const ScoreArgs& a, bool bf16, int num_cus, hipStream_t s);
 hipError_t launch_presto(const PrestoArgs& a, hipStream_t s);

@@ -34,6 +34,8 @@ CONFIG_DESCRIPTIONS = {
 }
 
 
+DRAFT_PEAK_DEFAULT = (4.0, 7.0)
+
 # ----------------------------------------------------------------------------
 # random streams and bf16 storage helpers
 # ----------------------------------------------------------------------------
@@ -595,6 +597,21 @@ def presto_batch(seed: int, *, T: int, n_pf: int, Hq: int, Hkv: int, D: int, dty
                     sm_scale=1.0 / math.sqrt(D), node_offsets=node_offsets, parent=parent,
                     prefix_len=prefix_len, q=q, k_node=k_node, v_node=v_node, k_cache=k_cache,
                     v_cache=v_cache, block_table=table, presto=pr)
+
+
+def draft_logits_row(seed: int, b: int, cid: int, V: int, std: float = 3.0, peak=DRAFT_PEAK_DEFAULT):
+    """A drafter's bf16 logits at candidate `cid` of tree `b`: N(0, std^2) with the largest entry
+    raised by U(peak) (a confident next token, as in the expansion trees above); bf16 bits."""
+    z = _normal(_key(seed, "draft_logits", b, cid), (V,), std)
+    if peak is not None:
+        r = _rng(seed, "draft_peak", b, cid)
+        z[int(np.argmax(z))] += np.float32(r.uniform(peak[0], peak[1]))
+    return f32_to_bf16_bits(z)
+
+
+def draft_uniform(seed: int, b: int, d: int, rank: int) -> float:
+    """The uniform of the parent of rank `rank` at depth d of tree b (float32 value)."""
+    return float(np.float32(_rng(seed, "draft_uniform", b, d, rank).random()))
 
 
 def device_logits(seed: int, rows: int, V: int, std: float = 3.0, device="cuda"):
