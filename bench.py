@@ -461,6 +461,8 @@ def main():
                     help="headline workload with sparse draft rows of this support (0: dense)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sub", action="store_true", help="headline workload only (profiling runs)")
+    ap.add_argument("--sub", default="",
+                    help="comma-separated sub-record names to run (default: all of them)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (counter calibration)")
     ap.add_argument("--kernel-steps", type=int, default=20,
@@ -509,22 +511,34 @@ def main():
     subs = {}
     if not args.no_sub:
         sub_steps = max(5, min(args.steps, 20))
-        subs["c5_long_context"] = tree_sub_record(gen.make("c5", args.seed), sub_steps, 3, ach,
-                                                  "c5: " + gen.CONFIG_DESCRIPTIONS["c5"])
-        w4 = gen.make("c4", args.seed)
-        subs["c4_presto"] = presto_sub_record(w4, sub_steps, 3, ach)
-        subs["c4_token_scores"] = scorer_record(args.seed, w4.N + w4.presto.T)
-        del w4
-        wg = copy.copy(w)
-        wg.temperature = np.zeros_like(w.temperature)
-        subs["c3_greedy"] = tree_sub_record(wg, sub_steps, 3, ach,
-                                            "c3 at temperature 0: greedy verification (argmax verification tokens)")
-        if args.workload == "c3" and not args.draft_support:
+        only = set(filter(None, args.sub.split(",")))
+
+        def want(name):
+            return not only or name in only
+
+        if want("c5_long_context"):
+            subs["c5_long_context"] = tree_sub_record(gen.make("c5", args.seed), sub_steps, 3, ach,
+                                                      "c5: " + gen.CONFIG_DESCRIPTIONS["c5"])
+        if want("c4_presto") or want("c4_token_scores"):
+            w4 = gen.make("c4", args.seed)
+            if want("c4_presto"):
+                subs["c4_presto"] = presto_sub_record(w4, sub_steps, 3, ach)
+            if want("c4_token_scores"):
+                subs["c4_token_scores"] = scorer_record(args.seed, w4.N + w4.presto.T)
+            del w4
+        if want("c3_greedy"):
+            wg = copy.copy(w)
+            wg.temperature = np.zeros_like(w.temperature)
+            subs["c3_greedy"] = tree_sub_record(wg, sub_steps, 3, ach,
+                                                "c3 at temperature 0: greedy verification (argmax verification tokens)")
+        if args.workload == "c3" and not args.draft_support and want("c3_sparse_draft_k128"):
             subs["c3_sparse_draft_k128"] = tree_sub_record(
                 gen.make("c3", args.seed, draft_support=128), sub_steps, 3, ach,
                 "c3 with sparse draft rows: top-128 support per row (RheoSampling's sparse draft)")
-        subs["prefetch_builder_host"] = prefetch_builder_record(args.seed)
-        subs["draft_tree_gpu"] = draft_tree_record(args.seed)
+        if want("prefetch_builder_host"):
+            subs["prefetch_builder_host"] = prefetch_builder_record(args.seed)
+        if want("draft_tree_gpu"):
+            subs["draft_tree_gpu"] = draft_tree_record(args.seed)
         torch.cuda.empty_cache()
 
     cpu = None

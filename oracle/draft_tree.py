@@ -26,8 +26,9 @@ Readings where the pages leave a step open:
 * per depth d the parents are the top min(K, candidates of depth d-1) candidates of depth d-1
   (depth 1: the root); a pool has min(K_slots, S) slots;
 * nodes of the pruned tree are numbered by (depth, id), the root first.
-Decisions that floating-point rounding could flip (scores within 1e-9 relative at a cut, a
-uniform within 1e-9 of a CDF step) are recorded as near-ties.
+Decisions that floating-point rounding could flip (different scores within 1e-9 relative at a
+cut, a uniform within 1e-9 of a CDF step) are recorded as near-ties; equal scores at a cut go by
+the tie rule (the next parents: smaller id; the prune: shallower, then smaller id).
 """
 
 from __future__ import annotations
@@ -111,9 +112,11 @@ class DraftTreeBuilder:
         return list(self.frontier)
 
     def _cut_tie(self, order, k):
+        """Records a near-tie at a cut: two scores that differ, but by at most TIE relative.  Equal
+        scores are not recorded: the stated tie rule decides them."""
         if 0 < k < len(order):
             a, b = self.score[order[k - 1]], self.score[order[k]]
-            if abs(a - b) <= TIE * max(abs(a), abs(b)):
+            if a != b and abs(a - b) <= TIE * max(abs(a), abs(b)):
                 self.ties.append(("cut", order[k - 1], order[k]))
 
     def prune(self):

@@ -20,9 +20,10 @@ import gpu_util as gu
 pytestmark = pytest.mark.gpu
 
 
-def build_both(seed, B, V, D, K, slots, m, hybrid, S, R, T):
+def build_both(seed, B, V, D, K, slots, m, hybrid, S, R, T, row_fn=None):
     import tree_masked_verification_attn_amd as tav
 
+    row_fn = row_fn or gen.draft_logits_row
     hyb = {"all": tav.TAV_DRAFT_HYBRID_ALL, "first": tav.TAV_DRAFT_HYBRID_FIRST, "none": tav.TAV_DRAFT_HYBRID_NONE}
     prm = tav.draft_params(num_seqs=B, vocab=V, depth=D, expand_k=K, slots=slots, lead_m=m, hybrid=hyb[hybrid],
                            support=S, budget=R, temperature=T, eps=1e-6)
@@ -37,7 +38,7 @@ def build_both(seed, B, V, D, K, slots, m, hybrid, S, R, T):
         uni = np.zeros((B, kd), np.float32)
         for b in range(B):
             for j, c in enumerate(gpu_front[b]):
-                rows[b, j] = gen.draft_logits_row(seed, b, c, V)
+                rows[b, j] = row_fn(seed, b, c, V)
                 uni[b, j] = gen.draft_uniform(seed, b, d, j)
         lg = torch.from_numpy(rows.view(np.int16)).view(torch.bfloat16).cuda()
         tav.tav_draft_expand(prm, d, lg, torch.from_numpy(uni).cuda(), front, ws)
@@ -101,6 +102,49 @@ CASES = {
 def test_draft_tree_parity(case, seed):
     got, compared = build_both(seed, *CASES[case])
     assert compared >= 1
+
+
+def _bf16_bits(x):
+    return (np.asarray(x, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def tied_row(seed, b, c, V, S=16, n_top=24):
+    """n_top tokens at logit 2, the rest at -3: the support is the S smallest of those ids (ties at
+    the threshold), q = 1/S exactly on it, so every proxy and path score is a power of two and
+    scores tie exactly across parents and slots (the next parents and the prune go by the tie
+    rule)."""
+    rng = np.random.default_rng([seed, b, c, 17])
+    z = np.full(V, -3.0, np.float32)
+    z[rng.choice(V, n_top, replace=False)] = 2.0
+    return _bf16_bits(z)
+
+
+def one_stride_row(seed, b, c, V, S=128):
+    """S distinct logits in [1, 3) on tokens 8192 k + (0..7) (one 8-token group every 8192 tokens),
+    every other token at 0: the largest logits gather in few groups, far more than 4096 tokens
+    share the next value, and the top S are still distinct."""
+    rng = np.random.default_rng([seed, b, c, 29])
+    ids = np.array([8192 * k + e for k in range(V // 8192 + 1) for e in range(8)])
+    ids = ids[ids < V][:S]
+    assert ids.size == S
+    z = np.zeros(V, np.float32)
+    z[ids] = 1.0 + rng.permutation(S) / 64.0
+    return _bf16_bits(z)
+
+
+def test_draft_tree_exact_ties():
+    """Exact score ties everywhere (powers of two) and logits tied at the support's threshold: the
+    frontier, the prune and the support all go by their tie rules on both sides."""
+    got, compared = build_both(3, 2, 4096, 4, 4, 4, 1, "all", 16, 30, 1.0, row_fn=tied_row)
+    assert compared == 2
+
+
+def test_draft_tree_top_in_few_groups():
+    """Rows whose largest logits sit in a few 8-token groups and whose remaining tokens all tie:
+    the support is still the S largest (the select does not rely on the largest logits being
+    spread over the row)."""
+    got, compared = build_both(5, 1, 151936, 3, 2, 4, 1, "all", 128, 8, 1.0, row_fn=one_stride_row)
+    assert compared == 1
 
 
 def test_draft_tree_feeds_the_scoring_pass():

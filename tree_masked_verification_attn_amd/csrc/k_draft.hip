@@ -11,47 +11,90 @@
 // remaining tokens as fills; the draft logits are truncated to their top entries before the
 // softmax (the sparse draft); global pruning breaks score ties by depth, then left to right.
 //
-// Per depth, one 256-thread workgroup per (sequence, parent): the row's S largest logits are found
-// by a two-pass radix select on the bf16 bit patterns (a 256-bin histogram of the high byte, then
-// of the low byte inside the threshold bin; tokens at the threshold value go to the smaller ids),
-// sorted by (logit, id); q = softmax over the support in fp64, the tail of softmax(z / T) for the
+// Per depth, one 1024-thread workgroup per (sequence, parent): the row's S largest logits are
+// found from the bf16 bit patterns -- a lower bound L from the threads' own maxima (the S-th
+// largest of them), the pairs (key, id) with key >= L gathered in LDS, a two-pass radix select
+// there (over the whole row again if they do not fit); tokens at the threshold value go to the
+// smaller ids, sorted by (logit, id); q = softmax over the support in fp64, the tail of softmax(z / T) for the
 // sampled token (inverse CDF in token-id order), the pool, the children's scores, and for a hybrid
 // parent its draft row (support ids ascending, q~).  One workgroup per sequence then ranks the
-// depth's candidates for the next parents, and at the end ranks all candidates for the prune
-// (rank = number of candidates ahead under the ordering: deterministic, no sort).
+// depth's candidates for the next parents (rank = number of candidates ahead: deterministic, no
+// sort), and at the end keeps the R best of all candidates: a byte-wise radix select on the
+// scores' fp64 bit patterns, candidates tied at the threshold ranked by (depth, id).
 #include "tav_internal.h"
 
 namespace tav {
 namespace {
 
-constexpr int kDraftThreads = 256;
+constexpr int kDraftThreads = 256;    // frontier ranking
+constexpr int kExpandThreads = 1024;  // one logits row per workgroup
+constexpr int kNearCap = 4096;        // near-top (key, id) pairs kept in LDS for the collection
 constexpr int kEqCap = 2048;   // tokens at the threshold logit held for the smallest-id choice
 
 __device__ inline uint32_t bf16_key(uint32_t b) { return b ^ ((b & 0x8000u) ? 0xFFFFu : 0x8000u); }
+// Calls f(key, token) for every element of a bf16 row of nunits * 8 entries, each thread keeping
+// four 16-byte loads in flight (one workgroup streams a whole row, so latency hiding is per thread).
+template <class F>
+__device__ inline void scan_row(const uint16_t* row, int nunits, F&& f) {
+  constexpr int kUnroll = 4;
+  for (int u0 = threadIdx.x; u0 < nunits; u0 += kUnroll * kExpandThreads) {
+    uint4 x[kUnroll];
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) {
+      const int u = u0 + k * kExpandThreads;
+      if (u < nunits) x[k] = *(const uint4*)(row + (size_t)u * 8);
+    }
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) {
+      const int u = u0 + k * kExpandThreads;
+      if (u >= nunits) break;
+      const uint32_t w4[4] = {x[k].x, x[k].y, x[k].z, x[k].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f((w4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu, u * 8 + e);
+    }
+  }
+}
+
+// Number of threads of the (kExpandThreads-wide) block with pred set; every thread gets it.
+__device__ inline int block_count(bool pred, int* lds) {
+  const int c = __popcll(__ballot(pred));
+  if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = c;
+  __syncthreads();
+  int t = 0;
+#pragma unroll
+  for (int w = 0; w < kExpandThreads / 64; ++w) t += lds[w];
+  __syncthreads();
+  return t;
+}
+
+// Slot of this lane in a wave-aggregated append to *counter (one LDS atomic per wave), or -1
+// when take is false.
+__device__ inline int wave_append(bool take, int* counter) {
+  const unsigned long long m = __ballot(take);
+  if (m == 0) return -1;
+  const int lane = __lane_id();
+  const int leader = __ffsll((long long)__ballot(1)) - 1;
+  int base = 0;
+  if (lane == leader) base = atomicAdd(counter, __popcll(m));
+  base = __shfl(base, leader);
+  return take ? base + __popcll(m & ((1ull << lane) - 1)) : -1;
+}
+
 __device__ inline float key_value(uint32_t k) {
   const uint32_t b = (k & 0x8000u) ? (k ^ 0x8000u) : (k ^ 0xFFFFu);
   return __uint_as_float(b << 16);
 }
 
-// Block-wide sum of one int per thread (all threads get it).
-__device__ int block_sum(int v, int* lds) {
-  for (int d = 32; d > 0; d >>= 1) v += __shfl_xor(v, d);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = v;
-  __syncthreads();
-  int t = 0;
-  for (int w = 0; w < kDraftThreads / 64; ++w) t += lds[w];
-  return t;
-}
-
-__global__ __launch_bounds__(kDraftThreads) void draft_expand_kernel(DraftArgs a, int d, const uint16_t* logits,
-                                                                     const float* uniforms) {
+__global__ __launch_bounds__(kExpandThreads) void draft_expand_kernel(DraftArgs a, int d, const uint16_t* logits,
+                                                                      const float* uniforms) {
   __shared__ int hist[256];
-  __shared__ int red[kDraftThreads / 64];
-  __shared__ int n_sel, n_eq;
+  __shared__ int red[kExpandThreads / 64];
+  __shared__ int n_sel, n_eq, n_near;
   __shared__ uint32_t sel_key[kMaxDraftSupport];
   __shared__ int sel_id[kMaxDraftSupport];
   __shared__ int eq_id[kEqCap];
+  __shared__ uint32_t near_key[kNearCap];
+  __shared__ int near_id[kNearCap];
   __shared__ uint32_t s_key[kMaxDraftSupport];   // the support by (logit desc, id asc)
   __shared__ int s_id[kMaxDraftSupport];
   __shared__ int id_rank[kMaxDraftSupport];      // position of each support entry in token-id order
@@ -80,25 +123,49 @@ __global__ __launch_bounds__(kDraftThreads) void draft_expand_kernel(DraftArgs a
     if (pid < 0) return;
   }
   const uint16_t* row = logits + ((size_t)b * a.Kd + j) * V;
-  if (tid == 0) { n_sel = 0; n_eq = 0; bad = 0; }
-  for (int i = tid; i < 256; i += kDraftThreads) hist[i] = 0;
+  if (tid == 0) { n_sel = 0; n_eq = 0; n_near = 0; bad = 0; }
+  for (int i = tid; i < 256; i += kExpandThreads) hist[i] = 0;
   __syncthreads();
-  // ---- pass 1: high byte of the keys; non-finite logits are errors
+  // ---- pass 1: each thread's largest key (non-finite logits are errors)
   int nonfin = 0;
-  for (int u = tid; u < nunits; u += kDraftThreads) {
-    const uint4 x = *(const uint4*)(row + (size_t)u * 8);
-    const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t bits = (w4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-      nonfin |= (bits & 0x7F80u) == 0x7F80u;
-      atomicAdd(&hist[bf16_key(bits) >> 8], 1);
-    }
-  }
+  uint32_t kmax = 0;
+  scan_row(row, nunits, [&](uint32_t bits, int) {
+    nonfin |= (bits & 0x7F80u) == 0x7F80u;
+    kmax = max(kmax, bf16_key(bits));
+  });
   if (nonfin) atomicOr(&bad, (int)TAV_DEV_NONFINITE_LOGITS);
+  // L = the S-th largest of the threads' maxima (binary search on the 16-bit key with ballot
+  // counts): at least S elements are >= L, so the support lies among the keys >= L -- for rows
+  // without heavy ties only a little more than S of them
+  uint32_t lo = 0, hi = 0xFFFFu;
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi + 1) >> 1;
+    const int c = block_count(kmax >= mid, red);
+    if (c >= S) lo = mid; else hi = mid - 1;
+  }
+  const uint32_t L = lo;
+  // ---- pass 2: the (key, id) pairs at or above L into LDS
+  scan_row(row, nunits, [&](uint32_t bits, int id) {
+    const uint32_t k = bf16_key(bits);
+    const int at = wave_append(k >= L, &n_near);
+    if (at >= 0 && at < kNearCap) { near_key[at] = k; near_id[at] = id; }
+  });
   __syncthreads();
-  // the high byte b1 of the S-th largest key, and the count strictly above it
-  int b1 = 0, above = 0;
+  const int nn = n_near;
+  const bool in_lds = nn <= kNearCap;
+  // ---- the threshold: radix select (high byte, then low byte) over the LDS pairs, or over the
+  // whole row when they did not fit
+  auto radix_pass = [&](auto&& each) {
+    if (in_lds) {
+      for (int i = tid; i < nn; i += kExpandThreads) each(near_key[i]);
+    } else {
+      scan_row(row, nunits, [&](uint32_t bits, int) { each(bf16_key(bits)); });
+    }
+  };
+  int above = 0;
+  radix_pass([&](uint32_t k) { atomicAdd(&hist[k >> 8], 1); });
+  __syncthreads();
+  int b1 = 0;
   {
     int cum = 0;
     for (int h = 255; h >= 0; --h) {
@@ -107,18 +174,11 @@ __global__ __launch_bounds__(kDraftThreads) void draft_expand_kernel(DraftArgs a
     }
   }
   __syncthreads();
-  for (int i = tid; i < 256; i += kDraftThreads) hist[i] = 0;
+  for (int i = tid; i < 256; i += kExpandThreads) hist[i] = 0;
   __syncthreads();
-  // ---- pass 2: low byte inside bin b1
-  for (int u = tid; u < nunits; u += kDraftThreads) {
-    const uint4 x = *(const uint4*)(row + (size_t)u * 8);
-    const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t k = bf16_key((w4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-      if ((k >> 8) == (uint32_t)b1) atomicAdd(&hist[k & 0xFF], 1);
-    }
-  }
+  radix_pass([&](uint32_t k) {
+    if ((k >> 8) == (uint32_t)b1) atomicAdd(&hist[k & 0xFF], 1);
+  });
   __syncthreads();
   int b2 = 0;
   {
@@ -130,21 +190,20 @@ __global__ __launch_bounds__(kDraftThreads) void draft_expand_kernel(DraftArgs a
   }
   const uint32_t thr = ((uint32_t)b1 << 8) | (uint32_t)b2;
   const int need_eq = S - above;   // >= 1
-  // ---- pass 3: keys above the threshold, and the tokens at it
-  for (int u = tid; u < nunits; u += kDraftThreads) {
-    const uint4 x = *(const uint4*)(row + (size_t)u * 8);
-    const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t k = bf16_key((w4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-      if (k > thr) {
-        const int at = atomicAdd(&n_sel, 1);
-        if (at < kMaxDraftSupport) { sel_key[at] = k; sel_id[at] = u * 8 + e; }
-      } else if (k == thr) {
-        const int at = atomicAdd(&n_eq, 1);
-        if (at < kEqCap) eq_id[at] = u * 8 + e;
-      }
+  // ---- collection: keys above the threshold, and the tokens at it
+  auto collect = [&](uint32_t k, int id) {
+    if (k > thr) {
+      const int at = atomicAdd(&n_sel, 1);
+      if (at < kMaxDraftSupport) { sel_key[at] = k; sel_id[at] = id; }
+    } else if (k == thr) {
+      const int at = atomicAdd(&n_eq, 1);
+      if (at < kEqCap) eq_id[at] = id;
     }
+  };
+  if (in_lds) {
+    for (int i = tid; i < nn; i += kExpandThreads) collect(near_key[i], near_id[i]);
+  } else {
+    scan_row(row, nunits, [&](uint32_t bits, int id) { collect(bf16_key(bits), id); });
   }
   __syncthreads();
   if (n_eq > kEqCap) {
@@ -153,7 +212,7 @@ __global__ __launch_bounds__(kDraftThreads) void draft_expand_kernel(DraftArgs a
   }
   const int neq = min(n_eq, kEqCap);
   // the need_eq smallest ids among the tokens at the threshold: rank of each by id
-  for (int i = tid; i < neq; i += kDraftThreads) {
+  for (int i = tid; i < neq; i += kExpandThreads) {
     const int id = eq_id[i];
     int r = 0;
     for (int k = 0; k < neq; ++k) r += eq_id[k] < id;
@@ -161,7 +220,7 @@ __global__ __launch_bounds__(kDraftThreads) void draft_expand_kernel(DraftArgs a
   }
   __syncthreads();
   // the support by (key desc, id asc) and its token-id order
-  for (int i = tid; i < S; i += kDraftThreads) {
+  for (int i = tid; i < S; i += kExpandThreads) {
     const uint32_t k = sel_key[i];
     const int id = sel_id[i];
     int r = 0, ri = 0;
@@ -291,6 +350,7 @@ __global__ __launch_bounds__(kDraftThreads) void draft_expand_kernel(DraftArgs a
 // The next parents: the K best of depth d's candidates by (score desc, id asc); one block per
 // sequence (rank of each candidate = the number ahead of it).
 __global__ __launch_bounds__(kDraftThreads) void draft_frontier_kernel(DraftArgs a, int d, int32_t* frontier_out) {
+  __shared__ double sc[kMaxDraftCandidates];
   const int b = blockIdx.x, tid = threadIdx.x;
   const size_t cb = (size_t)b * a.C;
   const int c0 = a.base[d], n = a.base[d + 1] - c0;
@@ -299,12 +359,14 @@ __global__ __launch_bounds__(kDraftThreads) void draft_frontier_kernel(DraftArgs
     a.frontier[(size_t)b * a.K + i] = -1;
     if (frontier_out) frontier_out[(size_t)b * a.K + i] = -1;
   }
+  for (int i = tid; i < n; i += kDraftThreads) sc[i] = a.cand_score[cb + c0 + i];
   __syncthreads();
   for (int i = tid; i < n; i += kDraftThreads) {
-    const double s = a.cand_score[cb + c0 + i];
+    const double s = sc[i];
     int r = 0;
+#pragma unroll 8
     for (int t = 0; t < n; ++t) {
-      const double st = a.cand_score[cb + c0 + t];
+      const double st = sc[t];
       r += st > s || (st == s && t < i);
     }
     if (r < kn) {
@@ -315,39 +377,109 @@ __global__ __launch_bounds__(kDraftThreads) void draft_frontier_kernel(DraftArgs
 }
 
 // Global prune to R nodes by (score desc, depth asc, id asc); nodes renumbered by (depth, id),
-// which is ascending id; outputs per sequence b at rows b * (R + 1) ...
-__global__ __launch_bounds__(1024) void draft_prune_kernel(DraftArgs a, DraftOut o) {
+// which is ascending id; outputs per sequence b at rows b * (R + 1) ... (b + 1) * (R + 1) - 1.
+__global__ __launch_bounds__(kExpandThreads) void draft_prune_kernel(DraftArgs a, DraftOut o) {
   __shared__ uint8_t kept[kMaxDraftCandidates];
   __shared__ int new_id[kMaxDraftCandidates];
+  __shared__ uint64_t key[kMaxDraftCandidates];
+  __shared__ uint8_t dp[kMaxDraftCandidates];
+  __shared__ int row_cand[kMaxDraftCandidates];   // also the candidates tied at the threshold
+  __shared__ int hist[256];
   __shared__ int red[16];
+  __shared__ int n_rows, n_tie, sel_digit, sel_above;
   const int b = blockIdx.x, tid = threadIdx.x;
   const size_t cb = (size_t)b * a.C;
   const int C = a.base[a.D + 1], R = a.R;
-  for (int c = tid; c < C; c += blockDim.x) {
-    int k = c == 0;
-    if (c > 0) {
-      const double s = a.cand_score[cb + c];
-      const int dc = a.cand_depth[cb + c];
-      int r = 0;
-      for (int t = 1; t < C; ++t) {
-        const double st = a.cand_score[cb + t];
-        const int dt = a.cand_depth[cb + t];
-        r += st > s || (st == s && (dt < dc || (dt == dc && t < c)));
+  // the scores are products of probabilities (>= 0): their fp64 bit patterns order as integers
+  for (int c = tid; c < C; c += kExpandThreads) {
+    key[c] = (uint64_t)__double_as_longlong(a.cand_score[cb + c]);
+    dp[c] = a.cand_depth[cb + c];
+    kept[c] = 1;
+  }
+  if (tid == 0) n_tie = 0;
+  __syncthreads();
+  const int Rk = min(R, C - 1);   // non-root candidates kept
+  if (Rk < C - 1) {
+    // the Rk-th largest key among candidates 1..C-1: radix select, one byte per pass from the top
+    uint64_t prefix = 0;
+    int above = 0;
+    for (int shift = 56; shift >= 0; shift -= 8) {
+      for (int i = tid; i < 256; i += kExpandThreads) hist[i] = 0;
+      __syncthreads();
+      for (int c = 1 + tid; c < C; c += kExpandThreads) {
+        const uint64_t k = key[c];
+        if (shift == 56 || ((k ^ prefix) >> (shift + 8)) == 0) atomicAdd(&hist[(k >> shift) & 0xFF], 1);
       }
-      k = r < R;
+      __syncthreads();
+      // bins from the top (waves 0-3, one bin per lane): inclusive scan; the bin where the count
+      // reaches Rk is the next byte
+      int v = 0, inc = 0;
+      if (tid < 256) {
+        v = hist[255 - tid];
+        inc = v;
+        const int lane = tid & 63;
+        for (int o2 = 1; o2 < 64; o2 <<= 1) {
+          const int y = __shfl_up(inc, o2, 64);
+          if (lane >= o2) inc += y;
+        }
+        if (lane == 63) red[tid >> 6] = inc;
+      }
+      __syncthreads();
+      if (tid < 256) {
+        for (int w = 0; w < (tid >> 6); ++w) inc += red[w];
+        if (above + inc >= Rk && above + inc - v < Rk) { sel_digit = 255 - tid; sel_above = above + inc - v; }
+      }
+      __syncthreads();
+      prefix |= (uint64_t)sel_digit << shift;
+      above = sel_above;
     }
-    kept[c] = (uint8_t)k;
+    // candidates tied at the threshold: the first Rk - above by (depth asc, id asc)
+    for (int c = 1 + tid; c < C; c += kExpandThreads) {
+      const uint64_t k = key[c];
+      kept[c] = k > prefix;
+      if (k == prefix) row_cand[atomicAdd(&n_tie, 1)] = c;
+    }
+    __syncthreads();
+    const int nt = n_tie, need = Rk - above;
+    for (int i = tid; i < nt; i += kExpandThreads) {
+      const int c = row_cand[i], dc = dp[c];
+      int r = 0;
+      for (int t = 0; t < nt; ++t) {
+        const int ct = row_cand[t], dt = dp[ct];
+        r += dt < dc || (dt == dc && ct < c);
+      }
+      kept[c] = r < need;
+    }
   }
   __syncthreads();
-  if (tid == 0) {   // ids of the kept nodes in ascending candidate id (the root first)
-    int n = 0;
-    for (int c = 0; c < C; ++c) new_id[c] = kept[c] ? n++ : -1;
-    red[0] = n;
+  // ids of the kept nodes in ascending candidate id (the root first): exclusive block scan of
+  // the kept flags, two candidates per thread
+  {
+    const int c0 = 2 * tid;
+    const int k0 = c0 < C ? kept[c0] : 0, k1 = c0 + 1 < C ? kept[c0 + 1] : 0;
+    int inc = k0 + k1;
+    const int lane = tid & 63, wv = tid >> 6;
+    for (int o2 = 1; o2 < 64; o2 <<= 1) {
+      const int y = __shfl_up(inc, o2, 64);
+      if (lane >= o2) inc += y;
+    }
+    if (lane == 63) red[wv] = inc;
+    __syncthreads();
+    int before = inc - (k0 + k1);
+    int total = 0;
+    for (int w = 0; w < 16; ++w) {
+      before += w < wv ? red[w] : 0;
+      total += red[w];
+    }
+    if (c0 < C) new_id[c0] = k0 ? before : -1;
+    if (c0 + 1 < C) new_id[c0 + 1] = k1 ? before + k0 : -1;
+    if (tid == 0) n_rows = 0;
+    __syncthreads();
+    if (tid == 0) red[0] = total;
   }
-  __syncthreads();
   const size_t ob = (size_t)b * (R + 1);
   uint32_t err = 0;
-  for (int c = tid; c < C; c += blockDim.x) {
+  for (int c = tid; c < C; c += kExpandThreads) {
     const int v = new_id[c];
     if (v < 0) continue;
     const int p = a.cand_parent[cb + c];
@@ -355,30 +487,30 @@ __global__ __launch_bounds__(1024) void draft_prune_kernel(DraftArgs a, DraftOut
     if (c > 0 && pv < 0) err |= TAV_DEV_BAD_PARENT;   // not ancestor-closed (cannot happen)
     o.parent[ob + v] = pv;
     o.token[ob + v] = c == 0 ? -1 : a.cand_token[cb + c];
-    o.sampled[ob + v] = c == 0 ? 0 : a.cand_sampled[cb + c];
+    const uint8_t smp = c == 0 ? 0 : a.cand_sampled[cb + c];
+    o.sampled[ob + v] = smp;
     if (o.cand_id) o.cand_id[ob + v] = c;
-    o.draft_row[ob + v] = -1;
+    // a kept sampled node: its parent's draft row goes to the parent's output row (a pool has
+    // at most one sampled slot, so each parent is listed once)
+    if (smp && pv >= 0) row_cand[atomicAdd(&n_rows, 1)] = p;
   }
   __syncthreads();
-  // a kept sampled node: its parent's draft row goes to the parent's output row
-  for (int c = tid; c < C; c += blockDim.x) {
+  for (int c = tid; c < C; c += kExpandThreads) {
     const int v = new_id[c];
-    if (v <= 0 || !a.cand_sampled[cb + c]) continue;
-    const int p = a.cand_parent[cb + c];
-    const int pv = new_id[p];
-    if (pv < 0) continue;
-    o.draft_row[ob + pv] = (int)(ob + pv);
+    if (v >= 0) o.draft_row[ob + v] = -1;
   }
   __syncthreads();
-  for (int c = 0; c < C; ++c) {
+  const int nr = n_rows;
+  for (int r = tid; r < nr; r += kExpandThreads) {
+    const int v = new_id[row_cand[r]];
+    o.draft_row[ob + v] = (int)(ob + v);
+  }
+  for (int e = tid; e < nr * a.S; e += kExpandThreads) {
+    const int r = e / a.S, i = e - r * a.S;
+    const int c = row_cand[r];
     const int v = new_id[c];
-    if (v < 0 || o.draft_row[ob + v] < 0) continue;
-    const int32_t* ridx = a.row_idx + (cb + c) * a.S;
-    const float* rval = a.row_val + (cb + c) * a.S;
-    for (int i = tid; i < a.S; i += blockDim.x) {
-      o.draft_idx[(ob + v) * a.S + i] = ridx[i];
-      o.draft_val[(ob + v) * a.S + i] = rval[i];
-    }
+    o.draft_idx[(ob + v) * a.S + i] = a.row_idx[(cb + c) * a.S + i];
+    o.draft_val[(ob + v) * a.S + i] = a.row_val[(cb + c) * a.S + i];
   }
   if (red[0] != R + 1) err |= TAV_DEV_PLAN_MISMATCH;
   if (err) {
@@ -391,7 +523,7 @@ __global__ __launch_bounds__(1024) void draft_prune_kernel(DraftArgs a, DraftOut
 
 hipError_t launch_draft_expand(const DraftArgs& a, int d, const uint16_t* logits, const float* uniforms,
                                int32_t* frontier_out, hipStream_t s) {
-  draft_expand_kernel<<<a.B * a.Kd, kDraftThreads, 0, s>>>(a, d, logits, uniforms);
+  draft_expand_kernel<<<a.B * a.Kd, kExpandThreads, 0, s>>>(a, d, logits, uniforms);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   draft_frontier_kernel<<<a.B, kDraftThreads, 0, s>>>(a, d, frontier_out);
@@ -399,7 +531,7 @@ hipError_t launch_draft_expand(const DraftArgs& a, int d, const uint16_t* logits
 }
 
 hipError_t launch_draft_prune(const DraftArgs& a, const DraftOut& o, hipStream_t s) {
-  draft_prune_kernel<<<a.B, 1024, 0, s>>>(a, o);
+  draft_prune_kernel<<<a.B, kExpandThreads, 0, s>>>(a, o);
   return hipGetLastError();
 }
 
