@@ -10,8 +10,9 @@
 // E / F).  p = softmax(logits / T) (RheoSampling Section 5.4).
 //
 // The vocabulary work of every node (M, S, Z, p and q~ at the children's tokens,
-// the would-be final draw) is done by the workers of vocab_worker.h, one
-// 512-thread workgroup per compute unit taking nodes from a queue.  walk_kernel
+// the would-be final draw) is done by the kernels of vocab_worker.h: streaming
+// workers (512-thread workgroups taking nodes from a queue), then the pick of
+// every node (one wave each).  walk_kernel
 // (one wave per sequence) then takes the accept/reject decisions in fp64 from
 // these values.
 #include "tav_internal.h"
@@ -20,13 +21,38 @@
 namespace tav {
 namespace {
 
-// Workers that take nodes from the device queue until none is left: 512 threads, one workgroup
-// per compute unit.
-using WorkerCfg = vw::Cfg<512, 8>;
+// Streaming workers that take nodes from the device queue until none is left (as many workgroups
+// per compute unit as fit).  Shape: threads, sixteen-byte units per thread and step, KB of a dense
+// draft node's logits row kept in LDS for its second pass, waves per SIMD the registers allow.
+#ifndef TAV_VW_THREADS
+#define TAV_VW_THREADS 512
+#endif
+#ifndef TAV_VW_UNITS
+#define TAV_VW_UNITS 8
+#endif
+#ifndef TAV_VW_CACHE_KB
+#define TAV_VW_CACHE_KB 128
+#endif
+#ifndef TAV_VW_WAVES_PER_EU
+#define TAV_VW_WAVES_PER_EU 2
+#endif
+using WorkerCfg = vw::Cfg<TAV_VW_THREADS, TAV_VW_UNITS, TAV_VW_CACHE_KB>;
 template <typename LT>
-__global__ __launch_bounds__(512) void vocab_worker_kernel(VocabArgs a) {
+__global__ __launch_bounds__(TAV_VW_THREADS) __attribute__((amdgpu_waves_per_eu(TAV_VW_WAVES_PER_EU)))
+void vocab_worker_kernel(VocabArgs a) {
   __shared__ vw::Lds<WorkerCfg> L;
-  vw::vocab_worker<LT, WorkerCfg>(a, L);
+  vw::vocab_stream<LT, WorkerCfg>(a, L);
+}
+
+// The pick of every node: one wave per node, kPickWaves nodes per workgroup.
+constexpr int kPickWaves = 4;
+template <typename LT>
+__global__ __launch_bounds__(64 * kPickWaves) void pick_kernel(VocabArgs a) {
+  __shared__ vw::PickLds P[kPickWaves];
+  const int wave = threadIdx.x >> 6;
+  const int v = blockIdx.x * kPickWaves + wave;
+  if (v >= a.N) return;
+  vw::pick_node<LT>(a, P[wave], v);
 }
 
 constexpr int kWalkLds = 1024;  // nodes whose walk data fit in LDS
@@ -192,11 +218,15 @@ __global__ __launch_bounds__(64) void walk_kernel(WalkArgs a) {
 template <typename LT>
 hipError_t launch_vocab_t(const VocabArgs& a, int num_cus, hipStream_t s) {
   int per_cu = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, vocab_worker_kernel<LT>, 512, 0);
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, vocab_worker_kernel<LT>,
+                                                              WorkerCfg::kThreads, 0);
   if (e != hipSuccess) return e;
   if (per_cu < 1) per_cu = 1;
   const int grid = a.N < per_cu * num_cus ? a.N : per_cu * num_cus;
-  vocab_worker_kernel<LT><<<grid, 512, 0, s>>>(a);
+  vocab_worker_kernel<LT><<<grid, WorkerCfg::kThreads, 0, s>>>(a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  pick_kernel<LT><<<(a.N + kPickWaves - 1) / kPickWaves, 64 * kPickWaves, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -187,6 +187,8 @@ tav_status make_plan(const tav_problem* p, const tav_presto_io* pr, Plan* out,
   P.off_order = o; o = align_up(o + (size_t)(p->vocab > 0 ? P.N : 0) * 4);
   P.off_seq_err = o; o = align_up(o + (size_t)P.B * 4);
   if (p->vocab > 0) P.nch = ceil_div(ceil_div(p->vocab, p->dtype == TAV_BF16 ? 8 : 4), 64);
+  P.off_cw = o; o = align_up(o + (size_t)(p->vocab > 0 ? P.N : 0) * P.nch * 4);
+  P.off_rec = o; o = align_up(o + (size_t)(p->vocab > 0 ? P.N : 0) * sizeof(NodeRec));
   P.total = o;
   *out = P;
   return TAV_OK;
@@ -370,6 +372,8 @@ VocabArgs vocab_args(const tav_problem* p, const Plan& P, const tav_tree* t, con
   va.B = P.B; va.N = P.N; va.V = p->vocab; va.R = io->num_draft_rows;
   va.queue = (int32_t*)(status + kCounterWord);
   va.order = ws_at<int32_t>(ws, P.off_order);
+  va.cw = ws_at<float>(ws, P.off_cw);
+  va.rec = ws_at<NodeRec>(ws, P.off_rec);
   va.nch = P.nch;
   return va;
 }

@@ -43,7 +43,7 @@ struct Plan {
   size_t off_status = 0, off_chain = 0, off_mask = 0, off_seq_rb = 0, off_rb_seq = 0,
          off_rb_tile = 0, off_tail_blk = 0, off_wg_rb = 0, off_wg_tile = 0, off_rb_meta = 0, off_ktail = 0, off_vtail = 0, off_part_o = 0,
          off_part_lse = 0, off_stats = 0, off_term = 0, off_child_p = 0, off_child_q = 0,
-         off_presto = 0, off_order = 0, off_seq_err = 0, total = 0;
+         off_presto = 0, off_order = 0, off_seq_err = 0, off_cw = 0, off_rec = 0, total = 0;
   int nch = 0;            // vocabulary chunks (64 sixteen-byte units) per row
 };
 
@@ -103,6 +103,22 @@ struct AttnArgs {
   float scale;        // softmax scale (natural)
 };
 
+// What the vocabulary streaming kernel leaves for the pick kernel, per node.
+struct NodeRec {
+  double S;      // sum exp(l / T - M)
+  double Z;      // sum (p - q~)+ over the row (dense draft rows with a sampled child)
+  float M;       // max l / T (0 when no logit is finite); greedy rows: max l
+  int A;         // greedy rows: the argmax (smallest id among equal maxima), else -1
+  int b;         // the node's sequence
+  uint32_t err;  // errors found while streaming (TAV_DEV_* bits)
+  int flags;     // kRec* bits
+  int s0, n;     // the sequence's first node and node count
+  int pad;
+};
+constexpr int kRecResidual = 1;   // the chunk weights are those of (p - q~)+
+constexpr int kRecNoMass = 2;     // no finite logit
+constexpr int kRecGreedy = 4;     // temperature 0: M and A are the row's max and argmax
+
 struct VocabArgs {
   const void* logits;
   const float* temperature;
@@ -124,6 +140,8 @@ struct VocabArgs {
   uint32_t* seq_err;     // [B] device-detected errors of each sequence
   int32_t* queue;        // node counter of the workers' queue (cleared with the status word)
   const int32_t* order;  // [N] the nodes in the order the workers take them (nodes with a draft row first)
+  float* cw;             // [N, nch] chunk weights under p or (p - q~)+, from the streaming kernel
+  NodeRec* rec;          // [N] from the streaming kernel
   int B, N, V, R, nch;
 };
 

@@ -1,4 +1,5 @@
-// Per-node vocabulary work of the verification, done by one 512-thread workgroup per node.
+// Per-node vocabulary work of the verification: a streaming kernel (one workgroup per node,
+// taking nodes from a queue) and a pick kernel (one wave per node).
 //
 // RheoSampling, Section 3.3 Algorithm 1 (RheoVerification): the target distribution at
 // node v is p = softmax(l / T) (temperature only in sampling and verification, Section
@@ -9,26 +10,27 @@
 // sampled child this is the sequential rejection of Progressive Tree Drafting (Section
 // 3.2, Appendix E / F).
 //
-// For node v the worker computes, with the logits row streamed from HBM once:
+// For node v the streaming kernel computes, with the logits row streamed from HBM once:
 //   M = max l / T, S = sum exp(l / T - M)                (the normaliser of p),
-//   Z = sum (p - q~)+ when v has a sampled child          (the normaliser of r),
-//   p and q~ at each child's token                       (the walk's tests),
-//   the token the final draw at v would give               (inverse CDF in token order with
-//                                                           u[v][1], deterministic children's
-//                                                           tokens removed).
+//   Z = sum (p - q~)+ when v has a dense draft row        (the normaliser of r),
+//   the weight of every chunk of 512 (bf16) or 256 (f32) tokens under p, or under (p - q~)+,
+// and leaves them in the workspace; the pick kernel then takes, for every node at once, p and q~
+// at each child's token (the walk's tests) and the token the final draw at v would give (inverse
+// CDF in token order with u[v][1], deterministic children's tokens removed).
 // Pass 1 streams the row in steps of 64 KB (512 threads x 8 sixteen-byte units, the next step's
 // loads in flight while the current one is summed): each wave keeps the largest raw logit m of
 // its part of the step as a reference and writes sum exp2(l log2e / T - ref(m)) of every chunk of
 // 64 units (one unit per lane) to LDS.  M and S follow from these pieces in fp64.  Pass 2 (nodes
-// with a sampled child) streams the draft row with the logits row again (the second read of a
-// row just read mostly hits the cache) and replaces the chunk weights with those of (p - q~)+.
-// The pick then runs on one wave: point values of the children, the deterministic children's
-// weights taken out of their chunks, an fp64 scan over the chunks for u * W, and one chunk re-read.
-// With sparse draft rows (at most 128 support tokens per row, RheoSampling Section 3.2) there is no
-// pass 2: the support's min(p, q~) is taken out of the chunk weights of p and Z is summed over the
-// support.  Nodes are taken from a device queue, in the order of an index list (nodes with a dense
-// draft row first, so that the long items do not come last); a worker never waits for another
-// workgroup.
+// with a sampled child and a dense draft row) streams the draft row with the logits row again
+// (the row's first 128 KB kept in LDS, the rest mostly from the cache) and replaces the chunk
+// weights with those of (p - q~)+.  Greedy rows (T = 0) take one pass for the argmax.  The pick:
+// point values of the children, the deterministic children's weights taken out of their chunks,
+// an fp64 scan over the chunks for u * W, and one chunk re-read.  With sparse draft rows (at most
+// 128 support tokens per row, RheoSampling Section 3.2) there is no pass 2: the pick takes the
+// support's min(p, q~) out of the chunk weights of p and sums Z over the support.  Nodes are taken
+// from a device queue, in the order of an index list (nodes with a dense draft row first, so that
+// the long items do not come last); a worker never waits for another workgroup, and claims its
+// next node while it streams the current one.
 #pragma once
 
 #include "tav_internal.h"
@@ -40,7 +42,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 // A worker of NT threads reading NU sixteen-byte units per thread and step.  A chunk is 64 units,
 // one per lane of a wave, so chunk k * waves + w of a step is unit k of every lane of wave w.
-template <int NT, int NU>
+template <int NT, int NU, int CACHE_KB>
 struct Cfg {
   static constexpr int kThreads = NT;
   static constexpr int kWaves = NT / 64;
@@ -50,8 +52,8 @@ struct Cfg {
   static constexpr int kMaxSteps = kMaxChunks / kChunksPerStep;   // rows of up to kMaxChunks chunks
   static constexpr int kMaxPieces = kMaxSteps * kWaves;           // (step, wave) references
   // the first steps of a logits row kept in LDS for the second pass (nodes with a draft row)
-  static constexpr int kCacheSteps = (128 * 1024) / (kStepUnits * 16);
-  static constexpr int kCacheUnits = kCacheSteps * kStepUnits;
+  static constexpr int kCacheSteps = (CACHE_KB * 1024) / (kStepUnits * 16);
+  static constexpr int kCacheUnits = kCacheSteps > 0 ? kCacheSteps * kStepUnits : 1;
   static_assert((NU == 2 || NU % 4 == 0) && NU <= 64 && NT % 64 == 0, "worker shape");
 };
 
@@ -62,23 +64,23 @@ struct Lds {
   float ref_m[C::kMaxPieces];                // largest raw logit of each (step, wave) piece
   double ref_s[C::kMaxPieces];               // sum exp2(l log2e / T - ref) of each piece
   double red_d[C::kWaves];
-  int kid_id[kMaxChildren];                  // children of the node (sequence-local ids, ascending) ...
-  int kid_tok[kMaxChildren];                 // ... their tokens
-  uint8_t kid_smp[kMaxChildren];             // ... and sampled flags
-  float kid_w[kMaxChildren];                 // ... and their weights in the final draw's chunks
-  int kid_cnt[C::kWaves];                    // children found by each wave in one round of the scan
   float g_best[C::kWaves];                   // greedy rows: each wave's largest logit ...
   int g_idx[C::kWaves];                      // ... and its smallest token id
-  int item, cnt, nk, ns, err;
-  union {
-    uint4 lc[C::kCacheUnits];                // dense draft rows: the logits row's first kCacheSteps
+  int item, cnt, ns, err;
+  uint4 lc[C::kCacheUnits];                  // dense draft rows: the logits row's first kCacheSteps
                                              // steps (each thread its own units)
-    struct {                                 // sparse draft rows: the node's support (ascending ids),
-      int idx[kMaxDraftSupport];             // q~ there and the part of each token's p taken out of
-      float val[kMaxDraftSupport];           // its chunk (min(p, q~))
-      float take[kMaxDraftSupport];
-    } sp;
-  };
+};
+
+// The pick's LDS, one per wave.
+struct PickLds {
+  float cw[kMaxChunks];
+  int kid_id[kMaxChildren];                  // children of the node (sequence-local ids, ascending) ...
+  int kid_tok[kMaxChildren];                 // ... their tokens
+  float kid_w[kMaxChildren];                 // ... their weights in the final draw's chunks
+  uint8_t kid_smp[kMaxChildren];             // ... and sampled flags
+  int sp_idx[kMaxDraftSupport];              // sparse draft row: support (ascending ids), q~ there
+  float sp_val[kMaxDraftSupport];            // and the part of each token's p taken out of its
+  float sp_take[kMaxDraftSupport];           // chunk (min(p, q~))
 };
 
 template <typename LT>
@@ -218,15 +220,13 @@ __device__ inline void better_of(float& best, int& bi, float ob, int oi) {
 // Greedy decoding (temperature 0; Progressive Tree Drafting, Section 3.2): the node's verification
 // token is its highest-probability prediction, the argmax of the logits (smallest id among equal
 // maxima).  One pass over the row (the first step's loads already in flight in cur) with no
-// exponentials; the walk accepts the child carrying that token.  Stats: M = max l, S = 1, Z = 0;
-// p at a child's token is 1 for the argmax and 0 otherwise; the would-be final token is the argmax.
+// exponentials; the walk accepts the child carrying that token.
 template <typename LT, class C>
-__device__ void greedy_node(const VocabArgs& a, Lds<C>& L, int v, int b, int s0, uint4 (&cur)[C::kUnits],
-                            const LT* row, int nunits, int nsteps) {
+__device__ void greedy_stream(const VocabArgs& a, Lds<C>& L, int v, int b, int s0, int n, uint4 (&cur)[C::kUnits],
+                              const LT* row, int nunits, int nsteps) {
   constexpr int kThreads = C::kThreads, kUnits = C::kUnits, kStepUnits = C::kStepUnits;
   constexpr int EPU = 16 / sizeof(LT);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int V = a.V;
   float best = -INFINITY;
   int bi = -1;
   bool bad = false;
@@ -266,54 +266,44 @@ __device__ void greedy_node(const VocabArgs& a, Lds<C>& L, int v, int b, int s0,
     if (any_bad) atomicOr(&L.err, (int)TAV_DEV_NONFINITE_LOGITS);
   }
   __syncthreads();
-  if (wave != 0) return;
-  float M = -INFINITY;
-  int A = -1;
+  if (tid == 0) {
+    float M = -INFINITY;
+    int A = -1;
 #pragma unroll
-  for (int w = 0; w < C::kWaves; ++w) better_of(M, A, L.g_best[w], L.g_idx[w]);
-  uint32_t err = (uint32_t)L.err;
-  if (L.nk > kMaxChildren) err |= TAV_DEV_TOO_MANY_CHILDREN;
-  if (M == -INFINITY) err |= TAV_DEV_NONFINITE_LOGITS;   // no finite logit: no prediction
-  const int nk = L.nk < kMaxChildren ? L.nk : kMaxChildren;
-  for (int k = lane; k < nk; k += 64) {
-    const int tk = L.kid_tok[k];
-    if (tk < 0 || tk >= V) err |= TAV_DEV_BAD_TOKEN;
-    for (int k2 = 0; k2 < k; ++k2)
-      if (L.kid_tok[k2] == tk) err |= TAV_DEV_DUP_SIBLING_TOKEN;
-    const int cid = s0 + L.kid_id[k];
-    a.child_p[cid] = tk == A ? 1.0 : 0.0;
-    a.child_q[cid] = 0.f;
-  }
-#pragma unroll
-  for (int d = 32; d > 0; d >>= 1) err |= (uint32_t)__shfl_xor((int)err, d);
-  if (lane == 0) {
-    a.stats[(size_t)v * 3 + 0] = M;
-    a.stats[(size_t)v * 3 + 1] = 1.f;
-    a.stats[(size_t)v * 3 + 2] = 0.f;
-    a.term_token[v] = M == -INFINITY ? -1 : A;
-    if (err) {
-      atomicOr(a.status, err);
-      atomicOr(a.seq_err + b, err);
-    }
+    for (int w = 0; w < C::kWaves; ++w) better_of(M, A, L.g_best[w], L.g_idx[w]);
+    NodeRec r;
+    r.S = 1.0;
+    r.Z = 0.0;
+    r.M = M;
+    r.A = A;
+    r.b = b;
+    r.err = (uint32_t)L.err;
+    r.flags = kRecGreedy;
+    r.s0 = s0;
+    r.n = n;
+    r.pad = 0;
+    a.rec[v] = r;
   }
 }
 
-// Everything the walk needs of node v.
+// The streaming part of node v: its sequence, whether it has a sampled child, then pass 1 (and
+// pass 2), the chunk weights and the node's record into the workspace.  Thread 0 claims the next
+// queue slot into qn (read back after the node).
 template <typename LT, class C>
-__device__ void process_node(const VocabArgs& a, Lds<C>& L, int v) {
+__device__ void stream_node(const VocabArgs& a, Lds<C>& L, int v, int& qn) {
   constexpr int kThreads = C::kThreads, kWaves = C::kWaves, kUnits = C::kUnits;
   constexpr int kStepUnits = C::kStepUnits, kChunksPerStep = C::kChunksPerStep;
   constexpr int TPC = 64 / kUnits;   // lanes per chunk total
   constexpr int EPU = 16 / sizeof(LT);
   constexpr int QPU = EPU / 4;
-  constexpr int CT = 64 * EPU;   // tokens per chunk
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int V = a.V, nunits = V / EPU, nch = a.nch;
   const int nsteps = (nunits + kStepUnits - 1) / kStepUnits;
   const LT* row = (const LT*)a.logits + (size_t)v * V;
-  // the first step's loads go out before anything else
+  // the first step's loads go out before anything else, then the claim of the next node
   uint4 cur[kUnits];
   load_step<LT, C>(cur, row, 0, tid, nunits);
+  if (tid == 0) qn = atomicAdd(a.queue, 1);
   // sequence of v: the number of sequence ends node_offsets[1..B] that are <= v
   if (tid == 0) { L.cnt = 0; L.ns = 0; L.err = 0; }
   __syncthreads();
@@ -331,53 +321,24 @@ __device__ void process_node(const VocabArgs& a, Lds<C>& L, int v) {
   const float invTl2 = invT * kLog2e;
   const int dr = a.draft_row[v];
   const bool dr_ok = dr >= 0 && dr < a.R;
-  // children of v in ascending id (a compaction with fixed order, so that everything computed from
-  // the list is the same on every run), the parent-array and temperature checks
+  // whether v has a sampled child (the pick checks the children in full)
   {
-    uint32_t err = 0;
-    int nk = 0, ns = 0;
-    for (int base = 0; base < n; base += kThreads) {
-      const int c = base + tid;
-      bool kid = false, smp = false;
-      if (c < n) {
-        const int pc = a.parent[s0 + c];
-        if (c == 0 ? pc != -1 : (pc < 0 || pc >= c)) err |= TAV_DEV_BAD_PARENT;
-        kid = c > 0 && pc == v - s0;
-        smp = kid && a.sampled[s0 + c] != 0;
-      }
-      const unsigned long long m = __ballot(kid);
-      const unsigned long long ms = __ballot(smp);
-      if (lane == 0) L.kid_cnt[wave] = __popcll(m);
-      __syncthreads();
-      int before = nk, total = 0;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const int cw = L.kid_cnt[w];
-        before += w < wave ? cw : 0;
-        total += cw;
-      }
-      if (kid) {
-        const int k = before + __popcll(m & ((1ull << lane) - 1ull));
-        if (k < kMaxChildren) {
-          L.kid_id[k] = c;
-          L.kid_tok[k] = a.token[s0 + c];
-          L.kid_smp[k] = smp;
-        }
-      }
-      if (lane == 0 && ms) atomicAdd(&L.ns, __popcll(ms));
-      nk += total;
-      __syncthreads();   // kid_cnt is reused by the next round
+    int ns = 0;
+    for (int c = tid + 1; c < n; c += kThreads) {
+      const int pc = a.parent[s0 + c];
+      const uint8_t sm = a.sampled[s0 + c];
+      ns += pc == v - s0 && sm != 0;
     }
-    if (tid == 0) L.nk = nk;
-    if (tid == 0 && !(Tb >= 0.f && Tb < INFINITY)) err |= TAV_DEV_BAD_TEMPERATURE;
-    if (err) atomicOr(&L.err, (int)err);
+    if (ns) atomicAdd(&L.ns, ns);
   }
+  __syncthreads();
   if (Tb == 0.f) {   // greedy decoding: the verification token is the argmax
-    greedy_node<LT, C>(a, L, v, b, s0, cur, row, nunits, nsteps);
+    greedy_stream<LT, C>(a, L, v, b, s0, n, cur, row, nunits, nsteps);
     return;
   }
   // ---- pass 1: per-piece references and sums, chunk weights relative to their piece
   float* part = L.part[wave];
+  const bool dense_draft = L.ns > 0 && dr_ok && a.K == 0;
   for (int s = 0; s < nsteps; ++s) {
     uint4 nxt[kUnits];
     if (s + 1 < nsteps) load_step<LT, C>(nxt, row, s + 1, tid, nunits);
@@ -391,7 +352,7 @@ __device__ void process_node(const VocabArgs& a, Lds<C>& L, int v) {
       }
     mx = wave_max_f(mx);
     const float r2 = ref_l2(mx, invT);
-    // a NaN or +inf logit makes the sum NaN, which is reported below
+    // a NaN or +inf logit makes the sum NaN, which is reported by the pick
     float su[kUnits];
     double sd = 0.0;
 #pragma unroll
@@ -403,7 +364,7 @@ __device__ void process_node(const VocabArgs& a, Lds<C>& L, int v) {
       }
       sd += (double)su[k];
     }
-    if (dr_ok && a.K == 0 && s < C::kCacheSteps) {
+    if (dense_draft && s < C::kCacheSteps) {
       // kept for the second pass, which reads them back in the same thread
 #pragma unroll
       for (int k = 0; k < kUnits; ++k) L.lc[s * kStepUnits + k * kThreads + tid] = cur[k];
@@ -437,11 +398,8 @@ __device__ void process_node(const VocabArgs& a, Lds<C>& L, int v) {
   }
   const double S = wave_sum_d(sc);
   const float invS = (float)(1.0 / S);
-  const int nk = L.nk < kMaxChildren ? L.nk : kMaxChildren;
-  const bool use_draft = L.ns > 0 && dr_ok;
-  const bool sparse = a.K > 0;
   double Zt = 0.0;
-  if (use_draft && !sparse) {
+  if (dense_draft) {
     // ---- pass 2: chunk weights of (p - q~)+ and their total Z.  Each step is taken in two
     // halves of kUnits / 2 units per thread, one half computed while the other's loads fly.
     constexpr int HU = kUnits / 2;
@@ -503,13 +461,137 @@ __device__ void process_node(const VocabArgs& a, Lds<C>& L, int v) {
     }
     __syncthreads();
   }
-  if (wave != 0) return;
-  // ---- the pick, on wave 0
-  uint32_t err = (uint32_t)L.err;
-  if (L.nk > kMaxChildren) err |= TAV_DEV_TOO_MANY_CHILDREN;
-  if (L.ns > 1) err |= TAV_DEV_MULTI_SAMPLED;
-  if (L.ns > 0 && !dr_ok) err |= TAV_DEV_NO_DRAFT;
+  float* cwo = a.cw + (size_t)v * nch;
+  for (int c = tid; c < nch; c += kThreads) cwo[c] = L.cw[c];
+  if (tid == 0) {
+    NodeRec r;
+    r.S = S;
+    r.Z = Zt;
+    r.M = M;
+    r.A = -1;
+    r.b = b;
+    r.err = (uint32_t)L.err;
+    r.flags = (dense_draft ? kRecResidual : 0) | (no_mass ? kRecNoMass : 0);
+    r.s0 = s0;
+    r.n = n;
+    r.pad = 0;
+    a.rec[v] = r;
+  }
+}
+
+// Takes nodes from the device queue (in the order of order[]: nodes with a dense draft row first)
+// until none is left.  Called by every thread of a workgroup of C::kThreads threads; L is the
+// workgroup's LDS.
+template <typename LT, class C>
+__device__ void vocab_stream(const VocabArgs& a, Lds<C>& L) {
+  if (threadIdx.x == 0) {
+    const int i = atomicAdd(a.queue, 1);
+    L.item = i < a.N ? a.order[i] : -1;
+  }
+  __syncthreads();
+  for (;;) {
+    const int v = L.item;
+    if (v < 0) return;
+    int qn = 0;
+    stream_node<LT, C>(a, L, v, qn);   // (every thread has read L.item before its first barrier)
+    if (threadIdx.x == 0) L.item = qn < a.N ? a.order[qn] : -1;
+    __syncthreads();   // LDS reused by the next node
+  }
+}
+
+// Everything the walk needs of node v, on one wave (P: the wave's LDS), from the streaming kernel's
+// record and chunk weights.
+template <typename LT>
+__device__ void pick_node(const VocabArgs& a, PickLds& P, int v) {
+  constexpr int EPU = 16 / sizeof(LT);
+  constexpr int CT = 64 * EPU;   // tokens per chunk
+  const int lane = threadIdx.x & 63;
+  const int V = a.V, nch = a.nch;
+  // every load that does not depend on another goes out first: the record, the draft row index,
+  // the uniform, this lane's chunk weights, then the children's fields
+  const NodeRec rec = a.rec[v];
+  const int dr = a.draft_row[v];
+  const float uf = a.uniforms[(size_t)v * 2 + 1];
+  const int b = rec.b, s0 = rec.s0, n = rec.n;
+  const float Tb = a.temperature[b];
+  const float invT = 1.f / Tb;
+  const float invTl2 = invT * kLog2e;
+  const bool dr_ok = dr >= 0 && dr < a.R;
+  uint32_t err = rec.err;
+  if (!(rec.flags & kRecGreedy)) {
+    const float* cwi = a.cw + (size_t)v * nch;
+    for (int c = lane; c < nch; c += 64) P.cw[c] = cwi[c];
+  }
+  // children of v in ascending id (a compaction with fixed order, so that everything computed from
+  // the list is the same on every run), the parent-array and temperature checks
+  int nk = 0, ns = 0;
+  for (int base = 0; base < n; base += 64) {
+    const int c = base + lane;
+    bool kid = false, smp = false;
+    int tk = 0;
+    if (c < n) {
+      const int pc = a.parent[s0 + c];
+      const uint8_t sm = a.sampled[s0 + c];
+      tk = a.token[s0 + c];
+      if (c == 0 ? pc != -1 : (pc < 0 || pc >= c)) err |= TAV_DEV_BAD_PARENT;
+      kid = c > 0 && pc == v - s0;
+      smp = kid && sm != 0;
+    }
+    const unsigned long long m = __ballot(kid);
+    if (kid) {
+      const int k = nk + __popcll(m & ((1ull << lane) - 1ull));
+      if (k < kMaxChildren) {
+        P.kid_id[k] = c;
+        P.kid_tok[k] = tk;
+        P.kid_smp[k] = smp;
+      }
+    }
+    nk += __popcll(m);
+    ns += __popcll(__ballot(smp));
+  }
+  if (!(Tb >= 0.f && Tb < INFINITY)) err |= TAV_DEV_BAD_TEMPERATURE;
+  if (nk > kMaxChildren) err |= TAV_DEV_TOO_MANY_CHILDREN;
+  nk = nk < kMaxChildren ? nk : kMaxChildren;
+  wave_sync();
+  if (rec.flags & kRecGreedy) {
+    const float M = rec.M;
+    const int A = rec.A;
+    if (M == -INFINITY) err |= TAV_DEV_NONFINITE_LOGITS;   // no finite logit: no prediction
+    for (int k = lane; k < nk; k += 64) {
+      const int tk = P.kid_tok[k];
+      if (tk < 0 || tk >= V) err |= TAV_DEV_BAD_TOKEN;
+      for (int k2 = 0; k2 < k; ++k2)
+        if (P.kid_tok[k2] == tk) err |= TAV_DEV_DUP_SIBLING_TOKEN;
+      const int cid = s0 + P.kid_id[k];
+      a.child_p[cid] = tk == A ? 1.0 : 0.0;
+      a.child_q[cid] = 0.f;
+    }
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) err |= (uint32_t)__shfl_xor((int)err, d);
+    if (lane == 0) {
+      a.stats[(size_t)v * 3 + 0] = M;
+      a.stats[(size_t)v * 3 + 1] = 1.f;
+      a.stats[(size_t)v * 3 + 2] = 0.f;
+      a.term_token[v] = M == -INFINITY ? -1 : A;
+      if (err) {
+        atomicOr(a.status, err);
+        atomicOr(a.seq_err + b, err);
+      }
+    }
+    return;
+  }
+  const float M = rec.M;
+  const float Ml2 = M * kLog2e;
+  const double S = rec.S;
+  const float invS = (float)(1.0 / S);
+  const bool no_mass = (rec.flags & kRecNoMass) != 0;
+  const bool use_draft = ns > 0 && dr_ok;
+  const bool sparse = a.K > 0;
+  double Zt = rec.Z;
+  if (ns > 1) err |= TAV_DEV_MULTI_SAMPLED;
+  if (ns > 0 && !dr_ok) err |= TAV_DEV_NO_DRAFT;
   if (no_mass || !(S > 0.0 && S < INFINITY)) err |= TAV_DEV_NONFINITE_LOGITS;
+  if (((rec.flags & kRecResidual) != 0) != (use_draft && !sparse)) err |= TAV_DEV_PLAN_MISMATCH;
   // sparse draft row (RheoSampling Section 3.2: support of at most 128 tokens, q~ = 0 elsewhere):
   // outside the support (p - q~)+ = p, so the chunk weights of p only lose min(p, q~) at the
   // support tokens, and Z = sum (p - q~)+ = sum over the support of (q~ - p)+ (the two sides of
@@ -519,10 +601,11 @@ __device__ void process_node(const VocabArgs& a, Lds<C>& L, int v) {
     int lo = 0, hi = K;
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
-      if (L.sp.idx[mid] < tok) lo = mid + 1; else hi = mid;
+      if (P.sp_idx[mid] < tok) lo = mid + 1; else hi = mid;
     }
-    return lo < K && L.sp.idx[lo] == tok ? L.sp.val[lo] : 0.f;
+    return lo < K && P.sp_idx[lo] == tok ? P.sp_val[lo] : 0.f;
   };
+  wave_sync();
   if (use_draft && sparse) {
     const int32_t* didx = a.draft_idx + (size_t)dr * K;
     const float* dval = a.draft_val + (size_t)dr * K;
@@ -541,59 +624,79 @@ __device__ void process_node(const VocabArgs& a, Lds<C>& L, int v) {
       } else {
         err |= TAV_DEV_BAD_DRAFT;
       }
-      L.sp.idx[j] = ok ? tk : -1;
-      L.sp.val[j] = ok ? qj : 0.f;
-      L.sp.take[j] = take;
+      P.sp_idx[j] = ok ? tk : -1;
+      P.sp_val[j] = ok ? qj : 0.f;
+      P.sp_take[j] = take;
     }
     Zt = wave_sum_d(zl);
     wave_sync();
     // each chunk's support tokens are consecutive entries; the last entry of a chunk's run sums the
     // run in order and takes it out of the chunk (one lane per chunk, a fixed order of additions)
     for (int j = lane; j < K; j += 64) {
-      const int tk = L.sp.idx[j];
+      const int tk = P.sp_idx[j];
       if (tk < 0) continue;
       const int c = tk / CT;
-      const int nx = j + 1 < K ? L.sp.idx[j + 1] : -1;
+      const int nx = j + 1 < K ? P.sp_idx[j + 1] : -1;
       if (nx >= 0 && nx / CT == c) continue;
       int j0 = j;
-      while (j0 > 0 && L.sp.idx[j0 - 1] >= 0 && L.sp.idx[j0 - 1] / CT == c) --j0;
+      while (j0 > 0 && P.sp_idx[j0 - 1] >= 0 && P.sp_idx[j0 - 1] / CT == c) --j0;
       float t = 0.f;
-      for (int i = j0; i <= j; ++i) t += L.sp.take[i];
-      L.cw[c] -= t;
+      for (int i = j0; i <= j; ++i) t += P.sp_take[i];
+      P.cw[c] -= t;
     }
     wave_sync();
   }
-  // children: point values for the walk; deterministic children leave the final draw
+  // children: point values for the walk; deterministic children leave the final draw.  Children
+  // 0..63 are also held one per lane (token; -1 for a sampled child or one whose token is out of
+  // range, which leave the final draw untouched) and read back with readlane, without LDS round
+  // trips; children past 64 (up to kMaxChildren) come from LDS.
+  int det_r = -1;
+  float kw_r = 0.f;
   for (int k = lane; k < nk; k += 64) {
-    const int tk = L.kid_tok[k];
+    const int tk = P.kid_tok[k];
     if (tk < 0 || tk >= V) err |= TAV_DEV_BAD_TOKEN;
-    for (int k2 = 0; k2 < k; ++k2)
-      if (L.kid_tok[k2] == tk) err |= TAV_DEV_DUP_SIBLING_TOKEN;
+    if (k < 64) {
+      for (int k2 = 0; k2 < min(nk, 64); ++k2)
+        if (k2 < k && __builtin_amdgcn_readlane(tk, k2) == tk) err |= TAV_DEV_DUP_SIBLING_TOKEN;
+    } else {
+      for (int k2 = 0; k2 < k; ++k2)
+        if (P.kid_tok[k2] == tk) err |= TAV_DEV_DUP_SIBLING_TOKEN;
+    }
     if (tk >= 0 && tk < V) {
       const float z = logit_at<LT>(a.logits, (size_t)v * V + tk);
       const float qz = !use_draft ? 0.f : sparse ? sp_q(tk) : a.draft[(size_t)dr * V + tk];
-      const int cid = s0 + L.kid_id[k];
+      const int cid = s0 + P.kid_id[k];
       a.child_p[cid] = exp((double)(z * invT) - (double)M) / S;
       a.child_q[cid] = use_draft ? qz : 0.f;
       const float p = __builtin_amdgcn_exp2f(z * invTl2 - Ml2) * invS;
-      L.kid_w[k] = use_draft ? fmaxf(0.f, p - qz) : p;
+      const float kw = use_draft ? fmaxf(0.f, p - qz) : p;
+      P.kid_w[k] = kw;
+      if (k < 64) {
+        det_r = P.kid_smp[k] ? -1 : tk;
+        kw_r = kw;
+      }
     }
   }
   wave_sync();
+  auto det_tok = [&](int k) -> int {   // token of deterministic child k, or -1
+    if (k < 64) return __builtin_amdgcn_readlane(det_r, k);
+    const int tk = P.kid_tok[k];
+    return !P.kid_smp[k] && tk >= 0 && tk < V ? tk : -1;
+  };
   // the deterministic children's weights taken out of their chunks, one lane, in child order (a
   // fixed order of the float subtractions: two runs give the same chunk weights bit for bit)
-  if (lane == 0)
-    for (int k = 0; k < nk; ++k) {
-      const int tk = L.kid_tok[k];
-      if (!L.kid_smp[k] && tk >= 0 && tk < V) L.cw[tk / CT] -= L.kid_w[k];
-    }
+  for (int k = 0; k < nk; ++k) {
+    const int tk = det_tok(k);
+    const float kw = k < 64 ? __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(kw_r), k)) : P.kid_w[k];
+    if (lane == 0 && tk >= 0) P.cw[tk / CT] -= kw;
+  }
   wave_sync();
   // fp64 scan over chunks: lane l owns chunks [l * per, (l + 1) * per)
   const int per = (nch + 63) / 64;
   double pm = 0.0;
   for (int k = 0; k < per; ++k) {
     const int c = lane * per + k;
-    if (c < nch) pm += (double)fmaxf(L.cw[c], 0.f);
+    if (c < nch) pm += (double)fmaxf(P.cw[c], 0.f);
   }
   double incl = pm;
 #pragma unroll
@@ -602,7 +705,7 @@ __device__ void process_node(const VocabArgs& a, Lds<C>& L, int v) {
     if (lane >= d) incl += y;
   }
   const double W = __shfl(incl, 63);
-  const double target = (double)a.uniforms[(size_t)v * 2 + 1] * W;
+  const double target = (double)uf * W;
   int tok = -1;
   if (W > 0.0) {
     const unsigned long long hit = __ballot(pm > 0.0 && incl > target);
@@ -616,7 +719,7 @@ __device__ void process_node(const VocabArgs& a, Lds<C>& L, int v) {
       for (int k = 0; k < per; ++k) {
         const int c = lane * per + k;
         if (c >= nch) break;
-        const double cs = (double)fmaxf(L.cw[c], 0.f);
+        const double cs = (double)fmaxf(P.cw[c], 0.f);
         if (cs > 0.0) {
           cl = c; cum_l = cum;
           if (pc < 0 && cum + cs > target) { pc = c; break; }
@@ -638,13 +741,13 @@ __device__ void process_node(const VocabArgs& a, Lds<C>& L, int v) {
       int lo = 0, hi = K;
       while (lo < hi) {
         const int mid = (lo + hi) >> 1;
-        if (L.sp.idx[mid] < pc * CT) lo = mid + 1; else hi = mid;
+        if (P.sp_idx[mid] < pc * CT) lo = mid + 1; else hi = mid;
       }
 #pragma unroll
       for (int e = 0; e < EPU; ++e) {
         qv[e] = 0.f;
-        for (int j = lo; j < K && L.sp.idx[j] >= 0 && L.sp.idx[j] < (pc + 1) * CT; ++j)
-          if (L.sp.idx[j] == e0 + e) qv[e] = L.sp.val[j];
+        for (int j = lo; j < K && P.sp_idx[j] >= 0 && P.sp_idx[j] < (pc + 1) * CT; ++j)
+          if (P.sp_idx[j] == e0 + e) qv[e] = P.sp_val[j];
       }
     } else if (use_draft) {
 #pragma unroll
@@ -652,6 +755,11 @@ __device__ void process_node(const VocabArgs& a, Lds<C>& L, int v) {
         const float4 t = *(const float4*)(a.draft + (size_t)dr * V + (in ? e0 : 0) + 4 * i);
         qv[4 * i + 0] = t.x; qv[4 * i + 1] = t.y; qv[4 * i + 2] = t.z; qv[4 * i + 3] = t.w;
       }
+    }
+    uint32_t zmask = 0;   // positions of this lane's tokens that are deterministic children
+    for (int k = 0; k < nk; ++k) {
+      const int d = det_tok(k) - e0;
+      if ((unsigned)d < (unsigned)EPU) zmask |= 1u << d;
     }
     float w[EPU];
     float lsum = 0.f;
@@ -661,8 +769,7 @@ __device__ void process_node(const VocabArgs& a, Lds<C>& L, int v) {
       if (in) {
         const float p = __builtin_amdgcn_exp2f(unit_elem<LT>(ru, e) * invTl2 - Ml2) * invS;
         x = use_draft ? fmaxf(0.f, p - qv[e]) : p;
-        for (int k = 0; k < nk; ++k)
-          if (L.kid_tok[k] == e0 + e && !L.kid_smp[k]) x = 0.f;
+        if ((zmask >> e) & 1u) x = 0.f;
       }
       w[e] = x;
       lsum += x;
@@ -703,24 +810,6 @@ __device__ void process_node(const VocabArgs& a, Lds<C>& L, int v) {
       atomicOr(a.status, err);
       atomicOr(a.seq_err + b, err);
     }
-  }
-}
-
-// Takes nodes from the device queue (in the order of order[]: nodes with a draft row first) until
-// none is left.  Called by every thread of a workgroup of C::kThreads threads; L is the workgroup's
-// LDS.
-template <typename LT, class C>
-__device__ void vocab_worker(const VocabArgs& a, Lds<C>& L) {
-  for (;;) {
-    if (threadIdx.x == 0) {
-      const int i = atomicAdd(a.queue, 1);
-      L.item = i < a.N ? a.order[i] : -1;
-    }
-    __syncthreads();
-    const int v = L.item;
-    if (v < 0) return;
-    process_node<LT, C>(a, L, v);
-    __syncthreads();   // LDS reused by the next node
   }
 }
 
