@@ -187,7 +187,17 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h32 = lane >> 5, l32 = lane & 31;
-  const int wg = blockIdx.x, g = blockIdx.y;
+  // Workgroup L of the 1-D grid runs on XCD L % 8 (round-robin dispatch over the 8 XCDs); each XCD
+  // is given a contiguous run of the head-major work list (logical id g * W + wg), so the row blocks
+  // of one (sequence, KV head) -- which stream the same prefix tiles at the same time -- share one
+  // XCD's L2 instead of reading the tiles once per XCD.
+  int wg, g;
+  {
+    const int L = blockIdx.x, nwg = gridDim.x;
+    const int vl = (nwg & 7) == 0 ? (L & 7) * (nwg >> 3) + (L >> 3) : L;
+    g = vl / a.W;
+    wg = vl - g * a.W;
+  }
   const int j_begin = a.wg_tile[wg];
   const int j_end = a.wg_tile[wg + 1];
   if (j_begin >= j_end) return;
@@ -756,7 +766,7 @@ __global__ __launch_bounds__(256) void attn_sentinel_f32_kernel(AttnArgs a, int 
 
 template <int D>
 hipError_t launch_bf16_d(const Plan& p, const AttnArgs& a, hipStream_t s) {
-  dim3 grid(p.W, p.Hkv);
+  const dim3 grid(p.W * p.Hkv);
   switch (p.log2G) {
     case 0: attn_bf16_kernel<D, 0><<<grid, 512, 0, s>>>(a); break;
     case 1: attn_bf16_kernel<D, 1><<<grid, 512, 0, s>>>(a); break;
