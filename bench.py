@@ -322,7 +322,7 @@ def tree_sub_record(w, steps, warmup, ach, label):
            "pass_roofline_frac": round(max((attn_b + ver_b) / (HBM_PEAK_GBS * 1e9),
                                            flops / (BF16_PEAK_TFLOPS * 1e12)) / (ms * 1e-3), 4),
            "draft_rows_used": _used_draft_rows(w), "draft_k": int(w.draft_k),
-           "vocab_workers": roofline_hbm("vocab_worker_kernel", ver_b, k_ms, ach, launches=kn),
+           "vocab_workers": roofline_hbm("vocab_worker_kernel + pick_kernel", ver_b, k_ms, ach, launches=kn),
            "attention_kernel": attention_record(p, flops, attn_b, min(steps, 10), ach)}
     del p
     return rec
@@ -505,7 +505,8 @@ def main():
     attn_rec = attention_record(p, flops, attn_b, args.kernel_steps, ach) if args.kernel_steps > 0 else None
     del p
     step_gbs = (attn_b + ver_b) / (ms * 1e-3) / 1e9
-    roof = roofline_hbm("vocab_worker_kernel (verification: logits and draft rows streamed per node)",
+    roof = roofline_hbm("vocab_worker_kernel + pick_kernel (verification: logits and draft rows streamed "
+                        "per node, then the pick of every node)",
                         ver_b, kern_ms, ach, traffic=measured_traffic(), launches=kern_n)
 
     subs = {}

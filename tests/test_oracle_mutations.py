@@ -8,8 +8,10 @@ afterwards.  The unmutated oracle passes every pin (checked first).  The mistake
 cover the temperature (ignored, multiplied, applied to one statistic only), the
 accept ratio, the residual and its normaliser, the sequential rejection's zeroing
 and renormalisation, the inverse-CDF side, the terminal statistics, the visibility
-sets, the attention scale and key set, and PreSTO's log-acceptance, state
-inheritance and walk.
+sets, the attention scale and key set, PreSTO's log-acceptance, state inheritance
+and walk, the per-token scorer and greedy verification, the prefetching tree (the
+cut generator, Condition 1, deferral, Equations 10, 11 and 14) and the draft-tree
+builder (the sampled token's proxy, the tail off the leads).
 """
 
 import contextlib
@@ -21,11 +23,17 @@ import pytest
 
 import oracle
 import oracle.attention
+import oracle.draft_tree
+import oracle.prefetch
 import oracle.presto
+import oracle.scorer
 import oracle.tree
 import oracle.verify
 
+import test_oracle_draft_tree as tdt
+import test_oracle_prefetch as tpf
 import test_oracle_presto as tp
+import test_oracle_scorer as tsc
 import test_oracle_softmax_pins as ts
 import test_oracle_tree_attention as ta
 import test_oracle_verify as tv
@@ -93,9 +101,26 @@ PINS = [
     ("example 5", tp.test_example5_walk_golden),
     ("proposition 1", lambda: tp.test_proposition1_coupling_with_sequential_mh(1, 20, 30)),
     ("proposition 1, forced decisions", tp.test_proposition1_coupling_forced_decisions),
+    ("truncated draft lossless", lambda: tv.test_one_layer_lossless_with_truncated_draft(0, 3, 1, 3, 3)),
+    ("scorer vs torch", lambda: tsc.test_log_probs_match_torch(0.25)),
+    ("scorer entropy", tsc.test_entropy_matches_torch_and_closed_forms),
+    ("argmax first of ties", tsc.test_argmax_first_of_ties),
+    ("greedy = T -> 0 limit", lambda: tsc.test_greedy_is_the_zero_temperature_limit(0, "random")),
+    ("splitmix64 outputs", tpf.test_splitmix64_known_outputs),
+    ("example 2 BFS", tpf.test_example2_bfs_golden),
+    ("BFS deferral", tpf.test_bfs_deferral),
+    ("lemma 1 = lemma 2 = traversal", lambda: tpf.test_lemma1_equals_lemma2_equals_traversal(0, "bfs", 0.01)),
+    ("equation 10", tpf.test_equation10_rounding),
+    ("equation 14 = lemma 3 midpoint", tpf.test_equation14_is_lemma3_midpoint),
+    ("proposition 2", lambda: tpf.test_proposition2_dp_is_brute_force_optimum(0, 3, 5)),
+    ("rheo table 1", tdt.test_table1_golden),
+    ("lemma 4", lambda: tdt.test_lemma4_sampled_proxy_above_fills(0, 1, 20)),
+    ("lemma 5", lambda: tdt.test_lemma5_scores_fall_and_prune_is_ancestor_closed(0)),
+    ("draft tree lossless", lambda: tdt.test_theorem1_one_layer_lossless(0, 3, 1, 3, 6)),
 ]
 
 V, A, T, P = oracle.verify, oracle.attention, oracle.tree, oracle.presto
+S, PF, DT = oracle.scorer, oracle.prefetch, oracle.draft_tree
 TEMP_LINE = "z = np.asarray(logits_row, dtype=np.float64) / float(temperature)"
 
 MUTATIONS = {
@@ -132,6 +157,23 @@ MUTATIONS = {
     "log A not clamped": (P, "logA[i] = min(0.0, ", "logA[i] = (", 0),
     "rejection child takes the root state": (P, "states[v] = states[par]", "states[v] = states[0]", 0),
     "walk direction inverted": (P, "go = uu <= A", "go = uu > A", 0),
+    # per-token scorer and greedy verification
+    "scorer: tau ignored": (S, "z = l / float(tau)", "z = l", 0),
+    "scorer: entropy sign": (S, "H = float(-np.sum(p[nz] * np.log(p[nz])))", "H = float(np.sum(p[nz] * np.log(p[nz])))", 0),
+    "scorer: last of equal maxima": (S, "int(np.flatnonzero(l == l.max())[0])", "int(np.flatnonzero(l == l.max())[-1])", 0),
+    "scorer: log p0 with the tempered normaliser": (S, "lp0 = float(l[token]) - _lse(l)", "lp0 = float(l[token]) - _lse(l / float(tau))", 0),
+    "greedy: sampled child always accepted": (V, "hit = int(token[c]) == a", "hit = bool(sampled[c]) or int(token[c]) == a", 0),
+    # prefetching tree
+    "splitmix64 finaliser shift": (PF, "return z ^ (z >> 31)", "return z ^ (z >> 30)", 0),
+    "condition 1 inverted": (PF, "if cut[a] <= cut[v]:", "if cut[a] >= cut[v]:", 0),
+    "deferred request's sibling dropped": (PF, "queue.append(r)", "pass", 0),
+    "equation 14 sign": (PF, "return 0.5 * (1.0 + P[ACCEPT] - P[REJECT])", "return 0.5 * (1.0 - P[ACCEPT] + P[REJECT])", 0),
+    "equation 10 never rounds down": (PF, "if A <= eps:", "if A < 0.0:", 0),
+    "rejection child's reaching weight": (PF, "R[v] = R[p] * (h if is_accept[v] else 1.0 - h)", "R[v] = R[p] * (h if is_accept[v] else h)", 0),
+    # draft-tree builder
+    "sampled token's proxy = its own q": (DT, "proxy = min(float(q[m - 1]), zres) if m > 0 else float(q[0]) + self.eps",
+                                          "proxy = float(q[list(keep).index(y)])", 0),
+    "leads left in the sampling tail": (DT, "tail[:m] = 0.0", "pass", 0),
 }
 
 

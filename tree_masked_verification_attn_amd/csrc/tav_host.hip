@@ -401,8 +401,9 @@ tav_status num_compute_units(int* cus) {
   return TAV_OK;
 }
 
-// Verification: the vocabulary workers' kernel (the node order was built by the start kernel), then
-// the walk (after wait_before, when given, on s).
+// Verification: the vocabulary streaming and pick kernels (the workers' node order was built earlier
+// in the call: by the bf16 prelude's order block, else by the start kernel), then the walk (after
+// wait_before, when given, on s).
 tav_status enqueue_verify(const tav_problem* p, const Plan& P, const tav_tree* t,
                           const tav_verify_io* io, void* ws, hipStream_t s, hipEvent_t wait_before = nullptr) {
   const VocabArgs va = vocab_args(p, P, t, io, ws);
