@@ -88,13 +88,22 @@ __device__ inline int kpos(int c, int key) {
 }
 
 typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+
+// A kernel argument read again from the kernarg segment where it is used (one scalar load), for the
+// arguments only row-block switches, segment ends and error paths need: the tile loop then keeps
+// fewer scalar registers live (the rest no longer spill into vector-register lanes).
+template <typename T>
+__device__ __forceinline__ T cold_arg(size_t off) {
+  const __attribute__((address_space(4))) char* kp =
+      (const __attribute__((address_space(4))) char*)__builtin_amdgcn_kernarg_segment_ptr();
+  return *(const volatile T __attribute__((address_space(4)))*)(kp + off);
+}
+#define TAV_COLD(field) cold_arg<decltype(AttnArgs::field)>(offsetof(AttnArgs, field))
 typedef const __attribute__((address_space(4))) uint8_t* const_u8_ptr;
 
 // Scalar-cache views of the work plan (wave-uniform reads).
 struct PlanView {
-  const_i32_ptr rb_tile, rb_seq, pref_len, tail_blk;
-  const int32_t* block_table;
-  int max_blocks, total_rb;
+  int total_rb;
 };
 
 // Where the tiles of one row block come from (wave-uniform).
@@ -112,15 +121,19 @@ struct TileCursor {
 };
 
 __device__ __forceinline__ void cursor_load(TileCursor& c, const PlanView& pv, int r) {
-  const int b = pv.rb_seq[r];
+  const const_i32_ptr rb_seq = (const_i32_ptr)TAV_COLD(rb_seq);
+  const const_i32_ptr rb_tile = (const_i32_ptr)TAV_COLD(rb_tile);
+  const const_i32_ptr pref_len = (const_i32_ptr)TAV_COLD(prefix_len);
+  const const_i32_ptr tail_blk = (const_i32_ptr)TAV_COLD(tail_blk);
+  const int b = rb_seq[r];
   c.r = r;
   c.seq = b;
-  c.T = pv.rb_tile[r + 1] - pv.rb_tile[r];
-  c.L = pv.pref_len[b];
+  c.T = rb_tile[r + 1] - rb_tile[r];
+  c.L = pref_len[b];
   c.Tp = (c.L + kTileKeys - 1) / kTileKeys;
-  c.tail_off = pv.tail_blk[b];
-  c.tail_nblk = pv.tail_blk[b + 1] - c.tail_off;
-  c.btab = (const_i32_ptr)(pv.block_table + (size_t)b * pv.max_blocks);
+  c.tail_off = tail_blk[b];
+  c.tail_nblk = tail_blk[b + 1] - c.tail_off;
+  c.btab = (const_i32_ptr)(TAV_COLD(block_table) + (size_t)b * TAV_COLD(max_blocks));
   c.first_blk = c.L > 0 ? c.btab[0] : 0;
 }
 
@@ -204,16 +217,11 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
   const int Hq = a.Hq, Hkv = a.Hkv, bs = a.block_size;
   const int lbs = __builtin_ctz(bs);   // block sizes are powers of two
   const const_i32_ptr rb_tile = (const_i32_ptr)a.rb_tile;
-  const const_i32_ptr rb_seq = (const_i32_ptr)a.rb_seq;
-  const const_i32_ptr pref_len = (const_i32_ptr)a.prefix_len;
-  const const_i32_ptr tail_blk = (const_i32_ptr)a.tail_blk;
-  const const_i32_ptr rb_meta = (const_i32_ptr)a.rb_meta;
-  const const_i32_ptr chain_w = (const_i32_ptr)a.is_chain;   // chain flags, 4 per word
   const uint16_t* kc = (const uint16_t*)a.k_cache;
   const uint16_t* vc = (const uint16_t*)a.v_cache;
   const uint16_t* ktl = (const uint16_t*)a.k_tail;
   const uint16_t* vtl = (const uint16_t*)a.v_tail;
-  const PlanView pview{rb_tile, rb_seq, pref_len, tail_blk, a.block_table, a.max_blocks, a.total_rb};
+  const PlanView pview{a.total_rb};
   const int sb = wave >> 1;   // 16-key sub-block of each tile this wave copies
 
   // ---- global -> LDS copies of tile j into ring slot (j - j_begin) % kStages.  Wave w copies
@@ -232,8 +240,8 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
     int blk = nref.blk;
     if (!nref.tail && (unsigned)blk >= (unsigned)a.num_blocks) {
       if (lane == 0) {
-        atomicOr(a.status, (uint32_t)TAV_DEV_BAD_BLOCK);
-        atomicOr(a.seq_err + nref.seq, (uint32_t)TAV_DEV_BAD_BLOCK);
+        atomicOr(TAV_COLD(status), (uint32_t)TAV_DEV_BAD_BLOCK);
+        atomicOr(TAV_COLD(seq_err) + nref.seq, (uint32_t)TAV_DEV_BAD_BLOCK);
       }
       blk = 0;   // (the sequence's rows become sentinels after the kernel)
     }
@@ -268,7 +276,8 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
   // every copy issued before it.  Rows past the block's nodes read node 0's query (finite values
   // whose outputs are dropped); rows without mask words read node 0's and clear them.
   auto start_segment = [&](int r) __attribute__((always_inline)) {
-    const const_i32_ptr m = rb_meta + (size_t)r * kMetaWords;
+    const const_i32_ptr m = (const_i32_ptr)TAV_COLD(rb_meta) + (size_t)r * kMetaWords;
+    const const_i32_ptr chain_w = (const_i32_ptr)TAV_COLD(is_chain);   // chain flags, 4 per word
     seg_r = r;
     seg_A = m[kMetaTile0];
     seg_E = m[kMetaTileEnd];
@@ -287,8 +296,8 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
     rhead = g * G + (row & (G - 1));
     const bool mask_rows = !seg_chain && seg_ok && rvalid;
     const int qnode = seg_s0 + (rvalid ? rnode : 0);
-    const uint4* mp = (const uint4*)(a.mask + (size_t)(mask_rows ? qnode : seg_s0) * kMaskWords);
-    const uint16_t* qp = (const uint16_t*)a.q + ((size_t)qnode * Hq + rhead) * D + h32 * 8;
+    const uint4* mp = (const uint4*)(TAV_COLD(mask) + (size_t)(mask_rows ? qnode : seg_s0) * kMaskWords);
+    const uint16_t* qp = (const uint16_t*)TAV_COLD(q) + ((size_t)qnode * Hq + rhead) * D + h32 * 8;
     static_assert(KS == 4 || KS == 8, "query registers");
     if constexpr (KS == 8) {
       asm volatile(
@@ -410,7 +419,7 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
     const float lse_nat = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
     if (o_.A >= j_begin && o_.E <= j_end) {
       if (o_.valid) {
-        uint16_t* op = (uint16_t*)a.out + ((size_t)(o_.s0 + o_.node) * Hq + rhead) * D;
+        uint16_t* op = (uint16_t*)TAV_COLD(out) + ((size_t)(o_.s0 + o_.node) * Hq + rhead) * D;
 #pragma unroll
         for (int mb = 0; mb < DB; ++mb) {
 #pragma unroll
@@ -421,12 +430,13 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
             *(uint2*)(op + mb * 32 + rq * 8 + h32 * 4) = o.u;
           }
         }
-        if (h32 == 0 && a.lse) a.lse[(size_t)(o_.s0 + o_.node) * Hq + rhead] = lse_nat;
+        float* lsep = TAV_COLD(lse);
+        if (h32 == 0 && lsep) lsep[(size_t)(o_.s0 + o_.node) * Hq + rhead] = lse_nat;
       }
     } else {
       const int slot = o_.A < j_begin ? 2 * wg : 2 * wg + 1;
       const size_t prow = ((size_t)slot * Hkv + g) * kRowsPerWG + row;
-      uint16_t* po = a.part_o + prow * D;
+      uint16_t* po = TAV_COLD(part_o) + prow * D;
 #pragma unroll
       for (int mb = 0; mb < DB; ++mb) {
 #pragma unroll
@@ -437,7 +447,7 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
           *(uint2*)(po + mb * 32 + rq * 8 + h32 * 4) = o.u;
         }
       }
-      if (h32 == 0) a.part_lse[prow] = lse_nat;
+      if (h32 == 0) TAV_COLD(part_lse)[prow] = lse_nat;
     }
     m_run = -INFINITY;
     l_run = 0.f;

@@ -13,8 +13,11 @@
 //   s1 = sum 2^(t), s2 = sum 2^(t) * t, st = sum 2^(t / tau),    t = (l - m) log2e,
 // rescaled when m rises (once per step, from the step's maximum), so that
 //   log S1 = ln2 (m + log2 s1),  sum p0 (l - M) = ln2 s2 / s1,  H = log S1 - that,
-// and the argmax is located only in steps whose maximum beats the best so far.  When 1 / tau is
-// a whole number up to 8 (PreSTO's tau = 1 / alpha), 2^(t / tau) = (2^t)^(1 / tau) by squaring.
+// and each thread notes the unit of its first largest logit (per-unit maxima, compared only in steps
+// whose maximum beats its best), re-reading that one unit at the end of the row for the position.
+// When 1 / tau is a whole number up to 8 (PreSTO's tau = 1 / alpha), 2^(t / tau) = (2^t)^(1 / tau)
+// by squaring (a kernel compiled per exponent).  The units of a partial last step past the row's
+// end are set to -inf, so the element loops carry no bounds checks.
 #include "tav_internal.h"
 
 namespace tav {
@@ -38,17 +41,37 @@ __device__ inline float elem<float>(const uint4& u, int e) {
   return __uint_as_float(e == 0 ? u.x : e == 1 ? u.y : e == 2 ? u.z : u.w);
 }
 
-// x^k for a whole k in 1..8 (k = 0: unused)
-__device__ inline float ipow(float x, int k) {
+// x^K for a whole K in 1..8, by squaring (compile-time K)
+template <int K>
+__device__ inline float ipow(float x) {
   const float x2 = x * x, x4 = x2 * x2;
-  float r = (k & 1) ? x : 1.f;
-  if (k & 2) r *= x2;
-  if (k & 4) r *= x4;
-  if (k & 8) r *= x4 * x4;
-  return r;
+  if constexpr (K == 1) return x;
+  else if constexpr (K == 2) return x2;
+  else if constexpr (K == 3) return x2 * x;
+  else if constexpr (K == 4) return x4;
+  else if constexpr (K == 5) return x4 * x;
+  else if constexpr (K == 6) return x4 * x2;
+  else if constexpr (K == 7) return x4 * x2 * x;
+  else return x4 * x4;
 }
 
+// 2^(t / tau): by squaring when 1 / tau is the whole number KP, else a second exponential
+template <int KP>
+__device__ inline float pow_tau(float x, float t, float inv_tau) {
+  if constexpr (KP > 0) return ipow<KP>(x);
+  else return __builtin_amdgcn_exp2f(t * inv_tau);
+}
+
+// The units of a partial last step past the row's end: set to -inf (no mass, never the maximum),
+// so the arithmetic needs no per-element bounds checks.
 template <typename LT>
+__device__ inline uint4 neg_inf_unit();
+template <>
+__device__ inline uint4 neg_inf_unit<uint16_t>() { return make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u); }
+template <>
+__device__ inline uint4 neg_inf_unit<float>() { return make_uint4(0xFF800000u, 0xFF800000u, 0xFF800000u, 0xFF800000u); }
+
+template <typename LT, int KP>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   constexpr int EPU = 16 / sizeof(LT);
   __shared__ double red[kScoreThreads / 64][4];
@@ -58,7 +81,6 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   const int V = a.V, nunits = V / EPU;
   const int nsteps = (nunits + kScoreStep - 1) / kScoreStep;
   const float inv_tau = 1.f / a.tau;
-  const int kpow = a.kpow;                      // 1 / tau when it is a whole number in 1..8, else 0
   for (int row = blockIdx.x; row < a.N; row += gridDim.x) {
     const LT* lr = (const LT*)a.logits + (size_t)row * V;
     auto load = [&](uint4 (&r)[kScoreUnits], int s) __attribute__((always_inline)) {
@@ -72,30 +94,31 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     load(cur, 0);
     float m = -INFINITY, s1 = 0.f, s2 = 0.f, st = 0.f;   // m in log2 units
     float best = -INFINITY;
-    int bi = -1;
+    int bu = -1;   // the unit holding this thread's first largest logit
     for (int s = 0; s < nsteps; ++s) {
       uint4 nxt[kScoreUnits];
       if (s + 1 < nsteps) load(nxt, s + 1);
-      float mx = -INFINITY;
+      if ((s + 1) * kScoreStep > nunits) {   // the partial last step
 #pragma unroll
-      for (int k = 0; k < kScoreUnits; ++k)
-        if (s * kScoreStep + k * kScoreThreads + tid < nunits) {
+        for (int k = 0; k < kScoreUnits; ++k)
+          if (s * kScoreStep + k * kScoreThreads + tid >= nunits) cur[k] = neg_inf_unit<LT>();
+      }
+      float um[kScoreUnits];
 #pragma unroll
-          for (int e = 0; e < EPU; ++e) mx = fmaxf(mx, elem<LT>(cur[k], e));
-        }
-      if (mx > best) {   // the step holds a new best: its first position (positions rise in a thread)
+      for (int k = 0; k < kScoreUnits; ++k) {
+        um[k] = elem<LT>(cur[k], 0);
+#pragma unroll
+        for (int e = 1; e < EPU; ++e) um[k] = fmaxf(um[k], elem<LT>(cur[k], e));
+      }
+      float mx = um[0];
+#pragma unroll
+      for (int k = 1; k < kScoreUnits; ++k) mx = fmaxf(mx, um[k]);
+      if (mx > best) {   // a new best: its first unit (positions rise with (step, unit) in a thread)
         best = mx;
-        bool found = false;
+        int kk = kScoreUnits - 1;
 #pragma unroll
-        for (int k = 0; k < kScoreUnits; ++k) {
-          const int u = s * kScoreStep + k * kScoreThreads + tid;
-#pragma unroll
-          for (int e = 0; e < EPU; ++e)
-            if (!found && u < nunits && elem<LT>(cur[k], e) == mx) {
-              bi = u * EPU + e;
-              found = true;
-            }
-        }
+        for (int k = kScoreUnits - 2; k >= 0; --k) kk = um[k] == mx ? k : kk;
+        bu = s * kScoreStep + kk * kScoreThreads + tid;
       }
       const float m2 = mx * kLog2e;
       if (m2 > m) {   // rescale the running sums to the new maximum
@@ -104,67 +127,43 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
           const float f = __builtin_amdgcn_exp2f(d);
           s2 = f * (s2 + s1 * d);
           s1 *= f;
-          st *= kpow ? ipow(f, kpow) : __builtin_amdgcn_exp2f(d * inv_tau);
+          st *= pow_tau<KP>(f, d, inv_tau);
         }
         m = m2;
       }
       if (m != -INFINITY) {
 #pragma unroll
-        for (int k = 0; k < kScoreUnits; ++k)
-          if (s * kScoreStep + k * kScoreThreads + tid < nunits) {
+        for (int k = 0; k < kScoreUnits; ++k) {
 #pragma unroll
-            for (int e = 0; e < EPU; ++e) {
-              // t <= 0 (a NaN logit makes s1 NaN, which is reported); a -inf logit gives 2^t = 0,
-              // and its t is clamped in the product so that 0 * -inf does not appear
-              const float t = fmaf(elem<LT>(cur[k], e), kLog2e, -m);
-              const float x = __builtin_amdgcn_exp2f(t);
-              s1 += x;
-              s2 = fmaf(x, fmaxf(t, -1.0e30f), s2);
-              st += kpow ? ipow(x, kpow) : __builtin_amdgcn_exp2f(t * inv_tau);
-            }
+          for (int e = 0; e < EPU; ++e) {
+            // t <= 0 (a NaN logit makes s1 NaN, which is reported); a -inf logit gives 2^t = 0,
+            // and its t is clamped in the product so that 0 * -inf does not appear
+            const float t = fmaf(elem<LT>(cur[k], e), kLog2e, -m);
+            const float x = __builtin_amdgcn_exp2f(t);
+            s1 += x;
+            s2 = fmaf(x, fmaxf(t, -1.0e30f), s2);
+            st += pow_tau<KP>(x, t, inv_tau);
           }
+        }
       }
       if (s + 1 < nsteps) {
 #pragma unroll
         for (int k = 0; k < kScoreUnits; ++k) cur[k] = nxt[k];
       }
     }
+    // the position of this thread's best inside its unit (one re-read of that unit, from the cache;
+    // issued now, used after the sums' reductions)
+    uint4 bunit = make_uint4(0u, 0u, 0u, 0u);
+    if (bu >= 0) bunit = *(const uint4*)(lr + (size_t)bu * EPU);
     // the block's maximum, then every thread's sums moved to it and added in fp64
     float wm = m;
 #pragma unroll
     for (int d = 32; d > 0; d >>= 1) wm = fmaxf(wm, __shfl_xor(wm, d));
-    float wb = best;
-    int wi = bi;
-#pragma unroll
-    for (int d = 32; d > 0; d >>= 1) {
-      const float ob = __shfl_xor(wb, d);
-      const int oi = __shfl_xor(wi, d);
-      if (ob > wb || (ob == wb && (unsigned)oi < (unsigned)wi)) {
-        wb = ob;
-        wi = oi;
-      }
-    }
-    if (lane == 0) {
-      bred[wave] = wm;
-      ired[wave] = wi;
-      red[wave][3] = (double)wb;
-    }
+    if (lane == 0) bred[wave] = wm;
     __syncthreads();
     float M2 = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kScoreThreads / 64; ++w) M2 = fmaxf(M2, bred[w]);
-    float bb = -INFINITY;
-    int A = -1;
-#pragma unroll
-    for (int w = 0; w < kScoreThreads / 64; ++w) {
-      const float ob = (float)red[w][3];
-      const int oi = ired[w];
-      if (ob > bb || (ob == bb && (unsigned)oi < (unsigned)A)) {
-        bb = ob;
-        A = oi;
-      }
-    }
-    __syncthreads();   // red is reused below
     double d1 = 0.0, d2 = 0.0, dt = 0.0;
     if (m != -INFINITY) {
       const double d = (double)m - (double)M2;   // <= 0
@@ -179,18 +178,46 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
       d2 += __shfl_xor(d2, o);
       dt += __shfl_xor(dt, o);
     }
+    int bi = -1;
+    if (bu >= 0) {
+      int ee = EPU - 1;
+#pragma unroll
+      for (int e = EPU - 2; e >= 0; --e) ee = elem<LT>(bunit, e) == best ? e : ee;
+      bi = bu * EPU + ee;
+    }
+    float wb = best;
+    int wi = bi;
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) {
+      const float ob = __shfl_xor(wb, d);
+      const int oi = __shfl_xor(wi, d);
+      if (ob > wb || (ob == wb && (unsigned)oi < (unsigned)wi)) {
+        wb = ob;
+        wi = oi;
+      }
+    }
     if (lane == 0) {
       red[wave][0] = d1;
       red[wave][1] = d2;
       red[wave][2] = dt;
+      red[wave][3] = (double)wb;
+      ired[wave] = wi;
     }
     __syncthreads();
     if (tid == 0) {
       double S1 = 0.0, S2 = 0.0, ST = 0.0;
+      float bb = -INFINITY;
+      int A = -1;
       for (int w = 0; w < kScoreThreads / 64; ++w) {
         S1 += red[w][0];
         S2 += red[w][1];
         ST += red[w][2];
+        const float ob = (float)red[w][3];
+        const int oi = ired[w];
+        if (ob > bb || (ob == bb && (unsigned)oi < (unsigned)A)) {
+          bb = ob;
+          A = oi;
+        }
       }
       uint32_t err = 0;
       const double Mn = (double)M2 * (double)kLn2;          // max l (natural units)
@@ -223,15 +250,30 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   }
 }
 
-template <typename LT>
-hipError_t launch_score_t(const ScoreArgs& a, int num_cus, hipStream_t s) {
+template <typename LT, int KP>
+hipError_t launch_score_k(const ScoreArgs& a, int num_cus, hipStream_t s) {
   int per_cu = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, score_kernel<LT>, kScoreThreads, 0);
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, score_kernel<LT, KP>, kScoreThreads, 0);
   if (e != hipSuccess) return e;
   if (per_cu < 1) per_cu = 1;
   const int grid = a.N < per_cu * num_cus ? a.N : per_cu * num_cus;
-  score_kernel<LT><<<grid, kScoreThreads, 0, s>>>(a);
+  score_kernel<LT, KP><<<grid, kScoreThreads, 0, s>>>(a);
   return hipGetLastError();
+}
+
+template <typename LT>
+hipError_t launch_score_t(const ScoreArgs& a, int num_cus, hipStream_t s) {
+  switch (a.kpow) {
+    case 1: return launch_score_k<LT, 1>(a, num_cus, s);
+    case 2: return launch_score_k<LT, 2>(a, num_cus, s);
+    case 3: return launch_score_k<LT, 3>(a, num_cus, s);
+    case 4: return launch_score_k<LT, 4>(a, num_cus, s);
+    case 5: return launch_score_k<LT, 5>(a, num_cus, s);
+    case 6: return launch_score_k<LT, 6>(a, num_cus, s);
+    case 7: return launch_score_k<LT, 7>(a, num_cus, s);
+    case 8: return launch_score_k<LT, 8>(a, num_cus, s);
+    default: return launch_score_k<LT, 0>(a, num_cus, s);
+  }
 }
 
 }  // namespace
