@@ -228,31 +228,50 @@ __device__ void greedy_stream(const VocabArgs& a, Lds<C>& L, int v, int b, int s
   constexpr int EPU = 16 / sizeof(LT);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   float best = -INFINITY;
-  int bi = -1;
+  int bu = -1;   // the unit holding this thread's first largest logit
   bool bad = false;
   for (int s = 0; s < nsteps; ++s) {
     uint4 nxt[kUnits];
     if (s + 1 < nsteps) load_step<LT, C>(nxt, row, s + 1, tid, nunits);
-    // a thread's positions rise with (step, unit, element), so a strict > keeps the smallest id
+    // per-unit maxima (NaN ignored by the max, caught by the unordered compare; +inf caught below)
+    float um[kUnits];
 #pragma unroll
     for (int k = 0; k < kUnits; ++k) {
       const int u = s * kStepUnits + k * kThreads + tid;
+      um[k] = -INFINITY;
       if (u < nunits) {
 #pragma unroll
         for (int e = 0; e < EPU; ++e) {
           const float x = unit_elem<LT>(cur[k], e);
-          bad |= !(x < INFINITY);   // +inf or NaN
-          if (x > best) {
-            best = x;
-            bi = u * EPU + e;
-          }
+          bad |= x != x;
+          um[k] = fmaxf(um[k], x);
         }
       }
+    }
+    float mx = um[0];
+#pragma unroll
+    for (int k = 1; k < kUnits; ++k) mx = fmaxf(mx, um[k]);
+    if (mx > best) {   // a new best: its first unit (positions rise with (step, unit) in a thread)
+      best = mx;
+      int kk = kUnits - 1;
+#pragma unroll
+      for (int k = kUnits - 2; k >= 0; --k) kk = um[k] == mx ? k : kk;
+      bu = s * kStepUnits + kk * kThreads + tid;
     }
     if (s + 1 < nsteps) {
 #pragma unroll
       for (int k = 0; k < kUnits; ++k) cur[k] = nxt[k];
     }
+  }
+  bad |= best == INFINITY;
+  // the position inside the best unit (one re-read of that unit, from the cache)
+  int bi = -1;
+  if (bu >= 0) {
+    const uint4 bunit = *(const uint4*)(row + (size_t)bu * EPU);
+    int ee = EPU - 1;
+#pragma unroll
+    for (int e = EPU - 2; e >= 0; --e) ee = unit_elem<LT>(bunit, e) == best ? e : ee;
+    bi = bu * EPU + ee;
   }
 #define TAV_GREEDY_STAGE(S)                                                                  \
   better_of(best, bi, lane_move_f<S>(best), (int)lane_move<S>((uint32_t)bi));
