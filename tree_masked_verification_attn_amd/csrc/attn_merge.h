@@ -12,14 +12,14 @@ namespace tav {
 // (their workgroup's first segment).  A thread owns 4 outputs at a time.
 template <typename OutT>
 __device__ inline void merge_rows(const AttnArgs& a, int D, int log2G, int r, int g, int row0, int nrows) {
+  // the row block's record from the plan (one round of loads beside the status words)
+  const int32_t* m = a.rb_meta + (size_t)r * kMetaWords;
+  const int b = m[kMetaSeq], s0 = m[kMetaS0], n = m[kMetaN], node0 = m[kMetaNode0];
+  const int wf = m[kMetaWf], wl = m[kMetaWl];
   if (a.status[0] & TAV_DEV_PLAN_MISMATCH) return;
-  const int b = a.rb_seq[r];
   if (b < 0 || b >= a.B) return;
-  const int s0 = a.node_offsets[b];
-  const int n = a.node_offsets[b + 1] - s0;
   const int NB = kRowsPerWG >> log2G;
   const int G = 1 << log2G;
-  const int node0 = (r - a.seq_rb_off[b]) * NB;
   const int nodes_here = min(NB, n - node0);
   if (a.seq_err[b] & kAttnErrBits) {
     // the sequence's tree or prefix is unusable: its rows become sentinels (out = 0, lse = -inf)
@@ -32,18 +32,6 @@ __device__ inline void merge_rows(const AttnArgs& a, int D, int log2G, int r, in
     }
     return;
   }
-  const int rA = a.rb_tile[r], rE = a.rb_tile[r + 1];
-  // the workgroups holding the row block's first and last tiles: the largest w with
-  // wg_tile[w] <= tile (never an empty share: the next share starts at the same tile)
-  auto owner = [&](int t) {
-    int lo = 0, hi = a.W;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (a.wg_tile[mid] <= t) lo = mid; else hi = mid;
-    }
-    return lo;
-  };
-  const int wf = owner(rA), wl = owner(rE - 1);
   if (wf == wl) return;  // one workgroup held the whole row block
   const int DQ = D / 4;
   constexpr int kPre = 4;   // pieces whose loads are all issued before any is used

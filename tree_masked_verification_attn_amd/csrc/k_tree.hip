@@ -137,7 +137,7 @@ struct PlanArgs {
 // TAV_DEV_PLAN_MISMATCH.  The row-block offsets and tiles are staged in LDS when they fit.
 __device__ void plan_block(const PlanArgs& p, const AttnArgs& a) {
   __shared__ int scan_s[16];
-  __shared__ int off_s[kPlanLds], tile_s[kPlanLds];
+  __shared__ int off_s[kPlanLds], tile_s[kPlanLds], wt_s[kPlanLds];
   const int B = p.B, NB = p.NB, bs = p.bs, C = p.C, W = p.W;
   const int32_t* node_offsets = a.node_offsets;
   const int32_t* prefix_len = a.prefix_len;
@@ -222,6 +222,7 @@ __device__ void plan_block(const PlanArgs& p, const AttnArgs& a) {
     // a share starting inside a row block's fixed-cost gap starts at the next row block
     const int j = w == W ? tcarry : min(tile[lo] + (x - tile[lo] - kRbCost * lo), tile[lo + 1]);
     wg_tile[w] = j;
+    if (W + 1 <= kPlanLds) wt_s[w] = j;
     if (w < W) {
       int r = lo;   // the row block holding tile j (an empty share keeps any valid index)
       if (j >= tile[lo + 1] && lo + 1 < total_rb) r = lo + 1;
@@ -229,7 +230,18 @@ __device__ void plan_block(const PlanArgs& p, const AttnArgs& a) {
     }
   }
   // the attention kernel's record of each row block (the chain flag is read by the attention
-  // kernel itself from the preparation's output)
+  // kernel itself from the preparation's output), with the workgroups holding its first and last
+  // tiles for the merge: the largest w with wg_tile[w] <= tile (never an empty share)
+  __syncthreads();
+  const int* wt = W + 1 <= kPlanLds ? wt_s : wg_tile;
+  auto owner = [&](int t) {
+    int lo = 0, hi = W;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (wt[mid] <= t) lo = mid; else hi = mid;
+    }
+    return lo;
+  };
   for (int r = threadIdx.x; r < total_rb; r += blockDim.x) {
     int lo = 0, hi = B;  // the row block's sequence: largest b with off[b] <= r
     while (hi - lo > 1) {
@@ -250,6 +262,8 @@ __device__ void plan_block(const PlanArgs& p, const AttnArgs& a) {
     m[kMetaTailN] = min(n, node0 + NB);
     m[kMetaFlags] = n <= kMaxTreeNodes ? 2 : 0;
     m[kMetaSeq] = b;
+    m[kMetaWf] = owner(tile[r]);
+    m[kMetaWl] = owner(tile[r + 1] - 1);
   }
 }
 

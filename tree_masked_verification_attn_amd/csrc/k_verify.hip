@@ -156,30 +156,31 @@ __global__ __launch_bounds__(64) void walk_kernel(WalkArgs a) {
     } else if (lane == 0) {
       bool resid = false;
       const double Zv = (double)(staged ? z_s[v] : a.stats[(size_t)(s0 + v) * 3 + 2]);
+      // the tests u <= min(1, p / q~) and u <= r / (1 - rejected mass) are taken as products
+      // (u q~ <= p, u (1 - rejected) <= r): the same decisions up to the last bits of the ratios, with
+      // no fp64 division on the walk's serial path (one reciprocal of Z per residual node)
       if (s >= 0) {
         const double qs = q_of(s);
         if (!(qs > 0.0)) {
           err |= TAV_DEV_ZERO_DRAFT_MASS;
+        } else if (u_of(s) * qs <= p_of(s)) {
+          next = s;
         } else {
-          const double ratio = fmin(1.0, p_of(s) / qs);
-          if (u_of(s) <= ratio) {
-            next = s;
-          } else {
-            a.node_status[s0 + s] = 2;
-            resid = true;
-          }
+          a.node_status[s0 + s] = 2;
+          resid = true;
         }
       }
       if (!err && next < 0) {
+        const double invZ = resid && Zv > 0.0 ? 1.0 / Zv : 0.0;
         double rej = 0.0;
         for (int k = 0; k < nk && next < 0; ++k) {
           const int c = kids[k];
           if (c == s) continue;
           const double p = p_of(c);
-          const double r0 = resid ? (Zv > 0.0 ? fmax(0.0, p - q_of(c)) / Zv : 0.0) : p;
+          const double r0 = resid ? fmax(0.0, p - q_of(c)) * invZ : p;
           const double rem = 1.0 - rej;
-          const double rc = rem > 0.0 ? r0 / rem : 0.0;
-          if (u_of(c) <= rc) {
+          const double uc = u_of(c);
+          if (rem > 0.0 ? uc * rem <= r0 : uc <= 0.0) {
             next = c;
           } else {
             a.node_status[s0 + c] = 2;

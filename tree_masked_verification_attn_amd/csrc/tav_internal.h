@@ -71,7 +71,7 @@ __host__ __device__ static inline int rb_tiles(int L, int n, int rb, int NB) {
 constexpr int kRbCost = 4;
 
 enum RbMeta { kMetaTile0 = 0, kMetaTileEnd, kMetaS0, kMetaN, kMetaL, kMetaNode0, kMetaTailN, kMetaFlags,
-              kMetaSeq, kMetaWords };
+              kMetaSeq, kMetaWf, kMetaWl, kMetaWords };   // Wf / Wl: workgroups of the first / last tile
 
 struct AttnArgs {
   const void* q;
