@@ -426,8 +426,9 @@ def draft_tree_record(seed, reps=10):
                        None, launches=reps)
     rec.update({"trees": B, "depth": D, "parents_per_depth": K, "slots": slots, "support": S, "kept": R,
                 "ms_per_build": round(ms, 4), "us_per_depth": round(ms * 1e3 / D, 1),
-                "note": "latency-bound: each depth reads 8 logits rows per tree (9.7 MB) three times "
-                        "(two radix-select passes and the collection pass, the last two from the cache)"})
+                "note": "latency-bound: 32 rows per depth on 256 compute units; each depth reads 8 logits rows "
+                        "per tree (9.7 MB) from HBM once (the per-thread maxima) and again from the cache (the "
+                        "gather of the pairs at or above the bound)"})
     return rec
 
 
