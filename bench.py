@@ -432,6 +432,53 @@ def draft_tree_record(seed, reps=10):
     return rec
 
 
+def call_latency_record(seed, steps=50, warmup=5):
+    """The two launch-latency configurations (c1: one 15-node tree in fp32; c2: one 60-node tree
+    behind a 2048-token prefix, bf16): microseconds per whole-pass call, launched eagerly and as a
+    HIP-graph replay of the same call (one graph per input copy, captured once)."""
+    import torch
+
+    import tree_masked_verification_attn_amd as tav
+    from workloads import gen
+
+    rec = {}
+    for name in ("c1", "c2"):
+        w = gen.make(name, seed)
+        p = Pass(w)
+        eager_ms = p.time_steps(steps, warmup)
+        s = torch.cuda.Stream()
+        graphs = []
+        for c in p.copies:
+            with torch.cuda.stream(s):
+                tav.tav_tree_attn_verify(c.prob, c.tree, c.attn, c.verify, None, None, c.workspace, s, s)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                tav.tav_tree_attn_verify(c.prob, c.tree, c.attn, c.verify, None, None, c.workspace, s, s)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for i in range(warmup):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1e3 / steps
+        for c in p.copies:
+            bits = tav.tav_read_status(c.workspace)
+            if bits:
+                raise RuntimeError(f"device status bits set: {tav.device_status_names(bits)}")
+        attn_b, ver_b = algorithmic_bytes(w)
+        rec[name] = {"workload": f"{name}: {w.info['description']}", "nodes": int(w.N),
+                     "us_per_call_eager": round(eager_ms * 1e3, 1), "us_per_call_graph": round(graph_ms * 1e3, 1),
+                     "algorithmic_bytes": attn_b + ver_b}
+        del graphs, p
+        torch.cuda.empty_cache()
+    rec["note"] = "launch-latency configurations: microseconds per call, not a bandwidth result"
+    return rec
+
+
 def prefetch_builder_record(seed, reps=200):
     """Host time of tav_prefetch_build at the PreSTO batch's shape (T = 4096, N_pf = 32, K' = 100),
     both rules, and each tree's predicted transition count."""
@@ -537,6 +584,8 @@ def main():
             subs["c3_sparse_draft_k128"] = tree_sub_record(
                 gen.make("c3", args.seed, draft_support=128), sub_steps, 3, ach,
                 "c3 with sparse draft rows: top-128 support per row (RheoSampling's sparse draft)")
+        if want("c1_c2_call_latency"):
+            subs["c1_c2_call_latency"] = call_latency_record(args.seed)
         if want("prefetch_builder_host"):
             subs["prefetch_builder_host"] = prefetch_builder_record(args.seed)
         if want("draft_tree_gpu"):
