@@ -434,8 +434,9 @@ tav_status tav_read_status(const void* workspace, void* stream, uint32_t* status
  * it is per calling host thread).  tav_kernel_timing(which) with
  * which = 1 records a pair of HIP events on the attention stream immediately before and after
  * every bf16 tree-attention kernel launch (not around the preparation or merge launches); with
- * which = 2 around every launch of the vocabulary workers' kernel of the verification, on the
- * stream the verification runs on; which = 0 stops recording and releases the events.
+ * which = 2 before every launch of the verification's vocabulary streaming kernel and after the
+ * pick kernel that follows it, on the stream the verification runs on; which = 0 stops recording
+ * and releases the events.
  * tav_kernel_timing_read waits for the recorded events, returns the summed elapsed milliseconds
  * and the number of launches recorded since the previous read or enable, and starts a new
  * record.  The events are timing-only (no system-scope fence when recorded).  They belong to the

@@ -36,7 +36,8 @@ def _scores(logits_np, tokens, tau, dtype):
 
 
 @pytest.mark.parametrize("dtype,V,tau", [("bf16", 151936, 0.25), ("bf16", 4096, 1.0), ("bf16", 1000, 0.7),
-                                         ("f32", 20004, 0.25), ("f32", 8, 2.0)])
+                                         ("f32", 20004, 0.25), ("f32", 8, 2.0), ("bf16", 50000, 0.5),
+                                         ("bf16", 3000, 1.0 / 3.0), ("f32", 5000, 0.125)])
 def test_scores_match_oracle(dtype, V, tau):
     rng = np.random.default_rng(V)
     N = 37
@@ -45,6 +46,9 @@ def test_scores_match_oracle(dtype, V, tau):
     x[5, :] = 1.25                                                 # all equal: argmax 0, entropy log V
     x[6, V // 2] = x[6].max() + 1.0
     x[6, V - 1] = x[6, V // 2]                                     # tie: the smaller id
+    if V >= 16:
+        x[7, [5, 6]] = x[7].max() + 2.0                            # tie inside one 16-byte unit
+        x[8, [V - 2, 1]] = x[8].max() + 2.0                        # tie far apart (first wins)
     stored = gen.f32_to_bf16_bits(x) if dtype == "bf16" else x
     tokens = rng.integers(0, V, N)
     tokens[3] = int(np.flatnonzero(np.isfinite(x[3]))[0])
