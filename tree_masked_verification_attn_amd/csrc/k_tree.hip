@@ -7,7 +7,9 @@
 // For bf16 attention the three jobs run as one launch (prelude_kernel): blocks
 // [0, B) prepare one sequence each, block B computes the work plan, and the
 // remaining blocks pack one (node block, KV head) each.  None of them reads
-// another's output; the attention kernel that follows reads all three.
+// another's output; the attention kernel that follows reads all three.  In the
+// whole scoring pass the start of the call (status word, workers' counter,
+// per-sequence error words) is folded into the same launch.
 #include "tav_internal.h"
 
 namespace tav {
@@ -57,15 +59,19 @@ struct PrepArgs {
   uint8_t* chain_out;
   uint32_t* status;
   uint32_t* seq_err;
+  int fused_start;   // the call's start is folded into the prelude: errors go to seq_err[b] only
 };
 
 // Sequence b: validate parents, detect a chain, and build depth, position and the 256-bit
-// ancestor masks of a non-chain tree.
+// ancestor masks of a non-chain tree.  With fused_start the block first clears seq_err[b] (no start
+// kernel ran) and reports its errors there only: another block of the same launch clears the status
+// word, and the call's last kernel folds the sequences' error words into it.
 __device__ void prep_sequence(const PrepArgs& a, int b) {
   __shared__ int par_s[kMaxTreeNodes];
   const int s0 = a.node_offsets[b];
   const int n = a.node_offsets[b + 1] - s0;
   const int L = a.prefix_len[b];
+  if (a.fused_start && threadIdx.x == 0) a.seq_err[b] = 0u;
   int bad = 0, not_chain = 0;
   for (int v = threadIdx.x; v < n; v += blockDim.x) {
     int p = a.parent[s0 + v];
@@ -76,7 +82,7 @@ __device__ void prep_sequence(const PrepArgs& a, int b) {
   not_chain = __syncthreads_or(not_chain);
   if (bad) {
     if (threadIdx.x == 0) {
-      atomicOr(a.status, (uint32_t)TAV_DEV_BAD_PARENT);
+      if (!a.fused_start) atomicOr(a.status, (uint32_t)TAV_DEV_BAD_PARENT);
       atomicOr(a.seq_err + b, (uint32_t)TAV_DEV_BAD_PARENT);
       a.chain_ws[b] = 0;
     }
@@ -99,7 +105,7 @@ __device__ void prep_sequence(const PrepArgs& a, int b) {
   }
   if (n > kMaxTreeNodes) {
     if (threadIdx.x == 0) {
-      atomicOr(a.status, (uint32_t)TAV_DEV_TREE_TOO_LARGE);
+      if (!a.fused_start) atomicOr(a.status, (uint32_t)TAV_DEV_TREE_TOO_LARGE);
       atomicOr(a.seq_err + b, (uint32_t)TAV_DEV_TREE_TOO_LARGE);
     }
     return;
@@ -128,6 +134,7 @@ __device__ void prep_sequence(const PrepArgs& a, int b) {
 
 struct PlanArgs {
   int B, NB, bs, total_rb_host, tiles_host, tail_blocks_host, C, W;
+  int fused_start;   // the plan block clears the status word and the workers' counter first
 };
 
 // The attention work plan (one block): seq_rb_off[B+1] (row blocks per sequence), rb_seq,
@@ -148,6 +155,10 @@ __device__ void plan_block(const PlanArgs& p, const AttnArgs& a) {
   int32_t* wg_rb = const_cast<int32_t*>(a.wg_rb);
   int32_t* wg_tile = const_cast<int32_t*>(a.wg_tile);
   int32_t* rb_meta = const_cast<int32_t*>(a.rb_meta);
+  if (p.fused_start && threadIdx.x == 0) {   // (only this block writes the status word in this launch)
+    a.status[0] = 0u;
+    a.status[kCounterWord] = 0u;
+  }
   const bool small = B + 1 <= kPlanLds && p.total_rb_host + 1 <= kPlanLds;
   int* off = small ? off_s : seq_rb_off;   // working copies (LDS or the outputs themselves)
   int* tile = small ? tile_s : rb_tile;
@@ -393,6 +404,7 @@ PrepArgs prep_args(const int32_t* node_offsets, const int32_t* prefix_len, const
   a.chain_out = out ? out->is_chain : nullptr;
   a.status = status;
   a.seq_err = seq_err;
+  a.fused_start = 0;
   return a;
 }
 
@@ -413,10 +425,12 @@ hipError_t launch_prep(const Plan& p, const int32_t* node_offsets, const int32_t
 }
 
 hipError_t launch_prelude(const Plan& p, const int32_t* parent, const tav_tree_out* out, const AttnArgs& a,
-                          const OrderArgs& o, hipStream_t s) {
-  const PrepArgs pa = prep_args(a.node_offsets, a.prefix_len, parent, const_cast<uint8_t*>(a.is_chain),
-                                const_cast<uint64_t*>(a.mask), out, a.status, a.seq_err);
+                          const OrderArgs& o, bool fused_start, hipStream_t s) {
+  PrepArgs pa = prep_args(a.node_offsets, a.prefix_len, parent, const_cast<uint8_t*>(a.is_chain),
+                          const_cast<uint64_t*>(a.mask), out, a.status, a.seq_err);
+  pa.fused_start = fused_start ? 1 : 0;
   PlanArgs pl;
+  pl.fused_start = fused_start ? 1 : 0;
   pl.B = p.B; pl.NB = p.NB; pl.bs = p.bs; pl.total_rb_host = p.total_rb; pl.tiles_host = p.tiles_per_head;
   pl.tail_blocks_host = p.tail_blocks; pl.C = p.C; pl.W = p.W;
   const int grid = p.B + 1 + p.tail_blocks * p.Hkv + (o.order ? 1 : 0);

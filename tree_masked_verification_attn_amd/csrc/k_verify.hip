@@ -73,8 +73,12 @@ __global__ __launch_bounds__(64) void walk_kernel(WalkArgs a) {
   const int b = blockIdx.x, lane = threadIdx.x;
   const int s0 = a.node_offsets[b];
   const int n = a.node_offsets[b + 1] - s0;
-  // a sequence with an error found by an earlier kernel of the call: sentinel outputs
-  if (a.seq_err[b] != 0u || (a.status[0] & TAV_DEV_PLAN_MISMATCH) != 0u) {
+  // a sequence with an error found by an earlier kernel of the call: sentinel outputs (its error
+  // bits also go into the status word here: a call whose start was folded into the prelude reports
+  // the preparation's errors in seq_err only)
+  const uint32_t serr = a.seq_err[b];
+  if (serr != 0u || (a.status[0] & TAV_DEV_PLAN_MISMATCH) != 0u) {
+    if (lane == 0 && serr) atomicOr(a.status, serr);
     for (int j = lane; j < n; j += 64) a.node_status[s0 + j] = 0;
     for (int j = lane; j < a.max_path; j += 64) a.path[(size_t)b * a.max_path + j] = -1;
     if (lane == 0) {

@@ -334,10 +334,11 @@ tav_status timing_pair(hipEvent_t* start, hipEvent_t* stop) {
 // attention kernel and the merge of split row blocks).
 tav_status enqueue_prep_attention(const tav_problem* p, const Plan& P, const tav_tree* t,
                                   const tav_tree_out* out, const tav_attn_io* io, void* ws, hipStream_t s,
-                                  const OrderArgs& order = OrderArgs{nullptr, 0, 0, nullptr}) {
+                                  const OrderArgs& order = OrderArgs{nullptr, 0, 0, nullptr},
+                                  bool fused_start = false) {
   const AttnArgs a = attn_args(p, P, io, ws);
   if (p->dtype == TAV_BF16) {
-    TAV_HIP(launch_prelude(P, t->parent, out, a, order, s));
+    TAV_HIP(launch_prelude(P, t->parent, out, a, order, fused_start, s));
     hipEvent_t ev0 = nullptr, ev1 = nullptr;
     if (g_timing.which == 1) {
       const tav_status st = timing_pair(&ev0, &ev1);
@@ -505,15 +506,20 @@ tav_status attn_verify_impl(const tav_problem* prob, const tav_tree* tree, const
     st = get_events(&fork, &join);
     if (st != TAV_OK) return st;
   }
-  // attn_stream: start, preparation, attention, merge, the verification's workers, the walk.  The
+  // attn_stream: start, preparation, attention, merge, the verification's kernels, the walk.  The
   // attention kernel and the workers each take whole compute units, so they run one after the
   // other.  PreSTO is independent: on verify_stream (if different) from the start.
   // the workers' node order: built by an extra block of the bf16 prelude, else by the start kernel
   const bool order_in_prelude = verify && prob->dtype == TAV_BF16;
   const OrderArgs order{verify ? verify->draft_row : nullptr, verify ? verify->num_draft_rows : 0, P.N,
                         verify ? ws_at<int32_t>(workspace, P.off_order) : nullptr};
-  TAV_HIP(launch_start(ws_at<uint32_t>(workspace, P.off_status), ws_at<uint32_t>(workspace, P.off_seq_err), P.B,
-                       order_in_prelude ? nullptr : order.draft_row, order.R, P.N, order.order, sa));
+  // the start of the call folded into the prelude (one launch fewer) when nothing else starts before
+  // it: bf16 with verification (the walk then folds the sequences' error words into the status word)
+  // and no PreSTO batch (which would run beside the prelude on its own stream)
+  const bool fused_start = order_in_prelude && !presto;
+  if (!fused_start)
+    TAV_HIP(launch_start(ws_at<uint32_t>(workspace, P.off_status), ws_at<uint32_t>(workspace, P.off_seq_err), P.B,
+                         order_in_prelude ? nullptr : order.draft_row, order.R, P.N, order.order, sa));
   if (two) {
     TAV_HIP(hipEventRecord(fork, sa));
     TAV_HIP(hipStreamWaitEvent(sv, fork, 0));
@@ -524,7 +530,7 @@ tav_status attn_verify_impl(const tav_problem* prob, const tav_tree* tree, const
   }
   if (two) TAV_HIP(hipEventRecord(join, sv));
   st = enqueue_prep_attention(prob, P, tree, tree_out, attn, workspace, sa,
-                              order_in_prelude ? order : OrderArgs{nullptr, 0, 0, nullptr});
+                              order_in_prelude ? order : OrderArgs{nullptr, 0, 0, nullptr}, fused_start);
   if (st != TAV_OK) return st;
   if (verify) {
     st = enqueue_verify(prob, P, tree, verify, workspace, sa, two ? join : nullptr);

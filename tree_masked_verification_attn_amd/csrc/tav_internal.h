@@ -258,7 +258,7 @@ struct OrderArgs {
   int32_t* order;
 };
 hipError_t launch_prelude(const Plan& p, const int32_t* parent, const tav_tree_out* out, const AttnArgs& a,
-                          const OrderArgs& o, hipStream_t s);
+                          const OrderArgs& o, bool fused_start, hipStream_t s);
 hipError_t launch_attn_bf16(const Plan& p, const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_f32(const Plan& p, const AttnArgs& a, hipStream_t s);
 // Merge of the cut row blocks; also writes the sentinel rows (out = 0, lse = -inf) of every
