@@ -7,12 +7,13 @@
 namespace tav {
 
 // out = sum_s exp(lse_s - LSE) O_s over the pieces of row block r, KV head g, rows [row0, row0 +
-// nrows); the pieces O_s are normalised by their own sums and stored in bf16, lse_s in float.  Row block r's key tiles [A, E) were cut into the pieces of workgroups A/C .. (E-1)/C;
-// the first piece sits in slot 2w+1 of its workgroup (its last segment), the others in slot 2w
-// (their workgroup's first segment).  A thread owns 4 outputs at a time.
+// nrows); the pieces O_s are normalised by their own sums and stored in bf16, lse_s in float.  Row
+// block r's key tiles [A, E) were cut into the pieces of workgroups A/C .. (E-1)/C; the first piece
+// sits in slot 2w+1 of its workgroup (its last segment), the others in slot 2w (their workgroup's
+// first segment).  A thread owns 4 outputs at a time.
 template <typename OutT>
 __device__ inline void merge_rows(const AttnArgs& a, int D, int log2G, int r, int g, int row0, int nrows) {
-  // the row block's record from the plan (one round of loads beside the status words)
+  // the row block's record from the plan (one round of loads beside the status word)
   const int32_t* m = a.rb_meta + (size_t)r * kMetaWords;
   const int b = m[kMetaSeq], s0 = m[kMetaS0], n = m[kMetaN], node0 = m[kMetaNode0];
   const int wf = m[kMetaWf], wl = m[kMetaWl];
@@ -21,6 +22,48 @@ __device__ inline void merge_rows(const AttnArgs& a, int D, int log2G, int r, in
   const int NB = kRowsPerWG >> log2G;
   const int G = 1 << log2G;
   const int nodes_here = min(NB, n - node0);
+  const int DQ = D / 4;
+  const int ntask = nrows * DQ;   // a task: four outputs of one row
+  const bool cut = wf != wl;
+  constexpr int kT = 2;      // tasks per thread taken with their loads in flight together (16 rows x
+                             // D / 4 at D <= 128 on 256 threads); further tasks go one by one
+  constexpr int kPre = 6;    // pieces loaded together (a batch), folded in by an online softmax
+  auto task_row = [&](int task) { return row0 + task / DQ; };
+  auto task_ok = [&](int task) { return task < ntask && (task_row(task) >> log2G) < nodes_here; };
+  auto base_of = [&](int w, int row) {
+    const int slot = w == wf ? 2 * w + 1 : 2 * w;
+    return ((size_t)slot * a.Hkv + g) * kRowsPerWG + row;
+  };
+  auto load_batch = [&](int task, int w0, float (&ls)[kPre], uint2 (&ob)[kPre]) {
+    const int row = task_row(task), dq = task % DQ;
+#pragma unroll
+    for (int q = 0; q < kPre; ++q) {
+      ls[q] = -INFINITY;
+      ob[q] = make_uint2(0u, 0u);
+      if (w0 + q <= wl) {
+        const size_t base = base_of(w0 + q, row);
+        ls[q] = a.part_lse[base];
+        ob[q] = *(const uint2*)(a.part_o + base * D + dq * 4);   // 4 bf16
+      }
+    }
+  };
+  // second round: the first batch of this thread's first kT tasks, issued with the sequence's error
+  // word (the pieces' slots are valid whatever the sequence's state; they are used only without errors)
+  float ls0[kT][kPre];
+  uint2 ob0[kT][kPre];
+#pragma unroll
+  for (int i = 0; i < kT; ++i) {
+    const int task = threadIdx.x + i * blockDim.x;
+    if (cut && task_ok(task)) {
+      load_batch(task, wf, ls0[i], ob0[i]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < kPre; ++q) {
+        ls0[i][q] = -INFINITY;
+        ob0[i][q] = make_uint2(0u, 0u);
+      }
+    }
+  }
   if (a.seq_err[b] & kAttnErrBits) {
     // the sequence's tree or prefix is unusable: its rows become sentinels (out = 0, lse = -inf)
     for (int task = threadIdx.x; task < nrows * D; task += blockDim.x) {
@@ -32,62 +75,71 @@ __device__ inline void merge_rows(const AttnArgs& a, int D, int log2G, int r, in
     }
     return;
   }
-  if (wf == wl) return;  // one workgroup held the whole row block
-  const int DQ = D / 4;
-  constexpr int kPre = 4;   // pieces whose loads are all issued before any is used
-  const int np = wl - wf + 1;
-  for (int task = threadIdx.x; task < nrows * DQ; task += blockDim.x) {
-    const int row = row0 + task / DQ, dq = task % DQ;
-    if ((row >> log2G) >= nodes_here) continue;
+  if (!cut) return;  // one workgroup held the whole row block
+  // out = sum_s exp(lse_s - LSE) O_s / sum_s exp(lse_s - LSE), LSE the running maximum of the lse_s
+  struct Acc {
+    float M = -INFINITY, den = 0.f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  };
+  auto fold = [](Acc& c, const float (&ls)[kPre], const uint2 (&ob)[kPre]) {
+    float mb = c.M;
+#pragma unroll
+    for (int q = 0; q < kPre; ++q) mb = fmaxf(mb, ls[q]);
+    if (mb > c.M) {
+      const float sc = c.M == -INFINITY ? 0.f : __expf(c.M - mb);
+      c.den *= sc;
+      c.o.x *= sc; c.o.y *= sc; c.o.z *= sc; c.o.w *= sc;
+      c.M = mb;
+    }
+#pragma unroll
+    for (int q = 0; q < kPre; ++q) {
+      if (ls[q] == -INFINITY) continue;
+      const float wgt = __expf(ls[q] - c.M);
+      c.den += wgt;
+      c.o.x += wgt * __uint_as_float(ob[q].x << 16);
+      c.o.y += wgt * __uint_as_float(ob[q].x & 0xFFFF0000u);
+      c.o.z += wgt * __uint_as_float(ob[q].y << 16);
+      c.o.w += wgt * __uint_as_float(ob[q].y & 0xFFFF0000u);
+    }
+  };
+  auto finish = [&](int task, const Acc& c) {
+    const int row = task_row(task), dq = task % DQ;
     const int node = s0 + node0 + (row >> log2G);
     const int head = g * G + (row & (G - 1));
-    float M = -INFINITY;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    float den = 0.f;
-    auto add_piece = [&](float ls, uint2 ob) {
-      if (ls == -INFINITY) return;
-      const float wgt = __expf(ls - M);
-      den += wgt;
-      acc.x += wgt * __uint_as_float(ob.x << 16);
-      acc.y += wgt * __uint_as_float(ob.x & 0xFFFF0000u);
-      acc.z += wgt * __uint_as_float(ob.y << 16);
-      acc.w += wgt * __uint_as_float(ob.y & 0xFFFF0000u);
-    };
-    auto base_of = [&](int w) {
-      const int slot = w == wf ? 2 * w + 1 : 2 * w;
-      return ((size_t)slot * a.Hkv + g) * kRowsPerWG + row;
-    };
-    if (np <= kPre) {
+    const float inv = c.den > 0.f ? 1.f / c.den : 0.f;
+    OutT* op = (OutT*)a.out + ((size_t)node * a.Hq + head) * D + dq * 4;
+    op[0] = (OutT)(c.o.x * inv);
+    op[1] = (OutT)(c.o.y * inv);
+    op[2] = (OutT)(c.o.z * inv);
+    op[3] = (OutT)(c.o.w * inv);
+    if (dq == 0 && a.lse) a.lse[(size_t)node * a.Hq + head] = c.den > 0.f ? c.M + __logf(c.den) : -INFINITY;
+  };
+  auto rest = [&](int task, Acc& c) {   // the batches after the first
+    for (int w0 = wf + kPre; w0 <= wl; w0 += kPre) {
       float ls[kPre];
       uint2 ob[kPre];
-#pragma unroll
-      for (int i = 0; i < kPre; ++i) {
-        ls[i] = -INFINITY;
-        ob[i] = make_uint2(0u, 0u);
-        if (i < np) {
-          const size_t base = base_of(wf + i);
-          ls[i] = a.part_lse[base];
-          ob[i] = *(const uint2*)(a.part_o + base * D + dq * 4);   // 4 bf16
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < kPre; ++i) M = fmaxf(M, ls[i]);
-#pragma unroll
-      for (int i = 0; i < kPre; ++i) add_piece(ls[i], ob[i]);
-    } else {
-      for (int w = wf; w <= wl; ++w) M = fmaxf(M, a.part_lse[base_of(w)]);
-      for (int w = wf; w <= wl; ++w) {
-        const size_t base = base_of(w);
-        add_piece(a.part_lse[base], *(const uint2*)(a.part_o + base * D + dq * 4));
-      }
+      load_batch(task, w0, ls, ob);
+      fold(c, ls, ob);
     }
-    const float inv = den > 0.f ? 1.f / den : 0.f;
-    OutT* op = (OutT*)a.out + ((size_t)node * a.Hq + head) * D + dq * 4;
-    op[0] = (OutT)(acc.x * inv);
-    op[1] = (OutT)(acc.y * inv);
-    op[2] = (OutT)(acc.z * inv);
-    op[3] = (OutT)(acc.w * inv);
-    if (dq == 0 && a.lse) a.lse[(size_t)node * a.Hq + head] = den > 0.f ? M + __logf(den) : -INFINITY;
+  };
+#pragma unroll
+  for (int i = 0; i < kT; ++i) {
+    const int task = threadIdx.x + i * blockDim.x;
+    if (!task_ok(task)) continue;
+    Acc c;
+    fold(c, ls0[i], ob0[i]);
+    rest(task, c);
+    finish(task, c);
+  }
+  for (int task = threadIdx.x + kT * blockDim.x; task < ntask; task += blockDim.x) {
+    if (!task_ok(task)) continue;
+    float ls[kPre];
+    uint2 ob[kPre];
+    load_batch(task, wf, ls, ob);
+    Acc c;
+    fold(c, ls, ob);
+    rest(task, c);
+    finish(task, c);
   }
 }
 

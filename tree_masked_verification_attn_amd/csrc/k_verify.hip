@@ -12,11 +12,12 @@
 // The vocabulary work of every node (M, S, Z, p and q~ at the children's tokens,
 // the would-be final draw) is done by the kernels of vocab_worker.h: streaming
 // workers (512-thread workgroups taking nodes from a queue), then the pick of
-// every node (one wave each).  walk_kernel
-// (one wave per sequence) then takes the accept/reject decisions in fp64 from
-// these values.
+// every node (one wave each), which also takes the node's accept/reject step in
+// fp64 (a step depends on the node's own values only).  walk_kernel (one
+// workgroup per sequence) follows the accepted children from the root.
 #include "tav_internal.h"
 #include "vocab_worker.h"
+#include "attn_merge.h"
 
 namespace tav {
 namespace {
@@ -55,169 +56,114 @@ __global__ __launch_bounds__(64 * kPickWaves) void pick_kernel(VocabArgs a) {
   vw::pick_node<LT>(a, P[wave], v);
 }
 
-constexpr int kWalkLds = 1024;  // nodes whose walk data fit in LDS
+constexpr int kWalkThreads = 256;
+constexpr int kWalkLds = 1024;   // nodes whose steps are staged in LDS
+constexpr int kPathLds = 256;    // path entries kept in LDS
+constexpr int kWalkPre = 4;      // nodes per thread whose parent and mark are loaded before the chase
 
-// One wave per sequence: the layer-by-layer walk, decisions in fp64 from the values the
-// vocabulary kernels left: p(token) and q~(token) of every child, Z and the final draw of
-// every node.  For sequences of up to kWalkLds nodes these values, the parents and the
-// sampled flags are first staged in LDS (one round of loads).
-__global__ __launch_bounds__(64) void walk_kernel(WalkArgs a) {
-  __shared__ int par_s[kWalkLds];
-  __shared__ uint8_t smp_s[kWalkLds];
-  __shared__ double cp_s[kWalkLds];
-  __shared__ float cq_s[kWalkLds];
-  __shared__ float u_s[kWalkLds];
-  __shared__ float z_s[kWalkLds];
-  __shared__ int tt_s[kWalkLds];
-  __shared__ int kids[kMaxChildren];
-  const int b = blockIdx.x, lane = threadIdx.x;
+// The walk of sequence b (one 256-thread workgroup): from the root, each node's accepted child (the
+// steps the pick took for every node) until a node accepts none; the path's last node gives the
+// bonus token (its final draw).  Statuses: 1 on the path, 2 for a child rejected by its parent's step
+// where that parent lies on the path, else 0.  A sequence with an error found by an earlier kernel
+// of the call, or by the walk, gets the sentinel outputs (statuses 0, path -1, path_len 0, bonus -1).
+__device__ void walk_sequence(const WalkArgs& a, int b) {
+  __shared__ StepRec st_s[kWalkLds];
+  __shared__ int path_s[kPathLds];
+  __shared__ int res[4];   // sentinel flag, path length, bonus, error bits
+  const int tid = threadIdx.x;
   const int s0 = a.node_offsets[b];
   const int n = a.node_offsets[b + 1] - s0;
-  // a sequence with an error found by an earlier kernel of the call: sentinel outputs (its error
-  // bits also go into the status word here: a call whose start was folded into the prelude reports
-  // the preparation's errors in seq_err only)
-  const uint32_t serr = a.seq_err[b];
-  if (serr != 0u || (a.status[0] & TAV_DEV_PLAN_MISMATCH) != 0u) {
-    if (lane == 0 && serr) atomicOr(a.status, serr);
-    for (int j = lane; j < n; j += 64) a.node_status[s0 + j] = 0;
-    for (int j = lane; j < a.max_path; j += 64) a.path[(size_t)b * a.max_path + j] = -1;
-    if (lane == 0) {
+  int32_t* path = a.path + (size_t)b * a.max_path;
+  if (tid == 0) {
+    // errors of the sequence found earlier in the call (their bits also go into the status word
+    // here: a call whose start was folded into the prelude reports the preparation's errors in
+    // seq_err only); read by one thread so that the whole workgroup takes the same branch
+    const uint32_t serr = a.seq_err[b];
+    if (serr) atomicOr(a.status, serr);
+    res[0] = serr != 0u || (a.status[0] & TAV_DEV_PLAN_MISMATCH) != 0u;
+  }
+  for (int j = tid; j < n && j < kWalkLds; j += kWalkThreads) st_s[j] = a.step[s0 + j];
+  int pj[kWalkPre];
+  uint8_t mj[kWalkPre];
+#pragma unroll
+  for (int i = 0; i < kWalkPre; ++i) {
+    const int j = tid + i * kWalkThreads;
+    pj[i] = j < n ? a.parent[s0 + j] : -1;
+    mj[i] = j < n ? a.node_status[s0 + j] : 0;
+  }
+  __syncthreads();
+  if (tid == 0 && !res[0]) {
+    int v = 0, plen = 1, bonus = -1;
+    uint32_t err = 0;
+    path[0] = 0;
+    path_s[0] = 0;
+    for (int it = 0; it < n; ++it) {
+      const StepRec r = v < kWalkLds ? st_s[v] : a.step[s0 + v];
+      if (r.err) { err = r.err; break; }
+      if (r.next < 0) { bonus = r.bonus; break; }
+      if (r.next <= v || r.next >= n) { err = TAV_DEV_BAD_PARENT; break; }   // (children follow parents)
+      if (plen >= a.max_path) { err = TAV_DEV_PATH_OVERFLOW; break; }
+      path[plen] = r.next;
+      if (plen < kPathLds) path_s[plen] = r.next;
+      ++plen;
+      v = r.next;
+    }
+    if (err) atomicOr(a.status, err);
+    res[0] = err != 0u;
+    res[1] = plen;
+    res[2] = bonus;
+  }
+  __syncthreads();
+  if (res[0]) {
+    for (int j = tid; j < n; j += kWalkThreads) a.node_status[s0 + j] = 0;
+    for (int j = tid; j < a.max_path; j += kWalkThreads) path[j] = -1;
+    if (tid == 0) {
       a.path_len[b] = 0;
       a.bonus[b] = -1;
     }
     return;
   }
-  const bool staged = n <= kWalkLds;
-  for (int j = lane; j < n; j += 64) {
-    a.node_status[s0 + j] = 0;
-    if (staged) {
-      par_s[j] = a.parent[s0 + j];
-      smp_s[j] = a.sampled[s0 + j];
-      cp_s[j] = a.child_p[s0 + j];
-      cq_s[j] = a.child_q[s0 + j];
-      u_s[j] = a.uniforms[(size_t)(s0 + j) * 2];
-      z_s[j] = a.stats[(size_t)(s0 + j) * 3 + 2];
-      tt_s[j] = a.term_token[s0 + j];
+  const int plen = res[1];
+  // node x is on the path iff it is one of its (ascending) entries
+  auto on_path = [&](int x) -> bool {
+    int lo = 0, hi = plen;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      const int e = mid < kPathLds ? path_s[mid] : path[mid];
+      if (e < x) lo = mid + 1; else hi = mid;
     }
-  }
-  for (int j = lane; j < a.max_path; j += 64) a.path[(size_t)b * a.max_path + j] = -1;
-  auto parent_of = [&](int j) { return staged ? par_s[j] : a.parent[s0 + j]; };
-  auto sampled_of = [&](int j) { return staged ? (int)smp_s[j] : (int)a.sampled[s0 + j]; };
-  auto p_of = [&](int j) { return staged ? cp_s[j] : a.child_p[s0 + j]; };
-  auto q_of = [&](int j) { return (double)(staged ? cq_s[j] : a.child_q[s0 + j]); };
-  auto u_of = [&](int j) { return (double)(staged ? u_s[j] : a.uniforms[(size_t)(s0 + j) * 2]); };
-  __syncthreads();
-  uint32_t err = 0;
-  int plen = 1, v = 0, bonus = -1;
-  // temperature 0: greedy decoding (Progressive Tree Drafting, Section 3.2) -- the child whose
-  // token is the node's verification token (p = 1 there, 0 elsewhere) is accepted, the children
-  // passed over before it (sampled child first, then ascending id) are rejected
-  const bool greedy = a.temperature[b] == 0.f;
-  if (lane == 0) {
-    a.node_status[s0] = 1;
-    a.path[(size_t)b * a.max_path] = 0;
-  }
-  for (int iter = 0; iter < n; ++iter) {
-    // children of v in ascending id (sampled child found on the way)
-    int nk = 0, s = -1;
-    for (int base = 1; base < n; base += 64) {
-      const int j = base + lane;
-      const int pj = j < n ? parent_of(j) : -2;
-      const bool is_kid = pj == v;
-      const unsigned long long m = __ballot(is_kid);
-      if (is_kid) {
-        const int at = nk + __popcll(m & ((1ull << lane) - 1ull));
-        if (at < kMaxChildren) kids[at] = j;
-        if (sampled_of(j)) s = j;
-      }
-      nk += __popcll(m);
-    }
-    __syncthreads();
+    return lo < plen && (lo < kPathLds ? path_s[lo] : path[lo]) == x;
+  };
+  auto status_of = [&](int j, int pr, uint8_t mk) -> uint8_t {
+    return on_path(j) ? 1 : (j > 0 && mk == 2 && on_path(pr)) ? 2 : 0;
+  };
 #pragma unroll
-    for (int d = 32; d > 0; d >>= 1) s = max(s, __shfl_xor(s, d));
-    if (nk > kMaxChildren) { err |= TAV_DEV_TOO_MANY_CHILDREN; break; }
-    int next = -1;
-    if (lane == 0 && greedy) {
-      if (s >= 0) {
-        if (p_of(s) == 1.0) next = s;
-        else a.node_status[s0 + s] = 2;
-      }
-      for (int k = 0; k < nk && next < 0; ++k) {
-        const int c = kids[k];
-        if (c == s) continue;
-        if (p_of(c) == 1.0) next = c;
-        else a.node_status[s0 + c] = 2;
-      }
-      if (next >= 0) {
-        a.node_status[s0 + next] = 1;
-        if (plen >= a.max_path) err |= TAV_DEV_PATH_OVERFLOW;
-        else a.path[(size_t)b * a.max_path + plen] = next;
-        ++plen;
-      } else {
-        bonus = staged ? tt_s[v] : a.term_token[s0 + v];
-        if (bonus < 0) err |= TAV_DEV_EMPTY_RESIDUAL;
-      }
-    } else if (lane == 0) {
-      bool resid = false;
-      const double Zv = (double)(staged ? z_s[v] : a.stats[(size_t)(s0 + v) * 3 + 2]);
-      // the tests u <= min(1, p / q~) and u <= r / (1 - rejected mass) are taken as products
-      // (u q~ <= p, u (1 - rejected) <= r): the same decisions up to the last bits of the ratios, with
-      // no fp64 division on the walk's serial path (one reciprocal of Z per residual node)
-      if (s >= 0) {
-        const double qs = q_of(s);
-        if (!(qs > 0.0)) {
-          err |= TAV_DEV_ZERO_DRAFT_MASS;
-        } else if (u_of(s) * qs <= p_of(s)) {
-          next = s;
-        } else {
-          a.node_status[s0 + s] = 2;
-          resid = true;
-        }
-      }
-      if (!err && next < 0) {
-        const double invZ = resid && Zv > 0.0 ? 1.0 / Zv : 0.0;
-        double rej = 0.0;
-        for (int k = 0; k < nk && next < 0; ++k) {
-          const int c = kids[k];
-          if (c == s) continue;
-          const double p = p_of(c);
-          const double r0 = resid ? fmax(0.0, p - q_of(c)) * invZ : p;
-          const double rem = 1.0 - rej;
-          const double uc = u_of(c);
-          if (rem > 0.0 ? uc * rem <= r0 : uc <= 0.0) {
-            next = c;
-          } else {
-            a.node_status[s0 + c] = 2;
-            rej += r0;
-          }
-        }
-      }
-      if (!err && next >= 0) {
-        a.node_status[s0 + next] = 1;
-        if (plen >= a.max_path) err |= TAV_DEV_PATH_OVERFLOW;
-        else a.path[(size_t)b * a.max_path + plen] = next;
-        ++plen;
-      } else if (!err) {
-        bonus = staged ? tt_s[v] : a.term_token[s0 + v];
-        if (bonus < 0) err |= TAV_DEV_EMPTY_RESIDUAL;
-      }
-    }
-    next = __shfl(next, 0);
-    err = __shfl(err, 0);
-    __syncthreads();
-    if (next < 0 || err) break;
-    v = next;
+  for (int i = 0; i < kWalkPre; ++i) {
+    const int j = tid + i * kWalkThreads;
+    if (j < n) a.node_status[s0 + j] = status_of(j, pj[i], mj[i]);
   }
-  __syncthreads();
-  if (err) {   // an error found by the walk itself: the same sentinel outputs
-    for (int j = lane; j < n; j += 64) a.node_status[s0 + j] = 0;
-    for (int j = lane; j < a.max_path; j += 64) a.path[(size_t)b * a.max_path + j] = -1;
+  for (int j = tid + kWalkPre * kWalkThreads; j < n; j += kWalkThreads)
+    a.node_status[s0 + j] = status_of(j, a.parent[s0 + j], a.node_status[s0 + j]);
+  for (int j = plen + tid; j < a.max_path; j += kWalkThreads) path[j] = -1;
+  if (tid == 0) {
+    a.path_len[b] = plen;
+    a.bonus[b] = res[2];
   }
-  if (lane == 0) {
-    if (err) atomicOr(a.status, err);
-    a.path_len[b] = err ? 0 : min(plen, a.max_path);
-    a.bonus[b] = err ? -1 : bonus;
+}
+
+// Workgroups [0, B) walk the sequences; with nm > 0 the next nm workgroups merge the cut attention
+// row blocks (the work of merge_kernel, 16 rows of one (row block, KV head) each), which run beside
+// the walks instead of in a launch of their own.
+__global__ __launch_bounds__(kWalkThreads) void walk_kernel(WalkArgs w, AttnArgs a, int D, int log2G, int nm) {
+  const int blk = blockIdx.x;
+  if (blk < w.B) {
+    walk_sequence(w, blk);
+    return;
   }
+  const int m = blk - w.B;
+  if (m >= nm) return;
+  constexpr int kZ = kRowsPerWG / 16;
+  merge_rows<__bf16>(a, D, log2G, m / (kZ * a.Hkv), (m / kZ) % a.Hkv, (m % kZ) * 16, 16);
 }
 
 template <typename LT>
@@ -242,8 +188,10 @@ hipError_t launch_vocab(const VocabArgs& a, bool bf16_logits, int num_cus, hipSt
   return bf16_logits ? launch_vocab_t<uint16_t>(a, num_cus, s) : launch_vocab_t<float>(a, num_cus, s);
 }
 
-hipError_t launch_walk(const WalkArgs& a, hipStream_t s) {
-  walk_kernel<<<a.B, 64, 0, s>>>(a);
+hipError_t launch_walk(const WalkArgs& w, const Plan* merge_plan, const AttnArgs* merge, hipStream_t s) {
+  const int nm = merge ? merge_plan->total_rb * merge_plan->Hkv * (kRowsPerWG / 16) : 0;
+  const int D = merge ? merge_plan->D : 0, log2G = merge ? merge_plan->log2G : 0;
+  walk_kernel<<<w.B + nm, kWalkThreads, 0, s>>>(w, merge ? *merge : AttnArgs{}, D, log2G, nm);
   return hipGetLastError();
 }
 

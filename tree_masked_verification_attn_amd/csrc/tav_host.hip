@@ -181,8 +181,7 @@ tav_status make_plan(const tav_problem* p, const tav_presto_io* pr, Plan* out,
   o = align_up(o + (size_t)2 * P.W * P.Hkv * kRowsPerWG * 4);
   P.off_stats = o; o = align_up(o + (size_t)P.N * 3 * 4);
   P.off_term = o; o = align_up(o + (size_t)P.N * 4);
-  P.off_child_p = o; o = align_up(o + (size_t)P.N * 8);
-  P.off_child_q = o; o = align_up(o + (size_t)P.N * 4);
+  P.off_step = o; o = align_up(o + (size_t)P.N * sizeof(StepRec));
   P.off_presto = o; o = align_up(o + (size_t)(pr ? pr->num_requests : 0) * 8);
   P.off_order = o; o = align_up(o + (size_t)(p->vocab > 0 ? P.N : 0) * 4);
   P.off_seq_err = o; o = align_up(o + (size_t)P.B * 4);
@@ -335,7 +334,7 @@ tav_status timing_pair(hipEvent_t* start, hipEvent_t* stop) {
 tav_status enqueue_prep_attention(const tav_problem* p, const Plan& P, const tav_tree* t,
                                   const tav_tree_out* out, const tav_attn_io* io, void* ws, hipStream_t s,
                                   const OrderArgs& order = OrderArgs{nullptr, 0, 0, nullptr},
-                                  bool fused_start = false) {
+                                  bool fused_start = false, bool defer_merge = false) {
   const AttnArgs a = attn_args(p, P, io, ws);
   if (p->dtype == TAV_BF16) {
     TAV_HIP(launch_prelude(P, t->parent, out, a, order, fused_start, s));
@@ -347,7 +346,7 @@ tav_status enqueue_prep_attention(const tav_problem* p, const Plan& P, const tav
     }
     TAV_HIP(launch_attn_bf16(P, a, s));
     if (ev1) TAV_HIP(hipEventRecord(ev1, s));
-    TAV_HIP(launch_merge(P, a, true, s));
+    if (!defer_merge) TAV_HIP(launch_merge(P, a, true, s));
   } else {
     const tav_status st = enqueue_prep(p, P, t, out, ws, s);
     if (st != TAV_OK) return st;
@@ -368,8 +367,8 @@ VocabArgs vocab_args(const tav_problem* p, const Plan& P, const tav_tree* t, con
   va.term_token = io->node_term_token ? io->node_term_token : ws_at<int32_t>(ws, P.off_term);
   va.status = status;
   va.seq_err = ws_at<uint32_t>(ws, P.off_seq_err);
-  va.child_p = ws_at<double>(ws, P.off_child_p);
-  va.child_q = ws_at<float>(ws, P.off_child_q);
+  va.step = ws_at<StepRec>(ws, P.off_step);
+  va.node_status = io->node_status;
   va.B = P.B; va.N = P.N; va.V = p->vocab; va.R = io->num_draft_rows;
   va.queue = (int32_t*)(status + kCounterWord);
   va.order = ws_at<int32_t>(ws, P.off_order);
@@ -379,18 +378,14 @@ VocabArgs vocab_args(const tav_problem* p, const Plan& P, const tav_tree* t, con
   return va;
 }
 
-tav_status enqueue_walk(const tav_problem* p, const Plan& P, const tav_tree* t, const tav_verify_io* io,
-                        const VocabArgs& va, hipStream_t s) {
+tav_status enqueue_walk(const Plan& P, const tav_verify_io* io, const VocabArgs& va, hipStream_t s,
+                        const AttnArgs* merge = nullptr) {
   WalkArgs wa;
-  wa.logits = io->logits; wa.temperature = io->temperature; wa.draft = io->draft;
-  wa.draft_row = io->draft_row; wa.node_offsets = p->node_offsets; wa.parent = t->parent;
-  wa.token = t->token; wa.sampled = t->sampled; wa.uniforms = io->uniforms;
-  wa.stats = va.stats; wa.term_token = va.term_token; wa.node_status = io->node_status; wa.path = io->path;
-  wa.child_p = va.child_p; wa.child_q = va.child_q;
-  wa.path_len = io->path_len; wa.bonus = io->bonus_token; wa.status = va.status; wa.seq_err = va.seq_err;
-  wa.B = P.B; wa.V = p->vocab; wa.R = io->num_draft_rows; wa.max_path = io->max_path;
-  wa.logits_bf16 = p->dtype == TAV_BF16;
-  TAV_HIP(launch_walk(wa, s));
+  wa.node_offsets = va.node_offsets; wa.parent = va.parent; wa.step = va.step;
+  wa.node_status = io->node_status; wa.path = io->path; wa.path_len = io->path_len; wa.bonus = io->bonus_token;
+  wa.status = va.status; wa.seq_err = va.seq_err;
+  wa.B = P.B; wa.max_path = io->max_path;
+  TAV_HIP(launch_walk(wa, &P, merge, s));
   return TAV_OK;
 }
 
@@ -406,7 +401,8 @@ tav_status num_compute_units(int* cus) {
 // in the call: by the bf16 prelude's order block, else by the start kernel), then the walk (after
 // wait_before, when given, on s).
 tav_status enqueue_verify(const tav_problem* p, const Plan& P, const tav_tree* t,
-                          const tav_verify_io* io, void* ws, hipStream_t s, hipEvent_t wait_before = nullptr) {
+                          const tav_verify_io* io, void* ws, hipStream_t s, hipEvent_t wait_before = nullptr,
+                          const AttnArgs* merge = nullptr) {
   const VocabArgs va = vocab_args(p, P, t, io, ws);
   int cus = 0;
   tav_status st = num_compute_units(&cus);
@@ -420,7 +416,7 @@ tav_status enqueue_verify(const tav_problem* p, const Plan& P, const tav_tree* t
   TAV_HIP(launch_vocab(va, p->dtype == TAV_BF16, cus, s));
   if (ev1) TAV_HIP(hipEventRecord(ev1, s));
   if (wait_before) TAV_HIP(hipStreamWaitEvent(s, wait_before, 0));
-  return enqueue_walk(p, P, t, io, va, s);
+  return enqueue_walk(P, io, va, s, merge);
 }
 
 tav_status enqueue_presto(const Plan& P, const tav_presto_io* io, void* ws, hipStream_t s) {
@@ -506,9 +502,10 @@ tav_status attn_verify_impl(const tav_problem* prob, const tav_tree* tree, const
     st = get_events(&fork, &join);
     if (st != TAV_OK) return st;
   }
-  // attn_stream: start, preparation, attention, merge, the verification's kernels, the walk.  The
-  // attention kernel and the workers each take whole compute units, so they run one after the
-  // other.  PreSTO is independent: on verify_stream (if different) from the start.
+  // attn_stream: start, preparation, attention, the verification's kernels, the walk (with the merge
+  // of the cut row blocks in bf16).  The attention kernel and the workers each take whole compute
+  // units, so they run one after the other.  PreSTO is independent: on verify_stream (if different)
+  // from the start.
   // the workers' node order: built by an extra block of the bf16 prelude, else by the start kernel
   const bool order_in_prelude = verify && prob->dtype == TAV_BF16;
   const OrderArgs order{verify ? verify->draft_row : nullptr, verify ? verify->num_draft_rows : 0, P.N,
@@ -529,11 +526,15 @@ tav_status attn_verify_impl(const tav_problem* prob, const tav_tree* tree, const
     if (st != TAV_OK) return st;
   }
   if (two) TAV_HIP(hipEventRecord(join, sv));
+  // bf16 with verification: the merge of the cut row blocks runs in the walk's launch (beside the walks)
+  const bool defer_merge = verify && prob->dtype == TAV_BF16;
   st = enqueue_prep_attention(prob, P, tree, tree_out, attn, workspace, sa,
-                              order_in_prelude ? order : OrderArgs{nullptr, 0, 0, nullptr}, fused_start);
+                              order_in_prelude ? order : OrderArgs{nullptr, 0, 0, nullptr}, fused_start,
+                              defer_merge);
   if (st != TAV_OK) return st;
   if (verify) {
-    st = enqueue_verify(prob, P, tree, verify, workspace, sa, two ? join : nullptr);
+    const AttnArgs ma = attn_args(prob, P, attn, workspace);
+    st = enqueue_verify(prob, P, tree, verify, workspace, sa, two ? join : nullptr, defer_merge ? &ma : nullptr);
     if (st != TAV_OK) return st;
   } else if (two) {
     TAV_HIP(hipStreamWaitEvent(sa, join, 0));

@@ -42,7 +42,7 @@ struct Plan {
   // workspace layout (byte offsets)
   size_t off_status = 0, off_chain = 0, off_mask = 0, off_seq_rb = 0, off_rb_seq = 0,
          off_rb_tile = 0, off_tail_blk = 0, off_wg_rb = 0, off_wg_tile = 0, off_rb_meta = 0, off_ktail = 0, off_vtail = 0, off_part_o = 0,
-         off_part_lse = 0, off_stats = 0, off_term = 0, off_child_p = 0, off_child_q = 0,
+         off_part_lse = 0, off_stats = 0, off_term = 0, off_step = 0,
          off_presto = 0, off_order = 0, off_seq_err = 0, off_cw = 0, off_rec = 0, total = 0;
   int nch = 0;            // vocabulary chunks (64 sixteen-byte units) per row
 };
@@ -119,6 +119,15 @@ constexpr int kRecResidual = 1;   // the chunk weights are those of (p - q~)+
 constexpr int kRecNoMass = 2;     // no finite logit
 constexpr int kRecGreedy = 4;     // temperature 0: M and A are the row's max and argmax
 
+// A node's verification step, taken by the pick for every node (it depends on the node's own values
+// only); the walk follows the accepted children from the root.
+struct StepRec {
+  int next;       // the accepted child (sequence-local id), or -1: the path ends here
+  int bonus;      // with next == -1: the token drawn at this node
+  uint32_t err;   // TAV_DEV_* bits that count only if the walk reaches this node
+  int pad;
+};
+
 struct VocabArgs {
   const void* logits;
   const float* temperature;
@@ -134,8 +143,9 @@ struct VocabArgs {
   const float* uniforms;
   float* stats;          // [N, 3]
   int32_t* term_token;   // [N]
-  double* child_p;       // [N] p of the node's token under its parent's target distribution
-  float* child_q;        // [N] q~ of the node's token under its parent's draft row (0 if none)
+  StepRec* step;         // [N] each node's verification step, for the walk
+  uint8_t* node_status;  // [N] output; the pick writes 2 for every child its step rejects, else 0 (the walk
+                         // keeps the 2 only where the parent lies on the accepted path)
   uint32_t* status;
   uint32_t* seq_err;     // [B] device-detected errors of each sequence
   int32_t* queue;        // node counter of the workers' queue (cleared with the status word)
@@ -146,26 +156,16 @@ struct VocabArgs {
 };
 
 struct WalkArgs {
-  const void* logits;
-  const float* temperature;
-  const float* draft;
-  const int32_t* draft_row;
   const int32_t* node_offsets;
   const int32_t* parent;
-  const int32_t* token;
-  const uint8_t* sampled;
-  const float* uniforms;
-  const float* stats;
-  const int32_t* term_token;
-  const double* child_p;
-  const float* child_q;
-  uint8_t* node_status;
+  const StepRec* step;         // [N] each node's step, from the pick
+  uint8_t* node_status;        // [N] the pick's rejection marks in, the walk's statuses out
   int32_t* path;
   int32_t* path_len;
   int32_t* bonus;
   uint32_t* status;
-  const uint32_t* seq_err;   // [B] errors found by the earlier kernels of the call
-  int B, V, R, max_path, logits_bf16;
+  const uint32_t* seq_err;     // [B] errors found by the earlier kernels of the call
+  int B, max_path;
 };
 
 struct PrestoArgs {
@@ -268,7 +268,9 @@ hipError_t launch_merge(const Plan& p, const AttnArgs& a, bool bf16_out, hipStre
 hipError_t launch_attn_sentinel_f32(const Plan& p, const AttnArgs& a, hipStream_t s);
 // Vocabulary workers: one 512-thread workgroup per compute unit, persistent over the node queue.
 hipError_t launch_vocab(const VocabArgs& a, bool bf16_logits, int num_cus, hipStream_t s);
-hipError_t launch_walk(const WalkArgs& a, hipStream_t s);
+// The walk: one 256-thread workgroup per sequence; with merge != nullptr the same launch also runs the
+// merge of the cut attention row blocks (launch_merge's work) in further workgroups.
+hipError_t launch_walk(const WalkArgs& a, const Plan* merge_plan, const AttnArgs* merge, hipStream_t s);
 // Draft-tree construction: depth d's pools (one workgroup per (sequence, parent)) and the next
 // parents (one workgroup per sequence); the global prune.
 hipError_t launch_draft_expand(const DraftArgs& a, int d, const uint16_t* logits, const float* uniforms,

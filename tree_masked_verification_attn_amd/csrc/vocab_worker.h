@@ -77,6 +77,9 @@ struct PickLds {
   int kid_id[kMaxChildren];                  // children of the node (sequence-local ids, ascending) ...
   int kid_tok[kMaxChildren];                 // ... their tokens
   float kid_w[kMaxChildren];                 // ... their weights in the final draw's chunks
+  double kid_p[kMaxChildren];                // ... p (fp64) and q~ at their tokens under this node's
+  float kid_q[kMaxChildren];                 // distributions, their acceptance uniforms
+  float kid_u[kMaxChildren];
   uint8_t kid_smp[kMaxChildren];             // ... and sampled flags
   int sp_idx[kMaxDraftSupport];              // sparse draft row: support (ascending ids), q~ there
   float sp_val[kMaxDraftSupport];            // and the part of each token's p taken out of its
@@ -518,6 +521,84 @@ __device__ void vocab_stream(const VocabArgs& a, Lds<C>& L) {
   }
 }
 
+// The verification step at one node, on one wave, in fp64 from its children's values in P (children
+// in ascending id): RheoSampling Section 3.3 Algorithm 1 for one layer -- the sampled child is
+// accepted when u q~ <= p (the test u <= min(1, p / q~) without the division); after its rejection
+// the residual r = (p - q~)+ / Z replaces p; the other children are tested in turn, child c accepted
+// when u_c (1 - rejected mass) <= r(c), the rejected mass being the sum of r over the children
+// tested before c.  At temperature 0 (greedy decoding, Progressive Tree Drafting Section 3.2) the
+// child whose token is the argmax (p = 1) is accepted and the children tested before it are
+// rejected.  A node's step depends on its own values only, so every node's step is taken here and
+// the walk follows the accepted children from the root.  The tests of all children are taken at
+// once (the rejected mass before each child as a prefix sum over the wave); the first child that
+// passes is the accepted one.  Returns its index in the list (-1: none, the final draw at this node
+// ends the path) and the sampled child's index in ks; errors that count only if the walk reaches
+// this node go to derr.  Wave-uniform results.
+__device__ inline int node_step(const PickLds& P, int nk, bool greedy, double Zv, int& ks, uint32_t& derr) {
+  const int lane = threadIdx.x & 63;
+  ks = -1;   // the sampled child (the last one if several: an error reported by the pick)
+  for (int base = 0; base < nk; base += 64) {
+    const int k = base + lane;
+    const unsigned long long m = __ballot(k < nk && P.kid_smp[k]);
+    if (m) ks = base + 63 - __clzll((long long)m);
+  }
+  if (greedy) {
+    if (ks >= 0 && P.kid_p[ks] == 1.0) return ks;
+    for (int base = 0; base < nk; base += 64) {
+      const int k = base + lane;
+      const unsigned long long m = __ballot(k < nk && k != ks && P.kid_p[k] == 1.0);
+      if (m) return base + __ffsll((long long)m) - 1;
+    }
+    return -1;
+  }
+  bool resid = false;
+  if (ks >= 0) {
+    const double qs = (double)P.kid_q[ks];
+    if (!(qs > 0.0)) {
+      derr |= TAV_DEV_ZERO_DRAFT_MASS;
+      return -1;
+    }
+    if ((double)P.kid_u[ks] * qs <= P.kid_p[ks]) return ks;
+    resid = true;
+  }
+  const double invZ = resid && Zv > 0.0 ? 1.0 / Zv : 0.0;
+  double carry = 0.0;   // mass of the children of earlier groups of 64
+  for (int base = 0; base < nk; base += 64) {
+    const int k = base + lane;
+    const bool tested = k < nk && k != ks;
+    const double p = tested ? P.kid_p[k] : 0.0;
+    const double r0 = !tested ? 0.0 : resid ? fmax(0.0, p - (double)P.kid_q[k]) * invZ : p;
+    double incl = r0;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const double y = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += y;
+    }
+    double before = __shfl_up(incl, 1, 64);
+    if (lane == 0) before = 0.0;
+    const double rem = 1.0 - (carry + before);
+    const double uc = tested ? (double)P.kid_u[k] : 0.0;
+    const unsigned long long m = __ballot(tested && (rem > 0.0 ? uc * rem <= r0 : uc <= 0.0));
+    if (m) return base + __ffsll((long long)m) - 1;
+    carry += __shfl(incl, 63);
+  }
+  return -1;
+}
+
+// The step's outputs: the rejection marks of the children (node_status: 2 for the children tested
+// and rejected, kept by the walk where this node lies on the path) and the node's record (accepted
+// child nx, or the final draw `bonus`, an empty residual being an error when the path ends here).
+__device__ inline void store_step(const VocabArgs& a, const PickLds& P, int v, int s0, int nk, int nx, int ks,
+                                  uint32_t derr, int bonus) {
+  const int lane = threadIdx.x & 63;
+  if (nx < 0 && !derr && bonus < 0) derr |= TAV_DEV_EMPTY_RESIDUAL;
+  // tested: the sampled child first, then the others in order up to the accepted one
+  const bool sampled_taken = ks >= 0 && nx == ks;
+  for (int k = lane; k < nk; k += 64)
+    a.node_status[s0 + P.kid_id[k]] = !sampled_taken && (k == ks || nx < 0 || k < nx) ? 2 : 0;
+  if (lane == 0) a.step[v] = StepRec{nx >= 0 ? P.kid_id[nx] : -1, bonus, derr, 0};
+}
+
 // Everything the walk needs of node v, on one wave (P: the wave's LDS), from the streaming kernel's
 // record and chunk weights.
 template <typename LT>
@@ -581,9 +662,7 @@ __device__ void pick_node(const VocabArgs& a, PickLds& P, int v) {
       if (tk < 0 || tk >= V) err |= TAV_DEV_BAD_TOKEN;
       for (int k2 = 0; k2 < k; ++k2)
         if (P.kid_tok[k2] == tk) err |= TAV_DEV_DUP_SIBLING_TOKEN;
-      const int cid = s0 + P.kid_id[k];
-      a.child_p[cid] = tk == A ? 1.0 : 0.0;
-      a.child_q[cid] = 0.f;
+      P.kid_p[k] = tk == A ? 1.0 : 0.0;
     }
 #pragma unroll
     for (int d = 32; d > 0; d >>= 1) err |= (uint32_t)__shfl_xor((int)err, d);
@@ -597,6 +676,11 @@ __device__ void pick_node(const VocabArgs& a, PickLds& P, int v) {
         atomicOr(a.seq_err + b, err);
       }
     }
+    wave_sync();
+    int ks = -1;
+    uint32_t derr = 0;
+    const int nx = node_step(P, nk, true, 0.0, ks, derr);
+    store_step(a, P, v, s0, nk, nx, ks, derr, M == -INFINITY ? -1 : A);
     return;
   }
   const float M = rec.M;
@@ -681,12 +765,14 @@ __device__ void pick_node(const VocabArgs& a, PickLds& P, int v) {
       for (int k2 = 0; k2 < k; ++k2)
         if (P.kid_tok[k2] == tk) err |= TAV_DEV_DUP_SIBLING_TOKEN;
     }
+    P.kid_u[k] = a.uniforms[(size_t)(s0 + P.kid_id[k]) * 2];
+    P.kid_p[k] = 0.0;
+    P.kid_q[k] = 0.f;
     if (tk >= 0 && tk < V) {
       const float z = logit_at<LT>(a.logits, (size_t)v * V + tk);
       const float qz = !use_draft ? 0.f : sparse ? sp_q(tk) : a.draft[(size_t)dr * V + tk];
-      const int cid = s0 + P.kid_id[k];
-      a.child_p[cid] = exp((double)(z * invT) - (double)M) / S;
-      a.child_q[cid] = use_draft ? qz : 0.f;
+      P.kid_p[k] = exp((double)(z * invT) - (double)M) / S;
+      P.kid_q[k] = use_draft ? qz : 0.f;
       const float p = __builtin_amdgcn_exp2f(z * invTl2 - Ml2) * invS;
       const float kw = use_draft ? fmaxf(0.f, p - qz) : p;
       P.kid_w[k] = kw;
@@ -726,6 +812,11 @@ __device__ void pick_node(const VocabArgs& a, PickLds& P, int v) {
   const double W = __shfl(incl, 63);
   const double target = (double)uf * W;
   int tok = -1;
+  // this node's verification step (Z as the node's statistics report it, in float)
+  const float Zf = use_draft ? (float)Zt : 0.f;
+  int nx = -2, ks = -1;
+  uint32_t derr = 0;
+  auto take_step = [&]() __attribute__((always_inline)) { nx = node_step(P, nk, false, (double)Zf, ks, derr); };
   if (W > 0.0) {
     const unsigned long long hit = __ballot(pm > 0.0 && incl > target);
     const unsigned long long has = __ballot(pm > 0.0);
@@ -775,6 +866,7 @@ __device__ void pick_node(const VocabArgs& a, PickLds& P, int v) {
         qv[4 * i + 0] = t.x; qv[4 * i + 1] = t.y; qv[4 * i + 2] = t.z; qv[4 * i + 3] = t.w;
       }
     }
+    take_step();   // (while the chunk's loads are in flight)
     uint32_t zmask = 0;   // positions of this lane's tokens that are deterministic children
     for (int k = 0; k < nk; ++k) {
       const int d = det_tok(k) - e0;
@@ -820,16 +912,18 @@ __device__ void pick_node(const VocabArgs& a, PickLds& P, int v) {
   // status bits of any lane
 #pragma unroll
   for (int d = 32; d > 0; d >>= 1) err |= (uint32_t)__shfl_xor((int)err, d);
+  if (nx == -2) take_step();   // (no final draw: W = 0)
   if (lane == 0) {
     a.stats[(size_t)v * 3 + 0] = M;
     a.stats[(size_t)v * 3 + 1] = (float)S;
-    a.stats[(size_t)v * 3 + 2] = use_draft ? (float)Zt : 0.f;
+    a.stats[(size_t)v * 3 + 2] = Zf;
     a.term_token[v] = tok;
     if (err) {
       atomicOr(a.status, err);
       atomicOr(a.seq_err + b, err);
     }
   }
+  store_step(a, P, v, s0, nk, nx, ks, derr, tok);
 }
 
 }  // namespace vw
