@@ -149,3 +149,23 @@ def test_greedy_verification(case, seed):
     gu.check_verify(w, got)
     gu.check_node_stats(w, got, range(w.N))
     assert max(int(got["path_len"][b]) for b in range(w.B - 1)) > 1
+
+
+def test_greedy_long_accepted_path():
+    """Greedy chains whose every child carries its parent's argmax: the whole chain is accepted, so
+    the walk follows 1100 steps (more than it stages in LDS, a path longer than it keeps in LDS) and
+    its statuses cover more nodes than each thread holds in registers; a mixed batch with a short
+    stochastic chain beside it."""
+    w = gen.tree_batch(4, B=2, prefix_len=[10, 40], tree="chain", n_nodes=[1100, 30], Hq=4, Hkv=1, D=64,
+                       dtype="bf16", V=256, temperature=1.0)
+    s, e = int(w.node_offsets[0]), int(w.node_offsets[1])
+    for c in range(s + 1, e):
+        w.token[c] = oracle.argmax_token(oracle.verify._logits_f64(w, int(w.parent[c]) + s))
+    w.sampled = w.sampled.copy()
+    w.sampled[s:e] = 0
+    w.temperature = w.temperature.copy()
+    w.temperature[0] = 0.0
+    got = gu.run(w, max_path=1200)
+    assert got["status"] == 0, got["status"]
+    assert int(got["path_len"][0]) == 1100
+    gu.check_verify(w, got)
