@@ -5,10 +5,10 @@ a paged KV cache (block 16, shuffled block table), 64-node random trees of depth
 32 query / 8 KV heads, head_dim 128, bf16, vocabulary 151936, T = 1.0, seed 10086 --
 the batched verification shape.  Inputs are synthetic (seeded).
 
-One step = one whole pass, one tav_tree_attn_verify call: the call's start kernel,
-tree preparation (with the attention work plan, node packing and the verification
-workers' node order), split-KV tree attention and its merge, then the verification's
-vocabulary workers and the walk, all on one stream.  Inputs are resident in HBM; two
+One step = one whole pass, one tav_tree_attn_verify call: the call's start with tree
+preparation (the attention work plan, node packing and the verification workers' node
+order), split-KV tree attention, the verification's vocabulary workers and pick, then the
+walk with the merge of the attention row blocks cut between workgroups, all on one stream.  Inputs are resident in HBM; two
 input copies alternate so consecutive steps do not re-read one step's data from the
 256 MB last-level cache.  The K timed steps carry no events.
 

@@ -56,13 +56,15 @@ union Bf16Pack8 {
 // all copies in flight before each read, so the copies of later tiles never overlap the
 // math).  The copies are ordered explicitly instead: wait_vm on the copy count of each tile,
 // a barrier, and compiler-only memory barriers around both.
-__device__ inline void dma16(const void* gsrc, void* lds_wave_base) {
+// The source is a wave-uniform base (scalar registers) plus a per-lane byte offset, so a tile's
+// copies need no per-lane address arithmetic: only the scalar base changes from tile to tile.
+__device__ inline void dma16(const void* gbase, uint32_t goff, void* lds_wave_base) {
   const uint32_t lds_off = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)lds_wave_base;
   asm volatile(
-      "s_mov_b32 m0, %1\n\t"
+      "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, off"
-      :: "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds_off)) : "memory", "m0");
+      "global_load_lds_dwordx4 %0, %1"
+      :: "v"(goff), "s"(gbase), "s"(__builtin_amdgcn_readfirstlane(lds_off)) : "memory", "m0");
 }
 
 // s_waitcnt on outstanding vector-memory operations only (lgkm / exp counters untouched).
@@ -236,26 +238,31 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
     nref = cursor_block(cur, sb, lbs);
     cursor_advance(cur, pview);
   };
+  // this lane's byte offsets inside a block of the caches (the same for every tile): key rows
+  // 8w..8w+7 of the tile (16-byte chunks permuted by kpos), value rows (w%2)*D/2 .. of sub-block w/2
+  uint32_t k_off[DMA_PER_OPERAND], v_off[DMA_PER_OPERAND];
+#pragma unroll
+  for (int i = 0; i < DMA_PER_OPERAND; ++i) {
+    const int kt = wave * 8 + i * KEYS_PER_DMA + lane / CH;   // key of the tile
+    k_off[i] = (uint32_t)(((kt - sb * 16) * D + kpos<D>(lane % CH, kt) * 8) * 2);
+    v_off[i] = (uint32_t)((((wave & 1) * (D / 2) + i * 32 + l32) * bs + h32 * 8) * 2);
+  }
   auto issue = [&](int j) __attribute__((always_inline)) {
-    int blk = nref.blk;
-    if (!nref.tail && (unsigned)blk >= (unsigned)a.num_blocks) {
-      if (lane == 0) {
-        atomicOr(TAV_COLD(status), (uint32_t)TAV_DEV_BAD_BLOCK);
-        atomicOr(TAV_COLD(seq_err) + nref.seq, (uint32_t)TAV_DEV_BAD_BLOCK);
-      }
-      blk = 0;   // (the sequence's rows become sentinels after the kernel)
+    // (wave-uniform: the block index and both bases stay in scalar registers)
+    const bool bad = !nref.tail && (unsigned)nref.blk >= (unsigned)a.num_blocks;
+    if (bad && lane == 0) {
+      atomicOr(TAV_COLD(status), (uint32_t)TAV_DEV_BAD_BLOCK);
+      atomicOr(TAV_COLD(seq_err) + nref.seq, (uint32_t)TAV_DEV_BAD_BLOCK);
     }
+    const int blk = bad ? 0 : nref.blk;   // (the sequence's rows become sentinels after the kernel)
     const uint16_t* rk = (nref.tail ? ktl : kc) + (((size_t)blk * Hkv + g) * bs + nref.slot0) * D;
     const uint16_t* rv = (nref.tail ? vtl : vc) + ((size_t)blk * Hkv + g) * D * bs + nref.slot0;
     uint8_t* kbase = lds[(unsigned)(j - j_begin) % kStages];
     uint8_t* vbase = kbase + TILE_BYTES + sb * SUB_BYTES;
 #pragma unroll
     for (int i = 0; i < DMA_PER_OPERAND; ++i) {
-      const int kt = wave * 8 + i * KEYS_PER_DMA + lane / CH;   // key of the tile
-      const int k_off = (kt - sb * 16) * D + kpos<D>(lane % CH, kt) * 8;
-      const int v_off = ((wave & 1) * (D / 2) + i * 32 + l32) * bs + h32 * 8;
-      dma16(rk + k_off, kbase + (wave * 8 + i * KEYS_PER_DMA) * (D * 2));
-      dma16(rv + v_off, vbase + (((wave & 1) * (D / 2) + i * 32) >> 5) * 1024);
+      dma16(rk, k_off[i], kbase + (wave * 8 + i * KEYS_PER_DMA) * (D * 2));
+      dma16(rv, v_off[i], vbase + (((wave & 1) * (D / 2) + i * 32) >> 5) * 1024);
     }
   };
 
