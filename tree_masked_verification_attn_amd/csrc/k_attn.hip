@@ -58,8 +58,8 @@ union Bf16Pack8 {
 // a barrier, and compiler-only memory barriers around both.
 // The source is a wave-uniform base (scalar registers) plus a per-lane byte offset, so a tile's
 // copies need no per-lane address arithmetic: only the scalar base changes from tile to tile.
-__device__ inline void dma16(const void* gbase, uint32_t goff, void* lds_wave_base) {
-  const uint32_t lds_off = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)lds_wave_base;
+// lds_off: the wave's destination as an LDS address (wave-uniform).
+__device__ inline void dma16(const void* gbase, uint32_t goff, uint32_t lds_off) {
   asm volatile(
       "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
@@ -247,7 +247,11 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
     k_off[i] = (uint32_t)(((kt - sb * 16) * D + kpos<D>(lane % CH, kt) * 8) * 2);
     v_off[i] = (uint32_t)((((wave & 1) * (D / 2) + i * 32 + l32) * bs + h32 * 8) * 2);
   }
-  auto issue = [&](int j) __attribute__((always_inline)) {
+  // the ring's LDS address (taken once: per-tile destinations are then plain 32-bit sums) and the
+  // slot the next copies go to (slot of tile j = (j - j_begin) % kStages, kept as a running count)
+  const uint32_t lds_addr = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)&lds[0][0];
+  int issue_slot = 0;
+  auto issue = [&]() __attribute__((always_inline)) {   // the next tile, next_issue
     // (wave-uniform: the block index and both bases stay in scalar registers)
     const bool bad = !nref.tail && (unsigned)nref.blk >= (unsigned)a.num_blocks;
     if (bad && lane == 0) {
@@ -257,8 +261,9 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
     const int blk = bad ? 0 : nref.blk;   // (the sequence's rows become sentinels after the kernel)
     const uint16_t* rk = (nref.tail ? ktl : kc) + (((size_t)blk * Hkv + g) * bs + nref.slot0) * D;
     const uint16_t* rv = (nref.tail ? vtl : vc) + ((size_t)blk * Hkv + g) * D * bs + nref.slot0;
-    uint8_t* kbase = lds[(unsigned)(j - j_begin) % kStages];
-    uint8_t* vbase = kbase + TILE_BYTES + sb * SUB_BYTES;
+    const uint32_t kbase = lds_addr + (uint32_t)issue_slot * (2 * TILE_BYTES);
+    const uint32_t vbase = kbase + TILE_BYTES + sb * SUB_BYTES;
+    issue_slot = issue_slot + 1 == kStages ? 0 : issue_slot + 1;
 #pragma unroll
     for (int i = 0; i < DMA_PER_OPERAND; ++i) {
       dma16(rk, k_off[i], kbase + (wave * 8 + i * KEYS_PER_DMA) * (D * 2));
@@ -469,7 +474,7 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
   int next_issue = j_begin;
   resolve();
   for (int k = 0; k < kStages - 2 && next_issue < j_end; ++k) {
-    issue(next_issue);
+    issue();
     ++next_issue;
     if (next_issue < j_end) resolve();
   }
@@ -487,9 +492,9 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
   constexpr int PF = 3;
   constexpr int NPV = 4 * DB;   // P V MFMAs of a tile
   constexpr int NS = 2 * KS;    // score MFMAs of a tile (the two key halves interleaved)
-  auto m_phase = [&](int k) __attribute__((always_inline)) {
+  auto m_phase = [&](int k, int st_prev, int st_k) __attribute__((always_inline)) {
     if (k >= 1) {
-      const int st = (unsigned)(k - 1) % kStages;
+      const int st = st_prev;
       bf16x8_t op[PF];
 #pragma unroll
       for (int f = 0; f < PF; ++f) op[f] = vread(st, f / DB, f % DB);
@@ -511,7 +516,7 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
       }
     }
     if (k < n) {
-      const int st = (unsigned)k % kStages;
+      const int st = st_k;
       bf16x8_t op[PF];
 #pragma unroll
       for (int f = 0; f < PF; ++f) op[f] = kread(st, f & 1, f >> 1);
@@ -534,13 +539,13 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
   // pp.  In the partial last prefix tile the first group also zeroes the values of keys past the
   // prefix (cache slots past it may hold anything, and 0 * NaN would reach the output); nobody
   // reads them before the next barrier.
-  auto v_phase = [&](int k) __attribute__((always_inline)) {
+  auto v_phase = [&](int k, int st_k) __attribute__((always_inline)) {
     const int t = j_begin + k - seg_A;
     const bool masked = needs_mask(t);
     if (masked && t < seg_Tp && tid < 256) {
       // 16-byte units of V^T are [sub-block][32-d group][key half][32 d] of 8 keys each
       const int lim = seg_L - t * kTileKeys;
-      uint8_t* vbase = lds[(unsigned)k % kStages] + TILE_BYTES;
+      uint8_t* vbase = lds[st_k] + TILE_BYTES;
       for (int u = tid; u < 4 * (D / 32) * 2 * 32; u += 256) {
         const int k0 = (u / ((D / 32) * 64)) * 16 + ((u >> 5) & 1) * 8;   // first key of the unit
         if (k0 + 8 <= lim) continue;
@@ -615,7 +620,7 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (next_issue < j_end) {
-      issue(next_issue);
+      issue();
       ++next_issue;
       if (next_issue < j_end) resolve();
     }
@@ -626,23 +631,28 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
     asm volatile("" ::: "memory");
   };
   // (each group as its own straight loop: the phases follow each other in a fixed order)
+  // (st_m: ring slot of tile m, st_p: of tile m - 1, as running counts)
   if (wave < 4) {
-    for (int m = 0; m <= n; ++m) {
+    for (int m = 0, st_m = 0, st_p = kStages - 1; m <= n; ++m) {
       open_pair(m);
       __builtin_amdgcn_s_setprio(1);
-      m_phase(m);
+      m_phase(m, st_p, st_m);
       __builtin_amdgcn_s_setprio(0);
       mid_pair();
-      if (m < n) v_phase(m);
+      if (m < n) v_phase(m, st_m);
+      st_p = st_m;
+      st_m = st_m + 1 == kStages ? 0 : st_m + 1;
     }
   } else {
-    for (int m = 0; m <= n; ++m) {
+    for (int m = 0, st_m = 0, st_p = kStages - 1; m <= n; ++m) {
       open_pair(m);
-      if (m >= 1) v_phase(m - 1);
+      if (m >= 1) v_phase(m - 1, st_p);
       mid_pair();
       __builtin_amdgcn_s_setprio(1);
-      m_phase(m);
+      m_phase(m, st_p, st_m);
       __builtin_amdgcn_s_setprio(0);
+      st_p = st_m;
+      st_m = st_m + 1 == kStages ? 0 : st_m + 1;
     }
   }
 }
