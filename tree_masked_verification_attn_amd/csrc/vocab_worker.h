@@ -169,8 +169,8 @@ __device__ inline float ref_l2(float m_raw, float invT) {
 }
 
 // Sums x[k] over the 64 lanes of the wave for each k (chunk k * waves + wave of the step),
-// through the wave's LDS transpose buffer; returns chunk (lane / (64 / NU))'s total in the first
-// lane of each group of 64 / NU lanes.
+// through the wave's LDS transpose buffer; returns chunk (lane / (64 / NU))'s total in every lane
+// of each group of 64 / NU lanes.
 template <int NU>
 __device__ inline float wave_chunk_totals(const float (&x)[NU], float* part, int lane) {
   constexpr int TPC = 64 / NU;   // lanes per chunk, each summing NU values
@@ -376,7 +376,6 @@ __device__ void stream_node(const VocabArgs& a, Lds<C>& L, int v, int& qn) {
     const float r2 = ref_l2(mx, invT);
     // a NaN or +inf logit makes the sum NaN, which is reported by the pick
     float su[kUnits];
-    double sd = 0.0;
 #pragma unroll
     for (int k = 0; k < kUnits; ++k) {
       su[k] = 0.f;
@@ -384,7 +383,6 @@ __device__ void stream_node(const VocabArgs& a, Lds<C>& L, int v, int& qn) {
 #pragma unroll
         for (int e = 0; e < EPU; ++e) su[k] += __builtin_amdgcn_exp2f(unit_elem<LT>(cur[k], e) * invTl2 - r2);
       }
-      sd += (double)su[k];
     }
     if (dense_draft && s < C::kCacheSteps) {
       // kept for the second pass, which reads them back in the same thread
@@ -394,7 +392,15 @@ __device__ void stream_node(const VocabArgs& a, Lds<C>& L, int v, int& qn) {
     const float ct = wave_chunk_totals(su, part, lane);
     const int c = s * kChunksPerStep + (lane / TPC) * kWaves + wave;
     if ((lane % TPC) == 0 && c < nch) L.cw[c] = ct;
-    sd = wave_sum_d(sd);
+    // the piece's sum in fp64: its chunk totals (each already in all TPC lanes of its group) added
+    // across the groups
+    double sd = (double)ct;
+    if constexpr (TPC <= 1) sd += lane_move_d<1>(sd);
+    if constexpr (TPC <= 2) sd += lane_move_d<2>(sd);
+    if constexpr (TPC <= 4) sd += lane_move_d<3>(sd);
+    if constexpr (TPC <= 8) sd += lane_move_d<4>(sd);
+    if constexpr (TPC <= 16) sd += lane_move_d<5>(sd);
+    if constexpr (TPC <= 32) sd += lane_move_d<6>(sd);
     if (lane == 0) {
       L.ref_m[s * kWaves + wave] = mx;
       L.ref_s[s * kWaves + wave] = sd;
