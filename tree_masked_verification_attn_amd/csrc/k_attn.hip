@@ -538,7 +538,7 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
   // V phase of tile k: masking, one online-softmax update with all 64 keys, probabilities into
   // pp.  In the partial last prefix tile the first group also zeroes the values of keys past the
   // prefix (cache slots past it may hold anything, and 0 * NaN would reach the output); nobody
-  // reads them before the next barrier.
+  // reads them before the next period.
   auto v_phase = [&](int k, int st_k) __attribute__((always_inline)) {
     const int t = j_begin + k - seg_A;
     const bool masked = needs_mask(t);
@@ -598,14 +598,16 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
     l_run += ps;
   };
 
-  // Ping-pong: a wave takes the phases M(0) V(0) M(1) V(1) ... V(n-1) M(n), one per interval
-  // between workgroup barriers, and the second group of waves (4..7; wave w runs on SIMD w % 4)
-  // runs one interval behind the first, so on every SIMD one wave feeds the matrix cores while
-  // the other does the softmax.  Tile m is read in intervals 2m .. 2m+3 (its keys by the two
-  // groups in 2m and 2m+1, its values in 2m+2 and 2m+3): before the barrier that opens interval
-  // 2m every wave waits for its copies of tile m, and after it issues tile m+3 into the slot of
-  // tile m-2, which nobody reads any more.
-  auto open_pair = [&](int m) __attribute__((always_inline)) {   // the barrier opening interval 2m
+  // Ping-pong: a wave takes the phases M(0) V(0) M(1) V(1) ... V(n-1) M(n); period m (between the
+  // workgroup barriers that open tiles m and m+1) holds M(m) then V(m) for the first group of waves
+  // and V(m-1) then M(m) for the second (4..7; wave w runs on SIMD w % 4), so on every SIMD one wave
+  // feeds the matrix cores while the other does the softmax.  Tile m's keys are read in period m and
+  // its values in period m + 1 (in the partial last prefix tile the first group zeroes the values
+  // past the prefix in its V(m), in period m): before the barrier that opens period m every wave
+  // waits for its copies of tile m, and after it issues tile m+3 into the slot of tile m-2, which
+  // nobody reads any more.  One barrier per tile: the two groups' phases are not
+  // otherwise synchronised (a second barrier between the phases kept them in step and cost 1-2 %).
+  auto open_pair = [&](int m) __attribute__((always_inline)) {   // the barrier opening period m
     const int need = j_begin + m;
     asm volatile("" ::: "memory");
     if (need < j_end && need > landed) {
@@ -625,9 +627,7 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
       if (next_issue < j_end) resolve();
     }
   };
-  auto mid_pair = [&]() __attribute__((always_inline)) {   // the barrier opening interval 2m+1
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
+  auto mid_pair = [&]() __attribute__((always_inline)) {   // between the phases: no LDS access moves across
     asm volatile("" ::: "memory");
   };
   // (each group as its own straight loop: the phases follow each other in a fixed order)
