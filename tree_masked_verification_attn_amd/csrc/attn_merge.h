@@ -1,5 +1,5 @@
 // Online-softmax merge of the pieces of attention row blocks cut between workgroups (merge_kernel),
-// and the sentinel rows of sequences whose tree or prefix has a device-detected error.
+// and the sentinel rows of sequences whose tree or prefix has a device-detected error (both paths).
 #pragma once
 
 #include "tav_internal.h"
@@ -141,6 +141,20 @@ __device__ inline void merge_rows(const AttnArgs& a, int D, int log2G, int r, in
     rest(task, c);
     finish(task, c);
   }
+}
+
+// The float32 path's sentinel rows of sequence b (out = 0, lse = -inf) when its tree or prefix has a
+// device-detected error (every sequence when the call's plan disagreed).
+__device__ inline void sentinel_rows_f32(const AttnArgs& a, int D, int b) {
+  const bool all = (a.status[0] & TAV_DEV_PLAN_MISMATCH) != 0;
+  if (!all && !(a.seq_err[b] & kAttnErrBits)) return;
+  const int s0 = a.node_offsets[b], e0 = a.node_offsets[b + 1];
+  const size_t row_elems = (size_t)a.Hq * D;
+  float* out = (float*)a.out;
+  for (size_t i = threadIdx.x; i < (size_t)(e0 - s0) * row_elems; i += blockDim.x)
+    out[(size_t)s0 * row_elems + i] = 0.f;
+  if (a.lse)
+    for (int i = threadIdx.x; i < (e0 - s0) * a.Hq; i += blockDim.x) a.lse[(size_t)s0 * a.Hq + i] = -INFINITY;
 }
 
 }  // namespace tav

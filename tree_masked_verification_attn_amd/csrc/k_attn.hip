@@ -779,16 +779,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
 // float32 path: the rows of a sequence whose tree or prefix has a device-detected error become
 // sentinels (out = 0, lse = -inf); one block per sequence.
 __global__ __launch_bounds__(256) void attn_sentinel_f32_kernel(AttnArgs a, int D) {
-  const int b = blockIdx.x;
-  const bool all = (a.status[0] & TAV_DEV_PLAN_MISMATCH) != 0;
-  if (!all && !(a.seq_err[b] & kAttnErrBits)) return;
-  const int s0 = a.node_offsets[b], e0 = a.node_offsets[b + 1];
-  const size_t row_elems = (size_t)a.Hq * D;
-  float* out = (float*)a.out;
-  for (size_t i = threadIdx.x; i < (size_t)(e0 - s0) * row_elems; i += blockDim.x)
-    out[(size_t)s0 * row_elems + i] = 0.f;
-  if (a.lse)
-    for (int i = threadIdx.x; i < (e0 - s0) * a.Hq; i += blockDim.x) a.lse[(size_t)s0 * a.Hq + i] = -INFINITY;
+  sentinel_rows_f32(a, D, blockIdx.x);
 }
 
 template <int D>

@@ -373,6 +373,23 @@ __global__ __launch_bounds__(kPrepThreads) void start_kernel(uint32_t* status, u
 
 __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) { prep_sequence(a, blockIdx.x); }
 
+// Preparation with the call's start folded in (blocks [0, B): sequence blockIdx.x, each clearing and
+// reporting into its own error word; block B: the status word and the workers' node counter; with
+// an order to build, block B + 1: the verification workers' node order).
+__global__ __launch_bounds__(kPrepThreads) void prep_start_kernel(PrepArgs a, int B, OrderArgs o) {
+  const int bid = blockIdx.x;
+  if (bid < B) {
+    prep_sequence(a, bid);
+  } else if (bid == B) {
+    if (threadIdx.x == 0) {
+      a.status[0] = 0u;
+      a.status[kCounterWord] = 0u;
+    }
+  } else {
+    order_block(o.draft_row, o.R, o.N, o.order);
+  }
+}
+
 // Blocks [0, B): preparation of sequence blockIdx.x; block B: the work plan; with an order to
 // build, the last block: the verification workers' node order; the blocks between: one packed node
 // block (index % tail_blocks) of one KV head (index / tail_blocks).
@@ -421,6 +438,15 @@ hipError_t launch_prep(const Plan& p, const int32_t* node_offsets, const int32_t
                        const tav_tree_out* out, uint32_t* status, uint32_t* seq_err, hipStream_t s) {
   prep_kernel<<<p.B, kPrepThreads, 0, s>>>(
       prep_args(node_offsets, prefix_len, parent, chain_ws, mask_ws, out, status, seq_err));
+  return hipGetLastError();
+}
+
+hipError_t launch_prep_start(const Plan& p, const int32_t* node_offsets, const int32_t* prefix_len,
+                             const int32_t* parent, uint8_t* chain_ws, uint64_t* mask_ws, const tav_tree_out* out,
+                             uint32_t* status, uint32_t* seq_err, const OrderArgs& o, hipStream_t s) {
+  PrepArgs pa = prep_args(node_offsets, prefix_len, parent, chain_ws, mask_ws, out, status, seq_err);
+  pa.fused_start = 1;
+  prep_start_kernel<<<p.B + 1 + (o.order ? 1 : 0), kPrepThreads, 0, s>>>(pa, p.B, o);
   return hipGetLastError();
 }
 

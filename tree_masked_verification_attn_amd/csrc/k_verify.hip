@@ -151,19 +151,24 @@ __device__ void walk_sequence(const WalkArgs& a, int b) {
   }
 }
 
-// Workgroups [0, B) walk the sequences; with nm > 0 the next nm workgroups merge the cut attention
-// row blocks (the work of merge_kernel, 16 rows of one (row block, KV head) each), which run beside
-// the walks instead of in a launch of their own.
-__global__ __launch_bounds__(kWalkThreads) void walk_kernel(WalkArgs w, AttnArgs a, int D, int log2G, int nm) {
+// Workgroups [0, B) walk the sequences; the next nm workgroups merge the cut bf16 attention row blocks
+// (the work of merge_kernel, 16 rows of one (row block, KV head) each) and the next ns write the
+// float32 path's sentinel rows (one sequence each): work that runs beside the walks instead of in a
+// launch of its own.
+__global__ __launch_bounds__(kWalkThreads) void walk_kernel(WalkArgs w, AttnArgs a, int D, int log2G, int nm,
+                                                            int ns) {
   const int blk = blockIdx.x;
   if (blk < w.B) {
     walk_sequence(w, blk);
     return;
   }
   const int m = blk - w.B;
-  if (m >= nm) return;
-  constexpr int kZ = kRowsPerWG / 16;
-  merge_rows<__bf16>(a, D, log2G, m / (kZ * a.Hkv), (m / kZ) % a.Hkv, (m % kZ) * 16, 16);
+  if (m < nm) {
+    constexpr int kZ = kRowsPerWG / 16;
+    merge_rows<__bf16>(a, D, log2G, m / (kZ * a.Hkv), (m / kZ) % a.Hkv, (m % kZ) * 16, 16);
+  } else if (m - nm < ns) {
+    sentinel_rows_f32(a, D, m - nm);
+  }
 }
 
 template <typename LT>
@@ -188,10 +193,12 @@ hipError_t launch_vocab(const VocabArgs& a, bool bf16_logits, int num_cus, hipSt
   return bf16_logits ? launch_vocab_t<uint16_t>(a, num_cus, s) : launch_vocab_t<float>(a, num_cus, s);
 }
 
-hipError_t launch_walk(const WalkArgs& w, const Plan* merge_plan, const AttnArgs* merge, hipStream_t s) {
-  const int nm = merge ? merge_plan->total_rb * merge_plan->Hkv * (kRowsPerWG / 16) : 0;
-  const int D = merge ? merge_plan->D : 0, log2G = merge ? merge_plan->log2G : 0;
-  walk_kernel<<<w.B + nm, kWalkThreads, 0, s>>>(w, merge ? *merge : AttnArgs{}, D, log2G, nm);
+hipError_t launch_walk(const WalkArgs& w, const Plan* plan, const AttnArgs* attn, bool f32_sentinels,
+                       hipStream_t s) {
+  const int nm = attn && !f32_sentinels ? plan->total_rb * plan->Hkv * (kRowsPerWG / 16) : 0;
+  const int ns = attn && f32_sentinels ? plan->B : 0;
+  const int D = attn ? plan->D : 0, log2G = attn ? plan->log2G : 0;
+  walk_kernel<<<w.B + nm + ns, kWalkThreads, 0, s>>>(w, attn ? *attn : AttnArgs{}, D, log2G, nm, ns);
   return hipGetLastError();
 }
 

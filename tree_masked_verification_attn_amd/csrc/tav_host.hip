@@ -330,7 +330,9 @@ tav_status timing_pair(hipEvent_t* start, hipEvent_t* stop) {
 }
 
 // Tree preparation and attention (bf16: preparation, plan and node packing in one launch, then the
-// attention kernel and the merge of split row blocks).
+// attention kernel and the merge of split row blocks; float32: preparation, the attention kernel and
+// the sentinel rows).  fused_start: the call's start is folded into the preparation launch;
+// defer_merge: the merge (bf16) or the sentinel rows (float32) run later, in the walk's launch.
 tav_status enqueue_prep_attention(const tav_problem* p, const Plan& P, const tav_tree* t,
                                   const tav_tree_out* out, const tav_attn_io* io, void* ws, hipStream_t s,
                                   const OrderArgs& order = OrderArgs{nullptr, 0, 0, nullptr},
@@ -348,10 +350,15 @@ tav_status enqueue_prep_attention(const tav_problem* p, const Plan& P, const tav
     if (ev1) TAV_HIP(hipEventRecord(ev1, s));
     if (!defer_merge) TAV_HIP(launch_merge(P, a, true, s));
   } else {
-    const tav_status st = enqueue_prep(p, P, t, out, ws, s);
-    if (st != TAV_OK) return st;
+    if (fused_start) {
+      TAV_HIP(launch_prep_start(P, p->node_offsets, p->prefix_len, t->parent, ws_at<uint8_t>(ws, P.off_chain),
+                                ws_at<uint64_t>(ws, P.off_mask), out, a.status, a.seq_err, order, s));
+    } else {
+      const tav_status st = enqueue_prep(p, P, t, out, ws, s);
+      if (st != TAV_OK) return st;
+    }
     TAV_HIP(launch_attn_f32(P, a, s));
-    TAV_HIP(launch_attn_sentinel_f32(P, a, s));
+    if (!defer_merge) TAV_HIP(launch_attn_sentinel_f32(P, a, s));
   }
   return TAV_OK;
 }
@@ -379,13 +386,13 @@ VocabArgs vocab_args(const tav_problem* p, const Plan& P, const tav_tree* t, con
 }
 
 tav_status enqueue_walk(const Plan& P, const tav_verify_io* io, const VocabArgs& va, hipStream_t s,
-                        const AttnArgs* merge = nullptr) {
+                        const AttnArgs* attn = nullptr, bool f32_sentinels = false) {
   WalkArgs wa;
   wa.node_offsets = va.node_offsets; wa.parent = va.parent; wa.step = va.step;
   wa.node_status = io->node_status; wa.path = io->path; wa.path_len = io->path_len; wa.bonus = io->bonus_token;
   wa.status = va.status; wa.seq_err = va.seq_err;
   wa.B = P.B; wa.max_path = io->max_path;
-  TAV_HIP(launch_walk(wa, &P, merge, s));
+  TAV_HIP(launch_walk(wa, &P, attn, f32_sentinels, s));
   return TAV_OK;
 }
 
@@ -402,7 +409,7 @@ tav_status num_compute_units(int* cus) {
 // wait_before, when given, on s).
 tav_status enqueue_verify(const tav_problem* p, const Plan& P, const tav_tree* t,
                           const tav_verify_io* io, void* ws, hipStream_t s, hipEvent_t wait_before = nullptr,
-                          const AttnArgs* merge = nullptr) {
+                          const AttnArgs* attn = nullptr) {
   const VocabArgs va = vocab_args(p, P, t, io, ws);
   int cus = 0;
   tav_status st = num_compute_units(&cus);
@@ -416,7 +423,7 @@ tav_status enqueue_verify(const tav_problem* p, const Plan& P, const tav_tree* t
   TAV_HIP(launch_vocab(va, p->dtype == TAV_BF16, cus, s));
   if (ev1) TAV_HIP(hipEventRecord(ev1, s));
   if (wait_before) TAV_HIP(hipStreamWaitEvent(s, wait_before, 0));
-  return enqueue_walk(P, io, va, s, merge);
+  return enqueue_walk(P, io, va, s, attn, p->dtype != TAV_BF16);
 }
 
 tav_status enqueue_presto(const Plan& P, const tav_presto_io* io, void* ws, hipStream_t s) {
@@ -503,17 +510,18 @@ tav_status attn_verify_impl(const tav_problem* prob, const tav_tree* tree, const
     if (st != TAV_OK) return st;
   }
   // attn_stream: start, preparation, attention, the verification's kernels, the walk (with the merge
-  // of the cut row blocks in bf16).  The attention kernel and the workers each take whole compute
+  // of the cut row blocks in bf16, the sentinel rows in float32).  The attention kernel and the workers each take whole compute
   // units, so they run one after the other.  PreSTO is independent: on verify_stream (if different)
   // from the start.
-  // the workers' node order: built by an extra block of the bf16 prelude, else by the start kernel
-  const bool order_in_prelude = verify && prob->dtype == TAV_BF16;
+  // the start of the call folded into the preparation launch (one launch fewer) when nothing else
+  // starts before it: with verification (the walk then folds the sequences' error words into the
+  // status word) and no PreSTO batch (which would run beside the preparation on its own stream)
+  const bool fused_start = verify && !presto;
+  // the workers' node order: built by an extra block of the preparation launch (the bf16 prelude, or
+  // the float32 preparation when the start is folded into it), else by the start kernel
+  const bool order_in_prelude = verify && (prob->dtype == TAV_BF16 || fused_start);
   const OrderArgs order{verify ? verify->draft_row : nullptr, verify ? verify->num_draft_rows : 0, P.N,
                         verify ? ws_at<int32_t>(workspace, P.off_order) : nullptr};
-  // the start of the call folded into the prelude (one launch fewer) when nothing else starts before
-  // it: bf16 with verification (the walk then folds the sequences' error words into the status word)
-  // and no PreSTO batch (which would run beside the prelude on its own stream)
-  const bool fused_start = order_in_prelude && !presto;
   if (!fused_start)
     TAV_HIP(launch_start(ws_at<uint32_t>(workspace, P.off_status), ws_at<uint32_t>(workspace, P.off_seq_err), P.B,
                          order_in_prelude ? nullptr : order.draft_row, order.R, P.N, order.order, sa));
@@ -526,8 +534,9 @@ tav_status attn_verify_impl(const tav_problem* prob, const tav_tree* tree, const
     if (st != TAV_OK) return st;
   }
   if (two) TAV_HIP(hipEventRecord(join, sv));
-  // bf16 with verification: the merge of the cut row blocks runs in the walk's launch (beside the walks)
-  const bool defer_merge = verify && prob->dtype == TAV_BF16;
+  // with verification the merge of the cut row blocks (bf16) or the sentinel rows (float32) run in
+  // the walk's launch, beside the walks
+  const bool defer_merge = verify != nullptr;
   st = enqueue_prep_attention(prob, P, tree, tree_out, attn, workspace, sa,
                               order_in_prelude ? order : OrderArgs{nullptr, 0, 0, nullptr}, fused_start,
                               defer_merge);

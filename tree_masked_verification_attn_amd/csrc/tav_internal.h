@@ -259,6 +259,11 @@ struct OrderArgs {
 };
 hipError_t launch_prelude(const Plan& p, const int32_t* parent, const tav_tree_out* out, const AttnArgs& a,
                           const OrderArgs& o, bool fused_start, hipStream_t s);
+// The float32 pass's preparation with the call's start folded in (status word, workers' counter, each
+// sequence's error word; the workers' node order when o.order is set).
+hipError_t launch_prep_start(const Plan& p, const int32_t* node_offsets, const int32_t* prefix_len,
+                             const int32_t* parent, uint8_t* chain_ws, uint64_t* mask_ws, const tav_tree_out* out,
+                             uint32_t* status, uint32_t* seq_err, const OrderArgs& o, hipStream_t s);
 hipError_t launch_attn_bf16(const Plan& p, const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_f32(const Plan& p, const AttnArgs& a, hipStream_t s);
 // Merge of the cut row blocks; also writes the sentinel rows (out = 0, lse = -inf) of every
@@ -268,9 +273,11 @@ hipError_t launch_merge(const Plan& p, const AttnArgs& a, bool bf16_out, hipStre
 hipError_t launch_attn_sentinel_f32(const Plan& p, const AttnArgs& a, hipStream_t s);
 // Vocabulary workers: one 512-thread workgroup per compute unit, persistent over the node queue.
 hipError_t launch_vocab(const VocabArgs& a, bool bf16_logits, int num_cus, hipStream_t s);
-// The walk: one 256-thread workgroup per sequence; with merge != nullptr the same launch also runs the
-// merge of the cut attention row blocks (launch_merge's work) in further workgroups.
-hipError_t launch_walk(const WalkArgs& a, const Plan* merge_plan, const AttnArgs* merge, hipStream_t s);
+// The walk: one 256-thread workgroup per sequence; with attn != nullptr the same launch also runs, in
+// further workgroups, the merge of the cut bf16 attention row blocks (launch_merge's work) or, with
+// f32_sentinels, the float32 path's sentinel rows (launch_attn_sentinel_f32's work).
+hipError_t launch_walk(const WalkArgs& a, const Plan* plan, const AttnArgs* attn, bool f32_sentinels,
+                       hipStream_t s);
 // Draft-tree construction: depth d's pools (one workgroup per (sequence, parent)) and the next
 // parents (one workgroup per sequence); the global prune.
 hipError_t launch_draft_expand(const DraftArgs& a, int d, const uint16_t* logits, const float* uniforms,
