@@ -64,17 +64,8 @@ __device__ inline void merge_rows(const AttnArgs& a, int D, int log2G, int r, in
       }
     }
   }
-  if (a.seq_err[b] & kAttnErrBits) {
-    // the sequence's tree or prefix is unusable: its rows become sentinels (out = 0, lse = -inf)
-    for (int task = threadIdx.x; task < nrows * D; task += blockDim.x) {
-      const int row = row0 + task / D, d = task % D;
-      if ((row >> log2G) >= nodes_here) continue;
-      const size_t orow = (size_t)(s0 + node0 + (row >> log2G)) * a.Hq + g * G + (row & (G - 1));
-      ((OutT*)a.out)[orow * D + d] = (OutT)0.f;
-      if (d == 0 && a.lse) a.lse[orow] = -INFINITY;
-    }
-    return;
-  }
+  // (a sequence whose tree or prefix is unusable gets sentinel rows from sentinel_rows instead)
+  if (a.seq_err[b] & kAttnErrBits) return;
   if (!cut) return;  // one workgroup held the whole row block
   // out = sum_s exp(lse_s - LSE) O_s / sum_s exp(lse_s - LSE), LSE the running maximum of the lse_s
   struct Acc {
@@ -143,18 +134,49 @@ __device__ inline void merge_rows(const AttnArgs& a, int D, int log2G, int r, in
   }
 }
 
-// The float32 path's sentinel rows of sequence b (out = 0, lse = -inf) when its tree or prefix has a
-// device-detected error (every sequence when the call's plan disagreed).
-__device__ inline void sentinel_rows_f32(const AttnArgs& a, int D, int b) {
+// The sentinel rows of sequence b (out = 0, lse = -inf) when its tree or prefix has a device-detected
+// error (every sequence when the call's plan disagreed with the host's).
+template <typename OutT>
+__device__ inline void sentinel_rows(const AttnArgs& a, int D, int b) {
   const bool all = (a.status[0] & TAV_DEV_PLAN_MISMATCH) != 0;
   if (!all && !(a.seq_err[b] & kAttnErrBits)) return;
   const int s0 = a.node_offsets[b], e0 = a.node_offsets[b + 1];
   const size_t row_elems = (size_t)a.Hq * D;
-  float* out = (float*)a.out;
+  OutT* out = (OutT*)a.out;
   for (size_t i = threadIdx.x; i < (size_t)(e0 - s0) * row_elems; i += blockDim.x)
-    out[(size_t)s0 * row_elems + i] = 0.f;
+    out[(size_t)s0 * row_elems + i] = (OutT)0.f;
   if (a.lse)
     for (int i = threadIdx.x; i < (e0 - s0) * a.Hq; i += blockDim.x) a.lse[(size_t)s0 * a.Hq + i] = -INFINITY;
+}
+
+// Merge workgroups: one per (unit, KV head, 16 rows).  A unit is a row block when the launch covers
+// every row block (few row blocks), else a boundary between consecutive workgroup shares (many row
+// blocks: only a row block holding a share boundary strictly inside it was cut, and the first such
+// boundary names it), so the launch's size does not grow with the number of row blocks.
+struct MergeGrid {
+  int units;          // row blocks or share boundaries
+  bool by_boundary;
+};
+__host__ __device__ inline MergeGrid merge_grid(int total_rb, int W) {
+  return total_rb > W - 1 ? MergeGrid{W - 1, true} : MergeGrid{total_rb, false};
+}
+// The row block that unit u merges, or -1.
+__device__ inline int merge_unit_rb(const AttnArgs& a, int u, bool by_boundary) {
+  if (!by_boundary) return u;
+  const int w = u + 1;   // the boundary where workgroup w's share starts
+  const int r = a.wg_rb[w];
+  const int t = a.wg_tile[w];
+  if (r < 0 || r >= a.total_rb || !(t > a.rb_tile[r] && t < a.rb_tile[r + 1])) return -1;
+  return a.wg_tile[w - 1] > a.rb_tile[r] ? -1 : r;   // an earlier boundary inside r names it
+}
+// Merge workgroup i of a launch laid out by merge_grid (rows of 16 per (unit, KV head)).
+template <typename OutT>
+__device__ inline void merge_block(const AttnArgs& a, int D, int log2G, int i, bool by_boundary) {
+  constexpr int kZ = kRowsPerWG / 16;
+  if (a.status[0] & TAV_DEV_PLAN_MISMATCH) return;   // (the plan's arrays are not to be trusted)
+  const int r = merge_unit_rb(a, i / (kZ * a.Hkv), by_boundary);
+  if (r < 0) return;
+  merge_rows<OutT>(a, D, log2G, r, (i / kZ) % a.Hkv, (i % kZ) * 16, 16);
 }
 
 }  // namespace tav

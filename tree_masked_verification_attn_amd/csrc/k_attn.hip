@@ -657,11 +657,13 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
   }
 }
 
-// Online-softmax merge of the split row blocks (attn_merge.h): one block per (row block, KV head,
-// group of 16 rows).
+// Online-softmax merge of the split row blocks (attn_merge.h): nmerge workgroups laid out by
+// merge_grid, then one workgroup per sequence for its sentinel rows.
 template <typename OutT>
-__global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int D, int log2G) {
-  merge_rows<OutT>(a, D, log2G, blockIdx.x, blockIdx.y, blockIdx.z * 16, 16);
+__global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int D, int log2G, int nmerge, int by_boundary) {
+  const int i = blockIdx.x;
+  if (i < nmerge) merge_block<OutT>(a, D, log2G, i, by_boundary != 0);
+  else sentinel_rows<OutT>(a, D, i - nmerge);
 }
 
 __device__ inline float wave_max(float x) {
@@ -779,7 +781,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
 // float32 path: the rows of a sequence whose tree or prefix has a device-detected error become
 // sentinels (out = 0, lse = -inf); one block per sequence.
 __global__ __launch_bounds__(256) void attn_sentinel_f32_kernel(AttnArgs a, int D) {
-  sentinel_rows_f32(a, D, blockIdx.x);
+  sentinel_rows<float>(a, D, blockIdx.x);
 }
 
 template <int D>
@@ -817,9 +819,11 @@ hipError_t launch_attn_f32(const Plan& p, const AttnArgs& a, hipStream_t s) {
 
 hipError_t launch_merge(const Plan& p, const AttnArgs& a, bool bf16_out, hipStream_t s) {
   // (launched also when nothing was cut: it writes the sentinel rows of sequences with errors)
-  dim3 grid(p.total_rb, p.Hkv, kRowsPerWG / 16);
-  if (bf16_out) merge_kernel<__bf16><<<grid, 256, 0, s>>>(a, p.D, p.log2G);
-  else merge_kernel<float><<<grid, 256, 0, s>>>(a, p.D, p.log2G);
+  const MergeGrid mg = merge_grid(p.total_rb, p.W);
+  const int nmerge = mg.units * p.Hkv * (kRowsPerWG / 16);
+  const int grid = nmerge + p.B;
+  if (bf16_out) merge_kernel<__bf16><<<grid, 256, 0, s>>>(a, p.D, p.log2G, nmerge, mg.by_boundary ? 1 : 0);
+  else merge_kernel<float><<<grid, 256, 0, s>>>(a, p.D, p.log2G, nmerge, mg.by_boundary ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -151,12 +151,12 @@ __device__ void walk_sequence(const WalkArgs& a, int b) {
   }
 }
 
-// Workgroups [0, B) walk the sequences; the next nm workgroups merge the cut bf16 attention row blocks
-// (the work of merge_kernel, 16 rows of one (row block, KV head) each) and the next ns write the
-// float32 path's sentinel rows (one sequence each): work that runs beside the walks instead of in a
-// launch of its own.
+// Workgroups [0, B) walk the sequences; the next nm workgroups merge the cut bf16 attention row
+// blocks (merge_kernel's work, laid out by merge_grid) and the next ns write sentinel rows of
+// sequences with attention errors (one sequence each; bf16 or, with f32, float32 outputs): work
+// that runs beside the walks instead of in a launch of its own.
 __global__ __launch_bounds__(kWalkThreads) void walk_kernel(WalkArgs w, AttnArgs a, int D, int log2G, int nm,
-                                                            int ns) {
+                                                            int by_boundary, int ns, int f32) {
   const int blk = blockIdx.x;
   if (blk < w.B) {
     walk_sequence(w, blk);
@@ -164,10 +164,10 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(WalkArgs w, AttnArgs
   }
   const int m = blk - w.B;
   if (m < nm) {
-    constexpr int kZ = kRowsPerWG / 16;
-    merge_rows<__bf16>(a, D, log2G, m / (kZ * a.Hkv), (m / kZ) % a.Hkv, (m % kZ) * 16, 16);
+    merge_block<__bf16>(a, D, log2G, m, by_boundary != 0);
   } else if (m - nm < ns) {
-    sentinel_rows_f32(a, D, m - nm);
+    if (f32) sentinel_rows<float>(a, D, m - nm);
+    else sentinel_rows<__bf16>(a, D, m - nm);
   }
 }
 
@@ -195,10 +195,12 @@ hipError_t launch_vocab(const VocabArgs& a, bool bf16_logits, int num_cus, hipSt
 
 hipError_t launch_walk(const WalkArgs& w, const Plan* plan, const AttnArgs* attn, bool f32_sentinels,
                        hipStream_t s) {
-  const int nm = attn && !f32_sentinels ? plan->total_rb * plan->Hkv * (kRowsPerWG / 16) : 0;
-  const int ns = attn && f32_sentinels ? plan->B : 0;
+  const MergeGrid mg = attn ? merge_grid(plan->total_rb, plan->W) : MergeGrid{0, false};
+  const int nm = attn && !f32_sentinels ? mg.units * plan->Hkv * (kRowsPerWG / 16) : 0;
+  const int ns = attn ? plan->B : 0;
   const int D = attn ? plan->D : 0, log2G = attn ? plan->log2G : 0;
-  walk_kernel<<<w.B + nm + ns, kWalkThreads, 0, s>>>(w, attn ? *attn : AttnArgs{}, D, log2G, nm, ns);
+  walk_kernel<<<w.B + nm + ns, kWalkThreads, 0, s>>>(w, attn ? *attn : AttnArgs{}, D, log2G, nm,
+                                                    mg.by_boundary ? 1 : 0, ns, f32_sentinels ? 1 : 0);
   return hipGetLastError();
 }
 
