@@ -69,10 +69,10 @@ def check_tree_prep(w, got):
             np.testing.assert_array_equal(got["mask"][v], want, err_msg=f"mask of node {v}")
 
 
-def check_attention(w, got, nodes=None, tol=None):
+def check_attention(w, got, nodes=None, tol=None, prep=None):
     if tol is None:
         tol = 2e-2 if w.dtype == "bf16" else 1e-5
-    ref_out, ref_lse = oracle.tree_attention(w, nodes)
+    ref_out, ref_lse = oracle.tree_attention(w, nodes, prep)
     idx = list(range(w.N)) if nodes is None else list(nodes)
     o = got["out"][idx]
     l = got["lse"][idx]

@@ -153,6 +153,57 @@ def test_attention_kernel_timing_events():
     assert n == 3 and ms > 0.0
 
 
+BLOCK_CASES = {
+    # name: (block_size, dtype, D, Hkv): caches of 32 and 64 rows per block in bf16 (the packed node
+    # blocks then take two heads, or one, per LDS round) and of 8 rows in fp32
+    "bf16_bs32_d128": (32, "bf16", 128, 8),
+    "bf16_bs64_d64": (64, "bf16", 64, 3),
+    "bf16_bs64_d128": (64, "bf16", 128, 2),
+    "f32_bs8_d64": (8, "f32", 64, 2),
+}
+
+
+@pytest.mark.parametrize("case", sorted(BLOCK_CASES))
+def test_block_sizes(case):
+    """Prefix copies, packed node blocks and their tiles at block sizes other than 16, with ragged
+    prefixes and trees (a tree of one node, trees ending inside and on a block boundary)."""
+    bs, dtype, D, Hkv = BLOCK_CASES[case]
+    _say("block size case", case)
+    w = gen.tree_batch(11, B=4, prefix_len=[0, 100, 777, 64], tree="random", n_nodes=[70, 1, 130, 64],
+                       Hq=4 * Hkv, Hkv=Hkv, D=D, dtype=dtype, V=2048, temperature=1.0, block_size=bs)
+    got = gu.run(w)
+    assert got["status"] == 0, got["status"]
+    gu.check_tree_prep(w, got)
+    gu.check_attention(w, got)
+    gu.check_verify(w, got)
+    gu.check_node_stats(w, got, range(w.N))
+
+
+@pytest.mark.parametrize("bs,n", [(32, [12000, 13000]), (64, [9000, 8000])])
+def test_long_chains_packed_heads(bs, n):
+    """Long chains at 32 and 64 rows per block: with thousands of (node block, KV head) pairs each
+    packing block takes several heads (4 and 2 here), in two LDS rounds; sampled rows at the
+    sequences' ends, block edges and middles."""
+    _say("long chains, block size", bs)
+    w = gen.tree_batch(4, B=2, prefix_len=[100, 37], tree="chain", n_nodes=n, Hq=32, Hkv=8, D=128,
+                       dtype="bf16", V=256, temperature=1.0, block_size=bs)
+    got = gu.run(w, max_path=max(n) + 1)
+    assert got["status"] == 0, got["status"]
+    picks = []
+    for b in range(2):
+        s, e = int(w.node_offsets[b]), int(w.node_offsets[b + 1])
+        picks += [s, s + bs - 1, s + bs, (s + e) // 2, e - bs - 1, e - 1]
+    # a chain's visibility sets by their definition (node i of a chain sees nodes 0..i), so that
+    # the oracle does not list the sets of every node of the long chains
+    anc = [None] * w.N
+    for b in range(2):
+        s = int(w.node_offsets[b])
+        for v in picks[6 * b:6 * b + 6]:
+            anc[v] = list(range(v - s + 1))
+    gu.check_attention(w, got, sorted(set(picks)), prep={"anc": anc})
+    gu.check_verify(w, got)
+
+
 @pytest.mark.parametrize("B", [300, 2100])
 def test_many_sequences(B):
     """More sequences than one block-wide scan of the preparation covers (300), and more than the

@@ -12,11 +12,32 @@
 // per-sequence error words) is folded into the same launch.
 #include "tav_internal.h"
 
+#include <algorithm>
+
 namespace tav {
 namespace {
 
 constexpr int kPrepThreads = 256;
 constexpr int kPlanLds = 2048;   // sequences / row blocks whose plan arrays are staged in LDS
+
+// The LDS of each job.  A launch that runs several jobs in different blocks overlays them (one union),
+// so that it holds only the largest and more of its blocks fit on a compute unit.
+struct PrepLds {
+  int par[kMaxTreeNodes];
+};
+struct PlanLds {
+  int scan[16];
+  int off[kPlanLds], tile[kPlanLds], wt[kPlanLds];
+};
+template <int D>
+struct PackLds {
+  alignas(16) uint16_t vs[64][D + 8];   // values of up to 64 / block_size heads, [head, slot][d]
+  int scan[16];
+  int seq, base;
+};
+struct OrderLds {
+  int scan[16];
+};
 
 
 // Exclusive scan of one int per thread over the block; also returns the total.
@@ -66,8 +87,8 @@ struct PrepArgs {
 // ancestor masks of a non-chain tree.  With fused_start the block first clears seq_err[b] (no start
 // kernel ran) and reports its errors there only: another block of the same launch clears the status
 // word, and the call's last kernel folds the sequences' error words into it.
-__device__ void prep_sequence(const PrepArgs& a, int b) {
-  __shared__ int par_s[kMaxTreeNodes];
+__device__ void prep_sequence(const PrepArgs& a, int b, PrepLds& S) {
+  int* par_s = S.par;
   const int s0 = a.node_offsets[b];
   const int n = a.node_offsets[b + 1] - s0;
   const int L = a.prefix_len[b];
@@ -142,9 +163,11 @@ struct PlanArgs {
 // packed node block of each sequence), each workgroup's share wg_tile / wg_rb, and the record
 // of each row block, identical to the host plan; a disagreement with the host's totals sets
 // TAV_DEV_PLAN_MISMATCH.  The row-block offsets and tiles are staged in LDS when they fit.
-__device__ void plan_block(const PlanArgs& p, const AttnArgs& a) {
-  __shared__ int scan_s[16];
-  __shared__ int off_s[kPlanLds], tile_s[kPlanLds], wt_s[kPlanLds];
+__device__ void plan_block(const PlanArgs& p, const AttnArgs& a, PlanLds& S) {
+  int* scan_s = S.scan;
+  int* off_s = S.off;
+  int* tile_s = S.tile;
+  int* wt_s = S.wt;
   const int B = p.B, NB = p.NB, bs = p.bs, C = p.C, W = p.W;
   const int32_t* node_offsets = a.node_offsets;
   const int32_t* prefix_len = a.prefix_len;
@@ -279,72 +302,93 @@ __device__ void plan_block(const PlanArgs& p, const AttnArgs& a) {
 }
 
 // Copies the keys and values of block_size consecutive tree nodes of one sequence (packed node
-// block tb, KV head g) into the paged cache's layout (keys [block, head, slot, d], values
+// block tb, KV heads [ga, gb)) into the paged cache's layout (keys [block, head, slot, d], values
 // [block, head, d, slot]), zero-padded past the sequence's last node, so tree-tail tiles take the
-// same copy path as prefix tiles.  The sequence of block tb is found from the node counts.
+// same copy path as prefix tiles.  The block's node rows ([node, head, d]) are one range of memory
+// and so is each destination; keys keep their 16-byte pieces, values are transposed through LDS,
+// 64 / block_size heads at a time.  The sequence of block tb is found from the node counts.  Runs on
+// kPrepThreads threads.
 template <int D>
-__device__ void pack_block(const AttnArgs& a, int tb, int g) {
-  constexpr int CH = D / 8;
-  __shared__ uint16_t vs[64][D + 8];   // values of the block, [slot][d]
-  __shared__ int scan_s[16];
-  __shared__ int seq_s, base_s;
+__device__ void pack_block(const AttnArgs& a, int tb, int ga, int gb, PackLds<D>& S) {
+  constexpr int CH = D / 8;     // 16-byte pieces of a row
   const int bs = a.block_size, Hkv = a.Hkv, B = a.B;
   // sequence b with tail offset off(b) <= tb < off(b) + ceil(n_b / bs)
-  if (threadIdx.x == 0) seq_s = -1;
+  if (threadIdx.x == 0) S.seq = -1;
   int carry = 0;
   for (int base = 0; base < B; base += blockDim.x) {
     const int b = base + threadIdx.x;
     const int nblk = b < B ? (a.node_offsets[b + 1] - a.node_offsets[b] + bs - 1) / bs : 0;
     int tot;
-    const int ex = block_exclusive_scan(nblk, scan_s, &tot);   // (its barriers order seq_s)
+    const int ex = block_exclusive_scan(nblk, S.scan, &tot);   // (its barriers order S.seq)
     if (b < B && tb >= carry + ex && tb < carry + ex + nblk) {
-      seq_s = b;
-      base_s = carry + ex;
+      S.seq = b;
+      S.base = carry + ex;
     }
     carry += tot;
     __syncthreads();
-    if (seq_s >= 0) break;
+    if (S.seq >= 0) break;
   }
-  const int b = seq_s;
+  const int b = S.seq;
   if (b < 0) return;   // tb past the last block (not launched)
   const int s0 = a.node_offsets[b];
   const int n = a.node_offsets[b + 1] - s0;
-  const int node_base = (tb - base_s) * bs;
+  const int node_base = (tb - S.base) * bs;
   const uint16_t* kn = (const uint16_t*)a.k_node;
   const uint16_t* vn = (const uint16_t*)a.v_node;
-  uint16_t* kt = (uint16_t*)a.k_tail;
-  uint16_t* vt = (uint16_t*)a.v_tail;
-  for (int c = threadIdx.x; c < bs * CH; c += blockDim.x) {
-    const int slot = c / CH, ch = c % CH;
+  // the piece c = (head, slot, piece of the row) of the block, zero past the last node
+  auto piece = [&](const uint16_t* src, int g0, int c) {
+    const int g = g0 + c / (bs * CH), slot = (c / CH) % bs, ch = c % CH;
     const int node = node_base + slot;
-    uint4 kv = make_uint4(0u, 0u, 0u, 0u), vv = kv;
-    if (node < n) {
-      const size_t off = ((size_t)(s0 + node) * Hkv + g) * D + ch * 8;
-      kv = *(const uint4*)(kn + off);
-      vv = *(const uint4*)(vn + off);
+    return node < n ? *(const uint4*)(src + ((size_t)(s0 + node) * Hkv + g) * D + ch * 8)
+                    : make_uint4(0u, 0u, 0u, 0u);
+  };
+  // rounds of hg heads: their key and value pieces loaded together, the keys stored as they are
+  // (piece c of the round's heads lands at piece c of their destination), the values staged in LDS
+  // as [head, slot][d] and written d-major
+  constexpr int kPer = 64 * CH / kPrepThreads;   // pieces per thread and round, of keys and of values
+  static_assert(kPer * kPrepThreads == 64 * CH, "packing round shape");
+  uint16_t* vt = (uint16_t*)a.v_tail;
+  const int hg = 64 / bs, groups = bs / 8;
+  for (int g0 = ga; g0 < gb; g0 += hg) {
+    const int ng = min(hg, gb - g0);
+    const int np = ng * bs * CH;
+    uint4 kr[kPer], vr[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = threadIdx.x + i * kPrepThreads;
+      if (c < np) {
+        kr[i] = piece(kn, g0, c);
+        vr[i] = piece(vn, g0, c);
+      }
     }
-    *(uint4*)(kt + (((size_t)tb * Hkv + g) * bs + slot) * D + ch * 8) = kv;
-    const uint32_t w4[4] = {vv.x, vv.y, vv.z, vv.w};
+    uint4* kt = (uint4*)a.k_tail + ((size_t)tb * Hkv + g0) * bs * CH;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) vs[slot][ch * 8 + e] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
-  }
-  __syncthreads();
-  const int groups = bs / 8;
-  for (int c = threadIdx.x; c < D * groups; c += blockDim.x) {
-    const int d = c / groups, sg = c % groups;
-    uint32_t w4[4];
+    for (int i = 0; i < kPer; ++i) {
+      const int c = threadIdx.x + i * kPrepThreads;
+      if (c < np) {
+        kt[c] = kr[i];
+        *(uint4*)&S.vs[c / CH][(c % CH) * 8] = vr[i];
+      }
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < ng * D * groups; c += kPrepThreads) {
+      const int gi = c / (D * groups), d = (c / groups) % D, sg = c % groups;
+      const int row = gi * bs + sg * 8;
+      uint32_t w4[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      w4[e] = (uint32_t)vs[sg * 8 + 2 * e][d] | ((uint32_t)vs[sg * 8 + 2 * e + 1][d] << 16);
-    *(uint4*)(vt + (((size_t)tb * Hkv + g) * D + d) * bs + sg * 8) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+      for (int e = 0; e < 4; ++e)
+        w4[e] = (uint32_t)S.vs[row + 2 * e][d] | ((uint32_t)S.vs[row + 2 * e + 1][d] << 16);
+      *(uint4*)(vt + (((size_t)tb * Hkv + g0 + gi) * D + d) * bs + sg * 8) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+    }
+    __syncthreads();
   }
 }
 
 // The order in which the verification's workers take the nodes: nodes with a draft row (which
 // stream their draft row too, three times the bytes of the others) first, in node order, then the
 // others, so that the long items do not come last.
-__device__ void order_block(const int32_t* draft_row, int R, int N, int32_t* order) {
-  __shared__ int scan_s[16];
+__device__ void order_block(const int32_t* draft_row, int R, int N, int32_t* order, OrderLds& S) {
+  int* scan_s = S.scan;
   int hcarry = 0;
   for (int base = 0; base < N; base += blockDim.x) {
     const int v = base + threadIdx.x;
@@ -362,50 +406,65 @@ __device__ void order_block(const int32_t* draft_row, int R, int N, int32_t* ord
 __global__ __launch_bounds__(kPrepThreads) void start_kernel(uint32_t* status, uint32_t* seq_err, int B,
                                                              const int32_t* draft_row, int R, int N,
                                                              int32_t* order) {
+  __shared__ OrderLds lds;
   if (threadIdx.x == 0) {
     status[0] = 0u;
     status[kCounterWord] = 0u;
   }
   if (seq_err)
     for (int b = threadIdx.x; b < B; b += blockDim.x) seq_err[b] = 0u;
-  if (draft_row) order_block(draft_row, R, N, order);
+  if (draft_row) order_block(draft_row, R, N, order, lds);
 }
 
-__global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) { prep_sequence(a, blockIdx.x); }
+__global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) {
+  __shared__ PrepLds lds;
+  prep_sequence(a, blockIdx.x, lds);
+}
 
 // Preparation with the call's start folded in (blocks [0, B): sequence blockIdx.x, each clearing and
 // reporting into its own error word; block B: the status word and the workers' node counter; with
 // an order to build, block B + 1: the verification workers' node order).
 __global__ __launch_bounds__(kPrepThreads) void prep_start_kernel(PrepArgs a, int B, OrderArgs o) {
+  __shared__ union {
+    PrepLds prep;
+    OrderLds order;
+  } lds;
   const int bid = blockIdx.x;
   if (bid < B) {
-    prep_sequence(a, bid);
+    prep_sequence(a, bid, lds.prep);
   } else if (bid == B) {
     if (threadIdx.x == 0) {
       a.status[0] = 0u;
       a.status[kCounterWord] = 0u;
     }
   } else {
-    order_block(o.draft_row, o.R, o.N, o.order);
+    order_block(o.draft_row, o.R, o.N, o.order, lds.order);
   }
 }
 
 // Blocks [0, B): preparation of sequence blockIdx.x; block B: the work plan; with an order to
-// build, the last block: the verification workers' node order; the blocks between: one packed node
-// block (index % tail_blocks) of one KV head (index / tail_blocks).
+// build, the last block: the verification workers' node order; the blocks between: hp KV heads of
+// one packed node block each.  The jobs' LDS is overlaid.
 template <int D>
-__global__ __launch_bounds__(kPrepThreads) void prelude_kernel(PrepArgs pa, PlanArgs pl, AttnArgs a,
-                                                               int tail_blocks, OrderArgs o) {
+__global__ __launch_bounds__(kPrepThreads) void prelude_kernel(PrepArgs pa, PlanArgs pl, AttnArgs a, OrderArgs o,
+                                                               int hp) {
+  __shared__ union {
+    PrepLds prep;
+    PlanLds plan;
+    PackLds<D> pack;
+    OrderLds order;
+  } lds;
   const int bid = blockIdx.x;
   if (bid < pl.B) {
-    prep_sequence(pa, bid);
+    prep_sequence(pa, bid, lds.prep);
   } else if (bid == pl.B) {
-    plan_block(pl, a);
+    plan_block(pl, a, lds.plan);
   } else if (o.order && bid == (int)gridDim.x - 1) {
-    order_block(o.draft_row, o.R, o.N, o.order);
+    order_block(o.draft_row, o.R, o.N, o.order, lds.order);
   } else {
-    const int i = bid - pl.B - 1;
-    pack_block<D>(a, i % tail_blocks, i / tail_blocks);
+    const int i = bid - pl.B - 1, nhg = (a.Hkv + hp - 1) / hp;
+    const int ga = (i % nhg) * hp;
+    pack_block<D>(a, i / nhg, ga, min(a.Hkv, ga + hp), lds.pack);
   }
 }
 
@@ -459,10 +518,14 @@ hipError_t launch_prelude(const Plan& p, const int32_t* parent, const tav_tree_o
   pl.fused_start = fused_start ? 1 : 0;
   pl.B = p.B; pl.NB = p.NB; pl.bs = p.bs; pl.total_rb_host = p.total_rb; pl.tiles_host = p.tiles_per_head;
   pl.tail_blocks_host = p.tail_blocks; pl.C = p.C; pl.W = p.W;
-  const int grid = p.B + 1 + p.tail_blocks * p.Hkv + (o.order ? 1 : 0);
-  const int tb = p.tail_blocks > 0 ? p.tail_blocks : 1;
-  if (p.D == 128) prelude_kernel<128><<<grid, kPrepThreads, 0, s>>>(pa, pl, a, tb, o);
-  else prelude_kernel<64><<<grid, kPrepThreads, 0, s>>>(pa, pl, a, tb, o);
+  // KV heads per packing block: one while (node block, head) pairs are few, more when they would be
+  // tens of thousands of small blocks
+  constexpr int64_t kPackBlocks = 2048;
+  const int64_t pairs = (int64_t)p.tail_blocks * p.Hkv;
+  const int hp = (int)std::min<int64_t>(p.Hkv, std::max<int64_t>(1, (pairs + kPackBlocks - 1) / kPackBlocks));
+  const int grid = p.B + 1 + p.tail_blocks * ((p.Hkv + hp - 1) / hp) + (o.order ? 1 : 0);
+  if (p.D == 128) prelude_kernel<128><<<grid, kPrepThreads, 0, s>>>(pa, pl, a, o, hp);
+  else prelude_kernel<64><<<grid, kPrepThreads, 0, s>>>(pa, pl, a, o, hp);
   return hipGetLastError();
 }
 
