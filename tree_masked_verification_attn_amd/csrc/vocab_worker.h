@@ -33,6 +33,8 @@
 // next node while it streams the current one.
 #pragma once
 
+#include <type_traits>
+
 #include "tav_internal.h"
 
 namespace tav {
@@ -429,17 +431,28 @@ __device__ void stream_node(const VocabArgs& a, Lds<C>& L, int v, int& qn) {
   double Zt = 0.0;
   if (dense_draft) {
     // ---- pass 2: chunk weights of (p - q~)+ and their total Z.  Each step is taken in two
-    // halves of kUnits / 2 units per thread, one half computed while the other's loads fly.
+    // halves of kUnits / 2 units per thread, one half computed while the other's loads fly.  The
+    // steps in reverse (the last steps of pass 1 are the likeliest still to be in the cache): first
+    // those read from memory, then those in the LDS cache, in two loops, so that every load has
+    // one known address space (a load through a pointer chosen between LDS and memory is a flat
+    // load, which makes every use wait for all loads in flight).
     constexpr int HU = kUnits / 2;
     const float* drow = a.draft + (size_t)dr * V;
-    auto load_half = [&](uint4 (&r)[HU], float4 (&q)[HU][QPU], int s, int h) __attribute__((always_inline)) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const __attribute__((address_space(3))) u32x4* lc3 = (const __attribute__((address_space(3))) u32x4*)&L.lc[0];
+    const __attribute__((address_space(1))) u32x4* row1 = (const __attribute__((address_space(1))) u32x4*)row;
+    auto load_half = [&](uint4 (&r)[HU], float4 (&q)[HU][QPU], int s, int h, auto cached)
+        __attribute__((always_inline)) {
 #pragma unroll
       for (int k = 0; k < HU; ++k) {
         const int u = s * kStepUnits + (h * HU + k) * kThreads + tid;
-        const size_t e0 = (size_t)(u < nunits ? u : 0) * EPU;
-        r[k] = s < C::kCacheSteps ? L.lc[u] : *(const uint4*)(row + e0);
+        const int uc = u < nunits ? u : 0;
+        u32x4 x;
+        if constexpr (decltype(cached)::value) x = lc3[u];
+        else x = row1[uc];
+        r[k] = make_uint4(x[0], x[1], x[2], x[3]);
 #pragma unroll
-        for (int i = 0; i < QPU; ++i) q[k][i] = *(const float4*)(drow + e0 + 4 * i);
+        for (int i = 0; i < QPU; ++i) q[k][i] = *(const float4*)(drow + (size_t)uc * EPU + 4 * i);
       }
     };
     float wu[kUnits];
@@ -460,21 +473,39 @@ __device__ void stream_node(const VocabArgs& a, Lds<C>& L, int v, int& qn) {
         wu[h * HU + k] = w;
       }
     };
-    // the steps in reverse: the last steps of pass 1 are the likeliest still to be in the cache
-    uint4 ra[HU], rb[HU];
-    float4 qa[HU][QPU], qb[HU][QPU];
-    load_half(ra, qa, nsteps - 1, 0);
     double zl = 0.0;
-    for (int s = nsteps - 1; s >= 0; --s) {
-      load_half(rb, qb, s, 1);
-      compute_half(ra, qa, s, 0);
-      if (s > 0) load_half(ra, qa, s - 1, 0);
-      compute_half(rb, qb, s, 1);
+    auto finish = [&](int s) __attribute__((always_inline)) {
 #pragma unroll
       for (int k = 0; k < kUnits; ++k) zl += (double)wu[k];
       const float ct = wave_chunk_totals(wu, part, lane);
       const int c = s * kChunksPerStep + (lane / TPC) * kWaves + wave;
       if ((lane % TPC) == 0 && c < nch) L.cw[c] = ct;
+    };
+    constexpr std::true_type kFromLds{};
+    constexpr std::false_type kFromMemory{};
+    const int sc = nsteps < C::kCacheSteps ? nsteps : C::kCacheSteps;   // steps [0, sc) are in the cache
+    uint4 ra[HU], rb[HU];
+    float4 qa[HU][QPU], qb[HU][QPU];
+    int s = nsteps - 1;
+    if (s >= sc) {
+      load_half(ra, qa, s, 0, kFromMemory);
+      for (; s >= sc; --s) {
+        load_half(rb, qb, s, 1, kFromMemory);
+        compute_half(ra, qa, s, 0);
+        if (s - 1 >= sc) load_half(ra, qa, s - 1, 0, kFromMemory);
+        else if (s > 0) load_half(ra, qa, s - 1, 0, kFromLds);
+        compute_half(rb, qb, s, 1);
+        finish(s);
+      }
+    } else {
+      load_half(ra, qa, s, 0, kFromLds);
+    }
+    for (; s >= 0; --s) {
+      load_half(rb, qb, s, 1, kFromLds);
+      compute_half(ra, qa, s, 0);
+      if (s > 0) load_half(ra, qa, s - 1, 0, kFromLds);
+      compute_half(rb, qb, s, 1);
+      finish(s);
     }
     zl = wave_sum_d(zl);
     if (lane == 0) L.red_d[wave] = zl;
