@@ -162,8 +162,12 @@ struct PlanArgs {
 // rb_tile[total_rb+1] (first key tile of each row block, per KV head), tail_blk[B+1] (first
 // packed node block of each sequence), each workgroup's share wg_tile / wg_rb, and the record
 // of each row block, identical to the host plan; a disagreement with the host's totals sets
-// TAV_DEV_PLAN_MISMATCH.  The row-block offsets and tiles are staged in LDS when they fit.
-__device__ void plan_block(const PlanArgs& p, const AttnArgs& a, PlanLds& S) {
+// TAV_DEV_PLAN_MISMATCH.  The row-block offsets and tiles are staged in LDS when they fit (SMALL), and
+// so are the workgroups' first tiles (SMALL_W); the choice is made at compile time, so that every
+// access has one address space (an access through a pointer to either is a flat access, which waits
+// for all memory operations in flight).
+template <bool SMALL, bool SMALL_W>
+__device__ void plan_block_t(const PlanArgs& p, const AttnArgs& a, PlanLds& S) {
   int* scan_s = S.scan;
   int* off_s = S.off;
   int* tile_s = S.tile;
@@ -182,9 +186,8 @@ __device__ void plan_block(const PlanArgs& p, const AttnArgs& a, PlanLds& S) {
     a.status[0] = 0u;
     a.status[kCounterWord] = 0u;
   }
-  const bool small = B + 1 <= kPlanLds && p.total_rb_host + 1 <= kPlanLds;
-  int* off = small ? off_s : seq_rb_off;   // working copies (LDS or the outputs themselves)
-  int* tile = small ? tile_s : rb_tile;
+  int* off = SMALL ? off_s : seq_rb_off;   // working copies (LDS or the outputs themselves)
+  int* tile = SMALL ? tile_s : rb_tile;
   int carry = 0, bcarry = 0;
   for (int base = 0; base < B; base += blockDim.x) {
     const int b = base + threadIdx.x;
@@ -240,7 +243,7 @@ __device__ void plan_block(const PlanArgs& p, const AttnArgs& a, PlanLds& S) {
   }
   if (tcarry != p.tiles_host) return;
   __syncthreads();
-  if (small) {
+  if constexpr (SMALL) {
     for (int b = threadIdx.x; b <= B; b += blockDim.x) seq_rb_off[b] = off[b];
     for (int r = threadIdx.x; r <= total_rb; r += blockDim.x) rb_tile[r] = tile[r];
   }
@@ -256,7 +259,7 @@ __device__ void plan_block(const PlanArgs& p, const AttnArgs& a, PlanLds& S) {
     // a share starting inside a row block's fixed-cost gap starts at the next row block
     const int j = w == W ? tcarry : min(tile[lo] + (x - tile[lo] - kRbCost * lo), tile[lo + 1]);
     wg_tile[w] = j;
-    if (W + 1 <= kPlanLds) wt_s[w] = j;
+    if constexpr (SMALL_W) wt_s[w] = j;
     if (w < W) {
       int r = lo;   // the row block holding tile j (an empty share keeps any valid index)
       if (j >= tile[lo + 1] && lo + 1 < total_rb) r = lo + 1;
@@ -267,7 +270,7 @@ __device__ void plan_block(const PlanArgs& p, const AttnArgs& a, PlanLds& S) {
   // kernel itself from the preparation's output), with the workgroups holding its first and last
   // tiles for the merge: the largest w with wg_tile[w] <= tile (never an empty share)
   __syncthreads();
-  const int* wt = W + 1 <= kPlanLds ? wt_s : wg_tile;
+  const int* wt = SMALL_W ? wt_s : wg_tile;
   auto owner = [&](int t) {
     int lo = 0, hi = W;
     while (hi - lo > 1) {
@@ -298,6 +301,18 @@ __device__ void plan_block(const PlanArgs& p, const AttnArgs& a, PlanLds& S) {
     m[kMetaSeq] = b;
     m[kMetaWf] = owner(tile[r]);
     m[kMetaWl] = owner(tile[r + 1] - 1);
+  }
+}
+
+__device__ void plan_block(const PlanArgs& p, const AttnArgs& a, PlanLds& S) {
+  const bool small = p.B + 1 <= kPlanLds && p.total_rb_host + 1 <= kPlanLds;
+  const bool small_w = p.W + 1 <= kPlanLds;
+  if (small) {
+    if (small_w) plan_block_t<true, true>(p, a, S);
+    else plan_block_t<true, false>(p, a, S);
+  } else {
+    if (small_w) plan_block_t<false, true>(p, a, S);
+    else plan_block_t<false, false>(p, a, S);
   }
 }
 

@@ -95,19 +95,25 @@ __device__ void walk_sequence(const WalkArgs& a, int b) {
   if (tid == 0 && !res[0]) {
     int v = 0, plen = 1, bonus = -1;
     uint32_t err = 0;
-    path[0] = 0;
     path_s[0] = 0;
-    for (int it = 0; it < n; ++it) {
-      const StepRec r = v < kWalkLds ? st_s[v] : a.step[s0 + v];
-      if (r.err) { err = r.err; break; }
-      if (r.next < 0) { bonus = r.bonus; break; }
-      if (r.next <= v || r.next >= n) { err = TAV_DEV_BAD_PARENT; break; }   // (children follow parents)
-      if (plen >= a.max_path) { err = TAV_DEV_PATH_OVERFLOW; break; }
-      path[plen] = r.next;
+    // one step of the chase; false when the path ends.  The steps of nodes below kWalkLds come from
+    // LDS, the others from memory, in two loops (ids ascend along the path), so that each load has
+    // one address space; path entries past kPathLds go straight to memory, the others are written
+    // out by the whole workgroup after the chase.
+    auto follow = [&](const StepRec& r) -> bool {
+      if (r.err) { err = r.err; return false; }
+      if (r.next < 0) { bonus = r.bonus; return false; }
+      if (r.next <= v || r.next >= n) { err = TAV_DEV_BAD_PARENT; return false; }   // (children follow parents)
+      if (plen >= a.max_path) { err = TAV_DEV_PATH_OVERFLOW; return false; }
       if (plen < kPathLds) path_s[plen] = r.next;
+      else path[plen] = r.next;
       ++plen;
       v = r.next;
-    }
+      return true;
+    };
+    bool more = true;
+    while (more && v < kWalkLds && v < n) more = follow(st_s[v]);
+    while (more && v < n) more = follow(a.step[s0 + v]);
     if (err) atomicOr(a.status, err);
     res[0] = err != 0u;
     res[1] = plen;
@@ -124,15 +130,25 @@ __device__ void walk_sequence(const WalkArgs& a, int b) {
     return;
   }
   const int plen = res[1];
-  // node x is on the path iff it is one of its (ascending) entries
+  const int nl = plen < kPathLds ? plen : kPathLds;   // path entries in LDS
+  for (int j = tid; j < nl; j += kWalkThreads) path[j] = path_s[j];
+  // node x is on the path iff it is one of its (ascending) entries: the first kPathLds in LDS, the
+  // rest in memory (written by thread 0 before the barrier above)
   auto on_path = [&](int x) -> bool {
-    int lo = 0, hi = plen;
+    if (x <= path_s[nl - 1]) {
+      int lo = 0, hi = nl;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (path_s[mid] < x) lo = mid + 1; else hi = mid;
+      }
+      return path_s[lo] == x;
+    }
+    int lo = nl, hi = plen;
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
-      const int e = mid < kPathLds ? path_s[mid] : path[mid];
-      if (e < x) lo = mid + 1; else hi = mid;
+      if (path[mid] < x) lo = mid + 1; else hi = mid;
     }
-    return lo < plen && (lo < kPathLds ? path_s[lo] : path[lo]) == x;
+    return lo < plen && path[lo] == x;
   };
   auto status_of = [&](int j, int pr, uint8_t mk) -> uint8_t {
     return on_path(j) ? 1 : (j > 0 && mk == 2 && on_path(pr)) ? 2 : 0;
