@@ -113,7 +113,7 @@ struct NodeRec {
   uint32_t err;  // errors found while streaming (TAV_DEV_* bits)
   int flags;     // kRec* bits
   int s0, n;     // the sequence's first node and node count
-  int pad;
+  float T;       // the sequence's temperature
 };
 constexpr int kRecResidual = 1;   // the chunk weights are those of (p - q~)+
 constexpr int kRecNoMass = 2;     // no finite logit

@@ -41,6 +41,7 @@ namespace tav {
 namespace vw {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kCwBatch = 8;   // chunk weights per lane loaded together by the pick
 
 // A worker of NT threads reading NU sixteen-byte units per thread and step.  A chunk is 64 units,
 // one per lane of a wave, so chunk k * waves + w of a step is unit k of every lane of wave w.
@@ -163,6 +164,59 @@ __device__ inline float wave_max_f(float x) {
 __device__ inline void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
+}
+
+// Prefix sums over the 64 lanes of a wave without LDS round trips: inside each row of 16 lanes by
+// DPP row shifts (a lane whose source lies outside its row adds 0), then the rows' totals read with
+// readlane and added to the later rows.  A fixed order of additions (the same on every run).  Every
+// lane of the wave must be active.
+template <int CTRL>
+__device__ inline uint32_t dpp0(uint32_t x) { return __builtin_amdgcn_update_dpp(0u, x, CTRL, 0xF, 0xF, false); }
+constexpr int kDppRowShr = 0x110;    // row_shr:n = kDppRowShr + n
+constexpr int kDppWaveShr1 = 0x138;  // wave_shr:1 (lane i takes lane i - 1, lane 0 takes 0)
+template <int CTRL>
+__device__ inline double dpp0_d(double x) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(x);
+  const uint32_t lo = dpp0<CTRL>((uint32_t)b), hi = dpp0<CTRL>((uint32_t)(b >> 32));
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+__device__ inline double readlane_d(double x, int l) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(x);
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)b, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+__device__ inline float readlane_f(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+__device__ inline double wave_scan_d(double x) {   // inclusive
+  x += dpp0_d<kDppRowShr + 1>(x);
+  x += dpp0_d<kDppRowShr + 2>(x);
+  x += dpp0_d<kDppRowShr + 4>(x);
+  x += dpp0_d<kDppRowShr + 8>(x);
+  const double t0 = readlane_d(x, 15), t1 = readlane_d(x, 31), t2 = readlane_d(x, 47);
+  const double t01 = t0 + t1;
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row == 0 ? 0.0 : row == 1 ? t0 : row == 2 ? t01 : t01 + t2);
+}
+__device__ inline float wave_scan_f(float x) {   // inclusive
+  x += __uint_as_float(dpp0<kDppRowShr + 1>(__float_as_uint(x)));
+  x += __uint_as_float(dpp0<kDppRowShr + 2>(__float_as_uint(x)));
+  x += __uint_as_float(dpp0<kDppRowShr + 4>(__float_as_uint(x)));
+  x += __uint_as_float(dpp0<kDppRowShr + 8>(__float_as_uint(x)));
+  const float t0 = readlane_f(x, 15), t1 = readlane_f(x, 31), t2 = readlane_f(x, 47);
+  const float t01 = t0 + t1;
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row == 0 ? 0.f : row == 1 ? t0 : row == 2 ? t01 : t01 + t2);
+}
+__device__ inline uint32_t wave_or(uint32_t x) {
+  x |= lane_move<1>(x);
+  x |= lane_move<2>(x);
+  x |= lane_move<3>(x);
+  x |= lane_move<4>(x);
+  x |= lane_move<5>(x);
+  x |= lane_move<6>(x);
+  return x;
 }
 
 // log2-domain reference of a piece maximum (a piece of -inf logits uses 0; its sum is 0).
@@ -305,7 +359,7 @@ __device__ void greedy_stream(const VocabArgs& a, Lds<C>& L, int v, int b, int s
     r.flags = kRecGreedy;
     r.s0 = s0;
     r.n = n;
-    r.pad = 0;
+    r.T = 0.f;   // (greedy rows: temperature 0)
     a.rec[v] = r;
   }
 }
@@ -533,7 +587,7 @@ __device__ void stream_node(const VocabArgs& a, Lds<C>& L, int v, int& qn) {
     r.flags = (dense_draft ? kRecResidual : 0) | (no_mass ? kRecNoMass : 0);
     r.s0 = s0;
     r.n = n;
-    r.pad = 0;
+    r.T = Tb;
     a.rec[v] = r;
   }
 }
@@ -605,19 +659,13 @@ __device__ inline int node_step(const PickLds& P, int nk, bool greedy, double Zv
     const bool tested = k < nk && k != ks;
     const double p = tested ? P.kid_p[k] : 0.0;
     const double r0 = !tested ? 0.0 : resid ? fmax(0.0, p - (double)P.kid_q[k]) * invZ : p;
-    double incl = r0;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const double y = __shfl_up(incl, d, 64);
-      if (lane >= d) incl += y;
-    }
-    double before = __shfl_up(incl, 1, 64);
-    if (lane == 0) before = 0.0;
+    const double incl = wave_scan_d(r0);
+    const double before = dpp0_d<kDppWaveShr1>(incl);
     const double rem = 1.0 - (carry + before);
     const double uc = tested ? (double)P.kid_u[k] : 0.0;
     const unsigned long long m = __ballot(tested && (rem > 0.0 ? uc * rem <= r0 : uc <= 0.0));
     if (m) return base + __ffsll((long long)m) - 1;
-    carry += __shfl(incl, 63);
+    carry += readlane_d(incl, 63);
   }
   return -1;
 }
@@ -644,47 +692,79 @@ __device__ void pick_node(const VocabArgs& a, PickLds& P, int v) {
   constexpr int CT = 64 * EPU;   // tokens per chunk
   const int lane = threadIdx.x & 63;
   const int V = a.V, nch = a.nch;
-  // every load that does not depend on another goes out first: the record, the draft row index,
-  // the uniform, this lane's chunk weights, then the children's fields
+  // Round one of loads: everything that depends on v alone -- the record, the draft row index, the
+  // final draw's uniform, the chunk weights, the node's own parent and a window of the kWin * 64
+  // nodes after v (parent, token, sampled flag, acceptance uniform), among which its children lie
+  // when its sequence ends inside the window (children come after their parent).
+  constexpr int kWin = 2;
   const NodeRec rec = a.rec[v];
   const int dr = a.draft_row[v];
   const float uf = a.uniforms[(size_t)v * 2 + 1];
+  const int own_parent = a.parent[v];
+  int w_par[kWin], w_tok[kWin];
+  uint8_t w_smp[kWin];
+  float w_u[kWin];
+#pragma unroll
+  for (int i = 0; i < kWin; ++i) {
+    const int c = v + 1 + 64 * i + lane;
+    const int cc = c < a.N ? c : v;
+    w_par[i] = a.parent[cc];
+    w_tok[i] = a.token[cc];
+    w_smp[i] = a.sampled[cc];
+    w_u[i] = a.uniforms[(size_t)cc * 2];
+  }
+  float cwr[kCwBatch];   // this lane's chunk weights c = lane + 64 j (rows of up to 64 * kCwBatch chunks)
+  const bool stoch = !(rec.flags & kRecGreedy);
+  const float* cwi = a.cw + (size_t)v * nch;
+#pragma unroll
+  for (int j = 0; j < kCwBatch; ++j) {
+    const int c = lane + 64 * j;
+    cwr[j] = stoch && c < nch ? cwi[c] : 0.f;
+  }
   const int b = rec.b, s0 = rec.s0, n = rec.n;
-  const float Tb = a.temperature[b];
+  const int lv = v - s0;   // v's id in its sequence
+  const float Tb = rec.T;
   const float invT = 1.f / Tb;
   const float invTl2 = invT * kLog2e;
   const bool dr_ok = dr >= 0 && dr < a.R;
   uint32_t err = rec.err;
-  if (!(rec.flags & kRecGreedy)) {
-    const float* cwi = a.cw + (size_t)v * nch;
-    for (int c = lane; c < nch; c += 64) P.cw[c] = cwi[c];
+  // every node checks its own parent (a bad one reaches the sequence's error word from that node)
+  if (lv == 0 ? own_parent != -1 : (own_parent < 0 || own_parent >= lv)) err |= TAV_DEV_BAD_PARENT;
+  if (stoch) {
+#pragma unroll
+    for (int j = 0; j < kCwBatch; ++j)
+      if (lane + 64 * j < nch) P.cw[lane + 64 * j] = cwr[j];
+    for (int c = lane + 64 * kCwBatch; c < nch; c += 64) P.cw[c] = cwi[c];   // (longer rows)
   }
   // children of v in ascending id (a compaction with fixed order, so that everything computed from
-  // the list is the same on every run), the parent-array and temperature checks
+  // the list is the same on every run): from the window, then from the rest of the sequence
   int nk = 0, ns = 0;
-  for (int base = 0; base < n; base += 64) {
-    const int c = base + lane;
-    bool kid = false, smp = false;
-    int tk = 0;
-    if (c < n) {
-      const int pc = a.parent[s0 + c];
-      const uint8_t sm = a.sampled[s0 + c];
-      tk = a.token[s0 + c];
-      if (c == 0 ? pc != -1 : (pc < 0 || pc >= c)) err |= TAV_DEV_BAD_PARENT;
-      kid = c > 0 && pc == v - s0;
-      smp = kid && sm != 0;
-    }
+  auto take = [&](int c, bool in_seq, int pc, int tk, uint8_t sm, float u) __attribute__((always_inline)) {
+    const bool kid = in_seq && pc == lv;
+    const bool smp = kid && sm != 0;
     const unsigned long long m = __ballot(kid);
     if (kid) {
       const int k = nk + __popcll(m & ((1ull << lane) - 1ull));
       if (k < kMaxChildren) {
-        P.kid_id[k] = c;
+        P.kid_id[k] = c - s0;
         P.kid_tok[k] = tk;
         P.kid_smp[k] = smp;
+        P.kid_u[k] = u;
       }
     }
     nk += __popcll(m);
     ns += __popcll(__ballot(smp));
+  };
+#pragma unroll
+  for (int i = 0; i < kWin; ++i) {
+    const int c = v + 1 + 64 * i + lane;
+    take(c, c < s0 + n, w_par[i], w_tok[i], w_smp[i], w_u[i]);
+  }
+  for (int base = v + 1 + 64 * kWin; base < s0 + n; base += 64) {
+    const int c = base + lane;
+    const bool in_seq = c < s0 + n;
+    const int cc = in_seq ? c : v;
+    take(c, in_seq, a.parent[cc], a.token[cc], a.sampled[cc], a.uniforms[(size_t)cc * 2]);
   }
   if (!(Tb >= 0.f && Tb < INFINITY)) err |= TAV_DEV_BAD_TEMPERATURE;
   if (nk > kMaxChildren) err |= TAV_DEV_TOO_MANY_CHILDREN;
@@ -701,8 +781,7 @@ __device__ void pick_node(const VocabArgs& a, PickLds& P, int v) {
         if (P.kid_tok[k2] == tk) err |= TAV_DEV_DUP_SIBLING_TOKEN;
       P.kid_p[k] = tk == A ? 1.0 : 0.0;
     }
-#pragma unroll
-    for (int d = 32; d > 0; d >>= 1) err |= (uint32_t)__shfl_xor((int)err, d);
+    err = wave_or(err);
     if (lane == 0) {
       a.stats[(size_t)v * 3 + 0] = M;
       a.stats[(size_t)v * 3 + 1] = 1.f;
@@ -802,7 +881,6 @@ __device__ void pick_node(const VocabArgs& a, PickLds& P, int v) {
       for (int k2 = 0; k2 < k; ++k2)
         if (P.kid_tok[k2] == tk) err |= TAV_DEV_DUP_SIBLING_TOKEN;
     }
-    P.kid_u[k] = a.uniforms[(size_t)(s0 + P.kid_id[k]) * 2];
     P.kid_p[k] = 0.0;
     P.kid_q[k] = 0.f;
     if (tk >= 0 && tk < V) {
@@ -840,13 +918,8 @@ __device__ void pick_node(const VocabArgs& a, PickLds& P, int v) {
     const int c = lane * per + k;
     if (c < nch) pm += (double)fmaxf(P.cw[c], 0.f);
   }
-  double incl = pm;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const double y = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += y;
-  }
-  const double W = __shfl(incl, 63);
+  const double incl = wave_scan_d(pm);
+  const double W = readlane_d(incl, 63);
   const double target = (double)uf * W;
   int tok = -1;
   // this node's verification step (Z as the node's statistics report it, in float)
@@ -876,8 +949,8 @@ __device__ void pick_node(const VocabArgs& a, PickLds& P, int v) {
       if (pc < 0) { pc = cl; cum = cum_l; }   // rounding past the total: last chunk with mass
       rem = target - cum;
     }
-    pc = __shfl(pc, owner);
-    rem = __shfl(rem, owner);
+    pc = __builtin_amdgcn_readlane(pc, owner);
+    rem = readlane_d(rem, owner);
     // the final draw inside the chosen chunk
     const int e0 = pc * CT + lane * EPU;
     const bool in = e0 < V;
@@ -922,12 +995,7 @@ __device__ void pick_node(const VocabArgs& a, PickLds& P, int v) {
       w[e] = x;
       lsum += x;
     }
-    float inc = lsum;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const float y = __shfl_up(inc, d, 64);
-      if (lane >= d) inc += y;
-    }
+    const float inc = wave_scan_f(lsum);
     const float remf = (float)rem;
     const unsigned long long hit2 = __ballot(inc > remf && lsum > 0.f);
     const unsigned long long has2 = __ballot(lsum > 0.f);
@@ -944,11 +1012,10 @@ __device__ void pick_node(const VocabArgs& a, PickLds& P, int v) {
       }
       if (mine < 0) mine = lastpos;
     }
-    tok = chosen >= 0 ? __shfl(mine, chosen) : -1;
+    tok = chosen >= 0 ? __builtin_amdgcn_readlane(mine, chosen) : -1;
   }
   // status bits of any lane
-#pragma unroll
-  for (int d = 32; d > 0; d >>= 1) err |= (uint32_t)__shfl_xor((int)err, d);
+  err = wave_or(err);
   if (nx == -2) take_step();   // (no final draw: W = 0)
   if (lane == 0) {
     a.stats[(size_t)v * 3 + 0] = M;
