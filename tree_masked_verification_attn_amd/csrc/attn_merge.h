@@ -10,7 +10,7 @@ namespace tav {
 // nrows); the pieces O_s are normalised by their own sums and stored in bf16, lse_s in float.  Row
 // block r's key tiles [A, E) were cut into the pieces of workgroups A/C .. (E-1)/C; the first piece
 // sits in slot 2w+1 of its workgroup (its last segment), the others in slot 2w (their workgroup's
-// first segment).  A thread owns 4 outputs at a time.
+// first segment).  A thread owns 8 outputs at a time (16-byte loads and stores).
 template <typename OutT>
 __device__ inline void merge_rows(const AttnArgs& a, int D, int log2G, int r, int g, int row0, int nrows) {
   // the row block's record from the plan (one round of loads beside the status word)
@@ -22,11 +22,11 @@ __device__ inline void merge_rows(const AttnArgs& a, int D, int log2G, int r, in
   const int NB = kRowsPerWG >> log2G;
   const int G = 1 << log2G;
   const int nodes_here = min(NB, n - node0);
-  const int DQ = D / 4;
-  const int ntask = nrows * DQ;   // a task: four outputs of one row
+  const int DQ = D / 8;
+  const int ntask = nrows * DQ;   // a task: eight outputs of one row
   const bool cut = wf != wl;
-  constexpr int kT = 2;      // tasks per thread taken with their loads in flight together (16 rows x
-                             // D / 4 at D <= 128 on 256 threads); further tasks go one by one
+  constexpr int kT = 1;      // tasks per thread taken with their loads in flight together (16 rows x
+                             // D / 8 at D <= 128 on 256 threads); further tasks go one by one
   constexpr int kPre = 6;    // pieces loaded together (a batch), folded in by an online softmax
   auto task_row = [&](int task) { return row0 + task / DQ; };
   auto task_ok = [&](int task) { return task < ntask && (task_row(task) >> log2G) < nodes_here; };
@@ -34,23 +34,23 @@ __device__ inline void merge_rows(const AttnArgs& a, int D, int log2G, int r, in
     const int slot = w == wf ? 2 * w + 1 : 2 * w;
     return ((size_t)slot * a.Hkv + g) * kRowsPerWG + row;
   };
-  auto load_batch = [&](int task, int w0, float (&ls)[kPre], uint2 (&ob)[kPre]) {
+  auto load_batch = [&](int task, int w0, float (&ls)[kPre], uint4 (&ob)[kPre]) {
     const int row = task_row(task), dq = task % DQ;
 #pragma unroll
     for (int q = 0; q < kPre; ++q) {
       ls[q] = -INFINITY;
-      ob[q] = make_uint2(0u, 0u);
+      ob[q] = make_uint4(0u, 0u, 0u, 0u);
       if (w0 + q <= wl) {
         const size_t base = base_of(w0 + q, row);
         ls[q] = a.part_lse[base];
-        ob[q] = *(const uint2*)(a.part_o + base * D + dq * 4);   // 4 bf16
+        ob[q] = *(const uint4*)(a.part_o + base * D + dq * 8);   // 8 bf16
       }
     }
   };
   // second round: the first batch of this thread's first kT tasks, issued with the sequence's error
   // word (the pieces' slots are valid whatever the sequence's state; they are used only without errors)
   float ls0[kT][kPre];
-  uint2 ob0[kT][kPre];
+  uint4 ob0[kT][kPre];
 #pragma unroll
   for (int i = 0; i < kT; ++i) {
     const int task = threadIdx.x + i * blockDim.x;
@@ -60,7 +60,7 @@ __device__ inline void merge_rows(const AttnArgs& a, int D, int log2G, int r, in
 #pragma unroll
       for (int q = 0; q < kPre; ++q) {
         ls0[i][q] = -INFINITY;
-        ob0[i][q] = make_uint2(0u, 0u);
+        ob0[i][q] = make_uint4(0u, 0u, 0u, 0u);
       }
     }
   }
@@ -70,16 +70,17 @@ __device__ inline void merge_rows(const AttnArgs& a, int D, int log2G, int r, in
   // out = sum_s exp(lse_s - LSE) O_s / sum_s exp(lse_s - LSE), LSE the running maximum of the lse_s
   struct Acc {
     float M = -INFINITY, den = 0.f;
-    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   };
-  auto fold = [](Acc& c, const float (&ls)[kPre], const uint2 (&ob)[kPre]) {
+  auto fold = [](Acc& c, const float (&ls)[kPre], const uint4 (&ob)[kPre]) {
     float mb = c.M;
 #pragma unroll
     for (int q = 0; q < kPre; ++q) mb = fmaxf(mb, ls[q]);
     if (mb > c.M) {
       const float sc = c.M == -INFINITY ? 0.f : __expf(c.M - mb);
       c.den *= sc;
-      c.o.x *= sc; c.o.y *= sc; c.o.z *= sc; c.o.w *= sc;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) c.o[e] *= sc;
       c.M = mb;
     }
 #pragma unroll
@@ -87,10 +88,12 @@ __device__ inline void merge_rows(const AttnArgs& a, int D, int log2G, int r, in
       if (ls[q] == -INFINITY) continue;
       const float wgt = __expf(ls[q] - c.M);
       c.den += wgt;
-      c.o.x += wgt * __uint_as_float(ob[q].x << 16);
-      c.o.y += wgt * __uint_as_float(ob[q].x & 0xFFFF0000u);
-      c.o.z += wgt * __uint_as_float(ob[q].y << 16);
-      c.o.w += wgt * __uint_as_float(ob[q].y & 0xFFFF0000u);
+      const uint32_t w4[4] = {ob[q].x, ob[q].y, ob[q].z, ob[q].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        c.o[2 * e] += wgt * __uint_as_float(w4[e] << 16);
+        c.o[2 * e + 1] += wgt * __uint_as_float(w4[e] & 0xFFFF0000u);
+      }
     }
   };
   auto finish = [&](int task, const Acc& c) {
@@ -98,17 +101,23 @@ __device__ inline void merge_rows(const AttnArgs& a, int D, int log2G, int r, in
     const int node = s0 + node0 + (row >> log2G);
     const int head = g * G + (row & (G - 1));
     const float inv = c.den > 0.f ? 1.f / c.den : 0.f;
-    OutT* op = (OutT*)a.out + ((size_t)node * a.Hq + head) * D + dq * 4;
-    op[0] = (OutT)(c.o.x * inv);
-    op[1] = (OutT)(c.o.y * inv);
-    op[2] = (OutT)(c.o.z * inv);
-    op[3] = (OutT)(c.o.w * inv);
+    OutT* op = (OutT*)a.out + ((size_t)node * a.Hq + head) * D + dq * 8;
+    if constexpr (sizeof(OutT) == 2) {
+      union { OutT e[8]; uint4 u; } w;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w.e[e] = (OutT)(c.o[e] * inv);
+      *(uint4*)op = w.u;
+    } else {
+      float4* o4 = (float4*)op;
+      o4[0] = make_float4(c.o[0] * inv, c.o[1] * inv, c.o[2] * inv, c.o[3] * inv);
+      o4[1] = make_float4(c.o[4] * inv, c.o[5] * inv, c.o[6] * inv, c.o[7] * inv);
+    }
     if (dq == 0 && a.lse) a.lse[(size_t)node * a.Hq + head] = c.den > 0.f ? c.M + __logf(c.den) : -INFINITY;
   };
   auto rest = [&](int task, Acc& c) {   // the batches after the first
     for (int w0 = wf + kPre; w0 <= wl; w0 += kPre) {
       float ls[kPre];
-      uint2 ob[kPre];
+      uint4 ob[kPre];
       load_batch(task, w0, ls, ob);
       fold(c, ls, ob);
     }
@@ -125,7 +134,7 @@ __device__ inline void merge_rows(const AttnArgs& a, int D, int log2G, int r, in
   for (int task = threadIdx.x + kT * blockDim.x; task < ntask; task += blockDim.x) {
     if (!task_ok(task)) continue;
     float ls[kPre];
-    uint2 ob[kPre];
+    uint4 ob[kPre];
     load_batch(task, wf, ls, ob);
     Acc c;
     fold(c, ls, ob);
