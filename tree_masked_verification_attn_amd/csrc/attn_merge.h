@@ -2,9 +2,15 @@
 // and the sentinel rows of sequences whose tree or prefix has a device-detected error (both paths).
 #pragma once
 
+#ifndef TAV_MERGE_ROWS
+#define TAV_MERGE_ROWS 16
+#endif
+
 #include "tav_internal.h"
 
 namespace tav {
+
+constexpr int kMergeRows = TAV_MERGE_ROWS;   // rows of one merge workgroup (256 threads)
 
 // out = sum_s exp(lse_s - LSE) O_s over the pieces of row block r, KV head g, rows [row0, row0 +
 // nrows); the pieces O_s are normalised by their own sums and stored in bf16, lse_s in float.  Row
@@ -25,8 +31,9 @@ __device__ inline void merge_rows(const AttnArgs& a, int D, int log2G, int r, in
   const int DQ = D / 8;
   const int ntask = nrows * DQ;   // a task: eight outputs of one row
   const bool cut = wf != wl;
-  constexpr int kT = 1;      // tasks per thread taken with their loads in flight together (16 rows x
-                             // D / 8 at D <= 128 on 256 threads); further tasks go one by one
+  constexpr int kT = kMergeRows / 16;   // tasks per thread taken with their loads in flight together
+                                        // (kMergeRows rows x D / 8 at D <= 128 on 256 threads); further
+                                        // tasks go one by one
   constexpr int kPre = 6;    // pieces loaded together (a batch), folded in by an online softmax
   auto task_row = [&](int task) { return row0 + task / DQ; };
   auto task_ok = [&](int task) { return task < ntask && (task_row(task) >> log2G) < nodes_here; };
@@ -158,7 +165,7 @@ __device__ inline void sentinel_rows(const AttnArgs& a, int D, int b) {
     for (int i = threadIdx.x; i < (e0 - s0) * a.Hq; i += blockDim.x) a.lse[(size_t)s0 * a.Hq + i] = -INFINITY;
 }
 
-// Merge workgroups: one per (unit, KV head, 16 rows).  A unit is a row block when the launch covers
+// Merge workgroups: one per (unit, KV head, kMergeRows rows).  A unit is a row block when the launch covers
 // every row block (few row blocks), else a boundary between consecutive workgroup shares (many row
 // blocks: only a row block holding a share boundary strictly inside it was cut, and the first such
 // boundary names it), so the launch's size does not grow with the number of row blocks.
@@ -181,11 +188,11 @@ __device__ inline int merge_unit_rb(const AttnArgs& a, int u, bool by_boundary) 
 // Merge workgroup i of a launch laid out by merge_grid (rows of 16 per (unit, KV head)).
 template <typename OutT>
 __device__ inline void merge_block(const AttnArgs& a, int D, int log2G, int i, bool by_boundary) {
-  constexpr int kZ = kRowsPerWG / 16;
+  constexpr int kZ = kRowsPerWG / kMergeRows;
   if (a.status[0] & TAV_DEV_PLAN_MISMATCH) return;   // (the plan's arrays are not to be trusted)
   const int r = merge_unit_rb(a, i / (kZ * a.Hkv), by_boundary);
   if (r < 0) return;
-  merge_rows<OutT>(a, D, log2G, r, (i / kZ) % a.Hkv, (i % kZ) * 16, 16);
+  merge_rows<OutT>(a, D, log2G, r, (i / kZ) % a.Hkv, (i % kZ) * kMergeRows, kMergeRows);
 }
 
 }  // namespace tav

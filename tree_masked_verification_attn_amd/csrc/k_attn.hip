@@ -820,7 +820,7 @@ hipError_t launch_attn_f32(const Plan& p, const AttnArgs& a, hipStream_t s) {
 hipError_t launch_merge(const Plan& p, const AttnArgs& a, bool bf16_out, hipStream_t s) {
   // (launched also when nothing was cut: it writes the sentinel rows of sequences with errors)
   const MergeGrid mg = merge_grid(p.total_rb, p.W);
-  const int nmerge = mg.units * p.Hkv * (kRowsPerWG / 16);
+  const int nmerge = mg.units * p.Hkv * (kRowsPerWG / kMergeRows);
   const int grid = nmerge + p.B;
   if (bf16_out) merge_kernel<__bf16><<<grid, 256, 0, s>>>(a, p.D, p.log2G, nmerge, mg.by_boundary ? 1 : 0);
   else merge_kernel<float><<<grid, 256, 0, s>>>(a, p.D, p.log2G, nmerge, mg.by_boundary ? 1 : 0);

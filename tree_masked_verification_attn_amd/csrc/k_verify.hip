@@ -212,7 +212,7 @@ hipError_t launch_vocab(const VocabArgs& a, bool bf16_logits, int num_cus, hipSt
 hipError_t launch_walk(const WalkArgs& w, const Plan* plan, const AttnArgs* attn, bool f32_sentinels,
                        hipStream_t s) {
   const MergeGrid mg = attn ? merge_grid(plan->total_rb, plan->W) : MergeGrid{0, false};
-  const int nm = attn && !f32_sentinels ? mg.units * plan->Hkv * (kRowsPerWG / 16) : 0;
+  const int nm = attn && !f32_sentinels ? mg.units * plan->Hkv * (kRowsPerWG / kMergeRows) : 0;
   const int ns = attn ? plan->B : 0;
   const int D = attn ? plan->D : 0, log2G = attn ? plan->log2G : 0;
   walk_kernel<<<w.B + nm + ns, kWalkThreads, 0, s>>>(w, attn ? *attn : AttnArgs{}, D, log2G, nm,
