@@ -87,6 +87,7 @@ struct PickLds {
   int sp_idx[kMaxDraftSupport];              // sparse draft row: support (ascending ids), q~ there
   float sp_val[kMaxDraftSupport];            // and the part of each token's p taken out of its
   float sp_take[kMaxDraftSupport];           // chunk (min(p, q~))
+  uint32_t zm[64];                           // final draw: each lane's positions holding a deterministic child
 };
 
 template <typename LT>
@@ -903,12 +904,28 @@ __device__ void pick_node(const VocabArgs& a, PickLds& P, int v) {
     const int tk = P.kid_tok[k];
     return !P.kid_smp[k] && tk >= 0 && tk < V ? tk : -1;
   };
-  // the deterministic children's weights taken out of their chunks, one lane, in child order (a
-  // fixed order of the float subtractions: two runs give the same chunk weights bit for bit)
-  for (int k = 0; k < nk; ++k) {
-    const int tk = det_tok(k);
-    const float kw = k < 64 ? __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(kw_r), k)) : P.kid_w[k];
-    if (lane == 0 && tk >= 0) P.cw[tk / CT] -= kw;
+  // the deterministic children's weights taken out of their chunks in a fixed order (two runs give the
+  // same chunk weights bit for bit): with up to 64 children the last child of each chunk sums the
+  // weights of that chunk's children in child order and takes the sum out (one lane per chunk, all
+  // chunks at once); more children go one at a time on one lane
+  if (nk <= 64) {
+    const int myc = lane < nk && det_r >= 0 ? det_r / CT : -1;
+    bool last = myc >= 0;
+    float sum = 0.f;
+    for (int k = 0; k < nk; ++k) {
+      const int tk = __builtin_amdgcn_readlane(det_r, k);
+      const float wk = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(kw_r), k));
+      const bool same = tk >= 0 && tk / CT == myc;
+      if (same && k <= lane) sum += wk;
+      if (same && k > lane) last = false;
+    }
+    if (last) P.cw[myc] -= sum;
+  } else {
+    for (int k = 0; k < nk; ++k) {
+      const int tk = det_tok(k);
+      const float kw = k < 64 ? __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(kw_r), k)) : P.kid_w[k];
+      if (lane == 0 && tk >= 0) P.cw[tk / CT] -= kw;
+    }
   }
   wave_sync();
   // fp64 scan over chunks: lane l owns chunks [l * per, (l + 1) * per)
@@ -977,11 +994,16 @@ __device__ void pick_node(const VocabArgs& a, PickLds& P, int v) {
       }
     }
     take_step();   // (while the chunk's loads are in flight)
-    uint32_t zmask = 0;   // positions of this lane's tokens that are deterministic children
-    for (int k = 0; k < nk; ++k) {
-      const int d = det_tok(k) - e0;
-      if ((unsigned)d < (unsigned)EPU) zmask |= 1u << d;
+    // positions of this lane's tokens that are deterministic children: each child in the chosen chunk
+    // sets its bit in its owner lane's word (an OR, the same whatever the order)
+    P.zm[lane] = 0u;
+    wave_sync();
+    for (int k = lane; k < nk; k += 64) {
+      const int d = (k < 64 ? det_r : det_tok(k)) - pc * CT;   // (child k < 64 is this lane's)
+      if ((unsigned)d < (unsigned)CT) atomicOr(&P.zm[d / EPU], 1u << (d % EPU));
     }
+    wave_sync();
+    const uint32_t zmask = P.zm[lane];
     float w[EPU];
     float lsum = 0.f;
 #pragma unroll
