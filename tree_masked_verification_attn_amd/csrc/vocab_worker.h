@@ -874,7 +874,12 @@ __device__ void pick_node(const VocabArgs& a, PickLds& P, int v) {
   float kw_r = 0.f;
   for (int k = lane; k < nk; k += 64) {
     const int tk = P.kid_tok[k];
-    if (tk < 0 || tk >= V) err |= TAV_DEV_BAD_TOKEN;
+    const bool tok_ok = tk >= 0 && tk < V;
+    // the point loads go out first (token 0 stands in for a bad token), the checks run under them
+    const int tkc = tok_ok ? tk : 0;
+    const float z = logit_at<LT>(a.logits, (size_t)v * V + tkc);
+    const float qd = use_draft && !sparse ? a.draft[(size_t)dr * V + tkc] : 0.f;
+    if (!tok_ok) err |= TAV_DEV_BAD_TOKEN;
     if (k < 64) {
       for (int k2 = 0; k2 < min(nk, 64); ++k2)
         if (k2 < k && __builtin_amdgcn_readlane(tk, k2) == tk) err |= TAV_DEV_DUP_SIBLING_TOKEN;
@@ -884,9 +889,8 @@ __device__ void pick_node(const VocabArgs& a, PickLds& P, int v) {
     }
     P.kid_p[k] = 0.0;
     P.kid_q[k] = 0.f;
-    if (tk >= 0 && tk < V) {
-      const float z = logit_at<LT>(a.logits, (size_t)v * V + tk);
-      const float qz = !use_draft ? 0.f : sparse ? sp_q(tk) : a.draft[(size_t)dr * V + tk];
+    if (tok_ok) {
+      const float qz = !use_draft ? 0.f : sparse ? sp_q(tk) : qd;
       P.kid_p[k] = exp((double)(z * invT) - (double)M) / S;
       P.kid_q[k] = use_draft ? qz : 0.f;
       const float p = __builtin_amdgcn_exp2f(z * invTl2 - Ml2) * invS;
