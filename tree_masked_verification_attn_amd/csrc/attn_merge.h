@@ -34,7 +34,7 @@ __device__ inline void merge_rows(const AttnArgs& a, int D, int log2G, int r, in
   constexpr int kT = kMergeRows / 16;   // tasks per thread taken with their loads in flight together
                                         // (kMergeRows rows x D / 8 at D <= 128 on 256 threads); further
                                         // tasks go one by one
-  constexpr int kPre = 6;    // pieces loaded together (a batch), folded in by an online softmax
+  constexpr int kPre = 4;    // pieces loaded together (a batch), folded in by an online softmax
   auto task_row = [&](int task) { return row0 + task / DQ; };
   auto task_ok = [&](int task) { return task < ntask && (task_row(task) >> log2G) < nodes_here; };
   auto base_of = [&](int w, int row) {

@@ -660,7 +660,7 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
 // Online-softmax merge of the split row blocks (attn_merge.h): nmerge workgroups laid out by
 // merge_grid, then one workgroup per sequence for its sentinel rows.
 template <typename OutT>
-__global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int D, int log2G, int nmerge, int by_boundary) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void merge_kernel(AttnArgs a, int D, int log2G, int nmerge, int by_boundary) {
   const int i = blockIdx.x;
   if (i < nmerge) merge_block<OutT>(a, D, log2G, i, by_boundary != 0);
   else sentinel_rows<OutT>(a, D, i - nmerge);

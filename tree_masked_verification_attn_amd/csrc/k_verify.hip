@@ -171,7 +171,7 @@ __device__ void walk_sequence(const WalkArgs& a, int b) {
 // blocks (merge_kernel's work, laid out by merge_grid) and the next ns write sentinel rows of
 // sequences with attention errors (one sequence each; bf16 or, with f32, float32 outputs): work
 // that runs beside the walks instead of in a launch of its own.
-__global__ __launch_bounds__(kWalkThreads) void walk_kernel(WalkArgs w, AttnArgs a, int D, int log2G, int nm,
+__global__ __launch_bounds__(kWalkThreads) __attribute__((amdgpu_waves_per_eu(8))) void walk_kernel(WalkArgs w, AttnArgs a, int D, int log2G, int nm,
                                                             int by_boundary, int ns, int f32) {
   const int blk = blockIdx.x;
   if (blk < w.B) {
