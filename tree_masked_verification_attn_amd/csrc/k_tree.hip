@@ -40,32 +40,38 @@ struct OrderLds {
 };
 
 
-// Exclusive scan of one int per thread over the block; also returns the total.
+// Inclusive scan of one int per lane over the wave without LDS round trips: DPP row shifts inside each
+// row of 16 lanes (a lane whose source lies outside its row adds 0), then the rows' totals read with
+// readlane and added to the later rows.  Every lane of the wave must be active.
+template <int CTRL>
+__device__ inline int dpp_shr(int x) { return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false); }
+__device__ inline int wave_inclusive_scan(int x) {
+  x += dpp_shr<0x111>(x);   // row_shr:1
+  x += dpp_shr<0x112>(x);   // row_shr:2
+  x += dpp_shr<0x114>(x);   // row_shr:4
+  x += dpp_shr<0x118>(x);   // row_shr:8
+  const int t0 = __builtin_amdgcn_readlane(x, 15), t1 = __builtin_amdgcn_readlane(x, 31);
+  const int t2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row == 0 ? 0 : row == 1 ? t0 : row == 2 ? t0 + t1 : t0 + t1 + t2);
+}
+
+// Exclusive scan of one int per thread over the block; also returns the total.  Called by every thread.
 __device__ int block_exclusive_scan(int v, int* lds, int* total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    int y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
+  const int x = wave_inclusive_scan(v);
   if (lane == 63) lds[wid] = x;
   __syncthreads();
-  if (wid == 0) {
-    int s = lane < nw ? lds[lane] : 0;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      int y = __shfl_up(s, d, 64);
-      if (lane >= d) s += y;
-    }
-    if (lane < nw) lds[lane] = s;
+  int before = 0, tot = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int t = lds[w];
+    before += w < wid ? t : 0;
+    tot += t;
   }
-  __syncthreads();
-  int excl = (wid > 0 ? lds[wid - 1] : 0) + x - v;
-  *total = lds[nw - 1];
-  __syncthreads();
-  return excl;
+  *total = tot;
+  __syncthreads();   // (lds is reused by the next scan)
+  return before + x - v;
 }
 
 struct PrepArgs {
