@@ -42,6 +42,7 @@ namespace vw {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kCwBatch = 8;   // chunk weights per lane loaded together by the pick
+constexpr int kNoffLds = 256;   // sequence offsets a worker keeps in LDS (more sequences: read from memory)
 
 // A worker of NT threads reading NU sixteen-byte units per thread and step.  A chunk is 64 units,
 // one per lane of a wave, so chunk k * waves + w of a step is unit k of every lane of wave w.
@@ -69,7 +70,8 @@ struct Lds {
   double red_d[C::kWaves];
   float g_best[C::kWaves];                   // greedy rows: each wave's largest logit ...
   int g_idx[C::kWaves];                      // ... and its smallest token id
-  int item, cnt, ns, err;
+  int item, cnt, ns, err, next;
+  int noff[kNoffLds];                        // node_offsets[0..B] when B < kNoffLds
   uint4 lc[C::kCacheUnits];                  // dense draft rows: the logits row's first kCacheSteps
                                              // steps (each thread its own units)
 };
@@ -269,6 +271,30 @@ __device__ inline void load_step(uint4 (&r)[C::kUnits], const LT* row, int step,
   }
 }
 
+__device__ inline void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// The first step of a row copied from memory straight into the LDS cache, in the cache's layout
+// (unit k * NT + tid of the step for thread tid), holding no register while in flight: lane i of wave w
+// copies units k * NT + 64 w + i.  Issued through inline assembly, so that the compiler does not wait for
+// the copies before unrelated LDS accesses; every later load of the wave completes after them (the
+// counter is in order), so once a later load has been waited for, the cache holds the step.
+template <typename LT, class C>
+__device__ inline void dma_first_step(const LT* row, int nunits, uint32_t lc_addr, int tid) {
+  constexpr int EPU = 16 / sizeof(LT);
+  const int wave = tid >> 6;
+#pragma unroll
+  for (int k = 0; k < C::kUnits; ++k) {
+    const int u = k * C::kThreads + tid;
+    const LT* src = row + (size_t)(u < nunits ? u : 0) * EPU;
+    const uint32_t dst = lc_addr + (uint32_t)((k * C::kThreads + wave * 64) * 16);
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, off"
+        :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(dst)) : "memory", "m0");
+  }
+}
+
 // (value, token id) pairs: the larger value wins, equal values go to the smaller id.
 __device__ inline void better_of(float& best, int& bi, float ob, int oi) {
   if (ob > best || (ob == best && (unsigned)oi < (unsigned)bi)) {
@@ -323,6 +349,7 @@ __device__ void greedy_stream(const VocabArgs& a, Lds<C>& L, int v, int b, int s
       for (int k = 0; k < kUnits; ++k) cur[k] = nxt[k];
     }
   }
+  wait_vm0();   // (nothing else is in flight: the copies of the next node's first step, for one-step rows)
   bad |= best == INFINITY;
   // the position inside the best unit (one re-read of that unit, from the cache)
   int bi = -1;
@@ -369,7 +396,7 @@ __device__ void greedy_stream(const VocabArgs& a, Lds<C>& L, int v, int b, int s
 // pass 2), the chunk weights and the node's record into the workspace.  Thread 0 claims the next
 // queue slot into qn (read back after the node).
 template <typename LT, class C>
-__device__ void stream_node(const VocabArgs& a, Lds<C>& L, int v, int& qn) {
+__device__ void stream_node(const VocabArgs& a, Lds<C>& L, int v, int& qn, bool& pre_lds) {
   constexpr int kThreads = C::kThreads, kWaves = C::kWaves, kUnits = C::kUnits;
   constexpr int kStepUnits = C::kStepUnits, kChunksPerStep = C::kChunksPerStep;
   constexpr int TPC = 64 / kUnits;   // lanes per chunk total
@@ -379,22 +406,40 @@ __device__ void stream_node(const VocabArgs& a, Lds<C>& L, int v, int& qn) {
   const int V = a.V, nunits = V / EPU, nch = a.nch;
   const int nsteps = (nunits + kStepUnits - 1) / kStepUnits;
   const LT* row = (const LT*)a.logits + (size_t)v * V;
-  // the first step's loads go out before anything else, then the claim of the next node
+  // the first step: from the LDS cache when the previous node of this worker copied it there (its
+  // loads were waited for long ago), else its loads go out before anything else; then the claim of the
+  // next node and its id
   uint4 cur[kUnits];
-  load_step<LT, C>(cur, row, 0, tid, nunits);
-  if (tid == 0) qn = atomicAdd(a.queue, 1);
-  // sequence of v: the number of sequence ends node_offsets[1..B] that are <= v
+  if (pre_lds) {
+#pragma unroll
+    for (int k = 0; k < kUnits; ++k) cur[k] = L.lc[k * kThreads + tid];
+  } else {
+    load_step<LT, C>(cur, row, 0, tid, nunits);
+  }
+  pre_lds = false;
+  int nv = -1;
+  if (tid == 0) {
+    qn = atomicAdd(a.queue, 1);
+    nv = qn < a.N ? a.order[qn] : -1;
+  }
+  // sequence of v: the number of sequence ends node_offsets[1..B] that are <= v (from the worker's LDS
+  // copy when the batch has at most kNoffLds sequences)
+  const bool noff_lds = a.B < kNoffLds;
   if (tid == 0) { L.cnt = 0; L.ns = 0; L.err = 0; }
   __syncthreads();
   {
     int c = 0;
-    for (int t = tid + 1; t <= a.B; t += kThreads) c += a.node_offsets[t] <= v;
+    if (noff_lds) {
+      for (int t = tid + 1; t <= a.B; t += kThreads) c += L.noff[t] <= v;
+    } else {
+      for (int t = tid + 1; t <= a.B; t += kThreads) c += a.node_offsets[t] <= v;
+    }
     if (c) atomicAdd(&L.cnt, c);
   }
   __syncthreads();
   const int b = L.cnt < a.B ? L.cnt : a.B - 1;
-  const int s0 = a.node_offsets[b];
-  const int n = a.node_offsets[b + 1] - s0;
+  const int s0 = noff_lds ? L.noff[b] : a.node_offsets[b];
+  const int n = (noff_lds ? L.noff[b + 1] : a.node_offsets[b + 1]) - s0;
   const float Tb = a.temperature[b];
   const float invT = 1.f / Tb;
   const float invTl2 = invT * kLog2e;
@@ -410,14 +455,23 @@ __device__ void stream_node(const VocabArgs& a, Lds<C>& L, int v, int& qn) {
     }
     if (ns) atomicAdd(&L.ns, ns);
   }
+  if (tid == 0) L.next = nv;
   __syncthreads();
+  // a greedy row leaves the LDS cache unused and its pass (no exponentials) keeps too few bytes in flight:
+  // the next node's first step is copied into the cache while this node streams
+  const int next_v = __builtin_amdgcn_readfirstlane(L.next);
+  const bool dense_draft = L.ns > 0 && dr_ok && a.K == 0 && Tb != 0.f;
+  if (Tb == 0.f && next_v >= 0) {
+    const uint32_t lc_addr = (uint32_t)(size_t)(__attribute__((address_space(3))) uint4*)&L.lc[0];
+    dma_first_step<LT, C>((const LT*)a.logits + (size_t)next_v * V, nunits, lc_addr, tid);
+    pre_lds = true;
+  }
   if (Tb == 0.f) {   // greedy decoding: the verification token is the argmax
     greedy_stream<LT, C>(a, L, v, b, s0, n, cur, row, nunits, nsteps);
     return;
   }
   // ---- pass 1: per-piece references and sums, chunk weights relative to their piece
   float* part = L.part[wave];
-  const bool dense_draft = L.ns > 0 && dr_ok && a.K == 0;
   for (int s = 0; s < nsteps; ++s) {
     uint4 nxt[kUnits];
     if (s + 1 < nsteps) load_step<LT, C>(nxt, row, s + 1, tid, nunits);
@@ -467,6 +521,7 @@ __device__ void stream_node(const VocabArgs& a, Lds<C>& L, int v, int& qn) {
       for (int k = 0; k < kUnits; ++k) cur[k] = nxt[k];
     }
   }
+  wait_vm0();   // (nothing else is in flight: the copies of the next node's first step, for one-step rows)
   __syncthreads();
   // ---- M and S from the pieces (every wave computes the same values)
   const int npieces = nsteps * kWaves;
@@ -602,13 +657,15 @@ __device__ void vocab_stream(const VocabArgs& a, Lds<C>& L) {
     const int i = atomicAdd(a.queue, 1);
     L.item = i < a.N ? a.order[i] : -1;
   }
+  for (int t = threadIdx.x; t <= a.B && t < kNoffLds; t += C::kThreads) L.noff[t] = a.node_offsets[t];
   __syncthreads();
+  bool pre_lds = false;   // the first step of the worker's next node is in the LDS cache
   for (;;) {
     const int v = L.item;
     if (v < 0) return;
     int qn = 0;
-    stream_node<LT, C>(a, L, v, qn);   // (every thread has read L.item before its first barrier)
-    if (threadIdx.x == 0) L.item = qn < a.N ? a.order[qn] : -1;
+    stream_node<LT, C>(a, L, v, qn, pre_lds);   // (every thread has read L.item before its first barrier)
+    if (threadIdx.x == 0) L.item = L.next;
     __syncthreads();   // LDS reused by the next node
   }
 }
