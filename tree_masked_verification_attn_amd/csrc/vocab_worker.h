@@ -30,7 +30,8 @@
 // support's min(p, q~) out of the chunk weights of p and sums Z over the support.  Nodes are taken
 // from a device queue, in the order of an index list (nodes with a dense draft row first, so that
 // the long items do not come last); a worker never waits for another workgroup, and claims its
-// next node while it streams the current one.
+// next node while it streams the current one (after a greedy row, whose pass leaves the LDS cache
+// unused, it also copies the next node's first step into that cache).
 #pragma once
 
 #include <type_traits>
