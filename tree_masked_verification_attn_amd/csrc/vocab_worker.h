@@ -522,7 +522,6 @@ __device__ void stream_node(const VocabArgs& a, Lds<C>& L, int v, int& qn, bool&
       for (int k = 0; k < kUnits; ++k) cur[k] = nxt[k];
     }
   }
-  wait_vm0();   // (nothing else is in flight: the copies of the next node's first step, for one-step rows)
   __syncthreads();
   // ---- M and S from the pieces (every wave computes the same values)
   const int npieces = nsteps * kWaves;
