@@ -211,3 +211,32 @@ def test_two_runs_bit_identical():
     gu.check_attention(w, first, [v for b in range(w.B) for v in list(w.seq_nodes(b))[:5]])
     gu.check_verify(w, first)
     gu.check_node_stats(w, first, [int(w.node_offsets[b]) for b in range(w.B)])
+
+
+def test_many_children_packed_chunks():
+    """255 children of one root (more than one wave's worth, most of them past the window of
+    following nodes a node's children are gathered from) with the deterministic children's
+    tokens packed into one 512-token chunk, and 99 children spread over a few chunks: matches
+    the oracle and repeats bit for bit."""
+    w = gen.tree_batch(21, B=2, prefix_len=[300, 41], tree="star", n_nodes=[256, 100], Hq=16, Hkv=4,
+                       D=128, dtype="bf16", V=8192, temperature=0.8)
+    for b in range(w.B):
+        kids = _children(w, b, 0)
+        det = [c for c in kids if not w.sampled[c]]
+        samp_tok = {int(w.token[c]) for c in kids if w.sampled[c]}
+        lo, hi = (1024, 1536) if b == 0 else (1000, 2200)
+        free = [t for t in range(lo, hi) if t not in samp_tok]
+        step = 1 if b == 0 else 7
+        assert len(det) <= len(free)
+        for i, c in enumerate(det):
+            w.token[c] = free[(step * i) % len(free)]
+        assert len({int(w.token[c]) for c in kids}) == len(kids)
+    _say("many children packed chunks")
+    first = gu.run(w)
+    second = gu.run(w)
+    assert first["status"] == 0 and second["status"] == 0, (first["status"], second["status"])
+    for key in ("stats", "term", "node_status", "path", "path_len", "bonus"):
+        a, b = np.asarray(first[key]), np.asarray(second[key])
+        assert a.tobytes() == b.tobytes(), key
+    gu.check_verify(w, first)
+    gu.check_node_stats(w, first, [int(w.node_offsets[b]) for b in range(w.B)])
