@@ -143,13 +143,14 @@ def kernel_source_sha256():
     return h.hexdigest()
 
 
-def measured_traffic():
+def measured_traffic(workload):
     """HBM bytes per launch of the vocabulary workers' kernel from the committed counter data, or
-    None when the kernel sources have changed since the counters were taken."""
+    None when the counters were taken on another workload or the kernel sources have changed
+    since."""
     if not os.path.exists(PMC_FILE):
         return None
     rec = json.load(open(PMC_FILE))
-    if rec.get("kernel_source_sha256") != kernel_source_sha256():
+    if rec.get("workload") != workload or rec.get("kernel_source_sha256") != kernel_source_sha256():
         return None
     return int(rec["hbm_bytes_per_launch"])
 
@@ -555,7 +556,7 @@ def main():
     step_gbs = (attn_b + ver_b) / (ms * 1e-3) / 1e9
     roof = roofline_hbm("vocab_worker_kernel + pick_kernel (verification: logits and draft rows streamed "
                         "per node, then the pick of every node)",
-                        ver_b, kern_ms, ach, traffic=measured_traffic(), launches=kern_n)
+                        ver_b, kern_ms, ach, traffic=measured_traffic(args.workload), launches=kern_n)
 
     subs = {}
     if not args.no_sub:
