@@ -523,7 +523,7 @@ def main():
         print(kernel_source_sha256())
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the scoring pass has no multi-GPU path in this build "
+        print("bench.py measures one GPU: the scoring pass has no multi-GPU path "
               "(each configuration is one GPU's share); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
